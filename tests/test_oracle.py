@@ -1,0 +1,342 @@
+"""Pins for the CPU oracle: each test ties a part of it to something other than itself.
+
+Kinds of pin used: exact arithmetic (Python integers / fractions), a library routine that is
+independent of the oracle's code (torch's bf16 conversion, torch's scaled-dot-product attention
+in float64), brute force on tiny inputs (rank counting instead of sorting), closed forms
+(uniform weights over a bit-coded value table), and the complexity claim printed in the
+release post's "Key idea" section (tests/golden/complexity_claim.json).
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# ------------------------------------------------------------------------------------------ kappa
+def test_round_to_bf16_matches_torch_conversion():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32),
+                        (rng.standard_normal(2000) * 1e-30).astype(np.float32),
+                        (rng.standard_normal(2000) * 1e30).astype(np.float32),
+                        np.array([0.0, -0.0, 1.0, -3.5, 2.0 ** -126, 2.0 ** -130], dtype=np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(O.round_to_bf16(x), ref)
+
+
+def test_round_to_bf16_ties_to_even():
+    one = 1.0
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7 (odd significand) -> 1
+    assert O.round_to_bf16(np.float32(one + 2.0 ** -8)) == np.float32(1.0)
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even) -> 1 + 2^-6
+    assert O.round_to_bf16(np.float32(one + 3 * 2.0 ** -8)) == np.float32(1 + 2.0 ** -6)
+    # just above the halfway point rounds up
+    assert O.round_to_bf16(np.float32(one + 2.0 ** -8 + 2.0 ** -20)) == np.float32(1 + 2.0 ** -7)
+
+
+# ---------------------------------------------------------------------------------- summaries
+def test_summary_of_constant_span_is_that_constant():
+    S, d = 16, 8
+    for c in [0.375, -2.5, 1.0 / 1024]:  # dyadic constants: every partial sum is exact in fp32
+        keys = np.full((2, 5 * S, d), c, dtype=np.float32)
+        means, run = O.summaries(keys, 5 * S, S)
+        assert np.all(means == np.float32(c))
+        assert np.all(run == 0)
+
+
+def test_summary_integer_keys_exact_mean():
+    """Small-integer keys sum exactly in fp32; the mean must be the exact rational sum/S."""
+    rng = np.random.default_rng(2)
+    S, d, L = 8, 6, 8 * 7 + 3
+    ints = rng.integers(-50, 51, size=(3, L, d))
+    keys = ints.astype(np.float32)
+    means, run = O.summaries(keys, L, S)
+    assert means.shape == (3, L // S, d)
+    for h in range(3):
+        for j in range(L // S):
+            for e in range(d):
+                exact = Fraction(int(ints[h, j * S:(j + 1) * S, e].sum()), S)
+                assert Fraction(float(means[h, j, e])) == exact
+        # open span: running sum of the 3 tail tokens, exact
+        for e in range(d):
+            assert run[h, e] == float(ints[h, (L // S) * S:, e].sum())
+
+
+def test_summary_sums_in_token_order_in_fp32():
+    """1 followed by S-1 copies of 2^-24: each fp32 addition 1 + 2^-24 ties to even -> 1."""
+    S = 4
+    keys = np.array([[[1.0], [2.0 ** -24], [2.0 ** -24], [2.0 ** -24]]], dtype=np.float32)
+    means, _ = O.summaries(keys, S, S)
+    assert means[0, 0, 0] == np.float32(0.25)
+    # the exactly rounded mean would differ: the order-of-addition reading is what is pinned
+    assert np.float32((1 + 3 * 2.0 ** -24) / 4) != np.float32(0.25)
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 16, 100])
+def test_summary_incremental_equals_one_shot(chunk):
+    rng = np.random.default_rng(3)
+    S, d, L = 16, 8, 16 * 9 + 5
+    keys = rng.standard_normal((2, L, d)).astype(np.float32)
+    m1, r1 = O.summaries(keys, L, S)
+    means = np.zeros((2, L // S, d), dtype=np.float32)
+    run = np.zeros((2, d), dtype=np.float32)
+    p = 0
+    while p < L:
+        q = min(L, p + chunk)
+        O.summary_update(keys, means, run, p, q, S)
+        p = q
+    assert np.array_equal(means, m1) and np.array_equal(run, r1)
+
+
+def test_summary_close_to_exact_mean():
+    rng = np.random.default_rng(4)
+    S, d, L = 64, 16, 64 * 6
+    keys = rng.standard_normal((1, L, d)).astype(np.float32)
+    means, _ = O.summaries(keys, L, S)
+    exact = keys.astype(np.float64).reshape(1, 6, S, d).mean(axis=2)
+    bound = S * 2.0 ** -24 * np.abs(keys.astype(np.float64)).reshape(1, 6, S, d).mean(axis=2) * 1.01 + 1e-30
+    assert np.all(np.abs(means - exact) <= bound)
+
+
+# ------------------------------------------------------------------------------ window / spans
+def test_window_and_routable_closed_forms():
+    S, W = 64, 64
+    assert O.window_start(0, S, W) == 0 and O.num_routable(0, S, W) == 0
+    assert O.num_routable(126, S, W) == 0
+    assert O.num_routable(127, S, W) == 1 and O.window_start(127, S, W) == 64
+    for t in range(0, 2000):
+        w0 = O.window_start(t, S, W)
+        assert w0 % S == 0 and w0 <= max(0, t - W + 1)
+        size = t - w0 + 1
+        assert size <= W + S - 1
+        assert t < W - 1 or size >= W
+    # W = 3S: window holds 3S .. 4S-1 tokens once t is large
+    for t in range(1000, 1200):
+        assert 3 * 16 <= t - O.window_start(t, 16, 48) + 1 <= 4 * 16 - 1
+
+
+def test_every_past_token_is_routable_or_in_window():
+    for S, W in [(8, 8), (8, 1), (8, 20), (5, 13)]:
+        for t in range(0, 200):
+            r = O.num_routable(t, S, W)
+            covered = set(range(0, r * S)) | set(range(O.window_start(t, S, W), t + 1))
+            assert covered == set(range(t + 1)), (S, W, t)
+
+
+# ------------------------------------------------------------------------------------ scores
+def test_scores_exact_on_integers_and_unscaled():
+    rng = np.random.default_rng(5)
+    d, r = 32, 20
+    q = rng.integers(-4, 5, size=d).astype(np.float32)
+    means = rng.integers(-3, 4, size=(r + 3, d)).astype(np.float32)
+    s = O.route_scores(q, means, r, is_bf16=True)  # small integers are bf16-exact
+    for j in range(r):
+        assert s[j] == sum(int(q[e]) * int(means[j, e]) for e in range(d))
+    assert len(s) == r
+
+
+def test_scores_round_mean_to_bf16_for_bf16_inputs():
+    means = np.array([[1.0 + 2.0 ** -9, 0.0]], dtype=np.float32)
+    q = np.array([1.0, 0.0], dtype=np.float32)
+    assert O.route_scores(q, means, 1, is_bf16=True)[0] == 1.0
+    assert O.route_scores(q, means, 1, is_bf16=False)[0] == 1.0 + 2.0 ** -9
+
+
+# --------------------------------------------------------------------------------- selection
+def _brute_selection(scores, k):
+    """j is kept iff fewer than m spans beat it: rank counting, no sorting."""
+    r = len(scores)
+    m = min(k, r)
+    keep = [j for j in range(r)
+            if sum(1 for i in range(r) if scores[i] > scores[j] or (scores[i] == scores[j] and i < j)) < m]
+    return keep + [-1] * (k - len(keep))
+
+
+def test_selection_matches_rank_counting_with_ties():
+    rng = np.random.default_rng(6)
+    for trial in range(300):
+        r = int(rng.integers(0, 25))
+        k = int(rng.integers(1, 10))
+        scores = rng.integers(-3, 4, size=r).astype(np.float64) * 0.5  # many exact ties
+        assert list(O.select_spans(scores, k)) == _brute_selection(list(scores), k)
+
+
+def test_selection_matches_exhaustive_subset_search():
+    """The kept set maximises the score sum; among maximisers, it is lexicographically smallest."""
+    rng = np.random.default_rng(7)
+    for _ in range(60):
+        r = int(rng.integers(1, 11))
+        k = int(rng.integers(1, 6))
+        scores = rng.standard_normal(r)
+        m = min(k, r)
+        best = max(itertools.combinations(range(r), m), key=lambda c: (sum(scores[j] for j in c), [-j for j in c]))
+        assert list(O.select_spans(scores, k)[:m]) == sorted(best)
+
+
+def test_selection_special_cases():
+    assert list(O.select_spans(np.zeros(10), 4)) == [0, 1, 2, 3]          # q = 0: lowest indices win
+    assert list(O.select_spans(np.array([1.0, 2.0]), 4)) == [0, 1, -1, -1]  # k > r: all spans
+    assert list(O.select_spans(np.array([]), 3)) == [-1, -1, -1]           # r = 0: window only
+    s = np.array([0.1, 5.0, 3.0, 5.0, 3.0])                               # duplicates: lower index wins
+    assert list(O.select_spans(s, 3)) == [1, 2, 3]
+
+
+# ------------------------------------------------------------------------- attended set / softmax
+def _count_bit_set(a, b, e):
+    """How many integers in [a, b] have bit e set (closed form)."""
+    def upto(n):  # integers in [0, n)
+        block = 1 << (e + 1)
+        return (n // block) * (1 << e) + max(0, n % block - (1 << e))
+    return upto(b + 1) - upto(a)
+
+
+def _bitcoded_problem(L, S, k, W, d, hkv=1, hq=1, bf16=False):
+    pos = np.arange(L)
+    vals = ((pos[:, None] >> np.arange(d)[None, :]) & 1).astype(np.float32)
+    values = np.broadcast_to(vals, (hkv, L, d)).copy()
+    rng = np.random.default_rng(8)
+    keys = rng.standard_normal((hkv, L, d)).astype(np.float32)
+    return keys, values
+
+
+def test_zero_query_gives_uniform_average_over_exact_token_set():
+    L, S, k, W, d = 1500, 16, 5, 24, 12
+    keys, values = _bitcoded_problem(L, S, k, W, d)
+    prob = O.Problem(keys, values, L, 1, S, k, W, is_bf16=False)
+    q = np.zeros(d, dtype=np.float32)
+    for t in [0, 5, 38, 39, 40, 100, 777, 1499]:
+        res = prob.row(q, 0, t)
+        r = O.num_routable(t, S, W)
+        m = min(k, r)
+        w0 = O.window_start(t, S, W)
+        ranges = [(j * S, j * S + S - 1) for j in range(m)] + [(w0, t)]  # q = 0 -> spans 0..m-1
+        n = sum(b - a + 1 for a, b in ranges)
+        assert res["n_attended"] == n
+        for e in range(d):
+            frac = Fraction(sum(_count_bit_set(a, b, e) for a, b in ranges), n)
+            assert abs(res["out"][e] - float(frac)) < 1e-12, (t, e)
+        assert abs(res["weight_sum"] - 1.0) < 1e-12
+
+
+def test_constant_values_give_constant_output_and_weights_sum_to_one():
+    rng = np.random.default_rng(9)
+    L, S, k, W, d = 900, 8, 3, 8, 16
+    keys = (rng.standard_normal((2, L, d)) * 3).astype(np.float32)
+    values = np.ones((2, L, d), dtype=np.float32)
+    prob = O.Problem(keys, values, L, 4, S, k, W, is_bf16=False)
+    for t in [3, 64, 899]:
+        q = (rng.standard_normal(d) * 4).astype(np.float32)
+        for hq in range(4):
+            res = prob.row(q, hq, t)
+            assert np.allclose(res["out"], 1.0, atol=1e-13, rtol=0)
+            assert abs(res["weight_sum"] - 1.0) < 1e-12
+
+
+def test_dominant_key_wins():
+    L, S, k, W, d = 256, 8, 2, 8, 4
+    keys = np.zeros((1, L, d), dtype=np.float32)
+    values = np.random.default_rng(10).standard_normal((1, L, d)).astype(np.float32)
+    keys[0, 37] = [100.0, 0, 0, 0]
+    # span 4 (positions 32..39) holds the only large key; its mean dominates routing
+    prob = O.Problem(keys, values, L, 1, S, k, W, is_bf16=False)
+    res = prob.row(np.array([10.0, 0, 0, 0], dtype=np.float32), 0, 255)
+    assert 4 in res["sel"]
+    assert np.allclose(res["out"], values[0, 37], atol=1e-12)
+
+
+# ------------------------------------------------------------------- whole path vs a library routine
+def _sdpa_f64(q, keys, values, mask):
+    """torch scaled_dot_product_attention in float64 (independent of the oracle's code)."""
+    qt = torch.from_numpy(np.asarray(q, dtype=np.float64))[None, None, None, :]
+    kt = torch.from_numpy(keys.astype(np.float64))[None, None]
+    vt = torch.from_numpy(values.astype(np.float64))[None, None]
+    mt = torch.from_numpy(mask)[None, None, None, :]
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mt)[0, 0, 0].numpy()
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_k_all_spans_equals_dense_causal_attention(bf16):
+    rng = np.random.default_rng(11)
+    L, S, W, d, hkv, hq = 333, 8, 8, 16, 2, 4
+    keys = rng.standard_normal((hkv, L, d)).astype(np.float32)
+    values = rng.standard_normal((hkv, L, d)).astype(np.float32)
+    qs = rng.standard_normal((L, hq, d)).astype(np.float32)
+    if bf16:
+        to_bits = lambda a: (torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+        keys, values, qs = to_bits(keys), to_bits(values), to_bits(qs)
+    k_all = L // S + 1
+    prob = O.Problem(keys, values, L, hq, S, k_all, W, is_bf16=bf16)
+    kd, vd, qd = O.widen(keys, bf16), O.widen(values, bf16), O.widen(qs, bf16)
+    for t in list(range(0, 40)) + list(range(300, L)):
+        for h in range(hq):
+            res = prob.row(qs[t, h], h, t)
+            mask = np.arange(L) <= t
+            ref = _sdpa_f64(qd[t, h], kd[h // 2], vd[h // 2], mask)
+            assert np.abs(res["out"] - ref).max() < 1e-12, (t, h)
+
+
+def test_routed_equals_masked_attention_over_selected_tokens():
+    rng = np.random.default_rng(12)
+    L, S, W, k, d = 640, 16, 20, 3, 8
+    keys = rng.standard_normal((1, L, d)).astype(np.float32)
+    values = rng.standard_normal((1, L, d)).astype(np.float32)
+    prob = O.Problem(keys, values, L, 1, S, k, W, is_bf16=False)
+    for t in [100, 333, 639]:
+        q = rng.standard_normal(d).astype(np.float32)
+        res = prob.row(q, 0, t)
+        mask = np.zeros(L, dtype=bool)
+        for j in res["sel"]:
+            if j >= 0:
+                mask[j * S:(j + 1) * S] = True
+        mask[O.window_start(t, S, W):t + 1] = True
+        assert not mask[t + 1:].any()
+        ref = _sdpa_f64(q, keys[0], values[0], mask)
+        assert np.abs(res["out"] - ref).max() < 1e-12
+
+
+def test_planted_needle_is_routed():
+    rng = np.random.default_rng(13)
+    L, S, W, k, d = 4096, 64, 64, 2, 32
+    keys = rng.standard_normal((1, L, d)).astype(np.float32)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    keys[0, 17 * S:18 * S] += (4 * u).astype(np.float32)  # span 17 carries a strong direction
+    values = rng.standard_normal((1, L, d)).astype(np.float32)
+    prob = O.Problem(keys, values, L, 1, S, k, W, is_bf16=False)
+    res = prob.row((8 * u).astype(np.float32), 0, L - 1)
+    assert 17 in res["sel"]
+
+
+# --------------------------------------------------------------------------------- comparator
+def test_comparator_accepts_near_ties_and_rejects_real_swaps():
+    scores = np.array([1.0, 0.5, 0.5000001, 0.2, -1.0])
+    oracle_sel = O.select_spans(scores, 2)
+    assert list(oracle_sel) == [0, 2]
+    assert O.selection_verdict(oracle_sel, oracle_sel, scores, 2, 0.0) == "exact"
+    assert O.selection_verdict(np.array([0, 1]), oracle_sel, scores, 2, 0.0) == "near_tie"
+    assert O.selection_verdict(np.array([0, 3]), oracle_sel, scores, 2, 0.0).startswith("fail")
+    assert O.selection_verdict(np.array([1, 2]), oracle_sel, scores, 2, 0.0).startswith("fail")
+    assert O.selection_verdict(np.array([2, 0]), oracle_sel, scores, 2, 0.0).startswith("fail")
+    assert O.selection_verdict(np.array([0, -1]), oracle_sel, scores, 2, 0.0).startswith("fail")
+    assert O.selection_verdict(np.array([0, 7]), oracle_sel, scores, 2, 0.0).startswith("fail")
+
+
+# ------------------------------------------------------------------------- the page's claim
+def test_search_budget_grows_like_sqrt_of_context():
+    with open(os.path.join(HERE, "golden", "complexity_claim.json")) as f:
+        claim = json.load(f)
+    ratio_ctx = claim["context_growth"]
+    budget = []
+    for L in [2 ** 20, 2 ** 20 * ratio_ctx]:
+        S = int(round(math.sqrt(L)))
+        t = L - 1
+        budget.append(O.num_routable(t, S, S) + 1)  # spans scored by the last query (+ its window span)
+    assert abs(budget[1] / budget[0] - claim["search_budget_growth"]) <= claim["tolerance"]
