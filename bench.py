@@ -1,0 +1,224 @@
+"""Benchmark: one decode step of content-routed sparse attention at 1M context, on one GPU.
+
+A step is the whole hot path for one new token of one sequence at L = 1,048,576 (32 query
+heads, 4 kv heads, d = 128, bf16 cache, spans of 1024, top-16 + window of 1024):
+span_summary_update (the new token) -> route_scores -> topk_spans -> routed_attn_decode.
+Inputs are synthetic (seeded generator), resident in HBM before timing starts.
+
+So that every step reads its keys and values from HBM rather than from the 256 MB Infinity
+Cache, the bench keeps `--caches` independent 1M-token sequences (2 GiB of K/V each) and step
+i works on sequence i mod caches; each step is the same single-sequence workload.
+
+Prints one JSON line.  `--gpus` above 1 is refused: this path runs on one GPU.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-attn decode & prefill tokens/s per layer @1M ctx; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--caches", type=int, default=4)
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs the single-GPU path only (one GPU per process, no sharding); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import content_routed_sparse_amd as ra
+    from synth import BF16
+    from synth import workloads as WL
+
+    w = WL.WORKLOADS["decode_1m"]
+    L = w.decode_len
+    NC = args.caches
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg1 = ra.Config(w.num_q_heads, w.num_kv_heads, w.head_dim, w.span_size, w.top_k, w.window, ra.RA_BF16, 1, L)
+
+    # ---- inputs: NC independent sequences, generated on the host, copied once into HBM
+    t0 = time.time()
+    K = torch.empty(NC, w.num_kv_heads, L, w.head_dim, dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    for s in range(NC):
+        K[s] = torch.from_numpy(WL.kv_slab(w, s, 0, L, "k").view(np.int16)).view(torch.bfloat16).to(dev)
+        V[s] = torch.from_numpy(WL.kv_slab(w, s, 0, L, "v").view(np.int16)).view(torch.bfloat16).to(dev)
+    qs = [torch.from_numpy(WL.query_at(w, s, L - 1)[None].view(np.int16)).view(torch.bfloat16).to(dev)
+          for s in range(NC)]
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+
+    # ---- per-sequence state and buffers (allocated once)
+    stride = cfg1.num_routable(L - 1)
+    st = []
+    for s in range(NC):
+        d = {
+            "k": K[s:s + 1], "v": V[s:s + 1],
+            "mean": torch.zeros(1, w.num_kv_heads, cfg1.max_spans, w.head_dim, dtype=torch.float32, device=dev),
+            "run": torch.zeros(1, w.num_kv_heads, w.head_dim, dtype=torch.float32, device=dev),
+            "rows": ra.Rows(qs[s], torch.zeros(1, dtype=torch.int32, device=dev),
+                            torch.full((1,), L - 1, dtype=torch.int64, device=dev), L - 1),
+            "scores": torch.empty(1, w.num_q_heads, stride, dtype=torch.float32, device=dev),
+            "sel": torch.empty(1, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev),
+            "out": torch.empty(1, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev),
+        }
+        st.append(d)
+    ws = torch.empty(ra.workspace_bytes(cfg1, ra.RA_OP_DECODE, 1, L - 1), dtype=torch.uint8, device=dev)
+    zero = torch.zeros(1, dtype=torch.int64, device=dev)
+    before = torch.full((1,), L - 1, dtype=torch.int64, device=dev)
+    after = torch.full((1,), L, dtype=torch.int64, device=dev)
+    # setup (untimed): summaries of the L-1 tokens already in each cache
+    for d in st:
+        ra.span_summary_update(cfg1, d["k"], d["mean"], d["run"], zero, before, L - 1)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    n_ev = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+
+    def step(i, timed):
+        d = st[i % NC]
+        # the new token (position L-1) joins its span; re-running the step re-closes that span,
+        # which lies inside the window and is never routed at this position
+        ra.span_summary_update(cfg1, d["k"], d["mean"], d["run"], before, after, 1)
+        ra.route_scores(cfg1, d["rows"], d["mean"], d["scores"])
+        ra.topk_spans(cfg1, d["rows"], d["scores"], d["sel"])
+        if timed:
+            ev[i][0].record(stream)
+        ra.routed_attn_decode(cfg1, d["rows"], d["k"], d["v"], d["sel"], d["out"], ws)
+        if timed:
+            ev[i][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    first = [d["out"].clone() for d in st]
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+
+    ms_per_step = t_total * 1e3 / args.steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    same = all(torch.equal(first[s], st[s]["out"]) for s in range(NC))
+
+    # ---- algorithmic bytes of routed_attn_decode: K and V rows of the union of the spans the
+    # query heads of each kv head selected, plus the window, plus q (bf16) and out (fp32)
+    G = w.group
+    win = (L - 1) - (w.span_size * (max(0, L - 1 - w.window + 1) // w.span_size)) + 1
+    per_seq = []
+    for d in st:
+        sel = d["sel"][0].cpu().numpy()
+        uni = sum(len(set(sel[g * G:(g + 1) * G].ravel().tolist()) - {-1}) for g in range(w.num_kv_heads))
+        kv = (uni * w.span_size + w.num_kv_heads * win) * w.head_dim * 2 * 2
+        per_seq.append(kv + w.num_q_heads * w.head_dim * (2 + 4))
+    bytes_step = float(np.mean([per_seq[i % NC] for i in range(args.steps)]))
+    achieved = bytes_step / (attn_ms * 1e-3) / 1e9
+
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "decode_attn_decode_1m_traffic.json")
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
+        src = open(os.path.join(ROOT, "content_routed_sparse_amd", "csrc", "decode.hip"), "rb").read()
+        if rec.get("source_sha256") == hashlib.sha256(src).hexdigest():
+            traffic = rec.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_per_step, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_1m", "context": L, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "span": w.span_size, "top_k": w.top_k, "window": w.window, "batch": 1,
+                   "rotated_sequences": NC},
+        "roofline": {"bound": "hbm", "kernel": "routed_attn_decode (decode_attn + combine)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(bytes_step), "avg_launch_ms": round(attn_ms, 5)},
+        "repeat_bitwise_identical": bool(same),
+        "setup_seconds": round(gen_s, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], result["oracle_check"] = cpu_baseline(w, st[0], args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, d0, seconds):
+    """The CPU oracle, untuned, on decode steps of sequence 0 (single thread)."""
+    import threadpoolctl
+
+    import oracle as O
+    from synth import workloads as WL
+
+    L = w.decode_len
+    kh = WL.kv_slab(w, 0, 0, L, "k")
+    vh = WL.kv_slab(w, 0, 0, L, "v")
+    q = WL.query_at(w, 0, L - 1)
+    with threadpoolctl.threadpool_limits(1):
+        kf = O.widen_f32(kh, True)
+        means, run = O.summaries(kf[:, :L - 1], L - 1, w.span_size, max_spans=L // w.span_size)  # setup, untimed
+        steps, outs = 0, None
+        t0 = time.perf_counter()
+        while True:
+            m2, r2 = means.copy(), run.copy()
+            O.summary_update(kf, m2, r2, L - 1, L, w.span_size)
+            prob = O.Problem(kh, vh, L, w.num_q_heads, w.span_size, w.top_k, w.window, True, means=m2)
+            outs = [prob.row(q[h], h, L - 1) for h in range(w.num_q_heads)]
+            steps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        el = time.perf_counter() - t0
+    # the oracle's result for this step, compared with the GPU's (selection exact or near-tie)
+    gsel = d0["sel"][0].cpu().numpy()
+    gout = d0["out"][0].cpu().numpy()
+    worst, kinds = 0.0, {"exact": 0, "near_tie": 0, "fail": 0}
+    for h, res in enumerate(outs):
+        r = len(res["scores"])
+        bound = O.score_abs_bound(prob.q64(q[h]), prob.means[h // w.group], r, True)
+        v = O.selection_verdict(gsel[h], res["sel"], res["scores"], w.top_k, bound)
+        kinds["fail" if v.startswith("fail") else v] += 1
+        ref = res["out"] if v == "exact" else prob.row(q[h], h, L - 1, sel=gsel[h])["out"]
+        worst = max(worst, float(np.abs(gout[h] - ref).max()))
+    base = {"value": round(steps / el, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d decode steps of one 1M-token sequence (summary update + 32 rows), numpy float64, "
+                      "1 BLAS thread" % steps}
+    return base, {"selection": kinds, "max_abs_err": worst}
+
+
+if __name__ == "__main__":
+    main()

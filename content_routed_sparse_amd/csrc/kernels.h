@@ -1,0 +1,41 @@
+// Internal launch interface between the C ABI layer (abi.hip) and the kernel files.
+// Arguments arrive here already validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+struct SummaryArgs {
+    const void *k;
+    float *mean, *run_sum;
+    const int64_t *old_len, *new_len;
+    int dtype, d, B, Hkv, S;
+    int64_t cap, max_spans, max_new;
+};
+
+struct RowArgs {  // query rows and shapes shared by routing, selection and attention
+    const void *q;
+    const int32_t *row_seq;
+    const int64_t *row_pos;
+    int64_t n_rows, max_pos;
+    int dtype, d, Hq, Hkv, G, S, k, W, B;
+    int64_t cap, max_spans;
+};
+
+hipError_t launch_summary(const SummaryArgs &a, hipStream_t st);
+hipError_t launch_route(const RowArgs &a, const float *mean, float *scores, int64_t stride, hipStream_t st);
+hipError_t launch_topk(const RowArgs &a, const float *scores, int64_t stride, int32_t *sel, hipStream_t st);
+
+// Decode: workspace holds partial records [n_rows][Hq][k + max_window_spans][n_sub].
+size_t decode_workspace_bytes(const RowArgs &a);
+hipError_t launch_decode(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out,
+                         void *ws, hipStream_t st);
+
+// Prefill: span-major dispatch + tiles + merge.
+size_t prefill_workspace_bytes(const RowArgs &a);
+hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out,
+                          void *ws, hipStream_t st);
+
+}  // namespace ra

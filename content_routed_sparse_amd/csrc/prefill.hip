@@ -1,0 +1,211 @@
+// Prefill attention: the same exact attention for a chunk of many rows (release post, "Key
+// idea"; the post's stack processes long prompts by chunked prefill).
+//
+// Rows that attend to the same span share its keys, so the work is regrouped span by span, the
+// way tokens are dispatched to experts: every (row-head, entry) pair -- entries are the k
+// selected spans and the window spans of the row -- is appended to the bucket of its
+// (sequence, kv head, span).  Buckets are cut into tiles of at most MT entries, a tile runs as
+// one block over the span's keys (a dense Q.K^T / softmax / P.V on MFMA for bf16), and the
+// per-span partial softmax states are merged per row in fixed order by the combine kernel.
+// Keys after a row's own position are masked (only window spans can contain them).  Results do
+// not depend on the order of entries inside a bucket: every row's state is computed from its
+// own query and the span's keys alone.
+//
+// Workspace (all offsets 256-byte aligned):
+//   counts[n_exp+1], offsets[n_exp+1], tile_off[n_exp+1]   int32
+//   local[n_ent], list[n_ent]                               int32   (n_ent = n_rowheads * NE)
+//   tiles[max_tiles]                                        int2    (expert, first entry)
+//   records[n_ent]                                          float x (4 + d)
+#include "common.h"
+#include "kernels.h"
+#include "prefill_tiles.h"
+
+namespace ra {
+
+hipError_t launch_combine(const RowArgs &a, const float *part, const int32_t *sel, float *out, int nsub, int TK,
+                          hipStream_t st);
+
+namespace {
+
+struct PrefillLayout {
+    int64_t n_exp, n_ent, max_tiles, span_slots;
+    size_t off_counts, off_offsets, off_tile_off, off_local, off_list, off_tiles, off_records, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+PrefillLayout prefill_layout(const RowArgs &a) {
+    PrefillLayout L;
+    const int NE = a.k + max_window_spans(a.S, a.W);
+    L.span_slots = ceil_div(a.cap, a.S);
+    L.n_exp = (int64_t)a.B * a.Hkv * L.span_slots;
+    L.n_ent = a.n_rows * a.Hq * NE;
+    const int MT = prefill_tile_rows(a);
+    L.max_tiles = ceil_div(L.n_ent, MT) + (L.n_exp < L.n_ent ? L.n_exp : L.n_ent);
+    size_t o = 0;
+    L.off_counts = o;   o = align256(o + (L.n_exp + 1) * 4);
+    L.off_offsets = o;  o = align256(o + (L.n_exp + 1) * 4);
+    L.off_tile_off = o; o = align256(o + (L.n_exp + 1) * 4);
+    L.off_local = o;    o = align256(o + L.n_ent * 4);
+    L.off_list = o;     o = align256(o + L.n_ent * 4);
+    L.off_tiles = o;    o = align256(o + L.max_tiles * 8);
+    L.off_records = o;  o = align256(o + (size_t)L.n_ent * record_floats(a.d) * 4);
+    L.total = o;
+    return L;
+}
+
+__global__ void fill_i32(int32_t *p, int64_t n, int32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// expert id and key range of entry e of a row-head; false if the entry attends to nothing
+__device__ __forceinline__ bool entry_span(const int32_t *sel, int64_t rh, int e, int k, int64_t t, int S, int W,
+                                           int64_t &j) {
+    const int64_t w0 = window_start(t, S, W);
+    if (e < k) {
+        j = sel[rh * k + e];
+        return j >= 0 && j < w0 / S;
+    }
+    j = w0 / S + (e - k);
+    return j * S <= t;
+}
+
+__global__ void count_kernel(const int32_t *__restrict__ sel, const int32_t *__restrict__ row_seq,
+                             const int64_t *__restrict__ row_pos, int32_t *__restrict__ counts,
+                             int32_t *__restrict__ local, int64_t n_ent, int NE, int Hq, int Hkv, int G, int S, int k,
+                             int W, int B, int64_t max_pos, int64_t span_slots) {
+    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= n_ent) return;
+    const int64_t rh = x / NE;
+    const int e = (int)(x % NE);
+    const int64_t row = rh / Hq;
+    const int g = (int)(rh % Hq) / G;
+    int64_t t = row_pos[row];
+    t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
+    int seq = row_seq[row];
+    seq = seq < 0 ? 0 : (seq >= B ? B - 1 : seq);
+    int64_t j;
+    int32_t slot = -1;
+    if (entry_span(sel, rh, e, k, t, S, W, j)) {
+        const int64_t expert = ((int64_t)seq * Hkv + g) * span_slots + j;
+        slot = atomicAdd(&counts[expert], 1);
+    }
+    local[x] = slot;
+}
+
+// Exclusive scans of counts and of tiles per expert, in one block.
+__global__ void __launch_bounds__(1024) scan_kernel(const int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                                    int32_t *__restrict__ tile_off, int64_t n_exp, int MT) {
+    __shared__ int32_t sa[1024], sb[1024];
+    __shared__ int32_t carry_a, carry_b;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        carry_a = 0;
+        carry_b = 0;
+    }
+    __syncthreads();
+    for (int64_t base = 0; base < n_exp; base += 1024) {
+        const int64_t i = base + tid;
+        const int32_t c = i < n_exp ? counts[i] : 0;
+        int32_t va = c, vb = (c + MT - 1) / MT;
+        sa[tid] = va;
+        sb[tid] = vb;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele inclusive scan
+            const int32_t ta = tid >= off ? sa[tid - off] : 0;
+            const int32_t tb = tid >= off ? sb[tid - off] : 0;
+            __syncthreads();
+            sa[tid] += ta;
+            sb[tid] += tb;
+            __syncthreads();
+        }
+        if (i < n_exp) {
+            offsets[i] = carry_a + sa[tid] - va;
+            tile_off[i] = carry_b + sb[tid] - vb;
+        }
+        __syncthreads();
+        if (tid == 1023) {
+            carry_a += sa[1023];
+            carry_b += sb[1023];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        offsets[n_exp] = carry_a;
+        tile_off[n_exp] = carry_b;
+    }
+}
+
+__global__ void scatter_kernel(const int32_t *__restrict__ sel, const int32_t *__restrict__ row_seq,
+                               const int64_t *__restrict__ row_pos, const int32_t *__restrict__ offsets,
+                               const int32_t *__restrict__ local, int32_t *__restrict__ list, int64_t n_ent, int NE,
+                               int Hq, int Hkv, int G, int S, int k, int W, int B, int64_t max_pos,
+                               int64_t span_slots) {
+    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= n_ent) return;
+    const int32_t slot = local[x];
+    if (slot < 0) return;
+    const int64_t rh = x / NE;
+    const int e = (int)(x % NE);
+    const int64_t row = rh / Hq;
+    const int g = (int)(rh % Hq) / G;
+    int64_t t = row_pos[row];
+    t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
+    int seq = row_seq[row];
+    seq = seq < 0 ? 0 : (seq >= B ? B - 1 : seq);
+    int64_t j;
+    entry_span(sel, rh, e, k, t, S, W, j);
+    const int64_t expert = ((int64_t)seq * Hkv + g) * span_slots + j;
+    list[offsets[expert] + slot] = (int32_t)x;
+}
+
+__global__ void tiles_kernel(const int32_t *__restrict__ counts, const int32_t *__restrict__ tile_off,
+                             int2 *__restrict__ tiles, int64_t n_exp, int MT) {
+    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= n_exp) return;
+    const int32_t c = counts[x];
+    const int32_t base = tile_off[x];
+    for (int32_t i = 0; i * MT < c; ++i) tiles[base + i] = make_int2((int32_t)x, i * MT);
+}
+
+}  // namespace
+
+size_t prefill_workspace_bytes(const RowArgs &a) { return prefill_layout(a).total; }
+
+int64_t prefill_entry_count(const RowArgs &a) { return prefill_layout(a).n_ent; }
+
+hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out, void *ws,
+                          hipStream_t st) {
+    if (a.n_rows == 0) return hipSuccess;
+    const PrefillLayout L = prefill_layout(a);
+    char *w = (char *)ws;
+    int32_t *counts = (int32_t *)(w + L.off_counts);
+    int32_t *offsets = (int32_t *)(w + L.off_offsets);
+    int32_t *tile_off = (int32_t *)(w + L.off_tile_off);
+    int32_t *local = (int32_t *)(w + L.off_local);
+    int32_t *list = (int32_t *)(w + L.off_list);
+    int2 *tiles = (int2 *)(w + L.off_tiles);
+    float *records = (float *)(w + L.off_records);
+    const int NE = a.k + max_window_spans(a.S, a.W);
+    const int MT = prefill_tile_rows(a);
+
+    hipLaunchKernelGGL(fill_i32, dim3((unsigned)ceil_div(L.n_exp + 1, 256)), dim3(256), 0, st, counts, L.n_exp + 1, 0);
+    hipLaunchKernelGGL(count_kernel, dim3((unsigned)ceil_div(L.n_ent, 256)), dim3(256), 0, st, sel, a.row_seq,
+                       a.row_pos, counts, local, L.n_ent, NE, a.Hq, a.Hkv, a.G, a.S, a.k, a.W, a.B, a.max_pos,
+                       L.span_slots);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, tile_off, L.n_exp, MT);
+    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)ceil_div(L.n_ent, 256)), dim3(256), 0, st, sel, a.row_seq,
+                       a.row_pos, offsets, local, list, L.n_ent, NE, a.Hq, a.Hkv, a.G, a.S, a.k, a.W, a.B, a.max_pos,
+                       L.span_slots);
+    hipLaunchKernelGGL(tiles_kernel, dim3((unsigned)ceil_div(L.n_exp, 256)), dim3(256), 0, st, counts, tile_off, tiles,
+                       L.n_exp, MT);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    TileArgs ta{a, K, V, counts, offsets, tile_off, list, tiles, records, L.n_exp, L.max_tiles, L.span_slots, NE};
+    e = launch_prefill_tiles(ta, st);
+    if (e != hipSuccess) return e;
+    return launch_combine(a, records, sel, out, 1, a.S, st);
+}
+
+}  // namespace ra

@@ -1,0 +1,166 @@
+/*
+ * routed_attn.h -- C ABI of the MI355X (gfx950) content-routed sparse attention library.
+ *
+ * The method (release post "Experimental model with subquadratic attention: 100 tok/s @ 1M
+ * context, 76 tok/s @ 10M context (30B model, single GPU)", section "Key idea"): the key/value
+ * cache of a sequence is cut into spans of S consecutive tokens (about sqrt(L) of them); each
+ * query scores every span, keeps the top-k spans, and runs token-level softmax attention over
+ * the tokens of those spans plus a local window, for O(L^(3/2)) total work.  The post does not
+ * fix the details; this library computes the following, step by step:
+ *
+ *   span summary      mean_j = (fp32 running sum of keys jS .. jS+S-1, in token order) / S
+ *   window            w0(t) = S * floor(max(0, t-W+1) / S);  window = [w0(t), t]
+ *   routable spans    j < r(t) = w0(t) / S   (complete spans wholly before the window)
+ *   score             s_j = q . kappa(mean_j)   (kappa = round-to-nearest-even to bf16 for bf16
+ *                     inputs, identity for fp32; no 1/sqrt(d) factor)
+ *   selection         m = min(k, r(t)) spans by (score descending, span index ascending)
+ *   attention         softmax(q . k_p / sqrt(d)) over p in window U selected spans; O = sum w_p v_p
+ *
+ * Each (token, query head) row routes on its own; query head h uses kv head h / (Hq / Hkv).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument except `cfg`/`rows` (host structs) is DEVICE memory owned by the
+ *    caller.  The library allocates nothing and keeps no state between calls.
+ *  - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
+ *    No call synchronises with the host.
+ *  - Arguments are validated on the host before anything is launched.  On error the call
+ *    returns a non-zero ra_status, records a message (ra_last_error, per thread) and launches
+ *    nothing.  RA_EHIP reports a launch failure; outputs are then undefined.
+ *  - Values that live in device memory (row positions, sequence ids, lengths, selections) are
+ *    trusted but clamped before use, so a wrong value gives a wrong result, never an access
+ *    outside the buffers described here.
+ *
+ * Layouts (all dense, row-major, innermost dimension contiguous)
+ *  - K cache, V cache : [batch][Hkv][capacity][d], dtype of cfg (fp32, or bf16 bit patterns).
+ *  - span_mean        : [batch][Hkv][max_spans][d] float.  Slot j holds the mean of span j once
+ *                       that span is complete; other slots are not read.
+ *  - run_sum          : [batch][Hkv][d] float, fp32 sum of the open span's keys; zero it before
+ *                       the first update of a sequence.
+ *  - q                : [n_rows][Hq][d], dtype of cfg.
+ *  - scores           : [n_rows][Hq][score_stride] float; entry j < r(t) holds s_j.
+ *  - sel              : [n_rows][Hq][k] int32; the m selected span ids ascending, then -1.
+ *  - out              : [n_rows][Hq][d] float.
+ */
+#ifndef ROUTED_ATTN_H
+#define ROUTED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RA_OK = 0,
+    RA_EINVAL = 1,       /* null pointer, inconsistent sizes, out-of-range parameter */
+    RA_EUNSUPPORTED = 2, /* valid but not implemented: head_dim, dtype, top_k, group size */
+    RA_ECAPACITY = 3,    /* a buffer is too small (capacity, max_spans, score_stride, workspace) */
+    RA_EHIP = 4          /* the HIP runtime reported an error when launching */
+} ra_status;
+
+typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+
+typedef enum { RA_OP_DECODE = 0, RA_OP_PREFILL = 1 } ra_op;
+
+/* Shapes and method parameters.  Supported: head_dim in {64, 128}; num_q_heads a multiple of
+ * num_kv_heads with Hq/Hkv <= 32; 1 <= top_k <= 64; span_size >= 1; window >= 1;
+ * max_spans >= floor(capacity / span_size). */
+typedef struct {
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t span_size;
+    int32_t top_k;
+    int32_t window;
+    int32_t dtype;     /* ra_dtype of q, K and V */
+    int32_t batch;     /* sequences in the cache */
+    int64_t capacity;  /* token slots per (sequence, kv head) */
+    int64_t max_spans; /* summary slots per (sequence, kv head) */
+} ra_config;
+
+/* Query rows.  Row i belongs to sequence row_seq[i] and sits at position row_pos[i]; its own
+ * K/V must already be in the cache (decode: the new token; prefill: the whole chunk). */
+typedef struct {
+    const void *q;          /* device [n_rows][Hq][d] */
+    const int32_t *row_seq; /* device [n_rows], each in [0, batch) */
+    const int64_t *row_pos; /* device [n_rows], each in [0, max_pos] */
+    int64_t n_rows;
+    int64_t max_pos; /* host-side upper bound on row_pos (< capacity), sizes grids and checks */
+} ra_rows;
+
+/*
+ * span_summary_update -- append tokens [old_len[b], new_len[b]) of every sequence b to its
+ * span summaries (the span summary of the method; release post, "Key idea").  Keys are added
+ * to the open span's fp32 running sum one token at a time in position order; when a span
+ * completes its mean (sum / S, IEEE division) is written to span_mean and the sum restarts at
+ * zero.  Incremental updates are bit-identical to a single update over the whole range.
+ *   k_cache        device K cache (layout above)
+ *   span_mean      device [batch][Hkv][max_spans][d] float (written)
+ *   run_sum        device [batch][Hkv][d] float (read and written)
+ *   old_len/new_len device int64 [batch]; new_len <= capacity; equal values = no-op
+ *   max_new_tokens host bound on new_len[b] - old_len[b] (used to size the grid; a larger
+ *                  device value leaves the excess spans unprocessed)
+ */
+ra_status span_summary_update(const ra_config *cfg, const void *k_cache, float *span_mean, float *run_sum,
+                              const int64_t *old_len, const int64_t *new_len, int64_t max_new_tokens,
+                              void *stream);
+
+/*
+ * route_scores -- every row scores every routable span of its sequence (release post, "Key
+ * idea": score the O(L^0.5) candidate spans):  scores[row][h][j] = q[row][h] . kappa(mean_j)
+ * for j < r(row_pos[row]); other entries are not written.  bf16 inputs run on bf16 MFMA with
+ * fp32 accumulation; fp32 inputs use fp32 FMA.
+ *   score_stride   floats per (row, head) in `scores`; must be >= r(max_pos).
+ */
+ra_status route_scores(const ra_config *cfg, const ra_rows *rows, const float *span_mean, float *scores,
+                       int64_t score_stride, void *stream);
+
+/*
+ * topk_spans -- per (row, head): keep the m = min(k, r) best routable spans by (score
+ * descending, index ascending), written ascending and padded with -1 (release post, "Key
+ * idea": select the top k).  One 64-lane wavefront per row.
+ */
+ra_status topk_spans(const ra_config *cfg, const ra_rows *rows, const float *scores, int64_t score_stride,
+                     int32_t *sel, void *stream);
+
+/*
+ * routed_attn_decode -- exact softmax attention of each row over its window and its selected
+ * spans (release post, "Key idea": token-level attention inside the chosen spans), tuned for
+ * few rows per sequence: the spans chosen by the query heads that share a kv head are read
+ * once and split into sub-tiles across the GPU, and the partial softmax states are merged in
+ * a second kernel (log-sum-exp, fixed order: results do not depend on scheduling).
+ * Entries of `sel` outside [0, r(t)) are ignored.
+ *   workspace      device scratch of at least ra_workspace_bytes(cfg, RA_OP_DECODE, n_rows,
+ *                  max_pos) bytes; contents on entry do not matter.
+ */
+ra_status routed_attn_decode(const ra_config *cfg, const ra_rows *rows, const void *k_cache, const void *v_cache,
+                             const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
+ * routed_attn_prefill -- the same result for many rows (a chunk of new tokens, causal in the
+ * chunk).  Rows are grouped span by span (every (sequence, kv head, span) gathers the rows
+ * that attend to it, as selected span or as window span), each group runs as dense tiles over
+ * the span's keys, and the per-span partial states are merged per row.
+ *   workspace      at least ra_workspace_bytes(cfg, RA_OP_PREFILL, n_rows, max_pos) bytes.
+ */
+ra_status routed_attn_prefill(const ra_config *cfg, const ra_rows *rows, const void *k_cache, const void *v_cache,
+                              const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* Workspace bytes needed by routed_attn_decode / routed_attn_prefill (op = ra_op); 0 if the
+ * configuration is invalid (ra_last_error then says why). */
+size_t ra_workspace_bytes(const ra_config *cfg, int32_t op, int64_t n_rows, int64_t max_pos);
+
+/* Static description of a status code. */
+const char *ra_status_string(int32_t status);
+
+/* Message of the last non-OK return on the calling thread ("" if none). */
+const char *ra_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROUTED_ATTN_H */

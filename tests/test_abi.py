@@ -1,0 +1,87 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point, and rejects
+invalid arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import content_routed_sparse_amd as ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names += re.findall(r"^(?:ra_status|size_t|const char \*)\s*(\w+)\(", text, flags=re.M)
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(ra.EXPORTED) <= set(names)
+    lib = ra.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def cfg(**kw):
+    base = dict(num_q_heads=32, num_kv_heads=4, head_dim=128, span_size=1024, top_k=16, window=1024,
+                dtype=ra.RA_BF16, batch=1, capacity=1 << 20)
+    base.update(kw)
+    if base["span_size"] < 1:
+        base["max_spans"] = 1
+    return ra.Config(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def rows(n=1, max_pos=(1 << 20) - 1):
+    return ra._Rows(0x1000, 0x1000, 0x1000, n, max_pos)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 2), (dict(num_q_heads=30), 1), (dict(top_k=0), 1), (dict(top_k=65), 2),
+    (dict(span_size=0), 1), (dict(window=0), 1), (dict(dtype=7), 2), (dict(batch=0), 1),
+    (dict(max_spans=3), 3), (dict(num_q_heads=64, num_kv_heads=1), 2),
+])
+def test_config_validation(kw, status):
+    c = cfg(**kw).c()
+    r = rows()
+    lib = ra.lib()
+    assert lib.topk_spans(ctypes.byref(c), ctypes.byref(r), FAKE, 1024, FAKE, None) == status
+    assert lib.ra_last_error().decode() != ""
+
+
+def test_argument_validation_before_launch():
+    lib = ra.lib()
+    c = cfg().c()
+    assert lib.route_scores(None, ctypes.byref(rows()), FAKE, FAKE, 1023, None) == 1
+    # score stride below the routable count at max_pos
+    assert lib.route_scores(ctypes.byref(c), ctypes.byref(rows()), FAKE, FAKE, 1022, None) == 3
+    # max_pos outside the cache
+    assert lib.topk_spans(ctypes.byref(c), ctypes.byref(rows(max_pos=1 << 20)), FAKE, 1023, FAKE, None) == 3
+    # NULL outputs
+    assert lib.routed_attn_decode(ctypes.byref(c), ctypes.byref(rows()), FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
+                                  None) == 1
+    # workspace too small
+    assert lib.routed_attn_prefill(ctypes.byref(c), ctypes.byref(rows(8192)), FAKE, FAKE, FAKE, FAKE, FAKE, 16,
+                                   None) == 3
+    # summary: max_new beyond capacity
+    assert lib.span_summary_update(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, (1 << 20) + 1, None) == 3
+    assert lib.span_summary_update(ctypes.byref(c), None, FAKE, FAKE, FAKE, FAKE, 1, None) == 1
+
+
+def test_workspace_sizes():
+    c = cfg()
+    d = ra.workspace_bytes(c, ra.RA_OP_DECODE, 1, (1 << 20) - 1)
+    # 32 heads x (16 selected + 2 window entries) x 4 sub-tiles x (4 + 128) floats
+    assert d == 32 * 18 * 4 * 132 * 4
+    p = ra.workspace_bytes(cfg(capacity=(1 << 20) + 8192), ra.RA_OP_PREFILL, 8192, (1 << 20) + 8191)
+    assert p > 8192 * 32 * 18 * 132 * 4  # at least the partial records
+    assert ra.lib().ra_workspace_bytes(ctypes.byref(c.c()), 5, 1, 0) == 0
+    assert ra.lib().ra_status_string(3) == b"buffer too small"
