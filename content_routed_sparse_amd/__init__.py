@@ -166,38 +166,103 @@ def _kv_shape(cfg):
     return (cfg.batch, cfg.num_kv_heads, cfg.capacity, cfg.head_dim)
 
 
+# Each entry point is split into an argument builder (validation + marshalling into ctypes
+# values) and the call itself, so that a caller in a tight loop can validate once and replay the
+# prepared call (see `prepare`).
+
+def _args_span_summary_update(cfg, k_cache, span_mean, run_sum, old_len, new_len, max_new_tokens, stream=None):
+    c = cfg.c()
+    return (ctypes.byref(c), _dev(k_cache, cfg.torch_dtype, _kv_shape(cfg), "k_cache"),
+            _dev(span_mean, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.max_spans, cfg.head_dim), "span_mean"),
+            _dev(run_sum, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.head_dim), "run_sum"),
+            _dev(old_len, torch.int64, (cfg.batch,), "old_len"), _dev(new_len, torch.int64, (cfg.batch,), "new_len"),
+            int(max_new_tokens), _stream(stream)), (c,)
+
+
+def _scores_shape_check(cfg, rows, scores):
+    n = rows.q.shape[0]
+    if scores.dim() != 3 or tuple(scores.shape[:2]) != (n, cfg.num_q_heads):
+        raise ValueError("scores must have shape [n_rows, Hq, stride]")
+
+
+def _args_route_scores(cfg, rows, span_mean, scores, stream=None):
+    c, r = cfg.c(), _rows(cfg, rows)
+    _scores_shape_check(cfg, rows, scores)
+    return (ctypes.byref(c), ctypes.byref(r),
+            _dev(span_mean, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.max_spans, cfg.head_dim), "span_mean"),
+            _dev(scores, torch.float32, None, "scores"), scores.shape[2], _stream(stream)), (c, r)
+
+
+def _args_topk_spans(cfg, rows, scores, sel, stream=None):
+    c, r = cfg.c(), _rows(cfg, rows)
+    _scores_shape_check(cfg, rows, scores)
+    n = rows.q.shape[0]
+    return (ctypes.byref(c), ctypes.byref(r), _dev(scores, torch.float32, None, "scores"), scores.shape[2],
+            _dev(sel, torch.int32, (n, cfg.num_q_heads, cfg.top_k), "sel"), _stream(stream)), (c, r)
+
+
+def _args_attn(cfg, rows, k_cache, v_cache, sel, out, workspace, stream=None):
+    c, r = cfg.c(), _rows(cfg, rows)
+    n = rows.q.shape[0]
+    return (ctypes.byref(c), ctypes.byref(r), _dev(k_cache, cfg.torch_dtype, _kv_shape(cfg), "k_cache"),
+            _dev(v_cache, cfg.torch_dtype, _kv_shape(cfg), "v_cache"),
+            _dev(sel, torch.int32, (n, cfg.num_q_heads, cfg.top_k), "sel"),
+            _dev(out, torch.float32, (n, cfg.num_q_heads, cfg.head_dim), "out"),
+            _dev(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream)), (c, r)
+
+
+_BUILDERS = {
+    "span_summary_update": _args_span_summary_update,
+    "route_scores": _args_route_scores,
+    "topk_spans": _args_topk_spans,
+    "routed_attn_decode": _args_attn,
+    "routed_attn_prefill": _args_attn,
+}
+
+
+class Prepared:
+    """A validated call of one entry point with fixed arguments; calling it launches again.
+
+    The tensors given at preparation are the ones used by every call; the caller keeps them
+    alive and unchanged in shape.  With stream=None the call goes to torch's current stream at
+    call time (so a prepared call can be captured into a graph); otherwise to the given stream.
+    """
+
+    def __init__(self, name, *args, stream=None):
+        self.fn = getattr(lib(), name)
+        self.args, self._keep = _BUILDERS[name](*args, stream=stream)
+        self._tensors = args
+        self.dynamic_stream = stream is None
+        self._head = self.args[:-1]
+
+    def __call__(self):
+        if self.dynamic_stream:
+            _check(self.fn(*self._head, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+        else:
+            _check(self.fn(*self.args))
+
+
+def prepare(name, *args, stream=None):
+    return Prepared(name, *args, stream=stream)
+
+
 def span_summary_update(cfg, k_cache, span_mean, run_sum, old_len, new_len, max_new_tokens, stream=None):
     """Append tokens [old_len[b], new_len[b]) of each sequence to its span summaries."""
-    c = cfg.c()
-    _check(lib().span_summary_update(
-        ctypes.byref(c), _dev(k_cache, cfg.torch_dtype, _kv_shape(cfg), "k_cache"),
-        _dev(span_mean, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.max_spans, cfg.head_dim), "span_mean"),
-        _dev(run_sum, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.head_dim), "run_sum"),
-        _dev(old_len, torch.int64, (cfg.batch,), "old_len"), _dev(new_len, torch.int64, (cfg.batch,), "new_len"),
-        int(max_new_tokens), _stream(stream)))
+    args, _keep = _args_span_summary_update(cfg, k_cache, span_mean, run_sum, old_len, new_len, max_new_tokens,
+                                            stream)
+    _check(lib().span_summary_update(*args))
 
 
 def route_scores(cfg, rows, span_mean, scores, stream=None):
     """scores[row][h][j] = q . kappa(mean_j) for every routable span j of the row."""
-    c, r = cfg.c(), _rows(cfg, rows)
-    n = rows.q.shape[0]
-    if scores.dim() != 3 or scores.shape[:2] != (n, cfg.num_q_heads):
-        raise ValueError("scores must have shape [n_rows, Hq, stride]")
-    _check(lib().route_scores(
-        ctypes.byref(c), ctypes.byref(r),
-        _dev(span_mean, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.max_spans, cfg.head_dim), "span_mean"),
-        _dev(scores, torch.float32, None, "scores"), scores.shape[2], _stream(stream)))
+    args, _keep = _args_route_scores(cfg, rows, span_mean, scores, stream)
+    _check(lib().route_scores(*args))
 
 
 def topk_spans(cfg, rows, scores, sel, stream=None):
     """sel[row][h] = the row's top-k routable spans, ascending, padded with -1."""
-    c, r = cfg.c(), _rows(cfg, rows)
-    n = rows.q.shape[0]
-    if scores.dim() != 3 or scores.shape[:2] != (n, cfg.num_q_heads):
-        raise ValueError("scores must have shape [n_rows, Hq, stride]")
-    _check(lib().topk_spans(ctypes.byref(c), ctypes.byref(r), _dev(scores, torch.float32, None, "scores"),
-                            scores.shape[2], _dev(sel, torch.int32, (n, cfg.num_q_heads, cfg.top_k), "sel"),
-                            _stream(stream)))
+    args, _keep = _args_topk_spans(cfg, rows, scores, sel, stream)
+    _check(lib().topk_spans(*args))
 
 
 def workspace_bytes(cfg, op, n_rows, max_pos):
@@ -208,24 +273,16 @@ def workspace_bytes(cfg, op, n_rows, max_pos):
     return n
 
 
-def _attn(fn, cfg, rows, k_cache, v_cache, sel, out, workspace, stream):
-    c, r = cfg.c(), _rows(cfg, rows)
-    n = rows.q.shape[0]
-    _check(fn(ctypes.byref(c), ctypes.byref(r), _dev(k_cache, cfg.torch_dtype, _kv_shape(cfg), "k_cache"),
-              _dev(v_cache, cfg.torch_dtype, _kv_shape(cfg), "v_cache"),
-              _dev(sel, torch.int32, (n, cfg.num_q_heads, cfg.top_k), "sel"),
-              _dev(out, torch.float32, (n, cfg.num_q_heads, cfg.head_dim), "out"),
-              _dev(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream)))
-
-
 def routed_attn_decode(cfg, rows, k_cache, v_cache, sel, out, workspace, stream=None):
     """Exact attention over window + selected spans, split-K over span sub-tiles (few rows)."""
-    _attn(lib().routed_attn_decode, cfg, rows, k_cache, v_cache, sel, out, workspace, stream)
+    args, _keep = _args_attn(cfg, rows, k_cache, v_cache, sel, out, workspace, stream)
+    _check(lib().routed_attn_decode(*args))
 
 
 def routed_attn_prefill(cfg, rows, k_cache, v_cache, sel, out, workspace, stream=None):
     """Exact attention over window + selected spans, rows grouped span by span (many rows)."""
-    _attn(lib().routed_attn_prefill, cfg, rows, k_cache, v_cache, sel, out, workspace, stream)
+    args, _keep = _args_attn(cfg, rows, k_cache, v_cache, sel, out, workspace, stream)
+    _check(lib().routed_attn_prefill(*args))
 
 
 class Pipeline:

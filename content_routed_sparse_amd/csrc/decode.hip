@@ -5,26 +5,38 @@
 // Work unit = (row, kv head, slot, sub-tile).  Slots are the G*k (query head, selection entry)
 // pairs of the kv head, then the window spans.  A span chosen by several query heads of the
 // kv head is read once: only the unit of the lowest head that chose it (its "owner") runs, and
-// it computes the partial state for every head that chose the span (GQA sharing).  Spans are
-// cut into sub-tiles of 4 x KPW keys so that ~2000 independent units keep all 256 CUs busy.
+// it computes the partial state for every head that chose the span (GQA sharing).  The kv
+// head's G*k selection entries are loaded into registers together with the row's position in
+// one round trip; the unit's span, its ownership and the list of heads sharing it then come
+// from register reads and wave ballots, so the K/V stream starts after a single dependent load
+// and no block-wide barrier.  Spans are cut into sub-tiles of 4 x KPW keys so that ~2000
+// independent units keep all 256 CUs busy.
+//
 // Inside a unit each wave streams KPW keys straight from HBM into registers with 16-byte loads
-// (LPR consecutive lanes cover one key row, so every load instruction reads whole rows), then
-// per head: dot products reduced over the LPR lanes, an online-softmax partial per wave, the
-// P.V product, and a 4-wave merge through LDS.  The partial states (m, l, o[d]) are written to
-// the workspace and merged per row in `combine_kernel` in a fixed order.
+// (LPR consecutive lanes cover one key row, so every load instruction reads whole rows); all K
+// and V loads are issued before any arithmetic.  Per head: per-lane partial dot products, a
+// butterfly reduce-scatter over the LPR lanes on DPP (each lane ends with one key's score), one
+// exp2 per lane, the probabilities broadcast through LDS, P.V in fp32, a reduce-scatter over
+// the row groups, and a 4-wave merge through LDS.  Partial states (m, l, o[d]) go to the
+// workspace; the combine kernel merges them per row in a fixed order.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
+#include "wave_ops.h"
 
 namespace ra {
 
-template <typename T, int D>
+template <typename T, int D, int NWAVE, int KPW_>
 struct Lanes {
     static constexpr int EPL = 16 / sizeof(T);          // elements per 16-byte load
     static constexpr int LPR = D / EPL;                 // lanes per key row
     static constexpr int RPI = 64 / LPR;                // key rows per load instruction
-    static constexpr int KPW = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // keys per wave
-    static constexpr int STEPS = KPW / RPI;
-    static constexpr int TK = 4 * KPW;                  // keys per unit (4 waves)
+    static constexpr int KPW = KPW_;                    // keys per wave
+    static constexpr int STEPS = KPW / RPI;             // load instructions per wave (K or V)
+    static constexpr int DUP = LPR / STEPS;             // lanes holding the same key's score
+    static constexpr int TK = NWAVE * KPW;              // keys per unit
 };
 
 __device__ __forceinline__ void unpack16(const uint4 &raw, float *f, uint16_t) {
@@ -45,21 +57,21 @@ __device__ __forceinline__ void unpack16(const uint4 &raw, float *f, float) {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kSelRegChunks = 4;  // selection entries of a kv head kept in registers: G*k <= 256
 
-template <typename T, int D>
-__global__ void __launch_bounds__(256) decode_attn(const T *__restrict__ q, const int32_t *__restrict__ row_seq,
-                                                   const int64_t *__restrict__ row_pos, const T *__restrict__ K,
-                                                   const T *__restrict__ V, const int32_t *__restrict__ sel,
-                                                   float *__restrict__ part, int Hq, int Hkv, int G, int S, int k,
-                                                   int W, int B, int64_t cap, int64_t max_pos, int n_slots, int NW,
-                                                   int nsub, float scale_log2) {
-    using L = Lanes<T, D>;
+template <typename T, int D, int NWAVE, int KPW_>
+__global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ q, const int32_t *__restrict__ row_seq,
+                                                   const int64_t *__restrict__ row_pos, const T *K, const T *V,
+                                                   const int32_t *__restrict__ sel, float *__restrict__ part, int Hq,
+                                                   int Hkv, int G, int S, int k, int W, int B, int64_t cap,
+                                                   int64_t max_pos, int n_slots, int NW, int nsub, float scale_log2) {
+    using L = Lanes<T, D, NWAVE, KPW_>;
     constexpr int EPL = L::EPL, LPR = L::LPR, RPI = L::RPI, KPW = L::KPW, STEPS = L::STEPS, TK = L::TK;
-    __shared__ int sel_s[32 * 64];
-    __shared__ int head_entry[32];
-    __shared__ int not_owner;
-    __shared__ float wm[4], wl[4];
-    __shared__ float wo[4][D];
+    constexpr int DUP = L::DUP;
+    __shared__ float pbuf[NWAVE][64];
+    __shared__ int match_s[NWAVE][32];
+    __shared__ float wm[NWAVE], wl[NWAVE];
+    __shared__ float wo[NWAVE][D];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sub = blockIdx.x % nsub;
@@ -68,25 +80,50 @@ __global__ void __launch_bounds__(256) decode_attn(const T *__restrict__ q, cons
     rest /= n_slots;
     const int g = (int)(rest % Hkv);
     const int64_t row = rest / Hkv;
+    const int Gk = G * k;
+    const bool is_window = slot >= Gk;
+    const int32_t *sel_rg = sel + (row * Hq + (int64_t)g * G) * k;
 
-    int64_t t = row_pos[row];
-    t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
-    int seq = row_seq[row];
-    seq = seq < 0 ? 0 : (seq >= B ? B - 1 : seq);
+    // one round trip: the row's position and sequence, and the kv head's selection entries
+    const int64_t t_raw = row_pos[row];
+    const int seq_raw = row_seq[row];
+    int32_t selv[kSelRegChunks];
+    const bool sel_in_regs = Gk <= 64 * kSelRegChunks;
+    if (!is_window && sel_in_regs) {
+        // unconditional loads from clamped indices, masked afterwards (no per-chunk round trips)
+#pragma unroll
+        for (int cc = 0; cc < kSelRegChunks; ++cc) {
+            const int x = cc * 64 + lane;
+            selv[cc] = sel_rg[x < Gk ? x : Gk - 1];
+        }
+#pragma unroll
+        for (int cc = 0; cc < kSelRegChunks; ++cc) selv[cc] = cc * 64 + lane < Gk ? selv[cc] : -1;
+    } else {
+#pragma unroll
+        for (int cc = 0; cc < kSelRegChunks; ++cc) selv[cc] = -1;
+    }
+    asm volatile("" ::: "memory");  // all of the above are in flight together
+    asm volatile("" ::"s"(t_raw), "s"(seq_raw));  // (and the scalar ones are not deferred)
+    int64_t t = t_raw < 0 ? 0 : (t_raw > max_pos ? max_pos : t_raw);
+    const int seq = seq_raw < 0 ? 0 : (seq_raw >= B ? B - 1 : seq_raw);
     const int64_t w0 = window_start(t, S, W);
     const int64_t r = w0 / S;
     const int NE = k + NW;  // entries per row-head in the workspace
-    const int32_t *sel_rg = sel + (row * Hq + (int64_t)g * G) * k;
 
     int64_t j, lo, hi;
-    const bool is_window = slot >= G * k;
     if (!is_window) {
-        j = sel_rg[slot];  // (head slot / k, entry slot % k)
+        if (sel_in_regs) {
+            const int cc = slot >> 6;
+            const int32_t v = cc == 0 ? selv[0] : cc == 1 ? selv[1] : cc == 2 ? selv[2] : selv[3];
+            j = __builtin_amdgcn_readlane(v, slot & 63);
+        } else {
+            j = sel_rg[slot];
+        }
         if (j < 0 || j >= r) return;
         lo = j * S;
         hi = lo + S;
     } else {
-        j = w0 / S + (slot - G * k);
+        j = w0 / S + (slot - Gk);
         lo = j * S;
         if (lo > t) return;
         hi = lo + S < t + 1 ? lo + S : t + 1;
@@ -95,35 +132,63 @@ __global__ void __launch_bounds__(256) decode_attn(const T *__restrict__ q, cons
     if (ulo >= hi) return;
     const int64_t uhi = ulo + TK < hi ? ulo + TK : hi;
 
-    // heads of this kv head that attend to span j, and the unit's ownership
-    if (tid < G) head_entry[tid] = is_window ? k + (slot - G * k) : -1;
-    if (tid == 0) not_owner = 0;
-    if (!is_window)
-        for (int x = tid; x < G * k; x += 256) sel_s[x] = sel_rg[x];
-    __syncthreads();
+    // heads to process.  Window: all G heads (entry k + w).  Span: every head whose selection
+    // contains j, in selection order (entry = its position in that head's list); the unit runs
+    // only if the first of them is its own head.
+    int nmatch;
     if (!is_window) {
-        const int my_head = slot / k;
-        for (int x = tid; x < G * k; x += 256) {
-            if (sel_s[x] == j) {
-                head_entry[x / k] = x % k;
-                if (x / k < my_head) not_owner = 1;
+        nmatch = 0;
+        if (sel_in_regs) {
+#pragma unroll
+            for (int cc = 0; cc < kSelRegChunks; ++cc) {
+                const bool eq = selv[cc] == (int32_t)j;
+                const uint64_t bal = __ballot(eq);
+                if (eq) {
+                    const int idx = nmatch + (int)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
+                    if (idx < 32) match_s[wave][idx] = cc * 64 + lane;
+                }
+                nmatch += (int)__builtin_popcountll(bal);
+            }
+        } else {
+            for (int base = 0; base < Gk; base += 64) {
+                const int x = base + lane;
+                const bool eq = x < Gk && sel_rg[x] == j;
+                const uint64_t bal = __ballot(eq);
+                if (eq) {
+                    const int idx = nmatch + (int)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
+                    if (idx < 32) match_s[wave][idx] = x;
+                }
+                nmatch += (int)__builtin_popcountll(bal);
             }
         }
-        __syncthreads();
-        if (not_owner) return;
+        if (nmatch > G) nmatch = G;  // at most one entry per head in a valid selection
+        __builtin_amdgcn_wave_barrier();
+        if (match_s[wave][0] / k != slot / k) return;  // uniform: a lower head's unit owns the span
+    } else {
+        nmatch = G;
     }
-
-    // stream this wave's KPW keys into registers
+    auto match_head = [&](int mi, int &entry) {
+        if (is_window) {
+            entry = k + (slot - Gk);
+            return mi;
+        }
+        const int x = match_s[wave][mi];
+        entry = x % k;
+        return x / k;
+    };
     const int c = lane % LPR, rr = lane / LPR;
+    int entry0;
+    const int h0 = match_head(0, entry0);
+    uint4 qraw = *reinterpret_cast<const uint4 *>(q + (row * Hq + g * G + h0) * D + c * EPL);
+
+    // stream this wave's keys: all K and V loads are issued before any use
     const int64_t kv_base = ((int64_t)seq * Hkv + g) * cap;
     const int64_t wkey0 = ulo + (int64_t)wave * KPW;
     uint4 kr[STEPS], vr[STEPS];
-    bool valid[STEPS];
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
         const int64_t key = wkey0 + s * RPI + rr;
-        valid[s] = key < uhi;
-        const int64_t kl = valid[s] ? key : uhi - 1;  // in-bounds, finite row for masked keys
+        const int64_t kl = key < uhi ? key : uhi - 1;  // in-bounds, finite row for masked keys
         kr[s] = *reinterpret_cast<const uint4 *>(K + (kv_base + kl) * D + c * EPL);
     }
 #pragma unroll
@@ -132,64 +197,71 @@ __global__ void __launch_bounds__(256) decode_attn(const T *__restrict__ q, cons
         const int64_t kl = key < uhi ? key : uhi - 1;
         vr[s] = *reinterpret_cast<const uint4 *>(V + (kv_base + kl) * D + c * EPL);
     }
+    asm volatile("" ::: "memory");  // keep the loads here: nothing may sink them into the head loop
 
-    for (int h = 0; h < G; ++h) {
-        const int entry = head_entry[h];
-        if (entry < 0) continue;  // uniform across the block
+    // the key whose score this lane holds after the reduce-scatter
+    const int s_own = c / DUP;
+    const bool own_valid = wkey0 + s_own * RPI + rr < uhi;
+    const bool counts = (c % DUP) == 0;  // one lane per key contributes to the sum
+
+    for (int mi = 0; mi < nmatch; ++mi) {
+        int entry;
+        const int h = match_head(mi, entry);
         const int hq = g * G + h;
+        // the packed K/V registers are "redefined" here, so the compiler cannot hoist their
+        // widening out of the head loop (that would hold 2x the registers and stall the loads)
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) asm volatile("" : "+v"(kr[s].x), "+v"(kr[s].y), "+v"(kr[s].z), "+v"(kr[s].w));
+        if (mi > 0) qraw = *reinterpret_cast<const uint4 *>(q + (row * Hq + hq) * D + c * EPL);
         float qf[EPL];
-        unpack16(*reinterpret_cast<const uint4 *>(q + (row * Hq + hq) * D + c * EPL), qf, T());
-        float z[STEPS];
-        float mloc = kNegInf;
+        unpack16(qraw, qf, T());
+        float acc[STEPS];
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
             float kf[EPL];
             unpack16(kr[s], kf, T());
-            float acc = 0.f;
+            float a = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc = fmaf(qf[e], kf[e], acc);
-#pragma unroll
-            for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-            z[s] = valid[s] ? acc * scale_log2 : kNegInf;
-            mloc = fmaxf(mloc, z[s]);
+            for (int e = 0; e < EPL; ++e) a = fmaf(qf[e], kf[e], a);
+            acc[s] = a;
         }
+        ReduceScatter<STEPS, ilog2(STEPS), LPR / 2>::run(acc, lane);
+        const float sc = allreduce_sum<DUP / 2>(acc[0]);
+        const float z = own_valid ? sc * scale_log2 : kNegInf;
+        const float m = wave_max(z);
+        const float p = (own_valid && m != kNegInf) ? exp2f(z - m) : 0.f;
+        const float ls = wave_sum(counts ? p : 0.f);
+        pbuf[wave][lane] = p;
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
-        float lsum = 0.f;
+        for (int s = 0; s < STEPS; ++s) asm volatile("" : "+v"(vr[s].x), "+v"(vr[s].y), "+v"(vr[s].z), "+v"(vr[s].w));
         float o[EPL];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-        if (mloc != kNegInf) {
 #pragma unroll
-            for (int s = 0; s < STEPS; ++s) {
-                const float p = valid[s] ? exp2f(z[s] - mloc) : 0.f;
-                lsum += p;
-                float vf[EPL];
-                unpack16(vr[s], vf, T());
+        for (int s = 0; s < STEPS; ++s) {
+            const float ps = pbuf[wave][rr * LPR + s * DUP];
+            float vf[EPL];
+            unpack16(vr[s], vf, T());
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vf[e], o[e]);
-            }
+            for (int e = 0; e < EPL; ++e) o[e] = fmaf(ps, vf[e], o[e]);
         }
-#pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) {
-            lsum += __shfl_xor(lsum, off);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) o[e] += __shfl_xor(o[e], off);
-        }
+        ReduceScatter<EPL, ilog2(RPI), 32>::run(o, lane);  // over the row groups: EPL -> EPL / RPI values
+        constexpr int KEEP = EPL / RPI;
         if (lane == 0) {
-            wm[wave] = mloc;
-            wl[wave] = lsum;
+            wm[wave] = m;
+            wl[wave] = ls;
         }
-        if (rr == 0) {
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) wo[wave][c * EPL + e] = o[e];
-        }
+        for (int i = 0; i < KEEP; ++i) wo[wave][c * EPL + rr * KEEP + i] = o[i];
         __syncthreads();
         if (tid < D) {
-            float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+            float M = wm[0];
+#pragma unroll
+            for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, wm[w]);
             float Lsum = 0.f, O = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < NWAVE; ++w) {
                 if (wm[w] != kNegInf) {
                     const float f = exp2f(wm[w] - M);
                     Lsum = fmaf(wl[w], f, Lsum);
@@ -207,15 +279,128 @@ __global__ void __launch_bounds__(256) decode_attn(const T *__restrict__ q, cons
     }
 }
 
-}  // namespace
+// Records of one row-head: entry e < k is selected span sel[e] (skipped unless 0 <= j < r),
+// entry k + w is window span w0/S + w (skipped once it starts after t); each covers its keys in
+// sub-tiles of TK.  Returns false for records that were not produced.
+__device__ __forceinline__ bool record_valid(const int32_t *sel_rh, int e, int sub, int64_t t, int64_t w0, int S,
+                                             int k, int TK) {
+    int64_t lo, hi;
+    if (e < k) {
+        const int64_t j = sel_rh[e];
+        if (j < 0 || j >= w0 / S) return false;
+        lo = j * S;
+        hi = lo + S;
+    } else {
+        lo = w0 + (int64_t)(e - k) * S;
+        if (lo > t) return false;
+        hi = lo + S < t + 1 ? lo + S : t + 1;
+    }
+    return lo + (int64_t)sub * TK < hi;
+}
 
-// Merge of the partial states of one row-head, in fixed order: selected entries ascending by
-// entry index, then window spans, each over its sub-tiles.  One wave per row-head.
+// Loads the output slices of B records (x0, x0 + stride, ...; indices clamped into range) and
+// pins them: every load of the batch is issued before the first use, so a batch costs one
+// memory round trip.  (Left alone, the compiler turns a load whose value is used only under a
+// condition into a conditional load and waits for each one separately.)
+template <int B, int PER, int D>
+__device__ __forceinline__ void load_record_batch(const float *base, int x0, int stride, int nrec, int lane,
+                                                  float (&v)[B][PER]) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        int x = x0 + stride * b;
+        x = x < nrec ? x : nrec - 1;
+        const float *rec = base + (int64_t)x * record_floats(D);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[b][i] = rec[4 + lane + 64 * i];
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(v[b][i]));
+}
+
+constexpr int kRecBatch = 8;
+
+// Merge for few row-heads with many records: one block per row-head, three dependent rounds
+// of loads: (1) the row's position and its k selections into LDS; (2) every thread reads (m, l)
+// of its records into LDS and the block takes the maximum; (3) wave w sums the weighted
+// outputs of records w, w+4, ... (independent loads), and the 4 waves merge in fixed order.
+constexpr int kCombineMaxRec = 1024;
+
 template <int D>
-__global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ part, const int32_t *__restrict__ sel,
-                                                      const int64_t *__restrict__ row_pos, float *__restrict__ out,
-                                                      int64_t n_rowheads, int Hq, int S, int k, int W,
-                                                      int64_t max_pos, int NW, int nsub, int TK) {
+__global__ void __launch_bounds__(256) combine_block(const float *__restrict__ part, const int32_t *__restrict__ sel,
+                                                     const int64_t *__restrict__ row_pos, float *__restrict__ out,
+                                                     int Hq, int S, int k, int W, int64_t max_pos, int NW, int nsub,
+                                                     int TK) {
+    constexpr int PER = D / 64;
+    __shared__ int32_t sel_s[64];
+    __shared__ float mrec[kCombineMaxRec], lrec[kCombineMaxRec];
+    __shared__ float red[4];
+    __shared__ float wsum[4], wout[4][D];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t rh = blockIdx.x;
+    int64_t t = row_pos[rh / Hq];
+    t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
+    const int64_t w0 = window_start(t, S, W);
+    const int NE = k + NW;
+    const int nrec = NE * nsub < kCombineMaxRec ? NE * nsub : kCombineMaxRec;  // host guarantees NE*nsub fits
+    if (tid < k) sel_s[tid] = sel[rh * k + tid];
+    const float *base = part + rh * (int64_t)(NE * nsub) * record_floats(D);
+    __syncthreads();
+
+    float mx = kNegInf;
+    for (int x = tid; x < nrec; x += 256) {
+        const float2 ml = *reinterpret_cast<const float2 *>(base + (int64_t)x * record_floats(D));
+        const bool ok = record_valid(sel_s, x / nsub, x % nsub, t, w0, S, k, TK);
+        const float m = ok ? ml.x : kNegInf, l = ok ? ml.y : 0.f;
+        mrec[x] = m;
+        lrec[x] = l;
+        mx = fmaxf(mx, m);
+    }
+    mx = wave_max(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+    float l = 0.f, o[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] = 0.f;
+    // records not produced hold stale bytes: their slices are loaded with the others and their
+    // contribution is discarded by a select
+    for (int x0 = wave; x0 < nrec; x0 += 4 * kRecBatch) {
+        float v[kRecBatch][PER];
+        load_record_batch<kRecBatch, PER, D>(base, x0, 4, nrec, lane, v);
+#pragma unroll
+        for (int b = 0; b < kRecBatch; ++b) {
+            const int x = x0 + 4 * b;
+            if (x >= nrec) break;
+            const float m = mrec[x];
+            const bool ok = m != kNegInf;
+            const float f = ok ? exp2f(m - M) : 0.f;
+            l = ok ? fmaf(lrec[x], f, l) : l;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) o[i] = ok ? fmaf(v[b][i], f, o[i]) : o[i];
+        }
+    }
+    if (lane == 0) wsum[wave] = l;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) wout[wave][lane + 64 * i] = o[i];
+    __syncthreads();
+    if (tid < D) {
+        const float Lt = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+        const float Ot = (wout[0][tid] + wout[1][tid]) + (wout[2][tid] + wout[3][tid]);
+        out[rh * D + tid] = Lt > 0.f ? Ot / Lt : 0.f;
+    }
+}
+
+// Merge for many row-heads with few records (prefill): one wave per row-head; lane x reads the
+// maximum of record x, then the records are summed in entry order with their weights.
+template <int D>
+__global__ void __launch_bounds__(256) combine_wave(const float *__restrict__ part, const int32_t *__restrict__ sel,
+                                                    const int64_t *__restrict__ row_pos, float *__restrict__ out,
+                                                    int64_t n_rowheads, int Hq, int S, int k, int W, int64_t max_pos,
+                                                    int NW, int nsub, int TK) {
     constexpr int PER = D / 64;
     const int lane = threadIdx.x & 63;
     const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -223,74 +408,130 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
     int64_t t = row_pos[rh / Hq];
     t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
     const int64_t w0 = window_start(t, S, W);
-    const int64_t r = w0 / S;
     const int NE = k + NW;
-    float M = kNegInf, Lsum = 0.f, O[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) O[i] = 0.f;
-    auto merge = [&](int entry, int64_t lo, int64_t hi) {
-        for (int sub = 0; sub < nsub && lo + (int64_t)sub * TK < hi; ++sub) {
-            const float *rec = part + ((rh * NE + entry) * (int64_t)nsub + sub) * record_floats(D);
-            const float m = rec[0], l = rec[1];
-            if (m == kNegInf) continue;
-            const float Mn = fmaxf(M, m);
-            const float a = (M == kNegInf) ? 0.f : exp2f(M - Mn);
-            const float b = exp2f(m - Mn);
-            Lsum = Lsum * a + l * b;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) O[i] = O[i] * a + rec[4 + lane + 64 * i] * b;
-            M = Mn;
+    const int nrec = NE * nsub;
+    const int32_t *sel_rh = sel + rh * k;
+    const float *base = part + rh * (int64_t)nrec * record_floats(D);
+
+    // lane x holds record x's (m, l) (one round trip for up to 64 records); invalid -> m = -inf
+    float M = kNegInf;
+    float mine_m = kNegInf, mine_l = 0.f;
+    for (int x0 = 0; x0 < nrec; x0 += 64) {
+        const int x = x0 + lane;
+        const int xc = x < nrec ? x : nrec - 1;
+        const float2 ml = *reinterpret_cast<const float2 *>(base + (int64_t)xc * record_floats(D));
+        const bool ok = x < nrec && record_valid(sel_rh, x / nsub, x % nsub, t, w0, S, k, TK);
+        const float m = ok ? ml.x : kNegInf;
+        if (x0 == 0) {
+            mine_m = m;
+            mine_l = ok ? ml.y : 0.f;
         }
-    };
-    for (int e = 0; e < k; ++e) {
-        const int64_t j = sel[rh * k + e];
-        if (j < 0 || j >= r) continue;
-        merge(e, j * S, j * S + S);
+        M = fmaxf(M, wave_max(m));
     }
-    for (int w = 0; w < NW; ++w) {
-        const int64_t lo = w0 + (int64_t)w * S;
-        if (lo > t) break;
-        const int64_t hi = lo + S < t + 1 ? lo + S : t + 1;
-        merge(k + w, lo, hi);
-    }
-    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    float l = 0.f, o[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) out[rh * D + lane + 64 * i] = O[i] * inv;
+    for (int i = 0; i < PER; ++i) o[i] = 0.f;
+    for (int x0 = 0; x0 < nrec; x0 += kRecBatch) {
+        float v[kRecBatch][PER];
+        load_record_batch<kRecBatch, PER, D>(base, x0, 1, nrec, lane, v);
+#pragma unroll
+        for (int b = 0; b < kRecBatch; ++b) {
+            const int x = x0 + b;
+            if (x >= nrec) break;
+            float m, lx;
+            if (x < 64) {
+                m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine_m), x));
+                lx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine_l), x));
+            } else {
+                const bool okx = record_valid(sel_rh, x / nsub, x % nsub, t, w0, S, k, TK);
+                const float2 ml = *reinterpret_cast<const float2 *>(base + (int64_t)x * record_floats(D));
+                m = okx ? ml.x : kNegInf;
+                lx = ml.y;
+            }
+            const bool ok = m != kNegInf;
+            const float f = ok ? exp2f(m - M) : 0.f;
+            l = ok ? fmaf(lx, f, l) : l;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) o[i] = ok ? fmaf(v[b][i], f, o[i]) : o[i];
+        }
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) out[rh * D + lane + 64 * i] = o[i] * inv;
 }
+
+}  // namespace
 
 hipError_t launch_combine(const RowArgs &a, const float *part, const int32_t *sel, float *out, int nsub, int TK,
                           hipStream_t st) {
     const int64_t n = a.n_rows * a.Hq;
     const int NW = max_window_spans(a.S, a.W);
-    auto kern = a.d == 64 ? combine_kernel<64> : combine_kernel<128>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(n, 4)), dim3(256), 0, st, part, sel, a.row_pos, out, n, a.Hq, a.S,
-                       a.k, a.W, a.max_pos, NW, nsub, TK);
+    if (n <= 4096 && (a.k + NW) * nsub <= kCombineMaxRec) {
+        auto kern = a.d == 64 ? combine_block<64> : combine_block<128>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)n), dim3(256), 0, st, part, sel, a.row_pos, out, a.Hq, a.S, a.k, a.W,
+                           a.max_pos, NW, nsub, TK);
+    } else {
+        auto kern = a.d == 64 ? combine_wave<64> : combine_wave<128>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(n, 4)), dim3(256), 0, st, part, sel, a.row_pos, out, n, a.Hq,
+                           a.S, a.k, a.W, a.max_pos, NW, nsub, TK);
+    }
     return hipGetLastError();
 }
 
 namespace {
-template <typename T, int D>
-int decode_tk() { return Lanes<T, D>::TK; }
 
-int decode_sub_tile(const RowArgs &a) {
-    if (a.dtype == RA_BF16) return a.d == 64 ? decode_tk<uint16_t, 64>() : decode_tk<uint16_t, 128>();
-    return a.d == 64 ? decode_tk<float, 64>() : decode_tk<float, 128>();
+// Unit shape: waves per block and keys per wave (tuning experiment: RA_DECODE_SHAPE=WxK).
+struct DecodeShape {
+    int nwave, kpw;
+};
+
+DecodeShape decode_shape(const RowArgs &a) {
+    DecodeShape s{4, (a.dtype == RA_F32 && a.d == 128) ? 32 : 64};
+    if (a.dtype == RA_BF16 && a.d == 128) {
+        if (const char *e = getenv("RA_DECODE_SHAPE")) {
+            int w = 0, kk = 0;
+            if (sscanf(e, "%dx%d", &w, &kk) == 2) s = DecodeShape{w, kk};
+        }
+    }
+    return s;
 }
 
-template <typename T, int D>
-hipError_t decode_launch(const RowArgs &a, const void *K, const void *V, const int32_t *sel, void *ws,
-                         hipStream_t st) {
-    using L = Lanes<T, D>;
+template <typename T, int D, int NWAVE, int KPW>
+hipError_t decode_launch_t(const RowArgs &a, const void *K, const void *V, const int32_t *sel, void *ws,
+                           hipStream_t st) {
+    using L = Lanes<T, D, NWAVE, KPW>;
     const int NW = max_window_spans(a.S, a.W);
     const int n_slots = a.G * a.k + NW;
     const int nsub = (int)ceil_div(a.S, L::TK);
     const int64_t blocks = a.n_rows * a.Hkv * n_slots * nsub;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    hipLaunchKernelGGL((decode_attn<T, D>), dim3((unsigned)blocks), dim3(256), 0, st, (const T *)a.q, a.row_seq,
-                       a.row_pos, (const T *)K, (const T *)V, sel, (float *)ws, a.Hq, a.Hkv, a.G, a.S, a.k, a.W, a.B,
-                       a.cap, a.max_pos, n_slots, NW, nsub, scale_log2);
+    hipLaunchKernelGGL((decode_attn<T, D, NWAVE, KPW>), dim3((unsigned)blocks), dim3(NWAVE * 64), 0, st, (const T *)a.q,
+                       a.row_seq, a.row_pos, (const T *)K, (const T *)V, sel, (float *)ws, a.Hq, a.Hkv, a.G, a.S, a.k,
+                       a.W, a.B, a.cap, a.max_pos, n_slots, NW, nsub, scale_log2);
     return hipGetLastError();
 }
+
+hipError_t decode_launch(const RowArgs &a, const void *K, const void *V, const int32_t *sel, void *ws,
+                         hipStream_t st) {
+    const DecodeShape sh = decode_shape(a);
+    if (a.dtype == RA_BF16 && a.d == 128) {
+        if (sh.nwave == 2 && sh.kpw == 64) return decode_launch_t<uint16_t, 128, 2, 64>(a, K, V, sel, ws, st);
+        if (sh.nwave == 4 && sh.kpw == 32) return decode_launch_t<uint16_t, 128, 4, 32>(a, K, V, sel, ws, st);
+        if (sh.nwave == 2 && sh.kpw == 32) return decode_launch_t<uint16_t, 128, 2, 32>(a, K, V, sel, ws, st);
+        if (sh.nwave == 8 && sh.kpw == 64) return decode_launch_t<uint16_t, 128, 8, 64>(a, K, V, sel, ws, st);
+        if (sh.nwave == 8 && sh.kpw == 32) return decode_launch_t<uint16_t, 128, 8, 32>(a, K, V, sel, ws, st);
+        return decode_launch_t<uint16_t, 128, 4, 64>(a, K, V, sel, ws, st);
+    }
+    if (a.dtype == RA_BF16) return decode_launch_t<uint16_t, 64, 4, 64>(a, K, V, sel, ws, st);
+    return a.d == 64 ? decode_launch_t<float, 64, 4, 64>(a, K, V, sel, ws, st)
+                     : decode_launch_t<float, 128, 4, 32>(a, K, V, sel, ws, st);
+}
+
+int decode_sub_tile(const RowArgs &a) {
+    const DecodeShape sh = decode_shape(a);
+    return sh.nwave * sh.kpw;
+}
+
 }  // namespace
 
 size_t decode_workspace_bytes(const RowArgs &a) {
@@ -302,11 +543,7 @@ size_t decode_workspace_bytes(const RowArgs &a) {
 hipError_t launch_decode(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out, void *ws,
                          hipStream_t st) {
     if (a.n_rows == 0) return hipSuccess;
-    hipError_t e;
-    if (a.dtype == RA_BF16)
-        e = a.d == 64 ? decode_launch<uint16_t, 64>(a, K, V, sel, ws, st) : decode_launch<uint16_t, 128>(a, K, V, sel, ws, st);
-    else
-        e = a.d == 64 ? decode_launch<float, 64>(a, K, V, sel, ws, st) : decode_launch<float, 128>(a, K, V, sel, ws, st);
+    const hipError_t e = decode_launch(a, K, V, sel, ws, st);
     if (e != hipSuccess) return e;
     const int TK = decode_sub_tile(a);
     return launch_combine(a, (const float *)ws, sel, out, (int)ceil_div(a.S, TK), TK, st);

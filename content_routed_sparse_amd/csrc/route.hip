@@ -7,10 +7,11 @@
 //    (4 waves x 16) and a chunk of spans; span summaries are rounded to bf16 once per block and
 //    staged in LDS, shared by the 4 waves.  Rows of different sequences in one tile are handled
 //    in successive passes (one pass in the usual single-sequence chunk).
-//  * route_valu (fp32 inputs, or few rows as in decode): one thread per span, fp32 FMA over the
-//    d elements in order, all query heads of the kv head at once.
+//  * route_valu (fp32 inputs, or few rows as in decode): fp32 FMA; lanes split each summary
+//    row, 8 query heads per pass, butterfly reduction over the lanes of a row.
 #include "common.h"
 #include "kernels.h"
+#include "wave_ops.h"
 
 namespace ra {
 namespace {
@@ -18,13 +19,19 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Few rows (decode) or fp32 inputs: a block scores 64 spans of one (row, kv head) for all the
+// kv head's query heads.  Lanes split each fp32 summary row (8 elements per lane, LPR lanes per
+// row, coalesced 32-byte loads); each lane forms partial dot products for 8 heads at once, and a
+// butterfly reduce-scatter over the LPR lanes leaves 2 finished scores per lane.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) route_valu(const T *__restrict__ q, const int32_t *__restrict__ row_seq,
                                                   const int64_t *__restrict__ row_pos,
                                                   const float *__restrict__ mean, float *__restrict__ scores,
                                                   int64_t stride, int Hq, int Hkv, int G, int S, int W, int B,
                                                   int64_t max_spans, int64_t max_pos) {
-    __shared__ float qs[8][D];
+    constexpr int LPR = D / 8, RPI = 64 / LPR, STEPS = 16 / RPI, N = STEPS * 8, KEEP = N / LPR;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = lane % LPR, rr = lane / LPR;
     const int rg = blockIdx.x;
     const int64_t row = rg / Hkv;
     const int g = rg % Hkv;
@@ -33,36 +40,84 @@ __global__ void __launch_bounds__(256) route_valu(const T *__restrict__ q, const
     int seq = row_seq[row];
     seq = seq < 0 ? 0 : (seq >= B ? B - 1 : seq);
     const int64_t r = num_routable(t, S, W);
-    const int64_t j = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
-    const float *m = mean + (((int64_t)seq * Hkv + g) * max_spans + (j < r ? j : 0)) * D;
+    const int64_t jw = (int64_t)blockIdx.y * 64 + wave * 16;  // this wave's first span
+    if (jw >= r) return;
+    const float *mbase = mean + ((int64_t)seq * Hkv + g) * max_spans * D;
+    // every load of the block (summaries and the first 8 heads' queries) is issued before any
+    // use and pinned there: one memory round trip instead of one per load
+    float4 mraw[STEPS][2];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        int64_t n = jw + s * RPI + rr;
+        n = n < r ? n : r - 1;
+        mraw[s][0] = *reinterpret_cast<const float4 *>(mbase + n * D + c * 8);
+        mraw[s][1] = *reinterpret_cast<const float4 *>(mbase + n * D + c * 8 + 4);
+    }
+    constexpr int QV = sizeof(T) == 2 ? 1 : 2;  // 16-byte pieces per head slice of 8 elements
+    uint4 qraw[8][QV];
+    auto load_q = [&](int hc) {
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            const int hh = hc + h < G ? hc + h : G - 1;  // clamped head; zeroed later if past G
+            const uint4 *qp = reinterpret_cast<const uint4 *>(q + (row * Hq + g * G + hh) * D + c * 8);
+#pragma unroll
+            for (int v = 0; v < QV; ++v) qraw[h][v] = qp[v];
+        }
+    };
+    load_q(0);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+            asm volatile("" : "+v"(mraw[s][v].x), "+v"(mraw[s][v].y), "+v"(mraw[s][v].z), "+v"(mraw[s][v].w));
+    float mv[STEPS][8];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        const float f[8] = {mraw[s][0].x, mraw[s][0].y, mraw[s][0].z, mraw[s][0].w,
+                            mraw[s][1].x, mraw[s][1].y, mraw[s][1].z, mraw[s][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mv[s][e] = sizeof(T) == 2 ? round_bf16(f[e]) : f[e];
+    }
     for (int hc = 0; hc < G; hc += 8) {
-        const int nh = G - hc < 8 ? G - hc : 8;
-        __syncthreads();
-        for (int x = threadIdx.x; x < nh * D; x += blockDim.x) {
-            const int h = x / D, e = x % D;
-            const T v = q[(row * Hq + g * G + hc + h) * D + e];
-            if constexpr (sizeof(T) == 2) qs[h][e] = bf16_bits_to_f32(v);
-            else qs[h][e] = v;
-        }
-        __syncthreads();
-        if (j >= r) continue;
-        float acc[8];
+        if (hc > 0) load_q(hc);
+        float acc[N];
 #pragma unroll
-        for (int h = 0; h < 8; ++h) acc[h] = 0.f;
-        for (int e = 0; e < D; e += 4) {
-            const float4 mv = *reinterpret_cast<const float4 *>(m + e);
-            float mm[4] = {mv.x, mv.y, mv.z, mv.w};
+        for (int h = 0; h < 8; ++h) {
+            float qf[8];
             if constexpr (sizeof(T) == 2) {
+                const uint32_t w[4] = {qraw[h][0].x, qraw[h][0].y, qraw[h][0].z, qraw[h][0].w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mm[i] = round_bf16(mm[i]);
+                for (int i = 0; i < 4; ++i) {
+                    qf[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+                    qf[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+                }
+            } else {
+                const uint32_t w[8] = {qraw[h][0].x, qraw[h][0].y, qraw[h][0].z, qraw[h][0].w,
+                                       qraw[h][1].x, qraw[h][1].y, qraw[h][1].z, qraw[h][1].w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) qf[i] = __uint_as_float(w[i]);
+            }
+            if (hc + h >= G) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[e] = 0.f;
             }
 #pragma unroll
-            for (int h = 0; h < 8; ++h) {
+            for (int s = 0; s < STEPS; ++s) {
+                float d = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[h] = fmaf(qs[h][e + i], mm[i], acc[h]);
+                for (int e = 0; e < 8; ++e) d = fmaf(qf[e], mv[s][e], d);
+                acc[s * 8 + h] = d;
             }
         }
-        for (int h = 0; h < nh; ++h) scores[(row * Hq + g * G + hc + h) * stride + j] = acc[h];
+        ReduceScatter<N, ilog2(LPR), LPR / 2>::run(acc, lane);
+#pragma unroll
+        for (int i = 0; i < KEEP; ++i) {
+            const int v = c * KEEP + i;
+            const int s = v / 8, h = v % 8;
+            const int64_t n = jw + s * RPI + rr;
+            if (n < r && hc + h < G) scores[(row * Hq + g * G + hc + h) * stride + n] = acc[i];
+        }
     }
 }
 
@@ -205,7 +260,7 @@ template <typename T, int D>
 hipError_t route_valu_launch(const RowArgs &a, const float *mean, float *scores, int64_t stride, hipStream_t st) {
     const int64_t rmax = num_routable(a.max_pos, a.S, a.W);
     if (rmax == 0 || a.n_rows == 0) return hipSuccess;
-    dim3 grid((unsigned)(a.n_rows * a.Hkv), (unsigned)ceil_div(rmax, 256));
+    dim3 grid((unsigned)(a.n_rows * a.Hkv), (unsigned)ceil_div(rmax, 64));
     hipLaunchKernelGGL((route_valu<T, D>), grid, dim3(256), 0, st, (const T *)a.q, a.row_seq, a.row_pos, mean, scores,
                        stride, a.Hq, a.Hkv, a.G, a.S, a.W, a.B, a.max_spans, a.max_pos);
     return hipGetLastError();

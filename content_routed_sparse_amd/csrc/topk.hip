@@ -8,6 +8,7 @@
 // winners are then written in ascending span order and padded with -1.
 #include "common.h"
 #include "kernels.h"
+#include "wave_ops.h"
 
 namespace ra {
 namespace {
@@ -16,15 +17,6 @@ __device__ __forceinline__ uint64_t score_key(float s, int64_t j) {
     uint32_t u = __float_as_uint(s);
     u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint64_t o = __shfl_xor(v, off);
-        v = o > v ? o : v;
-    }
-    return v;
 }
 
 // PER_LANE candidates per lane kept in registers (r <= 64 * PER_LANE).
@@ -40,20 +32,35 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
     const int64_t r = num_routable(t, S, W);
     const float *srow = scores + rh * stride;
 
+    // unconditional loads from clamped indices (a conditional load would be issued and waited
+    // for one at a time); every valid key is > 0, invalid candidates get key 0
     uint64_t key[PER_LANE];
+    float sv[PER_LANE];
+    const int64_t jmax = r > 0 ? r - 1 : 0;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) {
         const int64_t j = lane + 64 * i;
-        key[i] = j < r ? score_key(srow[j], j) : 0ull;  // every valid key is > 0
+        sv[i] = srow[j < jmax ? j : jmax];
+    }
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+        const int64_t j = lane + 64 * i;
+        key[i] = j < r ? score_key(sv[i], j) : 0ull;
     }
     const int m = (int)(r < k ? r : k);
     uint64_t last = ~0ull;
     uint32_t mine = 0xFFFFFFFFu;  // lane w keeps the w-th winner's span index
     for (int w = 0; w < m; ++w) {
-        uint64_t best = 0;
+        // candidates below the previous winner, maximum by a balanced tree (short dependency chain)
+        uint64_t f[PER_LANE];
 #pragma unroll
-        for (int i = 0; i < PER_LANE; ++i) best = (key[i] < last && key[i] > best) ? key[i] : best;
-        best = wave_max_u64(best);
+        for (int i = 0; i < PER_LANE; ++i) f[i] = key[i] < last ? key[i] : 0ull;
+#pragma unroll
+        for (int width = 1; width < PER_LANE; width *= 2) {
+#pragma unroll
+            for (int i = 0; i + width < PER_LANE; i += 2 * width) f[i] = f[i + width] > f[i] ? f[i + width] : f[i];
+        }
+        const uint64_t best = wave_max_u64(f[0]);
         last = best;
         if (lane == w) mine = 0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull);
     }
