@@ -54,6 +54,18 @@ __device__ __forceinline__ void unpack16(const uint4 &raw, float *f, float) {
     f[3] = __uint_as_float(raw.w);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Dot product of 8 bf16 pairs packed in two uint4 (four v_dot2_f32_bf16).
+__device__ __forceinline__ float dot8_bf16(const uint4 &a, const uint4 &b) {
+    float r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), 0.f,
+                                              false);
+    r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), r, false);
+    r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), r, false);
+    r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), r, false);
+    return r;
+}
+
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -64,7 +76,8 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
                                                    const int64_t *__restrict__ row_pos, const T *K, const T *V,
                                                    const int32_t *__restrict__ sel, float *__restrict__ part, int Hq,
                                                    int Hkv, int G, int S, int k, int W, int B, int64_t cap,
-                                                   int64_t max_pos, int n_slots, int NW, int nsub, float scale_log2) {
+                                                   int64_t max_pos, int64_t n_rows_total, int NW, int nsub,
+                                                   float scale_log2) {
     using L = Lanes<T, D, NWAVE, KPW_>;
     constexpr int EPL = L::EPL, LPR = L::LPR, RPI = L::RPI, KPW = L::KPW, STEPS = L::STEPS, TK = L::TK;
     constexpr int DUP = L::DUP;
@@ -74,13 +87,24 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
     __shared__ float wo[NWAVE][D];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int sub = blockIdx.x % nsub;
-    int64_t rest = blockIdx.x / nsub;
-    const int slot = (int)(rest % n_slots);
-    rest /= n_slots;
-    const int g = (int)(rest % Hkv);
-    const int64_t row = rest / Hkv;
     const int Gk = G * k;
+    // grid order: all window units first (they serve all G heads, so they carry the most work
+    // per block and should not form the tail), then the selected-span units
+    const int64_t n_win_units = n_rows_total * Hkv * (int64_t)NW * nsub;
+    int sub, slot, g;
+    int64_t row;
+    {
+        int64_t b = blockIdx.x;
+        const bool win = b < n_win_units;
+        if (!win) b -= n_win_units;
+        const int per = win ? NW : Gk;
+        sub = (int)(b % nsub);
+        b /= nsub;
+        slot = (int)(b % per) + (win ? Gk : 0);
+        b /= per;
+        g = (int)(b % Hkv);
+        row = b / Hkv;
+    }
     const bool is_window = slot >= Gk;
     const int32_t *sel_rg = sel + (row * Hq + (int64_t)g * G) * k;
 
@@ -213,17 +237,23 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) asm volatile("" : "+v"(kr[s].x), "+v"(kr[s].y), "+v"(kr[s].z), "+v"(kr[s].w));
         if (mi > 0) qraw = *reinterpret_cast<const uint4 *>(q + (row * Hq + hq) * D + c * EPL);
-        float qf[EPL];
-        unpack16(qraw, qf, T());
         float acc[STEPS];
+        if constexpr (sizeof(T) == 2) {
+            // bf16: packed pairs straight into v_dot2_f32_bf16 (exact products, fp32 sums)
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s) {
-            float kf[EPL];
-            unpack16(kr[s], kf, T());
-            float a = 0.f;
+            for (int s = 0; s < STEPS; ++s) acc[s] = dot8_bf16(qraw, kr[s]);
+        } else {
+            float qf[EPL];
+            unpack16(qraw, qf, T());
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) a = fmaf(qf[e], kf[e], a);
-            acc[s] = a;
+            for (int s = 0; s < STEPS; ++s) {
+                float kf[EPL];
+                unpack16(kr[s], kf, T());
+                float a = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) a = fmaf(qf[e], kf[e], a);
+                acc[s] = a;
+            }
         }
         ReduceScatter<STEPS, ilog2(STEPS), LPR / 2>::run(acc, lane);
         const float sc = allreduce_sum<DUP / 2>(acc[0]);
@@ -507,7 +537,7 @@ hipError_t decode_launch_t(const RowArgs &a, const void *K, const void *V, const
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     hipLaunchKernelGGL((decode_attn<T, D, NWAVE, KPW>), dim3((unsigned)blocks), dim3(NWAVE * 64), 0, st, (const T *)a.q,
                        a.row_seq, a.row_pos, (const T *)K, (const T *)V, sel, (float *)ws, a.Hq, a.Hkv, a.G, a.S, a.k,
-                       a.W, a.B, a.cap, a.max_pos, n_slots, NW, nsub, scale_log2);
+                       a.W, a.B, a.cap, a.max_pos, a.n_rows, NW, nsub, scale_log2);
     return hipGetLastError();
 }
 
