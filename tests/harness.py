@@ -166,7 +166,7 @@ def run_decode(w, lengths, capacity=None):
     return c, rows, q
 
 
-def run_prefill(w, prefix, chunk, pieces=1):
+def run_prefill(w, prefix, chunk, pieces=1, timed=False):
     """Cache of prefix + chunk tokens (one sequence); setup summaries of the prefix, then per
     piece: summary update of the piece's tokens and the prefill of its rows."""
     c = Case(w, [prefix + chunk])
@@ -174,9 +174,18 @@ def run_prefill(w, prefix, chunk, pieces=1):
     bounds = np.linspace(0, chunk, pieces + 1).astype(int)
     outs, sels = [], []
     for a, b in zip(bounds[:-1], bounds[1:]):
-        c.summarize([prefix + a], [prefix + b], b - a)
         rows, _ = c.chunk_rows(0, prefix + a, b - a)
+        torch.cuda.synchronize()
+        t0 = time.time()
+        c.summarize([prefix + a], [prefix + b], b - a)
         c.attend(rows, ra.RA_OP_PREFILL)
+        if timed:
+            log("  prefill of %d rows: %.2f ms (first call, includes setup of buffers)" % (b - a, (time.time() - t0) * 1e3))
+            for _ in range(2):
+                torch.cuda.synchronize()
+                t0 = time.time()
+                c.attend(rows, ra.RA_OP_PREFILL)
+                log("  route+topk+prefill again: %.2f ms" % ((time.time() - t0) * 1e3))
         outs.append(c.pipe.out.clone())
         sels.append(c.pipe.sel.clone())
     q = WL.queries(w, 0, prefix, chunk)

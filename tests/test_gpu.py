@@ -106,8 +106,11 @@ def test_last_prefill_row_matches_decode():
     # only inside the near-tie band, which the oracle checks below
     stats = cd.check([0], [4199], qd, [0])
     assert_stats(stats, True)
+    # the prefill tile rounds the softmax weights to bf16 for the P.V product (relative error
+    # up to 2^-9 per weight), the decode kernel keeps them in fp32: allow 2^-8 of max |o|
     diff = (out_p[-1] - cd.pipe.out[0]).abs().max(dim=1).values.cpu().numpy()
-    assert same.sum() >= 28 and np.all(diff[same] <= 1e-5), (same, diff)
+    scale = float(cd.pipe.out[0].abs().max())
+    assert same.sum() >= 28 and np.all(diff[same] <= max(scale, 0.1) * 2.0 ** -8), (same, diff)
 
 
 def test_repeatable_and_row_independent():
@@ -199,4 +202,22 @@ def test_ragged_decode_16_full():
     for b in sample:
         c.check_summaries(b)
     stats = c.check(sample, lengths[sample] - 1, q[sample], sample)
+    assert_stats(stats, True)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_8k_on_1m_full_sampled():
+    """8192-token chunk on a 1M-token cache: every row is computed; a seeded sample of 32
+    positions x 32 heads (always the chunk's first and last rows and span-boundary rows) is
+    compared with the oracle."""
+    w = W["prefill_8k_on_1m"]
+    P, n = w.prefix_len, w.chunk_len
+    log("prefill_8k_on_1m: prefix=%d chunk=%d" % (P, n))
+    c, q, out, sel = run_prefill(w, P, n, timed=True)
+    c.check_summaries(0)
+    rng = np.random.default_rng(w.seed)
+    must = [0, n - 1, 1022, 1023, 1024, 2047, 2048, 4095, 4096, n - 1025]
+    rest = sorted(set(rng.choice(n, 64, replace=False).tolist()) - set(must))[:32 - len(must)]
+    idx = np.array(sorted(set(must) | set(rest)))
+    stats = c.check([0] * len(idx), P + idx, q[idx], idx)
     assert_stats(stats, True)
