@@ -150,8 +150,11 @@ __global__ void __launch_bounds__(256) tile_valu(const T *__restrict__ q, const 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMfmaTile = 128;  // entries per tile: 4 waves x 32 rows
-constexpr int kChunk = 32;      // keys per LDS stage
+constexpr int kMfmaWaves = 8;                   // waves per block
+constexpr int kMfmaQT = 1;                      // 16-query tiles per wave
+constexpr int kMfmaTile = kMfmaWaves * 16 * kMfmaQT;  // entries per tile (128)
+constexpr int kChunk = 64;                      // keys per LDS stage
+constexpr int kMfmaThreads = kMfmaWaves * 64;
 
 // XCD-aware order: the hardware hands block b to XCD b % 8; give XCD x a contiguous range of
 // the tile list (tiles of one span are consecutive) so that they share its L2.
@@ -161,8 +164,74 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t grid) {
     return x * q + (x < rem ? x : rem) + i;
 }
 
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+// Global -> registers: the K rows and the V key pairs of chunk [k0, k0 + kChunk) that this
+// thread stages (rows past `hi` are clamped to hi - 1 and masked later).
+template <int D, int KPIECES, int VPIECES>
+__device__ __forceinline__ void stage_fetch(const uint16_t *Kb, const uint16_t *Vb, int64_t k0, int64_t hi, int tid,
+                                            uint4 (&kreg)[KPIECES], uint4 (&vreg)[VPIECES][2]) {
+#pragma unroll
+    for (int u = 0; u < KPIECES; ++u) {
+        const int v = tid + kMfmaThreads * u;
+        const int key = (v / (D / 8)) % kChunk, piece = v % (D / 8);
+        int64_t p = k0 + key;
+        p = p < hi ? p : hi - 1;
+        kreg[u] = *reinterpret_cast<const uint4 *>(Kb + p * D + piece * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < VPIECES; ++u) {
+        const int v = tid + kMfmaThreads * u;
+        const int kp = (v / (D / 8)) % (kChunk / 2), piece = v % (D / 8);
+        int64_t p0 = k0 + 2 * kp, p1 = p0 + 1;
+        p0 = p0 < hi ? p0 : hi - 1;
+        p1 = p1 < hi ? p1 : hi - 1;
+        vreg[u][0] = *reinterpret_cast<const uint4 *>(Vb + p0 * D + piece * 8);
+        vreg[u][1] = *reinterpret_cast<const uint4 *>(Vb + p1 * D + piece * 8);
+    }
+}
+
+// Registers -> LDS: K row-major (pitch D + 8), V transposed (pitch kChunk + 8), two keys per
+// 32-bit store.
+template <int D, int KPIECES, int VPIECES>
+__device__ __forceinline__ void stage_store(uint16_t *Ks, uint16_t *Vt, int tid, const uint4 (&kreg)[KPIECES],
+                                            const uint4 (&vreg)[VPIECES][2]) {
+    constexpr int KROW = D + 8, VROW = kChunk + 8;
+#pragma unroll
+    for (int u = 0; u < KPIECES; ++u) {
+        const int v = tid + kMfmaThreads * u;
+        if (v < kChunk * (D / 8)) {
+            const int key = v / (D / 8), piece = v % (D / 8);
+            *reinterpret_cast<uint4 *>(&Ks[key * KROW + piece * 8]) = kreg[u];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < VPIECES; ++u) {
+        const int v = tid + kMfmaThreads * u;
+        if (v < (kChunk / 2) * (D / 8)) {
+            const int kp = v / (D / 8), piece = v % (D / 8);
+            const uint32_t w0[4] = {vreg[u][0].x, vreg[u][0].y, vreg[u][0].z, vreg[u][0].w};
+            const uint32_t w1[4] = {vreg[u][1].x, vreg[u][1].y, vreg[u][1].z, vreg[u][1].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = piece * 8 + 2 * i;
+                *reinterpret_cast<uint32_t *>(&Vt[e * VROW + 2 * kp]) = (w0[i] & 0xFFFFu) | (w1[i] << 16);
+                *reinterpret_cast<uint32_t *>(&Vt[(e + 1) * VROW + 2 * kp]) = (w0[i] >> 16) | (w1[i] & 0xFFFF0000u);
+            }
+        }
+    }
+}
+
+// Transposed formulation.  S^T = K Q^T puts keys on the MFMA rows and queries on the columns,
+// so lane (lg, lr) holds keys 16kt + 4lg + i of query lr: every per-query quantity (running
+// max, sum, rescale of the output) is lane-local, and only the max/sum across the 4 lane
+// groups of a query needs cross-lane steps.  O^T = V^T P^T then takes P straight from the S^T
+// registers: its 32-key K dimension is ordered as the lanes hold it (keys 4lg..4lg+3 of two
+// 16-key tiles per lane group), and V^T is read from LDS in the same order.
 template <int D>
-__global__ void __launch_bounds__(256) tile_mfma(const uint16_t *__restrict__ q, const int64_t *__restrict__ row_pos,
+__global__ void __launch_bounds__(kMfmaThreads, 2) tile_mfma(const uint16_t *__restrict__ q, const int64_t *__restrict__ row_pos,
                                                  const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
                                                  const int32_t *__restrict__ counts,
                                                  const int32_t *__restrict__ offsets,
@@ -172,16 +241,19 @@ __global__ void __launch_bounds__(256) tile_mfma(const uint16_t *__restrict__ q,
                                                  int NE, int Hq, int S, int64_t cap, int64_t max_pos,
                                                  float scale_log2) {
     constexpr int KS = D / 32;   // k-steps of the QK product
-    constexpr int ET = D / 16;   // 16-wide output tiles of the PV product
-    constexpr int KROW = D + 8;  // LDS row pitch of K (bf16 elements)
-    constexpr int VROW = kChunk + 8;
-    constexpr int PROW = kChunk + 8;
+    constexpr int ET = D / 16;   // 16-wide e tiles of the PV product
+    constexpr int KT = kChunk / 16;
+    constexpr int KROW = D + 8;      // LDS pitch of K rows (bf16)
+    constexpr int VROW = kChunk + 8; // LDS pitch of V^T rows (bf16)
+    constexpr int NT = kMfmaThreads, QT = kMfmaQT;
+    constexpr int KPIECES = (kChunk * (D / 8) + NT - 1) / NT;        // 16-byte K pieces per thread
+    constexpr int VPIECES = ((kChunk / 2) * (D / 8) + NT - 1) / NT;  // key pairs x 16-byte pieces
+    constexpr float NEG = -__builtin_huge_valf();
     __shared__ uint16_t Ks[kChunk * KROW];
     __shared__ uint16_t Vt[D * VROW];
-    __shared__ uint16_t Ps[4][32 * PROW];
     __shared__ int64_t row_t[kMfmaTile];
     __shared__ int32_t row_x[kMfmaTile];
-    __shared__ int64_t tmax_s;
+    __shared__ unsigned long long tmax_s, tmin_s;
 
     const int64_t total = tile_off[n_exp];
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
@@ -196,7 +268,10 @@ __global__ void __launch_bounds__(256) tile_mfma(const uint16_t *__restrict__ q,
     const int32_t *entries = list + offsets[expert] + tl.y;
     const int64_t lo = j * S;
 
-    // rows of the tile: entry id and position (t = -1 for padding rows: everything masked)
+    if (tid == 0) {
+        tmax_s = 0;
+        tmin_s = ~0ull;
+    }
     if (tid < kMfmaTile) {
         int32_t x = -1;
         int64_t t = -1;
@@ -208,152 +283,151 @@ __global__ void __launch_bounds__(256) tile_mfma(const uint16_t *__restrict__ q,
         row_x[tid] = x;
         row_t[tid] = t;
     }
-    if (tid == 0) tmax_s = 0;  // valid rows have t >= 0 (and a tile holds at least one)
     __syncthreads();
-    if (tid < n) atomicMax((unsigned long long *)&tmax_s, (unsigned long long)row_t[tid]);
+    if (tid < n) {
+        atomicMax(&tmax_s, (unsigned long long)row_t[tid]);
+        atomicMin(&tmin_s, (unsigned long long)row_t[tid]);
+    }
     __syncthreads();
-    // keys of the span this tile needs: [lo, hi), hi <= tmax + 1 (keys after every row are skipped)
-    const int64_t tmax = tmax_s;
-    int64_t hi = lo + S;
+    const int64_t tmax = (int64_t)tmax_s, tmin = (int64_t)tmin_s;
+    int64_t hi = lo + S;  // keys of the span used by the tile: [lo, hi)
     if (hi > tmax + 1) hi = tmax + 1;
     if (hi > cap) hi = cap;
 
-    // A operand: this wave's 2 x 16 gathered query rows, all k-steps, in registers
-    bf16x8_t qa[2][KS];
+    // B operand of S^T: this wave's 2 x 16 gathered query rows, all k-steps, in registers
+    bf16x8_t qb[QT][KS];
+    int64_t tq[QT];  // position of query (a, lr); -1 for padding
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-        const int32_t x = row_x[32 * wave + 16 * a + lr];
+    for (int a = 0; a < QT; ++a) {
+        const int r = 16 * QT * wave + 16 * a + lr;
+        const int32_t x = row_x[r];
+        tq[a] = row_t[r];
         const int64_t rh = x >= 0 ? x / NE : 0;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 raw = *reinterpret_cast<const uint4 *>(q + rh * D + 32 * ks + 8 * lg);
             if (x < 0) raw = make_uint4(0, 0, 0, 0);
-            qa[a][ks] = __builtin_bit_cast(bf16x8_t, raw);
+            qb[a][ks] = __builtin_bit_cast(bf16x8_t, raw);
         }
     }
-    // positions of the rows this lane's outputs belong to: rows 32w + 16a + 4lg + i
-    int64_t trow[2][4];
+    float m[QT], l[QT];
+    f32x4_t o[QT][ET];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) trow[a][i] = row_t[32 * wave + 16 * a + 4 * lg + i];
-
-    float m[2][4], l[2][4];
-    f32x4_t o[2][ET];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            m[a][i] = -__builtin_huge_valf();
-            l[a][i] = 0.f;
-        }
+    for (int a = 0; a < QT; ++a) {
+        m[a] = NEG;
+        l[a] = 0.f;
 #pragma unroll
         for (int et = 0; et < ET; ++et) o[a][et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
     const uint16_t *Kb = K + sg * cap * D;
     const uint16_t *Vb = V + sg * cap * D;
+    // staging registers: the next chunk's K and V pieces are loaded during the current compute
+    uint4 kreg[KPIECES], vreg[VPIECES][2];
+    if (lo < hi) stage_fetch<D, KPIECES, VPIECES>(Kb, Vb, lo, hi, tid, kreg, vreg);
     for (int64_t k0 = lo; k0 < hi; k0 += kChunk) {
-        // stage K rows [k0, k0+32) (row-major) and V^T (keys contiguous per element)
+        __syncthreads();  // the previous chunk's LDS reads are done
+        stage_store<D, KPIECES, VPIECES>(Ks, Vt, tid, kreg, vreg);
         __syncthreads();
-        for (int v = tid; v < kChunk * (D / 8); v += 256) {
-            const int key = v / (D / 8), piece = v % (D / 8);
-            int64_t p = k0 + key;
-            p = p < hi ? p : hi - 1;
-            *reinterpret_cast<uint4 *>(&Ks[key * KROW + piece * 8]) =
-                *reinterpret_cast<const uint4 *>(Kb + p * D + piece * 8);
-        }
-        for (int v = tid; v < (kChunk / 2) * (D / 8); v += 256) {
-            const int kp = v / (D / 8), piece = v % (D / 8);
-            int64_t p0 = k0 + 2 * kp, p1 = p0 + 1;
-            p0 = p0 < hi ? p0 : hi - 1;
-            p1 = p1 < hi ? p1 : hi - 1;
-            const uint4 r0 = *reinterpret_cast<const uint4 *>(Vb + p0 * D + piece * 8);
-            const uint4 r1 = *reinterpret_cast<const uint4 *>(Vb + p1 * D + piece * 8);
-            const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w}, w1[4] = {r1.x, r1.y, r1.z, r1.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = piece * 8 + 2 * i;
-                *reinterpret_cast<uint32_t *>(&Vt[e * VROW + 2 * kp]) = (w0[i] & 0xFFFFu) | (w1[i] << 16);
-                *reinterpret_cast<uint32_t *>(&Vt[(e + 1) * VROW + 2 * kp]) = (w0[i] >> 16) | (w1[i] & 0xFFFF0000u);
-            }
-        }
-        __syncthreads();
+        if (k0 + kChunk < hi) stage_fetch<D, KPIECES, VPIECES>(Kb, Vb, k0 + kChunk, hi, tid, kreg, vreg);
+        // a chunk needs masks only where it passes the span's end or some row's position
+        const bool full = (k0 + kChunk <= hi) && (k0 + kChunk - 1 <= tmin);
 
-        // S = Q K^T for 2 row tiles x 2 key tiles
-        f32x4_t sacc[2][2];
+        // S^T = K Q^T: 4 key tiles x 2 query tiles
+        f32x4_t sc[KT][QT];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            bf16x8_t kb[KS];
+        for (int kt = 0; kt < KT; ++kt) {
+            bf16x8_t ka[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kb[ks] = __builtin_bit_cast(bf16x8_t,
-                                            *reinterpret_cast<const uint4 *>(&Ks[(16 * nb + lr) * KROW + 32 * ks + 8 * lg]));
+                ka[ks] = __builtin_bit_cast(bf16x8_t,
+                                            *reinterpret_cast<const uint4 *>(&Ks[(16 * kt + lr) * KROW + 32 * ks + 8 * lg]));
 #pragma unroll
-            for (int a = 0; a < 2; ++a) {
+            for (int a = 0; a < QT; ++a) {
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[a][ks], kb[ks], acc, 0, 0, 0);
-                sacc[a][nb] = acc;
+                for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qb[a][ks], acc, 0, 0, 0);
+                sc[kt][a] = acc;  // S^T[key 16kt + 4lg + i][query 16a + lr]
             }
         }
-        // online softmax per row (row = 16 lanes of one DPP row x 2 key tiles)
+        // online softmax, per query (lane-local) with the max/sum across the 4 lane groups
+        uint32_t pk[QT][KT][2];  // P as bf16 pairs: [a][kt][i/2]
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
+        for (int a = 0; a < QT; ++a) {
+            float cmax = NEG;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float z[2];
+            for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const int64_t p = k0 + 16 * nb + lr;
-                    z[nb] = (p < hi && p <= trow[a][i]) ? sacc[a][nb][i] * scale_log2 : -__builtin_huge_valf();
+                for (int i = 0; i < 4; ++i) {
+                    float z = sc[kt][a][i] * scale_log2;
+                    if (!full) {
+                        const int64_t p = k0 + 16 * kt + 4 * lg + i;
+                        z = (p < hi && p <= tq[a]) ? z : NEG;
+                    }
+                    sc[kt][a][i] = z;
+                    cmax = fmaxf(cmax, z);
                 }
-                const float cmax = allreduce_max<8>(fmaxf(z[0], z[1]));
-                const float mn = fmaxf(m[a][i], cmax);
-                const bool live = mn != -__builtin_huge_valf();
-                const float alpha = live ? exp2f(m[a][i] - mn) : 1.f;
-                float psum = 0.f;
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const float pv = live ? exp2f(z[nb] - mn) : 0.f;
-                    const uint32_t pb = f32_to_bf16_bits(pv);
-                    psum += bf16_bits_to_f32(pb);
-                    Ps[wave][(16 * a + 4 * lg + i) * PROW + 16 * nb + lr] = (uint16_t)pb;
-                }
-                l[a][i] = l[a][i] * alpha + allreduce_sum<8>(psum);
-                m[a][i] = mn;
-#pragma unroll
-                for (int et = 0; et < ET; ++et) o[a][et][i] *= alpha;
             }
+            cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+            cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+            const float mn = fmaxf(m[a], cmax);
+            const bool live = mn != NEG;
+            // v_exp_f32 directly: arguments are <= 0, results in [0, 1] (tiny ones may flush to 0)
+            const float alpha = live ? __builtin_amdgcn_exp2f(m[a] - mn) : 1.f;
+            float psum = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                float pv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pv[i] = live ? __builtin_amdgcn_exp2f(sc[kt][a][i] - mn) : 0.f;
+                    psum += pv[i];
+                }
+                pk[a][kt][0] = pack_bf16x2(pv[0], pv[1]);
+                pk[a][kt][1] = pack_bf16x2(pv[2], pv[3]);
+            }
+            psum += __shfl_xor(psum, 16);
+            psum += __shfl_xor(psum, 32);
+            l[a] = l[a] * alpha + psum;
+            m[a] = mn;
+#pragma unroll
+            for (int et = 0; et < ET; ++et) o[a][et] *= alpha;
         }
-        __builtin_amdgcn_wave_barrier();
-        // O += P V
-        bf16x8_t pa[2];
+        // O^T += V^T P^T, 32-key steps: K slots 8lg..8lg+7 <-> keys (2kk)16 + 4lg + 0..3 and
+        // (2kk+1)16 + 4lg + 0..3 for both operands
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-            pa[a] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(&Ps[wave][(16 * a + lr) * PROW + 8 * lg]));
+        for (int kk = 0; kk < KT / 2; ++kk) {
+            bf16x8_t pb[QT];
 #pragma unroll
-        for (int et = 0; et < ET; ++et) {
-            const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(&Vt[(16 * et + lr) * VROW + 8 * lg]));
+            for (int a = 0; a < QT; ++a) {
+                const uint4 raw = make_uint4(pk[a][2 * kk][0], pk[a][2 * kk][1], pk[a][2 * kk + 1][0], pk[a][2 * kk + 1][1]);
+                pb[a] = __builtin_bit_cast(bf16x8_t, raw);
+            }
 #pragma unroll
-            for (int a = 0; a < 2; ++a) o[a][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[a], vb, o[a][et], 0, 0, 0);
+            for (int et = 0; et < ET; ++et) {
+                const uint16_t *vp = &Vt[(16 * et + lr) * VROW + 32 * kk + 4 * lg];
+                const uint2 v0 = *reinterpret_cast<const uint2 *>(vp);
+                const uint2 v1 = *reinterpret_cast<const uint2 *>(vp + 16);
+                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+#pragma unroll
+                for (int a = 0; a < QT; ++a) o[a][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[a], o[a][et], 0, 0, 0);
+            }
         }
     }
 
-    // records: (m, l, o[d]) for each valid row
+    // records: (m, l, o[d]) per valid row; lane (lg, lr) holds o[16et + 4lg + i] of query lr
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < QT; ++a) {
+        const int32_t x = row_x[16 * QT * wave + 16 * a + lr];
+        if (x < 0) continue;
+        float *rec = records + (int64_t)x * record_floats(D);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int32_t x = row_x[32 * wave + 16 * a + 4 * lg + i];
-            if (x < 0) continue;
-            float *rec = records + (int64_t)x * record_floats(D);
-#pragma unroll
-            for (int et = 0; et < ET; ++et) rec[4 + 16 * et + lr] = o[a][et][i];
-            if (lr == 0) {
-                rec[0] = m[a][i];
-                rec[1] = l[a][i];
-            }
+        for (int et = 0; et < ET; ++et)
+            *reinterpret_cast<float4 *>(rec + 4 + 16 * et + 4 * lg) =
+                make_float4(o[a][et][0], o[a][et][1], o[a][et][2], o[a][et][3]);
+        if (lg == 0) {
+            rec[0] = m[a];
+            rec[1] = l[a];
         }
     }
 }
@@ -362,7 +436,7 @@ template <int D>
 hipError_t mfma_launch(const TileArgs &t, hipStream_t st) {
     const RowArgs &a = t.a;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    hipLaunchKernelGGL((tile_mfma<D>), dim3((unsigned)t.max_tiles), dim3(256), 0, st, (const uint16_t *)a.q, a.row_pos,
+    hipLaunchKernelGGL((tile_mfma<D>), dim3((unsigned)t.max_tiles), dim3(kMfmaThreads), 0, st, (const uint16_t *)a.q, a.row_pos,
                        (const uint16_t *)t.K, (const uint16_t *)t.V, t.counts, t.offsets, t.tile_off, t.list, t.tiles,
                        t.records, t.n_exp, t.span_slots, t.NE, a.Hq, a.S, a.cap, a.max_pos, scale_log2);
     return hipGetLastError();
