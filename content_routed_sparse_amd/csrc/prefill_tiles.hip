@@ -168,59 +168,36 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
-// Global -> registers: the K rows and the V key pairs of chunk [k0, k0 + kChunk) that this
-// thread stages (rows past `hi` are clamped to hi - 1 and masked later).
-template <int D, int KPIECES, int VPIECES>
-__device__ __forceinline__ void stage_fetch(const uint16_t *Kb, const uint16_t *Vb, int64_t k0, int64_t hi, int tid,
-                                            uint4 (&kreg)[KPIECES], uint4 (&vreg)[VPIECES][2]) {
-#pragma unroll
-    for (int u = 0; u < KPIECES; ++u) {
-        const int v = tid + kMfmaThreads * u;
-        const int key = (v / (D / 8)) % kChunk, piece = v % (D / 8);
-        int64_t p = k0 + key;
-        p = p < hi ? p : hi - 1;
-        kreg[u] = *reinterpret_cast<const uint4 *>(Kb + p * D + piece * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < VPIECES; ++u) {
-        const int v = tid + kMfmaThreads * u;
-        const int kp = (v / (D / 8)) % (kChunk / 2), piece = v % (D / 8);
-        int64_t p0 = k0 + 2 * kp, p1 = p0 + 1;
-        p0 = p0 < hi ? p0 : hi - 1;
-        p1 = p1 < hi ? p1 : hi - 1;
-        vreg[u][0] = *reinterpret_cast<const uint4 *>(Vb + p0 * D + piece * 8);
-        vreg[u][1] = *reinterpret_cast<const uint4 *>(Vb + p1 * D + piece * 8);
-    }
-}
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+#define RA_LDS __attribute__((address_space(3)))
 
-// Registers -> LDS: K row-major (pitch D + 8), V transposed (pitch kChunk + 8), two keys per
-// 32-bit store.
-template <int D, int KPIECES, int VPIECES>
-__device__ __forceinline__ void stage_store(uint16_t *Ks, uint16_t *Vt, int tid, const uint4 (&kreg)[KPIECES],
-                                            const uint4 (&vreg)[VPIECES][2]) {
-    constexpr int KROW = D + 8, VROW = kChunk + 8;
+// LDS layout of a staged chunk: kChunk rows of D bf16, unpadded (global_load_lds writes 1 KB
+// contiguous per wave instruction), with the 16-byte pieces of each row permuted by an XOR so
+// that the MFMA operand reads do not collide on banks:
+//   K: piece p of row r at position p ^ (r mod P), P = D / 8 pieces per row;
+//   V: piece p of row r at position p ^ 2 (r mod 4).
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return r % (D / 8); }
+__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
+
+// Issue the direct global -> LDS loads of chunk [c0, c0 + kChunk) into (Kd, Vd); rows past
+// `hi` repeat row hi - 1 (masked later).  Each wave instruction fills 1 KB = 1024 / (2 D) rows.
+template <int D>
+__device__ __forceinline__ void chunk_load(const uint16_t *Kb, const uint16_t *Vb, uint16_t *Kd, uint16_t *Vd,
+                                           int64_t c0, int64_t hi, int wave, int lane) {
+    constexpr int ROWS = 1024 / (2 * D);     // rows per wave instruction
+    constexpr int NI = kChunk / ROWS;        // instructions per tensor per chunk
+    constexpr int P = D / 8;                 // pieces per row
 #pragma unroll
-    for (int u = 0; u < KPIECES; ++u) {
-        const int v = tid + kMfmaThreads * u;
-        if (v < kChunk * (D / 8)) {
-            const int key = v / (D / 8), piece = v % (D / 8);
-            *reinterpret_cast<uint4 *>(&Ks[key * KROW + piece * 8]) = kreg[u];
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < VPIECES; ++u) {
-        const int v = tid + kMfmaThreads * u;
-        if (v < (kChunk / 2) * (D / 8)) {
-            const int kp = v / (D / 8), piece = v % (D / 8);
-            const uint32_t w0[4] = {vreg[u][0].x, vreg[u][0].y, vreg[u][0].z, vreg[u][0].w};
-            const uint32_t w1[4] = {vreg[u][1].x, vreg[u][1].y, vreg[u][1].z, vreg[u][1].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = piece * 8 + 2 * i;
-                *reinterpret_cast<uint32_t *>(&Vt[e * VROW + 2 * kp]) = (w0[i] & 0xFFFFu) | (w1[i] << 16);
-                *reinterpret_cast<uint32_t *>(&Vt[(e + 1) * VROW + 2 * kp]) = (w0[i] >> 16) | (w1[i] & 0xFFFF0000u);
-            }
-        }
+    for (int ii = wave; ii < NI; ii += kMfmaWaves) {
+        const int r = ii * ROWS + lane / P;  // chunk row written by this lane
+        const int phys = lane % P;
+        int64_t g = c0 + r;
+        g = g < hi ? g : hi - 1;
+        const uint16_t *ksrc = Kb + g * D + (phys ^ kswz<D>(r)) * 8;
+        const uint16_t *vsrc = Vb + g * D + (phys ^ vswz(r)) * 8;
+        __builtin_amdgcn_global_load_lds((const void *)ksrc, (RA_LDS void *)(Kd + ii * ROWS * D), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)vsrc, (RA_LDS void *)(Vd + ii * ROWS * D), 16, 0, 0);
     }
 }
 
@@ -231,7 +208,7 @@ __device__ __forceinline__ void stage_store(uint16_t *Ks, uint16_t *Vt, int tid,
 // registers: its 32-key K dimension is ordered as the lanes hold it (keys 4lg..4lg+3 of two
 // 16-key tiles per lane group), and V^T is read from LDS in the same order.
 template <int D>
-__global__ void __launch_bounds__(kMfmaThreads, 2) tile_mfma(const uint16_t *__restrict__ q, const int64_t *__restrict__ row_pos,
+__global__ void __launch_bounds__(kMfmaThreads) tile_mfma(const uint16_t *__restrict__ q, const int64_t *__restrict__ row_pos,
                                                  const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
                                                  const int32_t *__restrict__ counts,
                                                  const int32_t *__restrict__ offsets,
@@ -243,14 +220,10 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) tile_mfma(const uint16_t *__r
     constexpr int KS = D / 32;   // k-steps of the QK product
     constexpr int ET = D / 16;   // 16-wide e tiles of the PV product
     constexpr int KT = kChunk / 16;
-    constexpr int KROW = D + 8;      // LDS pitch of K rows (bf16)
-    constexpr int VROW = kChunk + 8; // LDS pitch of V^T rows (bf16)
     constexpr int NT = kMfmaThreads, QT = kMfmaQT;
-    constexpr int KPIECES = (kChunk * (D / 8) + NT - 1) / NT;        // 16-byte K pieces per thread
-    constexpr int VPIECES = ((kChunk / 2) * (D / 8) + NT - 1) / NT;  // key pairs x 16-byte pieces
     constexpr float NEG = -__builtin_huge_valf();
-    __shared__ uint16_t Ks[kChunk * KROW];
-    __shared__ uint16_t Vt[D * VROW];
+    __shared__ uint16_t Ks[2][kChunk * D];
+    __shared__ uint16_t Vs[2][kChunk * D];
     __shared__ int64_t row_t[kMfmaTile];
     __shared__ int32_t row_x[kMfmaTile];
     __shared__ unsigned long long tmax_s, tmin_s;
@@ -322,14 +295,15 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) tile_mfma(const uint16_t *__r
 
     const uint16_t *Kb = K + sg * cap * D;
     const uint16_t *Vb = V + sg * cap * D;
-    // staging registers: the next chunk's K and V pieces are loaded during the current compute
-    uint4 kreg[KPIECES], vreg[VPIECES][2];
-    if (lo < hi) stage_fetch<D, KPIECES, VPIECES>(Kb, Vb, lo, hi, tid, kreg, vreg);
-    for (int64_t k0 = lo; k0 < hi; k0 += kChunk) {
-        __syncthreads();  // the previous chunk's LDS reads are done
-        stage_store<D, KPIECES, VPIECES>(Ks, Vt, tid, kreg, vreg);
-        __syncthreads();
-        if (k0 + kChunk < hi) stage_fetch<D, KPIECES, VPIECES>(Kb, Vb, k0 + kChunk, hi, tid, kreg, vreg);
+    // double-buffered chunks: the loads of chunk c+1 fly while chunk c is computed
+    if (lo < hi) chunk_load<D>(Kb, Vb, Ks[0], Vs[0], lo, hi, wave, lane);
+    int buf = 0;
+    for (int64_t k0 = lo; k0 < hi; k0 += kChunk, buf ^= 1) {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of chunk c landed
+        __syncthreads();  // everyone's loads landed, and everyone finished reading the other buffer
+        if (k0 + kChunk < hi) chunk_load<D>(Kb, Vb, Ks[buf ^ 1], Vs[buf ^ 1], k0 + kChunk, hi, wave, lane);
+        const uint16_t *Kc = Ks[buf];
+        const uint16_t *Vc = Vs[buf];
         // a chunk needs masks only where it passes the span's end or some row's position
         const bool full = (k0 + kChunk <= hi) && (k0 + kChunk - 1 <= tmin);
 
@@ -339,9 +313,11 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) tile_mfma(const uint16_t *__r
         for (int kt = 0; kt < KT; ++kt) {
             bf16x8_t ka[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                ka[ks] = __builtin_bit_cast(bf16x8_t,
-                                            *reinterpret_cast<const uint4 *>(&Ks[(16 * kt + lr) * KROW + 32 * ks + 8 * lg]));
+            for (int ks = 0; ks < KS; ++ks) {
+                const int r = 16 * kt + lr;
+                ka[ks] = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const uint4 *>(&Kc[r * D + (((4 * ks + lg) ^ kswz<D>(r)) * 8)]));
+            }
 #pragma unroll
             for (int a = 0; a < QT; ++a) {
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -405,10 +381,19 @@ __global__ void __launch_bounds__(kMfmaThreads, 2) tile_mfma(const uint16_t *__r
             }
 #pragma unroll
             for (int et = 0; et < ET; ++et) {
-                const uint16_t *vp = &Vt[(16 * et + lr) * VROW + 32 * kk + 4 * lg];
-                const uint2 v0 = *reinterpret_cast<const uint2 *>(vp);
-                const uint2 v1 = *reinterpret_cast<const uint2 *>(vp + 16);
-                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                // transposed reads: lane (lg, i) gets V[key][16 et + i] for 4 consecutive keys; the
+                // 16 lanes of a group address rows base + j/4, columns 16 et + 4 (j % 4)
+                uint32_t vw[4];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 32 * kk + 16 * h + 4 * lg + (lr >> 2);
+                    const int col = 16 * et + 4 * (lr & 3);
+                    const int addr = r * D + (((col >> 3) ^ vswz(r)) << 3) + (col & 7);
+                    const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS v4i16_t *)(Vc + addr));
+                    vw[2 * h] = (uint32_t)(uint16_t)t[0] | ((uint32_t)(uint16_t)t[1] << 16);
+                    vw[2 * h + 1] = (uint32_t)(uint16_t)t[2] | ((uint32_t)(uint16_t)t[3] << 16);
+                }
+                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(vw[0], vw[1], vw[2], vw[3]));
 #pragma unroll
                 for (int a = 0; a < QT; ++a) o[a][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[a], o[a][et], 0, 0, 0);
             }
