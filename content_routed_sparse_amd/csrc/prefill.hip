@@ -94,6 +94,71 @@ __global__ void count_kernel(const int32_t *__restrict__ sel, const int32_t *__r
     local[x] = slot;
 }
 
+// Same counts with far fewer global atomics: a block takes kCountRows rows x the G heads of one
+// kv head, counts their entries per span in an LDS histogram (entries of other sequences than
+// the block's first row go straight to the global counters), then adds each non-empty bin to
+// the global counter once and hands the entries their final slots.
+constexpr int kCountRows = 32;
+constexpr int kCountMaxSpans = 8192;
+
+__global__ void __launch_bounds__(256) count_kernel_lds(const int32_t *__restrict__ sel,
+                                                        const int32_t *__restrict__ row_seq,
+                                                        const int64_t *__restrict__ row_pos,
+                                                        int32_t *__restrict__ counts, int32_t *__restrict__ local,
+                                                        int64_t n_rows, int NE, int Hq, int Hkv, int G, int S, int k,
+                                                        int W, int B, int64_t max_pos, int64_t span_slots) {
+    __shared__ int32_t hist[kCountMaxSpans];
+    const int tid = threadIdx.x;
+    const int g = blockIdx.y;
+    const int64_t r0 = (int64_t)blockIdx.x * kCountRows;
+    const int64_t r1 = r0 + kCountRows < n_rows ? r0 + kCountRows : n_rows;
+    int ref = row_seq[r0];
+    ref = ref < 0 ? 0 : (ref >= B ? B - 1 : ref);
+    for (int64_t j = tid; j < span_slots; j += 256) hist[j] = 0;
+    __syncthreads();
+    const int64_t per_row = (int64_t)G * NE;
+    const int64_t n_ent = (r1 - r0) * per_row;
+    for (int64_t y = tid; y < n_ent; y += 256) {
+        const int64_t row = r0 + y / per_row;
+        const int h = (int)((y % per_row) / NE), e = (int)(y % NE);
+        const int64_t rh = row * Hq + (int64_t)g * G + h;
+        const int64_t x = rh * NE + e;
+        int64_t t = row_pos[row];
+        t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
+        int seq = row_seq[row];
+        seq = seq < 0 ? 0 : (seq >= B ? B - 1 : seq);
+        int64_t j;
+        int32_t slot = -1;
+        if (entry_span(sel, rh, e, k, t, S, W, j)) {
+            if (seq == ref) slot = atomicAdd(&hist[j], 1);  // rank within this block's bin
+            else slot = -2 - atomicAdd(&counts[((int64_t)seq * Hkv + g) * span_slots + j], 1);
+        }
+        local[x] = slot;
+    }
+    __syncthreads();
+    for (int64_t j = tid; j < span_slots; j += 256) {
+        const int32_t c = hist[j];
+        hist[j] = c > 0 ? atomicAdd(&counts[((int64_t)ref * Hkv + g) * span_slots + j], c) : 0;
+    }
+    __syncthreads();
+    for (int64_t y = tid; y < n_ent; y += 256) {
+        const int64_t row = r0 + y / per_row;
+        const int h = (int)((y % per_row) / NE), e = (int)(y % NE);
+        const int64_t rh = row * Hq + (int64_t)g * G + h;
+        const int64_t x = rh * NE + e;
+        const int32_t v = local[x];
+        if (v >= 0) {
+            int64_t t = row_pos[row];
+            t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
+            int64_t j;
+            entry_span(sel, rh, e, k, t, S, W, j);
+            local[x] = hist[j] + v;
+        } else if (v <= -2) {
+            local[x] = -2 - v;  // slot taken directly in the global counter
+        }
+    }
+}
+
 // Exclusive scans of counts and of tiles per expert, in one block.
 __global__ void __launch_bounds__(1024) scan_kernel(const int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                     int32_t *__restrict__ tile_off, int64_t n_exp, int MT) {
@@ -191,9 +256,15 @@ hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const 
     const int MT = prefill_tile_rows(a);
 
     hipLaunchKernelGGL(fill_i32, dim3((unsigned)ceil_div(L.n_exp + 1, 256)), dim3(256), 0, st, counts, L.n_exp + 1, 0);
-    hipLaunchKernelGGL(count_kernel, dim3((unsigned)ceil_div(L.n_ent, 256)), dim3(256), 0, st, sel, a.row_seq,
-                       a.row_pos, counts, local, L.n_ent, NE, a.Hq, a.Hkv, a.G, a.S, a.k, a.W, a.B, a.max_pos,
-                       L.span_slots);
+    if (L.span_slots <= kCountMaxSpans) {
+        hipLaunchKernelGGL(count_kernel_lds, dim3((unsigned)ceil_div(a.n_rows, kCountRows), (unsigned)a.Hkv), dim3(256),
+                           0, st, sel, a.row_seq, a.row_pos, counts, local, a.n_rows, NE, a.Hq, a.Hkv, a.G, a.S, a.k,
+                           a.W, a.B, a.max_pos, L.span_slots);
+    } else {
+        hipLaunchKernelGGL(count_kernel, dim3((unsigned)ceil_div(L.n_ent, 256)), dim3(256), 0, st, sel, a.row_seq,
+                           a.row_pos, counts, local, L.n_ent, NE, a.Hq, a.Hkv, a.G, a.S, a.k, a.W, a.B, a.max_pos,
+                           L.span_slots);
+    }
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, tile_off, L.n_exp, MT);
     hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)ceil_div(L.n_ent, 256)), dim3(256), 0, st, sel, a.row_seq,
                        a.row_pos, offsets, local, list, L.n_ent, NE, a.Hq, a.Hkv, a.G, a.S, a.k, a.W, a.B, a.max_pos,

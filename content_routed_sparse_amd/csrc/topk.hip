@@ -3,9 +3,8 @@
 // One 64-lane wavefront per (row, query head).  Each routable span j < r(t) becomes a 64-bit
 // key  (order-preserving image of the fp32 score) << 32 | (0xFFFFFFFF - j),  so a larger key
 // means a higher score and, on equal scores, a lower span index: the selection order is a
-// strict total order.  Lanes hold their candidates in registers (lane l owns j = l + 64 i);
-// m = min(k, r) rounds each take the wave maximum among keys below the previous winner.  The
-// winners are then written in ascending span order and padded with -1.
+// strict total order.  Lanes hold their candidates in registers (lane l owns j = l + 64 i).
+// The winners are written in ascending span order and padded with -1.
 #include "common.h"
 #include "kernels.h"
 #include "wave_ops.h"
@@ -15,22 +14,39 @@ namespace {
 
 __device__ __forceinline__ uint64_t score_key(float s, int64_t j) {
     uint32_t u = __float_as_uint(s);
+    if (s == 0.f) u = 0u;  // -0 and +0 are the same score: the lower index must win
     u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
 }
 
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // PER_LANE candidates per lane kept in registers (r <= 64 * PER_LANE).
+//
+// Threshold first: T0 = the m-th largest of the 64 per-lane maxima (found by counting, per lane,
+// the lanes with a larger maximum).  The m lanes whose maxima are >= T0 hold at least m keys
+// >= T0, so every one of the m winners is >= T0.  The keys >= T0 (usually little more than m)
+// are compacted into LDS and each is ranked against the others; if more than 64 pass, the
+// selection falls back to m rounds of "largest key below the previous winner".
 template <int PER_LANE>
 __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ scores, int64_t stride,
                                                    const int64_t *__restrict__ row_pos, int32_t *__restrict__ sel,
                                                    int64_t n_rowheads, int Hq, int k, int S, int W, int64_t max_pos) {
-    const int lane = threadIdx.x & 63;
-    const int64_t rh = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    __shared__ uint64_t cand[4][64];
+    __shared__ uint32_t cidx[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t rh = (int64_t)blockIdx.x * (blockDim.x / 64) + wave;
     if (rh >= n_rowheads) return;
     int64_t t = row_pos[rh / Hq];
     t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
     const int64_t r = num_routable(t, S, W);
     const float *srow = scores + rh * stride;
+    int32_t *out = sel + rh * k;
+    const int m = (int)(r < k ? r : k);
 
     // unconditional loads from clamped indices (a conditional load would be issued and waited
     // for one at a time); every valid key is > 0, invalid candidates get key 0
@@ -47,31 +63,75 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
         const int64_t j = lane + 64 * i;
         key[i] = j < r ? score_key(sv[i], j) : 0ull;
     }
-    const int m = (int)(r < k ? r : k);
-    uint64_t last = ~0ull;
-    uint32_t mine = 0xFFFFFFFFu;  // lane w keeps the w-th winner's span index
-    for (int w = 0; w < m; ++w) {
-        // candidates below the previous winner, maximum by a balanced tree (short dependency chain)
-        uint64_t f[PER_LANE];
+    if (m == 0) {
+        if (lane < k) out[lane] = -1;
+        return;
+    }
+    // per-lane maximum (balanced tree)
+    uint64_t f[PER_LANE];
 #pragma unroll
-        for (int i = 0; i < PER_LANE; ++i) f[i] = key[i] < last ? key[i] : 0ull;
+    for (int i = 0; i < PER_LANE; ++i) f[i] = key[i];
+#pragma unroll
+    for (int width = 1; width < PER_LANE; width *= 2) {
+#pragma unroll
+        for (int i = 0; i + width < PER_LANE; i += 2 * width) f[i] = f[i + width] > f[i] ? f[i + width] : f[i];
+    }
+    const uint64_t lmax = f[0];
+    int above = 0;  // lanes whose maximum is larger than this lane's
+#pragma unroll 8
+    for (int l2 = 0; l2 < 64; ++l2) above += readlane_u64(lmax, l2) > lmax ? 1 : 0;
+    // at least m lanes hold a valid key (candidates are dealt round-robin and m <= r), so the
+    // m-th largest maximum is a valid, unique key
+    const uint64_t owner = __ballot(above == m - 1);
+    const uint64_t T0 = readlane_u64(lmax, (int)__builtin_ctzll(owner));
+
+    int C = 0;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+        const bool c = key[i] >= T0;
+        const uint64_t b = __ballot(c);
+        const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+        if (c && pos < 64) cand[wave][pos] = key[i];
+        C += (int)__builtin_popcountll(b);
+    }
+    if (C <= 64) {
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const uint64_t mine = lane < C ? cand[wave][lane] : 0ull;
+        int rank = 0;
+        for (int j2 = 0; j2 < C; ++j2) rank += cand[wave][j2] > mine ? 1 : 0;
+        const bool chosen = lane < C && rank < m;
+        const uint32_t idx = 0xFFFFFFFFu - (uint32_t)(mine & 0xFFFFFFFFull);
+        cidx[wave][lane] = chosen ? idx : 0xFFFFFFFFu;
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        int pos = 0;
+        for (int j2 = 0; j2 < C; ++j2) pos += cidx[wave][j2] < idx ? 1 : 0;
+        if (chosen) out[pos] = (int32_t)idx;
+        if (lane >= m && lane < k) out[lane] = -1;
+        return;
+    }
+
+    // fallback: m rounds, each taking the wave maximum among keys below the previous winner
+    uint64_t last = ~0ull;
+    uint32_t win = 0xFFFFFFFFu;  // lane w keeps the w-th winner's span index
+    for (int w = 0; w < m; ++w) {
+        uint64_t g[PER_LANE];
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) g[i] = key[i] < last ? key[i] : 0ull;
 #pragma unroll
         for (int width = 1; width < PER_LANE; width *= 2) {
 #pragma unroll
-            for (int i = 0; i + width < PER_LANE; i += 2 * width) f[i] = f[i + width] > f[i] ? f[i + width] : f[i];
+            for (int i = 0; i + width < PER_LANE; i += 2 * width) g[i] = g[i + width] > g[i] ? g[i + width] : g[i];
         }
-        const uint64_t best = wave_max_u64(f[0]);
+        const uint64_t best = wave_max_u64(g[0]);
         last = best;
-        if (lane == w) mine = 0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull);
+        if (lane == w) win = 0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull);
     }
-    // ascending order: rank of each winner among the winners
     int rank = 0;
     for (int w = 0; w < m; ++w) {
-        const uint32_t o = __shfl(mine, w);
-        rank += (o < mine) ? 1 : 0;
+        const uint32_t o = __shfl(win, w);
+        rank += (o < win) ? 1 : 0;
     }
-    int32_t *out = sel + rh * k;
-    if (lane < m) out[rank] = (int32_t)mine;
+    if (lane < m) out[rank] = (int32_t)win;
     else if (lane < k) out[lane] = -1;
 }
 

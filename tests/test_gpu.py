@@ -221,3 +221,47 @@ def test_prefill_8k_on_1m_full_sampled():
     idx = np.array(sorted(set(must) | set(rest)))
     stats = c.check([0] * len(idx), P + idx, q[idx], idx)
     assert_stats(stats, True)
+
+
+def _topk_case(r_values, pattern, k, seed):
+    """topk_spans on hand-made scores: rows at positions with the given routable counts."""
+    S = W = 4
+    rng = np.random.default_rng(seed)
+    n = len(r_values)
+    pos = np.array([4 * r + 3 for r in r_values], dtype=np.int64)  # r(t) = (t - 3) // 4 for t >= 3
+    stride = max(1, max(r_values))
+    sc = np.zeros((n, 1, stride), dtype=np.float32)
+    for i, r in enumerate(r_values):
+        if pattern == "normal":
+            sc[i, 0, :r] = rng.standard_normal(r)
+        elif pattern == "equal":
+            sc[i, 0, :r] = 0.25
+        elif pattern == "few_values":
+            sc[i, 0, :r] = rng.integers(-2, 3, r) * 0.5
+        elif pattern == "signed_zero":
+            sc[i, 0, :r] = np.where(rng.random(r) < 0.5, -0.0, 0.0)
+            sc[i, 0, :r:7] = -1.0
+        elif pattern == "one_lane":  # every large score sits in lane 0 (j = 0, 64, 128, ...)
+            sc[i, 0, :r] = rng.standard_normal(r) - 10.0
+            sc[i, 0, :r:64] = 100.0 + rng.standard_normal(len(range(0, r, 64)))
+        elif pattern == "descending":
+            sc[i, 0, :r] = -np.arange(r, dtype=np.float32)
+    cfg = ra.Config(1, 1, 64, S, k, W, ra.RA_BF16, 1, int(pos.max()) + 1)
+    rows = ra.Rows(torch.zeros(n, 1, 64, dtype=torch.bfloat16, device="cuda"),
+                   torch.zeros(n, dtype=torch.int32, device="cuda"), torch.as_tensor(pos).cuda(), int(pos.max()))
+    sel = torch.full((n, 1, k), 77, dtype=torch.int32, device="cuda")
+    ra.topk_spans(cfg, rows, torch.as_tensor(sc).cuda(), sel)
+    got = sel.cpu().numpy()
+    for i, r in enumerate(r_values):
+        want = O.select_spans(sc[i, 0, :r].astype(np.float64), k)
+        assert np.array_equal(got[i, 0], want), (pattern, r, got[i, 0], want)
+
+
+@pytest.mark.parametrize("pattern", ["normal", "equal", "few_values", "signed_zero", "one_lane", "descending"])
+def test_topk_spans_exact(pattern):
+    """Selection is exactly the oracle's on given scores, for every register width and the
+    fallback paths (r from 0 to beyond 64 x 40 candidates per lane)."""
+    for k in (1, 8, 16, 64):
+        for group in ([0, 1, 2, 15, 16, 17, 63, 64, 65, 100, 128], [129, 300, 511, 512], [513, 1000, 1031, 1088],
+                      [1089, 2000, 2559, 2560], [2561, 4000, 5000]):
+            _topk_case(group, pattern, k, seed=k * 1000 + len(group))
