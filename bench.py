@@ -36,6 +36,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true", help="replay the step from HIP graphs instead of launching")
+    p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    p.add_argument("--prefill-steps", type=int, default=5)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a 256 MiB device copy (reference kernel for HBM byte counters)")
     return p.parse_args()
 
 
@@ -185,12 +189,16 @@ def main():
     bytes_step = float(np.mean([per_seq[i % NC] for i in timed_ev]))
     achieved = bytes_step / (attn_ms * 1e-3) / 1e9
 
+    # counter-measured HBM bytes per launch (profiles/), valid only for the kernel sources they
+    # were taken on
     traffic = None
     tf = os.path.join(ROOT, "profiles", "decode_attn_decode_1m_traffic.json")
     if os.path.exists(tf):
         rec = json.load(open(tf))
-        src = open(os.path.join(ROOT, "content_routed_sparse_amd", "csrc", "decode.hip"), "rb").read()
-        if rec.get("source_sha256") == hashlib.sha256(src).hexdigest():
+        h = hashlib.sha256()
+        for f in rec.get("sources", []):
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if rec.get("source_sha256") == h.hexdigest():
             traffic = rec.get("bytes_per_launch")
 
     result = {
@@ -217,10 +225,95 @@ def main():
         "setup_seconds": round(gen_s, 1),
     }
 
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["oracle_check"] = cpu_baseline(w, st[0], args.cpu_seconds)
 
+    if not args.no_prefill:
+        del K, V, st
+        torch.cuda.empty_cache()
+        result["prefill"] = bench_prefill(args.prefill_steps)
+
     print(json.dumps(result), flush=True)
+
+
+def bench_prefill(steps):
+    """Chunked prefill: 8192 new tokens appended to a 1M-token cache (the chunk's K/V are in
+    the cache before timing).  A step = span_summary_update of the chunk + route_scores +
+    topk_spans + routed_attn_prefill for its 8192 x 32 row-heads."""
+    import torch
+
+    import content_routed_sparse_amd as ra
+    from synth import workloads as WL
+
+    w = WL.WORKLOADS["prefill_8k_on_1m"]
+    P, n = w.prefix_len, w.chunk_len
+    L = P + n
+    dev = torch.device("cuda:0")
+    cfg = ra.Config(w.num_q_heads, w.num_kv_heads, w.head_dim, w.span_size, w.top_k, w.window, ra.RA_BF16, 1, L)
+    K = torch.from_numpy(WL.kv_slab(w, 0, 0, L, "k").view(np.int16)).view(torch.bfloat16)[None].to(dev)
+    V = torch.from_numpy(WL.kv_slab(w, 0, 0, L, "v").view(np.int16)).view(torch.bfloat16)[None].to(dev)
+    q = torch.from_numpy(WL.queries(w, 0, P, n).view(np.int16)).view(torch.bfloat16).to(dev)
+    rows = ra.Rows(q, torch.zeros(n, dtype=torch.int32, device=dev),
+                   torch.arange(P, L, dtype=torch.int64, device=dev), L - 1)
+    mean = torch.zeros(1, w.num_kv_heads, cfg.max_spans, w.head_dim, dtype=torch.float32, device=dev)
+    run = torch.zeros(1, w.num_kv_heads, w.head_dim, dtype=torch.float32, device=dev)
+    t_p, t_l = torch.tensor([P], device=dev), torch.tensor([L], device=dev)
+    ra.span_summary_update(cfg, K, mean, run, torch.zeros(1, dtype=torch.int64, device=dev), t_p, P)  # setup
+    scores = torch.empty(n, w.num_q_heads, cfg.num_routable(L - 1), dtype=torch.float32, device=dev)
+    sel = torch.empty(n, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev)
+    out = torch.empty(n, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    ws = torch.empty(ra.workspace_bytes(cfg, ra.RA_OP_PREFILL, n, L - 1), dtype=torch.uint8, device=dev)
+    # the chunk starts and ends on span boundaries, so re-running the step recomputes the same
+    # summaries and leaves the running sum at zero: every step is the same work
+    calls = [ra.prepare("span_summary_update", cfg, K, mean, run, t_p, t_l, n),
+             ra.prepare("route_scores", cfg, rows, mean, scores),
+             ra.prepare("topk_spans", cfg, rows, scores, sel)]
+    attn = ra.prepare("routed_attn_prefill", cfg, rows, K, V, sel, out, ws)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for c in calls:
+        c()
+    attn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for c in calls:
+            c()
+        ev[i][0].record(stream)
+        attn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # algorithmic work: 4 d flops per (row-head, attended key) for Q.K^T and P.V, plus 2 d per
+    # (row-head, routable span) for routing; attended keys = selected spans' keys + window
+    pos = np.arange(P, L)
+    S, W = w.span_size, w.window
+    w0 = S * (np.maximum(0, pos - W + 1) // S)
+    r = w0 // S
+    m = np.minimum(w.top_k, r)
+    keys = (m * S + (pos - w0 + 1)).astype(np.float64)
+    d = w.head_dim
+    attn_flops = 4.0 * d * keys.sum() * w.num_q_heads
+    route_flops = 2.0 * d * r.astype(np.float64).sum() * w.num_q_heads
+    tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    return {
+        "workload": "prefill_8k_on_1m", "chunk": n, "context": L, "steps": steps,
+        "value": round(n / (step_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(step_ms, 4),
+        "roofline": {"bound": "mfma", "kernel": "routed_attn_prefill (dispatch + bf16 MFMA tiles + merge)",
+                     "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
+        "step_flops": attn_flops + route_flops,
+        "step_tflops": round((attn_flops + route_flops) / (step_ms * 1e-3) / 1e12, 1),
+    }
 
 
 def cpu_baseline(w, d0, seconds):
