@@ -265,3 +265,42 @@ def test_topk_spans_exact(pattern):
         for group in ([0, 1, 2, 15, 16, 17, 63, 64, 65, 100, 128], [129, 300, 511, 512], [513, 1000, 1031, 1088],
                       [1089, 2000, 2559, 2560], [2561, 4000, 5000]):
             _topk_case(group, pattern, k, seed=k * 1000 + len(group))
+
+
+@pytest.mark.timeout(1200)
+def test_decode_10m_full():
+    """Decode at L = 10,485,760 (20 GiB of bf16 K/V for one layer): all 32 rows."""
+    w = W["decode_10m"]
+    log("decode_10m: L=%d, 32 rows" % w.decode_len)
+    c, rows, q = run_decode(w, w.seq_lengths())
+    c.check_summaries(0)
+    stats = c.check([0], [w.decode_len - 1], q, [0])
+    assert_stats(stats, True)
+
+
+def test_decode_step_replays_from_a_hip_graph():
+    """The decode step captured in a HIP graph: every replay, with eager work and host
+    synchronisation in between, equals the eager result bit for bit."""
+    w = small("ragged_decode_16", batch=2, span_size=64, window=64, top_k=8, ragged=(3000, 6000))
+    lengths = w.seq_lengths()
+    c, rows, q = run_decode(w, lengths)
+    eager_out = c.pipe.out.clone()
+    eager_sel = c.pipe.sel.clone()
+    L = torch.as_tensor(lengths).cuda()
+    Lm1 = L - 1
+    cap_stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap_stream):
+        c.pipe.summarize(c.K, Lm1, L, 1)
+        c.pipe.attend(rows, c.K, c.V, ra.RA_OP_DECODE)
+    for rep in range(3):
+        c.pipe.out.zero_()
+        c.pipe.sel.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(c.pipe.out, eager_out), rep
+        assert torch.equal(c.pipe.sel, eager_sel), rep
+        # eager work between replays
+        c.attend(rows, ra.RA_OP_DECODE)
+        assert torch.equal(c.pipe.out, eager_out)
