@@ -143,17 +143,27 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
         } else {
             j = sel_rg[slot];
         }
-        if (j < 0 || j >= r) return;
         lo = j * S;
         hi = lo + S;
+        if (j < 0 || j >= r) hi = lo;  // entry selects nothing: its records are marked empty below
     } else {
         j = w0 / S + (slot - Gk);
         lo = j * S;
-        if (lo > t) return;
         hi = lo + S < t + 1 ? lo + S : t + 1;
     }
     const int64_t ulo = lo + (int64_t)sub * TK;
-    if (ulo >= hi) return;
+    if (ulo >= hi) {
+        // Every record slot is written on every call, so the combine never needs the selection:
+        // a unit without keys marks the records it stands for as empty (m = -inf, l = 0).
+        // (Records of a span entry that is not the owner's are written by the owner.)
+        if (tid < G && (is_window || tid == 0)) {
+            const int hq = g * G + (is_window ? tid : slot / k);
+            const int entry = is_window ? k + (slot - Gk) : slot % k;
+            float *rec = part + (((row * Hq + hq) * NE + entry) * (int64_t)nsub + sub) * record_floats(D);
+            *reinterpret_cast<float2 *>(rec) = make_float2(kNegInf, 0.f);
+        }
+        return;
+    }
     const int64_t uhi = ulo + TK < hi ? ulo + TK : hi;
 
     // heads to process.  Window: all G heads (entry k + w).  Span: every head whose selection
@@ -352,74 +362,80 @@ __device__ __forceinline__ void load_record_batch(const float *base, int x0, int
 
 constexpr int kRecBatch = 8;
 
-// Merge for few row-heads with many records: one block per row-head, three dependent rounds
-// of loads: (1) the row's position and its k selections into LDS; (2) every thread reads (m, l)
-// of its records into LDS and the block takes the maximum; (3) wave w sums the weighted
-// outputs of records w, w+4, ... (independent loads), and the 4 waves merge in fixed order.
-constexpr int kCombineMaxRec = 1024;
+// Merge for few row-heads with many records: one block of 16 waves per row-head.  Every record
+// slot is written by the decode kernel (empty ones have m = -inf), so each wave loads its records
+// (x = wave, wave + 16, ...) in batches with no dependent round trip, merges them with its own
+// running maximum, and the 16 wave states are merged in fixed order through LDS.
+constexpr int kCombineWaves = 16;
 
 template <int D>
-__global__ void __launch_bounds__(256) combine_block(const float *__restrict__ part, const int32_t *__restrict__ sel,
-                                                     const int64_t *__restrict__ row_pos, float *__restrict__ out,
-                                                     int Hq, int S, int k, int W, int64_t max_pos, int NW, int nsub,
-                                                     int TK) {
+__global__ void __launch_bounds__(kCombineWaves * 64) combine_block(const float *__restrict__ part,
+                                                                   float *__restrict__ out, int nrec) {
     constexpr int PER = D / 64;
-    __shared__ int32_t sel_s[64];
-    __shared__ float mrec[kCombineMaxRec], lrec[kCombineMaxRec];
-    __shared__ float red[4];
-    __shared__ float wsum[4], wout[4][D];
+    constexpr int B = 8;  // records per batch
+    __shared__ float wm[kCombineWaves], wl[kCombineWaves], wo[kCombineWaves][D];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t rh = blockIdx.x;
-    int64_t t = row_pos[rh / Hq];
-    t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
-    const int64_t w0 = window_start(t, S, W);
-    const int NE = k + NW;
-    const int nrec = NE * nsub < kCombineMaxRec ? NE * nsub : kCombineMaxRec;  // host guarantees NE*nsub fits
-    if (tid < k) sel_s[tid] = sel[rh * k + tid];
-    const float *base = part + rh * (int64_t)(NE * nsub) * record_floats(D);
-    __syncthreads();
-
-    float mx = kNegInf;
-    for (int x = tid; x < nrec; x += 256) {
-        const float2 ml = *reinterpret_cast<const float2 *>(base + (int64_t)x * record_floats(D));
-        const bool ok = record_valid(sel_s, x / nsub, x % nsub, t, w0, S, k, TK);
-        const float m = ok ? ml.x : kNegInf, l = ok ? ml.y : 0.f;
-        mrec[x] = m;
-        lrec[x] = l;
-        mx = fmaxf(mx, m);
-    }
-    mx = wave_max(mx);
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
-    float l = 0.f, o[PER];
+    const float *base = part + rh * (int64_t)nrec * record_floats(D);
+    float M = kNegInf, l = 0.f, o[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] = 0.f;
-    // records not produced hold stale bytes: their slices are loaded with the others and their
-    // contribution is discarded by a select
-    for (int x0 = wave; x0 < nrec; x0 += 4 * kRecBatch) {
-        float v[kRecBatch][PER];
-        load_record_batch<kRecBatch, PER, D>(base, x0, 4, nrec, lane, v);
+    for (int x0 = wave; x0 < nrec; x0 += kCombineWaves * B) {
+        float v[B][PER], mv[B], lv[B];
 #pragma unroll
-        for (int b = 0; b < kRecBatch; ++b) {
-            const int x = x0 + 4 * b;
-            if (x >= nrec) break;
-            const float m = mrec[x];
-            const bool ok = m != kNegInf;
-            const float f = ok ? exp2f(m - M) : 0.f;
-            l = ok ? fmaf(lrec[x], f, l) : l;
+        for (int b = 0; b < B; ++b) {
+            int x = x0 + kCombineWaves * b;
+            x = x < nrec ? x : nrec - 1;
+            const float *rec = base + (int64_t)x * record_floats(D);
+            const float2 ml = *reinterpret_cast<const float2 *>(rec);
+            mv[b] = ml.x;
+            lv[b] = ml.y;
 #pragma unroll
-            for (int i = 0; i < PER; ++i) o[i] = ok ? fmaf(v[b][i], f, o[i]) : o[i];
+            for (int i = 0; i < PER; ++i) v[b][i] = rec[4 + lane + 64 * i];
+        }
+        float bm = kNegInf;
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (x0 + kCombineWaves * b >= nrec) mv[b] = kNegInf;
+            bm = fmaxf(bm, mv[b]);
+        }
+        const float Mn = fmaxf(M, bm);
+        if (Mn != kNegInf) {
+            const float a = exp2f(M - Mn);  // 0 when M = -inf
+            l *= a;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) o[i] *= a;
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const bool ok = mv[b] != kNegInf;
+                const float f = ok ? exp2f(mv[b] - Mn) : 0.f;
+                l = ok ? fmaf(lv[b], f, l) : l;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) o[i] = ok ? fmaf(v[b][i], f, o[i]) : o[i];
+            }
+            M = Mn;
         }
     }
-    if (lane == 0) wsum[wave] = l;
+    if (lane == 0) {
+        wm[wave] = M;
+        wl[wave] = l;
+    }
 #pragma unroll
-    for (int i = 0; i < PER; ++i) wout[wave][lane + 64 * i] = o[i];
+    for (int i = 0; i < PER; ++i) wo[wave][lane + 64 * i] = o[i];
     __syncthreads();
     if (tid < D) {
-        const float Lt = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-        const float Ot = (wout[0][tid] + wout[1][tid]) + (wout[2][tid] + wout[3][tid]);
+        float Mt = kNegInf;
+#pragma unroll
+        for (int w = 0; w < kCombineWaves; ++w) Mt = fmaxf(Mt, wm[w]);
+        float Lt = 0.f, Ot = 0.f;
+#pragma unroll
+        for (int w = 0; w < kCombineWaves; ++w) {
+            if (wm[w] != kNegInf) {
+                const float f = exp2f(wm[w] - Mt);
+                Lt = fmaf(wl[w], f, Lt);
+                Ot = fmaf(wo[w][tid], f, Ot);
+            }
+        }
         out[rh * D + tid] = Lt > 0.f ? Ot / Lt : 0.f;
     }
 }
@@ -492,19 +508,14 @@ __global__ void __launch_bounds__(256) combine_wave(const float *__restrict__ pa
 
 }  // namespace
 
+// Prefill records of invalid entries are never written, so the prefill merge checks validity.
 hipError_t launch_combine(const RowArgs &a, const float *part, const int32_t *sel, float *out, int nsub, int TK,
                           hipStream_t st) {
     const int64_t n = a.n_rows * a.Hq;
     const int NW = max_window_spans(a.S, a.W);
-    if (n <= 4096 && (a.k + NW) * nsub <= kCombineMaxRec) {
-        auto kern = a.d == 64 ? combine_block<64> : combine_block<128>;
-        hipLaunchKernelGGL(kern, dim3((unsigned)n), dim3(256), 0, st, part, sel, a.row_pos, out, a.Hq, a.S, a.k, a.W,
-                           a.max_pos, NW, nsub, TK);
-    } else {
-        auto kern = a.d == 64 ? combine_wave<64> : combine_wave<128>;
-        hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(n, 4)), dim3(256), 0, st, part, sel, a.row_pos, out, n, a.Hq,
-                           a.S, a.k, a.W, a.max_pos, NW, nsub, TK);
-    }
+    auto kern = a.d == 64 ? combine_wave<64> : combine_wave<128>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(n, 4)), dim3(256), 0, st, part, sel, a.row_pos, out, n, a.Hq,
+                       a.S, a.k, a.W, a.max_pos, NW, nsub, TK);
     return hipGetLastError();
 }
 
@@ -576,7 +587,11 @@ hipError_t launch_decode(const RowArgs &a, const void *K, const void *V, const i
     const hipError_t e = decode_launch(a, K, V, sel, ws, st);
     if (e != hipSuccess) return e;
     const int TK = decode_sub_tile(a);
-    return launch_combine(a, (const float *)ws, sel, out, (int)ceil_div(a.S, TK), TK, st);
+    const int nrec = (a.k + max_window_spans(a.S, a.W)) * (int)ceil_div(a.S, TK);
+    auto kern = a.d == 64 ? combine_block<64> : combine_block<128>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_rows * a.Hq)), dim3(kCombineWaves * 64), 0, st, (const float *)ws,
+                       out, nrec);
+    return hipGetLastError();
 }
 
 }  // namespace ra
