@@ -18,10 +18,9 @@
 // butterfly reduce-scatter over the LPR lanes on DPP (each lane ends with one key's score), one
 // exp2 per lane, the probabilities broadcast through LDS, P.V in fp32, a reduce-scatter over
 // the row groups, and a 4-wave merge through LDS.  Partial states (m, l, o[d]) go to the
-// workspace; the combine kernel merges them per row in a fixed order.
-#include <stdio.h>
-#include <stdlib.h>
-
+// workspace, one record per (row, head, entry, sub-tile), and every record is written on every
+// call (units without keys mark theirs empty), so the combine kernel merges each row-head's
+// records in a fixed order without looking at the selection.
 #include "common.h"
 #include "kernels.h"
 #include "wave_ops.h"
@@ -70,6 +69,7 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kSelRegChunks = 4;  // selection entries of a kv head kept in registers: G*k <= 256
+constexpr int kMaxSelChunks = 32;  // G*k <= 32 * 64
 
 template <typename T, int D, int NWAVE, int KPW_>
 __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ q, const int32_t *__restrict__ row_seq,
@@ -82,7 +82,7 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
     constexpr int EPL = L::EPL, LPR = L::LPR, RPI = L::RPI, KPW = L::KPW, STEPS = L::STEPS, TK = L::TK;
     constexpr int DUP = L::DUP;
     __shared__ float pbuf[NWAVE][64];
-    __shared__ int match_s[NWAVE][32];
+    __shared__ uint64_t mask_s[NWAVE][kMaxSelChunks];
     __shared__ float wm[NWAVE], wl[NWAVE];
     __shared__ float wo[NWAVE][D];
 
@@ -106,6 +106,7 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
         row = b / Hkv;
     }
     const bool is_window = slot >= Gk;
+    const int h_own = slot / k, e_own = slot % k;  // span units: (query head, selection entry)
     const int32_t *sel_rg = sel + (row * Hq + (int64_t)g * G) * k;
 
     // one round trip: the row's position and sequence, and the kv head's selection entries
@@ -134,8 +135,24 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
     const int64_t r = w0 / S;
     const int NE = k + NW;  // entries per row-head in the workspace
 
+    // Which records this unit writes: (head h in `hw`, entry, sub).  Every (head, entry, sub)
+    // record of the call is written by exactly one unit, so the combine needs no selection:
+    //  - a window unit: all G heads, entry k + w (empty once the span starts after t);
+    //  - a span entry whose span id is out of range, or repeats an earlier entry of its head:
+    //    its own unit, empty;
+    //  - a valid span j: the unit of the lowest entry of the kv head that selects j (its "owner")
+    //    reads the span once and computes it for every head that selects j (GQA sharing), at
+    //    that head's first entry selecting j.
+    const uint32_t all_heads = G == 32 ? 0xFFFFFFFFu : (1u << G) - 1u;
+    uint32_t hw;
+    int first_e = -1;  // span owner: lane h < G holds the first entry of head h that selects j
     int64_t j, lo, hi;
-    if (!is_window) {
+    if (is_window) {
+        j = w0 / S + (slot - Gk);
+        lo = j * S;
+        hi = lo + S < t + 1 ? lo + S : t + 1;
+        hw = all_heads;
+    } else {
         if (sel_in_regs) {
             const int cc = slot >> 6;
             const int32_t v = cc == 0 ? selv[0] : cc == 1 ? selv[1] : cc == 2 ? selv[2] : selv[3];
@@ -143,180 +160,177 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
         } else {
             j = sel_rg[slot];
         }
-        lo = j * S;
-        hi = lo + S;
-        if (j < 0 || j >= r) hi = lo;  // entry selects nothing: its records are marked empty below
-    } else {
-        j = w0 / S + (slot - Gk);
-        lo = j * S;
-        hi = lo + S < t + 1 ? lo + S : t + 1;
+        lo = hi = 0;  // empty unless this unit owns a valid span
+        hw = 1u << h_own;
+        if (j >= 0 && j < r) {
+            // bit x of the mask: entry x of the kv head selects j
+            uint64_t b0 = 0, b1 = 0, b2 = 0, b3 = 0;
+            if (sel_in_regs) {  // (entries past G*k hold -1 and never match)
+                b0 = __ballot(selv[0] == (int32_t)j);
+                b1 = __ballot(selv[1] == (int32_t)j);
+                b2 = __ballot(selv[2] == (int32_t)j);
+                b3 = __ballot(selv[3] == (int32_t)j);
+            } else {
+                for (int cc = 0; cc * 64 < Gk; ++cc) {
+                    const int x = cc * 64 + lane;
+                    const uint64_t bal = __ballot(x < Gk && sel_rg[x] == (int32_t)j);
+                    if (lane == 0) mask_s[wave][cc] = bal;
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
+            if (lane < G) {  // head `lane`'s entries are mask bits lane*k .. lane*k + k - 1
+                const int pbit = lane * k, wd = pbit >> 6, sh = pbit & 63;
+                uint64_t lw, hw2;
+                if (sel_in_regs) {
+                    lw = wd == 0 ? b0 : wd == 1 ? b1 : wd == 2 ? b2 : b3;
+                    hw2 = wd == 0 ? b1 : wd == 1 ? b2 : wd == 2 ? b3 : 0ull;
+                } else {
+                    lw = mask_s[wave][wd];
+                    hw2 = (wd + 1) * 64 < Gk ? mask_s[wave][wd + 1] : 0ull;
+                }
+                uint64_t f = sh ? (lw >> sh) | (hw2 << (64 - sh)) : lw;
+                if (k < 64) f &= (1ull << k) - 1ull;
+                first_e = f ? (int)__builtin_ctzll(f) : -1;
+            }
+            const uint32_t hm = (uint32_t)__ballot(first_e >= 0);  // includes h_own
+            const int ho = (int)__builtin_ctz(hm);
+            if (ho == h_own && __builtin_amdgcn_readlane(first_e, ho) == e_own) {
+                hw = hm;  // the owner
+                lo = j * S;
+                hi = lo + S;
+            } else if (__builtin_amdgcn_readlane(first_e, h_own) == e_own) {
+                return;  // the owner writes this entry's records (and counts them)
+            }
+            // otherwise a repeated entry of its head: written empty below
+        }
     }
+    const bool owner_or_window = hi > lo;
+    auto rec_of = [&](int h, int entry) {
+        return part + (((row * Hq + g * G + h) * NE + entry) * (int64_t)nsub + sub) * record_floats(D);
+    };
     const int64_t ulo = lo + (int64_t)sub * TK;
     if (ulo >= hi) {
-        // Every record slot is written on every call, so the combine never needs the selection:
-        // a unit without keys marks the records it stands for as empty (m = -inf, l = 0).
-        // (Records of a span entry that is not the owner's are written by the owner.)
-        if (tid < G && (is_window || tid == 0)) {
-            const int hq = g * G + (is_window ? tid : slot / k);
-            const int entry = is_window ? k + (slot - Gk) : slot % k;
-            float *rec = part + (((row * Hq + hq) * NE + entry) * (int64_t)nsub + sub) * record_floats(D);
-            *reinterpret_cast<float2 *>(rec) = make_float2(kNegInf, 0.f);
+        // no keys: the unit's records are marked empty (m = -inf, l = 0)
+        if (tid < G && ((hw >> tid) & 1u)) {
+            const int entry = is_window ? k + (slot - Gk) : (owner_or_window ? first_e : e_own);
+            *reinterpret_cast<float2 *>(rec_of(tid, entry)) = make_float2(kNegInf, 0.f);
         }
-        return;
-    }
-    const int64_t uhi = ulo + TK < hi ? ulo + TK : hi;
-
-    // heads to process.  Window: all G heads (entry k + w).  Span: every head whose selection
-    // contains j, in selection order (entry = its position in that head's list); the unit runs
-    // only if the first of them is its own head.
-    int nmatch;
-    if (!is_window) {
-        nmatch = 0;
-        if (sel_in_regs) {
-#pragma unroll
-            for (int cc = 0; cc < kSelRegChunks; ++cc) {
-                const bool eq = selv[cc] == (int32_t)j;
-                const uint64_t bal = __ballot(eq);
-                if (eq) {
-                    const int idx = nmatch + (int)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
-                    if (idx < 32) match_s[wave][idx] = cc * 64 + lane;
-                }
-                nmatch += (int)__builtin_popcountll(bal);
-            }
-        } else {
-            for (int base = 0; base < Gk; base += 64) {
-                const int x = base + lane;
-                const bool eq = x < Gk && sel_rg[x] == j;
-                const uint64_t bal = __ballot(eq);
-                if (eq) {
-                    const int idx = nmatch + (int)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
-                    if (idx < 32) match_s[wave][idx] = x;
-                }
-                nmatch += (int)__builtin_popcountll(bal);
-            }
-        }
-        if (nmatch > G) nmatch = G;  // at most one entry per head in a valid selection
-        __builtin_amdgcn_wave_barrier();
-        if (match_s[wave][0] / k != slot / k) return;  // uniform: a lower head's unit owns the span
     } else {
-        nmatch = G;
-    }
-    auto match_head = [&](int mi, int &entry) {
-        if (is_window) {
-            entry = k + (slot - Gk);
-            return mi;
-        }
-        const int x = match_s[wave][mi];
-        entry = x % k;
-        return x / k;
-    };
-    const int c = lane % LPR, rr = lane / LPR;
-    int entry0;
-    const int h0 = match_head(0, entry0);
-    uint4 qraw = *reinterpret_cast<const uint4 *>(q + (row * Hq + g * G + h0) * D + c * EPL);
+        const int64_t uhi = ulo + TK < hi ? ulo + TK : hi;
+        const int c = lane % LPR, rr = lane / LPR;
+        const int h0 = (int)__builtin_ctz(hw);
+        uint4 qraw = *reinterpret_cast<const uint4 *>(q + (row * Hq + g * G + h0) * D + c * EPL);
 
-    // stream this wave's keys: all K and V loads are issued before any use
-    const int64_t kv_base = ((int64_t)seq * Hkv + g) * cap;
-    const int64_t wkey0 = ulo + (int64_t)wave * KPW;
-    uint4 kr[STEPS], vr[STEPS];
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        const int64_t key = wkey0 + s * RPI + rr;
-        const int64_t kl = key < uhi ? key : uhi - 1;  // in-bounds, finite row for masked keys
-        kr[s] = *reinterpret_cast<const uint4 *>(K + (kv_base + kl) * D + c * EPL);
-    }
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        const int64_t key = wkey0 + s * RPI + rr;
-        const int64_t kl = key < uhi ? key : uhi - 1;
-        vr[s] = *reinterpret_cast<const uint4 *>(V + (kv_base + kl) * D + c * EPL);
-    }
-    asm volatile("" ::: "memory");  // keep the loads here: nothing may sink them into the head loop
-
-    // the key whose score this lane holds after the reduce-scatter
-    const int s_own = c / DUP;
-    const bool own_valid = wkey0 + s_own * RPI + rr < uhi;
-    const bool counts = (c % DUP) == 0;  // one lane per key contributes to the sum
-
-    for (int mi = 0; mi < nmatch; ++mi) {
-        int entry;
-        const int h = match_head(mi, entry);
-        const int hq = g * G + h;
-        // the packed K/V registers are "redefined" here, so the compiler cannot hoist their
-        // widening out of the head loop (that would hold 2x the registers and stall the loads)
-#pragma unroll
-        for (int s = 0; s < STEPS; ++s) asm volatile("" : "+v"(kr[s].x), "+v"(kr[s].y), "+v"(kr[s].z), "+v"(kr[s].w));
-        if (mi > 0) qraw = *reinterpret_cast<const uint4 *>(q + (row * Hq + hq) * D + c * EPL);
-        float acc[STEPS];
-        if constexpr (sizeof(T) == 2) {
-            // bf16: packed pairs straight into v_dot2_f32_bf16 (exact products, fp32 sums)
-#pragma unroll
-            for (int s = 0; s < STEPS; ++s) acc[s] = dot8_bf16(qraw, kr[s]);
-        } else {
-            float qf[EPL];
-            unpack16(qraw, qf, T());
-#pragma unroll
-            for (int s = 0; s < STEPS; ++s) {
-                float kf[EPL];
-                unpack16(kr[s], kf, T());
-                float a = 0.f;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) a = fmaf(qf[e], kf[e], a);
-                acc[s] = a;
-            }
-        }
-        ReduceScatter<STEPS, ilog2(STEPS), LPR / 2>::run(acc, lane);
-        const float sc = allreduce_sum<DUP / 2>(acc[0]);
-        const float z = own_valid ? sc * scale_log2 : kNegInf;
-        const float m = wave_max(z);
-        const float p = (own_valid && m != kNegInf) ? exp2f(z - m) : 0.f;
-        const float ls = wave_sum(counts ? p : 0.f);
-        pbuf[wave][lane] = p;
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int s = 0; s < STEPS; ++s) asm volatile("" : "+v"(vr[s].x), "+v"(vr[s].y), "+v"(vr[s].z), "+v"(vr[s].w));
-        float o[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+        // stream this wave's keys: all K and V loads are issued before any use
+        const int64_t kv_base = ((int64_t)seq * Hkv + g) * cap;
+        const int64_t wkey0 = ulo + (int64_t)wave * KPW;
+        uint4 kr[STEPS], vr[STEPS];
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
-            const float ps = pbuf[wave][rr * LPR + s * DUP];
-            float vf[EPL];
-            unpack16(vr[s], vf, T());
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) o[e] = fmaf(ps, vf[e], o[e]);
-        }
-        ReduceScatter<EPL, ilog2(RPI), 32>::run(o, lane);  // over the row groups: EPL -> EPL / RPI values
-        constexpr int KEEP = EPL / RPI;
-        if (lane == 0) {
-            wm[wave] = m;
-            wl[wave] = ls;
+            const int64_t key = wkey0 + s * RPI + rr;
+            const int64_t kl = key < uhi ? key : uhi - 1;  // in-bounds, finite row for masked keys
+            kr[s] = *reinterpret_cast<const uint4 *>(K + (kv_base + kl) * D + c * EPL);
         }
 #pragma unroll
-        for (int i = 0; i < KEEP; ++i) wo[wave][c * EPL + rr * KEEP + i] = o[i];
-        __syncthreads();
-        if (tid < D) {
-            float M = wm[0];
+        for (int s = 0; s < STEPS; ++s) {
+            const int64_t key = wkey0 + s * RPI + rr;
+            const int64_t kl = key < uhi ? key : uhi - 1;
+            vr[s] = *reinterpret_cast<const uint4 *>(V + (kv_base + kl) * D + c * EPL);
+        }
+        asm volatile("" ::: "memory");  // keep the loads here: nothing may sink them into the head loop
+
+        // the key whose score this lane holds after the reduce-scatter
+        const int s_own = c / DUP;
+        const bool own_valid = wkey0 + s_own * RPI + rr < uhi;
+        const bool counts = (c % DUP) == 0;  // one lane per key contributes to the sum
+
+        uint32_t rem = hw;
+        bool first = true;
+        while (rem) {
+            const int h = (int)__builtin_ctz(rem);
+            rem &= rem - 1u;
+            const int entry = is_window ? k + (slot - Gk) : __builtin_amdgcn_readlane(first_e, h);
+            const int hq = g * G + h;
+            // the packed K/V registers are "redefined" here, so the compiler cannot hoist their
+            // widening out of the head loop (that would hold 2x the registers and stall the loads)
 #pragma unroll
-            for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, wm[w]);
-            float Lsum = 0.f, O = 0.f;
+            for (int s = 0; s < STEPS; ++s)
+                asm volatile("" : "+v"(kr[s].x), "+v"(kr[s].y), "+v"(kr[s].z), "+v"(kr[s].w));
+            if (!first) qraw = *reinterpret_cast<const uint4 *>(q + (row * Hq + hq) * D + c * EPL);
+            first = false;
+            float acc[STEPS];
+            if constexpr (sizeof(T) == 2) {
+                // bf16: packed pairs straight into v_dot2_f32_bf16 (exact products, fp32 sums)
 #pragma unroll
-            for (int w = 0; w < NWAVE; ++w) {
-                if (wm[w] != kNegInf) {
-                    const float f = exp2f(wm[w] - M);
-                    Lsum = fmaf(wl[w], f, Lsum);
-                    O = fmaf(wo[w][tid], f, O);
+                for (int s = 0; s < STEPS; ++s) acc[s] = dot8_bf16(qraw, kr[s]);
+            } else {
+                float qf[EPL];
+                unpack16(qraw, qf, T());
+#pragma unroll
+                for (int s = 0; s < STEPS; ++s) {
+                    float kf[EPL];
+                    unpack16(kr[s], kf, T());
+                    float a = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) a = fmaf(qf[e], kf[e], a);
+                    acc[s] = a;
                 }
             }
-            float *rec = part + (((row * Hq + hq) * NE + entry) * (int64_t)nsub + sub) * record_floats(D);
-            rec[4 + tid] = O;
-            if (tid == 0) {
-                rec[0] = M;
-                rec[1] = Lsum;
+            ReduceScatter<STEPS, ilog2(STEPS), LPR / 2>::run(acc, lane);
+            const float sc = allreduce_sum<DUP / 2>(acc[0]);
+            const float z = own_valid ? sc * scale_log2 : kNegInf;
+            const float m = wave_max(z);
+            const float p = (own_valid && m != kNegInf) ? exp2f(z - m) : 0.f;
+            const float ls = wave_sum(counts ? p : 0.f);
+            pbuf[wave][lane] = p;
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int s = 0; s < STEPS; ++s)
+                asm volatile("" : "+v"(vr[s].x), "+v"(vr[s].y), "+v"(vr[s].z), "+v"(vr[s].w));
+            float o[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+#pragma unroll
+            for (int s = 0; s < STEPS; ++s) {
+                const float ps = pbuf[wave][rr * LPR + s * DUP];
+                float vf[EPL];
+                unpack16(vr[s], vf, T());
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[e] = fmaf(ps, vf[e], o[e]);
             }
+            ReduceScatter<EPL, ilog2(RPI), 32>::run(o, lane);  // over the row groups: EPL -> EPL / RPI values
+            constexpr int KEEP = EPL / RPI;
+            if (lane == 0) {
+                wm[wave] = m;
+                wl[wave] = ls;
+            }
+#pragma unroll
+            for (int i = 0; i < KEEP; ++i) wo[wave][c * EPL + rr * KEEP + i] = o[i];
+            __syncthreads();
+            if (tid < D) {
+                float M = wm[0];
+#pragma unroll
+                for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, wm[w]);
+                float Lsum = 0.f, O = 0.f;
+#pragma unroll
+                for (int w = 0; w < NWAVE; ++w) {
+                    if (wm[w] != kNegInf) {
+                        const float f = exp2f(wm[w] - M);
+                        Lsum = fmaf(wl[w], f, Lsum);
+                        O = fmaf(wo[w][tid], f, O);
+                    }
+                }
+                float *rec = rec_of(h, entry);
+                rec[4 + tid] = O;
+                if (tid == 0) {
+                    rec[0] = M;
+                    rec[1] = Lsum;
+                }
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
+
 }
 
 // Records of one row-head: entry e < k is selected span sel[e] (skipped unless 0 <= j < r),
@@ -521,56 +535,33 @@ hipError_t launch_combine(const RowArgs &a, const float *part, const int32_t *se
 
 namespace {
 
-// Unit shape: waves per block and keys per wave (tuning experiment: RA_DECODE_SHAPE=WxK).
-struct DecodeShape {
-    int nwave, kpw;
-};
+// Keys per wave: 64 (16 loads of K and 16 of V per lane in flight), 32 for fp32 with d = 128
+// (the same 32 registers of data per lane); 4 waves per unit.
+constexpr int kDecodeWaves = 4;
 
-DecodeShape decode_shape(const RowArgs &a) {
-    DecodeShape s{4, (a.dtype == RA_F32 && a.d == 128) ? 32 : 64};
-    if (a.dtype == RA_BF16 && a.d == 128) {
-        if (const char *e = getenv("RA_DECODE_SHAPE")) {
-            int w = 0, kk = 0;
-            if (sscanf(e, "%dx%d", &w, &kk) == 2) s = DecodeShape{w, kk};
-        }
-    }
-    return s;
-}
+int decode_keys_per_wave(const RowArgs &a) { return (a.dtype == RA_F32 && a.d == 128) ? 32 : 64; }
 
-template <typename T, int D, int NWAVE, int KPW>
-hipError_t decode_launch_t(const RowArgs &a, const void *K, const void *V, const int32_t *sel, void *ws,
+int decode_sub_tile(const RowArgs &a) { return kDecodeWaves * decode_keys_per_wave(a); }
+
+template <typename T, int D, int KPW>
+hipError_t decode_launch_t(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out, void *ws,
                            hipStream_t st) {
-    using L = Lanes<T, D, NWAVE, KPW>;
+    using L = Lanes<T, D, kDecodeWaves, KPW>;
     const int NW = max_window_spans(a.S, a.W);
     const int n_slots = a.G * a.k + NW;
     const int nsub = (int)ceil_div(a.S, L::TK);
     const int64_t blocks = a.n_rows * a.Hkv * n_slots * nsub;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    hipLaunchKernelGGL((decode_attn<T, D, NWAVE, KPW>), dim3((unsigned)blocks), dim3(NWAVE * 64), 0, st, (const T *)a.q,
-                       a.row_seq, a.row_pos, (const T *)K, (const T *)V, sel, (float *)ws, a.Hq, a.Hkv, a.G, a.S, a.k,
-                       a.W, a.B, a.cap, a.max_pos, a.n_rows, NW, nsub, scale_log2);
+    float *part = (float *)ws;
+    hipLaunchKernelGGL((decode_attn<T, D, kDecodeWaves, KPW>), dim3((unsigned)blocks), dim3(kDecodeWaves * 64), 0, st,
+                       (const T *)a.q, a.row_seq, a.row_pos, (const T *)K, (const T *)V, sel, part, a.Hq, a.Hkv, a.G,
+                       a.S, a.k, a.W, a.B, a.cap, a.max_pos, a.n_rows, NW, nsub, scale_log2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nrec = (a.k + NW) * nsub;
+    hipLaunchKernelGGL((combine_block<D>), dim3((unsigned)(a.n_rows * a.Hq)), dim3(kCombineWaves * 64), 0, st, part,
+                       out, nrec);
     return hipGetLastError();
-}
-
-hipError_t decode_launch(const RowArgs &a, const void *K, const void *V, const int32_t *sel, void *ws,
-                         hipStream_t st) {
-    const DecodeShape sh = decode_shape(a);
-    if (a.dtype == RA_BF16 && a.d == 128) {
-        if (sh.nwave == 2 && sh.kpw == 64) return decode_launch_t<uint16_t, 128, 2, 64>(a, K, V, sel, ws, st);
-        if (sh.nwave == 4 && sh.kpw == 32) return decode_launch_t<uint16_t, 128, 4, 32>(a, K, V, sel, ws, st);
-        if (sh.nwave == 2 && sh.kpw == 32) return decode_launch_t<uint16_t, 128, 2, 32>(a, K, V, sel, ws, st);
-        if (sh.nwave == 8 && sh.kpw == 64) return decode_launch_t<uint16_t, 128, 8, 64>(a, K, V, sel, ws, st);
-        if (sh.nwave == 8 && sh.kpw == 32) return decode_launch_t<uint16_t, 128, 8, 32>(a, K, V, sel, ws, st);
-        return decode_launch_t<uint16_t, 128, 4, 64>(a, K, V, sel, ws, st);
-    }
-    if (a.dtype == RA_BF16) return decode_launch_t<uint16_t, 64, 4, 64>(a, K, V, sel, ws, st);
-    return a.d == 64 ? decode_launch_t<float, 64, 4, 64>(a, K, V, sel, ws, st)
-                     : decode_launch_t<float, 128, 4, 32>(a, K, V, sel, ws, st);
-}
-
-int decode_sub_tile(const RowArgs &a) {
-    const DecodeShape sh = decode_shape(a);
-    return sh.nwave * sh.kpw;
 }
 
 }  // namespace
@@ -584,14 +575,11 @@ size_t decode_workspace_bytes(const RowArgs &a) {
 hipError_t launch_decode(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out, void *ws,
                          hipStream_t st) {
     if (a.n_rows == 0) return hipSuccess;
-    const hipError_t e = decode_launch(a, K, V, sel, ws, st);
-    if (e != hipSuccess) return e;
-    const int TK = decode_sub_tile(a);
-    const int nrec = (a.k + max_window_spans(a.S, a.W)) * (int)ceil_div(a.S, TK);
-    auto kern = a.d == 64 ? combine_block<64> : combine_block<128>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_rows * a.Hq)), dim3(kCombineWaves * 64), 0, st, (const float *)ws,
-                       out, nrec);
-    return hipGetLastError();
+    if (a.dtype == RA_BF16)
+        return a.d == 64 ? decode_launch_t<uint16_t, 64, 64>(a, K, V, sel, out, ws, st)
+                         : decode_launch_t<uint16_t, 128, 64>(a, K, V, sel, out, ws, st);
+    return a.d == 64 ? decode_launch_t<float, 64, 64>(a, K, V, sel, out, ws, st)
+                     : decode_launch_t<float, 128, 32>(a, K, V, sel, out, ws, st);
 }
 
 }  // namespace ra

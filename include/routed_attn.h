@@ -130,7 +130,8 @@ ra_status topk_spans(const ra_config *cfg, const ra_rows *rows, const float *sco
  * few rows per sequence: the spans chosen by the query heads that share a kv head are read
  * once and split into sub-tiles across the GPU, and the partial softmax states are merged in
  * a second kernel (log-sum-exp, fixed order: results do not depend on scheduling).
- * Entries of `sel` outside [0, r(t)) are ignored.
+ * Entries of `sel` outside [0, r(t)) are ignored, and so is an entry that repeats an earlier
+ * entry of the same (row, head).
  *   workspace      device scratch of at least ra_workspace_bytes(cfg, RA_OP_DECODE, n_rows,
  *                  max_pos) bytes; contents on entry do not matter.
  */

@@ -57,6 +57,11 @@ DECODE_CASES = [
     ("fp32_d128", small("tiny_prefill_fp32", mode="decode", batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
                         span_size=128, window=200, top_k=4, ragged=(129, 3000)),),
     ("bf16_short_rows_r0", small("ragged_decode_16", batch=3, span_size=64, window=64, top_k=8, ragged=(1, 130)),),
+    # G*k > 256: the kv head's selection entries are matched from memory, not from registers
+    ("bf16_G32_k16", small("ragged_decode_16", batch=2, num_q_heads=32, num_kv_heads=1, span_size=32, window=32,
+                           top_k=16, ragged=(2000, 6000)),),
+    ("bf16_G8_k64", small("ragged_decode_16", batch=2, num_q_heads=16, num_kv_heads=2, span_size=16, window=40,
+                          top_k=64, ragged=(2500, 4000)),),
 ]
 
 
@@ -128,6 +133,50 @@ def test_repeatable_and_row_independent():
     rows3, _ = c.rows_for([3], lengths[[3]] - 1)
     out3 = c.attend(rows3, ra.RA_OP_DECODE).clone()
     assert torch.equal(out3[0], out1[3])
+
+
+@pytest.mark.parametrize("G,k", [(8, 8), (32, 16)])
+def test_decode_ignores_repeated_and_out_of_range_entries(G, k):
+    """A hand-made selection with repeated span ids (inside one head and across the heads of a
+    kv head) and ids outside [0, r): the result is attention over the distinct valid spans.
+    Two calls in a row give the same bits (the workspace counters are back at zero)."""
+    w = small("ragged_decode_16", batch=2, num_q_heads=2 * G, num_kv_heads=2, span_size=32, window=32, top_k=k,
+              ragged=(3000, 5000))
+    lengths = w.seq_lengths()
+    c, rows, q = run_decode(w, lengths)
+    rng = np.random.default_rng(7)
+    sel = np.empty((c.B, w.num_q_heads, k), dtype=np.int32)
+    for b in range(c.B):
+        r = c.cfg.num_routable(int(lengths[b]) - 1)
+        pool = rng.choice(r, size=3 * k // 2, replace=False)  # few distinct spans: heads share them
+        for h in range(w.num_q_heads):
+            row = rng.choice(pool, size=k)  # repeats inside the head
+            row[rng.random(k) < 0.15] = -1
+            row[rng.random(k) < 0.1] = r + rng.integers(0, 5)  # not routable
+            sel[b, h] = row
+    sel_d = torch.as_tensor(sel).cuda()
+    out = torch.empty(c.B, w.num_q_heads, w.head_dim, device="cuda")
+    ra.routed_attn_decode(c.cfg, rows, c.K, c.V, sel_d, out, c.pipe.workspace)
+    torch.cuda.synchronize()
+    first = out.clone()
+    ra.routed_attn_decode(c.cfg, rows, c.K, c.V, sel_d, out, c.pipe.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(first, out)
+    got = out.cpu().numpy()
+    worst = 0.0
+    for b in range(c.B):
+        t = int(lengths[b]) - 1
+        r = c.cfg.num_routable(t)
+        for h in range(w.num_q_heads):
+            used = []
+            for j in sel[b, h]:
+                if 0 <= j < r and j not in used:
+                    used.append(int(j))
+            ref = c.problem(b).row(q[b][h], h, t, sel=np.array(used, dtype=np.int64))["out"]
+            ma, rel = O.output_errors(got[b, h], ref)
+            worst = max(worst, ma)
+            assert ma <= O.compare.TOL_ABS["bf16"] and rel <= O.compare.TOL_REL_L2_BF16, (b, h, ma, rel)
+    log("  repeated/out-of-range entries: max abs %.3g" % worst)
 
 
 def test_empty_rows_are_a_no_op():
