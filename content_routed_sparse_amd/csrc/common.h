@@ -24,14 +24,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 __device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(f32_to_bf16_bits(f) << 16); }
 
 // ------------------------------------------------------------------------- span / window rules
-// Window start: span boundary at or below t - W + 1 (never below 0).
-__device__ __host__ __forceinline__ int64_t window_start(int64_t t, int S, int W) {
-    int64_t a = t - W + 1;
-    if (a < 0) a = 0;
-    return (a / S) * S;
+// a / b for a >= 0, b > 0, in 32-bit arithmetic whenever a fits (a 64-bit division is a long
+// instruction sequence on the GPU).
+__device__ __host__ __forceinline__ int64_t div_nonneg(int64_t a, int b) {
+    return (uint64_t)a <= 0x7FFFFFFFull ? (int64_t)((uint32_t)a / (uint32_t)b) : a / b;
 }
-// Number of routable spans: complete spans that end before the window.
-__device__ __host__ __forceinline__ int64_t num_routable(int64_t t, int S, int W) { return window_start(t, S, W) / S; }
+// Number of routable spans: complete spans that end before the window, floor(max(0, t-W+1) / S).
+__device__ __host__ __forceinline__ int64_t num_routable(int64_t t, int S, int W) {
+    const int64_t a = t - W + 1;
+    return a > 0 ? div_nonneg(a, S) : 0;
+}
+// Window start: span boundary at or below t - W + 1 (never below 0).
+__device__ __host__ __forceinline__ int64_t window_start(int64_t t, int S, int W) { return num_routable(t, S, W) * S; }
 
 // Largest number of spans a window can touch: the window has at most W + S - 1 tokens and
 // starts on a span boundary.

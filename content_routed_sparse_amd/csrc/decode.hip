@@ -97,24 +97,29 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
     __shared__ float wm[NWAVE], wl[NWAVE];
     __shared__ float wo[NWAVE][D];
 
+    // all kernel arguments in one round trip (otherwise some are fetched only where first used)
+    asm volatile("" ::"s"(q), "s"(row_seq), "s"(row_pos), "s"(K), "s"(V), "s"(sel), "s"(part), "s"(Hq), "s"(Hkv),
+                 "s"(G), "s"(S), "s"(k), "s"(W), "s"(B), "s"(cap), "s"(max_pos), "s"(n_rows_total), "s"(NW),
+                 "s"(nsub), "s"(scale_log2));
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Gk = G * k;
     // grid order: all window units first (they serve all G heads, so they carry the most work
     // per block and should not form the tail), then the selected-span units
-    const int64_t n_win_units = n_rows_total * Hkv * (int64_t)NW * nsub;
+    // (the grid has fewer than 2^32 blocks: 32-bit index arithmetic)
+    const uint32_t n_win_units = (uint32_t)(n_rows_total * Hkv * (int64_t)NW * nsub);
     int sub, slot, g;
     int64_t row;
     {
-        int64_t b = blockIdx.x;
+        uint32_t b = blockIdx.x;
         const bool win = b < n_win_units;
         if (!win) b -= n_win_units;
-        const int per = win ? NW : Gk;
-        sub = (int)(b % nsub);
-        b /= nsub;
+        const uint32_t per = win ? NW : Gk;
+        sub = (int)(b % (uint32_t)nsub);
+        b /= (uint32_t)nsub;
         slot = (int)(b % per) + (win ? Gk : 0);
         b /= per;
-        g = (int)(b % Hkv);
-        row = b / Hkv;
+        g = (int)(b % (uint32_t)Hkv);
+        row = b / (uint32_t)Hkv;
     }
     const bool is_window = slot >= Gk;
     const int h_own = slot / k, e_own = slot % k;  // span units: (query head, selection entry)
@@ -142,8 +147,8 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
     asm volatile("" ::"s"(t_raw), "s"(seq_raw));  // (and the scalar ones are not deferred)
     int64_t t = t_raw < 0 ? 0 : (t_raw > max_pos ? max_pos : t_raw);
     const int seq = seq_raw < 0 ? 0 : (seq_raw >= B ? B - 1 : seq_raw);
-    const int64_t w0 = window_start(t, S, W);
-    const int64_t r = w0 / S;
+    const int64_t r = num_routable(t, S, W);
+    const int64_t w0 = r * S;
     const int NE = k + NW;  // entries per row-head in the workspace
 
     // Which records this unit writes: (head h in `hw`, entry, sub).  Every (head, entry, sub)
@@ -159,7 +164,7 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
     int first_e = -1;  // span owner: lane h < G holds the first entry of head h that selects j
     int64_t j, lo, hi;
     if (is_window) {
-        j = w0 / S + (slot - Gk);
+        j = r + (slot - Gk);
         lo = j * S;
         hi = lo + S < t + 1 ? lo + S : t + 1;
         hw = all_heads;
@@ -352,7 +357,7 @@ __device__ __forceinline__ bool record_valid(const int32_t *sel_rh, int e, int s
     int64_t lo, hi;
     if (e < k) {
         const int64_t j = sel_rh[e];
-        if (j < 0 || j >= w0 / S) return false;
+        if (j < 0 || j >= div_nonneg(w0, S)) return false;
         lo = j * S;
         hi = lo + S;
     } else {
@@ -401,6 +406,7 @@ __global__ void __launch_bounds__(kCombineWaves * 64) combine_block(const float 
     __shared__ float wm[kCombineWaves], wl[kCombineWaves], wo[kCombineWaves][D];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t rh = blockIdx.x;
+    asm volatile("" ::"s"(part), "s"(out), "s"(nrec));  // all kernel arguments in one round trip
     const float *base = part + rh * (int64_t)nrec * record_floats(D);
     float M = kNegInf, l = 0.f, o[PER];
 #pragma unroll
@@ -417,6 +423,15 @@ __global__ void __launch_bounds__(kCombineWaves * 64) combine_block(const float 
             lv[b] = ml.y;
 #pragma unroll
             for (int i = 0; i < PER; ++i) v[b][i] = rec[4 + lane + 64 * i];
+        }
+        // every load of the batch stays here, ahead of the first use (left alone, the compiler
+        // sinks the l and o loads under the test of the maxima: a second round trip)
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            asm volatile("" : "+v"(mv[b]), "+v"(lv[b]));
+#pragma unroll
+            for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(v[b][i]));
         }
         float bm = kNegInf;
 #pragma unroll

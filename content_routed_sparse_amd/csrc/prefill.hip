@@ -59,15 +59,15 @@ __global__ void fill_i32(int32_t *p, int64_t n, int32_t v) {
     if (i < n) p[i] = v;
 }
 
-// expert id and key range of entry e of a row-head; false if the entry attends to nothing
+// span id of entry e of a row-head; false if the entry attends to nothing
 __device__ __forceinline__ bool entry_span(const int32_t *sel, int64_t rh, int e, int k, int64_t t, int S, int W,
                                            int64_t &j) {
     const int64_t w0 = window_start(t, S, W);
     if (e < k) {
         j = sel[rh * k + e];
-        return j >= 0 && j < w0 / S;
+        return j >= 0 && j < div_nonneg(w0, S);
     }
-    j = w0 / S + (e - k);
+    j = div_nonneg(w0, S) + (e - k);
     return j * S <= t;
 }
 

@@ -150,9 +150,8 @@ __global__ void __launch_bounds__(256) tile_valu(const T *__restrict__ q, const 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMfmaWaves = 8;                   // waves per block
-constexpr int kMfmaQT = 1;                      // 16-query tiles per wave
-constexpr int kMfmaTile = kMfmaWaves * 16 * kMfmaQT;  // entries per tile (128)
+constexpr int kMfmaWaves = 8;                   // waves per block, 16 queries each
+constexpr int kMfmaTile = kMfmaWaves * 16;      // entries per tile (128)
 constexpr int kChunk = 64;                      // keys per LDS stage
 constexpr int kMfmaThreads = kMfmaWaves * 64;
 
@@ -164,8 +163,13 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t grid) {
     return x * q + (x < rem ? x : rem) + i;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> bf16 (round to nearest even) packed in one register: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -180,11 +184,13 @@ template <int D>
 __device__ __forceinline__ int kswz(int r) { return r % (D / 8); }
 __device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
 
-// Issue the direct global -> LDS loads of chunk [c0, c0 + kChunk) into (Kd, Vd); rows past
-// `hi` repeat row hi - 1 (masked later).  Each wave instruction fills 1 KB = 1024 / (2 D) rows.
+// Issue the direct global -> LDS loads of the chunk at key offset c (from the span's first key,
+// whose K and V rows start at Ksp, Vsp) into (Kd, Vd); rows at or past `n` (the span's keys in
+// use) repeat row n - 1 (masked later).  Each wave instruction fills 1 KB = 1024 / (2 D) rows.
+// Offsets are 32-bit (a span's rows span S * D * 2 bytes), so the loads take a scalar base.
 template <int D>
-__device__ __forceinline__ void chunk_load(const uint16_t *Kb, const uint16_t *Vb, uint16_t *Kd, uint16_t *Vd,
-                                           int64_t c0, int64_t hi, int wave, int lane) {
+__device__ __forceinline__ void chunk_load(const uint16_t *Ksp, const uint16_t *Vsp, uint16_t *Kd, uint16_t *Vd,
+                                           int c, int n, int wave, int lane) {
     constexpr int ROWS = 1024 / (2 * D);     // rows per wave instruction
     constexpr int NI = kChunk / ROWS;        // instructions per tensor per chunk
     constexpr int P = D / 8;                 // pieces per row
@@ -192,12 +198,119 @@ __device__ __forceinline__ void chunk_load(const uint16_t *Kb, const uint16_t *V
     for (int ii = wave; ii < NI; ii += kMfmaWaves) {
         const int r = ii * ROWS + lane / P;  // chunk row written by this lane
         const int phys = lane % P;
-        int64_t g = c0 + r;
-        g = g < hi ? g : hi - 1;
-        const uint16_t *ksrc = Kb + g * D + (phys ^ kswz<D>(r)) * 8;
-        const uint16_t *vsrc = Vb + g * D + (phys ^ vswz(r)) * 8;
-        __builtin_amdgcn_global_load_lds((const void *)ksrc, (RA_LDS void *)(Kd + ii * ROWS * D), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)vsrc, (RA_LDS void *)(Vd + ii * ROWS * D), 16, 0, 0);
+        int g = c + r;
+        g = g < n ? g : n - 1;
+        const uint32_t kof = (uint32_t)(g * D + (phys ^ kswz<D>(r)) * 8);
+        const uint32_t vof = (uint32_t)(g * D + (phys ^ vswz(r)) * 8);
+        __builtin_amdgcn_global_load_lds((const void *)(Ksp + kof), (RA_LDS void *)(Kd + ii * ROWS * D), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(Vsp + vof), (RA_LDS void *)(Vd + ii * ROWS * D), 16, 0, 0);
+    }
+}
+
+// Per-lane LDS byte offsets of the MFMA operand reads inside a staged chunk (every other part
+// of an address is an immediate).  K: lane (lg, lr) reads row 16 kt + lr, piece 4 ks + lg, which
+// sits at piece (4 ks + lg) ^ (lr mod P).  V (transposed reads): lane (lg, lr) addresses row
+// 32 kk + 16 h + 4 lg + c and column 16 et + 4 (lr & 3), c = lr >> 2; with et = 4u + v the
+// swizzled 16-byte piece is 2 (4u + (v ^ c)) + ((lr & 3) >> 1).
+template <int D>
+__device__ __forceinline__ void operand_offsets(int lg, int lr, int (&kof)[D / 32], int (&vof)[4]) {
+    constexpr int P = D / 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) kof[ks] = 2 * (lr * D + (((4 * ks + lg) ^ (lr % P)) * 8));
+    const int c = lr >> 2, b = (lr & 3) >> 1, w = lr & 1;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) vof[v] = 2 * ((4 * lg + c) * D + 16 * (v ^ c) + 8 * b + 4 * w);
+}
+
+// Sum / maximum over the 4 lane groups (lanes l, l^16, l^32, l^48) with the gfx950 lane-swap
+// instructions (VALU, no LDS round trip).
+__device__ __forceinline__ float group_max4(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum4(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// One 64-key chunk of a wave's 16 queries (lane (lg, lr): query lr, keys 16kt + 4lg + i).
+// MASK: some key of the chunk lies past the span's end or past some query's position; `lim` is
+// then min(hi, t_query + 1) - k0 for this lane's query (keys at offsets >= lim are masked).
+// Scores stay raw until the exponent: 2^(s * c - m) is one FMA and one v_exp_f32.  The output
+// is rescaled only when some lane's running maximum moved.
+template <int D, bool MASK>
+__device__ __forceinline__ void tile_chunk(const char *Kbytes, const char *Vbytes, const int (&kof)[D / 32],
+                                           const int (&vof)[4], const bf16x8_t (&qb)[D / 32], float &m, float &l,
+                                           f32x4_t (&o)[D / 16], int lim, int lg, float scale_log2) {
+    constexpr int KS = D / 32, ET = D / 16, KT = kChunk / 16;
+    constexpr float NEG = -__builtin_huge_valf();
+    // S^T = K Q^T
+    f32x4_t sc[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        bf16x8_t ka[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            ka[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(Kbytes + kof[ks] + 2 * 16 * kt * D));
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qb[ks], acc, 0, 0, 0);
+        sc[kt] = acc;  // S^T[key 16kt + 4lg + i][query lr]
+    }
+    float cmax = NEG;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (MASK) sc[kt][i] = 16 * kt + 4 * lg + i < lim ? sc[kt][i] : NEG;
+            cmax = fmaxf(cmax, sc[kt][i]);
+        }
+    }
+    const float mn = fmaxf(m, group_max4(cmax) * scale_log2);
+    // (masked chunks only: a query with no valid key so far keeps m = -inf, p = 0)
+    const bool live = !MASK || mn != NEG;
+    const float nmn = live ? -mn : 0.f;
+    const float alpha = live ? __builtin_amdgcn_exp2f(m - mn) : 1.f;  // 0 while m = -inf
+    float psum = 0.f;
+    uint32_t pk[KT][2];  // P as bf16 pairs
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // v_exp_f32 directly: arguments are <= 0 (or -inf), results in [0, 1]
+            pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], scale_log2, nmn));
+            psum += pv[i];
+        }
+        pk[kt][0] = pack_bf16x2(pv[0], pv[1]);
+        pk[kt][1] = pack_bf16x2(pv[2], pv[3]);
+    }
+    l = fmaf(l, alpha, group_sum4(psum));
+    m = live ? mn : m;
+#pragma unroll
+    for (int et = 0; et < ET; ++et) o[et] *= alpha;
+    // O^T += V^T P^T, 32-key steps: K slots 8lg..8lg+7 <-> keys (2kk)16 + 4lg + 0..3 and
+    // (2kk+1)16 + 4lg + 0..3 for both operands
+#pragma unroll
+    for (int kk = 0; kk < KT / 2; ++kk) {
+        const bf16x8_t pb =
+            __builtin_bit_cast(bf16x8_t, make_uint4(pk[2 * kk][0], pk[2 * kk][1], pk[2 * kk + 1][0], pk[2 * kk + 1][1]));
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+            // transposed reads: lane (lg, i) gets V[key][16 et + i] for 4 consecutive keys
+            uint2 vw[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const char *pv_addr = Vbytes + vof[et & 3] + 2 * ((32 * kk + 16 * h) * D + 64 * (et >> 2));
+                vw[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS v4i16_t *)pv_addr));
+            }
+            const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(vw[0].x, vw[0].y, vw[1].x, vw[1].y));
+            o[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[et], 0, 0, 0);
+        }
     }
 }
 
@@ -219,11 +332,9 @@ __global__ void __launch_bounds__(kMfmaThreads) tile_mfma(const uint16_t *__rest
                                                  float scale_log2) {
     constexpr int KS = D / 32;   // k-steps of the QK product
     constexpr int ET = D / 16;   // 16-wide e tiles of the PV product
-    constexpr int KT = kChunk / 16;
-    constexpr int NT = kMfmaThreads, QT = kMfmaQT;
     constexpr float NEG = -__builtin_huge_valf();
-    __shared__ uint16_t Ks[2][kChunk * D];
-    __shared__ uint16_t Vs[2][kChunk * D];
+    // staged chunks: K buffers 0 and 1, then V buffers 0 and 1 (kChunk rows of D bf16 each)
+    __shared__ uint16_t stage[4][kChunk * D];
     __shared__ int64_t row_t[kMfmaTile];
     __shared__ int32_t row_x[kMfmaTile];
     __shared__ unsigned long long tmax_s, tmin_s;
@@ -267,152 +378,76 @@ __global__ void __launch_bounds__(kMfmaThreads) tile_mfma(const uint16_t *__rest
     if (hi > tmax + 1) hi = tmax + 1;
     if (hi > cap) hi = cap;
 
-    // B operand of S^T: this wave's 2 x 16 gathered query rows, all k-steps, in registers
-    bf16x8_t qb[QT][KS];
-    int64_t tq[QT];  // position of query (a, lr); -1 for padding
-#pragma unroll
-    for (int a = 0; a < QT; ++a) {
-        const int r = 16 * QT * wave + 16 * a + lr;
-        const int32_t x = row_x[r];
-        tq[a] = row_t[r];
-        const int64_t rh = x >= 0 ? x / NE : 0;
+    // B operand of S^T: this wave's 16 gathered query rows, all k-steps, in registers
+    bf16x8_t qb[KS];
+    const int r_own = 16 * wave + lr;
+    const int32_t x_own = row_x[r_own];
+    const int64_t tq = row_t[r_own];  // position of this lane's query; -1 for padding
+    {
+        const int64_t rh = x_own >= 0 ? x_own / NE : 0;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 raw = *reinterpret_cast<const uint4 *>(q + rh * D + 32 * ks + 8 * lg);
-            if (x < 0) raw = make_uint4(0, 0, 0, 0);
-            qb[a][ks] = __builtin_bit_cast(bf16x8_t, raw);
+            if (x_own < 0) raw = make_uint4(0, 0, 0, 0);
+            qb[ks] = __builtin_bit_cast(bf16x8_t, raw);
         }
     }
-    float m[QT], l[QT];
-    f32x4_t o[QT][ET];
+    float m = NEG, l = 0.f;
+    f32x4_t o[ET];
 #pragma unroll
-    for (int a = 0; a < QT; ++a) {
-        m[a] = NEG;
-        l[a] = 0.f;
-#pragma unroll
-        for (int et = 0; et < ET; ++et) o[a][et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int et = 0; et < ET; ++et) o[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const uint16_t *Kb = K + sg * cap * D;
-    const uint16_t *Vb = V + sg * cap * D;
-    // double-buffered chunks: the loads of chunk c+1 fly while chunk c is computed
-    if (lo < hi) chunk_load<D>(Kb, Vb, Ks[0], Vs[0], lo, hi, wave, lane);
-    int buf = 0;
-    for (int64_t k0 = lo; k0 < hi; k0 += kChunk, buf ^= 1) {
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of chunk c landed
+    const uint16_t *Ksp = K + (sg * cap + lo) * D;  // the span's first key row
+    const uint16_t *Vsp = V + (sg * cap + lo) * D;
+    const int n_keys = (int)(hi - lo);
+    int kof[KS], vof[4];
+    operand_offsets<D>(lg, lr, kof, vof);
+    // One chunk: wait for its loads (issued one chunk earlier), start the next chunk's loads
+    // into the other buffer, compute.  A chunk needs masks only where it passes the span's end
+    // or some row's position.  The loop is unrolled over the two buffers so that every LDS
+    // address is a per-lane constant plus an immediate offset.
+    // (key offsets from lo are ints: a span has S keys).  Chunks that end by full_end need no
+    // masks; they come first.  The operand offsets carry the buffer: flipping it is an XOR.
+    constexpr int BUF = kChunk * D * 2;  // bytes per staged buffer
+    const int full_end = (int)((tmin + 1 < hi ? tmin + 1 : hi) - lo);
+    const char *Kbytes = reinterpret_cast<const char *>(stage[0]);
+    const char *Vbytes = reinterpret_cast<const char *>(stage[2]);
+    int nb = 1;  // buffer that receives the next chunk
+    auto flip = [&]() {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kof[ks] ^= BUF;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) vof[v] ^= BUF;
+        nb ^= 1;
+    };
+    if (n_keys > 0) chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_keys, wave, lane);
+    int c = 0;
+    for (; c + kChunk <= full_end; c += kChunk) {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of the chunk landed
         __syncthreads();  // everyone's loads landed, and everyone finished reading the other buffer
-        if (k0 + kChunk < hi) chunk_load<D>(Kb, Vb, Ks[buf ^ 1], Vs[buf ^ 1], k0 + kChunk, hi, wave, lane);
-        const uint16_t *Kc = Ks[buf];
-        const uint16_t *Vc = Vs[buf];
-        // a chunk needs masks only where it passes the span's end or some row's position
-        const bool full = (k0 + kChunk <= hi) && (k0 + kChunk - 1 <= tmin);
-
-        // S^T = K Q^T: 4 key tiles x 2 query tiles
-        f32x4_t sc[KT][QT];
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            bf16x8_t ka[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int r = 16 * kt + lr;
-                ka[ks] = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const uint4 *>(&Kc[r * D + (((4 * ks + lg) ^ kswz<D>(r)) * 8)]));
-            }
-#pragma unroll
-            for (int a = 0; a < QT; ++a) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qb[a][ks], acc, 0, 0, 0);
-                sc[kt][a] = acc;  // S^T[key 16kt + 4lg + i][query 16a + lr]
-            }
-        }
-        // online softmax, per query (lane-local) with the max/sum across the 4 lane groups
-        uint32_t pk[QT][KT][2];  // P as bf16 pairs: [a][kt][i/2]
-#pragma unroll
-        for (int a = 0; a < QT; ++a) {
-            float cmax = NEG;
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float z = sc[kt][a][i] * scale_log2;
-                    if (!full) {
-                        const int64_t p = k0 + 16 * kt + 4 * lg + i;
-                        z = (p < hi && p <= tq[a]) ? z : NEG;
-                    }
-                    sc[kt][a][i] = z;
-                    cmax = fmaxf(cmax, z);
-                }
-            }
-            cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-            cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-            const float mn = fmaxf(m[a], cmax);
-            const bool live = mn != NEG;
-            // v_exp_f32 directly: arguments are <= 0, results in [0, 1] (tiny ones may flush to 0)
-            const float alpha = live ? __builtin_amdgcn_exp2f(m[a] - mn) : 1.f;
-            float psum = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                float pv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pv[i] = live ? __builtin_amdgcn_exp2f(sc[kt][a][i] - mn) : 0.f;
-                    psum += pv[i];
-                }
-                pk[a][kt][0] = pack_bf16x2(pv[0], pv[1]);
-                pk[a][kt][1] = pack_bf16x2(pv[2], pv[3]);
-            }
-            psum += __shfl_xor(psum, 16);
-            psum += __shfl_xor(psum, 32);
-            l[a] = l[a] * alpha + psum;
-            m[a] = mn;
-#pragma unroll
-            for (int et = 0; et < ET; ++et) o[a][et] *= alpha;
-        }
-        // O^T += V^T P^T, 32-key steps: K slots 8lg..8lg+7 <-> keys (2kk)16 + 4lg + 0..3 and
-        // (2kk+1)16 + 4lg + 0..3 for both operands
-#pragma unroll
-        for (int kk = 0; kk < KT / 2; ++kk) {
-            bf16x8_t pb[QT];
-#pragma unroll
-            for (int a = 0; a < QT; ++a) {
-                const uint4 raw = make_uint4(pk[a][2 * kk][0], pk[a][2 * kk][1], pk[a][2 * kk + 1][0], pk[a][2 * kk + 1][1]);
-                pb[a] = __builtin_bit_cast(bf16x8_t, raw);
-            }
-#pragma unroll
-            for (int et = 0; et < ET; ++et) {
-                // transposed reads: lane (lg, i) gets V[key][16 et + i] for 4 consecutive keys; the
-                // 16 lanes of a group address rows base + j/4, columns 16 et + 4 (j % 4)
-                uint32_t vw[4];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int r = 32 * kk + 16 * h + 4 * lg + (lr >> 2);
-                    const int col = 16 * et + 4 * (lr & 3);
-                    const int addr = r * D + (((col >> 3) ^ vswz(r)) << 3) + (col & 7);
-                    const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS v4i16_t *)(Vc + addr));
-                    vw[2 * h] = (uint32_t)(uint16_t)t[0] | ((uint32_t)(uint16_t)t[1] << 16);
-                    vw[2 * h + 1] = (uint32_t)(uint16_t)t[2] | ((uint32_t)(uint16_t)t[3] << 16);
-                }
-                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(vw[0], vw[1], vw[2], vw[3]));
-#pragma unroll
-                for (int a = 0; a < QT; ++a) o[a][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[a], o[a][et], 0, 0, 0);
-            }
-        }
+        if (c + kChunk < n_keys) chunk_load<D>(Ksp, Vsp, stage[nb], stage[2 + nb], c + kChunk, n_keys, wave, lane);
+        tile_chunk<D, false>(Kbytes, Vbytes, kof, vof, qb, m, l, o, kChunk, lg, scale_log2);
+        flip();
+    }
+    for (; c < n_keys; c += kChunk) {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (c + kChunk < n_keys) chunk_load<D>(Ksp, Vsp, stage[nb], stage[2 + nb], c + kChunk, n_keys, wave, lane);
+        int64_t lim = (hi < tq + 1 ? hi : tq + 1) - (lo + c);
+        lim = lim < 0 ? 0 : (lim > kChunk ? kChunk : lim);
+        tile_chunk<D, true>(Kbytes, Vbytes, kof, vof, qb, m, l, o, (int)lim, lg, scale_log2);
+        flip();
     }
 
     // records: (m, l, o[d]) per valid row; lane (lg, lr) holds o[16et + 4lg + i] of query lr
-#pragma unroll
-    for (int a = 0; a < QT; ++a) {
-        const int32_t x = row_x[16 * QT * wave + 16 * a + lr];
-        if (x < 0) continue;
-        float *rec = records + (int64_t)x * record_floats(D);
+    if (x_own >= 0) {
+        float *rec = records + (int64_t)x_own * record_floats(D);
 #pragma unroll
         for (int et = 0; et < ET; ++et)
-            *reinterpret_cast<float4 *>(rec + 4 + 16 * et + 4 * lg) =
-                make_float4(o[a][et][0], o[a][et][1], o[a][et][2], o[a][et][3]);
+            *reinterpret_cast<float4 *>(rec + 4 + 16 * et + 4 * lg) = make_float4(o[et][0], o[et][1], o[et][2], o[et][3]);
         if (lg == 0) {
-            rec[0] = m[a];
-            rec[1] = l[a];
+            rec[0] = m;
+            rec[1] = l;
         }
     }
 }

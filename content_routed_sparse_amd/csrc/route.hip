@@ -30,29 +30,14 @@ __global__ void __launch_bounds__(256) route_valu(const T *__restrict__ q, const
                                                   int64_t stride, int Hq, int Hkv, int G, int S, int W, int B,
                                                   int64_t max_spans, int64_t max_pos) {
     constexpr int LPR = D / 8, RPI = 64 / LPR, STEPS = 16 / RPI, N = STEPS * 8, KEEP = N / LPR;
+    // all kernel arguments in one round trip (otherwise some are fetched only where first used)
+    asm volatile("" ::"s"(q), "s"(row_seq), "s"(row_pos), "s"(mean), "s"(scores), "s"(stride), "s"(Hq), "s"(Hkv),
+                 "s"(G), "s"(S), "s"(W), "s"(B), "s"(max_spans), "s"(max_pos));
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane % LPR, rr = lane / LPR;
     const int rg = blockIdx.x;
     const int64_t row = rg / Hkv;
     const int g = rg % Hkv;
-    int64_t t = row_pos[row];
-    t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
-    int seq = row_seq[row];
-    seq = seq < 0 ? 0 : (seq >= B ? B - 1 : seq);
-    const int64_t r = num_routable(t, S, W);
-    const int64_t jw = (int64_t)blockIdx.y * 64 + wave * 16;  // this wave's first span
-    if (jw >= r) return;
-    const float *mbase = mean + ((int64_t)seq * Hkv + g) * max_spans * D;
-    // every load of the block (summaries and the first 8 heads' queries) is issued before any
-    // use and pinned there: one memory round trip instead of one per load
-    float4 mraw[STEPS][2];
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        int64_t n = jw + s * RPI + rr;
-        n = n < r ? n : r - 1;
-        mraw[s][0] = *reinterpret_cast<const float4 *>(mbase + n * D + c * 8);
-        mraw[s][1] = *reinterpret_cast<const float4 *>(mbase + n * D + c * 8 + 4);
-    }
     constexpr int QV = sizeof(T) == 2 ? 1 : 2;  // 16-byte pieces per head slice of 8 elements
     uint4 qraw[8][QV];
     auto load_q = [&](int hc) {
@@ -64,7 +49,27 @@ __global__ void __launch_bounds__(256) route_valu(const T *__restrict__ q, const
             for (int v = 0; v < QV; ++v) qraw[h][v] = qp[v];
         }
     };
+    // the row's position and sequence together with the first 8 heads' queries (which do not
+    // depend on them): one round trip
+    const int64_t t_raw = row_pos[row];
+    const int seq_raw = row_seq[row];
     load_q(0);
+    asm volatile("" ::"s"(t_raw), "s"(seq_raw));
+    const int64_t t = t_raw < 0 ? 0 : (t_raw > max_pos ? max_pos : t_raw);
+    const int seq = seq_raw < 0 ? 0 : (seq_raw >= B ? B - 1 : seq_raw);
+    const int64_t r = num_routable(t, S, W);
+    const int64_t jw = (int64_t)blockIdx.y * 64 + wave * 16;  // this wave's first span
+    if (jw >= r) return;
+    const float *mbase = mean + ((int64_t)seq * Hkv + g) * max_spans * D;
+    // then every summary load of the wave, issued before any use and pinned there
+    float4 mraw[STEPS][2];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        int64_t n = jw + s * RPI + rr;
+        n = n < r ? n : r - 1;
+        mraw[s][0] = *reinterpret_cast<const float4 *>(mbase + n * D + c * 8);
+        mraw[s][1] = *reinterpret_cast<const float4 *>(mbase + n * D + c * 8 + 4);
+    }
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int s = 0; s < STEPS; ++s)

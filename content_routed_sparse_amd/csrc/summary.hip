@@ -23,6 +23,9 @@ __global__ void __launch_bounds__(256) summary_kernel(const T *__restrict__ K, f
                                                       const int64_t *__restrict__ new_len, int Hkv, int S,
                                                       int64_t cap, int64_t max_spans, int u_base, int U) {
     __shared__ float stage[kStageTokens][D];
+    // all kernel arguments in one round trip (otherwise some are fetched only where first used)
+    asm volatile("" ::"s"(K), "s"(mean), "s"(run_sum), "s"(old_len), "s"(new_len), "s"(Hkv), "s"(S), "s"(cap),
+                 "s"(max_spans), "s"(u_base), "s"(U));
     const int unit = blockIdx.x;
     const int u = u_base + unit % U;
     const int bg = unit / U;  // sequence * Hkv + kv head
@@ -31,7 +34,7 @@ __global__ void __launch_bounds__(256) summary_kernel(const T *__restrict__ K, f
     if (hi > cap) hi = cap;
     if (lo < 0) lo = 0;
     if (lo >= hi) return;
-    const int64_t j = lo / S + u;
+    const int64_t j = div_nonneg(lo, S) + u;
     const int64_t p0 = j * S > lo ? j * S : lo;
     int64_t p1 = j * S + S;
     if (p1 > hi) p1 = hi;

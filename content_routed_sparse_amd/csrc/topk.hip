@@ -38,26 +38,32 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
                                                    int64_t n_rowheads, int Hq, int k, int S, int W, int64_t max_pos) {
     __shared__ uint64_t cand[4][64];
     __shared__ uint32_t cidx[4][64];
+    // all kernel arguments in one round trip (otherwise some are fetched only where first used)
+    asm volatile("" ::"s"(scores), "s"(stride), "s"(row_pos), "s"(sel), "s"(n_rowheads), "s"(Hq), "s"(k), "s"(S),
+                 "s"(W), "s"(max_pos));
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t rh = (int64_t)blockIdx.x * (blockDim.x / 64) + wave;
     if (rh >= n_rowheads) return;
-    int64_t t = row_pos[rh / Hq];
-    t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
-    const int64_t r = num_routable(t, S, W);
     const float *srow = scores + rh * stride;
     int32_t *out = sel + rh * k;
-    const int m = (int)(r < k ? r : k);
 
-    // unconditional loads from clamped indices (a conditional load would be issued and waited
-    // for one at a time); every valid key is > 0, invalid candidates get key 0
+    // The row's position and its scores in one round trip: the score loads do not wait for r
+    // (indices are clamped to the row's stride, which bounds r; entries j >= r are masked
+    // below).  Unconditional loads: a conditional load would be issued and waited for alone.
+    const int64_t t_raw = row_pos[rh / Hq];
     uint64_t key[PER_LANE];
     float sv[PER_LANE];
-    const int64_t jmax = r > 0 ? r - 1 : 0;
+    const int64_t jmax = stride - 1;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) {
         const int64_t j = lane + 64 * i;
         sv[i] = srow[j < jmax ? j : jmax];
     }
+    asm volatile("" ::: "memory");
+    const int64_t t = t_raw < 0 ? 0 : (t_raw > max_pos ? max_pos : t_raw);
+    const int64_t r = num_routable(t, S, W);
+    const int m = (int)(r < k ? r : k);
+    // every valid key is > 0, invalid candidates get key 0
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) {
         const int64_t j = lane + 64 * i;
