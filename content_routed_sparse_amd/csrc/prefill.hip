@@ -14,7 +14,8 @@
 // Workspace (all offsets 256-byte aligned):
 //   counts[n_exp+1], offsets[n_exp+1], tile_off[n_exp+1]   int32
 //   local[n_ent], list[n_ent]                               int32   (n_ent = n_rowheads * NE)
-//   tiles[max_tiles]                                        int2    (expert, first entry)
+//   list_t[n_ent]                                           int64   (position of the entry's row)
+//   tiles[max_tiles]                                        int4    (expert, first entry, entries)
 //   records[n_ent]                                          float x (4 + d)
 #include "common.h"
 #include "kernels.h"
@@ -29,7 +30,7 @@ namespace {
 
 struct PrefillLayout {
     int64_t n_exp, n_ent, max_tiles, span_slots;
-    size_t off_counts, off_offsets, off_tile_off, off_local, off_list, off_tiles, off_records, total;
+    size_t off_counts, off_offsets, off_tile_off, off_local, off_list, off_list_t, off_tiles, off_records, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -48,7 +49,8 @@ PrefillLayout prefill_layout(const RowArgs &a) {
     L.off_tile_off = o; o = align256(o + (L.n_exp + 1) * 4);
     L.off_local = o;    o = align256(o + L.n_ent * 4);
     L.off_list = o;     o = align256(o + L.n_ent * 4);
-    L.off_tiles = o;    o = align256(o + L.max_tiles * 8);
+    L.off_list_t = o;   o = align256(o + L.n_ent * 8);
+    L.off_tiles = o;    o = align256(o + L.max_tiles * 16);
     L.off_records = o;  o = align256(o + (size_t)L.n_ent * record_floats(a.d) * 4);
     L.total = o;
     return L;
@@ -204,7 +206,8 @@ __global__ void __launch_bounds__(1024) scan_kernel(const int32_t *__restrict__ 
 
 __global__ void scatter_kernel(const int32_t *__restrict__ sel, const int32_t *__restrict__ row_seq,
                                const int64_t *__restrict__ row_pos, const int32_t *__restrict__ offsets,
-                               const int32_t *__restrict__ local, int32_t *__restrict__ list, int64_t n_ent, int NE,
+                               const int32_t *__restrict__ local, int32_t *__restrict__ list,
+                               int64_t *__restrict__ list_t, int64_t n_ent, int NE,
                                int Hq, int Hkv, int G, int S, int k, int W, int B, int64_t max_pos,
                                int64_t span_slots) {
     const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -223,15 +226,19 @@ __global__ void scatter_kernel(const int32_t *__restrict__ sel, const int32_t *_
     entry_span(sel, rh, e, k, t, S, W, j);
     const int64_t expert = ((int64_t)seq * Hkv + g) * span_slots + j;
     list[offsets[expert] + slot] = (int32_t)x;
+    list_t[offsets[expert] + slot] = t;
 }
 
-__global__ void tiles_kernel(const int32_t *__restrict__ counts, const int32_t *__restrict__ tile_off,
-                             int2 *__restrict__ tiles, int64_t n_exp, int MT) {
+// Tile descriptors: (expert, first entry in the list, entries in the tile).
+__global__ void tiles_kernel(const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
+                             const int32_t *__restrict__ tile_off, int4 *__restrict__ tiles, int64_t n_exp, int MT) {
     const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (x >= n_exp) return;
     const int32_t c = counts[x];
     const int32_t base = tile_off[x];
-    for (int32_t i = 0; i * MT < c; ++i) tiles[base + i] = make_int2((int32_t)x, i * MT);
+    const int32_t first = offsets[x];
+    for (int32_t i = 0; i * MT < c; ++i)
+        tiles[base + i] = make_int4((int32_t)x, first + i * MT, c - i * MT < MT ? c - i * MT : MT, 0);
 }
 
 }  // namespace
@@ -250,7 +257,8 @@ hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const 
     int32_t *tile_off = (int32_t *)(w + L.off_tile_off);
     int32_t *local = (int32_t *)(w + L.off_local);
     int32_t *list = (int32_t *)(w + L.off_list);
-    int2 *tiles = (int2 *)(w + L.off_tiles);
+    int64_t *list_t = (int64_t *)(w + L.off_list_t);
+    int4 *tiles = (int4 *)(w + L.off_tiles);
     float *records = (float *)(w + L.off_records);
     const int NE = a.k + max_window_spans(a.S, a.W);
     const int MT = prefill_tile_rows(a);
@@ -267,13 +275,14 @@ hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const 
     }
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, tile_off, L.n_exp, MT);
     hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)ceil_div(L.n_ent, 256)), dim3(256), 0, st, sel, a.row_seq,
-                       a.row_pos, offsets, local, list, L.n_ent, NE, a.Hq, a.Hkv, a.G, a.S, a.k, a.W, a.B, a.max_pos,
+                       a.row_pos, offsets, local, list, list_t, L.n_ent, NE, a.Hq, a.Hkv, a.G, a.S, a.k, a.W, a.B,
+                       a.max_pos,
                        L.span_slots);
-    hipLaunchKernelGGL(tiles_kernel, dim3((unsigned)ceil_div(L.n_exp, 256)), dim3(256), 0, st, counts, tile_off, tiles,
-                       L.n_exp, MT);
+    hipLaunchKernelGGL(tiles_kernel, dim3((unsigned)ceil_div(L.n_exp, 256)), dim3(256), 0, st, counts, offsets,
+                       tile_off, tiles, L.n_exp, MT);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    TileArgs ta{a, K, V, counts, offsets, tile_off, list, tiles, records, L.n_exp, L.max_tiles, L.span_slots, NE};
+    TileArgs ta{a, K, V, tile_off, list, list_t, tiles, records, L.n_exp, L.max_tiles, L.span_slots, NE};
     e = launch_prefill_tiles(ta, st);
     if (e != hipSuccess) return e;
     return launch_combine(a, records, sel, out, 1, a.S, st);

@@ -8,8 +8,9 @@ namespace ra {
 struct TileArgs {
     RowArgs a;
     const void *K, *V;
-    const int32_t *counts, *offsets, *tile_off, *list;
-    const int2 *tiles;
+    const int32_t *tile_off, *list;  // tile count at tile_off[n_exp]; entries
+    const int64_t *list_t;           // the entries' row positions
+    const int4 *tiles;               // (expert, first entry, entries)
     float *records;
     int64_t n_exp, max_tiles, span_slots;
     int NE;

@@ -48,26 +48,23 @@ __device__ __forceinline__ void to_f32(const uint4 &raw, float *f, float) {
 constexpr int kValuTile = 16;
 
 template <typename T, int D>
-__global__ void __launch_bounds__(256) tile_valu(const T *__restrict__ q, const int64_t *__restrict__ row_pos,
-                                                 const T *__restrict__ K, const T *__restrict__ V,
-                                                 const int32_t *__restrict__ counts,
-                                                 const int32_t *__restrict__ offsets,
-                                                 const int32_t *__restrict__ tile_off,
-                                                 const int32_t *__restrict__ list, const int2 *__restrict__ tiles,
+__global__ void __launch_bounds__(256) tile_valu(const T *__restrict__ q, const T *__restrict__ K,
+                                                 const T *__restrict__ V, const int32_t *__restrict__ tile_off,
+                                                 const int32_t *__restrict__ list,
+                                                 const int64_t *__restrict__ list_t, const int4 *__restrict__ tiles,
                                                  float *__restrict__ records, int64_t n_exp, int64_t span_slots,
-                                                 int NE, int Hq, int Hkv, int S, int64_t cap, int64_t max_pos,
-                                                 float scale_log2) {
+                                                 int NE, int S, int64_t cap, float scale_log2) {
     using L = WaveLayout<T, D>;
     constexpr int EPL = L::EPL, LPR = L::LPR, RPI = L::RPI, KPW = L::KPW, STEPS = L::STEPS;
     const int64_t tile = blockIdx.x;
     if (tile >= tile_off[n_exp]) return;
-    const int2 tl = tiles[tile];
+    const int4 tl = tiles[tile];
     const int64_t expert = tl.x;
-    const int count = counts[expert];
-    const int n = count - tl.y < kValuTile ? count - tl.y : kValuTile;
+    const int n = tl.z;
     const int64_t j = expert % span_slots;
     const int64_t sg = expert / span_slots;  // sequence * Hkv + kv head
-    const int32_t *entries = list + offsets[expert] + tl.y;
+    const int32_t *entries = list + tl.y;
+    const int64_t *entries_t = list_t + tl.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = lane % LPR, rr = lane / LPR;
     const T *Kb = K + sg * cap * D;
@@ -76,9 +73,7 @@ __global__ void __launch_bounds__(256) tile_valu(const T *__restrict__ q, const 
     for (int i = wave; i < n; i += 4) {
         const int64_t x = entries[i];
         const int64_t rh = x / NE;
-        const int64_t row = rh / Hq;
-        int64_t t = row_pos[row];
-        t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
+        const int64_t t = entries_t[i];
         const int64_t lo = j * S;
         int64_t hi = lo + S < t + 1 ? lo + S : t + 1;
         if (hi > cap) hi = cap;
@@ -179,10 +174,13 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 // contiguous per wave instruction), with the 16-byte pieces of each row permuted by an XOR so
 // that the MFMA operand reads do not collide on banks:
 //   K: piece p of row r at position p ^ (r mod P), P = D / 8 pieces per row;
-//   V: piece p of row r at position p ^ 2 (r mod 4).
+//   V: piece p of row r at position p ^ (2 (r mod 4) + 8 ((r / 4) mod 2)) for D = 128 (the last
+//      term moves rows 4..7 of every 8 to the other half of the banks: a transposed read serves
+//      lanes that address rows r and r + 4 in the same cycle), p ^ 2 (r mod 4) for D = 64.
 template <int D>
 __device__ __forceinline__ int kswz(int r) { return r % (D / 8); }
-__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
+template <int D>
+__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3) + (D >= 128 ? 8 * ((r >> 2) & 1) : 0); }
 
 // Issue the direct global -> LDS loads of the chunk at key offset c (from the span's first key,
 // whose K and V rows start at Ksp, Vsp) into (Kd, Vd); rows at or past `n` (the span's keys in
@@ -201,7 +199,7 @@ __device__ __forceinline__ void chunk_load(const uint16_t *Ksp, const uint16_t *
         int g = c + r;
         g = g < n ? g : n - 1;
         const uint32_t kof = (uint32_t)(g * D + (phys ^ kswz<D>(r)) * 8);
-        const uint32_t vof = (uint32_t)(g * D + (phys ^ vswz(r)) * 8);
+        const uint32_t vof = (uint32_t)(g * D + (phys ^ vswz<D>(r)) * 8);
         __builtin_amdgcn_global_load_lds((const void *)(Ksp + kof), (RA_LDS void *)(Kd + ii * ROWS * D), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const void *)(Vsp + vof), (RA_LDS void *)(Vd + ii * ROWS * D), 16, 0, 0);
     }
@@ -211,18 +209,22 @@ __device__ __forceinline__ void chunk_load(const uint16_t *Ksp, const uint16_t *
 // of an address is an immediate).  K: lane (lg, lr) reads row 16 kt + lr, piece 4 ks + lg, which
 // sits at piece (4 ks + lg) ^ (lr mod P).  V (transposed reads): lane (lg, lr) addresses row
 // 32 kk + 16 h + 4 lg + c and column 16 et + 4 (lr & 3), c = lr >> 2; with et = 4u + v the
-// swizzled 16-byte piece is 2 (4u + (v ^ c)) + ((lr & 3) >> 1).
+// swizzled 16-byte piece is 2 (4 (u ^ e) + (v ^ c)) + ((lr & 3) >> 1), e = lg & 1 for D = 128
+// (0 for D = 64).  vof[u][v] holds the offset of column group et = 4u + v.
 template <int D>
-__device__ __forceinline__ void operand_offsets(int lg, int lr, int (&kof)[D / 32], int (&vof)[4]) {
+__device__ __forceinline__ void operand_offsets(int lg, int lr, int (&kof)[D / 32], int (&vof)[D / 64][4]) {
     constexpr int P = D / 8;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) kof[ks] = 2 * (lr * D + (((4 * ks + lg) ^ (lr % P)) * 8));
-    const int c = lr >> 2, b = (lr & 3) >> 1, w = lr & 1;
+    const int c = lr >> 2, b = (lr & 3) >> 1, w = lr & 1, e = D >= 128 ? (lg & 1) : 0;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) vof[v] = 2 * ((4 * lg + c) * D + 16 * (v ^ c) + 8 * b + 4 * w);
+    for (int u = 0; u < D / 64; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            vof[u][v] = 2 * ((4 * lg + c) * D + 8 * (2 * (4 * (u ^ e) + (v ^ c)) + b) + 4 * w);
 }
 
-// Sum / maximum over the 4 lane groups (lanes l, l^16, l^32, l^48) with the gfx950 lane-swap
+// Maximum over the 4 lane groups (lanes l, l^16, l^32, l^48) with the gfx950 lane-swap
 // instructions (VALU, no LDS round trip).
 __device__ __forceinline__ float group_max4(float x) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -230,24 +232,29 @@ __device__ __forceinline__ float group_max4(float x) {
     const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float group_sum4(float x) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 
 // One 64-key chunk of a wave's 16 queries (lane (lg, lr): query lr, keys 16kt + 4lg + i).
 // MASK: some key of the chunk lies past the span's end or past some query's position; `lim` is
 // then min(hi, t_query + 1) - k0 for this lane's query (keys at offsets >= lim are masked).
-// Scores stay raw until the exponent: 2^(s * c - m) is one FMA and one v_exp_f32.  The output
-// is rescaled only when some lane's running maximum moved.
+// Scores stay raw until the exponent: 2^(s * c - m) is one FMA and one v_exp_f32.
+// No rescaling: the reference maximum m of a query is fixed at the maximum of its first valid
+// keys, and later weights 2^(s c - m) may exceed 1 -- the same partial state, written relative
+// to a smaller m.  Should a score exceed m by more than 2^kJumpLog2 (`jump`), the tile is run
+// again with m set to the largest score seen (`mseen`), so weights never exceed 2^kJumpLog2.
+// Row sums l = sum_k P[q][k] come from the matrix core: an extra 16-row A tile whose row 0 is
+// all ones (`ones`) gives them in row 0 of `lsum` (lanes with lg = 0), in the same bf16 weights
+// that the P.V product uses.
+constexpr float kJumpLog2 = 32.f;
+
 template <int D, bool MASK>
-__device__ __forceinline__ void tile_chunk(const char *Kbytes, const char *Vbytes, const int (&kof)[D / 32],
-                                           const int (&vof)[4], const bf16x8_t (&qb)[D / 32], float &m, float &l,
+__device__ __forceinline__ void tile_chunk(const uint16_t *Kc, const uint16_t *Vc, const int (&kof)[D / 32],
+                                           const int (&vof)[D / 64][4], const bf16x8_t (&qb)[D / 32],
+                                           const bf16x8_t &ones, float &m, float &mseen, bool &jump, f32x4_t &lsum,
                                            f32x4_t (&o)[D / 16], int lim, int lg, float scale_log2) {
     constexpr int KS = D / 32, ET = D / 16, KT = kChunk / 16;
     constexpr float NEG = -__builtin_huge_valf();
+    const char *Kbytes = reinterpret_cast<const char *>(Kc);
+    const char *Vbytes = reinterpret_cast<const char *>(Vc);
     // S^T = K Q^T
     f32x4_t sc[KT];
 #pragma unroll
@@ -270,29 +277,20 @@ __device__ __forceinline__ void tile_chunk(const char *Kbytes, const char *Vbyte
             cmax = fmaxf(cmax, sc[kt][i]);
         }
     }
-    const float mn = fmaxf(m, group_max4(cmax) * scale_log2);
-    // (masked chunks only: a query with no valid key so far keeps m = -inf, p = 0)
-    const bool live = !MASK || mn != NEG;
-    const float nmn = live ? -mn : 0.f;
-    const float alpha = live ? __builtin_amdgcn_exp2f(m - mn) : 1.f;  // 0 while m = -inf
-    float psum = 0.f;
+    const float mx = group_max4(cmax) * scale_log2;
+    mseen = fmaxf(mseen, mx);
+    jump = jump || (m != NEG && mx > m + kJumpLog2);
+    m = m == NEG ? mx : m;  // a query's first valid keys fix m (its o and l are still 0)
+    const float nm = (!MASK || m != NEG) ? -m : 0.f;
     uint32_t pk[KT][2];  // P as bf16 pairs
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         float pv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // v_exp_f32 directly: arguments are <= 0 (or -inf), results in [0, 1]
-            pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], scale_log2, nmn));
-            psum += pv[i];
-        }
+        for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], scale_log2, nm));
         pk[kt][0] = pack_bf16x2(pv[0], pv[1]);
         pk[kt][1] = pack_bf16x2(pv[2], pv[3]);
     }
-    l = fmaf(l, alpha, group_sum4(psum));
-    m = live ? mn : m;
-#pragma unroll
-    for (int et = 0; et < ET; ++et) o[et] *= alpha;
     // O^T += V^T P^T, 32-key steps: K slots 8lg..8lg+7 <-> keys (2kk)16 + 4lg + 0..3 and
     // (2kk+1)16 + 4lg + 0..3 for both operands
 #pragma unroll
@@ -305,12 +303,13 @@ __device__ __forceinline__ void tile_chunk(const char *Kbytes, const char *Vbyte
             uint2 vw[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const char *pv_addr = Vbytes + vof[et & 3] + 2 * ((32 * kk + 16 * h) * D + 64 * (et >> 2));
+                const char *pv_addr = Vbytes + vof[et >> 2][et & 3] + 2 * (32 * kk + 16 * h) * D;
                 vw[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS v4i16_t *)pv_addr));
             }
             const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(vw[0].x, vw[0].y, vw[1].x, vw[1].y));
             o[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[et], 0, 0, 0);
         }
+        lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, lsum, 0, 0, 0);
     }
 }
 
@@ -321,70 +320,65 @@ __device__ __forceinline__ void tile_chunk(const char *Kbytes, const char *Vbyte
 // registers: its 32-key K dimension is ordered as the lanes hold it (keys 4lg..4lg+3 of two
 // 16-key tiles per lane group), and V^T is read from LDS in the same order.
 template <int D>
-__global__ void __launch_bounds__(kMfmaThreads) tile_mfma(const uint16_t *__restrict__ q, const int64_t *__restrict__ row_pos,
-                                                 const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-                                                 const int32_t *__restrict__ counts,
-                                                 const int32_t *__restrict__ offsets,
-                                                 const int32_t *__restrict__ tile_off,
-                                                 const int32_t *__restrict__ list, const int2 *__restrict__ tiles,
-                                                 float *__restrict__ records, int64_t n_exp, int64_t span_slots,
-                                                 int NE, int Hq, int S, int64_t cap, int64_t max_pos,
-                                                 float scale_log2) {
+__global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) tile_mfma(const uint16_t *__restrict__ q,
+                                                          const uint16_t *__restrict__ K,
+                                                          const uint16_t *__restrict__ V,
+                                                          const int32_t *__restrict__ tile_off,
+                                                          const int32_t *__restrict__ list,
+                                                          const int64_t *__restrict__ list_t,
+                                                          const int4 *__restrict__ tiles,
+                                                          float *__restrict__ records, int64_t n_exp,
+                                                          int64_t span_slots, int NE, int S, int64_t cap,
+                                                          float scale_log2, int64_t n_blocks) {
     constexpr int KS = D / 32;   // k-steps of the QK product
     constexpr int ET = D / 16;   // 16-wide e tiles of the PV product
     constexpr float NEG = -__builtin_huge_valf();
-    // staged chunks: K buffers 0 and 1, then V buffers 0 and 1 (kChunk rows of D bf16 each)
+    // staged chunks: K buffers 0 and 1, then V buffers 0 and 1 (kChunk rows of D bf16 each).  One
+    // array: the compiler then waits for a chunk's LDS loads before the next LDS read, so the
+    // loads of chunk c + 1 land before chunk c is computed.  (Measured: letting them overlap the
+    // computation of chunk c, with four distinct arrays, is slower.)
     __shared__ uint16_t stage[4][kChunk * D];
-    __shared__ int64_t row_t[kMfmaTile];
-    __shared__ int32_t row_x[kMfmaTile];
-    __shared__ unsigned long long tmax_s, tmin_s;
+    __shared__ int redo_s[kMfmaWaves];
+    __shared__ unsigned long long wmax_s[kMfmaWaves], wmin_s[kMfmaWaves];
 
+    // all kernel arguments in one round trip (otherwise some are fetched only where first used)
+    asm volatile("" ::"s"(q), "s"(K), "s"(V), "s"(tile_off), "s"(list), "s"(list_t), "s"(tiles), "s"(records),
+                 "s"(n_exp), "s"(span_slots), "s"(NE), "s"(S), "s"(cap), "s"(scale_log2), "s"(n_blocks));
+    const int64_t tile = xcd_tile(blockIdx.x, n_blocks);
+    // the tile count and this tile's descriptor in one round trip (a descriptor past the count is
+    // stale but in bounds: max_tiles of them are allocated)
     const int64_t total = tile_off[n_exp];
-    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int4 tl = tiles[tile];
+    asm volatile("" ::"s"(total), "s"(tl.x), "s"(tl.y), "s"(tl.z));
     if (tile >= total) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 4, lr = lane & 15;
-    const int2 tl = tiles[tile];
     const int64_t expert = tl.x;
-    const int count = counts[expert];
-    const int n = count - tl.y < kMfmaTile ? count - tl.y : kMfmaTile;
+    const int n = tl.z;  // entries in the tile (<= kMfmaTile)
     const int64_t j = expert % span_slots;
     const int64_t sg = expert / span_slots;
-    const int32_t *entries = list + offsets[expert] + tl.y;
     const int64_t lo = j * S;
+    const uint16_t *Ksp = K + (sg * cap + lo) * D;  // the span's first key row
+    const uint16_t *Vsp = V + (sg * cap + lo) * D;
+    const int n_span = (int)(cap - lo < S ? cap - lo : S);  // keys of the span inside the cache
 
-    if (tid == 0) {
-        tmax_s = 0;
-        tmin_s = ~0ull;
-    }
-    if (tid < kMfmaTile) {
-        int32_t x = -1;
-        int64_t t = -1;
-        if (tid < n) {
-            x = entries[tid];
-            t = row_pos[(x / NE) / Hq];
-            t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
-        }
-        row_x[tid] = x;
-        row_t[tid] = t;
-    }
-    __syncthreads();
-    if (tid < n) {
-        atomicMax(&tmax_s, (unsigned long long)row_t[tid]);
-        atomicMin(&tmin_s, (unsigned long long)row_t[tid]);
-    }
-    __syncthreads();
-    const int64_t tmax = (int64_t)tmax_s, tmin = (int64_t)tmin_s;
-    int64_t hi = lo + S;  // keys of the span used by the tile: [lo, hi)
-    if (hi > tmax + 1) hi = tmax + 1;
-    if (hi > cap) hi = cap;
+    // One round trip: the tile's entries and their positions, this lane's own row (for its
+    // query), and the first chunk of keys -- loaded up to the span's end, since the rows'
+    // positions that may cut it short are not known yet (rows past them are masked).
+    // (unconditional loads from clamped indices, masked afterwards: a load under a condition is
+    // waited for on its own)
+    const int i_blk = tid < n ? tid : n - 1;
+    const int r_own = 16 * wave + lr;
+    const int i_own = r_own < n ? r_own : n - 1;
+    const int64_t t_blk = list_t[tl.y + i_blk];
+    const int32_t x_ld = list[tl.y + i_own];
+    const int64_t t_ld = list_t[tl.y + i_own];
+    const int32_t x_own = r_own < n ? x_ld : -1;
+    const int64_t tq = r_own < n ? t_ld : -1;  // position of this lane's query
 
     // B operand of S^T: this wave's 16 gathered query rows, all k-steps, in registers
     bf16x8_t qb[KS];
-    const int r_own = 16 * wave + lr;
-    const int32_t x_own = row_x[r_own];
-    const int64_t tq = row_t[r_own];  // position of this lane's query; -1 for padding
     {
-        const int64_t rh = x_own >= 0 ? x_own / NE : 0;
+        const int64_t rh = x_ld / NE;  // (a padding row loads a valid row, then zero)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 raw = *reinterpret_cast<const uint4 *>(q + rh * D + 32 * ks + 8 * lg);
@@ -392,51 +386,98 @@ __global__ void __launch_bounds__(kMfmaThreads) tile_mfma(const uint16_t *__rest
             qb[ks] = __builtin_bit_cast(bf16x8_t, raw);
         }
     }
-    float m = NEG, l = 0.f;
-    f32x4_t o[ET];
+    // the first chunk's LDS loads fly with the query loads (issued after them: the compiler waits
+    // for everything before using a load's register while LDS loads are outstanding)
+    chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_span, wave, lane);
+    // the tile's first and last positions (wave reductions, then across the waves in LDS)
+    {
+        unsigned long long vmax = tid < n ? (unsigned long long)t_blk : 0ull;
+        unsigned long long vmin = tid < n ? (unsigned long long)t_blk : ~0ull;
+        vmax = wave_max_u64(vmax);
+        vmin = ~wave_max_u64(~vmin);
+        if (lane == 0) {
+            wmax_s[wave] = vmax;
+            wmin_s[wave] = vmin;
+        }
+    }
+    __syncthreads();
+    unsigned long long tmax_u = 0ull, tmin_u = ~0ull;
 #pragma unroll
-    for (int et = 0; et < ET; ++et) o[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < kMfmaWaves; ++w) {
+        tmax_u = wmax_s[w] > tmax_u ? wmax_s[w] : tmax_u;
+        tmin_u = wmin_s[w] < tmin_u ? wmin_s[w] : tmin_u;
+    }
+    const int64_t tmax = (int64_t)tmax_u, tmin = (int64_t)tmin_u;
+    int64_t hi = lo + S;  // keys of the span used by the tile: [lo, hi)
+    if (hi > tmax + 1) hi = tmax + 1;
+    if (hi > cap) hi = cap;
 
-    const uint16_t *Ksp = K + (sg * cap + lo) * D;  // the span's first key row
-    const uint16_t *Vsp = V + (sg * cap + lo) * D;
+    // A operand of the row sums: row 0 all ones (lanes with lr = 0), the other rows zero
+    const uint32_t one2 = lr == 0 ? 0x3F803F80u : 0u;
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(one2, one2, one2, one2));
+
     const int n_keys = (int)(hi - lo);
-    int kof[KS], vof[4];
+    int kof[KS], vof[D / 64][4];
     operand_offsets<D>(lg, lr, kof, vof);
     // One chunk: wait for its loads (issued one chunk earlier), start the next chunk's loads
     // into the other buffer, compute.  A chunk needs masks only where it passes the span's end
-    // or some row's position.  The loop is unrolled over the two buffers so that every LDS
-    // address is a per-lane constant plus an immediate offset.
-    // (key offsets from lo are ints: a span has S keys).  Chunks that end by full_end need no
-    // masks; they come first.  The operand offsets carry the buffer: flipping it is an XOR.
-    constexpr int BUF = kChunk * D * 2;  // bytes per staged buffer
+    // or some row's position; chunks that end by full_end need none, and they come first (key
+    // offsets from lo are ints: a span has S keys).  The operand offsets carry the buffer:
+    // flipping it is an XOR.
     const int full_end = (int)((tmin + 1 < hi ? tmin + 1 : hi) - lo);
-    const char *Kbytes = reinterpret_cast<const char *>(stage[0]);
-    const char *Vbytes = reinterpret_cast<const char *>(stage[2]);
+    constexpr int BUF = kChunk * D * 2;  // bytes per staged buffer
+    const uint16_t *Kst = stage[0], *Vst = stage[2];
     int nb = 1;  // buffer that receives the next chunk
+    auto begin = [&](int c) {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of chunk c landed
+        __syncthreads();  // everyone's loads landed, and everyone finished reading the other buffer
+        if (c + kChunk < n_keys) chunk_load<D>(Ksp, Vsp, stage[nb], stage[2 + nb], c + kChunk, n_keys, wave, lane);
+    };
     auto flip = [&]() {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kof[ks] ^= BUF;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) vof[v] ^= BUF;
+        for (int v = 0; v < 4 * (D / 64); ++v) vof[v / 4][v % 4] ^= BUF;
         nb ^= 1;
     };
-    if (n_keys > 0) chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_keys, wave, lane);
-    int c = 0;
-    for (; c + kChunk <= full_end; c += kChunk) {
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of the chunk landed
-        __syncthreads();  // everyone's loads landed, and everyone finished reading the other buffer
-        if (c + kChunk < n_keys) chunk_load<D>(Ksp, Vsp, stage[nb], stage[2 + nb], c + kChunk, n_keys, wave, lane);
-        tile_chunk<D, false>(Kbytes, Vbytes, kof, vof, qb, m, l, o, kChunk, lg, scale_log2);
-        flip();
-    }
-    for (; c < n_keys; c += kChunk) {
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (c + kChunk < n_keys) chunk_load<D>(Ksp, Vsp, stage[nb], stage[2 + nb], c + kChunk, n_keys, wave, lane);
+    auto lim_of = [&](int c) {
         int64_t lim = (hi < tq + 1 ? hi : tq + 1) - (lo + c);
-        lim = lim < 0 ? 0 : (lim > kChunk ? kChunk : lim);
-        tile_chunk<D, true>(Kbytes, Vbytes, kof, vof, qb, m, l, o, (int)lim, lg, scale_log2);
-        flip();
+        return (int)(lim < 0 ? 0 : (lim > kChunk ? kChunk : lim));
+    };
+    float m = NEG, mseen = NEG;
+    f32x4_t lsum, o[ET];
+    for (int pass = 0; pass < 2; ++pass) {
+        // pass 1 (rare): some score exceeded its reference by more than 2^kJumpLog2 in pass 0;
+        // redo the tile with every reference at the largest score seen
+        m = pass == 0 ? NEG : mseen;
+        bool jump = false;
+        lsum = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int et = 0; et < ET; ++et) o[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (pass > 0) {  // (pass 0: the first chunk was loaded with the tile's entries)
+            __syncthreads();  // everyone is done with the buffers
+            if (nb == 0) flip();  // back to buffer 0
+            chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_span, wave, lane);
+        }
+        int c = 0;
+        for (; c + kChunk <= full_end; c += kChunk) {
+            begin(c);
+            tile_chunk<D, false>(Kst, Vst, kof, vof, qb, ones, m, mseen, jump, lsum, o, kChunk, lg, scale_log2);
+            flip();
+        }
+        for (; c < n_keys; c += kChunk) {
+            begin(c);
+            tile_chunk<D, true>(Kst, Vst, kof, vof, qb, ones, m, mseen, jump, lsum, o, lim_of(c), lg, scale_log2);
+            flip();
+        }
+        // block-wide decision (every wave takes the same path through the chunk loads)
+        if (lane == 0) redo_s[wave] = __ballot(jump) != 0 ? 1 : 0;
+        __syncthreads();
+        int redo = 0;
+#pragma unroll
+        for (int w = 0; w < kMfmaWaves; ++w) redo |= redo_s[w];
+        __syncthreads();
+        if (!redo) break;
     }
 
     // records: (m, l, o[d]) per valid row; lane (lg, lr) holds o[16et + 4lg + i] of query lr
@@ -447,7 +488,7 @@ __global__ void __launch_bounds__(kMfmaThreads) tile_mfma(const uint16_t *__rest
             *reinterpret_cast<float4 *>(rec + 4 + 16 * et + 4 * lg) = make_float4(o[et][0], o[et][1], o[et][2], o[et][3]);
         if (lg == 0) {
             rec[0] = m;
-            rec[1] = l;
+            rec[1] = lsum[0];
         }
     }
 }
@@ -456,9 +497,9 @@ template <int D>
 hipError_t mfma_launch(const TileArgs &t, hipStream_t st) {
     const RowArgs &a = t.a;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    hipLaunchKernelGGL((tile_mfma<D>), dim3((unsigned)t.max_tiles), dim3(kMfmaThreads), 0, st, (const uint16_t *)a.q, a.row_pos,
-                       (const uint16_t *)t.K, (const uint16_t *)t.V, t.counts, t.offsets, t.tile_off, t.list, t.tiles,
-                       t.records, t.n_exp, t.span_slots, t.NE, a.Hq, a.S, a.cap, a.max_pos, scale_log2);
+    hipLaunchKernelGGL((tile_mfma<D>), dim3((unsigned)t.max_tiles), dim3(kMfmaThreads), 0, st, (const uint16_t *)a.q,
+                       (const uint16_t *)t.K, (const uint16_t *)t.V, t.tile_off, t.list, t.list_t, t.tiles, t.records,
+                       t.n_exp, t.span_slots, t.NE, a.S, a.cap, scale_log2, t.max_tiles);
     return hipGetLastError();
 }
 
@@ -466,9 +507,9 @@ template <typename T, int D>
 hipError_t valu_launch(const TileArgs &t, hipStream_t st) {
     const RowArgs &a = t.a;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    hipLaunchKernelGGL((tile_valu<T, D>), dim3((unsigned)t.max_tiles), dim3(256), 0, st, (const T *)a.q, a.row_pos,
-                       (const T *)t.K, (const T *)t.V, t.counts, t.offsets, t.tile_off, t.list, t.tiles, t.records,
-                       t.n_exp, t.span_slots, t.NE, a.Hq, a.Hkv, a.S, a.cap, a.max_pos, scale_log2);
+    hipLaunchKernelGGL((tile_valu<T, D>), dim3((unsigned)t.max_tiles), dim3(256), 0, st, (const T *)a.q,
+                       (const T *)t.K, (const T *)t.V, t.tile_off, t.list, t.list_t, t.tiles, t.records, t.n_exp,
+                       t.span_slots, t.NE, a.S, a.cap, scale_log2);
     return hipGetLastError();
 }
 

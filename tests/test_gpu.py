@@ -91,6 +91,29 @@ def test_k_all_spans_equals_dense_causal():
     assert worst <= 2e-2
 
 
+def test_prefill_outlier_keys_force_the_second_pass():
+    """Keys of norm far above the rest, planted past a span's first 64 keys: some rows then see a
+    score more than 2^32 (log2 units) above the maximum of their first keys, and the tile kernel
+    recomputes those tiles with the final maximum.  The result must still match the oracle."""
+    w = small("prefill_8k_on_1m", num_q_heads=8, num_kv_heads=2, span_size=256, window=256, top_k=4)
+    prefix, chunk = 3072, 256
+    c = Case(w, [prefix + chunk])
+    kh, vh = c.host[0]
+    big = np.uint16(0x41F0)  # bf16 30.0
+    planted = [(g, p) for g in range(2) for p in (100, 700, 1000, 1900, 2500)]  # offsets >= 64 in their spans
+    for g, p in planted:
+        kh[g, p, :] = big
+        c.K[0, g, p, :] = torch.full((w.head_dim,), 30.0, dtype=torch.bfloat16)
+    c._problems.clear()
+    c.summarize([0], [prefix], prefix)
+    rows, q = c.chunk_rows(0, prefix, chunk)
+    c.summarize([prefix], [prefix + chunk], chunk)
+    c.attend(rows, ra.RA_OP_PREFILL)
+    c.check_summaries(0)
+    stats = c.check([0] * chunk, np.arange(prefix, prefix + chunk), q, np.arange(chunk))
+    assert_stats(stats, True)
+
+
 def test_prefill_chunking_is_bitwise_invariant():
     w = small("prefill_8k_on_1m", span_size=32, window=32, top_k=4)
     _, _, out1, sel1 = run_prefill(w, 1000, 600, pieces=1)
