@@ -189,17 +189,7 @@ def main():
     bytes_step = float(np.mean([per_seq[i % NC] for i in timed_ev]))
     achieved = bytes_step / (attn_ms * 1e-3) / 1e9
 
-    # counter-measured HBM bytes per launch (profiles/), valid only for the kernel sources they
-    # were taken on
-    traffic = None
-    tf = os.path.join(ROOT, "profiles", "decode_attn_decode_1m_traffic.json")
-    if os.path.exists(tf):
-        rec = json.load(open(tf))
-        h = hashlib.sha256()
-        for f in rec.get("sources", []):
-            h.update(open(os.path.join(ROOT, f), "rb").read())
-        if rec.get("source_sha256") == h.hexdigest():
-            traffic = rec.get("bytes_per_launch")
+    traffic = counter_traffic("routed_attn_decode_1m")
 
     result = {
         "metric": METRIC,
@@ -217,7 +207,7 @@ def main():
         "config": {"workload": "decode_1m", "context": L, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "span": w.span_size, "top_k": w.top_k, "window": w.window, "batch": 1,
                    "rotated_sequences": NC, "hip_graphs": bool(args.graph)},
-        "roofline": {"bound": "hbm", "kernel": "routed_attn_decode (decode_attn + combine)",
+        "roofline": {"bound": "hbm", "kernel": "routed_attn_decode (decode_attn + combine_block)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(bytes_step), "avg_launch_ms": round(attn_ms, 5)},
@@ -241,6 +231,19 @@ def main():
         result["prefill"] = bench_prefill(args.prefill_steps)
 
     print(json.dumps(result), flush=True)
+
+
+def counter_traffic(tag):
+    """HBM bytes per call measured with rocprofv3 counters (profiles/<tag>_traffic.json), or
+    None when the kernel sources changed since they were taken."""
+    tf = os.path.join(ROOT, "profiles", tag + "_traffic.json")
+    if not os.path.exists(tf):
+        return None
+    rec = json.load(open(tf))
+    h = hashlib.sha256()
+    for f in rec.get("sources", []):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return rec.get("bytes_per_launch") if rec.get("source_sha256") == h.hexdigest() else None
 
 
 def bench_prefill(steps):
@@ -309,7 +312,7 @@ def bench_prefill(steps):
         "value": round(n / (step_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(step_ms, 4),
         "roofline": {"bound": "mfma", "kernel": "routed_attn_prefill (dispatch + bf16 MFMA tiles + merge)",
                      "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
-                     "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "frac": round(tflops / 2500.0, 4), "traffic": counter_traffic("routed_attn_prefill_8k_on_1m"),
                      "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
         "step_flops": attn_flops + route_flops,
         "step_tflops": round((attn_flops + route_flops) / (step_ms * 1e-3) / 1e12, 1),
