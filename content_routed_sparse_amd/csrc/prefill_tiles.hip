@@ -246,17 +246,12 @@ __device__ __forceinline__ float group_max4(float x) {
 // that the P.V product uses.
 constexpr float kJumpLog2 = 32.f;
 
-template <int D, bool MASK>
-__device__ __forceinline__ void tile_chunk(const uint16_t *Kc, const uint16_t *Vc, const int (&kof)[D / 32],
-                                           const int (&vof)[D / 64][4], const bf16x8_t (&qb)[D / 32],
-                                           const bf16x8_t &ones, float &m, float &mseen, bool &jump, f32x4_t &lsum,
-                                           f32x4_t (&o)[D / 16], int lim, int lg, float scale_log2) {
-    constexpr int KS = D / 32, ET = D / 16, KT = kChunk / 16;
-    constexpr float NEG = -__builtin_huge_valf();
+// S^T = K Q^T for one chunk: sc[kt][i] = S^T[key 16kt + 4lg + i][query lr].
+template <int D>
+__device__ __forceinline__ void qk_chunk(const uint16_t *Kc, const int (&kof)[D / 32], const bf16x8_t (&qb)[D / 32],
+                                         f32x4_t (&sc)[kChunk / 16]) {
+    constexpr int KS = D / 32, KT = kChunk / 16;
     const char *Kbytes = reinterpret_cast<const char *>(Kc);
-    const char *Vbytes = reinterpret_cast<const char *>(Vc);
-    // S^T = K Q^T
-    f32x4_t sc[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         bf16x8_t ka[KS];
@@ -266,8 +261,16 @@ __device__ __forceinline__ void tile_chunk(const uint16_t *Kc, const uint16_t *V
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qb[ks], acc, 0, 0, 0);
-        sc[kt] = acc;  // S^T[key 16kt + 4lg + i][query lr]
+        sc[kt] = acc;
     }
+}
+
+// The chunk's weights 2^(s c - m) as bf16 pairs (pk[kt][i/2]), with the reference bookkeeping.
+template <bool MASK>
+__device__ __forceinline__ void softmax_chunk(f32x4_t (&sc)[kChunk / 16], int lim, int lg, float scale_log2, float &m,
+                                              float &mseen, bool &jump, uint32_t (&pk)[kChunk / 16][2]) {
+    constexpr int KT = kChunk / 16;
+    constexpr float NEG = -__builtin_huge_valf();
     float cmax = NEG;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
@@ -282,7 +285,6 @@ __device__ __forceinline__ void tile_chunk(const uint16_t *Kc, const uint16_t *V
     jump = jump || (m != NEG && mx > m + kJumpLog2);
     m = m == NEG ? mx : m;  // a query's first valid keys fix m (its o and l are still 0)
     const float nm = (!MASK || m != NEG) ? -m : 0.f;
-    uint32_t pk[KT][2];  // P as bf16 pairs
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         float pv[4];
@@ -291,8 +293,16 @@ __device__ __forceinline__ void tile_chunk(const uint16_t *Kc, const uint16_t *V
         pk[kt][0] = pack_bf16x2(pv[0], pv[1]);
         pk[kt][1] = pack_bf16x2(pv[2], pv[3]);
     }
-    // O^T += V^T P^T, 32-key steps: K slots 8lg..8lg+7 <-> keys (2kk)16 + 4lg + 0..3 and
-    // (2kk+1)16 + 4lg + 0..3 for both operands
+}
+
+// O^T += V^T P^T and the row sums, 32-key steps: K slots 8lg..8lg+7 <-> keys (2kk)16 + 4lg + 0..3
+// and (2kk+1)16 + 4lg + 0..3 for both operands.
+template <int D>
+__device__ __forceinline__ void pv_chunk(const uint16_t *Vc, const int (&vof)[D / 64][4],
+                                         const uint32_t (&pk)[kChunk / 16][2], const bf16x8_t &ones, f32x4_t &lsum,
+                                         f32x4_t (&o)[D / 16]) {
+    constexpr int ET = D / 16, KT = kChunk / 16;
+    const char *Vbytes = reinterpret_cast<const char *>(Vc);
 #pragma unroll
     for (int kk = 0; kk < KT / 2; ++kk) {
         const bf16x8_t pb =
@@ -311,6 +321,18 @@ __device__ __forceinline__ void tile_chunk(const uint16_t *Kc, const uint16_t *V
         }
         lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, lsum, 0, 0, 0);
     }
+}
+
+template <int D, bool MASK>
+__device__ __forceinline__ void tile_chunk(const uint16_t *Kc, const uint16_t *Vc, const int (&kof)[D / 32],
+                                           const int (&vof)[D / 64][4], const bf16x8_t (&qb)[D / 32],
+                                           const bf16x8_t &ones, float &m, float &mseen, bool &jump, f32x4_t &lsum,
+                                           f32x4_t (&o)[D / 16], int lim, int lg, float scale_log2) {
+    f32x4_t sc[kChunk / 16];
+    qk_chunk<D>(Kc, kof, qb, sc);
+    uint32_t pk[kChunk / 16][2];
+    softmax_chunk<MASK>(sc, lim, lg, scale_log2, m, mseen, jump, pk);
+    pv_chunk<D>(Vc, vof, pk, ones, lsum, o);
 }
 
 // Transposed formulation.  S^T = K Q^T puts keys on the MFMA rows and queries on the columns,
