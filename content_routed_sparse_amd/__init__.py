@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "libroutedattn.so")
 RA_F32, RA_BF16 = 0, 1
 RA_OP_DECODE, RA_OP_PREFILL = 0, 1
 EXPORTED = ("span_summary_update", "route_scores", "topk_spans", "routed_attn_decode", "routed_attn_prefill",
-            "ra_workspace_bytes", "ra_status_string", "ra_last_error")
+            "attn_dense_causal", "ra_workspace_bytes", "ra_status_string", "ra_last_error")
 
 
 class RoutedAttnError(RuntimeError):
@@ -62,6 +62,7 @@ def lib():
             "topk_spans": [CP, RP, P, I64, P, P],
             "routed_attn_decode": [CP, RP, P, P, P, P, P, SZ, P],
             "routed_attn_prefill": [CP, RP, P, P, P, P, P, SZ, P],
+            "attn_dense_causal": [CP, RP, P, P, P, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -211,12 +212,21 @@ def _args_attn(cfg, rows, k_cache, v_cache, sel, out, workspace, stream=None):
             _dev(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream)), (c, r)
 
 
+def _args_dense(cfg, rows, k_cache, v_cache, out, stream=None):
+    c, r = cfg.c(), _rows(cfg, rows)
+    n = rows.q.shape[0]
+    return (ctypes.byref(c), ctypes.byref(r), _dev(k_cache, cfg.torch_dtype, _kv_shape(cfg), "k_cache"),
+            _dev(v_cache, cfg.torch_dtype, _kv_shape(cfg), "v_cache"),
+            _dev(out, torch.float32, (n, cfg.num_q_heads, cfg.head_dim), "out"), _stream(stream)), (c, r)
+
+
 _BUILDERS = {
     "span_summary_update": _args_span_summary_update,
     "route_scores": _args_route_scores,
     "topk_spans": _args_topk_spans,
     "routed_attn_decode": _args_attn,
     "routed_attn_prefill": _args_attn,
+    "attn_dense_causal": _args_dense,
 }
 
 
@@ -283,6 +293,12 @@ def routed_attn_prefill(cfg, rows, k_cache, v_cache, sel, out, workspace, stream
     """Exact attention over window + selected spans, rows grouped span by span (many rows)."""
     args, _keep = _args_attn(cfg, rows, k_cache, v_cache, sel, out, workspace, stream)
     _check(lib().routed_attn_prefill(*args))
+
+
+def attn_dense_causal(cfg, rows, k_cache, v_cache, out, stream=None):
+    """Exact attention over every key at or before each row's position (bf16; no workspace)."""
+    args, _keep = _args_dense(cfg, rows, k_cache, v_cache, out, stream)
+    _check(lib().attn_dense_causal(*args))
 
 
 class Pipeline:

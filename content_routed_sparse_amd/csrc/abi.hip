@@ -187,6 +187,22 @@ ra_status routed_attn_prefill(const ra_config *cfg, const ra_rows *rows, const v
         "routed_attn_prefill launch");
 }
 
+ra_status attn_dense_causal(const ra_config *cfg, const ra_rows *rows, const void *k_cache, const void *v_cache,
+                            float *out, void *stream) {
+    ra_status s = check_config(cfg);
+    if (s) return s;
+    if ((s = check_rows(cfg, rows))) return s;
+    if (cfg->dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "attn_dense_causal takes bf16 inputs only");
+    if (cfg->capacity * (int64_t)cfg->head_dim >= kMaxGrid)
+        return fail(RA_EUNSUPPORTED, "capacity * head_dim must be below 2^31 for attn_dense_causal");
+    if (rows->n_rows == 0) return ok();
+    if (!k_cache || !v_cache || !out) return fail(RA_EINVAL, "NULL K, V or out");
+    const ra::RowArgs a = row_args(cfg, rows);
+    const int RT = 128 / a.G;
+    if (a.Hkv * ra::ceil_div(a.n_rows, RT) >= kMaxGrid) return fail(RA_EUNSUPPORTED, "too many rows");
+    return hip_status(ra::launch_dense(a, k_cache, v_cache, out, (hipStream_t)stream), "attn_dense_causal launch");
+}
+
 size_t ra_workspace_bytes(const ra_config *cfg, int32_t op, int64_t n_rows, int64_t max_pos) {
     if (check_config(cfg)) return 0;
     if (op != RA_OP_DECODE && op != RA_OP_PREFILL) {

@@ -38,4 +38,7 @@ size_t prefill_workspace_bytes(const RowArgs &a);
 hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out,
                           void *ws, hipStream_t st);
 
+// Dense causal attention (bf16): every key at or before each row's position; no workspace.
+hipError_t launch_dense(const RowArgs &a, const void *K, const void *V, float *out, hipStream_t st);
+
 }  // namespace ra

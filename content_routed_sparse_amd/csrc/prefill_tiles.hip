@@ -535,9 +535,184 @@ hipError_t valu_launch(const TileArgs &t, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Dense causal attention (every key at or before the row's position: the "k = all spans" case
+// of the method, and the reference the routed path is measured against).  The same chunk step
+// as the routed tiles, with the span replaced by the whole prefix [0, t].
+//
+// Tile = (kv head g, RT = 128 / G consecutive rows of the call): its entries are the RT rows x
+// G query heads of the kv head (entry 16 w + i of the block belongs to wave w), so all entries
+// share the keys.  Rows of different sequences in one tile are handled in successive passes
+// (increasing sequence id; one pass for a chunk of one sequence): entries of other sequences
+// are padding during a pass.  Each entry's whole softmax state stays in registers, so the
+// output o / l is written directly: no workspace and no merge.
+template <int D>
+__global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, const int64_t *__restrict__ row_pos,
+           const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, float *__restrict__ out, int64_t n_rows,
+           int Hq, int Hkv, int G, int RT, int B, int64_t cap, int64_t max_pos, float scale_log2, int64_t n_blocks) {
+    constexpr int KS = D / 32, ET = D / 16;
+    constexpr float NEG = -__builtin_huge_valf();
+    __shared__ uint16_t stage[4][kChunk * D];  // (one array: see tile_mfma)
+    __shared__ int redo_s[kMfmaWaves];
+    __shared__ unsigned long long wred_s[3][kMfmaWaves];
+    asm volatile("" ::"s"(q), "s"(row_seq), "s"(row_pos), "s"(K), "s"(V), "s"(out), "s"(n_rows), "s"(Hq), "s"(Hkv),
+                 "s"(G), "s"(RT), "s"(B), "s"(cap), "s"(max_pos), "s"(scale_log2), "s"(n_blocks));
+    // tiles ordered (kv head, row block); XCD x takes a contiguous range of them (shared L2)
+    const int64_t tile = xcd_tile(blockIdx.x, n_blocks);
+    const int64_t n_rb = (n_rows + RT - 1) / RT;
+    const int g = (int)(tile / n_rb);
+    const int64_t r0 = (tile % n_rb) * RT;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 4, lr = lane & 15;
+
+    // this lane's entry (the B operand column lr of wave `wave`)
+    const int e = 16 * wave + lr;
+    const int64_t row_e = r0 + e / G;
+    const bool valid = e < RT * G && row_e < n_rows;
+    const int64_t row_c = valid ? row_e : r0;  // (a padding entry loads a valid row, then zero)
+    const int hq = g * G + (valid ? e % G : 0);
+    const int seq_raw = row_seq[row_c];
+    const int64_t t_raw = row_pos[row_c];
+    bf16x8_t qraw[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        qraw[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(q + (row_c * Hq + hq) * D + 32 * ks + 8 * lg));
+    const int seq_e = seq_raw < 0 ? 0 : (seq_raw >= B ? B - 1 : seq_raw);
+    const int64_t t_e = t_raw < 0 ? 0 : (t_raw > max_pos ? max_pos : t_raw);
+
+    int kof[KS], vof[D / 64][4];
+    operand_offsets<D>(lg, lr, kof, vof);
+    const uint32_t one2 = lr == 0 ? 0x3F803F80u : 0u;
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(one2, one2, one2, one2));
+    constexpr int BUF = kChunk * D * 2;
+
+    // block-wide min/max of three 64-bit values (wave reductions, then across the waves in LDS)
+    auto block_reduce = [&](unsigned long long a_min, unsigned long long b_min, unsigned long long c_max,
+                            unsigned long long &ra, unsigned long long &rb, unsigned long long &rc) {
+        a_min = ~wave_max_u64(~a_min);
+        b_min = ~wave_max_u64(~b_min);
+        c_max = wave_max_u64(c_max);
+        __syncthreads();  // (the previous reduction's values have been read)
+        if (lane == 0) {
+            wred_s[0][wave] = a_min;
+            wred_s[1][wave] = b_min;
+            wred_s[2][wave] = c_max;
+        }
+        __syncthreads();
+        ra = ~0ull, rb = ~0ull, rc = 0ull;
+#pragma unroll
+        for (int w = 0; w < kMfmaWaves; ++w) {
+            ra = wred_s[0][w] < ra ? wred_s[0][w] : ra;
+            rb = wred_s[1][w] < rb ? wred_s[1][w] : rb;
+            rc = wred_s[2][w] > rc ? wred_s[2][w] : rc;
+        }
+    };
+
+    int nb = 1;  // buffer that receives the next chunk; the operand offsets point to the other
+    auto flip = [&]() {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kof[ks] ^= BUF;
+#pragma unroll
+        for (int v = 0; v < 4 * (D / 64); ++v) vof[v / 4][v % 4] ^= BUF;
+        nb ^= 1;
+    };
+    int64_t prev_seq = -1;
+    for (;;) {
+        // the next sequence of the tile (smallest id above the last one done), its rows' first and
+        // last positions
+        unsigned long long nseq, tmin_u, tmax_u;
+        const bool pend = valid && seq_e > prev_seq;
+        block_reduce(pend ? (unsigned long long)seq_e : ~0ull, ~0ull, 0ull, nseq, tmin_u, tmax_u);
+        if (nseq == ~0ull) break;
+        const int seq = (int)nseq;
+        const bool active = valid && seq_e == seq;
+        block_reduce(~0ull, active ? (unsigned long long)t_e : ~0ull, active ? (unsigned long long)t_e : 0ull, nseq,
+                     tmin_u, tmax_u);
+        const int64_t tmin = (int64_t)tmin_u, tmax = (int64_t)tmax_u;
+        int64_t hi = tmax + 1;
+        if (hi > cap) hi = cap;
+        const int n_keys = (int)hi;
+        const int full_end = (int)(tmin + 1 < hi ? tmin + 1 : hi);
+        const uint16_t *Ksp = K + ((int64_t)seq * Hkv + g) * cap * D;
+        const uint16_t *Vsp = V + ((int64_t)seq * Hkv + g) * cap * D;
+        bf16x8_t qb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qb[ks] = active ? qraw[ks] : bf16x8_t{};
+        const int64_t tq = active ? t_e : -1;
+
+        auto begin = [&](int c) {
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (c + kChunk < n_keys) chunk_load<D>(Ksp, Vsp, stage[nb], stage[2 + nb], c + kChunk, n_keys, wave, lane);
+        };
+        auto lim_of = [&](int c) {
+            int64_t lim = (hi < tq + 1 ? hi : tq + 1) - c;
+            return (int)(lim < 0 ? 0 : (lim > kChunk ? kChunk : lim));
+        };
+        float m = NEG, mseen = NEG;
+        f32x4_t lsum, o[ET];
+        for (int pass = 0; pass < 2; ++pass) {
+            // pass 1 (rare): a score exceeded its reference by more than 2^kJumpLog2 in pass 0
+            m = pass == 0 ? NEG : mseen;
+            bool jump = false;
+            lsum = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int et = 0; et < ET; ++et) o[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            __syncthreads();  // everyone is done with the buffers
+            if (nb == 0) flip();  // back to buffer 0
+            chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_keys, wave, lane);
+            int c = 0;
+            for (; c + kChunk <= full_end; c += kChunk) {
+                begin(c);
+                tile_chunk<D, false>(stage[0], stage[2], kof, vof, qb, ones, m, mseen, jump, lsum, o, kChunk, lg,
+                                     scale_log2);
+                flip();
+            }
+            for (; c < n_keys; c += kChunk) {
+                begin(c);
+                tile_chunk<D, true>(stage[0], stage[2], kof, vof, qb, ones, m, mseen, jump, lsum, o, lim_of(c), lg,
+                                    scale_log2);
+                flip();
+            }
+            if (lane == 0) redo_s[wave] = __ballot(jump) != 0 ? 1 : 0;
+            __syncthreads();
+            int redo = 0;
+#pragma unroll
+            for (int w = 0; w < kMfmaWaves; ++w) redo |= redo_s[w];
+            if (!redo) break;
+        }
+        // out = o / l; l sits in lane (0, lr): broadcast it to the query's 4 lane groups
+        const float l = __shfl(lsum[0], lr);
+        if (active) {
+            const float inv = 1.f / l;
+            float *dst = out + (row_e * Hq + hq) * D;
+#pragma unroll
+            for (int et = 0; et < ET; ++et)
+                *reinterpret_cast<float4 *>(dst + 16 * et + 4 * lg) =
+                    make_float4(o[et][0] * inv, o[et][1] * inv, o[et][2] * inv, o[et][3] * inv);
+        }
+        prev_seq = seq;
+    }
+}
+
+template <int D>
+hipError_t dense_launch(const RowArgs &a, const void *K, const void *V, float *out, hipStream_t st) {
+    const int RT = kMfmaTile / a.G;
+    const int64_t blocks = a.Hkv * ((a.n_rows + RT - 1) / RT);
+    const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+    hipLaunchKernelGGL((dense_mfma<D>), dim3((unsigned)blocks), dim3(kMfmaThreads), 0, st, (const uint16_t *)a.q,
+                       a.row_seq, a.row_pos, (const uint16_t *)K, (const uint16_t *)V, out, a.n_rows, a.Hq, a.Hkv,
+                       a.G, RT, a.B, a.cap, a.max_pos, scale_log2, blocks);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int prefill_tile_rows(const RowArgs &a) { return a.dtype == RA_BF16 ? kMfmaTile : kValuTile; }
+
+hipError_t launch_dense(const RowArgs &a, const void *K, const void *V, float *out, hipStream_t st) {
+    if (a.n_rows == 0) return hipSuccess;
+    return a.d == 64 ? dense_launch<64>(a, K, V, out, st) : dense_launch<128>(a, K, V, out, st);
+}
 
 hipError_t launch_prefill_tiles(const TileArgs &t, hipStream_t st) {
     const RowArgs &a = t.a;

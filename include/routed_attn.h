@@ -150,6 +150,20 @@ ra_status routed_attn_prefill(const ra_config *cfg, const ra_rows *rows, const v
                               const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
                               void *stream);
 
+/*
+ * attn_dense_causal -- exact softmax attention of each row over every key of its sequence at or
+ * before its position: the brute-force scan that routing replaces (release post, "Key idea"),
+ * and the "k = all spans" case of the method (with k >= r(t) the routed result equals it).  It
+ * is the reference the routed path is measured against.  Rows are taken in tiles of 128 / G
+ * consecutive rows x the G query heads of a kv head; rows of several sequences in one tile are
+ * handled in successive passes, so a call is fastest when rows come grouped by sequence (as a
+ * prefill chunk does).
+ *   Supported: bf16 inputs (RA_EUNSUPPORTED otherwise), capacity * head_dim < 2^31.
+ *   k_cache, v_cache  [batch][Hkv][capacity][d]; out [n_rows][Hq][d] float.  No workspace.
+ */
+ra_status attn_dense_causal(const ra_config *cfg, const ra_rows *rows, const void *k_cache, const void *v_cache,
+                            float *out, void *stream);
+
 /* Workspace bytes needed by routed_attn_decode / routed_attn_prefill (op = ra_op); 0 if the
  * configuration is invalid (ra_last_error then says why). */
 size_t ra_workspace_bytes(const ra_config *cfg, int32_t op, int64_t n_rows, int64_t max_pos);

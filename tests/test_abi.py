@@ -74,6 +74,12 @@ def test_argument_validation_before_launch():
     # summary: max_new beyond capacity
     assert lib.span_summary_update(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, (1 << 20) + 1, None) == 3
     assert lib.span_summary_update(ctypes.byref(c), None, FAKE, FAKE, FAKE, FAKE, 1, None) == 1
+    # dense attention: bf16 only, capacity * d below 2^31, non-NULL buffers
+    c32 = cfg(dtype=ra.RA_F32).c()
+    assert lib.attn_dense_causal(ctypes.byref(c32), ctypes.byref(rows()), FAKE, FAKE, FAKE, None) == 2
+    big = cfg(capacity=1 << 24, max_spans=1 << 14).c()
+    assert lib.attn_dense_causal(ctypes.byref(big), ctypes.byref(rows()), FAKE, FAKE, FAKE, None) == 2
+    assert lib.attn_dense_causal(ctypes.byref(c), ctypes.byref(rows()), FAKE, FAKE, None, None) == 1
 
 
 def test_workspace_sizes():

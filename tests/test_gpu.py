@@ -202,6 +202,87 @@ def test_decode_ignores_repeated_and_out_of_range_entries(G, k):
     log("  repeated/out-of-range entries: max abs %.3g" % worst)
 
 
+DENSE_CASES = [
+    # name, workload, number of rows
+    ("d128_G4", small("ragged_decode_16", batch=3, num_q_heads=8, num_kv_heads=2, span_size=64, window=64, top_k=4,
+                      ragged=(500, 3000)), 70),
+    ("d64_G32", small("ragged_decode_16", batch=2, head_dim=64, num_q_heads=32, num_kv_heads=1, span_size=64,
+                      window=64, top_k=4, ragged=(900, 2000)), 21),
+    ("d128_G3", small("ragged_decode_16", batch=2, num_q_heads=6, num_kv_heads=2, span_size=32, window=32, top_k=4,
+                      ragged=(300, 1500)), 50),
+    ("d128_G1", small("ragged_decode_16", batch=2, num_q_heads=4, num_kv_heads=4, span_size=32, window=32, top_k=4,
+                      ragged=(100, 700)), 140),
+]
+
+
+@pytest.mark.parametrize("name,w,n", DENSE_CASES, ids=[c[0] for c in DENSE_CASES])
+def test_dense_causal_small(name, w, n):
+    """attn_dense_causal against the oracle's dense causal attention, rows of several sequences
+    in random order (several passes per tile), plus one contiguous run of rows."""
+    log("dense case", name)
+    lengths = w.seq_lengths()
+    c = Case(w, lengths)
+    rng = np.random.default_rng(11)
+    seqs = rng.integers(0, c.B, size=n)
+    pos = np.array([rng.integers(0, lengths[s]) for s in seqs])
+    run = np.arange(lengths[0] - 40, lengths[0])  # a chunk-like run of one sequence
+    seqs = np.concatenate([seqs, np.zeros(len(run), dtype=np.int64)])
+    pos = np.concatenate([pos, run])
+    rows, q = c.rows_for(seqs, pos)
+    out = torch.empty(len(seqs), w.num_q_heads, w.head_dim, device="cuda")
+    ra.attn_dense_causal(c.cfg, rows, c.K, c.V, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    worst_abs, worst_rel = 0.0, 0.0
+    for i, (s_, t) in enumerate(zip(seqs, pos)):
+        for h in range(w.num_q_heads):
+            ref = c.problem(int(s_)).dense_row(q[i][h], h, int(t))
+            ma, rel = O.output_errors(got[i, h], ref)
+            worst_abs, worst_rel = max(worst_abs, ma), max(worst_rel, rel)
+    log("  rows=%d max_abs=%.3g max_rel=%.3g" % (len(seqs), worst_abs, worst_rel))
+    assert worst_abs <= O.compare.TOL_ABS["bf16"] and worst_rel <= O.compare.TOL_REL_L2_BF16
+
+
+def test_dense_equals_routed_with_all_spans():
+    """With k >= the number of routable spans the routed prefill is dense causal attention: the
+    two GPU paths agree (both round the weights to bf16 for P.V)."""
+    w = small("prefill_8k_on_1m", num_q_heads=4, num_kv_heads=2, span_size=32, window=32, top_k=64)
+    c, q, out_r, sel = run_prefill(w, 1024, 900)  # at most 60 routable spans < k
+    rows, _ = c.chunk_rows(0, 1024, 900)
+    out_d = torch.empty_like(out_r)
+    ra.attn_dense_causal(c.cfg, rows, c.K, c.V, out_d)
+    torch.cuda.synchronize()
+    diff = (out_d - out_r).abs().max().item()
+    scale = out_r.abs().max().item()
+    log("  dense vs routed(k=all): max abs diff %.3g (max |o| %.3g)" % (diff, scale))
+    assert diff <= max(scale, 0.1) * 2.0 ** -7
+
+
+def test_dense_outlier_keys_force_the_second_pass():
+    w = small("prefill_8k_on_1m", num_q_heads=8, num_kv_heads=2, span_size=256, window=256, top_k=4)
+    L = 2600
+    c = Case(w, [L])
+    kh, _ = c.host[0]
+    for g in range(2):
+        for p in (900, 1700, 2300):  # far past the first chunk of every row
+            kh[g, p, :] = np.uint16(0x41F0)  # bf16 30.0
+            c.K[0, g, p, :] = torch.full((w.head_dim,), 30.0, dtype=torch.bfloat16)
+    c._problems.clear()
+    pos = np.arange(L - 200, L)
+    rows, q = c.rows_for(np.zeros(len(pos), dtype=np.int64), pos)
+    out = torch.empty(len(pos), w.num_q_heads, w.head_dim, device="cuda")
+    ra.attn_dense_causal(c.cfg, rows, c.K, c.V, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    worst = 0.0
+    for i, t in enumerate(pos):
+        for h in range(w.num_q_heads):
+            ma, rel = O.output_errors(got[i, h], c.problem(0).dense_row(q[i][h], h, int(t)))
+            worst = max(worst, ma)
+            assert ma <= O.compare.TOL_ABS["bf16"] and rel <= O.compare.TOL_REL_L2_BF16, (i, h, ma, rel)
+    log("  outliers: max abs %.3g" % worst)
+
+
 def test_empty_rows_are_a_no_op():
     w = small("ragged_decode_16", batch=1, span_size=64, window=64, top_k=8, ragged=(0, 0), decode_len=2000)
     c = Case(w, [2000])
