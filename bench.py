@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--graph", action="store_true", help="replay the step from HIP graphs instead of launching")
     p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     p.add_argument("--prefill-steps", type=int, default=5)
+    p.add_argument("--dense-steps", type=int, default=2,
+                   help="timed calls of dense causal attention on the prefill rows (0: skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 256 MiB device copy (reference kernel for HBM byte counters)")
     return p.parse_args()
@@ -228,7 +230,7 @@ def main():
     if not args.no_prefill:
         del K, V, st
         torch.cuda.empty_cache()
-        result["prefill"] = bench_prefill(args.prefill_steps)
+        result["prefill"] = bench_prefill(args.prefill_steps, args.dense_steps)
 
     print(json.dumps(result), flush=True)
 
@@ -246,7 +248,7 @@ def counter_traffic(tag):
     return rec.get("bytes_per_launch") if rec.get("source_sha256") == h.hexdigest() else None
 
 
-def bench_prefill(steps):
+def bench_prefill(steps, dense_steps=2):
     """Chunked prefill: 8192 new tokens appended to a 1M-token cache (the chunk's K/V are in
     the cache before timing).  A step = span_summary_update of the chunk + route_scores +
     topk_spans + routed_attn_prefill for its 8192 x 32 row-heads."""
@@ -307,6 +309,29 @@ def bench_prefill(steps):
     attn_flops = 4.0 * d * keys.sum() * w.num_q_heads
     route_flops = 2.0 * d * r.astype(np.float64).sum() * w.num_q_heads
     tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+
+    # the same rows with dense causal attention over the whole prefix (the brute-force scan that
+    # routing replaces; its flops are 4 d per (row-head, key <= t))
+    dense = None
+    if dense_steps > 0:
+        out_d = torch.empty_like(out)
+        call = ra.prepare("attn_dense_causal", cfg, rows, K, V, out_d)
+        call()
+        torch.cuda.synchronize()
+        evd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(dense_steps)]
+        for a, b in evd:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = float(np.mean([a.elapsed_time(b) for a, b in evd]))
+        dense_flops = 4.0 * d * (pos + 1).astype(np.float64).sum() * w.num_q_heads
+        dtf = dense_flops / (dense_ms * 1e-3) / 1e12
+        dense = {"kernel": "attn_dense_causal (bf16 MFMA tiles)", "ms_per_call": round(dense_ms, 3),
+                 "tokens_per_s": round(n / (dense_ms * 1e-3), 1), "flops_per_call": dense_flops,
+                 "achieved_tflops": round(dtf, 1), "mfma_frac": round(dtf / 2500.0, 4),
+                 "traffic": counter_traffic("attn_dense_causal_8k_on_1m"),
+                 "routed_attn_speedup": round(dense_ms / attn_ms, 2)}
     return {
         "workload": "prefill_8k_on_1m", "chunk": n, "context": L, "steps": steps,
         "value": round(n / (step_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(step_ms, 4),
@@ -316,6 +341,7 @@ def bench_prefill(steps):
                      "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
         "step_flops": attn_flops + route_flops,
         "step_tflops": round((attn_flops + route_flops) / (step_ms * 1e-3) / 1e12, 1),
+        "dense_causal": dense,
     }
 
 
