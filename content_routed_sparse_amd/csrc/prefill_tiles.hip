@@ -233,6 +233,14 @@ __device__ __forceinline__ float group_max4(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Sum over the 4 lane groups, in a fixed order: (l + l^32) + (l^16 + l^48).
+__device__ __forceinline__ float group_sum4(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // One 64-key chunk of a wave's 16 queries (lane (lg, lr): query lr, keys 16kt + 4lg + i).
 // MASK: some key of the chunk lies past the span's end or past some query's position; `lim` is
 // then min(hi, t_query + 1) - k0 for this lane's query (keys at offsets >= lim are masked).
@@ -241,9 +249,9 @@ __device__ __forceinline__ float group_max4(float x) {
 // keys, and later weights 2^(s c - m) may exceed 1 -- the same partial state, written relative
 // to a smaller m.  Should a score exceed m by more than 2^kJumpLog2 (`jump`), the tile is run
 // again with m set to the largest score seen (`mseen`), so weights never exceed 2^kJumpLog2.
-// Row sums l = sum_k P[q][k] come from the matrix core: an extra 16-row A tile whose row 0 is
-// all ones (`ones`) gives them in row 0 of `lsum` (lanes with lg = 0), in the same bf16 weights
-// that the P.V product uses.
+// Row sums l = sum_k P[q][k] are taken over the same bf16 weights that the P.V product uses:
+// one v_dot2_f32_bf16 against (1, 1) per packed pair, into a per-lane fp32 sum over the lane's
+// own keys (the 4 lane groups of a query are added once, at the end: group_sum4).
 constexpr float kJumpLog2 = 32.f;
 
 // S^T = K Q^T for one chunk: sc[kt][i] = S^T[key 16kt + 4lg + i][query lr].
@@ -295,12 +303,11 @@ __device__ __forceinline__ void softmax_chunk(f32x4_t (&sc)[kChunk / 16], int li
     }
 }
 
-// O^T += V^T P^T and the row sums, 32-key steps: K slots 8lg..8lg+7 <-> keys (2kk)16 + 4lg + 0..3
+// O^T += V^T P^T, 32-key steps: K slots 8lg..8lg+7 <-> keys (2kk)16 + 4lg + 0..3
 // and (2kk+1)16 + 4lg + 0..3 for both operands.
 template <int D>
 __device__ __forceinline__ void pv_chunk(const uint16_t *Vc, const int (&vof)[D / 64][4],
-                                         const uint32_t (&pk)[kChunk / 16][2], const bf16x8_t &ones, f32x4_t &lsum,
-                                         f32x4_t (&o)[D / 16]) {
+                                         const uint32_t (&pk)[kChunk / 16][2], f32x4_t (&o)[D / 16]) {
     constexpr int ET = D / 16, KT = kChunk / 16;
     const char *Vbytes = reinterpret_cast<const char *>(Vc);
 #pragma unroll
@@ -319,20 +326,24 @@ __device__ __forceinline__ void pv_chunk(const uint16_t *Vc, const int (&vof)[D 
             const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(vw[0].x, vw[0].y, vw[1].x, vw[1].y));
             o[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[et], 0, 0, 0);
         }
-        lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, lsum, 0, 0, 0);
     }
 }
 
 template <int D, bool MASK>
 __device__ __forceinline__ void tile_chunk(const uint16_t *Kc, const uint16_t *Vc, const int (&kof)[D / 32],
                                            const int (&vof)[D / 64][4], const bf16x8_t (&qb)[D / 32],
-                                           const bf16x8_t &ones, float &m, float &mseen, bool &jump, f32x4_t &lsum,
+                                           float &m, float &mseen, bool &jump, float &l,
                                            f32x4_t (&o)[D / 16], int lim, int lg, float scale_log2) {
     f32x4_t sc[kChunk / 16];
     qk_chunk<D>(Kc, kof, qb, sc);
     uint32_t pk[kChunk / 16][2];
     softmax_chunk<MASK>(sc, lim, lg, scale_log2, m, mseen, jump, pk);
-    pv_chunk<D>(Vc, vof, pk, ones, lsum, o);
+    const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+#pragma unroll
+    for (int kt = 0; kt < kChunk / 16; ++kt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kt][h]), one2, l, false);
+    pv_chunk<D>(Vc, vof, pk, o);
 }
 
 // Transposed formulation.  S^T = K Q^T puts keys on the MFMA rows and queries on the columns,
@@ -434,10 +445,6 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     if (hi > tmax + 1) hi = tmax + 1;
     if (hi > cap) hi = cap;
 
-    // A operand of the row sums: row 0 all ones (lanes with lr = 0), the other rows zero
-    const uint32_t one2 = lr == 0 ? 0x3F803F80u : 0u;
-    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(one2, one2, one2, one2));
-
     const int n_keys = (int)(hi - lo);
     int kof[KS], vof[D / 64][4];
     operand_offsets<D>(lg, lr, kof, vof);
@@ -467,13 +474,14 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
         return (int)(lim < 0 ? 0 : (lim > kChunk ? kChunk : lim));
     };
     float m = NEG, mseen = NEG;
-    f32x4_t lsum, o[ET];
+    float l;
+    f32x4_t o[ET];
     for (int pass = 0; pass < 2; ++pass) {
         // pass 1 (rare): some score exceeded its reference by more than 2^kJumpLog2 in pass 0;
         // redo the tile with every reference at the largest score seen
         m = pass == 0 ? NEG : mseen;
         bool jump = false;
-        lsum = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        l = 0.f;
 #pragma unroll
         for (int et = 0; et < ET; ++et) o[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (pass > 0) {  // (pass 0: the first chunk was loaded with the tile's entries)
@@ -484,12 +492,12 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
         int c = 0;
         for (; c + kChunk <= full_end; c += kChunk) {
             begin(c);
-            tile_chunk<D, false>(Kst, Vst, kof, vof, qb, ones, m, mseen, jump, lsum, o, kChunk, lg, scale_log2);
+            tile_chunk<D, false>(Kst, Vst, kof, vof, qb, m, mseen, jump, l, o, kChunk, lg, scale_log2);
             flip();
         }
         for (; c < n_keys; c += kChunk) {
             begin(c);
-            tile_chunk<D, true>(Kst, Vst, kof, vof, qb, ones, m, mseen, jump, lsum, o, lim_of(c), lg, scale_log2);
+            tile_chunk<D, true>(Kst, Vst, kof, vof, qb, m, mseen, jump, l, o, lim_of(c), lg, scale_log2);
             flip();
         }
         // block-wide decision (every wave takes the same path through the chunk loads)
@@ -503,6 +511,7 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     }
 
     // records: (m, l, o[d]) per valid row; lane (lg, lr) holds o[16et + 4lg + i] of query lr
+    l = group_sum4(l);
     if (x_own >= 0) {
         float *rec = records + (int64_t)x_own * record_floats(D);
 #pragma unroll
@@ -510,7 +519,7 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
             *reinterpret_cast<float4 *>(rec + 4 + 16 * et + 4 * lg) = make_float4(o[et][0], o[et][1], o[et][2], o[et][3]);
         if (lg == 0) {
             rec[0] = m;
-            rec[1] = lsum[0];
+            rec[1] = l;
         }
     }
 }
@@ -572,17 +581,12 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
     const int hq = g * G + (valid ? e % G : 0);
     const int seq_raw = row_seq[row_c];
     const int64_t t_raw = row_pos[row_c];
-    bf16x8_t qraw[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        qraw[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(q + (row_c * Hq + hq) * D + 32 * ks + 8 * lg));
+    const uint16_t *q_e = q + (row_c * Hq + hq) * D + 8 * lg;  // this lane's part of its query row
     const int seq_e = seq_raw < 0 ? 0 : (seq_raw >= B ? B - 1 : seq_raw);
     const int64_t t_e = t_raw < 0 ? 0 : (t_raw > max_pos ? max_pos : t_raw);
 
     int kof[KS], vof[D / 64][4];
     operand_offsets<D>(lg, lr, kof, vof);
-    const uint32_t one2 = lr == 0 ? 0x3F803F80u : 0u;
-    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(one2, one2, one2, one2));
     constexpr int BUF = kChunk * D * 2;
 
     // block-wide min/max of three 64-bit values (wave reductions, then across the waves in LDS)
@@ -634,9 +638,14 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
         const int full_end = (int)(tmin + 1 < hi ? tmin + 1 : hi);
         const uint16_t *Ksp = K + ((int64_t)seq * Hkv + g) * cap * D;
         const uint16_t *Vsp = V + ((int64_t)seq * Hkv + g) * cap * D;
+        // the query, loaded again for each sequence of the tile (zero for entries of other sequences)
         bf16x8_t qb[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qb[ks] = active ? qraw[ks] : bf16x8_t{};
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 raw = *reinterpret_cast<const uint4 *>(q_e + 32 * ks);
+            if (!active) raw = make_uint4(0, 0, 0, 0);
+            qb[ks] = __builtin_bit_cast(bf16x8_t, raw);
+        }
         const int64_t tq = active ? t_e : -1;
 
         auto begin = [&](int c) {
@@ -649,12 +658,13 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
             return (int)(lim < 0 ? 0 : (lim > kChunk ? kChunk : lim));
         };
         float m = NEG, mseen = NEG;
-        f32x4_t lsum, o[ET];
+        float l;
+        f32x4_t o[ET];
         for (int pass = 0; pass < 2; ++pass) {
             // pass 1 (rare): a score exceeded its reference by more than 2^kJumpLog2 in pass 0
             m = pass == 0 ? NEG : mseen;
             bool jump = false;
-            lsum = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            l = 0.f;
 #pragma unroll
             for (int et = 0; et < ET; ++et) o[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             __syncthreads();  // everyone is done with the buffers
@@ -663,13 +673,13 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
             int c = 0;
             for (; c + kChunk <= full_end; c += kChunk) {
                 begin(c);
-                tile_chunk<D, false>(stage[0], stage[2], kof, vof, qb, ones, m, mseen, jump, lsum, o, kChunk, lg,
+                tile_chunk<D, false>(stage[0], stage[2], kof, vof, qb, m, mseen, jump, l, o, kChunk, lg,
                                      scale_log2);
                 flip();
             }
             for (; c < n_keys; c += kChunk) {
                 begin(c);
-                tile_chunk<D, true>(stage[0], stage[2], kof, vof, qb, ones, m, mseen, jump, lsum, o, lim_of(c), lg,
+                tile_chunk<D, true>(stage[0], stage[2], kof, vof, qb, m, mseen, jump, l, o, lim_of(c), lg,
                                     scale_log2);
                 flip();
             }
@@ -680,8 +690,8 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
             for (int w = 0; w < kMfmaWaves; ++w) redo |= redo_s[w];
             if (!redo) break;
         }
-        // out = o / l; l sits in lane (0, lr): broadcast it to the query's 4 lane groups
-        const float l = __shfl(lsum[0], lr);
+        // out = o / l (l summed over the query's 4 lane groups: every lane holds the total)
+        l = group_sum4(l);
         if (active) {
             const float inv = 1.f / l;
             float *dst = out + (row_e * Hq + hq) * D;
