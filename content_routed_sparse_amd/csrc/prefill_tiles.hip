@@ -145,10 +145,16 @@ __global__ void __launch_bounds__(256) tile_valu(const T *__restrict__ q, const 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMfmaWaves = 8;                   // waves per block, 16 queries each
-constexpr int kMfmaTile = kMfmaWaves * 16;      // entries per tile (128)
+// Each wave computes kQG groups of 16 queries against every staged key: the K and V operands
+// it reads from LDS serve kQG MFMAs each, which sets the LDS bytes per flop (LDS bandwidth, not
+// the matrix core, bounds the chunk step at one group per wave).
+constexpr int kQG = 2;                          // groups of 16 queries per wave
+constexpr int kMfmaWaves = 4;                   // waves per block
+constexpr int kMfmaTile = kMfmaWaves * 16 * kQG;  // entries per tile (128)
 constexpr int kChunk = 64;                      // keys per LDS stage
 constexpr int kMfmaThreads = kMfmaWaves * 64;
+constexpr int kWavesPerEU = kQG == 1 ? 4 : 2;   // register budget: 128 or 256 per lane
+static_assert(kMfmaTile <= kMfmaThreads, "one thread per entry in the tile reductions");
 
 // XCD-aware order: the hardware hands block b to XCD b % 8; give XCD x a contiguous range of
 // the tile list (tiles of one span are consecutive) so that they share its L2.
@@ -185,23 +191,38 @@ __device__ __forceinline__ int vswz(int r) { return 2 * (r & 3) + (D >= 128 ? 8 
 // Issue the direct global -> LDS loads of the chunk at key offset c (from the span's first key,
 // whose K and V rows start at Ksp, Vsp) into (Kd, Vd); rows at or past `n` (the span's keys in
 // use) repeat row n - 1 (masked later).  Each wave instruction fills 1 KB = 1024 / (2 D) rows.
-// Offsets are 32-bit (a span's rows span S * D * 2 bytes), so the loads take a scalar base.
+// Buffer loads: the span is a buffer resource of its n rows, the chunk and row-block offsets are
+// scalar, and a lane's own part of the address (its row in the block, its swizzled piece) is the
+// same for every block of a chunk (the swizzles repeat every 16 rows, a wave's blocks every 16),
+// so a whole chunk costs no vector arithmetic.  Only a chunk that passes row n - 1 clamps rows
+// per lane.
 template <int D>
 __device__ __forceinline__ void chunk_load(const uint16_t *Ksp, const uint16_t *Vsp, uint16_t *Kd, uint16_t *Vd,
                                            int c, int n, int wave, int lane) {
     constexpr int ROWS = 1024 / (2 * D);     // rows per wave instruction
     constexpr int NI = kChunk / ROWS;        // instructions per tensor per chunk
     constexpr int P = D / 8;                 // pieces per row
+    static_assert(kMfmaWaves % 2 == 0 && (ROWS * kMfmaWaves) % 16 == 0, "swizzles repeat across a wave's blocks");
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)Ksp, 0, n * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)Vsp, 0, n * D * 2, 0x00020000);
+    const int rl = lane / P, phys = lane % P;
+    const int r0 = wave * ROWS + rl;  // the lane's row in its wave's first block
+    const int kpart = 16 * (phys ^ kswz<D>(r0)), vpart = 16 * (phys ^ vswz<D>(r0));
+    if (c + kChunk <= n) {
 #pragma unroll
-    for (int ii = wave; ii < NI; ii += kMfmaWaves) {
-        const int r = ii * ROWS + lane / P;  // chunk row written by this lane
-        const int phys = lane % P;
-        int g = c + r;
-        g = g < n ? g : n - 1;
-        const uint32_t kof = (uint32_t)(g * D + (phys ^ kswz<D>(r)) * 8);
-        const uint32_t vof = (uint32_t)(g * D + (phys ^ vswz<D>(r)) * 8);
-        __builtin_amdgcn_global_load_lds((const void *)(Ksp + kof), (RA_LDS void *)(Kd + ii * ROWS * D), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)(Vsp + vof), (RA_LDS void *)(Vd + ii * ROWS * D), 16, 0, 0);
+        for (int ii = wave; ii < NI; ii += kMfmaWaves) {
+            const int so = (c * D + ii * ROWS * D) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (RA_LDS void *)(Kd + ii * ROWS * D), 16, rl * D * 2 + kpart, so, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (RA_LDS void *)(Vd + ii * ROWS * D), 16, rl * D * 2 + vpart, so, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int ii = wave; ii < NI; ii += kMfmaWaves) {
+            int g = c + ii * ROWS + rl;
+            g = g < n ? g : n - 1;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (RA_LDS void *)(Kd + ii * ROWS * D), 16, g * D * 2 + kpart, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (RA_LDS void *)(Vd + ii * ROWS * D), 16, g * D * 2 + vpart, 0, 0, 0);
+        }
     }
 }
 
@@ -245,19 +266,24 @@ __device__ __forceinline__ float group_sum4(float x) {
 // MASK: some key of the chunk lies past the span's end or past some query's position; `lim` is
 // then min(hi, t_query + 1) - k0 for this lane's query (keys at offsets >= lim are masked).
 // Scores stay raw until the exponent: 2^(s * c - m) is one FMA and one v_exp_f32.
-// No rescaling: the reference maximum m of a query is fixed at the maximum of its first valid
-// keys, and later weights 2^(s c - m) may exceed 1 -- the same partial state, written relative
-// to a smaller m.  Should a score exceed m by more than 2^kJumpLog2 (`jump`), the tile is run
-// again with m set to the largest score seen (`mseen`), so weights never exceed 2^kJumpLog2.
+// No rescaling: the reference maximum m of a query is fixed at the maximum of its first chunk
+// of keys, and later weights 2^(s c - m) may exceed 1 -- the same partial state, written
+// relative to a smaller m.  Only the first chunk takes maxima (TRACK); later chunks just
+// exponentiate.  If some query's row sum ends above 2^kFastLog2 (or is not finite), a weight
+// may have grown past it: the tile then finds every query's largest score in a sweep over its
+// keys (max_chunk) and runs again with m set to it, so that no weight exceeds 1.  Weights thus
+// stay below 2^kFastLog2, far from fp32 overflow.
 // Row sums l = sum_k P[q][k] are taken over the same bf16 weights that the P.V product uses:
 // one v_dot2_f32_bf16 against (1, 1) per packed pair, into a per-lane fp32 sum over the lane's
 // own keys (the 4 lane groups of a query are added once, at the end: group_sum4).
-constexpr float kJumpLog2 = 32.f;
+constexpr float kFastLog2 = 40.f;
+constexpr float kFastLimit = 1099511627776.f;  // 2^kFastLog2
 
-// S^T = K Q^T for one chunk: sc[kt][i] = S^T[key 16kt + 4lg + i][query lr].
+// S^T = K Q^T for one chunk and kQG query groups: sc[g][kt][i] = S^T[key 16kt + 4lg + i][query lr
+// of group g].  Each K operand read from LDS feeds the kQG groups' MFMAs.
 template <int D>
-__device__ __forceinline__ void qk_chunk(const uint16_t *Kc, const int (&kof)[D / 32], const bf16x8_t (&qb)[D / 32],
-                                         f32x4_t (&sc)[kChunk / 16]) {
+__device__ __forceinline__ void qk_chunk(const uint16_t *Kc, const int (&kof)[D / 32], const bf16x8_t (&qb)[kQG][D / 32],
+                                         f32x4_t (&sc)[kQG][kChunk / 16]) {
     constexpr int KS = D / 32, KT = kChunk / 16;
     const char *Kbytes = reinterpret_cast<const char *>(Kc);
 #pragma unroll
@@ -266,33 +292,41 @@ __device__ __forceinline__ void qk_chunk(const uint16_t *Kc, const int (&kof)[D 
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             ka[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(Kbytes + kof[ks] + 2 * 16 * kt * D));
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qb[ks], acc, 0, 0, 0);
-        sc[kt] = acc;
+        for (int g = 0; g < kQG; ++g) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qb[g][ks], acc, 0, 0, 0);
+            sc[g][kt] = acc;
+        }
     }
 }
 
-// The chunk's weights 2^(s c - m) as bf16 pairs (pk[kt][i/2]), with the reference bookkeeping.
-template <bool MASK>
+// The chunk's weights 2^(s c - m) as bf16 pairs (pk[kt][i/2]); with TRACK, the reference
+// bookkeeping (maxima) too.
+template <bool MASK, bool TRACK>
 __device__ __forceinline__ void softmax_chunk(f32x4_t (&sc)[kChunk / 16], int lim, int lg, float scale_log2, float &m,
-                                              float &mseen, bool &jump, uint32_t (&pk)[kChunk / 16][2]) {
+                                              uint32_t (&pk)[kChunk / 16][2]) {
     constexpr int KT = kChunk / 16;
     constexpr float NEG = -__builtin_huge_valf();
-    float cmax = NEG;
+    if (MASK) {
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (MASK) sc[kt][i] = 16 * kt + 4 * lg + i < lim ? sc[kt][i] : NEG;
-            cmax = fmaxf(cmax, sc[kt][i]);
-        }
+            for (int i = 0; i < 4; ++i) sc[kt][i] = 16 * kt + 4 * lg + i < lim ? sc[kt][i] : NEG;
     }
-    const float mx = group_max4(cmax) * scale_log2;
-    mseen = fmaxf(mseen, mx);
-    jump = jump || (m != NEG && mx > m + kJumpLog2);
-    m = m == NEG ? mx : m;  // a query's first valid keys fix m (its o and l are still 0)
-    const float nm = (!MASK || m != NEG) ? -m : 0.f;
+    if (TRACK) {
+        float cmax = NEG;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, sc[kt][i]);
+        const float mx = group_max4(cmax) * scale_log2;
+        m = m == NEG ? mx : m;  // a query's first valid keys fix m (its o and l are still 0)
+    }
+    // (m is still unset only for a padding query with no key in the first chunk: its results
+    // are discarded, 0 keeps them finite)
+    const float nm = m != NEG ? -m : 0.f;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         float pv[4];
@@ -303,17 +337,20 @@ __device__ __forceinline__ void softmax_chunk(f32x4_t (&sc)[kChunk / 16], int li
     }
 }
 
-// O^T += V^T P^T, 32-key steps: K slots 8lg..8lg+7 <-> keys (2kk)16 + 4lg + 0..3
-// and (2kk+1)16 + 4lg + 0..3 for both operands.
+// O^T += V^T P^T, 32-key steps: K slots 8lg..8lg+7 <-> keys (2kk)16 + 4lg + 0..3 and
+// (2kk+1)16 + 4lg + 0..3 for both operands.  Each V operand read from LDS feeds the kQG groups.
 template <int D>
 __device__ __forceinline__ void pv_chunk(const uint16_t *Vc, const int (&vof)[D / 64][4],
-                                         const uint32_t (&pk)[kChunk / 16][2], f32x4_t (&o)[D / 16]) {
+                                         const uint32_t (&pk)[kQG][kChunk / 16][2], f32x4_t (&o)[kQG][D / 16]) {
     constexpr int ET = D / 16, KT = kChunk / 16;
     const char *Vbytes = reinterpret_cast<const char *>(Vc);
 #pragma unroll
     for (int kk = 0; kk < KT / 2; ++kk) {
-        const bf16x8_t pb =
-            __builtin_bit_cast(bf16x8_t, make_uint4(pk[2 * kk][0], pk[2 * kk][1], pk[2 * kk + 1][0], pk[2 * kk + 1][1]));
+        bf16x8_t pb[kQG];
+#pragma unroll
+        for (int g = 0; g < kQG; ++g)
+            pb[g] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[g][2 * kk][0], pk[g][2 * kk][1], pk[g][2 * kk + 1][0],
+                                                            pk[g][2 * kk + 1][1]));
 #pragma unroll
         for (int et = 0; et < ET; ++et) {
             // transposed reads: lane (lg, i) gets V[key][16 et + i] for 4 consecutive keys
@@ -324,26 +361,53 @@ __device__ __forceinline__ void pv_chunk(const uint16_t *Vc, const int (&vof)[D 
                 vw[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS v4i16_t *)pv_addr));
             }
             const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(vw[0].x, vw[0].y, vw[1].x, vw[1].y));
-            o[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[et], 0, 0, 0);
+#pragma unroll
+            for (int g = 0; g < kQG; ++g) o[g][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[g], o[g][et], 0, 0, 0);
         }
     }
 }
 
-template <int D, bool MASK>
+// One chunk for the wave's kQG query groups.  Per group g: reference m[g], row sum l[g] and,
+// for MASK chunks, the limit lim[g].
+template <int D, bool MASK, bool TRACK>
 __device__ __forceinline__ void tile_chunk(const uint16_t *Kc, const uint16_t *Vc, const int (&kof)[D / 32],
-                                           const int (&vof)[D / 64][4], const bf16x8_t (&qb)[D / 32],
-                                           float &m, float &mseen, bool &jump, float &l,
-                                           f32x4_t (&o)[D / 16], int lim, int lg, float scale_log2) {
-    f32x4_t sc[kChunk / 16];
+                                           const int (&vof)[D / 64][4], const bf16x8_t (&qb)[kQG][D / 32],
+                                           float (&m)[kQG], float (&l)[kQG], f32x4_t (&o)[kQG][D / 16],
+                                           const int (&lim)[kQG], int lg, float scale_log2) {
+    f32x4_t sc[kQG][kChunk / 16];
     qk_chunk<D>(Kc, kof, qb, sc);
-    uint32_t pk[kChunk / 16][2];
-    softmax_chunk<MASK>(sc, lim, lg, scale_log2, m, mseen, jump, pk);
+    uint32_t pk[kQG][kChunk / 16][2];
     const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
 #pragma unroll
-    for (int kt = 0; kt < kChunk / 16; ++kt)
+    for (int g = 0; g < kQG; ++g) {
+        softmax_chunk<MASK, TRACK>(sc[g], lim[g], lg, scale_log2, m[g], pk[g]);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kt][h]), one2, l, false);
+        for (int kt = 0; kt < kChunk / 16; ++kt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                l[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[g][kt][h]), one2, l[g], false);
+    }
     pv_chunk<D>(Vc, vof, pk, o);
+}
+
+// The sweep of the rare second pass: each query's largest score (times scale_log2) over one
+// chunk, folded into mx[g].
+template <int D, bool MASK>
+__device__ __forceinline__ void max_chunk(const uint16_t *Kc, const int (&kof)[D / 32], const bf16x8_t (&qb)[kQG][D / 32],
+                                          float (&mx)[kQG], const int (&lim)[kQG], int lg, float scale_log2) {
+    constexpr float NEG = -__builtin_huge_valf();
+    f32x4_t sc[kQG][kChunk / 16];
+    qk_chunk<D>(Kc, kof, qb, sc);
+#pragma unroll
+    for (int g = 0; g < kQG; ++g) {
+        float cmax = NEG;
+#pragma unroll
+        for (int kt = 0; kt < kChunk / 16; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                cmax = fmaxf(cmax, (!MASK || 16 * kt + 4 * lg + i < lim[g]) ? sc[g][kt][i] : NEG);
+        mx[g] = fmaxf(mx[g], group_max4(cmax) * scale_log2);
+    }
 }
 
 // Transposed formulation.  S^T = K Q^T puts keys on the MFMA rows and queries on the columns,
@@ -353,7 +417,7 @@ __device__ __forceinline__ void tile_chunk(const uint16_t *Kc, const uint16_t *V
 // registers: its 32-key K dimension is ordered as the lanes hold it (keys 4lg..4lg+3 of two
 // 16-key tiles per lane group), and V^T is read from LDS in the same order.
 template <int D>
-__global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) tile_mfma(const uint16_t *__restrict__ q,
+__global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU))) tile_mfma(const uint16_t *__restrict__ q,
                                                           const uint16_t *__restrict__ K,
                                                           const uint16_t *__restrict__ V,
                                                           const int32_t *__restrict__ tile_off,
@@ -384,7 +448,8 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     const int4 tl = tiles[tile];
     asm volatile("" ::"s"(total), "s"(tl.x), "s"(tl.y), "s"(tl.z));
     if (tile >= total) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 4, lr = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: scalar chunk-load offsets)
     const int64_t expert = tl.x;
     const int n = tl.z;  // entries in the tile (<= kMfmaTile)
     const int64_t j = expert % span_slots;
@@ -399,24 +464,31 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     // positions that may cut it short are not known yet (rows past them are masked).
     // (unconditional loads from clamped indices, masked afterwards: a load under a condition is
     // waited for on its own)
+    // entry 16 (kQG wave + g) + lr of the tile is query lr of group g of wave `wave`
     const int i_blk = tid < n ? tid : n - 1;
-    const int r_own = 16 * wave + lr;
-    const int i_own = r_own < n ? r_own : n - 1;
     const int64_t t_blk = list_t[tl.y + i_blk];
-    const int32_t x_ld = list[tl.y + i_own];
-    const int64_t t_ld = list_t[tl.y + i_own];
-    const int32_t x_own = r_own < n ? x_ld : -1;
-    const int64_t tq = r_own < n ? t_ld : -1;  // position of this lane's query
+    int32_t x_ld[kQG], x_own[kQG];
+    int64_t tq[kQG];  // position of the lane's query in each group (-1: padding)
+#pragma unroll
+    for (int g = 0; g < kQG; ++g) {
+        const int r_own = 16 * (kQG * wave + g) + lr;
+        const int i_own = r_own < n ? r_own : n - 1;
+        x_ld[g] = list[tl.y + i_own];
+        const int64_t t_ld = list_t[tl.y + i_own];
+        x_own[g] = r_own < n ? x_ld[g] : -1;
+        tq[g] = r_own < n ? t_ld : -1;
+    }
 
-    // B operand of S^T: this wave's 16 gathered query rows, all k-steps, in registers
-    bf16x8_t qb[KS];
-    {
-        const int64_t rh = x_ld / NE;  // (a padding row loads a valid row, then zero)
+    // B operands of S^T: the wave's gathered query rows, all k-steps, in registers
+    bf16x8_t qb[kQG][KS];
+#pragma unroll
+    for (int g = 0; g < kQG; ++g) {
+        const int64_t rh = x_ld[g] / NE;  // (a padding row loads a valid row, then zero)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 raw = *reinterpret_cast<const uint4 *>(q + rh * D + 32 * ks + 8 * lg);
-            if (x_own < 0) raw = make_uint4(0, 0, 0, 0);
-            qb[ks] = __builtin_bit_cast(bf16x8_t, raw);
+            if (x_own[g] < 0) raw = make_uint4(0, 0, 0, 0);
+            qb[g][ks] = __builtin_bit_cast(bf16x8_t, raw);
         }
     }
     // the first chunk's LDS loads fly with the query loads (issued after them: the compiler waits
@@ -469,39 +541,79 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
         for (int v = 0; v < 4 * (D / 64); ++v) vof[v / 4][v % 4] ^= BUF;
         nb ^= 1;
     };
-    auto lim_of = [&](int c) {
-        int64_t lim = (hi < tq + 1 ? hi : tq + 1) - (lo + c);
-        return (int)(lim < 0 ? 0 : (lim > kChunk ? kChunk : lim));
-    };
-    float m = NEG, mseen = NEG;
-    float l;
-    f32x4_t o[ET];
-    for (int pass = 0; pass < 2; ++pass) {
-        // pass 1 (rare): some score exceeded its reference by more than 2^kJumpLog2 in pass 0;
-        // redo the tile with every reference at the largest score seen
-        m = pass == 0 ? NEG : mseen;
-        bool jump = false;
-        l = 0.f;
+    auto lim_of = [&](int c, int (&lim)[kQG]) {
 #pragma unroll
-        for (int et = 0; et < ET; ++et) o[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (pass > 0) {  // (pass 0: the first chunk was loaded with the tile's entries)
+        for (int g = 0; g < kQG; ++g) {
+            int64_t v = (hi < tq[g] + 1 ? hi : tq[g] + 1) - (lo + c);
+            lim[g] = (int)(v < 0 ? 0 : (v > kChunk ? kChunk : v));
+        }
+    };
+    float m[kQG], l[kQG];
+    f32x4_t o[kQG][ET];
+    const int lim_full[kQG] = {};  // (unused by unmasked chunks)
+    // pass 1 (rare) finds every query's largest score first, then runs as pass 0 from it
+    for (int pass = 0; pass < 2; ++pass) {
+        float mx[kQG];
+#pragma unroll
+        for (int g = 0; g < kQG; ++g) mx[g] = NEG;
+        if (pass > 0) {
             __syncthreads();  // everyone is done with the buffers
             if (nb == 0) flip();  // back to buffer 0
             chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_span, wave, lane);
+            int c = 0;
+            for (; c + kChunk <= full_end; c += kChunk) {
+                begin(c);
+                max_chunk<D, false>(Kst, kof, qb, mx, lim_full, lg, scale_log2);
+                flip();
+            }
+            for (; c < n_keys; c += kChunk) {
+                begin(c);
+                int lim[kQG];
+                lim_of(c, lim);
+                max_chunk<D, true>(Kst, kof, qb, mx, lim, lg, scale_log2);
+                flip();
+            }
+            __syncthreads();
+            if (nb == 0) flip();
+            chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_span, wave, lane);
         }
-        int c = 0;
+#pragma unroll
+        for (int g = 0; g < kQG; ++g) {
+            m[g] = mx[g];
+            l[g] = 0.f;
+#pragma unroll
+            for (int et = 0; et < ET; ++et) o[g][et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        // the first chunk fixes the references of pass 0 (every valid query has a key in it)
+        begin(0);
+        if (kChunk <= full_end) {
+            tile_chunk<D, false, true>(Kst, Vst, kof, vof, qb, m, l, o, lim_full, lg, scale_log2);
+        } else {
+            int lim[kQG];
+            lim_of(0, lim);
+            tile_chunk<D, true, true>(Kst, Vst, kof, vof, qb, m, l, o, lim, lg, scale_log2);
+        }
+        flip();
+        int c = kChunk;
         for (; c + kChunk <= full_end; c += kChunk) {
             begin(c);
-            tile_chunk<D, false>(Kst, Vst, kof, vof, qb, m, mseen, jump, l, o, kChunk, lg, scale_log2);
+            tile_chunk<D, false, false>(Kst, Vst, kof, vof, qb, m, l, o, lim_full, lg, scale_log2);
             flip();
         }
         for (; c < n_keys; c += kChunk) {
             begin(c);
-            tile_chunk<D, true>(Kst, Vst, kof, vof, qb, m, mseen, jump, l, o, lim_of(c), lg, scale_log2);
+            int lim[kQG];
+            lim_of(c, lim);
+            tile_chunk<D, true, false>(Kst, Vst, kof, vof, qb, m, l, o, lim, lg, scale_log2);
             flip();
         }
+        if (pass > 0) break;
+        // a valid query whose row sum passed 2^kFastLog2 (or is not finite) needs pass 1;
         // block-wide decision (every wave takes the same path through the chunk loads)
-        if (lane == 0) redo_s[wave] = __ballot(jump) != 0 ? 1 : 0;
+        bool redo_q = false;
+#pragma unroll
+        for (int g = 0; g < kQG; ++g) redo_q = redo_q || (x_own[g] >= 0 && !(group_sum4(l[g]) <= kFastLimit));
+        if (lane == 0) redo_s[wave] = __ballot(redo_q) != 0 ? 1 : 0;
         __syncthreads();
         int redo = 0;
 #pragma unroll
@@ -511,15 +623,19 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     }
 
     // records: (m, l, o[d]) per valid row; lane (lg, lr) holds o[16et + 4lg + i] of query lr
-    l = group_sum4(l);
-    if (x_own >= 0) {
-        float *rec = records + (int64_t)x_own * record_floats(D);
 #pragma unroll
-        for (int et = 0; et < ET; ++et)
-            *reinterpret_cast<float4 *>(rec + 4 + 16 * et + 4 * lg) = make_float4(o[et][0], o[et][1], o[et][2], o[et][3]);
-        if (lg == 0) {
-            rec[0] = m;
-            rec[1] = l;
+    for (int g = 0; g < kQG; ++g) {
+        const float lt = group_sum4(l[g]);
+        if (x_own[g] >= 0) {
+            float *rec = records + (int64_t)x_own[g] * record_floats(D);
+#pragma unroll
+            for (int et = 0; et < ET; ++et)
+                *reinterpret_cast<float4 *>(rec + 4 + 16 * et + 4 * lg) =
+                    make_float4(o[g][et][0], o[g][et][1], o[g][et][2], o[g][et][3]);
+            if (lg == 0) {
+                rec[0] = m[g];
+                rec[1] = lt;
+            }
         }
     }
 }
@@ -555,7 +671,7 @@ hipError_t valu_launch(const TileArgs &t, hipStream_t st) {
 // are padding during a pass.  Each entry's whole softmax state stays in registers, so the
 // output o / l is written directly: no workspace and no merge.
 template <int D>
-__global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+__global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
 dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, const int64_t *__restrict__ row_pos,
            const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, float *__restrict__ out, int64_t n_rows,
            int Hq, int Hkv, int G, int RT, int B, int64_t cap, int64_t max_pos, float scale_log2, int64_t n_blocks) {
@@ -571,19 +687,27 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
     const int64_t n_rb = (n_rows + RT - 1) / RT;
     const int g = (int)(tile / n_rb);
     const int64_t r0 = (tile % n_rb) * RT;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 4, lr = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: scalar chunk-load offsets)
 
-    // this lane's entry (the B operand column lr of wave `wave`)
-    const int e = 16 * wave + lr;
-    const int64_t row_e = r0 + e / G;
-    const bool valid = e < RT * G && row_e < n_rows;
-    const int64_t row_c = valid ? row_e : r0;  // (a padding entry loads a valid row, then zero)
-    const int hq = g * G + (valid ? e % G : 0);
-    const int seq_raw = row_seq[row_c];
-    const int64_t t_raw = row_pos[row_c];
-    const uint16_t *q_e = q + (row_c * Hq + hq) * D + 8 * lg;  // this lane's part of its query row
-    const int seq_e = seq_raw < 0 ? 0 : (seq_raw >= B ? B - 1 : seq_raw);
-    const int64_t t_e = t_raw < 0 ? 0 : (t_raw > max_pos ? max_pos : t_raw);
+    // this lane's entries: query lr of group gi of wave `wave` is entry e = 16 (kQG wave + gi) + lr
+    // of the tile, i.e. row r0 + e / G, query head g G + e mod G
+    int64_t row_e[kQG], qoff[kQG], t_e[kQG];
+    bool valid[kQG];
+    int seq_e[kQG];
+#pragma unroll
+    for (int gi = 0; gi < kQG; ++gi) {
+        const int e = 16 * (kQG * wave + gi) + lr;
+        row_e[gi] = r0 + e / G;
+        valid[gi] = e < RT * G && row_e[gi] < n_rows;
+        const int64_t row_c = valid[gi] ? row_e[gi] : r0;  // (a padding entry loads a valid row, then zero)
+        const int hq = g * G + (valid[gi] ? e % G : 0);
+        const int seq_raw = row_seq[row_c];
+        const int64_t t_raw = row_pos[row_c];
+        qoff[gi] = (row_c * Hq + hq) * D;  // the entry's query row (and output row)
+        seq_e[gi] = seq_raw < 0 ? 0 : (seq_raw >= B ? B - 1 : seq_raw);
+        t_e[gi] = t_raw < 0 ? 0 : (t_raw > max_pos ? max_pos : t_raw);
+    }
 
     int kof[KS], vof[D / 64][4];
     operand_offsets<D>(lg, lr, kof, vof);
@@ -624,13 +748,24 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
         // the next sequence of the tile (smallest id above the last one done), its rows' first and
         // last positions
         unsigned long long nseq, tmin_u, tmax_u;
-        const bool pend = valid && seq_e > prev_seq;
-        block_reduce(pend ? (unsigned long long)seq_e : ~0ull, ~0ull, 0ull, nseq, tmin_u, tmax_u);
+        unsigned long long pmin = ~0ull;
+#pragma unroll
+        for (int gi = 0; gi < kQG; ++gi)
+            if (valid[gi] && seq_e[gi] > prev_seq && (unsigned long long)seq_e[gi] < pmin) pmin = seq_e[gi];
+        block_reduce(pmin, ~0ull, 0ull, nseq, tmin_u, tmax_u);
         if (nseq == ~0ull) break;
         const int seq = (int)nseq;
-        const bool active = valid && seq_e == seq;
-        block_reduce(~0ull, active ? (unsigned long long)t_e : ~0ull, active ? (unsigned long long)t_e : 0ull, nseq,
-                     tmin_u, tmax_u);
+        bool active[kQG];
+        unsigned long long amin = ~0ull, amax = 0ull;
+#pragma unroll
+        for (int gi = 0; gi < kQG; ++gi) {
+            active[gi] = valid[gi] && seq_e[gi] == seq;
+            if (active[gi]) {
+                amin = (unsigned long long)t_e[gi] < amin ? (unsigned long long)t_e[gi] : amin;
+                amax = (unsigned long long)t_e[gi] > amax ? (unsigned long long)t_e[gi] : amax;
+            }
+        }
+        block_reduce(~0ull, amin, amax, nseq, tmin_u, tmax_u);
         const int64_t tmin = (int64_t)tmin_u, tmax = (int64_t)tmax_u;
         int64_t hi = tmax + 1;
         if (hi > cap) hi = cap;
@@ -638,52 +773,96 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
         const int full_end = (int)(tmin + 1 < hi ? tmin + 1 : hi);
         const uint16_t *Ksp = K + ((int64_t)seq * Hkv + g) * cap * D;
         const uint16_t *Vsp = V + ((int64_t)seq * Hkv + g) * cap * D;
-        // the query, loaded again for each sequence of the tile (zero for entries of other sequences)
-        bf16x8_t qb[KS];
+        // the queries, loaded again for each sequence of the tile (zero for entries of other sequences)
+        bf16x8_t qb[kQG][KS];
+        int64_t tq[kQG];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint4 raw = *reinterpret_cast<const uint4 *>(q_e + 32 * ks);
-            if (!active) raw = make_uint4(0, 0, 0, 0);
-            qb[ks] = __builtin_bit_cast(bf16x8_t, raw);
+        for (int gi = 0; gi < kQG; ++gi) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                uint4 raw = *reinterpret_cast<const uint4 *>(q + qoff[gi] + 32 * ks + 8 * lg);
+                if (!active[gi]) raw = make_uint4(0, 0, 0, 0);
+                qb[gi][ks] = __builtin_bit_cast(bf16x8_t, raw);
+            }
+            tq[gi] = active[gi] ? t_e[gi] : -1;
         }
-        const int64_t tq = active ? t_e : -1;
 
         auto begin = [&](int c) {
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (c + kChunk < n_keys) chunk_load<D>(Ksp, Vsp, stage[nb], stage[2 + nb], c + kChunk, n_keys, wave, lane);
         };
-        auto lim_of = [&](int c) {
-            int64_t lim = (hi < tq + 1 ? hi : tq + 1) - c;
-            return (int)(lim < 0 ? 0 : (lim > kChunk ? kChunk : lim));
-        };
-        float m = NEG, mseen = NEG;
-        float l;
-        f32x4_t o[ET];
-        for (int pass = 0; pass < 2; ++pass) {
-            // pass 1 (rare): a score exceeded its reference by more than 2^kJumpLog2 in pass 0
-            m = pass == 0 ? NEG : mseen;
-            bool jump = false;
-            l = 0.f;
+        auto lim_of = [&](int c, int (&lim)[kQG]) {
 #pragma unroll
-            for (int et = 0; et < ET; ++et) o[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int gi = 0; gi < kQG; ++gi) {
+                int64_t v = (hi < tq[gi] + 1 ? hi : tq[gi] + 1) - c;
+                lim[gi] = (int)(v < 0 ? 0 : (v > kChunk ? kChunk : v));
+            }
+        };
+        float m[kQG], l[kQG];
+        f32x4_t o[kQG][ET];
+        const int lim_full[kQG] = {};  // (unused by unmasked chunks)
+        // as in the routed tiles: pass 1 (rare) finds every query's largest score first
+        for (int pass = 0; pass < 2; ++pass) {
+            float mx[kQG];
+#pragma unroll
+            for (int gi = 0; gi < kQG; ++gi) mx[gi] = NEG;
             __syncthreads();  // everyone is done with the buffers
             if (nb == 0) flip();  // back to buffer 0
             chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_keys, wave, lane);
-            int c = 0;
+            if (pass > 0) {
+                int c = 0;
+                for (; c + kChunk <= full_end; c += kChunk) {
+                    begin(c);
+                    max_chunk<D, false>(stage[0], kof, qb, mx, lim_full, lg, scale_log2);
+                    flip();
+                }
+                for (; c < n_keys; c += kChunk) {
+                    begin(c);
+                    int lim[kQG];
+                    lim_of(c, lim);
+                    max_chunk<D, true>(stage[0], kof, qb, mx, lim, lg, scale_log2);
+                    flip();
+                }
+                __syncthreads();
+                if (nb == 0) flip();
+                chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_keys, wave, lane);
+            }
+#pragma unroll
+            for (int gi = 0; gi < kQG; ++gi) {
+                m[gi] = mx[gi];
+                l[gi] = 0.f;
+#pragma unroll
+                for (int et = 0; et < ET; ++et) o[gi][et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            // the first chunk fixes the references of pass 0 (every active query has key 0)
+            begin(0);
+            if (kChunk <= full_end) {
+                tile_chunk<D, false, true>(stage[0], stage[2], kof, vof, qb, m, l, o, lim_full, lg, scale_log2);
+            } else {
+                int lim[kQG];
+                lim_of(0, lim);
+                tile_chunk<D, true, true>(stage[0], stage[2], kof, vof, qb, m, l, o, lim, lg, scale_log2);
+            }
+            flip();
+            int c = kChunk;
             for (; c + kChunk <= full_end; c += kChunk) {
                 begin(c);
-                tile_chunk<D, false>(stage[0], stage[2], kof, vof, qb, m, mseen, jump, l, o, kChunk, lg,
-                                     scale_log2);
+                tile_chunk<D, false, false>(stage[0], stage[2], kof, vof, qb, m, l, o, lim_full, lg, scale_log2);
                 flip();
             }
             for (; c < n_keys; c += kChunk) {
                 begin(c);
-                tile_chunk<D, true>(stage[0], stage[2], kof, vof, qb, m, mseen, jump, l, o, lim_of(c), lg,
-                                    scale_log2);
+                int lim[kQG];
+                lim_of(c, lim);
+                tile_chunk<D, true, false>(stage[0], stage[2], kof, vof, qb, m, l, o, lim, lg, scale_log2);
                 flip();
             }
-            if (lane == 0) redo_s[wave] = __ballot(jump) != 0 ? 1 : 0;
+            if (pass > 0) break;
+            bool redo_q = false;
+#pragma unroll
+            for (int gi = 0; gi < kQG; ++gi) redo_q = redo_q || (active[gi] && !(group_sum4(l[gi]) <= kFastLimit));
+            if (lane == 0) redo_s[wave] = __ballot(redo_q) != 0 ? 1 : 0;
             __syncthreads();
             int redo = 0;
 #pragma unroll
@@ -691,14 +870,17 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
             if (!redo) break;
         }
         // out = o / l (l summed over the query's 4 lane groups: every lane holds the total)
-        l = group_sum4(l);
-        if (active) {
-            const float inv = 1.f / l;
-            float *dst = out + (row_e * Hq + hq) * D;
 #pragma unroll
-            for (int et = 0; et < ET; ++et)
-                *reinterpret_cast<float4 *>(dst + 16 * et + 4 * lg) =
-                    make_float4(o[et][0] * inv, o[et][1] * inv, o[et][2] * inv, o[et][3] * inv);
+        for (int gi = 0; gi < kQG; ++gi) {
+            const float lt = group_sum4(l[gi]);
+            if (active[gi]) {
+                const float inv = 1.f / lt;
+                float *dst = out + qoff[gi];
+#pragma unroll
+                for (int et = 0; et < ET; ++et)
+                    *reinterpret_cast<float4 *>(dst + 16 * et + 4 * lg) =
+                        make_float4(o[gi][et][0] * inv, o[gi][et][1] * inv, o[gi][et][2] * inv, o[gi][et][3] * inv);
+            }
         }
         prev_seq = seq;
     }
