@@ -16,6 +16,8 @@
 #include "prefill_tiles.h"
 #include "wave_ops.h"
 
+#include <type_traits>
+
 namespace ra {
 namespace {
 
@@ -188,40 +190,35 @@ __device__ __forceinline__ int kswz(int r) { return r % (D / 8); }
 template <int D>
 __device__ __forceinline__ int vswz(int r) { return 2 * (r & 3) + (D >= 128 ? 8 * ((r >> 2) & 1) : 0); }
 
-// Issue the direct global -> LDS loads of the chunk at key offset c (from the span's first key,
-// whose K and V rows start at Ksp, Vsp) into (Kd, Vd); rows at or past `n` (the span's keys in
-// use) repeat row n - 1 (masked later).  Each wave instruction fills 1 KB = 1024 / (2 D) rows.
-// Buffer loads: the span is a buffer resource of its n rows, the chunk and row-block offsets are
-// scalar, and a lane's own part of the address (its row in the block, its swizzled piece) is the
-// same for every block of a chunk (the swizzles repeat every 16 rows, a wave's blocks every 16),
-// so a whole chunk costs no vector arithmetic.  Only a chunk that passes row n - 1 clamps rows
-// per lane.
-template <int D>
-__device__ __forceinline__ void chunk_load(const uint16_t *Ksp, const uint16_t *Vsp, uint16_t *Kd, uint16_t *Vd,
-                                           int c, int n, int wave, int lane) {
+// Issue the direct global -> LDS loads of one tensor's chunk at key offset c (from the tile's
+// first key, whose row starts at `base`) into `dst`: kChunk rows of D bf16, rows at or past `n`
+// (the rows that may be read) repeating row n - 1 (masked later).  Each wave instruction fills
+// 1 KB = 1024 / (2 D) rows.  Buffer loads: the rows are a buffer resource, the chunk and
+// row-block offsets are scalar, and a lane's own part of the address (its row in the block, its
+// swizzled piece) is the same for every block of a chunk (the swizzles repeat every 16 rows, a
+// wave's blocks every 16), so a whole chunk costs no vector arithmetic.  Only a chunk that
+// passes row n - 1 clamps rows per lane.  IS_V selects the V swizzle.
+template <int D, bool IS_V>
+__device__ __forceinline__ void chunk_rows(const uint16_t *base, uint16_t *dst, int c, int n, int wave, int lane) {
     constexpr int ROWS = 1024 / (2 * D);     // rows per wave instruction
-    constexpr int NI = kChunk / ROWS;        // instructions per tensor per chunk
+    constexpr int NI = kChunk / ROWS;        // instructions per chunk
     constexpr int P = D / 8;                 // pieces per row
     static_assert(kMfmaWaves % 2 == 0 && (ROWS * kMfmaWaves) % 16 == 0, "swizzles repeat across a wave's blocks");
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)Ksp, 0, n * D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)Vsp, 0, n * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, n * D * 2, 0x00020000);
     const int rl = lane / P, phys = lane % P;
     const int r0 = wave * ROWS + rl;  // the lane's row in its wave's first block
-    const int kpart = 16 * (phys ^ kswz<D>(r0)), vpart = 16 * (phys ^ vswz<D>(r0));
+    const int part = 16 * (phys ^ (IS_V ? vswz<D>(r0) : kswz<D>(r0)));
     if (c + kChunk <= n) {
 #pragma unroll
-        for (int ii = wave; ii < NI; ii += kMfmaWaves) {
-            const int so = (c * D + ii * ROWS * D) * 2;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (RA_LDS void *)(Kd + ii * ROWS * D), 16, rl * D * 2 + kpart, so, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (RA_LDS void *)(Vd + ii * ROWS * D), 16, rl * D * 2 + vpart, so, 0, 0);
-        }
+        for (int ii = wave; ii < NI; ii += kMfmaWaves)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (RA_LDS void *)(dst + ii * ROWS * D), 16, rl * D * 2 + part,
+                                                     (c * D + ii * ROWS * D) * 2, 0, 0);
     } else {
 #pragma unroll
         for (int ii = wave; ii < NI; ii += kMfmaWaves) {
             int g = c + ii * ROWS + rl;
             g = g < n ? g : n - 1;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (RA_LDS void *)(Kd + ii * ROWS * D), 16, g * D * 2 + kpart, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (RA_LDS void *)(Vd + ii * ROWS * D), 16, g * D * 2 + vpart, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (RA_LDS void *)(dst + ii * ROWS * D), 16, g * D * 2 + part, 0, 0, 0);
         }
     }
 }
@@ -367,29 +364,6 @@ __device__ __forceinline__ void pv_chunk(const uint16_t *Vc, const int (&vof)[D 
     }
 }
 
-// One chunk for the wave's kQG query groups.  Per group g: reference m[g], row sum l[g] and,
-// for MASK chunks, the limit lim[g].
-template <int D, bool MASK, bool TRACK>
-__device__ __forceinline__ void tile_chunk(const uint16_t *Kc, const uint16_t *Vc, const int (&kof)[D / 32],
-                                           const int (&vof)[D / 64][4], const bf16x8_t (&qb)[kQG][D / 32],
-                                           float (&m)[kQG], float (&l)[kQG], f32x4_t (&o)[kQG][D / 16],
-                                           const int (&lim)[kQG], int lg, float scale_log2) {
-    f32x4_t sc[kQG][kChunk / 16];
-    qk_chunk<D>(Kc, kof, qb, sc);
-    uint32_t pk[kQG][kChunk / 16][2];
-    const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
-#pragma unroll
-    for (int g = 0; g < kQG; ++g) {
-        softmax_chunk<MASK, TRACK>(sc[g], lim[g], lg, scale_log2, m[g], pk[g]);
-#pragma unroll
-        for (int kt = 0; kt < kChunk / 16; ++kt)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                l[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[g][kt][h]), one2, l[g], false);
-    }
-    pv_chunk<D>(Vc, vof, pk, o);
-}
-
 // The sweep of the rare second pass: each query's largest score (times scale_log2) over one
 // chunk, folded into mx[g].
 template <int D, bool MASK>
@@ -407,6 +381,105 @@ __device__ __forceinline__ void max_chunk(const uint16_t *Kc, const int (&kof)[D
             for (int i = 0; i < 4; ++i)
                 cmax = fmaxf(cmax, (!MASK || 16 * kt + 4 * lg + i < lim[g]) ? sc[g][kt][i] : NEG);
         mx[g] = fmaxf(mx[g], group_max4(cmax) * scale_log2);
+    }
+}
+
+// The keys of a tile: K and V rows from the tile's first key (Ksp, Vsp), n_load of them
+// readable, n_keys attended (chunks cover [0, n_keys)), and chunks ending by full_end need no
+// mask.  qlim[g] = keys (from the first) that the lane's query of group g may attend.
+struct TileKeys {
+    const uint16_t *Ksp, *Vsp;
+    int n_load, n_keys, full_end;
+};
+
+// The staged chunks: K and V of chunk x sit in kb[x & 1] and vb[x & 1].  Four distinct arrays:
+// the compiler then knows that a chunk's LDS loads do not touch the buffers being read, and
+// does not wait for them before those reads.
+template <int D>
+struct Stage {
+    uint16_t *kb0, *kb1, *vb0, *vb1;
+};
+
+// One pass over a tile's chunks with fixed references.  Chunk c's K and V sit in buffers c & 1;
+// at chunk c the loads of chunk c + 1 go to the other buffers, so that they fly while chunk c is
+// computed (the buffers are distinct arrays, so the compiler does not wait for those loads
+// before reading chunk c).  The first chunk takes maxima and fixes each query's reference where
+// it is unset.  `preloaded`: K(0) and V(0) are already being loaded.
+template <int D>
+__device__ __forceinline__ void fast_sweep(const Stage<D> &st, const TileKeys &tk, bool preloaded, const int (&qlim)[kQG],
+                                           const int (&kof)[D / 32], const int (&vof)[D / 64][4],
+                                           const bf16x8_t (&qb)[kQG][D / 32], float (&m)[kQG], float (&l)[kQG],
+                                           f32x4_t (&o)[kQG][D / 16], int wave, int lane, int lg, float scale_log2) {
+    constexpr int KT = kChunk / 16;
+    const int C = (tk.n_keys + kChunk - 1) / kChunk;
+    if (!preloaded) {
+        __syncthreads();  // everyone is done with the buffers
+        chunk_rows<D, false>(tk.Ksp, st.kb0, 0, tk.n_load, wave, lane);
+        chunk_rows<D, true>(tk.Vsp, st.vb0, 0, tk.n_load, wave, lane);
+    }
+    const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+    // chunk c with buffer parity P = c & 1
+    auto iter = [&](auto par, auto mask, auto track, int c) {
+        constexpr int P = decltype(par)::value;
+        constexpr bool MASK = decltype(mask)::value, TRACK = decltype(track)::value;
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of chunk c landed
+        __syncthreads();  // everyone's landed; everyone is done with chunk c - 1
+        if (c + 1 < C) {
+            chunk_rows<D, false>(tk.Ksp, P ? st.kb0 : st.kb1, (c + 1) * kChunk, tk.n_load, wave, lane);
+            chunk_rows<D, true>(tk.Vsp, P ? st.vb0 : st.vb1, (c + 1) * kChunk, tk.n_load, wave, lane);
+        }
+        f32x4_t sc[kQG][KT];
+        qk_chunk<D>(P ? st.kb1 : st.kb0, kof, qb, sc);
+        uint32_t pk[kQG][KT][2];
+#pragma unroll
+        for (int g = 0; g < kQG; ++g) {
+            int lim = qlim[g] - c * kChunk;
+            lim = lim < 0 ? 0 : (lim > kChunk ? kChunk : lim);
+            softmax_chunk<MASK, TRACK>(sc[g], lim, lg, scale_log2, m[g], pk[g]);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    l[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[g][kt][h]), one2, l[g], false);
+        }
+        pv_chunk<D>(P ? st.vb1 : st.vb0, vof, pk, o);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using BF = std::integral_constant<bool, false>;
+    using BT = std::integral_constant<bool, true>;
+    if (kChunk <= tk.full_end) iter(I0{}, BF{}, BT{}, 0);
+    else iter(I0{}, BT{}, BT{}, 0);
+    for (int c = 1; c < C; c += 2) {
+        if ((c + 1) * kChunk <= tk.full_end) iter(I1{}, BF{}, BF{}, c);
+        else iter(I1{}, BT{}, BF{}, c);
+        if (c + 1 >= C) break;
+        if ((c + 2) * kChunk <= tk.full_end) iter(I0{}, BF{}, BF{}, c + 1);
+        else iter(I0{}, BT{}, BF{}, c + 1);
+    }
+}
+
+// The rare sweep before a second pass: every query's largest score (times scale_log2) over the
+// tile's keys, into mx[g].  K only, one chunk ahead.
+template <int D>
+__device__ __forceinline__ void max_sweep(const Stage<D> &st, const TileKeys &tk, const int (&qlim)[kQG],
+                                          const int (&kof)[D / 32], const bf16x8_t (&qb)[kQG][D / 32],
+                                          float (&mx)[kQG], int wave, int lane, int lg, float scale_log2) {
+    const int C = (tk.n_keys + kChunk - 1) / kChunk;
+    __syncthreads();  // everyone is done with the buffers
+    chunk_rows<D, false>(tk.Ksp, st.kb0, 0, tk.n_load, wave, lane);
+    for (int c = 0; c < C; ++c) {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (c + 1 < C) chunk_rows<D, false>(tk.Ksp, (c & 1) ? st.kb0 : st.kb1, (c + 1) * kChunk, tk.n_load, wave, lane);
+        int lim[kQG];
+#pragma unroll
+        for (int g = 0; g < kQG; ++g) {
+            const int v = qlim[g] - c * kChunk;
+            lim[g] = v < 0 ? 0 : (v > kChunk ? kChunk : v);
+        }
+        if (c & 1) max_chunk<D, true>(st.kb1, kof, qb, mx, lim, lg, scale_log2);
+        else max_chunk<D, true>(st.kb0, kof, qb, mx, lim, lg, scale_log2);
     }
 }
 
@@ -430,13 +503,11 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     constexpr int KS = D / 32;   // k-steps of the QK product
     constexpr int ET = D / 16;   // 16-wide e tiles of the PV product
     constexpr float NEG = -__builtin_huge_valf();
-    // staged chunks: K buffers 0 and 1, then V buffers 0 and 1 (kChunk rows of D bf16 each).  One
-    // array: the compiler then waits for a chunk's LDS loads before the next LDS read, so the
-    // loads of chunk c + 1 land before chunk c is computed.  (Measured: letting them overlap the
-    // computation of chunk c, with four distinct arrays, is slower.)
-    __shared__ uint16_t stage[4][kChunk * D];
+    // staged chunks: K and V buffers 0 and 1 (kChunk rows of D bf16 each)
+    __shared__ uint16_t kb0[kChunk * D], kb1[kChunk * D], vb0[kChunk * D], vb1[kChunk * D];
     __shared__ int redo_s[kMfmaWaves];
     __shared__ unsigned long long wmax_s[kMfmaWaves], wmin_s[kMfmaWaves];
+    const Stage<D> st{kb0, kb1, vb0, vb1};
 
     // all kernel arguments in one round trip (otherwise some are fetched only where first used)
     asm volatile("" ::"s"(q), "s"(K), "s"(V), "s"(tile_off), "s"(list), "s"(list_t), "s"(tiles), "s"(records),
@@ -491,9 +562,11 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
             qb[g][ks] = __builtin_bit_cast(bf16x8_t, raw);
         }
     }
-    // the first chunk's LDS loads fly with the query loads (issued after them: the compiler waits
-    // for everything before using a load's register while LDS loads are outstanding)
-    chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_span, wave, lane);
+    // the first chunk's LDS loads (K and V of chunk 0) fly with the query loads,
+    // up to the span's end (issued after them: the compiler waits for everything before using a
+    // load's register while LDS loads are outstanding)
+    chunk_rows<D, false>(Ksp, st.kb0, 0, n_span, wave, lane);
+    chunk_rows<D, true>(Vsp, st.vb0, 0, n_span, wave, lane);
     // the tile's first and last positions (wave reductions, then across the waves in LDS)
     {
         unsigned long long vmax = tid < n ? (unsigned long long)t_blk : 0ull;
@@ -516,110 +589,49 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     int64_t hi = lo + S;  // keys of the span used by the tile: [lo, hi)
     if (hi > tmax + 1) hi = tmax + 1;
     if (hi > cap) hi = cap;
-
     const int n_keys = (int)(hi - lo);
+    // chunks that end by full_end need no mask (key offsets from lo are ints: a span has S keys)
+    const TileKeys tk{Ksp, Vsp, n_keys, n_keys, (int)((tmin + 1 < hi ? tmin + 1 : hi) - lo)};
+    int qlim[kQG];
+#pragma unroll
+    for (int g = 0; g < kQG; ++g) {
+        const int64_t v = tq[g] + 1 - lo;
+        qlim[g] = tq[g] < 0 ? 0 : (int)(v < n_keys ? v : n_keys);
+    }
     int kof[KS], vof[D / 64][4];
     operand_offsets<D>(lg, lr, kof, vof);
-    // One chunk: wait for its loads (issued one chunk earlier), start the next chunk's loads
-    // into the other buffer, compute.  A chunk needs masks only where it passes the span's end
-    // or some row's position; chunks that end by full_end need none, and they come first (key
-    // offsets from lo are ints: a span has S keys).  The operand offsets carry the buffer:
-    // flipping it is an XOR.
-    const int full_end = (int)((tmin + 1 < hi ? tmin + 1 : hi) - lo);
-    constexpr int BUF = kChunk * D * 2;  // bytes per staged buffer
-    const uint16_t *Kst = stage[0], *Vst = stage[2];
-    int nb = 1;  // buffer that receives the next chunk
-    auto begin = [&](int c) {
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of chunk c landed
-        __syncthreads();  // everyone's loads landed, and everyone finished reading the other buffer
-        if (c + kChunk < n_keys) chunk_load<D>(Ksp, Vsp, stage[nb], stage[2 + nb], c + kChunk, n_keys, wave, lane);
-    };
-    auto flip = [&]() {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kof[ks] ^= BUF;
-#pragma unroll
-        for (int v = 0; v < 4 * (D / 64); ++v) vof[v / 4][v % 4] ^= BUF;
-        nb ^= 1;
-    };
-    auto lim_of = [&](int c, int (&lim)[kQG]) {
-#pragma unroll
-        for (int g = 0; g < kQG; ++g) {
-            int64_t v = (hi < tq[g] + 1 ? hi : tq[g] + 1) - (lo + c);
-            lim[g] = (int)(v < 0 ? 0 : (v > kChunk ? kChunk : v));
-        }
-    };
+
     float m[kQG], l[kQG];
     f32x4_t o[kQG][ET];
-    const int lim_full[kQG] = {};  // (unused by unmasked chunks)
-    // pass 1 (rare) finds every query's largest score first, then runs as pass 0 from it
-    for (int pass = 0; pass < 2; ++pass) {
-        float mx[kQG];
-#pragma unroll
-        for (int g = 0; g < kQG; ++g) mx[g] = NEG;
-        if (pass > 0) {
-            __syncthreads();  // everyone is done with the buffers
-            if (nb == 0) flip();  // back to buffer 0
-            chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_span, wave, lane);
-            int c = 0;
-            for (; c + kChunk <= full_end; c += kChunk) {
-                begin(c);
-                max_chunk<D, false>(Kst, kof, qb, mx, lim_full, lg, scale_log2);
-                flip();
-            }
-            for (; c < n_keys; c += kChunk) {
-                begin(c);
-                int lim[kQG];
-                lim_of(c, lim);
-                max_chunk<D, true>(Kst, kof, qb, mx, lim, lg, scale_log2);
-                flip();
-            }
-            __syncthreads();
-            if (nb == 0) flip();
-            chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_span, wave, lane);
-        }
+    auto reset = [&](const float (&m0)[kQG]) {
 #pragma unroll
         for (int g = 0; g < kQG; ++g) {
-            m[g] = mx[g];
+            m[g] = m0[g];
             l[g] = 0.f;
 #pragma unroll
             for (int et = 0; et < ET; ++et) o[g][et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        // the first chunk fixes the references of pass 0 (every valid query has a key in it)
-        begin(0);
-        if (kChunk <= full_end) {
-            tile_chunk<D, false, true>(Kst, Vst, kof, vof, qb, m, l, o, lim_full, lg, scale_log2);
-        } else {
-            int lim[kQG];
-            lim_of(0, lim);
-            tile_chunk<D, true, true>(Kst, Vst, kof, vof, qb, m, l, o, lim, lg, scale_log2);
-        }
-        flip();
-        int c = kChunk;
-        for (; c + kChunk <= full_end; c += kChunk) {
-            begin(c);
-            tile_chunk<D, false, false>(Kst, Vst, kof, vof, qb, m, l, o, lim_full, lg, scale_log2);
-            flip();
-        }
-        for (; c < n_keys; c += kChunk) {
-            begin(c);
-            int lim[kQG];
-            lim_of(c, lim);
-            tile_chunk<D, true, false>(Kst, Vst, kof, vof, qb, m, l, o, lim, lg, scale_log2);
-            flip();
-        }
-        if (pass > 0) break;
-        // a valid query whose row sum passed 2^kFastLog2 (or is not finite) needs pass 1;
-        // block-wide decision (every wave takes the same path through the chunk loads)
-        bool redo_q = false;
+    };
+    const float unset[kQG] = {NEG, NEG};
+    static_assert(kQG == 2, "unset[] lists one reference per group");
+    reset(unset);
+    fast_sweep<D>(st, tk, true, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
+    // a valid query whose row sum passed 2^kFastLog2 (or is not finite) sends the tile to a
+    // second pass; block-wide decision (every wave takes the same path through the chunk loads)
+    bool redo_q = false;
 #pragma unroll
-        for (int g = 0; g < kQG; ++g) redo_q = redo_q || (x_own[g] >= 0 && !(group_sum4(l[g]) <= kFastLimit));
-        if (lane == 0) redo_s[wave] = __ballot(redo_q) != 0 ? 1 : 0;
-        __syncthreads();
-        int redo = 0;
+    for (int g = 0; g < kQG; ++g) redo_q = redo_q || (x_own[g] >= 0 && !(group_sum4(l[g]) <= kFastLimit));
+    const bool wave_redo = __ballot(redo_q) != 0;  // (all lanes vote: a ballot counts active lanes only)
+    if (lane == 0) redo_s[wave] = wave_redo ? 1 : 0;
+    __syncthreads();
+    int redo = 0;
 #pragma unroll
-        for (int w = 0; w < kMfmaWaves; ++w) redo |= redo_s[w];
-        __syncthreads();
-        if (!redo) break;
+    for (int w = 0; w < kMfmaWaves; ++w) redo |= redo_s[w];
+    if (redo) {
+        float mx[kQG] = {NEG, NEG};
+        max_sweep<D>(st, tk, qlim, kof, qb, mx, wave, lane, lg, scale_log2);
+        reset(mx);
+        fast_sweep<D>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
     }
 
     // records: (m, l, o[d]) per valid row; lane (lg, lr) holds o[16et + 4lg + i] of query lr
@@ -677,9 +689,10 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
            int Hq, int Hkv, int G, int RT, int B, int64_t cap, int64_t max_pos, float scale_log2, int64_t n_blocks) {
     constexpr int KS = D / 32, ET = D / 16;
     constexpr float NEG = -__builtin_huge_valf();
-    __shared__ uint16_t stage[4][kChunk * D];  // (one array: see tile_mfma)
+    __shared__ uint16_t kb0[kChunk * D], kb1[kChunk * D], vb0[kChunk * D], vb1[kChunk * D];
     __shared__ int redo_s[kMfmaWaves];
     __shared__ unsigned long long wred_s[3][kMfmaWaves];
+    const Stage<D> st{kb0, kb1, vb0, vb1};
     asm volatile("" ::"s"(q), "s"(row_seq), "s"(row_pos), "s"(K), "s"(V), "s"(out), "s"(n_rows), "s"(Hq), "s"(Hkv),
                  "s"(G), "s"(RT), "s"(B), "s"(cap), "s"(max_pos), "s"(scale_log2), "s"(n_blocks));
     // tiles ordered (kv head, row block); XCD x takes a contiguous range of them (shared L2)
@@ -711,7 +724,6 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
 
     int kof[KS], vof[D / 64][4];
     operand_offsets<D>(lg, lr, kof, vof);
-    constexpr int BUF = kChunk * D * 2;
 
     // block-wide min/max of three 64-bit values (wave reductions, then across the waves in LDS)
     auto block_reduce = [&](unsigned long long a_min, unsigned long long b_min, unsigned long long c_max,
@@ -735,14 +747,6 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
         }
     };
 
-    int nb = 1;  // buffer that receives the next chunk; the operand offsets point to the other
-    auto flip = [&]() {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kof[ks] ^= BUF;
-#pragma unroll
-        for (int v = 0; v < 4 * (D / 64); ++v) vof[v / 4][v % 4] ^= BUF;
-        nb ^= 1;
-    };
     int64_t prev_seq = -1;
     for (;;) {
         // the next sequence of the tile (smallest id above the last one done), its rows' first and
@@ -770,12 +774,11 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
         int64_t hi = tmax + 1;
         if (hi > cap) hi = cap;
         const int n_keys = (int)hi;
-        const int full_end = (int)(tmin + 1 < hi ? tmin + 1 : hi);
-        const uint16_t *Ksp = K + ((int64_t)seq * Hkv + g) * cap * D;
-        const uint16_t *Vsp = V + ((int64_t)seq * Hkv + g) * cap * D;
+        const TileKeys tk{K + ((int64_t)seq * Hkv + g) * cap * D, V + ((int64_t)seq * Hkv + g) * cap * D, n_keys, n_keys,
+                          (int)(tmin + 1 < hi ? tmin + 1 : hi)};
         // the queries, loaded again for each sequence of the tile (zero for entries of other sequences)
         bf16x8_t qb[kQG][KS];
-        int64_t tq[kQG];
+        int qlim[kQG];
 #pragma unroll
         for (int gi = 0; gi < kQG; ++gi) {
 #pragma unroll
@@ -784,90 +787,38 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
                 if (!active[gi]) raw = make_uint4(0, 0, 0, 0);
                 qb[gi][ks] = __builtin_bit_cast(bf16x8_t, raw);
             }
-            tq[gi] = active[gi] ? t_e[gi] : -1;
+            qlim[gi] = active[gi] ? (int)(t_e[gi] + 1 < n_keys ? t_e[gi] + 1 : n_keys) : 0;
         }
 
-        auto begin = [&](int c) {
-            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            if (c + kChunk < n_keys) chunk_load<D>(Ksp, Vsp, stage[nb], stage[2 + nb], c + kChunk, n_keys, wave, lane);
-        };
-        auto lim_of = [&](int c, int (&lim)[kQG]) {
-#pragma unroll
-            for (int gi = 0; gi < kQG; ++gi) {
-                int64_t v = (hi < tq[gi] + 1 ? hi : tq[gi] + 1) - c;
-                lim[gi] = (int)(v < 0 ? 0 : (v > kChunk ? kChunk : v));
-            }
-        };
         float m[kQG], l[kQG];
         f32x4_t o[kQG][ET];
-        const int lim_full[kQG] = {};  // (unused by unmasked chunks)
-        // as in the routed tiles: pass 1 (rare) finds every query's largest score first
-        for (int pass = 0; pass < 2; ++pass) {
-            float mx[kQG];
-#pragma unroll
-            for (int gi = 0; gi < kQG; ++gi) mx[gi] = NEG;
-            __syncthreads();  // everyone is done with the buffers
-            if (nb == 0) flip();  // back to buffer 0
-            chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_keys, wave, lane);
-            if (pass > 0) {
-                int c = 0;
-                for (; c + kChunk <= full_end; c += kChunk) {
-                    begin(c);
-                    max_chunk<D, false>(stage[0], kof, qb, mx, lim_full, lg, scale_log2);
-                    flip();
-                }
-                for (; c < n_keys; c += kChunk) {
-                    begin(c);
-                    int lim[kQG];
-                    lim_of(c, lim);
-                    max_chunk<D, true>(stage[0], kof, qb, mx, lim, lg, scale_log2);
-                    flip();
-                }
-                __syncthreads();
-                if (nb == 0) flip();
-                chunk_load<D>(Ksp, Vsp, stage[0], stage[2], 0, n_keys, wave, lane);
-            }
+        auto reset = [&](const float (&m0)[kQG]) {
 #pragma unroll
             for (int gi = 0; gi < kQG; ++gi) {
-                m[gi] = mx[gi];
+                m[gi] = m0[gi];
                 l[gi] = 0.f;
 #pragma unroll
                 for (int et = 0; et < ET; ++et) o[gi][et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
-            // the first chunk fixes the references of pass 0 (every active query has key 0)
-            begin(0);
-            if (kChunk <= full_end) {
-                tile_chunk<D, false, true>(stage[0], stage[2], kof, vof, qb, m, l, o, lim_full, lg, scale_log2);
-            } else {
-                int lim[kQG];
-                lim_of(0, lim);
-                tile_chunk<D, true, true>(stage[0], stage[2], kof, vof, qb, m, l, o, lim, lg, scale_log2);
-            }
-            flip();
-            int c = kChunk;
-            for (; c + kChunk <= full_end; c += kChunk) {
-                begin(c);
-                tile_chunk<D, false, false>(stage[0], stage[2], kof, vof, qb, m, l, o, lim_full, lg, scale_log2);
-                flip();
-            }
-            for (; c < n_keys; c += kChunk) {
-                begin(c);
-                int lim[kQG];
-                lim_of(c, lim);
-                tile_chunk<D, true, false>(stage[0], stage[2], kof, vof, qb, m, l, o, lim, lg, scale_log2);
-                flip();
-            }
-            if (pass > 0) break;
-            bool redo_q = false;
+        };
+        const float unset[kQG] = {NEG, NEG};
+        reset(unset);
+        fast_sweep<D>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
+        // as in the routed tiles: a row sum past 2^kFastLog2 sends the tile to a second pass
+        bool redo_q = false;
 #pragma unroll
-            for (int gi = 0; gi < kQG; ++gi) redo_q = redo_q || (active[gi] && !(group_sum4(l[gi]) <= kFastLimit));
-            if (lane == 0) redo_s[wave] = __ballot(redo_q) != 0 ? 1 : 0;
-            __syncthreads();
-            int redo = 0;
+        for (int gi = 0; gi < kQG; ++gi) redo_q = redo_q || (active[gi] && !(group_sum4(l[gi]) <= kFastLimit));
+        const bool wave_redo = __ballot(redo_q) != 0;  // (all lanes vote: a ballot counts active lanes only)
+        if (lane == 0) redo_s[wave] = wave_redo ? 1 : 0;
+        __syncthreads();
+        int redo = 0;
 #pragma unroll
-            for (int w = 0; w < kMfmaWaves; ++w) redo |= redo_s[w];
-            if (!redo) break;
+        for (int w = 0; w < kMfmaWaves; ++w) redo |= redo_s[w];
+        if (redo) {
+            float mx[kQG] = {NEG, NEG};
+            max_sweep<D>(st, tk, qlim, kof, qb, mx, wave, lane, lg, scale_log2);
+            reset(mx);
+            fast_sweep<D>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
         }
         // out = o / l (l summed over the query's 4 lane groups: every lane holds the total)
 #pragma unroll

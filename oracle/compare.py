@@ -80,8 +80,13 @@ def selection_verdict(tested, oracle_sel, scores, k, abs_bound):
 
 
 def output_errors(tested, reference):
+    """Max-abs and relative L2 error of an output row; a tested value that is not finite
+    (NaN or infinite, which no finite reference is close to) counts as an infinite error, so
+    that it fails every tolerance and survives max()."""
     tested = np.asarray(tested, dtype=np.float64)
     reference = np.asarray(reference, dtype=np.float64)
+    if not np.all(np.isfinite(tested)):
+        return float("inf"), float("inf")
     diff = tested - reference
     max_abs = float(np.abs(diff).max()) if diff.size else 0.0
     denom = float(np.linalg.norm(reference))

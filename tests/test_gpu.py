@@ -283,6 +283,64 @@ def test_dense_outlier_keys_force_the_second_pass():
     log("  outliers: max abs %.3g" % worst)
 
 
+def _aligned_outlier_key(q_bits, d, log2_units):
+    """bf16 bits of a key along one query's vector whose score with that query is about
+    `log2_units` in the kernels' log2 domain (other queries see ~|q|^-1 of it)."""
+    qf = (q_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    alpha = log2_units * np.sqrt(d) / (np.log2(np.e) * np.linalg.norm(qf))
+    k = torch.tensor(alpha * qf / np.linalg.norm(qf), dtype=torch.float32).to(torch.bfloat16)
+    return k.view(torch.int16).numpy().view(np.uint16), k
+
+
+@pytest.mark.parametrize("kind", ["prefill", "dense"])
+def test_single_query_overflow_sends_its_tile_to_the_second_pass(kind):
+    """Keys planted along single queries' vectors, past the first chunk of keys: each target
+    query alone sees a score ~160 (log2 units) above the maximum of its first keys, so its
+    weights overflow in the fast pass, while the other entries of its tile stay in range.  The
+    whole tile must take the second pass whatever place the query holds in it (every lane
+    votes).  Six targets in different rows and heads, so that some sit at no special place."""
+    w = small("prefill_8k_on_1m", num_q_heads=8, num_kv_heads=2, span_size=256, window=256, top_k=4)
+    G = w.num_q_heads // w.num_kv_heads
+    if kind == "prefill":
+        prefix, chunk = 3072, 256
+        c = Case(w, [prefix + chunk])
+        qs = WL.queries(w, 0, prefix, chunk)
+        # rows t in [3072, 3328) all see window span 11 = keys [2816, 3072) in full
+        targets = [(r, h, 2816 + 70 + 23 * i) for i, (r, h) in enumerate([(10, 0), (60, 3), (100, 5), (150, 2),
+                                                                          (200, 7), (250, 1)])]
+        qrows = [qs[r, h] for r, h, _ in targets]
+    else:
+        L = 2600
+        c = Case(w, [L])
+        pos = np.arange(L - 200, L)
+        targets = [(r, h, 700 + 211 * i) for i, (r, h) in enumerate([(5, 0), (40, 3), (100, 5), (130, 2),
+                                                                    (170, 7), (199, 1)])]
+        qrows = [WL.query_at(w, 0, int(pos[r]))[h] for r, h, _ in targets]
+    kh, _ = c.host[0]
+    for (r, h, p), qrow in zip(targets, qrows):
+        bits, kdev = _aligned_outlier_key(qrow, w.head_dim, 160.0)
+        kh[h // G, p, :] = bits
+        c.K[0, h // G, p, :] = kdev.to("cuda")
+    c._problems.clear()
+    if kind == "prefill":
+        c.summarize([0], [prefix], prefix)
+        rows, q = c.chunk_rows(0, prefix, chunk)
+        c.summarize([prefix], [prefix + chunk], chunk)
+        c.attend(rows, ra.RA_OP_PREFILL)
+        stats = c.check([0] * chunk, np.arange(prefix, prefix + chunk), q, np.arange(chunk))
+        assert_stats(stats, True)
+    else:
+        rows, q = c.rows_for(np.zeros(len(pos), dtype=np.int64), pos)
+        out = torch.empty(len(pos), w.num_q_heads, w.head_dim, device="cuda")
+        ra.attn_dense_causal(c.cfg, rows, c.K, c.V, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for i, t in enumerate(pos):
+            for hh in range(w.num_q_heads):
+                ma, rel = O.output_errors(got[i, hh], c.problem(0).dense_row(q[i][hh], hh, int(t)))
+                assert ma <= O.compare.TOL_ABS["bf16"] and rel <= O.compare.TOL_REL_L2_BF16, (i, hh, ma, rel)
+
+
 def test_empty_rows_are_a_no_op():
     w = small("ragged_decode_16", batch=1, span_size=64, window=64, top_k=8, ragged=(0, 0), decode_len=2000)
     c = Case(w, [2000])

@@ -316,6 +316,19 @@ def test_planted_needle_is_routed():
 
 
 # --------------------------------------------------------------------------------- comparator
+def test_comparator_rejects_non_finite_outputs():
+    """A NaN or infinite output element is an infinite error (and max() keeps it)."""
+    ref = np.array([0.5, -1.0, 2.0])
+    for bad in (np.nan, np.inf, -np.inf):
+        got = ref.copy()
+        got[1] = bad
+        ma, rel = O.output_errors(got, ref)
+        assert ma == np.inf and rel == np.inf
+        assert max(0.0, ma) == np.inf
+        assert not O.output_ok(got, ref, True)[0] and not O.output_ok(got, ref, False)[0]
+    assert O.output_errors(ref, ref) == (0.0, 0.0)
+
+
 def test_comparator_accepts_near_ties_and_rejects_real_swaps():
     scores = np.array([1.0, 0.5, 0.5000001, 0.2, -1.0])
     oracle_sel = O.select_spans(scores, 2)
