@@ -612,8 +612,9 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
             for (int et = 0; et < ET; ++et) o[g][et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     };
-    const float unset[kQG] = {NEG, NEG};
-    static_assert(kQG == 2, "unset[] lists one reference per group");
+    float unset[kQG];
+#pragma unroll
+    for (int g = 0; g < kQG; ++g) unset[g] = NEG;
     reset(unset);
     fast_sweep<D>(st, tk, true, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
     // a valid query whose row sum passed 2^kFastLog2 (or is not finite) sends the tile to a
@@ -628,7 +629,9 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int w = 0; w < kMfmaWaves; ++w) redo |= redo_s[w];
     if (redo) {
-        float mx[kQG] = {NEG, NEG};
+        float mx[kQG];
+#pragma unroll
+        for (int g = 0; g < kQG; ++g) mx[g] = NEG;
         max_sweep<D>(st, tk, qlim, kof, qb, mx, wave, lane, lg, scale_log2);
         reset(mx);
         fast_sweep<D>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
@@ -801,7 +804,9 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
                 for (int et = 0; et < ET; ++et) o[gi][et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
         };
-        const float unset[kQG] = {NEG, NEG};
+        float unset[kQG];
+#pragma unroll
+        for (int gi = 0; gi < kQG; ++gi) unset[gi] = NEG;
         reset(unset);
         fast_sweep<D>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
         // as in the routed tiles: a row sum past 2^kFastLog2 sends the tile to a second pass
@@ -815,7 +820,9 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
 #pragma unroll
         for (int w = 0; w < kMfmaWaves; ++w) redo |= redo_s[w];
         if (redo) {
-            float mx[kQG] = {NEG, NEG};
+            float mx[kQG];
+#pragma unroll
+        for (int g = 0; g < kQG; ++g) mx[g] = NEG;
             max_sweep<D>(st, tk, qlim, kof, qb, mx, wave, lane, lg, scale_log2);
             reset(mx);
             fast_sweep<D>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
