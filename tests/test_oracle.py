@@ -353,3 +353,83 @@ def test_search_budget_grows_like_sqrt_of_context():
         t = L - 1
         budget.append(O.num_routable(t, S, S) + 1)  # spans scored by the last query (+ its window span)
     assert abs(budget[1] / budget[0] - claim["search_budget_growth"]) <= claim["tolerance"]
+
+
+# ------------------------------------------------------------------------------ 8-bit cache
+def test_e4m3_decode_follows_the_format_and_torch():
+    """Every E4M3 bit pattern decodes as the format defines (bias 7, subnormals 2^-6 f/8, one NaN
+    pattern per sign, no infinity), and as torch's float8_e4m3fn does."""
+    Q = O.kv_fp8
+    assert Q.e4m3_decode(np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x3C, 0x7E, 0x80, 0xFE], np.uint8)).tolist() == [
+        0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.5, 448.0, -0.0, -448.0]
+    assert np.isnan(Q.e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all()
+    codes = np.arange(256, dtype=np.uint8)
+    ours = Q.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[~np.isnan(ours)], ref[~np.isnan(ref)])
+
+
+def test_e4m3_encode_rounds_to_nearest_even():
+    Q = O.kv_fp8
+    cases = {1.0625: 0x38, 1.1875: 0x3A, 2.0 ** -10: 0x00, 3 * 2.0 ** -11: 0x01, 1.5 * 2.0 ** -9: 0x02,
+             448.0: 0x7E, 440.0: 0x7E, 432.0: 0x7E, 431.9: 0x7D, -1.0: 0xB8, 2.0 ** -6: 0x08}
+    for x, c in cases.items():
+        assert int(Q.e4m3_encode(np.array([x]))[0]) == c, (x, c)
+    # every value back to itself, and a dense sweep against torch (its conversion rounds the same
+    # way inside the clamped range)
+    vals = Q.e4m3_decode(np.arange(256, dtype=np.uint8))
+    ok = ~np.isnan(vals)
+    assert np.array_equal(Q.e4m3_decode(Q.e4m3_encode(vals[ok])), vals[ok])
+    x = np.concatenate([np.linspace(-448, 448, 100001), np.ldexp(np.linspace(-1, 1, 2001), -5)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(Q.e4m3_encode(x), ref)
+
+
+def test_row_quantisation_error_and_special_rows():
+    """Each element lands within half an E4M3 step (times the row scale) of its value, the row
+    maximum maps to +-448, and an all-zero row gets codes 0 and scale 1."""
+    Q = O.kv_fp8
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((64, 128)) * np.exp(rng.uniform(-6, 6, (64, 1)))).astype(np.float32)
+    x[3] = 0.0
+    codes, s = Q.quantize_rows(x)
+    assert codes.dtype == np.uint8 and s.dtype == np.float32
+    assert np.all(codes[3] == 0) and s[3] == 1.0
+    back = Q.dequantize_rows(codes, s).astype(np.float64)
+    q = x.astype(np.float64) / s[:, None].astype(np.float64)
+    _, u = np.frexp(q)
+    step = np.ldexp(1.0, np.maximum(u - 4, -9))
+    err = np.abs(back - x) / s[:, None]
+    assert np.all(err <= 0.5 * step * (1 + 1e-6) + 1e-6)
+    nz = np.arange(64) != 3
+    assert np.all(np.abs(Q.e4m3_decode(codes[nz])).max(axis=1) == 448.0)
+
+
+def test_fp8_problem_reads_the_dequantised_cache():
+    """With values that E4M3 and their scale represent exactly, the 8-bit problem equals the
+    float32 problem of the same values (routing on bf16-rounded means, bf16 queries)."""
+    Q = O.kv_fp8
+    rng = np.random.default_rng(6)
+    Hkv, L, d, S, W, k = 2, 96, 64, 16, 16, 3
+    vals = Q.e4m3_decode(np.arange(0, 0x7E, dtype=np.uint8))
+    kq = rng.choice(vals, size=(Hkv, L, d)) * rng.choice([-1, 1], size=(Hkv, L, d))
+    vq = rng.choice(vals, size=(Hkv, L, d)) * rng.choice([-1, 1], size=(Hkv, L, d))
+    kq[..., 0] = 448.0
+    vq[..., 0] = -448.0  # row maxima 448: scale 1, codes = values
+    kc, ks = Q.quantize_rows(kq.astype(np.float32))
+    vc, vs = Q.quantize_rows(vq.astype(np.float32))
+    assert np.all(ks == 1.0) and np.all(vs == 1.0)
+    prob8 = Q.Fp8Problem(kc, ks, vc, vs, L, 4, S, k, W)
+    qb = (rng.standard_normal((4, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    probf = O.Problem(kq.astype(np.float32), vq.astype(np.float32), L, 4, S, k, W, False)
+    for h in range(4):
+        for t in (40, 95):
+            a = prob8.row(qb[h], h, t)
+            qf = O.widen(qb[h], True).astype(np.float32)
+            b = probf.row(qf, h, t)
+            assert np.array_equal(a["out"], b["out"])
+            # routing: bf16-rounded means (kappa), as the bf16 path
+            assert np.array_equal(a["scores"], O.route_scores(O.widen(qb[h], True), probf.means[h // 2],
+                                                              len(a["scores"]), True))
+
