@@ -40,6 +40,7 @@ def parse():
     p.add_argument("--prefill-steps", type=int, default=5)
     p.add_argument("--dense-steps", type=int, default=2,
                    help="timed calls of dense causal attention on the prefill rows (0: skip)")
+    p.add_argument("--no-fp8", action="store_true", help="skip the decode step over the 8-bit cache")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 256 MiB device copy (reference kernel for HBM byte counters)")
     return p.parse_args()
@@ -217,6 +218,9 @@ def main():
         "setup_seconds": round(gen_s, 1),
     }
 
+    if not args.no_fp8:
+        result["decode_fp8"] = bench_decode_fp8(args, w, K, V, qs)
+
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -343,6 +347,97 @@ def bench_prefill(steps, dense_steps=2):
         "step_tflops": round((attn_flops + route_flops) / (step_ms * 1e-3) / 1e12, 1),
         "dense_causal": dense,
     }
+
+
+def bench_decode_fp8(args, w, K, V, qs):
+    """The decode step over the 8-bit cache: the same sequences quantised to E4M3 codes with one
+    fp32 scale per (kv head, token) row (kv_quantize_fp8, untimed setup); a step is
+    span_summary_update_fp8 (the new token) -> route_scores -> topk_spans -> routed_attn_decode_fp8."""
+    import torch
+
+    import content_routed_sparse_amd as ra
+
+    L, NC, dev = w.decode_len, K.shape[0], K.device
+    cfg1 = ra.Config(w.num_q_heads, w.num_kv_heads, w.head_dim, w.span_size, w.top_k, w.window, ra.RA_BF16, 1, L)
+    K8 = torch.empty(K.shape, dtype=torch.uint8, device=dev)
+    V8 = torch.empty_like(K8)
+    KS = torch.empty(K.shape[:3], dtype=torch.float32, device=dev)
+    VS = torch.empty_like(KS)
+    zero = torch.zeros(1, dtype=torch.int64, device=dev)
+    full = torch.full((1,), L, dtype=torch.int64, device=dev)
+    before = torch.full((1,), L - 1, dtype=torch.int64, device=dev)
+    stride = cfg1.num_routable(L - 1)
+    ws = torch.empty(ra.workspace_bytes(cfg1, ra.RA_OP_DECODE, 1, L - 1), dtype=torch.uint8, device=dev)
+    st = []
+    for s in range(NC):
+        ra.kv_quantize_fp8(cfg1, K[s:s + 1], K8[s:s + 1], KS[s:s + 1], zero, full, L)
+        ra.kv_quantize_fp8(cfg1, V[s:s + 1], V8[s:s + 1], VS[s:s + 1], zero, full, L)
+        d = {"k": K8[s:s + 1], "v": V8[s:s + 1], "ks": KS[s:s + 1], "vs": VS[s:s + 1],
+             "mean": torch.zeros(1, w.num_kv_heads, cfg1.max_spans, w.head_dim, dtype=torch.float32, device=dev),
+             "run": torch.zeros(1, w.num_kv_heads, w.head_dim, dtype=torch.float32, device=dev),
+             "rows": ra.Rows(qs[s], torch.zeros(1, dtype=torch.int32, device=dev),
+                             torch.full((1,), L - 1, dtype=torch.int64, device=dev), L - 1),
+             "scores": torch.empty(1, w.num_q_heads, stride, dtype=torch.float32, device=dev),
+             "sel": torch.empty(1, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev),
+             "out": torch.empty(1, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)}
+        ra.span_summary_update_fp8(cfg1, d["k"], d["ks"], d["mean"], d["run"], zero, before, L - 1)
+        d["front"] = [ra.prepare("span_summary_update_fp8", cfg1, d["k"], d["ks"], d["mean"], d["run"], before, full, 1),
+                      ra.prepare("route_scores", cfg1, d["rows"], d["mean"], d["scores"]),
+                      ra.prepare("topk_spans", cfg1, d["rows"], d["scores"], d["sel"])]
+        d["attn"] = ra.prepare("routed_attn_decode_fp8", cfg1, d["rows"], d["k"], d["v"], d["ks"], d["vs"], d["sel"],
+                               d["out"], ws)
+        st.append(d)
+    torch.cuda.synchronize()
+    for d in st:
+        for c in d["front"]:
+            c()
+        d["attn"]()
+    torch.cuda.synchronize()
+    first = [d["out"].clone() for d in st]
+    stream = torch.cuda.current_stream()
+    EV_EVERY = 8
+    timed_ev = list(range(0, args.steps, EV_EVERY))
+    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in timed_ev}
+
+    def step(i, timed):
+        d = st[i % NC]
+        for c in d["front"]:
+            c()
+        if timed and i in ev:
+            ev[i][0].record(stream)
+        d["attn"]()
+        if timed and i in ev:
+            ev[i][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev.values()]))
+    same = all(torch.equal(first[s], st[s]["out"]) for s in range(NC))
+    # algorithmic bytes: codes (1 byte per value) and row scales (4 bytes) of the K and V rows of
+    # each kv head's union of selected spans plus the window, q (bf16) and out (fp32)
+    G = w.group
+    win = (L - 1) - (w.span_size * (max(0, L - 1 - w.window + 1) // w.span_size)) + 1
+    per_seq = []
+    for d in st:
+        sel = d["sel"][0].cpu().numpy()
+        uni = sum(len(set(sel[g * G:(g + 1) * G].ravel().tolist()) - {-1}) for g in range(w.num_kv_heads))
+        rows_kv = uni * w.span_size + w.num_kv_heads * win
+        per_seq.append(rows_kv * (w.head_dim + 4) * 2 + w.num_q_heads * w.head_dim * (2 + 4))
+    bytes_step = float(np.mean([per_seq[i % NC] for i in timed_ev]))
+    achieved = bytes_step / (attn_ms * 1e-3) / 1e9
+    return {"workload": "decode_1m, 8-bit cache (E4M3 codes, one fp32 scale per kv-head row)",
+            "value": round(1000.0 / ms, 2), "unit": "tokens/s", "ms_per_step": round(ms, 5),
+            "roofline": {"bound": "hbm", "kernel": "routed_attn_decode_fp8 (decode_attn + combine_block)",
+                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": int(bytes_step), "avg_launch_ms": round(attn_ms, 5)},
+            "repeat_bitwise_identical": bool(same)}
 
 
 def cpu_baseline(w, d0, seconds):

@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(HERE, "libroutedattn.so")
 RA_F32, RA_BF16 = 0, 1
 RA_OP_DECODE, RA_OP_PREFILL = 0, 1
 EXPORTED = ("span_summary_update", "route_scores", "topk_spans", "routed_attn_decode", "routed_attn_prefill",
-            "attn_dense_causal", "ra_workspace_bytes", "ra_status_string", "ra_last_error")
+            "attn_dense_causal", "kv_quantize_fp8", "span_summary_update_fp8", "routed_attn_decode_fp8",
+            "ra_workspace_bytes", "ra_status_string", "ra_last_error")
 
 
 class RoutedAttnError(RuntimeError):
@@ -63,6 +64,9 @@ def lib():
             "routed_attn_decode": [CP, RP, P, P, P, P, P, SZ, P],
             "routed_attn_prefill": [CP, RP, P, P, P, P, P, SZ, P],
             "attn_dense_causal": [CP, RP, P, P, P, P],
+            "kv_quantize_fp8": [CP, P, P, P, P, P, I64, P],
+            "span_summary_update_fp8": [CP, P, P, P, P, P, P, I64, P],
+            "routed_attn_decode_fp8": [CP, RP, P, P, P, P, P, P, P, SZ, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -220,6 +224,50 @@ def _args_dense(cfg, rows, k_cache, v_cache, out, stream=None):
             _dev(out, torch.float32, (n, cfg.num_q_heads, cfg.head_dim), "out"), _stream(stream)), (c, r)
 
 
+# 8-bit cache: codes [B][Hkv][cap][d] uint8, scales [B][Hkv][cap] float32; queries bf16.
+def _scale_shape(cfg):
+    return (cfg.batch, cfg.num_kv_heads, cfg.capacity)
+
+
+def _bf16_cfg(cfg):
+    if cfg.dtype != RA_BF16:
+        raise ValueError("8-bit caches go with bf16 queries: cfg.dtype must be RA_BF16")
+
+
+def _args_kv_quantize_fp8(cfg, src, codes, scales, old_len, new_len, max_new_tokens, stream=None):
+    _bf16_cfg(cfg)
+    c = cfg.c()
+    return (ctypes.byref(c), _dev(src, torch.bfloat16, _kv_shape(cfg), "src"),
+            _dev(codes, torch.uint8, _kv_shape(cfg), "codes"), _dev(scales, torch.float32, _scale_shape(cfg), "scales"),
+            _dev(old_len, torch.int64, (cfg.batch,), "old_len"), _dev(new_len, torch.int64, (cfg.batch,), "new_len"),
+            int(max_new_tokens), _stream(stream)), (c,)
+
+
+def _args_span_summary_update_fp8(cfg, k_codes, k_scales, span_mean, run_sum, old_len, new_len, max_new_tokens,
+                                  stream=None):
+    _bf16_cfg(cfg)
+    c = cfg.c()
+    return (ctypes.byref(c), _dev(k_codes, torch.uint8, _kv_shape(cfg), "k_codes"),
+            _dev(k_scales, torch.float32, _scale_shape(cfg), "k_scales"),
+            _dev(span_mean, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.max_spans, cfg.head_dim), "span_mean"),
+            _dev(run_sum, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.head_dim), "run_sum"),
+            _dev(old_len, torch.int64, (cfg.batch,), "old_len"), _dev(new_len, torch.int64, (cfg.batch,), "new_len"),
+            int(max_new_tokens), _stream(stream)), (c,)
+
+
+def _args_attn_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, workspace, stream=None):
+    _bf16_cfg(cfg)
+    c, r = cfg.c(), _rows(cfg, rows)
+    n = rows.q.shape[0]
+    return (ctypes.byref(c), ctypes.byref(r), _dev(k_codes, torch.uint8, _kv_shape(cfg), "k_codes"),
+            _dev(v_codes, torch.uint8, _kv_shape(cfg), "v_codes"),
+            _dev(k_scales, torch.float32, _scale_shape(cfg), "k_scales"),
+            _dev(v_scales, torch.float32, _scale_shape(cfg), "v_scales"),
+            _dev(sel, torch.int32, (n, cfg.num_q_heads, cfg.top_k), "sel"),
+            _dev(out, torch.float32, (n, cfg.num_q_heads, cfg.head_dim), "out"),
+            _dev(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream)), (c, r)
+
+
 _BUILDERS = {
     "span_summary_update": _args_span_summary_update,
     "route_scores": _args_route_scores,
@@ -227,6 +275,9 @@ _BUILDERS = {
     "routed_attn_decode": _args_attn,
     "routed_attn_prefill": _args_attn,
     "attn_dense_causal": _args_dense,
+    "kv_quantize_fp8": _args_kv_quantize_fp8,
+    "span_summary_update_fp8": _args_span_summary_update_fp8,
+    "routed_attn_decode_fp8": _args_attn_fp8,
 }
 
 
@@ -299,6 +350,26 @@ def attn_dense_causal(cfg, rows, k_cache, v_cache, out, stream=None):
     """Exact attention over every key at or before each row's position (bf16; no workspace)."""
     args, _keep = _args_dense(cfg, rows, k_cache, v_cache, out, stream)
     _check(lib().attn_dense_causal(*args))
+
+
+def kv_quantize_fp8(cfg, src, codes, scales, old_len, new_len, max_new_tokens, stream=None):
+    """8-bit cache: E4M3 codes and per-row scales of rows [old_len[b], new_len[b]) of a bf16 cache."""
+    args, _keep = _args_kv_quantize_fp8(cfg, src, codes, scales, old_len, new_len, max_new_tokens, stream)
+    _check(lib().kv_quantize_fp8(*args))
+
+
+def span_summary_update_fp8(cfg, k_codes, k_scales, span_mean, run_sum, old_len, new_len, max_new_tokens,
+                            stream=None):
+    """span_summary_update over an 8-bit K cache (sums of the dequantised values)."""
+    args, _keep = _args_span_summary_update_fp8(cfg, k_codes, k_scales, span_mean, run_sum, old_len, new_len,
+                                                max_new_tokens, stream)
+    _check(lib().span_summary_update_fp8(*args))
+
+
+def routed_attn_decode_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, workspace, stream=None):
+    """routed_attn_decode over an 8-bit K/V cache (bf16 queries)."""
+    args, _keep = _args_attn_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, workspace, stream)
+    _check(lib().routed_attn_decode_fp8(*args))
 
 
 class Pipeline:

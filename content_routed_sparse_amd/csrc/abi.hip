@@ -123,6 +123,7 @@ ra_status span_summary_update(const ra_config *cfg, const void *k_cache, float *
     if ((int64_t)cfg->batch * cfg->num_kv_heads * U >= kMaxGrid) return fail(RA_EUNSUPPORTED, "grid too large");
     ra::SummaryArgs a;
     a.k = k_cache;
+    a.kscale = nullptr;
     a.mean = span_mean;
     a.run_sum = run_sum;
     a.old_len = old_len;
@@ -201,6 +202,78 @@ ra_status attn_dense_causal(const ra_config *cfg, const ra_rows *rows, const voi
     const int RT = 128 / a.G;
     if (a.Hkv * ra::ceil_div(a.n_rows, RT) >= kMaxGrid) return fail(RA_EUNSUPPORTED, "too many rows");
     return hip_status(ra::launch_dense(a, k_cache, v_cache, out, (hipStream_t)stream), "attn_dense_causal launch");
+}
+
+// ------------------------------------------------------------------------- 8-bit K/V cache
+ra_status kv_quantize_fp8(const ra_config *cfg, const void *src_cache, uint8_t *codes, float *scales,
+                          const int64_t *old_len, const int64_t *new_len, int64_t max_new_tokens, void *stream) {
+    ra_status s = check_config(cfg);
+    if (s) return s;
+    if (cfg->dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "kv_quantize_fp8 takes a bf16 cache (cfg->dtype RA_BF16)");
+    if (!src_cache || !codes || !scales || !old_len || !new_len) return fail(RA_EINVAL, "NULL pointer argument");
+    if (max_new_tokens < 0) return fail(RA_EINVAL, "max_new_tokens must be >= 0");
+    if (max_new_tokens > cfg->capacity) return fail(RA_ECAPACITY, "max_new_tokens exceeds capacity");
+    if (max_new_tokens == 0) return ok();
+    const int rpb = 256 / (cfg->head_dim / 8);
+    if ((int64_t)cfg->batch * cfg->num_kv_heads * ra::ceil_div(max_new_tokens, rpb) >= kMaxGrid)
+        return fail(RA_EUNSUPPORTED, "grid too large");
+    ra::QuantArgs a;
+    a.src = (const uint16_t *)src_cache;
+    a.dst = codes;
+    a.scale = scales;
+    a.old_len = old_len;
+    a.new_len = new_len;
+    a.d = cfg->head_dim;
+    a.B = cfg->batch;
+    a.Hkv = cfg->num_kv_heads;
+    a.cap = cfg->capacity;
+    a.max_new = max_new_tokens;
+    return hip_status(ra::launch_quantize_fp8(a, (hipStream_t)stream), "kv_quantize_fp8 launch");
+}
+
+ra_status span_summary_update_fp8(const ra_config *cfg, const uint8_t *k_codes, const float *k_scales,
+                                  float *span_mean, float *run_sum, const int64_t *old_len, const int64_t *new_len,
+                                  int64_t max_new_tokens, void *stream) {
+    ra_status s = check_config(cfg);
+    if (s) return s;
+    if (cfg->dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "8-bit caches go with bf16 queries (cfg->dtype RA_BF16)");
+    if (!k_codes || !k_scales || !span_mean || !run_sum || !old_len || !new_len)
+        return fail(RA_EINVAL, "NULL pointer argument");
+    if (max_new_tokens < 0) return fail(RA_EINVAL, "max_new_tokens must be >= 0");
+    if (max_new_tokens > cfg->capacity) return fail(RA_ECAPACITY, "max_new_tokens exceeds capacity");
+    if (max_new_tokens == 0) return ok();
+    const int64_t U = (max_new_tokens - 1 + cfg->span_size - 1) / cfg->span_size + 1;
+    if ((int64_t)cfg->batch * cfg->num_kv_heads * U >= kMaxGrid) return fail(RA_EUNSUPPORTED, "grid too large");
+    ra::SummaryArgs a;
+    a.k = k_codes;
+    a.kscale = k_scales;
+    a.mean = span_mean;
+    a.run_sum = run_sum;
+    a.old_len = old_len;
+    a.new_len = new_len;
+    a.dtype = ra::kCacheFp8;
+    a.d = cfg->head_dim;
+    a.B = cfg->batch;
+    a.Hkv = cfg->num_kv_heads;
+    a.S = cfg->span_size;
+    a.cap = cfg->capacity;
+    a.max_spans = cfg->max_spans;
+    a.max_new = max_new_tokens;
+    return hip_status(ra::launch_summary(a, (hipStream_t)stream), "span_summary_update_fp8 launch");
+}
+
+ra_status routed_attn_decode_fp8(const ra_config *cfg, const ra_rows *rows, const uint8_t *k_codes,
+                                 const uint8_t *v_codes, const float *k_scales, const float *v_scales,
+                                 const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    ra_status s = check_attn(cfg, rows, k_codes, v_codes, sel, out, workspace, workspace_bytes, RA_OP_DECODE);
+    if (s) return s;
+    if (cfg->dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "8-bit caches go with bf16 queries (cfg->dtype RA_BF16)");
+    if (rows->n_rows > 0 && (!k_scales || !v_scales)) return fail(RA_EINVAL, "NULL k_scales or v_scales");
+    if (rows->n_rows == 0) return ok();
+    return hip_status(ra::launch_decode_fp8(row_args(cfg, rows), k_codes, v_codes, k_scales, v_scales, sel, out,
+                                            workspace, (hipStream_t)stream),
+                      "routed_attn_decode_fp8 launch");
 }
 
 size_t ra_workspace_bytes(const ra_config *cfg, int32_t op, int64_t n_rows, int64_t max_pos) {

@@ -25,6 +25,8 @@
 #include "kernels.h"
 #include "wave_ops.h"
 
+#include <type_traits>
+
 namespace ra {
 
 template <typename T, int D, int NWAVE, int KPW_>
@@ -44,6 +46,20 @@ __device__ __forceinline__ void unpack16(const uint4 &raw, float *f, uint16_t) {
     for (int i = 0; i < 4; ++i) {
         f[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
         f[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+}
+// 16 E4M3 codes of an 8-bit cache row (exact conversions; the row scale is applied separately).
+__device__ __forceinline__ void unpack16(const uint4 &raw, float *f, uint8_t) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+        f[4 * i] = lo.x;
+        f[4 * i + 1] = lo.y;
+        f[4 * i + 2] = hi.x;
+        f[4 * i + 3] = hi.y;
     }
 }
 __device__ __forceinline__ void unpack16(const uint4 &raw, float *f, float) {
@@ -82,15 +98,22 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kSelRegChunks = 4;  // selection entries of a kv head kept in registers: G*k <= 256
 constexpr int kMaxSelChunks = 32;  // G*k <= 32 * 64
 
+// T: element type of the K/V cache (fp32, bf16 bits, or 8-bit E4M3 codes with row scales ks,
+// vs); queries are of the same type, bf16 for an 8-bit cache.
 template <typename T, int D, int NWAVE, int KPW_>
-__global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ q, const int32_t *__restrict__ row_seq,
+__global__ void __launch_bounds__(NWAVE * 64) decode_attn(const void *__restrict__ qv, const int32_t *__restrict__ row_seq,
                                                    const int64_t *__restrict__ row_pos, const T *K, const T *V,
+                                                   const float *__restrict__ ks, const float *__restrict__ vs,
                                                    const int32_t *__restrict__ sel, float *__restrict__ part, int Hq,
                                                    int Hkv, int G, int S, int k, int W, int B, int64_t cap,
                                                    int64_t max_pos, int64_t n_rows_total, int NW, int nsub,
                                                    float scale_log2) {
     using L = Lanes<T, D, NWAVE, KPW_>;
     constexpr int EPL = L::EPL, LPR = L::LPR, RPI = L::RPI, KPW = L::KPW, STEPS = L::STEPS, TK = L::TK;
+    constexpr bool FP8 = sizeof(T) == 1;
+    using TQ = typename std::conditional<FP8, uint16_t, T>::type;
+    constexpr int QLOADS = FP8 ? 2 : 1;  // 16-byte loads of the lane's query slice
+    const TQ *q = reinterpret_cast<const TQ *>(qv);
     constexpr int DUP = L::DUP;
     __shared__ float pbuf[NWAVE][64];
     __shared__ uint64_t mask_s[NWAVE][kMaxSelChunks];
@@ -98,7 +121,7 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
     __shared__ float wo[NWAVE][D];
 
     // all kernel arguments in one round trip (otherwise some are fetched only where first used)
-    asm volatile("" ::"s"(q), "s"(row_seq), "s"(row_pos), "s"(K), "s"(V), "s"(sel), "s"(part), "s"(Hq), "s"(Hkv),
+    asm volatile("" ::"s"(qv), "s"(row_seq), "s"(row_pos), "s"(K), "s"(V), "s"(ks), "s"(vs), "s"(sel), "s"(part), "s"(Hq), "s"(Hkv),
                  "s"(G), "s"(S), "s"(k), "s"(W), "s"(B), "s"(cap), "s"(max_pos), "s"(n_rows_total), "s"(NW),
                  "s"(nsub), "s"(scale_log2));
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -235,7 +258,10 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
         const int64_t uhi = ulo + TK < hi ? ulo + TK : hi;
         const int c = lane % LPR, rr = lane / LPR;
         const int h0 = (int)__builtin_ctz(hw);
-        uint4 qraw = *reinterpret_cast<const uint4 *>(q + (row * Hq + g * G + h0) * D + c * EPL);
+        uint4 qraw[QLOADS];
+#pragma unroll
+        for (int i = 0; i < QLOADS; ++i)
+            qraw[i] = *reinterpret_cast<const uint4 *>(q + (row * Hq + g * G + h0) * D + c * EPL + 8 * i);
 
         // stream this wave's keys: all K and V loads are issued before any use
         const int64_t kv_base = ((int64_t)seq * Hkv + g) * cap;
@@ -253,11 +279,19 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
             const int64_t kl = key < uhi ? key : uhi - 1;
             vr[s] = load_stream(V + (kv_base + kl) * D + c * EPL);
         }
-        asm volatile("" ::: "memory");  // keep the loads here: nothing may sink them into the head loop
-
         // the key whose score this lane holds after the reduce-scatter
         const int s_own = c / DUP;
-        const bool own_valid = wkey0 + s_own * RPI + rr < uhi;
+        const int64_t own_key = wkey0 + s_own * RPI + rr;
+        const bool own_valid = own_key < uhi;
+        // 8-bit cache: that key's K and V row scales
+        float ksc = 1.f, vsc = 1.f;
+        if constexpr (FP8) {
+            const int64_t kl = own_key < uhi ? own_key : uhi - 1;
+            ksc = ks[kv_base + kl];
+            vsc = vs[kv_base + kl];
+        }
+        asm volatile("" ::: "memory");  // keep the loads here: nothing may sink them into the head loop
+
         const bool counts = (c % DUP) == 0;  // one lane per key contributes to the sum
 
         uint32_t rem = hw;
@@ -272,16 +306,34 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
 #pragma unroll
             for (int s = 0; s < STEPS; ++s)
                 asm volatile("" : "+v"(kr[s].x), "+v"(kr[s].y), "+v"(kr[s].z), "+v"(kr[s].w));
-            if (!first) qraw = *reinterpret_cast<const uint4 *>(q + (row * Hq + hq) * D + c * EPL);
+            if (!first) {
+#pragma unroll
+                for (int i = 0; i < QLOADS; ++i)
+                    qraw[i] = *reinterpret_cast<const uint4 *>(q + (row * Hq + hq) * D + c * EPL + 8 * i);
+            }
             first = false;
             float acc[STEPS];
-            if constexpr (sizeof(T) == 2) {
+            if constexpr (FP8) {
+                // bf16 query slice against 16 codes per row; the row scale multiplies the sum
+                float qf[EPL];
+                unpack16(qraw[0], qf, uint16_t());
+                unpack16(qraw[1], qf + 8, uint16_t());
+#pragma unroll
+                for (int s = 0; s < STEPS; ++s) {
+                    float kf[EPL];
+                    unpack16(kr[s], kf, T());
+                    float a = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) a = fmaf(qf[e], kf[e], a);
+                    acc[s] = a;
+                }
+            } else if constexpr (sizeof(T) == 2) {
                 // bf16: packed pairs straight into v_dot2_f32_bf16 (exact products, fp32 sums)
 #pragma unroll
-                for (int s = 0; s < STEPS; ++s) acc[s] = dot8_bf16(qraw, kr[s]);
+                for (int s = 0; s < STEPS; ++s) acc[s] = dot8_bf16(qraw[0], kr[s]);
             } else {
                 float qf[EPL];
-                unpack16(qraw, qf, T());
+                unpack16(qraw[0], qf, T());
 #pragma unroll
                 for (int s = 0; s < STEPS; ++s) {
                     float kf[EPL];
@@ -294,11 +346,11 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
             }
             ReduceScatter<STEPS, ilog2(STEPS), LPR / 2>::run(acc, lane);
             const float sc = allreduce_sum<DUP / 2>(acc[0]);
-            const float z = own_valid ? sc * scale_log2 : kNegInf;
+            const float z = own_valid ? sc * ksc * scale_log2 : kNegInf;
             const float m = wave_max(z);
             const float p = (own_valid && m != kNegInf) ? exp2f(z - m) : 0.f;
             const float ls = wave_sum(counts ? p : 0.f);
-            pbuf[wave][lane] = p;
+            pbuf[wave][lane] = p * vsc;  // (8-bit cache: the V row scale rides on the weight)
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int s = 0; s < STEPS; ++s)
@@ -314,7 +366,8 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const T *__restrict__ 
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) o[e] = fmaf(ps, vf[e], o[e]);
             }
-            ReduceScatter<EPL, ilog2(RPI), 32>::run(o, lane);  // over the row groups: EPL -> EPL / RPI values
+            // over the row groups (lanes of another row group hold other elements: exact partners)
+            ReduceScatter<EPL, ilog2(RPI), 32, true>::run(o, lane);  // EPL -> EPL / RPI values
             constexpr int KEEP = EPL / RPI;
             if (lane == 0) {
                 wm[wave] = m;
@@ -569,18 +622,18 @@ int decode_keys_per_wave(const RowArgs &a) { return (a.dtype == RA_F32 && a.d ==
 
 int decode_sub_tile(const RowArgs &a) { return kDecodeWaves * decode_keys_per_wave(a); }
 
-template <typename T, int D, int KPW>
-hipError_t decode_launch_t(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out, void *ws,
-                           hipStream_t st) {
-    using L = Lanes<T, D, kDecodeWaves, KPW>;
+template <typename T, int D, int KPW, int NWAVE = kDecodeWaves>
+hipError_t decode_launch_t(const RowArgs &a, const void *K, const void *V, const float *ks, const float *vs,
+                           const int32_t *sel, float *out, void *ws, hipStream_t st) {
+    using L = Lanes<T, D, NWAVE, KPW>;
     const int NW = max_window_spans(a.S, a.W);
     const int n_slots = a.G * a.k + NW;
     const int nsub = (int)ceil_div(a.S, L::TK);
     const int64_t blocks = a.n_rows * a.Hkv * n_slots * nsub;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     float *part = (float *)ws;
-    hipLaunchKernelGGL((decode_attn<T, D, kDecodeWaves, KPW>), dim3((unsigned)blocks), dim3(kDecodeWaves * 64), 0, st,
-                       (const T *)a.q, a.row_seq, a.row_pos, (const T *)K, (const T *)V, sel, part, a.Hq, a.Hkv, a.G,
+    hipLaunchKernelGGL((decode_attn<T, D, NWAVE, KPW>), dim3((unsigned)blocks), dim3(NWAVE * 64), 0, st,
+                       a.q, a.row_seq, a.row_pos, (const T *)K, (const T *)V, ks, vs, sel, part, a.Hq, a.Hkv, a.G,
                        a.S, a.k, a.W, a.B, a.cap, a.max_pos, a.n_rows, NW, nsub, scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -602,10 +655,24 @@ hipError_t launch_decode(const RowArgs &a, const void *K, const void *V, const i
                          hipStream_t st) {
     if (a.n_rows == 0) return hipSuccess;
     if (a.dtype == RA_BF16)
-        return a.d == 64 ? decode_launch_t<uint16_t, 64, 64>(a, K, V, sel, out, ws, st)
-                         : decode_launch_t<uint16_t, 128, 64>(a, K, V, sel, out, ws, st);
-    return a.d == 64 ? decode_launch_t<float, 64, 64>(a, K, V, sel, out, ws, st)
-                     : decode_launch_t<float, 128, 32>(a, K, V, sel, out, ws, st);
+        return a.d == 64 ? decode_launch_t<uint16_t, 64, 64>(a, K, V, nullptr, nullptr, sel, out, ws, st)
+                         : decode_launch_t<uint16_t, 128, 64>(a, K, V, nullptr, nullptr, sel, out, ws, st);
+    return a.d == 64 ? decode_launch_t<float, 64, 64>(a, K, V, nullptr, nullptr, sel, out, ws, st)
+                     : decode_launch_t<float, 128, 32>(a, K, V, nullptr, nullptr, sel, out, ws, st);
+}
+
+// 8-bit cache: 64 keys per wave (a lane's reduce-scatter then ends on one key) and
+// kDecodeWavesFp8 waves per unit (measured at 1M: 4 waves 34-36 us per call, 8 waves 40 us,
+// 16 waves 56 us: the number of units matters more than the bytes in flight per unit);
+// sub-tiles at least as long as bf16's, so the workspace of routed_attn_decode suffices.
+constexpr int kDecodeWavesFp8 = 4;
+static_assert(kDecodeWavesFp8 >= kDecodeWaves, "decode_workspace_bytes sizes records for the bf16 sub-tiles");
+
+hipError_t launch_decode_fp8(const RowArgs &a, const uint8_t *K8, const uint8_t *V8, const float *ks,
+                             const float *vs, const int32_t *sel, float *out, void *ws, hipStream_t st) {
+    if (a.n_rows == 0) return hipSuccess;
+    return a.d == 64 ? decode_launch_t<uint8_t, 64, 64, kDecodeWavesFp8>(a, K8, V8, ks, vs, sel, out, ws, st)
+                     : decode_launch_t<uint8_t, 128, 64, kDecodeWavesFp8>(a, K8, V8, ks, vs, sel, out, ws, st);
 }
 
 }  // namespace ra

@@ -7,8 +7,12 @@
 
 namespace ra {
 
+// Element types of a K/V cache (internal): the config's dtype, or 8-bit codes with row scales.
+constexpr int kCacheFp8 = 2;
+
 struct SummaryArgs {
     const void *k;
+    const float *kscale;  // per (sequence, kv head, token) scales of an 8-bit cache, else unused
     float *mean, *run_sum;
     const int64_t *old_len, *new_len;
     int dtype, d, B, Hkv, S;
@@ -25,6 +29,17 @@ struct RowArgs {  // query rows and shapes shared by routing, selection and atte
 };
 
 hipError_t launch_summary(const SummaryArgs &a, hipStream_t st);
+
+// 8-bit cache: quantise rows [old_len[b], new_len[b]) of a bf16 cache into codes and scales.
+struct QuantArgs {
+    const uint16_t *src;
+    uint8_t *dst;
+    float *scale;
+    const int64_t *old_len, *new_len;
+    int d, B, Hkv;
+    int64_t cap, max_new;
+};
+hipError_t launch_quantize_fp8(const QuantArgs &a, hipStream_t st);
 hipError_t launch_route(const RowArgs &a, const float *mean, float *scores, int64_t stride, hipStream_t st);
 hipError_t launch_topk(const RowArgs &a, const float *scores, int64_t stride, int32_t *sel, hipStream_t st);
 
@@ -32,6 +47,9 @@ hipError_t launch_topk(const RowArgs &a, const float *scores, int64_t stride, in
 size_t decode_workspace_bytes(const RowArgs &a);
 hipError_t launch_decode(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out,
                          void *ws, hipStream_t st);
+// Decode over an 8-bit cache (bf16 queries): codes K8/V8 with row scales ks/vs.
+hipError_t launch_decode_fp8(const RowArgs &a, const uint8_t *K8, const uint8_t *V8, const float *ks,
+                             const float *vs, const int32_t *sel, float *out, void *ws, hipStream_t st);
 
 // Prefill: span-major dispatch + tiles + merge.
 size_t prefill_workspace_bytes(const RowArgs &a);

@@ -17,14 +17,15 @@ namespace {
 constexpr int kStageTokens = 64;  // tokens staged through LDS per step
 
 template <typename T, int D>
-__global__ void __launch_bounds__(256) summary_kernel(const T *__restrict__ K, float *__restrict__ mean,
+__global__ void __launch_bounds__(256) summary_kernel(const T *__restrict__ K, const float *__restrict__ kscale,
+                                                      float *__restrict__ mean,
                                                       float *__restrict__ run_sum,
                                                       const int64_t *__restrict__ old_len,
                                                       const int64_t *__restrict__ new_len, int Hkv, int S,
                                                       int64_t cap, int64_t max_spans, int u_base, int U) {
     __shared__ float stage[kStageTokens][D];
     // all kernel arguments in one round trip (otherwise some are fetched only where first used)
-    asm volatile("" ::"s"(K), "s"(mean), "s"(run_sum), "s"(old_len), "s"(new_len), "s"(Hkv), "s"(S), "s"(cap),
+    asm volatile("" ::"s"(K), "s"(kscale), "s"(mean), "s"(run_sum), "s"(old_len), "s"(new_len), "s"(Hkv), "s"(S), "s"(cap),
                  "s"(max_spans), "s"(u_base), "s"(U));
     const int unit = blockIdx.x;
     const int u = u_base + unit % U;
@@ -54,7 +55,19 @@ __global__ void __launch_bounds__(256) summary_kernel(const T *__restrict__ K, f
         for (int v = tid; v < n * kVecPerTok; v += blockDim.x) {
             const int tok = v / kVecPerTok, piece = v % kVecPerTok;
             const uint4 raw = *reinterpret_cast<const uint4 *>(base + (p + tok) * D + piece * kVec);
-            if constexpr (sizeof(T) == 2) {
+            if constexpr (sizeof(T) == 1) {
+                // 8-bit codes: the cache's value is fl32(E4M3^-1(c) * s), s the token's scale
+                const float sc = kscale[(int64_t)bg * cap + p + tok];
+                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float *dst = &stage[tok][piece * 16 + 4 * i];
+                    dst[0] = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 0) * sc;
+                    dst[1] = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 1) * sc;
+                    dst[2] = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 2) * sc;
+                    dst[3] = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 3) * sc;
+                }
+            } else if constexpr (sizeof(T) == 2) {
                 const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -88,12 +101,12 @@ hipError_t launch_summary_t(const SummaryArgs &a, hipStream_t st) {
     const int64_t units0 = (int64_t)a.B * a.Hkv;
     const int threads = D < 128 ? 128 : D;
     hipLaunchKernelGGL((summary_kernel<T, D>), dim3((unsigned)units0), dim3(threads), 0, st,
-                       (const T *)a.k, a.mean, a.run_sum, a.old_len, a.new_len, a.Hkv, a.S, a.cap, a.max_spans,
+                       (const T *)a.k, a.kscale, a.mean, a.run_sum, a.old_len, a.new_len, a.Hkv, a.S, a.cap, a.max_spans,
                        0, 1);
     if (U > 1) {
         const int64_t rest = U - 1;
         hipLaunchKernelGGL((summary_kernel<T, D>), dim3((unsigned)(units0 * rest)), dim3(threads), 0, st,
-                           (const T *)a.k, a.mean, a.run_sum, a.old_len, a.new_len, a.Hkv, a.S, a.cap,
+                           (const T *)a.k, a.kscale, a.mean, a.run_sum, a.old_len, a.new_len, a.Hkv, a.S, a.cap,
                            a.max_spans, 1, (int)rest);
     }
     return hipGetLastError();
@@ -102,6 +115,7 @@ hipError_t launch_summary_t(const SummaryArgs &a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_summary(const SummaryArgs &a, hipStream_t st) {
+    if (a.dtype == kCacheFp8) return a.d == 64 ? launch_summary_t<uint8_t, 64>(a, st) : launch_summary_t<uint8_t, 128>(a, st);
     if (a.dtype == RA_BF16) return a.d == 64 ? launch_summary_t<uint16_t, 64>(a, st) : launch_summary_t<uint16_t, 128>(a, st);
     return a.d == 64 ? launch_summary_t<float, 64>(a, st) : launch_summary_t<float, 128>(a, st);
 }

@@ -46,6 +46,14 @@ __device__ __forceinline__ uint32_t partner_u(uint32_t v) {
     else return (uint32_t)__shfl_xor((int)v, OFF);
 }
 
+// The lane lane ^ OFF exactly (row_half_mirror, used by partner<4>, also flips bits 0 and 1):
+// for exchanges between lanes that must agree in every other bit.
+template <int OFF>
+__device__ __forceinline__ float partner_xor(float v) {
+    if constexpr (OFF == 4) return __shfl_xor(v, 4);
+    else return partner<OFF>(v);
+}
+
 // Sum over the lanes that share all bits above log2(OFF): stages OFF, OFF/2, ..., 1.
 template <int OFF>
 __device__ __forceinline__ float allreduce_sum(float v) {
@@ -108,26 +116,27 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 }
 
 // One butterfly stage of a reduce-scatter: lanes that differ in bit log2(OFF) exchange halves
-// of their N values and add; the lane whose bit is set keeps the upper half.
-template <int N, int OFF>
+// of their N values and add; the lane whose bit is set keeps the upper half.  EXACT: the
+// partner is lane ^ OFF (needed when the lanes below bit log2(OFF) hold different data).
+template <int N, int OFF, bool EXACT>
 __device__ __forceinline__ void rs_stage(float *v, int lane) {
     const bool hi = (lane & OFF) != 0;
 #pragma unroll
     for (int i = 0; i < N / 2; ++i) {
         const float keep = hi ? v[i + N / 2] : v[i];
         const float send = hi ? v[i] : v[i + N / 2];
-        v[i] = keep + partner<OFF>(send);
+        v[i] = keep + (EXACT ? partner_xor<OFF>(send) : partner<OFF>(send));
     }
 }
 
 // STAGES stages over N values at offsets OFF, OFF/2, ...: N -> N / 2^STAGES values per lane,
 // each summed over 2^STAGES lanes.  With all stages, lane bits (high to low) index the value.
-template <int N, int STAGES, int OFF>
+template <int N, int STAGES, int OFF, bool EXACT = false>
 struct ReduceScatter {
     __device__ __forceinline__ static void run(float *v, int lane) {
         if constexpr (STAGES > 0) {
-            rs_stage<N, OFF>(v, lane);
-            ReduceScatter<N / 2, STAGES - 1, OFF / 2>::run(v, lane);
+            rs_stage<N, OFF, EXACT>(v, lane);
+            ReduceScatter<N / 2, STAGES - 1, OFF / 2, EXACT>::run(v, lane);
         }
     }
 };

@@ -164,6 +164,37 @@ ra_status routed_attn_prefill(const ra_config *cfg, const ra_rows *rows, const v
 ra_status attn_dense_causal(const ra_config *cfg, const ra_rows *rows, const void *k_cache, const void *v_cache,
                             float *out, void *stream);
 
+/*
+ * 8-bit K/V cache.  The release post ("Limitations and next steps") plans 8-bit quantisation
+ * without a format; this library's: every (sequence, kv head, token) row of d values is stored
+ * as FP8 E4M3 codes (finite variant: bias 7, subnormals, largest value 448, no infinity) with
+ * one fp32 scale s = max|x| / 448 (1 for an all-zero row); code = E4M3(x / s) rounded to nearest
+ * even after clamping to +-448.  The cache then holds fl32(E4M3^-1(code) * s), and summaries,
+ * routing and attention read those values; queries stay bf16 (cfg->dtype = RA_BF16) and routing
+ * rounds the means to bf16 as for a bf16 cache.
+ * Layouts: codes [batch][Hkv][capacity][d] uint8, scales [batch][Hkv][capacity] float.
+ */
+
+/* kv_quantize_fp8 -- quantise rows [old_len[b], new_len[b]) of every (sequence b, kv head) of a
+ * bf16 cache (layout above) into codes and scales; other rows are not touched.  Call it once for
+ * K and once for V.  max_new_tokens: host bound on new_len[b] - old_len[b] (sizes the grid). */
+ra_status kv_quantize_fp8(const ra_config *cfg, const void *src_cache, uint8_t *codes, float *scales,
+                          const int64_t *old_len, const int64_t *new_len, int64_t max_new_tokens, void *stream);
+
+/* span_summary_update_fp8 -- span_summary_update over an 8-bit K cache: the running sums add the
+ * cache's values fl32(E4M3^-1(code) * s) in token order (same contract otherwise). */
+ra_status span_summary_update_fp8(const ra_config *cfg, const uint8_t *k_codes, const float *k_scales,
+                                  float *span_mean, float *run_sum, const int64_t *old_len, const int64_t *new_len,
+                                  int64_t max_new_tokens, void *stream);
+
+/* routed_attn_decode_fp8 -- routed_attn_decode over an 8-bit K/V cache (bf16 queries): half the
+ * K/V bytes of a bf16 cache per step.  Scores are s_k * (q . codes) and the weights carry s_v;
+ * same workspace size and contract as routed_attn_decode. */
+ra_status routed_attn_decode_fp8(const ra_config *cfg, const ra_rows *rows, const uint8_t *k_codes,
+                                 const uint8_t *v_codes, const float *k_scales, const float *v_scales,
+                                 const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
 /* Workspace bytes needed by routed_attn_decode / routed_attn_prefill (op = ra_op); 0 if the
  * configuration is invalid (ra_last_error then says why). */
 size_t ra_workspace_bytes(const ra_config *cfg, int32_t op, int64_t n_rows, int64_t max_pos);

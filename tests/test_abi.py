@@ -82,6 +82,29 @@ def test_argument_validation_before_launch():
     assert lib.attn_dense_causal(ctypes.byref(c), ctypes.byref(rows()), FAKE, FAKE, None, None) == 1
 
 
+def test_fp8_entry_points_validate_before_launch():
+    lib = ra.lib()
+    c = cfg().c()
+    c32 = cfg(dtype=ra.RA_F32).c()
+    n = ctypes.c_int64(10)
+    # 8-bit caches go with bf16 queries
+    assert lib.kv_quantize_fp8(ctypes.byref(c32), FAKE, FAKE, FAKE, FAKE, FAKE, 10, None) == 2
+    assert lib.span_summary_update_fp8(ctypes.byref(c32), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, None) == 2
+    # NULL pointers, negative or oversized token counts
+    assert lib.kv_quantize_fp8(ctypes.byref(c), FAKE, None, FAKE, FAKE, FAKE, 10, None) == 1
+    assert lib.kv_quantize_fp8(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, -1, None) == 1
+    assert lib.kv_quantize_fp8(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, (1 << 20) + 1, None) == 3
+    assert lib.span_summary_update_fp8(ctypes.byref(c), FAKE, None, FAKE, FAKE, FAKE, FAKE, 10, None) == 1
+    ws = 1 << 30
+    assert lib.routed_attn_decode_fp8(ctypes.byref(c), ctypes.byref(rows()), FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                      FAKE, ws, None) == 1
+    assert lib.routed_attn_decode_fp8(ctypes.byref(c32), ctypes.byref(rows()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, ws, None) == 2
+    assert lib.routed_attn_decode_fp8(ctypes.byref(c), ctypes.byref(rows()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, 16, None) == 3
+    assert lib.ra_last_error().decode() != ""
+
+
 def test_workspace_sizes():
     c = cfg()
     d = ra.workspace_bytes(c, ra.RA_OP_DECODE, 1, (1 << 20) - 1)
