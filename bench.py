@@ -435,7 +435,8 @@ def bench_decode_fp8(args, w, K, V, qs):
             "value": round(1000.0 / ms, 2), "unit": "tokens/s", "ms_per_step": round(ms, 5),
             "roofline": {"bound": "hbm", "kernel": "routed_attn_decode_fp8 (decode_attn + combine_block)",
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": counter_traffic("routed_attn_decode_fp8_1m"),
                          "algorithmic_bytes_per_launch": int(bytes_step), "avg_launch_ms": round(attn_ms, 5)},
             "repeat_bitwise_identical": bool(same)}
 
