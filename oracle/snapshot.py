@@ -16,9 +16,10 @@ library's own (readings, one plain choice each):
       span -- everything the routed attention reads; rows past L_b and unused summary slots are
       not state.  Restoring writes exactly these and nothing else.
   N2  Integrity: SHA-256 (FIPS 180-4) over 4096-byte chunks of header + payload, then over
-      4096-byte chunks (128 digests) of each digest level while a level has more than 128
+      groups of 16 digests (512 bytes) of each digest level while a level has more than 16
       digests, and a root digest over the last level.  Every stored digest can be checked, and a
-      mismatch names the chunk whose bytes changed.
+      mismatch names the chunk whose bytes changed.  (Small groups keep the hashing of the upper
+      levels short: SHA-256 of one message is sequential, 9 blocks for a group of 16.)
 
 Image (all integers little-endian):
 
@@ -28,13 +29,13 @@ Image (all integers little-endian):
             12  4  element type of K and V: 0 = float32, 1 = bfloat16
             16  4  B         20  4  Hkv        24  4  d        28  4  S
             32  8  payload bytes                40  8  header bytes
-            48  4  chunk bytes = 4096           52  4  fan-in = 128
+            48  4  chunk bytes = 4096           52  4  fan-in = 16
             56  8  zero
   payload  for b, for g: K[b][g][0:L_b][:] then V[b][g][0:L_b][:]  (element bytes)
            then for b, for g: span_mean[b][g][0:floor(L_b/S)][:] then run_sum[b][g][:]  (float32)
   levels   D_1 = SHA-256 of each 4096-byte chunk of header + payload (the last one may be short);
-           D_(l+1) = SHA-256 of each 4096-byte chunk of the bytes of D_l, while |D_l| > 128;
-           root = SHA-256 of the bytes of the last level.
+           D_(l+1) = SHA-256 of each 512-byte chunk (16 digests) of the bytes of D_l, while
+           |D_l| > 16; root = SHA-256 of the bytes of the last level.
   image    = header | payload | D_1 | D_2 | ... | D_m | root
 
 A chunk's "offset" is where its bytes start in the image (the root covers all of D_m, so its
@@ -49,7 +50,7 @@ import numpy as np
 MAGIC = b"CRSASNP1"
 VERSION = 1
 CHUNK = 4096
-FAN_IN = 128
+FAN_IN = 16
 DIGEST = 32
 FIELDS = 64
 
@@ -82,16 +83,16 @@ def image_bytes(lengths, Hkv, d, S, elem_bytes):
     return data + DIGEST * sum(level_counts(data)) + DIGEST
 
 
-def chunk_digests(data):
-    """SHA-256 of each CHUNK-byte piece of `data` (the last piece may be short)."""
-    return b"".join(sha256(data[i:i + CHUNK]) for i in range(0, len(data), CHUNK))
+def chunk_digests(data, size=CHUNK):
+    """SHA-256 of each `size`-byte piece of `data` (the last piece may be short)."""
+    return b"".join(sha256(data[i:i + size]) for i in range(0, len(data), size))
 
 
 def digest_levels(data):
     """[D_1, ..., D_m] (bytes each) and the root digest of header + payload bytes `data` (N2)."""
     levels = [chunk_digests(data)]
     while len(levels[-1]) > FAN_IN * DIGEST:
-        levels.append(chunk_digests(levels[-1]))
+        levels.append(chunk_digests(levels[-1], FAN_IN * DIGEST))
     return levels, sha256(levels[-1])
 
 
@@ -174,23 +175,24 @@ def parse_image(img):
     return h, lengths, seqs
 
 
-def verify(img):
+def verify(img, header=None):
     """Smallest image offset of a chunk whose stored digest differs from its bytes' digest, or
-    None when every digest matches (N2)."""
+    None when every digest matches (N2).  The layout comes from `header` (a separate copy of
+    the header bytes) when given, else from the image's own header."""
     img = bytes(img)
-    h = parse_header(img)
+    h = parse_header(img if header is None else header)
     data_end = h["header"] + h["payload"]
     counts = level_counts(data_end)
     bad = None
-    src, src_len = 0, data_end  # the byte range whose chunks level l digests
+    src, src_len, size = 0, data_end, CHUNK  # the byte range whose chunks level l digests
     pos = data_end  # where level l is stored
     for n in counts:
         stored = img[pos:pos + DIGEST * n]
         for i in range(n):
-            lo = src + i * CHUNK
-            if sha256(img[lo:min(lo + CHUNK, src + src_len)]) != stored[DIGEST * i:DIGEST * (i + 1)]:
+            lo = src + i * size
+            if sha256(img[lo:min(lo + size, src + src_len)]) != stored[DIGEST * i:DIGEST * (i + 1)]:
                 bad = lo if bad is None else min(bad, lo)
-        src, src_len = pos, DIGEST * n
+        src, src_len, size = pos, DIGEST * n, FAN_IN * DIGEST
         pos += DIGEST * n
     if sha256(img[src:src + src_len]) != img[pos:pos + DIGEST]:
         bad = src if bad is None else min(bad, src)

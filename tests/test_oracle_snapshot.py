@@ -23,8 +23,8 @@ def test_sha256_matches_the_standards_examples():
 
 
 @pytest.mark.parametrize("nbytes,counts", [
-    (64, [1]), (4096, [1]), (4097, [2]), (128 * 4096, [128]), (128 * 4096 + 16, [129, 2]),
-    (128 * 128 * 4096, [16384, 128]), (128 * 128 * 4096 + 16, [16385, 129, 2]),
+    (64, [1]), (4096, [1]), (4097, [2]), (16 * 4096, [16]), (16 * 4096 + 16, [17, 2]),
+    (256 * 4096, [256, 16]), (256 * 4096 + 16, [257, 17, 2]),
 ])
 def test_level_counts_closed_forms(nbytes, counts):
     assert N.level_counts(nbytes) == counts
@@ -57,7 +57,7 @@ def test_image_layout_follows_the_definition(dtype):
     assert struct.unpack("<4I", img[16:32]) == (3, 2, 64, 16)
     rows = 300 + 17
     P = 2 * 2 * rows * 64 * esz + 2 * (300 // 16 + 17 // 16 + 3) * 64 * 4
-    assert struct.unpack("<QQII", img[32:56]) == (P, H, 4096, 128)
+    assert struct.unpack("<QQII", img[32:56]) == (P, H, 4096, 16)
     assert struct.unpack("<3q", img[64:88]) == (300, 17, 0) and img[88:96] == b"\0" * 8
     # payload: K then V of (b=0, g=0), (0, 1), (1, 0), (1, 1); sequence 2 is empty
     row = 64 * esz
@@ -75,13 +75,20 @@ def test_image_layout_follows_the_definition(dtype):
             assert img[at:at + 256] == run[b, g].tobytes()
             at += 256
     assert at == H + P
-    # levels: (H + P) bytes in 4096-byte chunks, one level, then the root
+    # levels: (H + P) bytes in 4096-byte chunks (43 or 83 of them), their digests in groups of
+    # 16 (3 or 6 digests), then the root over those
     n1 = -(-(H + P) // 4096)
-    assert n1 <= 128 and len(img) == H + P + 32 * n1 + 32 == N.image_bytes(lengths, 2, 64, 16, esz)
+    n2 = -(-n1 // 16)
+    assert (n1, n2) == ((43, 3) if esz == 2 else (83, 6))
+    d1, d2 = H + P, H + P + 32 * n1
+    assert len(img) == d2 + 32 * n2 + 32 == N.image_bytes(lengths, 2, 64, 16, esz)
     for i in (0, n1 - 1):
         chunk = img[4096 * i:min(4096 * (i + 1), H + P)]
-        assert img[H + P + 32 * i:H + P + 32 * (i + 1)] == N.sha256(chunk)
-    assert img[-32:] == N.sha256(img[H + P:H + P + 32 * n1])
+        assert img[d1 + 32 * i:d1 + 32 * (i + 1)] == N.sha256(chunk)
+    for i in (0, n2 - 1):
+        group = img[d1 + 512 * i:min(d1 + 512 * (i + 1), d2)]
+        assert img[d2 + 32 * i:d2 + 32 * (i + 1)] == N.sha256(group)
+    assert img[-32:] == N.sha256(img[d2:d2 + 32 * n2])
 
 
 def test_parse_recovers_every_saved_array():
@@ -110,12 +117,12 @@ def test_rows_past_the_length_are_not_saved():
 def two_level_image():
     # K and V: 2 x 2 x 300 rows of 256 bytes each (bf16, d = 128) = 614400 bytes; summaries
     # 2 kv heads x (4 + 4 means + 2 running sums) x 512 bytes = 10240; header 80 -> 624720 bytes
-    # = 153 chunks -> D_1 (153 digests), D_2 (2 digests)
+    # = 153 chunks -> D_1 (153 digests), D_2 (10 digests, groups of 16)
     k, v, mean, run, lengths, S = caches(np.uint16, B=2, Hkv=2, cap=300, d=128, S=64, lengths=(300, 300))
     img = N.build_image(k, v, mean, run, lengths, S)
     h = N.parse_header(img)
     data = h["header"] + h["payload"]
-    assert data == 624720 and N.level_counts(data) == [153, 2]
+    assert data == 624720 and N.level_counts(data) == [153, 10]
     return bytearray(img), data
 
 
@@ -127,9 +134,12 @@ def test_verify_accepts_an_intact_image():
 @pytest.mark.parametrize("where", ["header", "payload", "last_data_byte"])
 def test_verify_names_the_corrupted_data_chunk(where):
     img, data = two_level_image()
+    header = bytes(img[:80])
     x = {"header": 70, "payload": 4096 * 77 + 1234, "last_data_byte": data - 1}[where]
     img[x] ^= 0x01
-    assert N.verify(img) == 4096 * (x // 4096)
+    assert N.verify(img, header) == 4096 * (x // 4096)
+    if where != "header":
+        assert N.verify(img) == 4096 * (x // 4096)
 
 
 def test_verify_names_the_chunk_of_a_corrupted_digest():
@@ -138,10 +148,10 @@ def test_verify_names_the_chunk_of_a_corrupted_digest():
     img[data + 32 * 140 + 5] ^= 0x80
     assert N.verify(img) == 4096 * 140
     img, data = two_level_image()
-    # a byte of D_2's second digest (over D_1's second 4096-byte chunk, digests 128..152)
+    # a byte of D_2's second digest (over D_1's second group, digests 16..31)
     d2 = data + 32 * 153
     img[d2 + 32 + 3] ^= 0x10
-    assert N.verify(img) == data + 4096
+    assert N.verify(img) == data + 512
     img, data = two_level_image()
     img[-1] ^= 0xFF  # the root covers D_2
     assert N.verify(img) == d2
