@@ -41,6 +41,7 @@ def parse():
     p.add_argument("--dense-steps", type=int, default=2,
                    help="timed calls of dense causal attention on the prefill rows (0: skip)")
     p.add_argument("--no-fp8", action="store_true", help="skip the decode step over the 8-bit cache")
+    p.add_argument("--no-snapshot", action="store_true", help="skip the session snapshot / restore measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 256 MiB device copy (reference kernel for HBM byte counters)")
     return p.parse_args()
@@ -220,6 +221,9 @@ def main():
 
     if not args.no_fp8:
         result["decode_fp8"] = bench_decode_fp8(args, w, K, V, qs)
+
+    if not args.no_snapshot:
+        result["snapshot"] = bench_snapshot(w, st[0], cfg1)
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -439,6 +443,81 @@ def bench_decode_fp8(args, w, K, V, qs):
                          "traffic": counter_traffic("routed_attn_decode_fp8_1m"),
                          "algorithmic_bytes_per_launch": int(bytes_step), "avg_launch_ms": round(attn_ms, 5)},
             "repeat_bitwise_identical": bool(same)}
+
+
+# SHA-256 of one 64-byte block takes at least 1,400 VALU instructions on gfx950: 48 schedule words
+# x 10 (two sigmas of 2 rotations + 1 shift + one three-input xor, two adds), 64 rounds x 14 (two
+# Sigmas x 4, choice 1, majority 1, four adds as three-input or plain adds), 8 final adds and 16
+# byte swaps.  The vector ALUs retire 64 lane-instructions per clock per CU: 256 CUs x 64 x 2.4 GHz
+# / 1400 x 64 bytes = 1.80 TB/s of hashed data.
+SHA_PEAK_GBS = 256 * 64 * 2.4e9 / 1400 * 64 / 1e9
+
+
+def bench_snapshot(w, d0, cfg1, reps=3):
+    """Session snapshot of one 1M-token sequence's state (2 GiB of bf16 K/V rows, span means,
+    running sums): kv_snapshot_pack (header, payload copies, SHA-256 digest levels),
+    kv_snapshot_verify (every digest recomputed and compared), kv_snapshot_unpack into a second
+    set of buffers, and the image's copies to and from pinned host memory (PCIe)."""
+    import torch
+
+    import content_routed_sparse_amd as ra
+
+    L, dev = w.decode_len, d0["k"].device
+    lengths = [L]
+    n = ra.snapshot_bytes(cfg1, lengths)
+    img = torch.empty(n, dtype=torch.uint8, device=dev)
+    img2 = torch.empty_like(img)
+    bad = torch.empty(1, dtype=torch.int64, device=dev)
+    K2, V2 = torch.empty_like(d0["k"]), torch.empty_like(d0["v"])
+    M2, R2 = torch.zeros_like(d0["mean"]), torch.zeros_like(d0["run"])
+    host = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        ts = []
+        for r in range(reps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            if r > 0:
+                ts.append(a.elapsed_time(b))
+        return float(np.mean(ts))
+
+    t_pack = timed(lambda: ra.kv_snapshot_pack(cfg1, d0["k"], d0["v"], d0["mean"], d0["run"], lengths, img))
+    header = img[:4096].cpu().numpy()
+    info, _ = ra.kv_snapshot_parse(header)
+    header = header[:info["header_bytes"]].copy()
+    t_verify = timed(lambda: ra.kv_snapshot_verify(header, img, bad))
+    intact = int(bad.item()) == -1
+    t_unpack = timed(lambda: ra.kv_snapshot_unpack(cfg1, header, img, K2, V2, M2, R2, guard=bad))
+    restored = (torch.equal(K2, d0["k"]) and torch.equal(V2, d0["v"]) and torch.equal(R2, d0["run"]) and
+                torch.equal(M2[:, :, :L // w.span_size], d0["mean"][:, :, :L // w.span_size]))
+    del K2, V2
+    d2h, h2d = [], []
+    for r in range(2):
+        t0 = time.perf_counter()
+        host.copy_(img)
+        d2h.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        img2.copy_(host, non_blocking=True)
+        torch.cuda.synchronize()
+        h2d.append(time.perf_counter() - t0)
+    round_trip = torch.equal(img, img2)
+    gbs = lambda ms: round(n / (ms * 1e-3) / 1e9, 1)
+    achieved = n / (t_verify * 1e-3) / 1e9
+    return {"workload": "decode_1m state of one sequence (1M tokens x 4 kv heads, bf16)",
+            "image_bytes": n, "root": bytes(host[-32:].numpy()).hex(),
+            "pack_ms": round(t_pack, 3), "pack_GBps": gbs(t_pack),
+            "verify_ms": round(t_verify, 3), "verify_GBps": gbs(t_verify),
+            "unpack_ms": round(t_unpack, 3), "unpack_GBps": gbs(t_unpack),
+            "d2h_pinned_GBps": round(n / min(d2h) / 1e9, 1), "h2d_pinned_GBps": round(n / min(h2d) / 1e9, 1),
+            "roofline": {"bound": "alu", "kernel": "kv_snapshot_verify (sha_chunks, every level)",
+                         "achieved": round(achieved, 1), "peak": round(SHA_PEAK_GBS, 1), "unit": "GB/s",
+                         "frac": round(achieved / SHA_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": n, "avg_launch_ms": round(t_verify, 5)},
+            "intact": intact, "restored_bitwise": bool(restored), "pcie_round_trip_bitwise": bool(round_trip)}
 
 
 def cpu_baseline(w, d0, seconds):

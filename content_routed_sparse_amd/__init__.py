@@ -23,7 +23,10 @@ RA_F32, RA_BF16 = 0, 1
 RA_OP_DECODE, RA_OP_PREFILL = 0, 1
 EXPORTED = ("span_summary_update", "route_scores", "topk_spans", "routed_attn_decode", "routed_attn_prefill",
             "attn_dense_causal", "kv_quantize_fp8", "span_summary_update_fp8", "routed_attn_decode_fp8",
-            "ra_workspace_bytes", "ra_status_string", "ra_last_error")
+            "kv_snapshot_bytes", "kv_snapshot_pack", "kv_snapshot_parse", "kv_snapshot_verify", "kv_snapshot_unpack",
+            "kv_snapshot_write_file", "kv_snapshot_read_file", "ra_workspace_bytes", "ra_status_string",
+            "ra_last_error")
+SNAPSHOT_INTACT = (1 << 64) - 1  # kv_snapshot_verify's word when every digest matches
 
 
 class RoutedAttnError(RuntimeError):
@@ -37,6 +40,13 @@ class _Config(ctypes.Structure):
                 ("span_size", ctypes.c_int32), ("top_k", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("batch", ctypes.c_int32), ("capacity", ctypes.c_int64),
                 ("max_spans", ctypes.c_int64)]
+
+
+class _SnapshotInfo(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("span_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("header_bytes", ctypes.c_uint64), ("payload_bytes", ctypes.c_uint64),
+                ("image_bytes", ctypes.c_uint64)]
 
 
 class _Rows(ctypes.Structure):
@@ -67,11 +77,19 @@ def lib():
             "kv_quantize_fp8": [CP, P, P, P, P, P, I64, P],
             "span_summary_update_fp8": [CP, P, P, P, P, P, P, I64, P],
             "routed_attn_decode_fp8": [CP, RP, P, P, P, P, P, P, P, SZ, P],
+            "kv_snapshot_pack": [CP, P, P, P, P, P, P, SZ, P],
+            "kv_snapshot_parse": [P, SZ, ctypes.POINTER(_SnapshotInfo), P, I32],
+            "kv_snapshot_verify": [P, SZ, P, SZ, P, P],
+            "kv_snapshot_unpack": [CP, P, SZ, P, SZ, P, P, P, P, P, P],
+            "kv_snapshot_write_file": [ctypes.c_char_p, P, SZ],
+            "kv_snapshot_read_file": [ctypes.c_char_p, P, SZ, ctypes.POINTER(SZ)],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = I32
+        L.kv_snapshot_bytes.argtypes = [CP, P]
+        L.kv_snapshot_bytes.restype = SZ
         L.ra_workspace_bytes.argtypes = [CP, I32, I64, I64]
         L.ra_workspace_bytes.restype = SZ
         L.ra_status_string.argtypes = [I32]
@@ -370,6 +388,126 @@ def routed_attn_decode_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel,
     """routed_attn_decode over an 8-bit K/V cache (bf16 queries)."""
     args, _keep = _args_attn_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, workspace, stream)
     _check(lib().routed_attn_decode_fp8(*args))
+
+
+# ------------------------------------------------------------------------ session snapshots
+# Image = header | payload (live K/V rows, span means, running sums) | SHA-256 digest levels |
+# root; layout in include/routed_attn.h.  `lengths` are host token counts per sequence, headers
+# are host bytes, images are uint8 device tensors (or pinned host tensors for the file helpers).
+
+def _host_lengths(cfg, lengths):
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(lengths, dtype=np.int64))
+    if arr.shape != (cfg.batch,):
+        raise ValueError("lengths must have cfg.batch = %d entries" % cfg.batch)
+    return arr
+
+
+def _host_bytes(header):
+    """(pointer, size, keep-alive) of host bytes: bytes, bytearray, numpy or a CPU tensor."""
+    import numpy as np
+    if isinstance(header, torch.Tensor):
+        if header.is_cuda:
+            raise TypeError("header must be host memory")
+        header = header.contiguous().numpy()
+    arr = np.ascontiguousarray(np.frombuffer(header, dtype=np.uint8) if isinstance(header, (bytes, bytearray))
+                               else np.asarray(header).view(np.uint8).reshape(-1))
+    return arr.ctypes.data, arr.nbytes, arr
+
+
+def snapshot_bytes(cfg, lengths):
+    """Image bytes of the state of sequences with these host lengths."""
+    arr = _host_lengths(cfg, lengths)
+    c = cfg.c()
+    n = lib().kv_snapshot_bytes(ctypes.byref(c), arr.ctypes.data)
+    if n == 0:
+        raise RoutedAttnError(1, lib().ra_last_error().decode())
+    return n
+
+
+def kv_snapshot_pack(cfg, k_cache, v_cache, span_mean, run_sum, lengths, image, stream=None):
+    """Write the snapshot image of the cache state into the uint8 device tensor `image`."""
+    arr = _host_lengths(cfg, lengths)
+    c = cfg.c()
+    _check(lib().kv_snapshot_pack(
+        ctypes.byref(c), _dev(k_cache, cfg.torch_dtype, _kv_shape(cfg), "k_cache"),
+        _dev(v_cache, cfg.torch_dtype, _kv_shape(cfg), "v_cache"),
+        _dev(span_mean, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.max_spans, cfg.head_dim), "span_mean"),
+        _dev(run_sum, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.head_dim), "run_sum"), arr.ctypes.data,
+        _dev(image, torch.uint8, None, "image"), image.numel(), _stream(stream)))
+
+
+def kv_snapshot_parse(header, max_batch=1 << 20):
+    """(info dict, lengths numpy array) of a host header."""
+    import numpy as np
+    ptr, n, _keep = _host_bytes(header)
+    info = _SnapshotInfo()
+    _check(lib().kv_snapshot_parse(ctypes.c_void_p(ptr), n, ctypes.byref(info), None, 0))
+    lengths = np.zeros(info.batch, dtype=np.int64)
+    _check(lib().kv_snapshot_parse(ctypes.c_void_p(ptr), n, ctypes.byref(info), lengths.ctypes.data, info.batch))
+    return {f: getattr(info, f) for f, _ in _SnapshotInfo._fields_ if f != "reserved"}, lengths
+
+
+def kv_snapshot_verify(header, image, bad_offset, stream=None):
+    """Recompute every digest of the device image; bad_offset (int64 device tensor [1]) receives
+    SNAPSHOT_INTACT (as int64: -1) or the smallest offset of a chunk whose digest differs."""
+    ptr, n, _keep = _host_bytes(header)
+    _check(lib().kv_snapshot_verify(ctypes.c_void_p(ptr), n, _dev(image, torch.uint8, None, "image"), image.numel(),
+                                    _dev(bad_offset, torch.int64, (1,), "bad_offset"), _stream(stream)))
+
+
+def kv_snapshot_unpack(cfg, header, image, k_cache, v_cache, span_mean, run_sum, guard=None, stream=None):
+    """Copy the saved state of the device image into the caches (only if *guard reads intact)."""
+    ptr, n, _keep = _host_bytes(header)
+    g = None if guard is None else _dev(guard, torch.int64, (1,), "guard")
+    _check(lib().kv_snapshot_unpack(
+        ctypes.byref(cfg.c()), ctypes.c_void_p(ptr), n, _dev(image, torch.uint8, None, "image"), image.numel(), g,
+        _dev(k_cache, cfg.torch_dtype, _kv_shape(cfg), "k_cache"),
+        _dev(v_cache, cfg.torch_dtype, _kv_shape(cfg), "v_cache"),
+        _dev(span_mean, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.max_spans, cfg.head_dim), "span_mean"),
+        _dev(run_sum, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.head_dim), "run_sum"), _stream(stream)))
+
+
+def kv_snapshot_write_file(path, host_image):
+    """Write a host uint8 tensor or buffer to `path` (through a temporary file renamed into place)."""
+    ptr, n, _keep = _host_bytes(host_image)
+    _check(lib().kv_snapshot_write_file(os.fsencode(path), ctypes.c_void_p(ptr), n))
+
+
+def kv_snapshot_read_file(path, pin=True):
+    """The bytes of a file as a host uint8 tensor (pinned by default)."""
+    n = ctypes.c_size_t(0)
+    _check(lib().kv_snapshot_read_file(os.fsencode(path), None, 0, ctypes.byref(n)))
+    buf = torch.empty(n.value, dtype=torch.uint8, pin_memory=pin)
+    _check(lib().kv_snapshot_read_file(os.fsencode(path), ctypes.c_void_p(buf.data_ptr()), n.value, ctypes.byref(n)))
+    return buf
+
+
+def save_snapshot(path, cfg, k_cache, v_cache, span_mean, run_sum, lengths):
+    """Pack the state on the device, copy the image to pinned host memory and write it to
+    `path`.  Returns the root digest (hex)."""
+    image = torch.empty(snapshot_bytes(cfg, lengths), dtype=torch.uint8, device=k_cache.device)
+    kv_snapshot_pack(cfg, k_cache, v_cache, span_mean, run_sum, lengths, image)
+    host = torch.empty(image.numel(), dtype=torch.uint8, pin_memory=True)
+    host.copy_(image)  # stream-ordered after the pack; synchronous for the host
+    kv_snapshot_write_file(path, host)
+    return bytes(host[-32:].numpy()).hex()
+
+
+def load_snapshot(path, cfg, k_cache, v_cache, span_mean, run_sum):
+    """Read `path`, check every digest on the device and restore the state into the caches.
+    Returns the restored lengths; raises (restoring nothing) if any digest differs."""
+    host = kv_snapshot_read_file(path)
+    info, lengths = kv_snapshot_parse(host[:min(host.numel(), 64 + 8 * (1 << 20))])
+    image = host.to(k_cache.device, non_blocking=True)
+    bad = torch.empty(1, dtype=torch.int64, device=k_cache.device)
+    header = host[:info["header_bytes"]]
+    kv_snapshot_verify(header, image, bad)
+    kv_snapshot_unpack(cfg, header, image, k_cache, v_cache, span_mean, run_sum, guard=bad)
+    b = int(bad.item()) & SNAPSHOT_INTACT
+    if b != SNAPSHOT_INTACT:
+        raise RoutedAttnError(6, "%s: digest mismatch in the chunk at byte %d; nothing restored" % (path, b))
+    return lengths
 
 
 class Pipeline:

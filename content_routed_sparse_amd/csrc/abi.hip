@@ -4,8 +4,11 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "common.h"
 #include "kernels.h"
+#include "snapshot_kernels.h"
 
 namespace {
 
@@ -276,6 +279,324 @@ ra_status routed_attn_decode_fp8(const ra_config *cfg, const ra_rows *rows, cons
                       "routed_attn_decode_fp8 launch");
 }
 
+// ------------------------------------------------------------------------- session snapshots
+}  // extern "C"
+
+namespace {
+
+constexpr uint64_t kSnapMagic = 0x31504E5341535243ull;  // "CRSASNP1" read as a little-endian word
+constexpr uint32_t kSnapVersion = 1, kSnapChunk = 4096, kSnapFanIn = 16;
+constexpr int kMaxLevels = 16;  // 4096 * 16^15 bytes exceed any image
+
+struct SnapLayout {
+    int B, Hkv, d, S, dtype, esz;
+    uint64_t H, P, data, image;
+    int n_levels;
+    uint64_t count[kMaxLevels], off[kMaxLevels];  // digests per level and where each level starts
+    uint64_t root;
+};
+
+uint64_t snap_header_bytes(int B) { return (64 + 8 * (uint64_t)B + 15) / 16 * 16; }
+
+// Layout of the image of B sequences with the given lengths (checked by the callers).
+SnapLayout snap_layout(int B, int Hkv, int d, int S, int dtype, const int64_t *lengths) {
+    SnapLayout L;
+    L.B = B;
+    L.Hkv = Hkv;
+    L.d = d;
+    L.S = S;
+    L.dtype = dtype;
+    L.esz = dtype == RA_BF16 ? 2 : 4;
+    uint64_t rows = 0, spans = 0;
+    for (int b = 0; b < B; ++b) {
+        rows += (uint64_t)lengths[b];
+        spans += (uint64_t)lengths[b] / (uint64_t)S;
+    }
+    L.H = snap_header_bytes(B);
+    L.P = 2ull * Hkv * rows * d * L.esz + (uint64_t)Hkv * (spans + B) * d * 4;
+    L.data = L.H + L.P;
+    uint64_t n = (L.data + kSnapChunk - 1) / kSnapChunk, at = L.data;
+    L.n_levels = 0;
+    while (true) {
+        L.count[L.n_levels] = n;
+        L.off[L.n_levels] = at;
+        at += 32 * n;
+        ++L.n_levels;
+        if (n <= kSnapFanIn) break;
+        n = (n + kSnapFanIn - 1) / kSnapFanIn;
+    }
+    L.root = at;
+    L.image = at + 32;
+    return L;
+}
+
+ra_status check_lengths(const ra_config *c, const int64_t *lengths, int B) {
+    if (!lengths) return fail(RA_EINVAL, "lengths is NULL");
+    for (int b = 0; b < B; ++b)
+        if (lengths[b] < 0 || lengths[b] > c->capacity)
+            return fail(RA_ECAPACITY, "lengths[%d] = %lld outside [0, capacity = %lld]", b, (long long)lengths[b],
+                        (long long)c->capacity);
+    return RA_OK;
+}
+
+// The payload's byte ranges in order, each paired with its place in the caches; `to_image`
+// selects the copy direction.
+ra_status snap_copy(const SnapLayout &L, const ra_config *c, const int64_t *lengths, uint8_t *image,
+                    const void *k, const void *v, const float *mean, const float *run, bool to_image,
+                    const unsigned long long *guard, hipStream_t st) {
+    ra::SegmentBatch sb;
+    sb.n = 0;
+    uint64_t at = L.H;
+    auto flush = [&]() -> hipError_t {
+        const hipError_t e = ra::launch_copy_segments(sb, guard, st);
+        sb.n = 0;
+        return e;
+    };
+    auto add = [&](const void *cache_ptr, uint64_t bytes) -> hipError_t {
+        if (bytes == 0) return hipSuccess;
+        ra::Segment &s = sb.seg[sb.n++];
+        s.src = to_image ? cache_ptr : (const void *)(image + at);
+        s.dst = to_image ? (void *)(image + at) : const_cast<void *>(cache_ptr);
+        s.n16 = bytes / 16;
+        at += bytes;
+        return sb.n == ra::kSegs ? flush() : hipSuccess;
+    };
+    const uint64_t row = (uint64_t)L.d * L.esz;
+    hipError_t e = hipSuccess;
+    for (int b = 0; b < L.B && e == hipSuccess; ++b)
+        for (int g = 0; g < L.Hkv && e == hipSuccess; ++g) {
+            const uint64_t base = ((uint64_t)b * c->num_kv_heads + g) * (uint64_t)c->capacity * row;
+            const uint64_t n = (uint64_t)lengths[b] * row;
+            e = add((const uint8_t *)k + base, n);
+            if (e == hipSuccess) e = add((const uint8_t *)v + base, n);
+        }
+    for (int b = 0; b < L.B && e == hipSuccess; ++b)
+        for (int g = 0; g < L.Hkv && e == hipSuccess; ++g) {
+            const uint64_t bg = (uint64_t)b * c->num_kv_heads + g;
+            e = add(mean + bg * (uint64_t)c->max_spans * L.d, (uint64_t)lengths[b] / L.S * L.d * 4);
+            if (e == hipSuccess) e = add(run + bg * L.d, (uint64_t)L.d * 4);
+        }
+    if (e == hipSuccess) e = flush();
+    if (e != hipSuccess) return hip_status(e, "snapshot copy launch");
+    return RA_OK;
+}
+
+// Digest levels and root of an image: stored (compare = false) or checked against the stored
+// ones (compare = true, mismatches reported in *bad).  Level 1 digests 4096-byte chunks of
+// header | payload, the levels above groups of kSnapFanIn digests.
+hipError_t snap_hash(const SnapLayout &L, uint8_t *image, bool compare, unsigned long long *bad, hipStream_t st) {
+    uint64_t src = 0, len = L.data, chunk = kSnapChunk;
+    for (int l = 0; l < L.n_levels; ++l) {
+        const hipError_t e = ra::launch_sha_chunks(image + src, len, chunk, image + L.off[l], compare, bad, src, st);
+        if (e != hipSuccess) return e;
+        src = L.off[l];
+        len = 32 * L.count[l];
+        chunk = 32 * kSnapFanIn;
+    }
+    return ra::launch_sha_chunks(image + src, len, len, image + L.root, compare, bad, src, st);
+}
+
+// Header fields of a host header (any alignment); fills the layout and the lengths.
+ra_status snap_parse(const void *header, size_t avail, SnapLayout *L, std::vector<int64_t> &lengths) {
+    if (!header) return fail(RA_EINVAL, "header is NULL");
+    if (avail < 64) return fail(RA_EFORMAT, "header needs at least 64 bytes, got %zu", avail);
+    const uint8_t *h = (const uint8_t *)header;
+    uint64_t magic, P, H, z;
+    uint32_t version, dtype, B, Hkv, d, S, chunk, fan;
+    memcpy(&magic, h, 8);
+    memcpy(&version, h + 8, 4);
+    memcpy(&dtype, h + 12, 4);
+    memcpy(&B, h + 16, 4);
+    memcpy(&Hkv, h + 20, 4);
+    memcpy(&d, h + 24, 4);
+    memcpy(&S, h + 28, 4);
+    memcpy(&P, h + 32, 8);
+    memcpy(&H, h + 40, 8);
+    memcpy(&chunk, h + 48, 4);
+    memcpy(&fan, h + 52, 4);
+    memcpy(&z, h + 56, 8);
+    if (magic != kSnapMagic) return fail(RA_EFORMAT, "not a snapshot image (magic)");
+    if (version != kSnapVersion || chunk != kSnapChunk || fan != kSnapFanIn || z != 0)
+        return fail(RA_EFORMAT, "unsupported snapshot version or digest parameters");
+    if (dtype != RA_F32 && dtype != RA_BF16) return fail(RA_EFORMAT, "unknown element type %u", dtype);
+    if (B < 1 || B > (1u << 24) || Hkv < 1 || Hkv > 4096 || (d != 64 && d != 128) || S < 1 || S > (1u << 30))
+        return fail(RA_EFORMAT, "header shape fields out of range");
+    if (H != snap_header_bytes((int)B)) return fail(RA_EFORMAT, "header size field inconsistent with B");
+    if (avail < H) return fail(RA_EFORMAT, "header of %llu bytes, %zu given", (unsigned long long)H, avail);
+    lengths.resize(B);
+    for (uint32_t b = 0; b < B; ++b) {
+        int64_t x;
+        memcpy(&x, h + 64 + 8 * (uint64_t)b, 8);
+        if (x < 0 || x >= (1LL << 40)) return fail(RA_EFORMAT, "length %lld of sequence %u out of range", (long long)x, b);
+        lengths[b] = x;
+    }
+    *L = snap_layout((int)B, (int)Hkv, (int)d, (int)S, (int)dtype, lengths.data());
+    if (L->P != P) return fail(RA_EFORMAT, "payload size field inconsistent with the lengths");
+    return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kv_snapshot_bytes(const ra_config *cfg, const int64_t *lengths) {
+    if (check_config(cfg) || check_lengths(cfg, lengths, cfg->batch)) return 0;
+    return (size_t)snap_layout(cfg->batch, cfg->num_kv_heads, cfg->head_dim, cfg->span_size, cfg->dtype, lengths).image;
+}
+
+ra_status kv_snapshot_pack(const ra_config *cfg, const void *k_cache, const void *v_cache, const float *span_mean,
+                           const float *run_sum, const int64_t *lengths, void *image, size_t image_bytes,
+                           void *stream) {
+    ra_status s = check_config(cfg);
+    if (s) return s;
+    if ((s = check_lengths(cfg, lengths, cfg->batch))) return s;
+    if (!k_cache || !v_cache || !span_mean || !run_sum || !image) return fail(RA_EINVAL, "NULL pointer argument");
+    if (((uintptr_t)image | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)span_mean | (uintptr_t)run_sum) & 15)
+        return fail(RA_EINVAL, "image and cache buffers must be 16-byte aligned");
+    const SnapLayout L =
+        snap_layout(cfg->batch, cfg->num_kv_heads, cfg->head_dim, cfg->span_size, cfg->dtype, lengths);
+    if (image_bytes < L.image)
+        return fail(RA_ECAPACITY, "image buffer of %zu bytes, %llu needed", image_bytes, (unsigned long long)L.image);
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t *img = (uint8_t *)image;
+    // header words: 8 fixed, B lengths, one zero word when B is odd
+    const uint64_t n_words = L.H / 8;
+    ra::WordBatch wb;
+    for (uint64_t w0 = 0; w0 < n_words; w0 += ra::kWords) {
+        wb.n = (int)(n_words - w0 < (uint64_t)ra::kWords ? n_words - w0 : ra::kWords);
+        for (int i = 0; i < wb.n; ++i) {
+            const uint64_t w = w0 + i;
+            uint64_t v = 0;
+            switch (w) {
+                case 0: v = kSnapMagic; break;
+                case 1: v = kSnapVersion | ((uint64_t)(uint32_t)cfg->dtype << 32); break;
+                case 2: v = (uint64_t)(uint32_t)cfg->batch | ((uint64_t)(uint32_t)cfg->num_kv_heads << 32); break;
+                case 3: v = (uint64_t)(uint32_t)cfg->head_dim | ((uint64_t)(uint32_t)cfg->span_size << 32); break;
+                case 4: v = L.P; break;
+                case 5: v = L.H; break;
+                case 6: v = kSnapChunk | ((uint64_t)kSnapFanIn << 32); break;
+                case 7: v = 0; break;
+                default: v = w - 8 < (uint64_t)cfg->batch ? (uint64_t)lengths[w - 8] : 0; break;
+            }
+            wb.v[i] = v;
+        }
+        const hipError_t e = ra::launch_write_words((uint64_t *)(img + 8 * w0), wb, st);
+        if (e != hipSuccess) return hip_status(e, "snapshot header launch");
+    }
+    if ((s = snap_copy(L, cfg, lengths, img, k_cache, v_cache, span_mean, run_sum, true, nullptr, st))) return s;
+    return hip_status(snap_hash(L, img, false, nullptr, st), "snapshot digest launch");
+}
+
+ra_status kv_snapshot_parse(const void *header, size_t header_avail, ra_snapshot_info *info, int64_t *lengths,
+                            int32_t max_batch) {
+    SnapLayout L;
+    std::vector<int64_t> len;
+    ra_status s = snap_parse(header, header_avail, &L, len);
+    if (s) return s;
+    if (lengths) {
+        if (L.B > max_batch) return fail(RA_ECAPACITY, "image holds %d sequences, room for %d", L.B, max_batch);
+        memcpy(lengths, len.data(), 8 * (size_t)L.B);
+    }
+    if (info) {
+        info->dtype = L.dtype;
+        info->batch = L.B;
+        info->num_kv_heads = L.Hkv;
+        info->head_dim = L.d;
+        info->span_size = L.S;
+        info->reserved = 0;
+        info->header_bytes = L.H;
+        info->payload_bytes = L.P;
+        info->image_bytes = L.image;
+    }
+    return ok();
+}
+
+ra_status kv_snapshot_verify(const void *header, size_t header_avail, const void *image, size_t image_bytes,
+                             uint64_t *bad_offset, void *stream) {
+    SnapLayout L;
+    std::vector<int64_t> len;
+    ra_status s = snap_parse(header, header_avail, &L, len);
+    if (s) return s;
+    if (!image || !bad_offset) return fail(RA_EINVAL, "NULL image or bad_offset");
+    if ((uintptr_t)image & 15) return fail(RA_EINVAL, "image must be 16-byte aligned");
+    if (image_bytes < L.image)
+        return fail(RA_EFORMAT, "image of %zu bytes, header describes %llu", image_bytes, (unsigned long long)L.image);
+    hipStream_t st = (hipStream_t)stream;
+    unsigned long long *bad = (unsigned long long *)bad_offset;
+    hipError_t e = ra::launch_fill_u64(bad, ~0ull, st);
+    if (e == hipSuccess) e = snap_hash(L, (uint8_t *)const_cast<void *>(image), true, bad, st);
+    return hip_status(e, "snapshot verify launch");
+}
+
+ra_status kv_snapshot_unpack(const ra_config *cfg, const void *header, size_t header_avail, const void *image,
+                             size_t image_bytes, const uint64_t *guard, void *k_cache, void *v_cache,
+                             float *span_mean, float *run_sum, void *stream) {
+    ra_status s = check_config(cfg);
+    if (s) return s;
+    SnapLayout L;
+    std::vector<int64_t> len;
+    if ((s = snap_parse(header, header_avail, &L, len))) return s;
+    if (L.dtype != cfg->dtype || L.Hkv != cfg->num_kv_heads || L.d != cfg->head_dim || L.S != cfg->span_size)
+        return fail(RA_EINVAL, "image (dtype %d, Hkv %d, d %d, S %d) does not match cfg (%d, %d, %d, %d)", L.dtype,
+                    L.Hkv, L.d, L.S, cfg->dtype, cfg->num_kv_heads, cfg->head_dim, cfg->span_size);
+    if (L.B > cfg->batch) return fail(RA_ECAPACITY, "image holds %d sequences, cfg->batch is %d", L.B, cfg->batch);
+    if ((s = check_lengths(cfg, len.data(), L.B))) return s;
+    if (!image || !k_cache || !v_cache || !span_mean || !run_sum) return fail(RA_EINVAL, "NULL pointer argument");
+    if (((uintptr_t)image | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)span_mean | (uintptr_t)run_sum) & 15)
+        return fail(RA_EINVAL, "image and cache buffers must be 16-byte aligned");
+    if (image_bytes < L.image)
+        return fail(RA_EFORMAT, "image of %zu bytes, header describes %llu", image_bytes, (unsigned long long)L.image);
+    return snap_copy(L, cfg, len.data(), (uint8_t *)const_cast<void *>(image), k_cache, v_cache, span_mean, run_sum, false,
+                     (const unsigned long long *)guard, (hipStream_t)stream);
+}
+
+ra_status kv_snapshot_write_file(const char *path, const void *data, size_t bytes) {
+    if (!path || (!data && bytes)) return fail(RA_EINVAL, "NULL path or data");
+    char tmp[4096];
+    if (snprintf(tmp, sizeof(tmp), "%s.tmp", path) >= (int)sizeof(tmp)) return fail(RA_EINVAL, "path too long");
+    FILE *f = fopen(tmp, "wb");
+    if (!f) return fail(RA_EIO, "cannot open %s for writing", tmp);
+    const size_t n = bytes ? fwrite(data, 1, bytes, f) : 0;
+    const bool flushed = fflush(f) == 0;
+    if (fclose(f) != 0 || n != bytes || !flushed) {
+        remove(tmp);
+        return fail(RA_EIO, "short write to %s", tmp);
+    }
+    if (rename(tmp, path) != 0) {
+        remove(tmp);
+        return fail(RA_EIO, "cannot rename %s to %s", tmp, path);
+    }
+    return ok();
+}
+
+ra_status kv_snapshot_read_file(const char *path, void *buf, size_t capacity, size_t *bytes) {
+    if (!path || !bytes) return fail(RA_EINVAL, "NULL path or bytes");
+    FILE *f = fopen(path, "rb");
+    if (!f) return fail(RA_EIO, "cannot open %s", path);
+    if (fseeko(f, 0, SEEK_END) != 0) {
+        fclose(f);
+        return fail(RA_EIO, "cannot seek in %s", path);
+    }
+    const off_t size = ftello(f);
+    if (size < 0 || fseeko(f, 0, SEEK_SET) != 0) {
+        fclose(f);
+        return fail(RA_EIO, "cannot size %s", path);
+    }
+    *bytes = (size_t)size;
+    if (!buf) {
+        fclose(f);
+        return ok();
+    }
+    if (capacity < (size_t)size) {
+        fclose(f);
+        return fail(RA_ECAPACITY, "%s has %lld bytes, buffer %zu", path, (long long)size, capacity);
+    }
+    const size_t n = size ? fread(buf, 1, (size_t)size, f) : 0;
+    fclose(f);
+    if (n != (size_t)size) return fail(RA_EIO, "short read from %s", path);
+    return ok();
+}
+
 size_t ra_workspace_bytes(const ra_config *cfg, int32_t op, int64_t n_rows, int64_t max_pos) {
     if (check_config(cfg)) return 0;
     if (op != RA_OP_DECODE && op != RA_OP_PREFILL) {
@@ -298,6 +619,8 @@ const char *ra_status_string(int32_t status) {
         case RA_EUNSUPPORTED: return "unsupported configuration";
         case RA_ECAPACITY: return "buffer too small";
         case RA_EHIP: return "HIP runtime error";
+        case RA_EIO: return "file error";
+        case RA_EFORMAT: return "not a readable snapshot";
         default: return "unknown status";
     }
 }

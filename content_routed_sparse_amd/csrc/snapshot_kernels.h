@@ -1,0 +1,34 @@
+// Internal launch interface of the snapshot kernels (snapshot.hip) for the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+// Snapshots: contiguous byte ranges copied in batches (16-byte multiples, 16-byte aligned),
+// optionally behind a guard word that must read ~0; 64-bit words written from the host by value;
+// SHA-256 of each `chunk`-byte piece of src (a multiple of 16 bytes, at most 4096; the last piece
+// may be short), stored at dig + 32 * index or compared with it (atomicMin(bad, src_offset +
+// the piece's offset) on a mismatch).
+struct Segment {
+    const void *src;
+    void *dst;
+    uint64_t n16;
+};
+constexpr int kSegs = 128;
+struct SegmentBatch {
+    Segment seg[kSegs];
+    int n;
+};
+constexpr int kWords = 256;
+struct WordBatch {
+    uint64_t v[kWords];
+    int n;
+};
+hipError_t launch_copy_segments(const SegmentBatch &sb, const unsigned long long *guard, hipStream_t st);
+hipError_t launch_write_words(uint64_t *dst, const WordBatch &wb, hipStream_t st);
+hipError_t launch_fill_u64(unsigned long long *dst, unsigned long long v, hipStream_t st);
+hipError_t launch_sha_chunks(const uint8_t *src, uint64_t n_bytes, uint64_t chunk, uint8_t *dig, bool compare,
+                             unsigned long long *bad, uint64_t src_offset, hipStream_t st);
+
+}  // namespace ra

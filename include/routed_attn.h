@@ -56,7 +56,9 @@ typedef enum {
     RA_EINVAL = 1,       /* null pointer, inconsistent sizes, out-of-range parameter */
     RA_EUNSUPPORTED = 2, /* valid but not implemented: head_dim, dtype, top_k, group size */
     RA_ECAPACITY = 3,    /* a buffer is too small (capacity, max_spans, score_stride, workspace) */
-    RA_EHIP = 4          /* the HIP runtime reported an error when launching */
+    RA_EHIP = 4,         /* the HIP runtime reported an error when launching */
+    RA_EIO = 5,          /* a file could not be opened, read or written */
+    RA_EFORMAT = 6       /* bytes that are not a snapshot this library can read */
 } ra_status;
 
 typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
@@ -194,6 +196,76 @@ ra_status routed_attn_decode_fp8(const ra_config *cfg, const ra_rows *rows, cons
                                  const uint8_t *v_codes, const float *k_scales, const float *v_scales,
                                  const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
                                  void *stream);
+
+/* ---------------------------------------------------------------- session snapshots
+ * Keeping the cache instead of reprocessing it, with sessions saved to and restored from disk
+ * (release post, on why fast long context matters; its stack lists session snapshots), with
+ * every saved byte covered by SHA-256 digests in the spirit of the InfiniteKV post's hashed
+ * receipts.  The image format is the library's own; all integers little-endian:
+ *
+ *   header   64 bytes of fields, then int64 lengths[B], zero-padded to a multiple of 16 bytes:
+ *              0 magic "CRSASNP1" | 8 u32 version 1 | 12 u32 element type (0 fp32, 1 bf16)
+ *             16 u32 B | 20 u32 Hkv | 24 u32 d | 28 u32 S | 32 u64 payload bytes
+ *             40 u64 header bytes | 48 u32 chunk bytes 4096 | 52 u32 fan-in 16 | 56 u64 0
+ *   payload  for b, for g: K[b][g][0:L_b][:] then V[b][g][0:L_b][:] (cache element bytes);
+ *            then for b, for g: span_mean[b][g][0:floor(L_b/S)][:] then run_sum[b][g][:] (fp32)
+ *   levels   D_1 = SHA-256 (FIPS 180-4) of each 4096-byte chunk of header|payload (the last one
+ *            may be short); D_(l+1) = SHA-256 of each group of 16 digests (512 bytes) of D_l while
+ *            |D_l| > 16; root = SHA-256 of the last level.
+ *   image    header | payload | D_1 | ... | D_m | root
+ *
+ * Only live state is saved (rows [0, L_b), complete span means, the running sums); restoring
+ * writes exactly those and leaves every other row and slot of the destination untouched.
+ * `lengths` arguments are HOST arrays of cfg->batch int64 token counts; `header` arguments are
+ * HOST copies of the first bytes of an image (at least the header); `image` is DEVICE memory.
+ * The 8-bit cache is not covered (snapshots hold fp32 or bf16 caches). */
+
+typedef struct {
+    int32_t dtype;         /* ra_dtype of the saved K/V rows */
+    int32_t batch;         /* B */
+    int32_t num_kv_heads;  /* Hkv */
+    int32_t head_dim;      /* d */
+    int32_t span_size;     /* S */
+    int32_t reserved;
+    uint64_t header_bytes;
+    uint64_t payload_bytes;
+    uint64_t image_bytes;  /* whole image including digest levels and root */
+} ra_snapshot_info;
+
+/* Image bytes for the given host lengths[cfg->batch]; 0 if cfg or a length is invalid. */
+size_t kv_snapshot_bytes(const ra_config *cfg, const int64_t *lengths);
+
+/* kv_snapshot_pack -- write the image of the cache state (K/V caches, span_mean, run_sum in the
+ * layouts above; lengths: host) into the device buffer `image` of at least kv_snapshot_bytes
+ * bytes: header, payload copies and every digest level, all enqueued on `stream`. */
+ra_status kv_snapshot_pack(const ra_config *cfg, const void *k_cache, const void *v_cache, const float *span_mean,
+                           const float *run_sum, const int64_t *lengths, void *image, size_t image_bytes,
+                           void *stream);
+
+/* kv_snapshot_parse -- read a header (host bytes, `header_avail` of them) into `info` and, when
+ * `lengths` is not NULL, its B lengths (B <= max_batch).  RA_EFORMAT for anything but a header
+ * written by kv_snapshot_pack (magic, version, chunk size, fan-in, sizes consistent). */
+ra_status kv_snapshot_parse(const void *header, size_t header_avail, ra_snapshot_info *info, int64_t *lengths,
+                            int32_t max_batch);
+
+/* kv_snapshot_verify -- recompute every digest of a device image and compare it with the stored
+ * one.  Writes to the device word *bad_offset: UINT64_MAX if all match, else the smallest image
+ * offset of a chunk whose digest differs (the root's chunk is the whole last level). */
+ra_status kv_snapshot_verify(const void *header, size_t header_avail, const void *image, size_t image_bytes,
+                             uint64_t *bad_offset, void *stream);
+
+/* kv_snapshot_unpack -- copy the saved state of a device image into K/V caches, span_mean and
+ * run_sum laid out per cfg (same dtype, Hkv, d and S as the image; image B <= cfg->batch; each
+ * length <= capacity).  If `guard` (device) is not NULL the copies run only when *guard reads
+ * UINT64_MAX, so unpack after verify on one stream restores nothing from a damaged image. */
+ra_status kv_snapshot_unpack(const ra_config *cfg, const void *header, size_t header_avail, const void *image,
+                             size_t image_bytes, const uint64_t *guard, void *k_cache, void *v_cache,
+                             float *span_mean, float *run_sum, void *stream);
+
+/* Host file helpers: write `bytes` bytes (through a temporary file renamed into place), or read
+ * a whole file into `buf` (capacity bytes); with buf NULL only *bytes (the file size) is set. */
+ra_status kv_snapshot_write_file(const char *path, const void *data, size_t bytes);
+ra_status kv_snapshot_read_file(const char *path, void *buf, size_t capacity, size_t *bytes);
 
 /* Workspace bytes needed by routed_attn_decode / routed_attn_prefill (op = ra_op); 0 if the
  * configuration is invalid (ra_last_error then says why). */

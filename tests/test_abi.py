@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import content_routed_sparse_amd as ra
@@ -114,3 +115,87 @@ def test_workspace_sizes():
     assert p > 8192 * 32 * 18 * 132 * 4  # at least the partial records
     assert ra.lib().ra_workspace_bytes(ctypes.byref(c.c()), 5, 1, 0) == 0
     assert ra.lib().ra_status_string(3) == b"buffer too small"
+
+
+# ------------------------------------------------------------------------- session snapshots
+def small_snapshot(dtype=np.uint16, lengths=(300, 17, 0)):
+    from oracle import snapshot as N
+    rng = np.random.default_rng(3)
+    B, Hkv, cap, d, S = len(lengths), 2, 300, 64, 16
+    k = rng.integers(0, 1 << 16, size=(B, Hkv, cap, d), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, size=(B, Hkv, cap, d), dtype=np.uint16)
+    if dtype == np.float32:
+        k, v = k.astype(np.float32), v.astype(np.float32)
+    mean = rng.standard_normal((B, Hkv, cap // S, d)).astype(np.float32)
+    run = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+    c = ra.Config(num_q_heads=4, num_kv_heads=Hkv, head_dim=d, span_size=S, top_k=4, window=S,
+                  dtype=ra.RA_BF16 if dtype == np.uint16 else ra.RA_F32, batch=B, capacity=cap)
+    return c, N.build_image(k, v, mean, run, np.array(lengths), S)
+
+
+@pytest.mark.parametrize("dtype", [np.uint16, np.float32], ids=["bf16", "fp32"])
+def test_snapshot_header_parse_and_size(dtype):
+    from oracle import snapshot as N
+    c, img = small_snapshot(dtype)
+    info, lengths = ra.kv_snapshot_parse(img)
+    assert list(lengths) == [300, 17, 0]
+    assert (info["dtype"], info["batch"], info["num_kv_heads"], info["head_dim"], info["span_size"]) == \
+        (c.dtype, 3, 2, 64, 16)
+    assert info["image_bytes"] == len(img) == ra.snapshot_bytes(c, [300, 17, 0])
+    assert info["header_bytes"] == N.header_bytes(3)
+    # only the header is needed; an unaligned copy of it parses the same
+    odd = bytearray(b"x") + img[:info["header_bytes"]]
+    info2, lengths2 = ra.kv_snapshot_parse(np.frombuffer(bytes(odd), dtype=np.uint8)[1:])
+    assert info2 == info and list(lengths2) == [300, 17, 0]
+
+
+@pytest.mark.parametrize("offset,value", [(0, b"X"), (8, b"\x02"), (12, b"\x05"), (32, b"\x01"), (48, b"\x00\x08"),
+                                          (64, b"\xff\xff\xff\xff\xff\xff\xff\xff")])
+def test_snapshot_parse_rejects_malformed_headers(offset, value):
+    _, img = small_snapshot()
+    bad = bytearray(img[:96])
+    bad[offset:offset + len(value)] = value
+    with pytest.raises(ra.RoutedAttnError) as e:
+        ra.kv_snapshot_parse(bytes(bad))
+    assert e.value.status == 6
+    with pytest.raises(ra.RoutedAttnError):
+        ra.kv_snapshot_parse(img[:80])  # shorter than the header
+
+
+def test_snapshot_entry_points_validate_before_launch():
+    c, img = small_snapshot()
+    lib = ra.lib()
+    cc = c.c()
+    L = np.array([300, 17, 0], dtype=np.int64)
+    Lp = ctypes.c_void_p(L.ctypes.data)
+    n = ra.snapshot_bytes(c, L)
+    # NULL buffers, an image too small, lengths past the capacity
+    assert lib.kv_snapshot_pack(ctypes.byref(cc), None, FAKE, FAKE, FAKE, Lp, FAKE, n, None) == 1
+    assert lib.kv_snapshot_pack(ctypes.byref(cc), FAKE, FAKE, FAKE, FAKE, Lp, FAKE, n - 1, None) == 3
+    L2 = np.array([301, 0, 0], dtype=np.int64)
+    assert lib.kv_snapshot_pack(ctypes.byref(cc), FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(L2.ctypes.data), FAKE,
+                                1 << 30, None) == 3
+    assert lib.kv_snapshot_bytes(ctypes.byref(cc), ctypes.c_void_p(L2.ctypes.data)) == 0
+    # verify: an image shorter than the header says
+    hdr = np.frombuffer(img, dtype=np.uint8)
+    assert lib.kv_snapshot_verify(ctypes.c_void_p(hdr.ctypes.data), 96, FAKE, len(img) - 1, FAKE, None) == 6
+    # unpack into a configuration of another shape / dtype / batch
+    for kw, status in ((dict(head_dim=128), 1), (dict(dtype=ra.RA_F32), 1), (dict(span_size=32, window=32), 1),
+                       (dict(batch=2), 3), (dict(capacity=200), 3)):
+        c2 = ra.Config(**{**c.__dict__, **kw, "max_spans": -1})
+        cc2 = c2.c()
+        st = lib.kv_snapshot_unpack(ctypes.byref(cc2), ctypes.c_void_p(hdr.ctypes.data), 96, FAKE, len(img), None,
+                                    FAKE, FAKE, FAKE, FAKE, None)
+        assert st == status, (kw, st, lib.ra_last_error())
+
+
+def test_snapshot_file_helpers_round_trip(tmp_path):
+    _, img = small_snapshot()
+    p = str(tmp_path / "s.bin")
+    ra.kv_snapshot_write_file(p, img)
+    back = ra.kv_snapshot_read_file(p, pin=False)
+    assert bytes(back.numpy()) == img
+    assert not os.path.exists(p + ".tmp")
+    with pytest.raises(ra.RoutedAttnError) as e:
+        ra.kv_snapshot_read_file(str(tmp_path / "missing.bin"), pin=False)
+    assert e.value.status == 5
