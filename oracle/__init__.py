@@ -7,4 +7,4 @@ from .routed_attention import (NO_SPAN, Problem, attend, attended_positions, num
                                route_scores, routed_rows, select_spans, summaries, summary_update, widen,
                                widen_f32, window_start)
 from .compare import output_errors, output_ok, score_abs_bound, selection_verdict
-from . import kv_fp8, snapshot
+from . import cold_retrieval, kv_fp8, snapshot
