@@ -42,6 +42,7 @@ def parse():
                    help="timed calls of dense causal attention on the prefill rows (0: skip)")
     p.add_argument("--no-fp8", action="store_true", help="skip the decode step over the 8-bit cache")
     p.add_argument("--no-snapshot", action="store_true", help="skip the session snapshot / restore measurement")
+    p.add_argument("--no-cold", action="store_true", help="skip the token-level cold retrieval decode step")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 256 MiB device copy (reference kernel for HBM byte counters)")
     return p.parse_args()
@@ -221,6 +222,9 @@ def main():
 
     if not args.no_fp8:
         result["decode_fp8"] = bench_decode_fp8(args, w, K, V, qs)
+
+    if not args.no_cold:
+        result["cold_retrieval"] = bench_cold(args, w, K, V, qs)
 
     if not args.no_snapshot:
         result["snapshot"] = bench_snapshot(w, st[0], cfg1)
@@ -442,6 +446,95 @@ def bench_decode_fp8(args, w, K, V, qs):
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": counter_traffic("routed_attn_decode_fp8_1m"),
                          "algorithmic_bytes_per_launch": int(bytes_step), "avg_launch_ms": round(attn_ms, 5)},
+            "repeat_bitwise_identical": bool(same)}
+
+
+COLD_HOT, COLD_K = 256, 64
+
+
+def bench_cold(args, w, K, V, qs):
+    """Token-level cold retrieval decode step on the same sequences: a 256-token hot window and 64
+    cold tokens per query head found by a Hamming scan over sign-bit signatures.  A step is
+    kv_signature_update (the new token) -> cold_select (scan + merge) -> cold_attn_decode."""
+    import torch
+
+    import content_routed_sparse_amd as ra
+
+    L, NC, dev = w.decode_len, K.shape[0], K.device
+    cfg1 = ra.Config(w.num_q_heads, w.num_kv_heads, w.head_dim, w.span_size, w.top_k, w.window, ra.RA_BF16, 1, L)
+    sig = torch.empty(NC, w.num_kv_heads, L, w.head_dim // 8, dtype=torch.uint8, device=dev)
+    zero = torch.zeros(1, dtype=torch.int64, device=dev)
+    before = torch.full((1,), L - 1, dtype=torch.int64, device=dev)
+    full = torch.full((1,), L, dtype=torch.int64, device=dev)
+    ws = torch.empty(ra.cold_workspace_bytes(cfg1, 1, L - 1, COLD_HOT, COLD_K), dtype=torch.uint8, device=dev)
+    st = []
+    for s in range(NC):
+        ra.kv_signature_update(cfg1, K[s:s + 1], sig[s:s + 1], zero, before, L - 1)
+        rows = ra.Rows(qs[s], torch.zeros(1, dtype=torch.int32, device=dev),
+                       torch.full((1,), L - 1, dtype=torch.int64, device=dev), L - 1)
+        d = {"rows": rows, "sel": torch.empty(1, w.num_q_heads, COLD_K, dtype=torch.int32, device=dev),
+             "out": torch.empty(1, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)}
+        d["sig"] = ra.prepare("kv_signature_update", cfg1, K[s:s + 1], sig[s:s + 1], before, full, 1)
+        d["select"] = ra.prepare("cold_select", cfg1, rows, sig[s:s + 1], COLD_HOT, COLD_K, d["sel"], ws)
+        d["attn"] = ra.prepare("cold_attn_decode", cfg1, rows, K[s:s + 1], V[s:s + 1], d["sel"], COLD_HOT, COLD_K,
+                               d["out"])
+        st.append(d)
+    torch.cuda.synchronize()
+    for d in st:
+        d["sig"]()
+        d["select"]()
+        d["attn"]()
+    torch.cuda.synchronize()
+    first = [(d["sel"].clone(), d["out"].clone()) for d in st]
+    stream = torch.cuda.current_stream()
+    EV_EVERY = 8
+    timed_ev = list(range(0, args.steps, EV_EVERY))
+    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in timed_ev}
+
+    def step(i, timed):
+        d = st[i % NC]
+        d["sig"]()
+        if timed and i in ev:
+            ev[i][0].record(stream)
+        d["select"]()
+        if timed and i in ev:
+            ev[i][1].record(stream)
+        d["attn"]()
+        if timed and i in ev:
+            ev[i][2].record(stream)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    sel_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev.values()]))
+    attn_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev.values()]))
+    same = all(torch.equal(f[0], d["sel"]) and torch.equal(f[1], d["out"]) for f, d in zip(first, st))
+    # algorithmic bytes of cold_select: the signatures of every cold position of each kv head, q,
+    # and the selection written; cold_attn_decode: K and V rows of each kv head's union of fetched
+    # positions plus its hot window, q and out
+    n_cold = L - 1 - COLD_HOT + 1
+    sel_bytes = w.num_kv_heads * n_cold * (w.head_dim // 8) + w.num_q_heads * (w.head_dim * 2 + COLD_K * 4)
+    G = w.group
+    per_seq = []
+    for d in st:
+        sel = d["sel"][0].cpu().numpy()
+        uni = sum(len(set(sel[g * G:(g + 1) * G].ravel().tolist()) - {-1}) for g in range(w.num_kv_heads))
+        per_seq.append((uni + w.num_kv_heads * COLD_HOT) * w.head_dim * 2 * 2 + w.num_q_heads * w.head_dim * 6)
+    attn_bytes = float(np.mean(per_seq))
+    achieved = sel_bytes / (sel_ms * 1e-3) / 1e9
+    return {"workload": "decode_1m, cold retrieval (hot window 256, top_k_cold 64, sign-bit signatures)",
+            "value": round(1000.0 / ms, 2), "unit": "tokens/s", "ms_per_step": round(ms, 5),
+            "roofline": {"bound": "hbm", "kernel": "cold_select (cold_tile scan + cold_merge)",
+                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic("cold_select_1m"),
+                         "algorithmic_bytes_per_launch": int(sel_bytes), "avg_launch_ms": round(sel_ms, 5)},
+            "cold_attn_decode": {"avg_launch_ms": round(attn_ms, 5), "algorithmic_bytes_per_launch": int(attn_bytes),
+                                 "achieved_GBps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1)},
             "repeat_bitwise_identical": bool(same)}
 
 

@@ -23,6 +23,7 @@ RA_F32, RA_BF16 = 0, 1
 RA_OP_DECODE, RA_OP_PREFILL = 0, 1
 EXPORTED = ("span_summary_update", "route_scores", "topk_spans", "routed_attn_decode", "routed_attn_prefill",
             "attn_dense_causal", "kv_quantize_fp8", "span_summary_update_fp8", "routed_attn_decode_fp8",
+            "kv_signature_update", "ra_cold_workspace_bytes", "cold_select", "cold_attn_decode",
             "kv_snapshot_bytes", "kv_snapshot_pack", "kv_snapshot_parse", "kv_snapshot_verify", "kv_snapshot_unpack",
             "kv_snapshot_write_file", "kv_snapshot_read_file", "ra_workspace_bytes", "ra_status_string",
             "ra_last_error")
@@ -77,6 +78,9 @@ def lib():
             "kv_quantize_fp8": [CP, P, P, P, P, P, I64, P],
             "span_summary_update_fp8": [CP, P, P, P, P, P, P, I64, P],
             "routed_attn_decode_fp8": [CP, RP, P, P, P, P, P, P, P, SZ, P],
+            "kv_signature_update": [CP, P, P, P, P, I64, P],
+            "cold_select": [CP, RP, P, I32, I32, P, P, SZ, P],
+            "cold_attn_decode": [CP, RP, P, P, P, I32, I32, P, P],
             "kv_snapshot_pack": [CP, P, P, P, P, P, P, SZ, P],
             "kv_snapshot_parse": [P, SZ, ctypes.POINTER(_SnapshotInfo), P, I32],
             "kv_snapshot_verify": [P, SZ, P, SZ, P, P],
@@ -88,6 +92,8 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = I32
+        L.ra_cold_workspace_bytes.argtypes = [CP, I64, I64, I32, I32]
+        L.ra_cold_workspace_bytes.restype = SZ
         L.kv_snapshot_bytes.argtypes = [CP, P]
         L.kv_snapshot_bytes.restype = SZ
         L.ra_workspace_bytes.argtypes = [CP, I32, I64, I64]
@@ -286,6 +292,36 @@ def _args_attn_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, wo
             _dev(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream)), (c, r)
 
 
+# Cold retrieval: signatures [B][Hkv][cap][d/8] uint8, sel_cold [n][Hq][top_k_cold] int32.
+def _sig_shape(cfg):
+    return (cfg.batch, cfg.num_kv_heads, cfg.capacity, cfg.head_dim // 8)
+
+
+def _args_kv_signature_update(cfg, k_cache, sig, old_len, new_len, max_new_tokens, stream=None):
+    c = cfg.c()
+    return (ctypes.byref(c), _dev(k_cache, cfg.torch_dtype, _kv_shape(cfg), "k_cache"),
+            _dev(sig, torch.uint8, _sig_shape(cfg), "sig"), _dev(old_len, torch.int64, (cfg.batch,), "old_len"),
+            _dev(new_len, torch.int64, (cfg.batch,), "new_len"), int(max_new_tokens), _stream(stream)), (c,)
+
+
+def _args_cold_select(cfg, rows, sig, hot_window, top_k_cold, sel_cold, workspace, stream=None):
+    c, r = cfg.c(), _rows(cfg, rows)
+    n = rows.q.shape[0]
+    return (ctypes.byref(c), ctypes.byref(r), _dev(sig, torch.uint8, _sig_shape(cfg), "sig"), int(hot_window),
+            int(top_k_cold), _dev(sel_cold, torch.int32, (n, cfg.num_q_heads, top_k_cold), "sel_cold"),
+            _dev(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream)), (c, r)
+
+
+def _args_cold_attn_decode(cfg, rows, k_cache, v_cache, sel_cold, hot_window, top_k_cold, out, stream=None):
+    c, r = cfg.c(), _rows(cfg, rows)
+    n = rows.q.shape[0]
+    return (ctypes.byref(c), ctypes.byref(r), _dev(k_cache, cfg.torch_dtype, _kv_shape(cfg), "k_cache"),
+            _dev(v_cache, cfg.torch_dtype, _kv_shape(cfg), "v_cache"),
+            _dev(sel_cold, torch.int32, (n, cfg.num_q_heads, top_k_cold), "sel_cold"), int(hot_window),
+            int(top_k_cold), _dev(out, torch.float32, (n, cfg.num_q_heads, cfg.head_dim), "out"),
+            _stream(stream)), (c, r)
+
+
 _BUILDERS = {
     "span_summary_update": _args_span_summary_update,
     "route_scores": _args_route_scores,
@@ -296,6 +332,9 @@ _BUILDERS = {
     "kv_quantize_fp8": _args_kv_quantize_fp8,
     "span_summary_update_fp8": _args_span_summary_update_fp8,
     "routed_attn_decode_fp8": _args_attn_fp8,
+    "kv_signature_update": _args_kv_signature_update,
+    "cold_select": _args_cold_select,
+    "cold_attn_decode": _args_cold_attn_decode,
 }
 
 
@@ -388,6 +427,32 @@ def routed_attn_decode_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel,
     """routed_attn_decode over an 8-bit K/V cache (bf16 queries)."""
     args, _keep = _args_attn_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, workspace, stream)
     _check(lib().routed_attn_decode_fp8(*args))
+
+
+def kv_signature_update(cfg, k_cache, sig, old_len, new_len, max_new_tokens, stream=None):
+    """Cold retrieval: sign-bit signatures of K rows [old_len[b], new_len[b])."""
+    args, _keep = _args_kv_signature_update(cfg, k_cache, sig, old_len, new_len, max_new_tokens, stream)
+    _check(lib().kv_signature_update(*args))
+
+
+def cold_workspace_bytes(cfg, n_rows, max_pos, hot_window, top_k_cold):
+    c = cfg.c()
+    n = lib().ra_cold_workspace_bytes(ctypes.byref(c), n_rows, max_pos, hot_window, top_k_cold)
+    if n == 0 and n_rows > 0:
+        raise RoutedAttnError(1, lib().ra_last_error().decode())
+    return n
+
+
+def cold_select(cfg, rows, sig, hot_window, top_k_cold, sel_cold, workspace, stream=None):
+    """Hamming scan: the top_k_cold cold positions of every (row, head), ascending, -1 padded."""
+    args, _keep = _args_cold_select(cfg, rows, sig, hot_window, top_k_cold, sel_cold, workspace, stream)
+    _check(lib().cold_select(*args))
+
+
+def cold_attn_decode(cfg, rows, k_cache, v_cache, sel_cold, hot_window, top_k_cold, out, stream=None):
+    """Exact attention over the selected cold positions and the hot window."""
+    args, _keep = _args_cold_attn_decode(cfg, rows, k_cache, v_cache, sel_cold, hot_window, top_k_cold, out, stream)
+    _check(lib().cold_attn_decode(*args))
 
 
 # ------------------------------------------------------------------------ session snapshots

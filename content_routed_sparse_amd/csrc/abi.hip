@@ -7,6 +7,7 @@
 #include <vector>
 
 #include "common.h"
+#include "cold_kernels.h"
 #include "kernels.h"
 #include "snapshot_kernels.h"
 
@@ -277,6 +278,93 @@ ra_status routed_attn_decode_fp8(const ra_config *cfg, const ra_rows *rows, cons
     return hip_status(ra::launch_decode_fp8(row_args(cfg, rows), k_codes, v_codes, k_scales, v_scales, sel, out,
                                             workspace, (hipStream_t)stream),
                       "routed_attn_decode_fp8 launch");
+}
+
+// ------------------------------------------------------------------- token-level cold retrieval
+}  // extern "C"
+
+namespace {
+
+ra_status check_cold(const ra_config *c, int32_t hot_window, int32_t top_k_cold) {
+    if (hot_window < 1) return fail(RA_EINVAL, "hot_window must be >= 1");
+    if (top_k_cold < 1 || top_k_cold > ra::kMaxCold)
+        return fail(RA_EUNSUPPORTED, "top_k_cold must be in [1, %d]", ra::kMaxCold);
+    if (c->capacity >= (1LL << 31)) return fail(RA_EUNSUPPORTED, "cold retrieval needs capacity < 2^31");
+    return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status kv_signature_update(const ra_config *cfg, const void *k_cache, uint8_t *sig, const int64_t *old_len,
+                              const int64_t *new_len, int64_t max_new_tokens, void *stream) {
+    ra_status s = check_config(cfg);
+    if (s) return s;
+    if (!k_cache || !sig || !old_len || !new_len) return fail(RA_EINVAL, "NULL pointer argument");
+    if (max_new_tokens < 0) return fail(RA_EINVAL, "max_new_tokens must be >= 0");
+    if (max_new_tokens > cfg->capacity) return fail(RA_ECAPACITY, "max_new_tokens exceeds capacity");
+    if ((uintptr_t)sig & 15) return fail(RA_EINVAL, "sig must be 16-byte aligned");
+    if (max_new_tokens == 0) return ok();
+    const int rpb = 256 / (cfg->head_dim / 32);
+    if ((int64_t)cfg->batch * cfg->num_kv_heads * ra::ceil_div(max_new_tokens, rpb) >= kMaxGrid)
+        return fail(RA_EUNSUPPORTED, "grid too large");
+    ra::SigArgs a;
+    a.k = k_cache;
+    a.sig = (uint32_t *)sig;
+    a.old_len = old_len;
+    a.new_len = new_len;
+    a.dtype = cfg->dtype;
+    a.d = cfg->head_dim;
+    a.B = cfg->batch;
+    a.Hkv = cfg->num_kv_heads;
+    a.cap = cfg->capacity;
+    a.max_new = max_new_tokens;
+    return hip_status(ra::launch_signatures(a, (hipStream_t)stream), "kv_signature_update launch");
+}
+
+size_t ra_cold_workspace_bytes(const ra_config *cfg, int64_t n_rows, int64_t max_pos, int32_t hot_window,
+                               int32_t top_k_cold) {
+    if (check_config(cfg) || check_cold(cfg, hot_window, top_k_cold)) return 0;
+    if (n_rows < 0 || max_pos < 0 || max_pos >= cfg->capacity) {
+        fail(RA_EINVAL, "n_rows must be >= 0 and max_pos in [0, capacity)");
+        return 0;
+    }
+    ra_rows r{nullptr, nullptr, nullptr, n_rows, max_pos};
+    return ra::cold_workspace_bytes(row_args(cfg, &r), hot_window, top_k_cold);
+}
+
+ra_status cold_select(const ra_config *cfg, const ra_rows *rows, const uint8_t *sig, int32_t hot_window,
+                      int32_t top_k_cold, int32_t *sel_cold, void *workspace, size_t workspace_bytes, void *stream) {
+    ra_status s = check_config(cfg);
+    if (s) return s;
+    if ((s = check_rows(cfg, rows))) return s;
+    if ((s = check_cold(cfg, hot_window, top_k_cold))) return s;
+    if (rows->n_rows == 0) return ok();
+    if (!sig || !sel_cold) return fail(RA_EINVAL, "NULL sig or sel_cold");
+    if ((uintptr_t)sig & 15) return fail(RA_EINVAL, "sig must be 16-byte aligned");
+    const ra::RowArgs a = row_args(cfg, rows);
+    if (a.n_rows * a.Hkv * (int64_t)ra::cold_tiles(a.max_pos, hot_window) >= kMaxGrid)
+        return fail(RA_EUNSUPPORTED, "scan grid too large: use fewer rows per call");
+    const size_t need = ra::cold_workspace_bytes(a, hot_window, top_k_cold);
+    if (!workspace || workspace_bytes < need)
+        return fail(RA_ECAPACITY, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+    return hip_status(ra::launch_cold_select(a, (const uint32_t *)sig, hot_window, top_k_cold, sel_cold, workspace,
+                                             (hipStream_t)stream),
+                      "cold_select launch");
+}
+
+ra_status cold_attn_decode(const ra_config *cfg, const ra_rows *rows, const void *k_cache, const void *v_cache,
+                           const int32_t *sel_cold, int32_t hot_window, int32_t top_k_cold, float *out, void *stream) {
+    ra_status s = check_config(cfg);
+    if (s) return s;
+    if ((s = check_rows(cfg, rows))) return s;
+    if ((s = check_cold(cfg, hot_window, top_k_cold))) return s;
+    if (rows->n_rows == 0) return ok();
+    if (!k_cache || !v_cache || !sel_cold || !out) return fail(RA_EINVAL, "NULL K, V, sel_cold or out");
+    return hip_status(ra::launch_cold_attn(row_args(cfg, rows), k_cache, v_cache, sel_cold, hot_window, top_k_cold,
+                                           out, (hipStream_t)stream),
+                      "cold_attn_decode launch");
 }
 
 // ------------------------------------------------------------------------- session snapshots

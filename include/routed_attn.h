@@ -197,6 +197,46 @@ ra_status routed_attn_decode_fp8(const ra_config *cfg, const ra_rows *rows, cons
                                  const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* ------------------------------------------------------- token-level cold retrieval
+ * A second way to reach old context (InfiniteKV post): the last H positions (the hot window)
+ * are attended exactly; every older ("cold") position is found by a Hamming scan over compact
+ * signatures, and the top_k_cold nearest are attended together with the hot window.  The post
+ * fixes no signature format; this library computes, for a row at position t with query q:
+ *
+ *   signature     sig(x) = the d sign bits of x (bit e set iff element e has its sign bit set,
+ *                 -0 included), packed little-endian: bit e is bit e % 8 of byte e / 8
+ *   cold set      positions [0, t-H+1);  hot window [max(0, t-H+1), t]
+ *   distance      popcount(sig(q) xor sig(k_p)) (integers: the selection is exact)
+ *   selection     m = min(top_k_cold, |cold set|) positions by (distance ascending, position
+ *                 ascending), listed ascending and padded with -1
+ *   attention     softmax(q . k_p / sqrt(d)) over selection U hot window; O = sum w_p v_p
+ *
+ * Query head h reads kv head h / (Hq / Hkv).  Layouts: sig [batch][Hkv][capacity][d/8] uint8
+ * (16-byte aligned), sel_cold [n_rows][Hq][top_k_cold] int32, out [n_rows][Hq][d] float; K, V, q
+ * as above.  Supported: 1 <= top_k_cold <= 128, hot_window >= 1, capacity < 2^31.  The span
+ * fields of cfg (span_size, top_k, window) are validated but not used by these calls. */
+
+/* kv_signature_update -- signatures of K rows [old_len[b], new_len[b]) of every (sequence b, kv
+ * head); other rows are not touched.  max_new_tokens: host bound on new_len[b] - old_len[b]. */
+ra_status kv_signature_update(const ra_config *cfg, const void *k_cache, uint8_t *sig, const int64_t *old_len,
+                              const int64_t *new_len, int64_t max_new_tokens, void *stream);
+
+/* Workspace bytes of cold_select (per-tile candidate lists); 0 if the arguments are invalid. */
+size_t ra_cold_workspace_bytes(const ra_config *cfg, int64_t n_rows, int64_t max_pos, int32_t hot_window,
+                               int32_t top_k_cold);
+
+/* cold_select -- the Hamming scan and selection of every (row, query head): sel_cold as above.
+ * Reads each signature of a row's cold set once per kv head (scored against all its query
+ * heads); workspace of at least ra_cold_workspace_bytes bytes. */
+ra_status cold_select(const ra_config *cfg, const ra_rows *rows, const uint8_t *sig, int32_t hot_window,
+                      int32_t top_k_cold, int32_t *sel_cold, void *workspace, size_t workspace_bytes, void *stream);
+
+/* cold_attn_decode -- exact attention of each row over its selected cold positions and its hot
+ * window; out as above.  Entries outside the row's cold set [0, t-H+1) (the -1 padding among
+ * them) are ignored, so no position is counted twice. */
+ra_status cold_attn_decode(const ra_config *cfg, const ra_rows *rows, const void *k_cache, const void *v_cache,
+                           const int32_t *sel_cold, int32_t hot_window, int32_t top_k_cold, float *out, void *stream);
+
 /* ---------------------------------------------------------------- session snapshots
  * Keeping the cache instead of reprocessing it, with sessions saved to and restored from disk
  * (release post, on why fast long context matters; its stack lists session snapshots), with

@@ -199,3 +199,28 @@ def test_snapshot_file_helpers_round_trip(tmp_path):
     with pytest.raises(ra.RoutedAttnError) as e:
         ra.kv_snapshot_read_file(str(tmp_path / "missing.bin"), pin=False)
     assert e.value.status == 5
+
+
+# ------------------------------------------------------------------- token-level cold retrieval
+def test_cold_entry_points_validate_before_launch():
+    lib = ra.lib()
+    c = cfg(batch=1)
+    cc = c.c()
+    r = rows()
+    L = 1 << 20
+    need = lib.ra_cold_workspace_bytes(ctypes.byref(cc), 1, L - 1, 256, 64)
+    assert need == 32 * ((L - 256 + 8191) // 8192) * 64 * 8
+    for hot, kc, status in ((0, 64, 1), (256, 0, 2), (256, 129, 2)):
+        assert lib.cold_select(ctypes.byref(cc), ctypes.byref(r), FAKE, hot, kc, FAKE, FAKE, 1 << 30, None) == status
+        assert lib.cold_attn_decode(ctypes.byref(cc), ctypes.byref(r), FAKE, FAKE, FAKE, hot, kc, FAKE, None) == status
+        assert lib.ra_cold_workspace_bytes(ctypes.byref(cc), 1, L - 1, hot, kc) == 0
+    assert lib.cold_select(ctypes.byref(cc), ctypes.byref(r), FAKE, 256, 64, FAKE, FAKE, need - 1, None) == 3
+    assert lib.cold_select(ctypes.byref(cc), ctypes.byref(r), None, 256, 64, FAKE, FAKE, need, None) == 1
+    assert lib.cold_attn_decode(ctypes.byref(cc), ctypes.byref(r), FAKE, None, FAKE, 256, 64, FAKE, None) == 1
+    big = cfg(capacity=1 << 31).c()
+    assert lib.cold_select(ctypes.byref(big), ctypes.byref(r), FAKE, 256, 64, FAKE, FAKE, 1 << 40, None) == 2
+    one = np.zeros(1, dtype=np.int64)
+    op = ctypes.c_void_p(one.ctypes.data)
+    assert lib.kv_signature_update(ctypes.byref(cc), FAKE, None, op, op, 1, None) == 1
+    assert lib.kv_signature_update(ctypes.byref(cc), FAKE, ctypes.c_void_p(0x1008), op, op, 1, None) == 1  # alignment
+    assert lib.kv_signature_update(ctypes.byref(cc), FAKE, FAKE, op, op, (1 << 20) + 1, None) == 3
