@@ -346,6 +346,8 @@ ra_status cold_select(const ra_config *cfg, const ra_rows *rows, const uint8_t *
     const ra::RowArgs a = row_args(cfg, rows);
     if (a.n_rows * a.Hkv * (int64_t)ra::cold_tiles(a.max_pos, hot_window) >= kMaxGrid)
         return fail(RA_EUNSUPPORTED, "scan grid too large: use fewer rows per call");
+    if (ra::cold_tiles(a.max_pos, hot_window) > ra::kMergeTiles)
+        return fail(RA_EUNSUPPORTED, "cold retrieval scans at most %d x 8192 cold positions per row", ra::kMergeTiles);
     const size_t need = ra::cold_workspace_bytes(a, hot_window, top_k_cold);
     if (!workspace || workspace_bytes < need)
         return fail(RA_ECAPACITY, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);

@@ -24,7 +24,7 @@ namespace ra {
 namespace {
 
 constexpr int kTile = 8192;                  // cold positions per scan block
-constexpr int kTileThreads = 256;
+constexpr int kTileThreads = 512;
 constexpr int kPerThread = kTile / kTileThreads;
 constexpr int kMaxGroup = 32;                // query heads per kv head
 constexpr int kBins = 129;                   // distances 0 .. 128
@@ -107,8 +107,20 @@ __device__ __forceinline__ uint32_t distance(const SigWords<D> &s, const uint32_
     return d;
 }
 
-// Exclusive prefix sum over the 256 threads of a block (x >= 0); also returns the total.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *wave_tot, uint32_t &total) {
+// LDS of cold_tile for G query heads (32-bit words): query signatures, distance histograms, tie
+// bitmasks, and per-wave candidate buffers of up to 128 entries per head within a 60 KB budget.
+constexpr int kTileLdsWords = 60 * 1024 / 4;
+constexpr int kTileWaves = kTileThreads / 64;
+__host__ __device__ constexpr int tile_buf(int G, int WPR) {
+    const int room = (kTileLdsWords - G * (WPR + kBinStride + kTile / 32)) / (G * kTileWaves);
+    return room < 128 ? room : 128;
+}
+__host__ __device__ constexpr int tile_lds_words(int G, int WPR) {
+    return G * (WPR + kBinStride + kTile / 32 + kTileWaves * tile_buf(G, WPR));
+}
+
+// Exclusive prefix sum over the kTileThreads threads of a block (x >= 0); also returns the total.
+__device__ __forceinline__ uint32_t tile_exclusive_scan(uint32_t x, uint32_t *wave_tot, uint32_t &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t inc = x;
 #pragma unroll
@@ -121,13 +133,41 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *w
     uint32_t before = 0;
     total = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kTileWaves; ++w) {
         const uint32_t t = wave_tot[w];
         if (w < wave) before += t;
         total += t;
     }
     __syncthreads();
     return before + inc - x;
+}
+
+// Cut distance of a distance histogram: the first bin x <= last with bins 0..x summing to at
+// least `target`, found by the 64 lanes of one wave (lane l holds bins l, l + 64, l + 128; a
+// scan per group of 64 bins); kBins if there is none.  Every lane returns the same values;
+// `below` = the sum of the bins before the cut.
+__device__ __forceinline__ uint32_t wave_cut(const uint32_t *hist, int last, uint32_t target, uint32_t &below) {
+    const int lane = threadIdx.x & 63;
+    uint32_t base = 0;
+    for (int seg = 0; seg * 64 <= last; ++seg) {
+        const int x = seg * 64 + lane;
+        const uint32_t v = x <= last ? hist[x] : 0u;
+        uint32_t inc = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(inc, off);
+            if (lane >= off) inc += y;
+        }
+        const uint64_t hit = __ballot(x <= last && base + inc >= target);
+        if (hit) {
+            const int f = (int)__builtin_ctzll(hit);
+            below = base + (uint32_t)__shfl((int)(inc - v), f);
+            return (uint32_t)(seg * 64 + f);
+        }
+        base += (uint32_t)__shfl((int)inc, 63);
+    }
+    below = base;
+    return kBins;
 }
 
 template <typename T, int D>
@@ -137,12 +177,16 @@ __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ 
                                                           int Hq, int Hkv, int G, int B, int64_t cap, int64_t max_pos,
                                                           int H, int kc, int n_tiles) {
     constexpr int WPR = D / 32;
-    __shared__ uint32_t qsig[kMaxGroup][WPR];
-    __shared__ uint32_t hist[kMaxGroup * kBinStride];
-    __shared__ uint32_t tie[kMaxGroup][kTile / 32];
-    __shared__ uint32_t cut[kMaxGroup], below[kMaxGroup], need[kMaxGroup], cnt[kMaxGroup];
-    __shared__ uint32_t wave_tot[4];
-    const int tid = threadIdx.x;
+    extern __shared__ uint32_t lds[];
+    const int BW = tile_buf(G, WPR);
+    uint32_t *qsig = lds;                              // [G][WPR]
+    uint32_t *hist = qsig + G * WPR;                   // [G][kBinStride]
+    uint32_t *tie = hist + G * kBinStride;             // [G][kTile / 32]
+    uint32_t *cbuf = tie + G * (kTile / 32);           // [G][kTileWaves][BW]: (distance << 16) | index
+    __shared__ uint32_t theta[kMaxGroup], cut[kMaxGroup], below[kMaxGroup], need[kMaxGroup], cnt[kMaxGroup];
+    __shared__ uint32_t wcount[kMaxGroup][kTileWaves];
+    __shared__ uint32_t wave_tot[kTileWaves], slow;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tile = blockIdx.x % n_tiles;
     const int64_t rg = blockIdx.x / n_tiles;
     const int g = (int)(rg % Hkv);
@@ -156,71 +200,142 @@ __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ 
     const int n_here = (int)(n_cold - lo <= 0 ? 0 : (n_cold - lo < kTile ? n_cold - lo : kTile));
     uint64_t *out0 = cand + ((row * Hq + (int64_t)g * G) * n_tiles + tile) * kc;  // + h * n_tiles * kc
     const int64_t head_stride = (int64_t)n_tiles * kc;
-    const int kc_eff = n_here < kc ? n_here : kc;
+    const uint32_t kc_eff = (uint32_t)(n_here < kc ? n_here : kc);
     if (n_here == 0) {
         for (int x = tid; x < G * kc; x += kTileThreads) out0[(x / kc) * head_stride + x % kc] = kNoKey;
         return;
     }
-    // query signatures, cleared histograms and tie masks
+    // the tile's signatures, kept in registers: token x = i * kTileThreads + tid
+    const uint32_t *sbase = sig + (((int64_t)seq * Hkv + g) * cap + lo) * WPR;
+    SigWords<D> sg[kPerThread];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const int x = i * kTileThreads + tid;
+        sg[i] = load_sig<D>(sbase + (int64_t)(x < n_here ? x : 0) * WPR);
+    }
     for (int x = tid; x < G * WPR; x += kTileThreads) {
         const int h = x / WPR, w = x % WPR;
-        qsig[h][w] = sig_word(q + ((row * Hq + (int64_t)g * G + h) * D), w);
+        qsig[x] = sig_word(q + ((row * Hq + (int64_t)g * G + h) * D), w);
     }
     for (int x = tid; x < G * kBinStride; x += kTileThreads) hist[x] = 0;
-    for (int h = 0; h < G; ++h) tie[h][tid] = 0;
+    for (int x = tid; x < G * (kTile / 32); x += kTileThreads) tie[x] = 0;
     if (tid < G) cnt[tid] = 0;
+    if (tid == 0) slow = 0;
     __syncthreads();
-    const uint32_t *sbase = sig + (((int64_t)seq * Hkv + g) * cap + lo) * WPR;
-    // sweep 1: distance histograms
-    for (int i = 0; i < kPerThread; ++i) {
-        const int x = i * kTileThreads + tid;
-        if (x < n_here) {
-            const SigWords<D> s = load_sig<D>(sbase + (int64_t)x * WPR);
-            for (int h = 0; h < G; ++h) atomicAdd(&hist[h * kBinStride + distance<D>(s, qsig[h])], 1u);
-        }
+    // 1. a sample of min(512, n) positions spread evenly over the tile sets a threshold per head
+    //    below which about 3 * kc of the tile's distances should fall
+    const int n_s = n_here < kTileThreads ? n_here : kTileThreads;
+    if (tid < n_s) {
+        const SigWords<D> smp = load_sig<D>(sbase + (int64_t)tid * (n_here / n_s) * WPR);
+        for (int h = 0; h < G; ++h) atomicAdd(&hist[h * kBinStride + distance<D>(smp, qsig + h * WPR)], 1u);
     }
     __syncthreads();
-    // cut distance per head: the smallest D* with at least kc_eff keys at or below it
-    if (tid < G) {
-        uint32_t cum = 0, dstar = kBins - 1;
-        for (int x = 0; x < kBins; ++x) {
-            const uint32_t c = hist[tid * kBinStride + x];
-            if (cum + c >= (uint32_t)kc_eff) {
-                dstar = x;
-                break;
+    for (int h = wave; h < G; h += kTileWaves) {
+        const uint32_t target = (uint32_t)((3 * (int64_t)kc_eff * n_s + n_here - 1) / n_here);
+        uint32_t b;
+        const uint32_t th = wave_cut(hist + h * kBinStride, kBins - 1, target, b);
+        if (lane == 0) theta[h] = th < kBins ? th : kBins - 1;
+    }
+    __syncthreads();
+    // 2. candidates at or below the threshold, appended per wave (ballot + mbcnt: no atomics)
+    for (int h = 0; h < G; ++h) {
+        const uint32_t th = theta[h];
+        uint32_t qw[WPR];
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) qw[w] = qsig[h * WPR + w];
+        uint32_t *wb = cbuf + (h * kTileWaves + wave) * BW;
+        uint32_t wc = 0;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int x = i * kTileThreads + tid;
+            const uint32_t dd = distance<D>(sg[i], qw);
+            const bool pass = x < n_here && dd <= th;
+            const uint64_t bal = __ballot(pass);
+            if (bal) {
+                const uint32_t idx = wc + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                if (pass && idx < (uint32_t)BW) wb[idx] = (dd << 16) | (uint32_t)x;
+                wc += (uint32_t)__popcll(bal);
             }
-            cum += c;
         }
-        cut[tid] = dstar;
-        below[tid] = cum;
-        need[tid] = kc_eff - cum;
+        if (lane == 0) wcount[h][wave] = wc;
+    }
+    for (int x = tid; x < G * kBinStride; x += kTileThreads) hist[x] = 0;
+    __syncthreads();
+    // 3. histograms of the candidates; the cut per head, or the slow path when a wave's buffer
+    //    overflowed or the threshold left fewer than kc_eff candidates
+    for (int e = tid; e < G * kTileWaves * BW; e += kTileThreads) {
+        const int h = e / (kTileWaves * BW), w = (e / BW) % kTileWaves, k = e % BW;
+        if ((uint32_t)k < wcount[h][w]) atomicAdd(&hist[h * kBinStride + (cbuf[e] >> 16)], 1u);
     }
     __syncthreads();
-    // sweep 2: keys below the cut (any order); ties at the cut marked in the bitmask
-    for (int i = 0; i < kPerThread; ++i) {
-        const int x = i * kTileThreads + tid;
-        if (x < n_here) {
-            const SigWords<D> s = load_sig<D>(sbase + (int64_t)x * WPR);
-            for (int h = 0; h < G; ++h) {
-                const uint32_t dd = distance<D>(s, qsig[h]);
+    for (int h = wave; h < G; h += kTileWaves) {
+        uint32_t b;
+        const uint32_t ct = wave_cut(hist + h * kBinStride, (int)theta[h], kc_eff, b);
+        if (lane == 0) {
+            bool over = false;
+            for (int w = 0; w < kTileWaves; ++w) over |= wcount[h][w] > (uint32_t)BW;
+            cut[h] = ct;
+            below[h] = b;
+            need[h] = kc_eff - b;
+            if (over || ct == kBins) atomicOr(&slow, 1u);
+        }
+    }
+    __syncthreads();
+    if (slow) {
+        // exact histograms of every distance, then the keys below the cut and the tie bitmasks
+        for (int x = tid; x < G * kBinStride; x += kTileThreads) hist[x] = 0;
+        __syncthreads();
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int i = 0; i < kPerThread; ++i)
+                if (i * kTileThreads + tid < n_here) atomicAdd(&hist[h * kBinStride + distance<D>(sg[i], qsig + h * WPR)], 1u);
+        __syncthreads();
+        for (int h = wave; h < G; h += kTileWaves) {
+            uint32_t b;
+            const uint32_t ct = wave_cut(hist + h * kBinStride, kBins - 1, kc_eff, b);
+            if (lane == 0) {
+                cut[h] = ct;
+                below[h] = b;
+                need[h] = kc_eff - b;
+            }
+        }
+        __syncthreads();
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int i = 0; i < kPerThread; ++i) {
+                const int x = i * kTileThreads + tid;
+                if (x >= n_here) continue;
+                const uint32_t dd = distance<D>(sg[i], qsig + h * WPR);
                 if (dd < cut[h]) {
-                    const uint32_t slot = atomicAdd(&cnt[h], 1u);
-                    out0[h * head_stride + slot] = cold_key(dd, lo + x);
+                    out0[h * head_stride + atomicAdd(&cnt[h], 1u)] = cold_key(dd, lo + x);
                 } else if (dd == cut[h]) {
-                    atomicOr(&tie[h][x >> 5], 1u << (x & 31));
+                    atomicOr(&tie[h * (kTile / 32) + (x >> 5)], 1u << (x & 31));
                 }
             }
+    } else {
+        // every distance up to the cut is among the candidates
+        for (int e = tid; e < G * kTileWaves * BW; e += kTileThreads) {
+            const int h = e / (kTileWaves * BW), w = (e / BW) % kTileWaves, k = e % BW;
+            if ((uint32_t)k >= wcount[h][w]) continue;
+            const uint32_t v = cbuf[e], dd = v >> 16, x = v & 0xFFFFu;
+            if (dd < cut[h]) {
+                out0[h * head_stride + atomicAdd(&cnt[h], 1u)] = cold_key(dd, lo + x);
+            } else if (dd == cut[h]) {
+                atomicOr(&tie[h * (kTile / 32) + (x >> 5)], 1u << (x & 31));
+            }
         }
     }
     __syncthreads();
-    // the first need[h] ties in position order: thread tid owns mask word tid (positions 32 tid ..)
+    // the first need[h] ties in position order: thread tid < kTile / 32 owns mask word tid
     for (int h = 0; h < G; ++h) {
-        uint32_t word = tie[h][tid];
+        uint32_t word = tid < kTile / 32 ? tie[h * (kTile / 32) + tid] : 0u;
         uint32_t total;
-        const uint32_t pre = block_exclusive_scan(__popc(word), wave_tot, total);
+        const uint32_t pre = tile_exclusive_scan(__popc(word), wave_tot, total);
         const uint32_t nd = need[h];
         if (pre < nd) {
-            uint32_t take = nd - pre, j = 0;
+            const uint32_t take = nd - pre;
+            uint32_t j = 0;
             while (word && j < take) {
                 const int bit = __builtin_ctz(word);
                 word &= word - 1;
@@ -231,85 +346,126 @@ __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ 
     }
     // padding past kc_eff
     for (int x = tid; x < G * kc; x += kTileThreads)
-        if (x % kc >= kc_eff) out0[(x / kc) * head_stride + x % kc] = kNoKey;
+        if ((uint32_t)(x % kc) >= kc_eff) out0[(x / kc) * head_stride + x % kc] = kNoKey;
 }
 
-// kc <= kMaxCold
-__global__ void __launch_bounds__(256) cold_merge(const uint64_t *__restrict__ cand, int32_t *__restrict__ sel,
-                                                  int n_tiles, int kc) {
-    __shared__ uint32_t hist[kBins];
+// kc <= kMaxCold, n_tiles <= kMergeTiles.  Candidates are read three times, coalesced and in
+// batches of kMergeBatch independent loads per thread (they stay in L2): the distance histogram;
+// keys below the cut and per-tile tie counts; the ties of every tile whose ties are all taken.
+// The one tile whose ties are taken in part ranks them by position.
+constexpr int kMergeThreads = 512;
+constexpr int kMergeBatch = 8;
+
+template <typename F>
+__device__ __forceinline__ void for_each_key(const uint64_t *c, int M, F f) {
+    for (int x0 = threadIdx.x; x0 < M; x0 += kMergeThreads * kMergeBatch) {
+        uint64_t k[kMergeBatch];
+#pragma unroll
+        for (int b = 0; b < kMergeBatch; ++b) {
+            const int x = x0 + b * kMergeThreads;
+            k[b] = x < M ? c[x] : kNoKey;
+        }
+#pragma unroll
+        for (int b = 0; b < kMergeBatch; ++b)
+            if (k[b] != kNoKey) f(x0 + b * kMergeThreads, k[b]);
+    }
+}
+
+__global__ void __launch_bounds__(kMergeThreads) cold_merge(const uint64_t *__restrict__ cand, int32_t *__restrict__ sel,
+                                                            int n_tiles, int kc) {
+    __shared__ uint32_t hist[kBinStride];
+    __shared__ uint32_t tcnt[kMergeTiles], tpre[kMergeTiles];
     __shared__ int64_t lst[kMaxCold];
-    __shared__ uint32_t wave_tot[4];
-    __shared__ uint32_t n_valid, n_lt, s_cut, s_need;
-    const int tid = threadIdx.x;
+    __shared__ uint32_t wave_tot[kMergeThreads / 64];
+    __shared__ uint32_t n_valid, n_lst, s_cut, s_need, b_tile, b_take;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t rh = blockIdx.x;
     const uint64_t *c = cand + rh * (int64_t)n_tiles * kc;
     const int M = n_tiles * kc;
-    for (int x = tid; x < kBins; x += 256) hist[x] = 0;
+    for (int x = tid; x < kBinStride; x += kMergeThreads) hist[x] = 0;
+    for (int x = tid; x < n_tiles; x += kMergeThreads) tcnt[x] = 0;
     if (tid == 0) {
         n_valid = 0;
-        n_lt = 0;
+        n_lst = 0;
+        b_tile = 0xFFFFFFFFu;
+        b_take = 0;
     }
     __syncthreads();
     uint32_t mine = 0;
-    for (int x = tid; x < M; x += 256) {
-        const uint64_t k = c[x];
-        if (k != kNoKey) {
-            atomicAdd(&hist[key_dist(k)], 1u);
-            ++mine;
-        }
-    }
+    for_each_key(c, M, [&](int, uint64_t k) {
+        atomicAdd(&hist[key_dist(k)], 1u);
+        ++mine;
+    });
     atomicAdd(&n_valid, mine);
     __syncthreads();
     const uint32_t kc_eff = n_valid < (uint32_t)kc ? n_valid : (uint32_t)kc;
-    if (tid == 0) {
-        uint32_t cum = 0, dstar = kBins - 1;
-        for (int x = 0; x < kBins; ++x) {
-            if (cum + hist[x] >= kc_eff) {
-                dstar = x;
-                break;
-            }
-            cum += hist[x];
+    if (wave == 0) {
+        uint32_t b;
+        const uint32_t ct = wave_cut(hist, kBins - 1, kc_eff, b);
+        if (lane == 0) {
+            s_cut = ct;
+            s_need = kc_eff - b;
         }
-        s_cut = dstar;
-        s_need = kc_eff - cum;
     }
     __syncthreads();
     const uint32_t dstar = s_cut, nd = s_need;
     if (kc_eff > 0) {
-        for (int x = tid; x < M; x += 256) {
-            const uint64_t k = c[x];
-            if (k != kNoKey && key_dist(k) < dstar) lst[atomicAdd(&n_lt, 1u)] = key_pos(k);
-        }
+        for_each_key(c, M, [&](int x, uint64_t k) {
+            const uint32_t dd = key_dist(k);
+            if (dd < dstar) lst[atomicAdd(&n_lst, 1u)] = key_pos(k);
+            else if (dd == dstar) atomicAdd(&tcnt[x / kc], 1u);
+        });
     }
     __syncthreads();
-    const uint32_t lt = n_lt;
-    // ties at D*: tile by tile (tiles cover increasing positions), each tile's smallest positions
-    uint32_t carry = 0;
-    for (int j0 = 0; j0 < n_tiles && kc_eff > 0; j0 += 256) {
-        const int j = j0 + tid;
-        uint32_t cj = 0;
-        if (j < n_tiles)
-            for (int e = 0; e < kc; ++e) {
-                const uint64_t k = c[(int64_t)j * kc + e];
-                cj += (k != kNoKey && key_dist(k) == dstar) ? 1u : 0u;
-            }
-        uint32_t total;
-        const uint32_t pre = carry + block_exclusive_scan(cj, wave_tot, total);
-        if (j < n_tiles && cj > 0 && pre < nd) {
-            const uint32_t take = nd - pre < cj ? nd - pre : cj;
-            for (int e = 0; e < kc; ++e) {
-                const uint64_t k = c[(int64_t)j * kc + e];
-                if (k == kNoKey || key_dist(k) != dstar) continue;
-                uint32_t rank = 0;
-                for (int f = 0; f < kc; ++f) {
-                    const uint64_t k2 = c[(int64_t)j * kc + f];
-                    rank += (k2 != kNoKey && key_dist(k2) == dstar && key_pos(k2) < key_pos(k)) ? 1u : 0u;
-                }
-                if (rank < take) lst[lt + pre + rank] = key_pos(k);
-            }
+    // exclusive prefix of the tie counts over tiles (tiles cover increasing positions): thread tid
+    // owns the contiguous tiles [tid * per, tid * per + per)
+    const int per = (n_tiles + kMergeThreads - 1) / kMergeThreads;
+    uint32_t local = 0;
+    for (int j = tid * per; j < tid * per + per && j < n_tiles; ++j) local += tcnt[j];
+    uint32_t run;
+    {
+        uint32_t inc = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(inc, off);
+            if (lane >= off) inc += y;
         }
-        carry += total;
+        if (lane == 63) wave_tot[wave] = inc;
+        __syncthreads();
+        uint32_t before = 0;
+        for (int w = 0; w < wave; ++w) before += wave_tot[w];
+        run = before + inc - local;
+    }
+    for (int j = tid * per; j < tid * per + per && j < n_tiles; ++j) {
+        tpre[j] = run;
+        if (run < nd && run + tcnt[j] > nd) {  // the one tile whose ties are taken in part
+            b_tile = (uint32_t)j;
+            b_take = nd - run;
+        }
+        run += tcnt[j];
+    }
+    __syncthreads();
+    if (kc_eff > 0) {
+        for_each_key(c, M, [&](int x, uint64_t k) {
+            const int j = x / kc;
+            if (key_dist(k) == dstar && tpre[j] + tcnt[j] <= nd) lst[atomicAdd(&n_lst, 1u)] = key_pos(k);
+        });
+    }
+    const uint32_t bt = b_tile;
+    if (bt != 0xFFFFFFFFu && wave == 0) {
+        // ties of the boundary tile: lane l holds entries l and l + 64; rank by position
+        const uint64_t *ct = c + (int64_t)bt * kc;
+        uint64_t k0 = lane < kc ? ct[lane] : kNoKey, k1 = lane + 64 < kc ? ct[lane + 64] : kNoKey;
+        const bool t0 = k0 != kNoKey && key_dist(k0) == dstar, t1 = k1 != kNoKey && key_dist(k1) == dstar;
+        const int64_t p0 = t0 ? key_pos(k0) : INT64_MAX, p1 = t1 ? key_pos(k1) : INT64_MAX;
+        uint32_t r0 = 0, r1 = 0;
+        for (int src = 0; src < 64; ++src) {
+            const int64_t a = __shfl(p0, src), b = __shfl(p1, src);
+            r0 += (a < p0 ? 1u : 0u) + (b < p0 ? 1u : 0u);
+            r1 += (a < p1 ? 1u : 0u) + (b < p1 ? 1u : 0u);
+        }
+        if (t0 && r0 < b_take) lst[atomicAdd(&n_lst, 1u)] = p0;
+        if (t1 && r1 < b_take) lst[atomicAdd(&n_lst, 1u)] = p1;
     }
     __syncthreads();
     // ascending order, padded with -1
@@ -326,28 +482,34 @@ __global__ void __launch_bounds__(256) cold_merge(const uint64_t *__restrict__ c
     }
 }
 
-// Attention over fetched + hot positions.  16-byte slices: LPR lanes per key row; the wave's
-// RPI row groups take keys x = 4 * (wave * RPI + rr) ... in turn; each group keeps its own online
-// softmax state over its slice of the output.
+// Attention over fetched + hot positions.  16-byte slices: LPR lanes per key row, RPI row groups
+// per wave, 16 waves: NGRP groups take keys x = grp, grp + NGRP, ... two at a time (both keys'
+// K and V loads issued before either is used); each group keeps its own online softmax state over
+// its slice of the output, and the groups are merged through LDS.  The selection is staged in LDS
+// first, so key positions cost no dependent global load.
+constexpr int kAttnWaves = 16;
+
 template <typename T, int D>
-__global__ void __launch_bounds__(256) cold_attn(const T *__restrict__ q, const int32_t *__restrict__ row_seq,
-                                                 const int64_t *__restrict__ row_pos, const T *__restrict__ K,
-                                                 const T *__restrict__ V, const int32_t *__restrict__ sel,
-                                                 float *__restrict__ out, int Hq, int Hkv, int G, int B, int64_t cap,
-                                                 int64_t max_pos, int H, int kc, float scale_log2) {
-    constexpr int EPL = 16 / sizeof(T), LPR = D / EPL, RPI = 64 / LPR, NGRP = 4 * RPI;
+__global__ void __launch_bounds__(kAttnWaves * 64) cold_attn(const T *__restrict__ q, const int32_t *__restrict__ row_seq,
+                                                        const int64_t *__restrict__ row_pos, const T *__restrict__ K,
+                                                        const T *__restrict__ V, const int32_t *__restrict__ sel,
+                                                        float *__restrict__ out, int Hq, int Hkv, int G, int B,
+                                                        int64_t cap, int64_t max_pos, int H, int kc,
+                                                        float scale_log2) {
+    constexpr int EPL = 16 / sizeof(T), LPR = D / EPL, RPI = 64 / LPR, NGRP = kAttnWaves * RPI;
     __shared__ float gm[NGRP], gl[NGRP], go[NGRP][D];
+    __shared__ int32_t ssel[kMaxCold];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane % LPR, rr = lane / LPR, grp = wave * RPI + rr;
     const int64_t rh = blockIdx.x;
     const int64_t row = rh / Hq;
     const int h = (int)(rh % Hq), g = h / G;
+    if (tid < kc) ssel[tid] = sel[rh * kc + tid];
     int64_t t = row_pos[row];
     t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
     int seq = row_seq[row];
     seq = seq < 0 ? 0 : (seq >= B ? B - 1 : seq);
     const int64_t hot_lo = t - H + 1 > 0 ? t - H + 1 : 0;
-    const int32_t *s = sel + rh * kc;
     const int64_t n_keys = kc + (t - hot_lo + 1);  // selection entries, then the hot window
     const T *kb = K + ((int64_t)seq * Hkv + g) * cap * D;
     const T *vb = V + ((int64_t)seq * Hkv + g) * cap * D;
@@ -365,40 +527,53 @@ __global__ void __launch_bounds__(256) cold_attn(const T *__restrict__ q, const 
             }
         }
     }
+    __syncthreads();
     float M = -__builtin_huge_valf(), L = 0.f, o[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) o[i] = 0.f;
-    for (int64_t x = grp; x < n_keys; x += NGRP) {
-        const int64_t p = x < kc ? (int64_t)s[x] : hot_lo + (x - kc);
-        if (x < kc && (p < 0 || p >= hot_lo)) continue;  // padding, or not a cold position
-        const uint4 kr = *reinterpret_cast<const uint4 *>(kb + p * D + c * EPL);
-        const uint4 vr = *reinterpret_cast<const uint4 *>(vb + p * D + c * EPL);
-        float kf[EPL], vf[EPL];
-        const uint32_t ku[4] = {kr.x, kr.y, kr.z, kr.w}, vu[4] = {vr.x, vr.y, vr.z, vr.w};
+    for (int64_t x0 = grp; x0 < n_keys; x0 += 2 * NGRP) {
+        bool ok[2];
+        uint4 kr[2], vr[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (sizeof(T) == 2) {
-                kf[2 * i] = bf16_bits_to_f32(ku[i] & 0xFFFFu);
-                kf[2 * i + 1] = bf16_bits_to_f32(ku[i] >> 16);
-                vf[2 * i] = bf16_bits_to_f32(vu[i] & 0xFFFFu);
-                vf[2 * i + 1] = bf16_bits_to_f32(vu[i] >> 16);
-            } else {
-                kf[i] = __uint_as_float(ku[i]);
-                vf[i] = __uint_as_float(vu[i]);
-            }
+        for (int u = 0; u < 2; ++u) {
+            const int64_t x = x0 + u * NGRP;
+            int64_t p = x < kc ? (int64_t)ssel[x < kc ? x : 0] : hot_lo + (x - kc);
+            // padding and entries outside the cold set are skipped; past the end as well
+            ok[u] = x < n_keys && (x >= kc || (p >= 0 && p < hot_lo));
+            p = ok[u] ? p : t;
+            kr[u] = *reinterpret_cast<const uint4 *>(kb + p * D + c * EPL);
+            vr[u] = *reinterpret_cast<const uint4 *>(vb + p * D + c * EPL);
         }
-        float z = 0.f;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) z = fmaf(qf[i], kf[i], z);
+        for (int u = 0; u < 2; ++u) {
+            float kf[EPL], vf[EPL];
+            const uint32_t ku[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w}, vu[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
 #pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
-        z *= scale_log2;
-        const float Mn = fmaxf(M, z);
-        const float a = exp2f(M - Mn), e = exp2f(z - Mn);
-        L = L * a + e;
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (sizeof(T) == 2) {
+                    kf[2 * i] = bf16_bits_to_f32(ku[i] & 0xFFFFu);
+                    kf[2 * i + 1] = bf16_bits_to_f32(ku[i] >> 16);
+                    vf[2 * i] = bf16_bits_to_f32(vu[i] & 0xFFFFu);
+                    vf[2 * i + 1] = bf16_bits_to_f32(vu[i] >> 16);
+                } else {
+                    kf[i] = __uint_as_float(ku[i]);
+                    vf[i] = __uint_as_float(vu[i]);
+                }
+            }
+            float z = 0.f;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) o[i] = fmaf(e, vf[i], o[i] * a);
-        M = Mn;
+            for (int i = 0; i < EPL; ++i) z = fmaf(qf[i], kf[i], z);
+#pragma unroll
+            for (int off = LPR / 2; off > 0; off >>= 1) z += __shfl_xor(z, off);
+            if (!ok[u]) continue;  // uniform over the group's lanes
+            z *= scale_log2;
+            const float Mn = fmaxf(M, z);
+            const float a = exp2f(M - Mn), e = exp2f(z - Mn);
+            L = L * a + e;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) o[i] = fmaf(e, vf[i], o[i] * a);
+            M = Mn;
+        }
     }
     if (c == 0) {
         gm[grp] = M;
@@ -435,12 +610,14 @@ hipError_t select_launch(const RowArgs &a, const uint32_t *sig, int H, int kc, i
                          hipStream_t st) {
     const int n_tiles = cold_tiles(a.max_pos, H);
     uint64_t *cand = (uint64_t *)ws;
-    hipLaunchKernelGGL((cold_tile<T, D>), dim3((unsigned)(a.n_rows * a.Hkv * n_tiles)), dim3(kTileThreads), 0, st,
+    const size_t lds = tile_lds_words(a.G, D / 32) * sizeof(uint32_t);
+    hipLaunchKernelGGL((cold_tile<T, D>), dim3((unsigned)(a.n_rows * a.Hkv * n_tiles)), dim3(kTileThreads), lds, st,
                        (const T *)a.q, a.row_seq, a.row_pos, sig, cand, a.Hq, a.Hkv, a.G, a.B, a.cap, a.max_pos, H, kc,
                        n_tiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(cold_merge, dim3((unsigned)(a.n_rows * a.Hq)), dim3(256), 0, st, cand, sel, n_tiles, kc);
+    hipLaunchKernelGGL(cold_merge, dim3((unsigned)(a.n_rows * a.Hq)), dim3(kMergeThreads), 0, st, cand, sel, n_tiles,
+                       kc);
     return hipGetLastError();
 }
 
@@ -448,7 +625,7 @@ template <typename T, int D>
 hipError_t attn_launch(const RowArgs &a, const void *K, const void *V, const int32_t *sel, int H, int kc, float *out,
                        hipStream_t st) {
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    hipLaunchKernelGGL((cold_attn<T, D>), dim3((unsigned)(a.n_rows * a.Hq)), dim3(256), 0, st, (const T *)a.q,
+    hipLaunchKernelGGL((cold_attn<T, D>), dim3((unsigned)(a.n_rows * a.Hq)), dim3(kAttnWaves * 64), 0, st, (const T *)a.q,
                        a.row_seq, a.row_pos, (const T *)K, (const T *)V, sel, out, a.Hq, a.Hkv, a.G, a.B, a.cap,
                        a.max_pos, H, kc, scale_log2);
     return hipGetLastError();

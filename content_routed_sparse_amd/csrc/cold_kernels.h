@@ -8,7 +8,8 @@
 
 namespace ra {
 
-constexpr int kMaxCold = 128;  // largest top_k_cold
+constexpr int kMaxCold = 128;      // largest top_k_cold
+constexpr int kMergeTiles = 4096;  // scan tiles (of 8192 cold positions) per row: 33.5M positions
 
 struct SigArgs {  // signatures of rows [old_len[b], new_len[b]) of a K cache
     const void *k;
