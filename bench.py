@@ -9,6 +9,11 @@ So that every step reads its keys and values from HBM rather than from the 256 M
 Cache, the bench keeps `--caches` independent 1M-token sequences (2 GiB of K/V each) and step
 i works on sequence i mod caches; each step is the same single-sequence workload.
 
+Further objects in the same line (each with its own roofline): the 8-bit cache decode step, the
+token-level cold retrieval step, a session snapshot of one 1M-token state, the chunked prefill
+(8192 tokens on 1M) with dense causal attention beside it, the CPU oracle's rate, and the decode
+steps of the 10M-token and ragged 16-sequence workloads.
+
 Prints one JSON line.  `--gpus` above 1 is refused: this path runs on one GPU.
 """
 import argparse
@@ -43,6 +48,8 @@ def parse():
     p.add_argument("--no-fp8", action="store_true", help="skip the decode step over the 8-bit cache")
     p.add_argument("--no-snapshot", action="store_true", help="skip the session snapshot / restore measurement")
     p.add_argument("--no-cold", action="store_true", help="skip the token-level cold retrieval decode step")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the decode steps of the 10M-token and ragged 16-sequence workloads")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 256 MiB device copy (reference kernel for HBM byte counters)")
     return p.parse_args()
@@ -243,6 +250,13 @@ def main():
         del K, V, st
         torch.cuda.empty_cache()
         result["prefill"] = bench_prefill(args.prefill_steps, args.dense_steps)
+
+    if not args.no_extra:
+        if args.no_prefill:
+            del K, V, st
+            torch.cuda.empty_cache()
+        result["decode_other"] = [bench_decode_workload(name, max(8, args.steps // 2), args.warmup)
+                                  for name in ("decode_10m", "ragged_decode_16")]
 
     print(json.dumps(result), flush=True)
 
@@ -611,6 +625,97 @@ def bench_snapshot(w, d0, cfg1, reps=3):
                          "frac": round(achieved / SHA_PEAK_GBS, 4), "traffic": None,
                          "algorithmic_bytes_per_launch": n, "avg_launch_ms": round(t_verify, 5)},
             "intact": intact, "restored_bitwise": bool(restored), "pcie_round_trip_bitwise": bool(round_trip)}
+
+
+def bench_decode_workload(name, steps, warmup):
+    """The decode step of another decode workload: decode_10m (one 10M-token sequence, spans of
+    4096) or ragged_decode_16 (16 sequences of 64K..512K tokens, spans of 512).  A step appends
+    one token to every sequence and runs span_summary_update -> route_scores -> topk_spans ->
+    routed_attn_decode for the last position of each; its working set (1-2 GB) is larger than
+    the 256 MB Infinity Cache, so steps repeat on the same caches."""
+    import torch
+
+    import content_routed_sparse_amd as ra
+    from synth import workloads as WL
+
+    w = WL.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    lengths = np.asarray(w.seq_lengths(), dtype=np.int64)
+    B, cap = len(lengths), int(lengths.max())
+    cfg = ra.Config(w.num_q_heads, w.num_kv_heads, w.head_dim, w.span_size, w.top_k, w.window, ra.RA_BF16, B, cap)
+    t0 = time.time()
+    K = torch.empty(B, w.num_kv_heads, cap, w.head_dim, dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    for b, L in enumerate(lengths):
+        for which, dst in (("k", K), ("v", V)):
+            dst[b, :, :L] = torch.from_numpy(WL.kv_slab(w, b, 0, int(L), which).view(np.int16)).view(torch.bfloat16).to(dev)
+    q = torch.from_numpy(np.stack([WL.query_at(w, b, int(L) - 1) for b, L in enumerate(lengths)]).view(np.int16))
+    q = q.view(torch.bfloat16).to(dev)
+    rows = ra.Rows(q, torch.arange(B, dtype=torch.int32, device=dev), torch.as_tensor(lengths - 1).to(dev), cap - 1)
+    mean = torch.zeros(B, w.num_kv_heads, cfg.max_spans, w.head_dim, dtype=torch.float32, device=dev)
+    run = torch.zeros(B, w.num_kv_heads, w.head_dim, dtype=torch.float32, device=dev)
+    zero = torch.zeros(B, dtype=torch.int64, device=dev)
+    before, after = torch.as_tensor(lengths - 1).to(dev), torch.as_tensor(lengths).to(dev)
+    ra.span_summary_update(cfg, K, mean, run, zero, before, int(lengths.max() - 1))  # setup, untimed
+    scores = torch.empty(B, w.num_q_heads, max(1, cfg.num_routable(cap - 1)), dtype=torch.float32, device=dev)
+    sel = torch.empty(B, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev)
+    out = torch.empty(B, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    ws = torch.empty(ra.workspace_bytes(cfg, ra.RA_OP_DECODE, B, cap - 1), dtype=torch.uint8, device=dev)
+    front = [ra.prepare("span_summary_update", cfg, K, mean, run, before, after, 1),
+             ra.prepare("route_scores", cfg, rows, mean, scores),
+             ra.prepare("topk_spans", cfg, rows, scores, sel)]
+    attn = ra.prepare("routed_attn_decode", cfg, rows, K, V, sel, out, ws)
+    torch.cuda.synchronize()
+    setup = time.time() - t0
+    for c in front:
+        c()
+    attn()
+    torch.cuda.synchronize()
+    first = out.clone()
+    stream = torch.cuda.current_stream()
+    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in range(0, steps, 4)}
+
+    def step(i, timed):
+        for c in front:
+            c()
+        if timed and i in ev:
+            ev[i][0].record(stream)
+        attn()
+        if timed and i in ev:
+            ev[i][1].record(stream)
+
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t1) * 1e3 / steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev.values()]))
+    same = torch.equal(first, out)
+    # algorithmic bytes of routed_attn_decode: per row and kv head, K and V rows of the union of
+    # the spans its query heads selected plus its window; q (bf16) and out (fp32)
+    G, S = w.group, w.span_size
+    selh = sel.cpu().numpy()
+    rows_kv = 0
+    for b, L in enumerate(lengths):
+        t = int(L) - 1
+        win = t - S * (max(0, t - w.window + 1) // S) + 1
+        for g in range(w.num_kv_heads):
+            uni = len(set(selh[b, g * G:(g + 1) * G].ravel().tolist()) - {-1})
+            rows_kv += uni * S + win
+    nbytes = rows_kv * w.head_dim * 2 * 2 + B * w.num_q_heads * w.head_dim * (2 + 4)
+    achieved = nbytes / (attn_ms * 1e-3) / 1e9
+    del K, V
+    torch.cuda.empty_cache()
+    return {"workload": name, "sequences": B, "context_max": cap, "span": S, "top_k": w.top_k, "window": w.window,
+            "value": round(B * 1000.0 / ms, 2), "unit": "tokens/s", "ms_per_step": round(ms, 5),
+            "roofline": {"bound": "hbm", "kernel": "routed_attn_decode (decode_attn + combine_block)",
+                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_ms": round(attn_ms, 5)},
+            "repeat_bitwise_identical": bool(same), "setup_seconds": round(setup, 1)}
 
 
 def cpu_baseline(w, d0, seconds):
