@@ -1,8 +1,9 @@
 """Benchmark: one decode step of content-routed sparse attention at 1M context, on one GPU.
 
 A step is the whole hot path for one new token of one sequence at L = 1,048,576 (32 query
-heads, 4 kv heads, d = 128, bf16 cache, spans of 1024, top-16 + window of 1024):
-span_summary_update (the new token) -> route_scores -> topk_spans -> routed_attn_decode.
+heads, 4 kv heads, d = 128, bf16 cache, spans of 1024, top-16 + window of 1024): route_scores ->
+topk_spans -> routed_attn_decode_append (the attention and, in its merge launch, the new token's
+span-summary update; equivalent to updating first, since the token completes no routable span).
 Inputs are synthetic (seeded generator), resident in HBM before timing starts.
 
 So that every step reads its keys and values from HBM rather than from the 256 MB Infinity
@@ -111,16 +112,18 @@ def main():
         ra.span_summary_update(cfg1, d["k"], d["mean"], d["run"], zero, before, L - 1)
     torch.cuda.synchronize()
 
-    # the step's four calls, validated once per sequence and replayed (ctypes only per call)
+    # the step's calls, validated once per sequence and replayed (ctypes only per call): routing
+    # and selection, then the attention with the new token's summary update in its merge launch.
+    # The new token (position L-1) completes no span that is routable at L-1 (that span lies in
+    # the window) and routing does not read the running sum, so this order selects exactly what
+    # update-then-route does.  Re-running the step re-closes that span: every step is the same work.
     for d in st:
         d["calls_front"] = [
-            # the new token (position L-1) joins its span; re-running the step re-closes that span,
-            # which lies inside the window and is never routed at this position
-            ra.prepare("span_summary_update", cfg1, d["k"], d["mean"], d["run"], before, after, 1),
             ra.prepare("route_scores", cfg1, d["rows"], d["mean"], d["scores"]),
             ra.prepare("topk_spans", cfg1, d["rows"], d["scores"], d["sel"]),
         ]
-        d["call_attn"] = ra.prepare("routed_attn_decode", cfg1, d["rows"], d["k"], d["v"], d["sel"], d["out"], ws)
+        d["call_attn"] = ra.prepare("routed_attn_decode_append", cfg1, d["rows"], d["k"], d["v"], d["sel"], d["out"],
+                                    ws, d["mean"], d["run"], before, after, 1)
 
     def front(d):
         for c in d["calls_front"]:
@@ -197,7 +200,8 @@ def main():
         sel = d["sel"][0].cpu().numpy()
         uni = sum(len(set(sel[g * G:(g + 1) * G].ravel().tolist()) - {-1}) for g in range(w.num_kv_heads))
         kv = (uni * w.span_size + w.num_kv_heads * win) * w.head_dim * 2 * 2
-        per_seq.append(kv + w.num_q_heads * w.head_dim * (2 + 4))
+        # + the summary update: the new K row, the running sum read and written, per kv head
+        per_seq.append(kv + w.num_q_heads * w.head_dim * (2 + 4) + w.num_kv_heads * w.head_dim * (2 + 8))
     bytes_step = float(np.mean([per_seq[i % NC] for i in timed_ev]))
     achieved = bytes_step / (attn_ms * 1e-3) / 1e9
 
@@ -219,7 +223,8 @@ def main():
         "config": {"workload": "decode_1m", "context": L, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "span": w.span_size, "top_k": w.top_k, "window": w.window, "batch": 1,
                    "rotated_sequences": NC, "hip_graphs": bool(args.graph)},
-        "roofline": {"bound": "hbm", "kernel": "routed_attn_decode (decode_attn + combine_block)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "routed_attn_decode_append (decode_attn + merge launch with the token's summary update)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(bytes_step), "avg_launch_ms": round(attn_ms, 5)},
@@ -373,8 +378,8 @@ def bench_prefill(steps, dense_steps=2):
 
 def bench_decode_fp8(args, w, K, V, qs):
     """The decode step over the 8-bit cache: the same sequences quantised to E4M3 codes with one
-    fp32 scale per (kv head, token) row (kv_quantize_fp8, untimed setup); a step is
-    span_summary_update_fp8 (the new token) -> route_scores -> topk_spans -> routed_attn_decode_fp8."""
+    fp32 scale per (kv head, token) row (kv_quantize_fp8, untimed setup); a step is route_scores ->
+    topk_spans -> routed_attn_decode_fp8_append (the attention and the new token's summary update)."""
     import torch
 
     import content_routed_sparse_amd as ra
@@ -403,11 +408,10 @@ def bench_decode_fp8(args, w, K, V, qs):
              "sel": torch.empty(1, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev),
              "out": torch.empty(1, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)}
         ra.span_summary_update_fp8(cfg1, d["k"], d["ks"], d["mean"], d["run"], zero, before, L - 1)
-        d["front"] = [ra.prepare("span_summary_update_fp8", cfg1, d["k"], d["ks"], d["mean"], d["run"], before, full, 1),
-                      ra.prepare("route_scores", cfg1, d["rows"], d["mean"], d["scores"]),
+        d["front"] = [ra.prepare("route_scores", cfg1, d["rows"], d["mean"], d["scores"]),
                       ra.prepare("topk_spans", cfg1, d["rows"], d["scores"], d["sel"])]
-        d["attn"] = ra.prepare("routed_attn_decode_fp8", cfg1, d["rows"], d["k"], d["v"], d["ks"], d["vs"], d["sel"],
-                               d["out"], ws)
+        d["attn"] = ra.prepare("routed_attn_decode_fp8_append", cfg1, d["rows"], d["k"], d["v"], d["ks"], d["vs"],
+                               d["sel"], d["out"], ws, d["mean"], d["run"], before, full, 1)
         st.append(d)
     torch.cuda.synchronize()
     for d in st:
@@ -450,12 +454,14 @@ def bench_decode_fp8(args, w, K, V, qs):
         sel = d["sel"][0].cpu().numpy()
         uni = sum(len(set(sel[g * G:(g + 1) * G].ravel().tolist()) - {-1}) for g in range(w.num_kv_heads))
         rows_kv = uni * w.span_size + w.num_kv_heads * win
-        per_seq.append(rows_kv * (w.head_dim + 4) * 2 + w.num_q_heads * w.head_dim * (2 + 4))
+        per_seq.append(rows_kv * (w.head_dim + 4) * 2 + w.num_q_heads * w.head_dim * (2 + 4) +
+                       w.num_kv_heads * (w.head_dim + 4 + w.head_dim * 8))
     bytes_step = float(np.mean([per_seq[i % NC] for i in timed_ev]))
     achieved = bytes_step / (attn_ms * 1e-3) / 1e9
     return {"workload": "decode_1m, 8-bit cache (E4M3 codes, one fp32 scale per kv-head row)",
             "value": round(1000.0 / ms, 2), "unit": "tokens/s", "ms_per_step": round(ms, 5),
-            "roofline": {"bound": "hbm", "kernel": "routed_attn_decode_fp8 (decode_attn + combine_block)",
+            "roofline": {"bound": "hbm",
+                         "kernel": "routed_attn_decode_fp8_append (decode_attn + merge launch with the summary update)",
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": counter_traffic("routed_attn_decode_fp8_1m"),
@@ -630,8 +636,8 @@ def bench_snapshot(w, d0, cfg1, reps=3):
 def bench_decode_workload(name, steps, warmup):
     """The decode step of another decode workload: decode_10m (one 10M-token sequence, spans of
     4096) or ragged_decode_16 (16 sequences of 64K..512K tokens, spans of 512).  A step appends
-    one token to every sequence and runs span_summary_update -> route_scores -> topk_spans ->
-    routed_attn_decode for the last position of each; its working set (1-2 GB) is larger than
+    one token to every sequence: route_scores -> topk_spans -> routed_attn_decode_append (with the
+    tokens' summary update) for the last position of each; its working set (1-2 GB) is larger than
     the 256 MB Infinity Cache, so steps repeat on the same caches."""
     import torch
 
@@ -661,10 +667,9 @@ def bench_decode_workload(name, steps, warmup):
     sel = torch.empty(B, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev)
     out = torch.empty(B, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
     ws = torch.empty(ra.workspace_bytes(cfg, ra.RA_OP_DECODE, B, cap - 1), dtype=torch.uint8, device=dev)
-    front = [ra.prepare("span_summary_update", cfg, K, mean, run, before, after, 1),
-             ra.prepare("route_scores", cfg, rows, mean, scores),
+    front = [ra.prepare("route_scores", cfg, rows, mean, scores),
              ra.prepare("topk_spans", cfg, rows, scores, sel)]
-    attn = ra.prepare("routed_attn_decode", cfg, rows, K, V, sel, out, ws)
+    attn = ra.prepare("routed_attn_decode_append", cfg, rows, K, V, sel, out, ws, mean, run, before, after, 1)
     torch.cuda.synchronize()
     setup = time.time() - t0
     for c in front:
@@ -711,7 +716,8 @@ def bench_decode_workload(name, steps, warmup):
     torch.cuda.empty_cache()
     return {"workload": name, "sequences": B, "context_max": cap, "span": S, "top_k": w.top_k, "window": w.window,
             "value": round(B * 1000.0 / ms, 2), "unit": "tokens/s", "ms_per_step": round(ms, 5),
-            "roofline": {"bound": "hbm", "kernel": "routed_attn_decode (decode_attn + combine_block)",
+            "roofline": {"bound": "hbm",
+                     "kernel": "routed_attn_decode_append (decode_attn + merge launch with the token's summary update)",
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                          "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_ms": round(attn_ms, 5)},

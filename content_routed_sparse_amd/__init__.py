@@ -23,6 +23,7 @@ RA_F32, RA_BF16 = 0, 1
 RA_OP_DECODE, RA_OP_PREFILL = 0, 1
 EXPORTED = ("span_summary_update", "route_scores", "topk_spans", "routed_attn_decode", "routed_attn_prefill",
             "attn_dense_causal", "kv_quantize_fp8", "span_summary_update_fp8", "routed_attn_decode_fp8",
+            "routed_attn_decode_append", "routed_attn_decode_fp8_append",
             "kv_signature_update", "ra_cold_workspace_bytes", "cold_select", "cold_attn_decode",
             "kv_snapshot_bytes", "kv_snapshot_pack", "kv_snapshot_parse", "kv_snapshot_verify", "kv_snapshot_unpack",
             "kv_snapshot_write_file", "kv_snapshot_read_file", "ra_workspace_bytes", "ra_status_string",
@@ -78,6 +79,8 @@ def lib():
             "kv_quantize_fp8": [CP, P, P, P, P, P, I64, P],
             "span_summary_update_fp8": [CP, P, P, P, P, P, P, I64, P],
             "routed_attn_decode_fp8": [CP, RP, P, P, P, P, P, P, P, SZ, P],
+            "routed_attn_decode_append": [CP, RP, P, P, P, P, P, SZ, P, P, P, P, I64, P],
+            "routed_attn_decode_fp8_append": [CP, RP, P, P, P, P, P, P, P, SZ, P, P, P, P, I64, P],
             "kv_signature_update": [CP, P, P, P, P, I64, P],
             "cold_select": [CP, RP, P, I32, I32, P, P, SZ, P],
             "cold_attn_decode": [CP, RP, P, P, P, I32, I32, P, P],
@@ -292,6 +295,26 @@ def _args_attn_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, wo
             _dev(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream)), (c, r)
 
 
+# Decode with the step's summary append (the token's update rides in the merge launch).
+def _append_tail(cfg, span_mean, run_sum, old_len, new_len, max_new_tokens):
+    return (_dev(span_mean, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.max_spans, cfg.head_dim), "span_mean"),
+            _dev(run_sum, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.head_dim), "run_sum"),
+            _dev(old_len, torch.int64, (cfg.batch,), "old_len"), _dev(new_len, torch.int64, (cfg.batch,), "new_len"),
+            int(max_new_tokens))
+
+
+def _args_attn_append(cfg, rows, k_cache, v_cache, sel, out, workspace, span_mean, run_sum, old_len, new_len,
+                      max_new_tokens, stream=None):
+    head, keep = _args_attn(cfg, rows, k_cache, v_cache, sel, out, workspace, stream)
+    return head[:-1] + _append_tail(cfg, span_mean, run_sum, old_len, new_len, max_new_tokens) + head[-1:], keep
+
+
+def _args_attn_fp8_append(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, workspace, span_mean, run_sum,
+                          old_len, new_len, max_new_tokens, stream=None):
+    head, keep = _args_attn_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, workspace, stream)
+    return head[:-1] + _append_tail(cfg, span_mean, run_sum, old_len, new_len, max_new_tokens) + head[-1:], keep
+
+
 # Cold retrieval: signatures [B][Hkv][cap][d/8] uint8, sel_cold [n][Hq][top_k_cold] int32.
 def _sig_shape(cfg):
     return (cfg.batch, cfg.num_kv_heads, cfg.capacity, cfg.head_dim // 8)
@@ -332,6 +355,8 @@ _BUILDERS = {
     "kv_quantize_fp8": _args_kv_quantize_fp8,
     "span_summary_update_fp8": _args_span_summary_update_fp8,
     "routed_attn_decode_fp8": _args_attn_fp8,
+    "routed_attn_decode_append": _args_attn_append,
+    "routed_attn_decode_fp8_append": _args_attn_fp8_append,
     "kv_signature_update": _args_kv_signature_update,
     "cold_select": _args_cold_select,
     "cold_attn_decode": _args_cold_attn_decode,
@@ -427,6 +452,23 @@ def routed_attn_decode_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel,
     """routed_attn_decode over an 8-bit K/V cache (bf16 queries)."""
     args, _keep = _args_attn_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, workspace, stream)
     _check(lib().routed_attn_decode_fp8(*args))
+
+
+def routed_attn_decode_append(cfg, rows, k_cache, v_cache, sel, out, workspace, span_mean, run_sum, old_len, new_len,
+                              max_new_tokens, stream=None):
+    """routed_attn_decode, then span_summary_update of tokens [old_len[b], new_len[b]) (one launch
+    less when a single token per sequence is appended)."""
+    args, _keep = _args_attn_append(cfg, rows, k_cache, v_cache, sel, out, workspace, span_mean, run_sum, old_len,
+                                    new_len, max_new_tokens, stream)
+    _check(lib().routed_attn_decode_append(*args))
+
+
+def routed_attn_decode_fp8_append(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, workspace, span_mean,
+                                  run_sum, old_len, new_len, max_new_tokens, stream=None):
+    """routed_attn_decode_fp8, then span_summary_update_fp8 of tokens [old_len[b], new_len[b])."""
+    args, _keep = _args_attn_fp8_append(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, workspace,
+                                        span_mean, run_sum, old_len, new_len, max_new_tokens, stream)
+    _check(lib().routed_attn_decode_fp8_append(*args))
 
 
 def kv_signature_update(cfg, k_cache, sig, old_len, new_len, max_new_tokens, stream=None):

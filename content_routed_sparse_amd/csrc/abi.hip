@@ -8,6 +8,7 @@
 
 #include "common.h"
 #include "cold_kernels.h"
+#include "decode_append.h"
 #include "kernels.h"
 #include "snapshot_kernels.h"
 
@@ -685,6 +686,75 @@ ra_status kv_snapshot_read_file(const char *path, void *buf, size_t capacity, si
     fclose(f);
     if (n != (size_t)size) return fail(RA_EIO, "short read from %s", path);
     return ok();
+}
+
+// ---------------------------------------------------- decode with the step's summary append
+}  // extern "C"
+
+namespace {
+
+// Validates the summary-update half of the *_append entry points and fills its arguments.
+ra_status append_args(const ra_config *cfg, const void *k, const float *kscale, float *span_mean, float *run_sum,
+                      const int64_t *old_len, const int64_t *new_len, int64_t max_new, int dtype,
+                      ra::SummaryArgs *a) {
+    if (!k || !span_mean || !run_sum || !old_len || !new_len) return fail(RA_EINVAL, "NULL summary argument");
+    if (max_new < 0) return fail(RA_EINVAL, "max_new_tokens must be >= 0");
+    if (max_new > cfg->capacity) return fail(RA_ECAPACITY, "max_new_tokens exceeds capacity");
+    const int64_t U = (max_new - 1 + cfg->span_size - 1) / cfg->span_size + 1;
+    if ((int64_t)cfg->batch * cfg->num_kv_heads * U >= kMaxGrid) return fail(RA_EUNSUPPORTED, "grid too large");
+    a->k = k;
+    a->kscale = kscale;
+    a->mean = span_mean;
+    a->run_sum = run_sum;
+    a->old_len = old_len;
+    a->new_len = new_len;
+    a->dtype = dtype;
+    a->d = cfg->head_dim;
+    a->B = cfg->batch;
+    a->Hkv = cfg->num_kv_heads;
+    a->S = cfg->span_size;
+    a->cap = cfg->capacity;
+    a->max_spans = cfg->max_spans;
+    a->max_new = max_new;
+    return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status routed_attn_decode_append(const ra_config *cfg, const ra_rows *rows, const void *k_cache,
+                                    const void *v_cache, const int32_t *sel, float *out, void *workspace,
+                                    size_t workspace_bytes, float *span_mean, float *run_sum, const int64_t *old_len,
+                                    const int64_t *new_len, int64_t max_new_tokens, void *stream) {
+    ra_status s = check_attn(cfg, rows, k_cache, v_cache, sel, out, workspace, workspace_bytes, RA_OP_DECODE);
+    if (s) return s;
+    ra::SummaryArgs app;
+    if ((s = append_args(cfg, k_cache, nullptr, span_mean, run_sum, old_len, new_len, max_new_tokens, cfg->dtype,
+                         &app)))
+        return s;
+    return hip_status(ra::launch_decode_app(row_args(cfg, rows), k_cache, v_cache, sel, out, workspace,
+                                            max_new_tokens > 0 ? &app : nullptr, (hipStream_t)stream),
+                      "routed_attn_decode_append launch");
+}
+
+ra_status routed_attn_decode_fp8_append(const ra_config *cfg, const ra_rows *rows, const uint8_t *k_codes,
+                                        const uint8_t *v_codes, const float *k_scales, const float *v_scales,
+                                        const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
+                                        float *span_mean, float *run_sum, const int64_t *old_len,
+                                        const int64_t *new_len, int64_t max_new_tokens, void *stream) {
+    ra_status s = check_attn(cfg, rows, k_codes, v_codes, sel, out, workspace, workspace_bytes, RA_OP_DECODE);
+    if (s) return s;
+    if (cfg->dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "8-bit caches go with bf16 queries (cfg->dtype RA_BF16)");
+    if (rows->n_rows > 0 && (!k_scales || !v_scales)) return fail(RA_EINVAL, "NULL k_scales or v_scales");
+    ra::SummaryArgs app;
+    if ((s = append_args(cfg, k_codes, k_scales, span_mean, run_sum, old_len, new_len, max_new_tokens, ra::kCacheFp8,
+                         &app)))
+        return s;
+    if (!k_scales) return fail(RA_EINVAL, "NULL k_scales");
+    return hip_status(ra::launch_decode_fp8_app(row_args(cfg, rows), k_codes, v_codes, k_scales, v_scales, sel, out,
+                                                workspace, max_new_tokens > 0 ? &app : nullptr, (hipStream_t)stream),
+                      "routed_attn_decode_fp8_append launch");
 }
 
 size_t ra_workspace_bytes(const ra_config *cfg, int32_t op, int64_t n_rows, int64_t max_pos) {

@@ -22,7 +22,9 @@
 // call (units without keys mark theirs empty), so the combine kernel merges each row-head's
 // records in a fixed order without looking at the selection.
 #include "common.h"
+#include "decode_append.h"
 #include "kernels.h"
+#include "summary_body.h"
 #include "wave_ops.h"
 
 #include <type_traits>
@@ -452,14 +454,11 @@ constexpr int kRecBatch = 8;
 constexpr int kCombineWaves = 16;
 
 template <int D>
-__global__ void __launch_bounds__(kCombineWaves * 64) combine_block(const float *__restrict__ part,
-                                                                   float *__restrict__ out, int nrec) {
+__device__ __forceinline__ void combine_rowhead(const float *__restrict__ part, float *__restrict__ out, int nrec,
+                                                int64_t rh, float *wm, float *wl, float (*wo)[D]) {
     constexpr int PER = D / 64;
     constexpr int B = 8;  // records per batch
-    __shared__ float wm[kCombineWaves], wl[kCombineWaves], wo[kCombineWaves][D];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t rh = blockIdx.x;
-    asm volatile("" ::"s"(part), "s"(out), "s"(nrec));  // all kernel arguments in one round trip
     const float *base = part + rh * (int64_t)nrec * record_floats(D);
     float M = kNegInf, l = 0.f, o[PER];
 #pragma unroll
@@ -530,6 +529,37 @@ __global__ void __launch_bounds__(kCombineWaves * 64) combine_block(const float 
             }
         }
         out[rh * D + tid] = Lt > 0.f ? Ot / Lt : 0.f;
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kCombineWaves * 64) combine_block(const float *__restrict__ part,
+                                                                   float *__restrict__ out, int nrec) {
+    __shared__ float wm[kCombineWaves], wl[kCombineWaves], wo[kCombineWaves][D];
+    asm volatile("" ::"s"(part), "s"(out), "s"(nrec));  // all kernel arguments in one round trip
+    combine_rowhead<D>(part, out, nrec, blockIdx.x, wm, wl, wo);
+}
+
+// The merge with a span-summary append in the same launch: blocks below n_rh merge row-heads,
+// the B * Hkv blocks after them add one new token per sequence to the summaries (the update
+// reads K and writes span_mean / run_sum, none of which the attention reads).
+template <int D, typename T>
+__global__ void __launch_bounds__(kCombineWaves * 64) combine_append(const float *__restrict__ part,
+                                                                    float *__restrict__ out, int nrec, int64_t n_rh,
+                                                                    const T *__restrict__ K,
+                                                                    const float *__restrict__ kscale,
+                                                                    float *__restrict__ mean,
+                                                                    float *__restrict__ run_sum,
+                                                                    const int64_t *__restrict__ old_len,
+                                                                    const int64_t *__restrict__ new_len, int Hkv,
+                                                                    int S, int64_t cap, int64_t max_spans) {
+    __shared__ float wm[kCombineWaves], wl[kCombineWaves], wo[kCombineWaves][D];
+    __shared__ float stage[kStageTokens][D];
+    if ((int64_t)blockIdx.x < n_rh) {
+        combine_rowhead<D>(part, out, nrec, blockIdx.x, wm, wl, wo);
+    } else {
+        summary_unit<T, D>(K, kscale, mean, run_sum, old_len, new_len, Hkv, S, cap, max_spans, 0, 1,
+                           (int)(blockIdx.x - n_rh), stage);
     }
 }
 
@@ -624,7 +654,7 @@ int decode_sub_tile(const RowArgs &a) { return kDecodeWaves * decode_keys_per_wa
 
 template <typename T, int D, int KPW, int NWAVE = kDecodeWaves>
 hipError_t decode_launch_t(const RowArgs &a, const void *K, const void *V, const float *ks, const float *vs,
-                           const int32_t *sel, float *out, void *ws, hipStream_t st) {
+                           const int32_t *sel, float *out, void *ws, const SummaryArgs *app, hipStream_t st) {
     using L = Lanes<T, D, NWAVE, KPW>;
     const int NW = max_window_spans(a.S, a.W);
     const int n_slots = a.G * a.k + NW;
@@ -638,9 +668,19 @@ hipError_t decode_launch_t(const RowArgs &a, const void *K, const void *V, const
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nrec = (a.k + NW) * nsub;
-    hipLaunchKernelGGL((combine_block<D>), dim3((unsigned)(a.n_rows * a.Hq)), dim3(kCombineWaves * 64), 0, st, part,
-                       out, nrec);
-    return hipGetLastError();
+    const int64_t n_rh = a.n_rows * a.Hq;
+    if (app != nullptr && app->max_new == 1) {
+        // one new token per sequence: its summary update rides in the merge launch
+        hipLaunchKernelGGL((combine_append<D, T>), dim3((unsigned)(n_rh + (int64_t)app->B * app->Hkv)),
+                           dim3(kCombineWaves * 64), 0, st, part, out, nrec, n_rh, (const T *)app->k, app->kscale,
+                           app->mean, app->run_sum, app->old_len, app->new_len, app->Hkv, app->S, app->cap,
+                           app->max_spans);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((combine_block<D>), dim3((unsigned)n_rh), dim3(kCombineWaves * 64), 0, st, part, out, nrec);
+    e = hipGetLastError();
+    if (e != hipSuccess || app == nullptr || app->max_new <= 0) return e;
+    return launch_summary(*app, st);
 }
 
 }  // namespace
@@ -651,14 +691,14 @@ size_t decode_workspace_bytes(const RowArgs &a) {
     return (size_t)(a.n_rows * a.Hq * (a.k + NW) * nsub * record_floats(a.d) * sizeof(float));
 }
 
-hipError_t launch_decode(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out, void *ws,
-                         hipStream_t st) {
-    if (a.n_rows == 0) return hipSuccess;
+hipError_t launch_decode_app(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out, void *ws,
+                             const SummaryArgs *app, hipStream_t st) {
+    if (a.n_rows == 0) return app != nullptr && app->max_new > 0 ? launch_summary(*app, st) : hipSuccess;
     if (a.dtype == RA_BF16)
-        return a.d == 64 ? decode_launch_t<uint16_t, 64, 64>(a, K, V, nullptr, nullptr, sel, out, ws, st)
-                         : decode_launch_t<uint16_t, 128, 64>(a, K, V, nullptr, nullptr, sel, out, ws, st);
-    return a.d == 64 ? decode_launch_t<float, 64, 64>(a, K, V, nullptr, nullptr, sel, out, ws, st)
-                     : decode_launch_t<float, 128, 32>(a, K, V, nullptr, nullptr, sel, out, ws, st);
+        return a.d == 64 ? decode_launch_t<uint16_t, 64, 64>(a, K, V, nullptr, nullptr, sel, out, ws, app, st)
+                         : decode_launch_t<uint16_t, 128, 64>(a, K, V, nullptr, nullptr, sel, out, ws, app, st);
+    return a.d == 64 ? decode_launch_t<float, 64, 64>(a, K, V, nullptr, nullptr, sel, out, ws, app, st)
+                     : decode_launch_t<float, 128, 32>(a, K, V, nullptr, nullptr, sel, out, ws, app, st);
 }
 
 // 8-bit cache: 64 keys per wave (a lane's reduce-scatter then ends on one key) and
@@ -668,11 +708,22 @@ hipError_t launch_decode(const RowArgs &a, const void *K, const void *V, const i
 constexpr int kDecodeWavesFp8 = 4;
 static_assert(kDecodeWavesFp8 >= kDecodeWaves, "decode_workspace_bytes sizes records for the bf16 sub-tiles");
 
+hipError_t launch_decode_fp8_app(const RowArgs &a, const uint8_t *K8, const uint8_t *V8, const float *ks,
+                                 const float *vs, const int32_t *sel, float *out, void *ws, const SummaryArgs *app,
+                                 hipStream_t st) {
+    if (a.n_rows == 0) return app != nullptr && app->max_new > 0 ? launch_summary(*app, st) : hipSuccess;
+    return a.d == 64 ? decode_launch_t<uint8_t, 64, 64, kDecodeWavesFp8>(a, K8, V8, ks, vs, sel, out, ws, app, st)
+                     : decode_launch_t<uint8_t, 128, 64, kDecodeWavesFp8>(a, K8, V8, ks, vs, sel, out, ws, app, st);
+}
+
+hipError_t launch_decode(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out, void *ws,
+                         hipStream_t st) {
+    return launch_decode_app(a, K, V, sel, out, ws, nullptr, st);
+}
+
 hipError_t launch_decode_fp8(const RowArgs &a, const uint8_t *K8, const uint8_t *V8, const float *ks,
                              const float *vs, const int32_t *sel, float *out, void *ws, hipStream_t st) {
-    if (a.n_rows == 0) return hipSuccess;
-    return a.d == 64 ? decode_launch_t<uint8_t, 64, 64, kDecodeWavesFp8>(a, K8, V8, ks, vs, sel, out, ws, st)
-                     : decode_launch_t<uint8_t, 128, 64, kDecodeWavesFp8>(a, K8, V8, ks, vs, sel, out, ws, st);
+    return launch_decode_fp8_app(a, K8, V8, ks, vs, sel, out, ws, nullptr, st);
 }
 
 }  // namespace ra

@@ -197,6 +197,26 @@ ra_status routed_attn_decode_fp8(const ra_config *cfg, const ra_rows *rows, cons
                                  const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* routed_attn_decode_append / routed_attn_decode_fp8_append -- the decode call together with
+ * the step's summary update: the same as routed_attn_decode (resp. _fp8) followed by
+ * span_summary_update (resp. _fp8) of tokens [old_len[b], new_len[b]) into span_mean / run_sum.
+ * The update reads only K and writes only the summaries, which the attention does not read, so
+ * with one new token per sequence (max_new_tokens = 1) it runs inside the attention's merge
+ * launch (one launch less per decode step); otherwise it runs as its own launches after the
+ * merge.  A decode step can call route_scores and topk_spans first and this last: the span that
+ * the token at position t completes is never routable at t (it lies in the window), and the
+ * running sum is not read by routing, so routing before the update selects what it would
+ * select after it. */
+ra_status routed_attn_decode_append(const ra_config *cfg, const ra_rows *rows, const void *k_cache,
+                                    const void *v_cache, const int32_t *sel, float *out, void *workspace,
+                                    size_t workspace_bytes, float *span_mean, float *run_sum, const int64_t *old_len,
+                                    const int64_t *new_len, int64_t max_new_tokens, void *stream);
+ra_status routed_attn_decode_fp8_append(const ra_config *cfg, const ra_rows *rows, const uint8_t *k_codes,
+                                        const uint8_t *v_codes, const float *k_scales, const float *v_scales,
+                                        const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
+                                        float *span_mean, float *run_sum, const int64_t *old_len,
+                                        const int64_t *new_len, int64_t max_new_tokens, void *stream);
+
 /* ------------------------------------------------------- token-level cold retrieval
  * A second way to reach old context (InfiniteKV post): the last H positions (the hot window)
  * are attended exactly; every older ("cold") position is found by a Hamming scan over compact
