@@ -12,8 +12,9 @@ i works on sequence i mod caches; each step is the same single-sequence workload
 
 Further objects in the same line (each with its own roofline): the 8-bit cache decode step, the
 token-level cold retrieval step, a session snapshot of one 1M-token state, the chunked prefill
-(8192 tokens on 1M) with dense causal attention beside it, the CPU oracle's rate, and the decode
-steps of the 10M-token and ragged 16-sequence workloads.
+(8192 tokens on 1M) with dense causal attention beside it and the routed-vs-dense ladder (the same
+chunk after 128K, 256K, 512K and 1M tokens), the CPU oracle's rate, and the decode steps of the
+10M-token and ragged 16-sequence workloads.
 
 Prints one JSON line.  `--gpus` above 1 is refused: this path runs on one GPU.
 """
@@ -46,6 +47,8 @@ def parse():
     p.add_argument("--prefill-steps", type=int, default=5)
     p.add_argument("--dense-steps", type=int, default=2,
                    help="timed calls of dense causal attention on the prefill rows (0: skip)")
+    p.add_argument("--no-ladder", action="store_true",
+                   help="skip the routed-vs-dense ladder (the same chunk after 128K, 256K and 512K tokens)")
     p.add_argument("--no-fp8", action="store_true", help="skip the decode step over the 8-bit cache")
     p.add_argument("--no-snapshot", action="store_true", help="skip the session snapshot / restore measurement")
     p.add_argument("--no-cold", action="store_true", help="skip the token-level cold retrieval decode step")
@@ -89,7 +92,7 @@ def main():
     gen_s = time.time() - t0
 
     # ---- per-sequence state and buffers (allocated once)
-    stride = cfg1.num_routable(L - 1)
+    stride = ra.score_stride(cfg1, L - 1)
     st = []
     for s in range(NC):
         d = {
@@ -254,7 +257,7 @@ def main():
     if not args.no_prefill:
         del K, V, st
         torch.cuda.empty_cache()
-        result["prefill"] = bench_prefill(args.prefill_steps, args.dense_steps)
+        result["prefill"] = bench_prefill(args.prefill_steps, args.dense_steps, not args.no_ladder)
 
     if not args.no_extra:
         if args.no_prefill:
@@ -279,7 +282,7 @@ def counter_traffic(tag):
     return rec.get("bytes_per_launch") if rec.get("source_sha256") == h.hexdigest() else None
 
 
-def bench_prefill(steps, dense_steps=2):
+def bench_prefill(steps, dense_steps=2, ladder=True):
     """Chunked prefill: 8192 new tokens appended to a 1M-token cache (the chunk's K/V are in
     the cache before timing).  A step = span_summary_update of the chunk + route_scores +
     topk_spans + routed_attn_prefill for its 8192 x 32 row-heads."""
@@ -302,7 +305,7 @@ def bench_prefill(steps, dense_steps=2):
     run = torch.zeros(1, w.num_kv_heads, w.head_dim, dtype=torch.float32, device=dev)
     t_p, t_l = torch.tensor([P], device=dev), torch.tensor([L], device=dev)
     ra.span_summary_update(cfg, K, mean, run, torch.zeros(1, dtype=torch.int64, device=dev), t_p, P)  # setup
-    scores = torch.empty(n, w.num_q_heads, cfg.num_routable(L - 1), dtype=torch.float32, device=dev)
+    scores = torch.empty(n, w.num_q_heads, ra.score_stride(cfg, L - 1), dtype=torch.float32, device=dev)
     sel = torch.empty(n, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev)
     out = torch.empty(n, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
     ws = torch.empty(ra.workspace_bytes(cfg, ra.RA_OP_PREFILL, n, L - 1), dtype=torch.uint8, device=dev)
@@ -363,6 +366,13 @@ def bench_prefill(steps, dense_steps=2):
                  "achieved_tflops": round(dtf, 1), "mfma_frac": round(dtf / 2500.0, 4),
                  "traffic": counter_traffic("attn_dense_causal_8k_on_1m"),
                  "routed_attn_speedup": round(dense_ms / attn_ms, 2)}
+
+    # the routed-vs-dense ladder: the same 8192-row chunk after shorter prefixes of the same cache
+    rungs = []
+    if ladder and dense_steps > 0:
+        rungs = prefill_ladder(w, cfg, K, V, q, mean, ws, dense_steps,
+                               {"prefix": P, "routed_path_ms": None, "routed_attn_ms": round(attn_ms, 4),
+                                "dense_ms": dense["ms_per_call"] if dense else None})
     return {
         "workload": "prefill_8k_on_1m", "chunk": n, "context": L, "steps": steps,
         "value": round(n / (step_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(step_ms, 4),
@@ -373,7 +383,60 @@ def bench_prefill(steps, dense_steps=2):
         "step_flops": attn_flops + route_flops,
         "step_tflops": round((attn_flops + route_flops) / (step_ms * 1e-3) / 1e12, 1),
         "dense_causal": dense,
+        "ladder": rungs,
     }
+
+
+def time_calls(calls, reps):
+    """Mean ms of one pass over `calls` (HIP events on the current stream around each pass)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for c in calls:
+        c()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        for c in calls:
+            c()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def prefill_ladder(w, cfg, K, V, q, mean, ws, dense_steps, top):
+    """Routed against dense attention for the chunk of 8192 rows placed after prefixes of 128K,
+    256K, 512K and 1M tokens (the last rung is the prefill leg's own chunk; its routed path is timed
+    here like the others).  Every span the rows can route to lies in the cache's first 1M tokens,
+    which the prefill leg has summarised, so the summaries need no update.  Reported per rung: the
+    routed attention call, the routed path (route_scores + topk_spans + routed_attn_prefill) and
+    attn_dense_causal, and the dense time over each."""
+    import torch
+
+    import content_routed_sparse_amd as ra
+
+    n = w.chunk_len
+    dev = q.device
+    out = []
+    for P in (131072, 262144, 524288, w.prefix_len):
+        L = P + n
+        rows = ra.Rows(q, torch.zeros(n, dtype=torch.int32, device=dev),
+                       torch.arange(P, L, dtype=torch.int64, device=dev), L - 1)
+        scores = torch.empty(n, w.num_q_heads, ra.score_stride(cfg, L - 1), dtype=torch.float32, device=dev)
+        sel = torch.empty(n, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev)
+        o = torch.empty(n, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+        front = [ra.prepare("route_scores", cfg, rows, mean, scores), ra.prepare("topk_spans", cfg, rows, scores, sel)]
+        attn = ra.prepare("routed_attn_prefill", cfg, rows, K, V, sel, o, ws)
+        path_ms = time_calls(front + [attn], 3)
+        attn_ms = time_calls([attn], 3)
+        if P == w.prefix_len and top["dense_ms"] is not None:
+            dense_ms = top["dense_ms"]
+        else:
+            dense_ms = time_calls([ra.prepare("attn_dense_causal", cfg, rows, K, V, o)], dense_steps)
+        out.append({"prefix": P, "context": L, "routed_path_ms": round(path_ms, 3), "routed_attn_ms": round(attn_ms, 3),
+                    "dense_ms": round(dense_ms, 3), "dense_over_routed_path": round(dense_ms / path_ms, 2),
+                    "dense_over_routed_attn": round(dense_ms / attn_ms, 2)})
+    return out
 
 
 def bench_decode_fp8(args, w, K, V, qs):
@@ -393,7 +456,7 @@ def bench_decode_fp8(args, w, K, V, qs):
     zero = torch.zeros(1, dtype=torch.int64, device=dev)
     full = torch.full((1,), L, dtype=torch.int64, device=dev)
     before = torch.full((1,), L - 1, dtype=torch.int64, device=dev)
-    stride = cfg1.num_routable(L - 1)
+    stride = ra.score_stride(cfg1, L - 1)
     ws = torch.empty(ra.workspace_bytes(cfg1, ra.RA_OP_DECODE, 1, L - 1), dtype=torch.uint8, device=dev)
     st = []
     for s in range(NC):
@@ -663,7 +726,7 @@ def bench_decode_workload(name, steps, warmup):
     zero = torch.zeros(B, dtype=torch.int64, device=dev)
     before, after = torch.as_tensor(lengths - 1).to(dev), torch.as_tensor(lengths).to(dev)
     ra.span_summary_update(cfg, K, mean, run, zero, before, int(lengths.max() - 1))  # setup, untimed
-    scores = torch.empty(B, w.num_q_heads, max(1, cfg.num_routable(cap - 1)), dtype=torch.float32, device=dev)
+    scores = torch.empty(B, w.num_q_heads, ra.score_stride(cfg, cap - 1), dtype=torch.float32, device=dev)
     sel = torch.empty(B, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev)
     out = torch.empty(B, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
     ws = torch.empty(ra.workspace_bytes(cfg, ra.RA_OP_DECODE, B, cap - 1), dtype=torch.uint8, device=dev)

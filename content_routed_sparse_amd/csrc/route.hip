@@ -3,9 +3,12 @@
 //
 // Two kernels:
 //  * route_mfma (bf16 inputs, many rows): a dense [row-heads x spans] contraction on bf16 MFMA
-//    (v_mfma_f32_16x16x32_bf16), fp32 accumulation.  A block owns 64 row-heads of one kv head
-//    (4 waves x 16) and a chunk of spans; span summaries are rounded to bf16 once per block and
-//    staged in LDS, shared by the 4 waves.  Rows of different sequences in one tile are handled
+//    (v_mfma_f32_16x16x32_bf16), fp32 accumulation.  A block owns 128 row-heads of one kv head
+//    (4 waves x 2 groups of 16) and a range of spans; span summaries are rounded to bf16 once per
+//    block and staged in LDS, shared by the 4 waves and the 2 groups of each.  The kernel is
+//    bound by its score stores (1.08 GB for an 8192-row chunk on 1M tokens): 16-byte stores,
+//    which run fastest when score rows start on 64-byte boundaries (a score stride that is a
+//    multiple of 16 floats).  Rows of different sequences in one tile are handled
 //    in successive passes (one pass in the usual single-sequence chunk).
 //  * route_valu (fp32 inputs, or few rows as in decode): fp32 FMA; lanes split each summary
 //    row, 8 query heads per pass, butterfly reduction over the lanes of a row.
@@ -126,87 +129,84 @@ __global__ void __launch_bounds__(256) route_valu(const T *__restrict__ q, const
     }
 }
 
-constexpr int kRowTile = 64;    // row-heads per block (4 waves x 16)
-constexpr int kSpanBlock = 64;  // spans staged per LDS step
-constexpr int kSpanChunk = 256; // spans per block (grid y)
+constexpr int kRouteGroups = 2;                // 16-row MFMA groups per wave (measured: 2 beats 1, 4 and 8)
+constexpr int kRowTile = 64 * kRouteGroups;     // row-heads per block (4 waves)
+constexpr int kSpanBlock = 64;                  // spans staged per LDS step
+constexpr int kRouteBlocks = 1024;              // blocks wanted before a tile's spans are split
 
-template <int D>
+// A block owns kRowTile row-heads of one kv head and the spans [jc0, jc0 + span_chunk).  Each
+// LDS step stages kappa(mean) of 64 spans as bf16 (double-buffered: the next step's summaries
+// are loaded into registers while the current step's products run, one barrier per step); every
+// staged span fragment feeds the MFMAs of all RG row groups of the wave.  The product is formed
+// as spans x row-heads, so a lane ends with 4 consecutive spans of one row-head and stores them
+// with one 16-byte store.  Each score is one chain of D/32 MFMAs over the same operands whatever
+// the tiling, so the values do not depend on it.
+template <int D, int RG>
 __global__ void __launch_bounds__(256) route_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq,
                                                   const int64_t *__restrict__ row_pos,
                                                   const float *__restrict__ mean, float *__restrict__ scores,
                                                   int64_t stride, int64_t n_rows, int Hq, int Hkv, int G, int S,
                                                   int W, int B, int64_t max_spans, int64_t max_pos,
-                                                  int64_t tiles_per_head) {
+                                                  int64_t tiles_per_head, int64_t span_chunk) {
     constexpr int KS = D / 32;          // k-steps of 32
     constexpr int LDS_ROW = D + 8;      // bf16 elements per staged span row (padding vs bank conflicts)
-    __shared__ uint16_t bstage[kSpanBlock * LDS_ROW];
-    __shared__ int tile_seq[kRowTile];
+    constexpr int TILE = 64 * RG;
+    constexpr int PER = kSpanBlock * (D / 4) / 256;  // float4 summary loads per thread per step
+    typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));  // score rows need not be 16-byte aligned
+    __shared__ uint16_t bstage[2][kSpanBlock * LDS_ROW];
+    __shared__ int tile_seq[TILE];
     __shared__ int pass_seq;
+    __shared__ int64_t rmax_w[4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = (int)(blockIdx.x / tiles_per_head);
-    const int64_t rh0 = (blockIdx.x % tiles_per_head) * kRowTile;
-    const int64_t jc0 = (int64_t)blockIdx.y * kSpanChunk;
+    const int64_t rh0 = (blockIdx.x % tiles_per_head) * TILE;
+    const int64_t jc0 = (int64_t)blockIdx.y * span_chunk;
     const int64_t n_rh = n_rows * G;
 
     // sequence of each row-head of the tile (-1 when past the last row)
-    if (tid < kRowTile) {
-        const int64_t rh = rh0 + tid;
+    for (int x = tid; x < TILE; x += 256) {
+        const int64_t rh = rh0 + x;
         int s = -1;
         if (rh < n_rh) {
             s = row_seq[rh / G];
             s = s < 0 ? 0 : (s >= B ? B - 1 : s);
         }
-        tile_seq[tid] = s;
+        tile_seq[x] = s;
     }
-    // this lane's A row (row-head) and its routable count
-    const int64_t my_rh = rh0 + wave * 16 + (lane & 15);
-    const bool rh_ok = my_rh < n_rh;
-    const int64_t my_row = rh_ok ? my_rh / G : 0;
-    const int my_h = rh_ok ? (int)(my_rh % G) : 0;
-    bf16x8 a[KS];
-    {
-        const uint16_t *qp = q + (my_row * Hq + g * G + my_h) * D + 8 * (lane >> 4);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint4 raw = rh_ok ? *reinterpret_cast<const uint4 *>(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
-            a[ks] = __builtin_bit_cast(bf16x8, raw);
-        }
-    }
-    // rows of the 4 outputs this lane holds: D[4*(lane/16)+i][lane%16]
-    int64_t out_row[4], out_r[4];
-    int out_h[4], out_seq[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t rh = rh0 + wave * 16 + 4 * (lane >> 4) + i;
-        out_row[i] = rh < n_rh ? rh / G : -1;
-        out_h[i] = rh < n_rh ? (int)(rh % G) : 0;
-        int64_t t = 0;
-        if (out_row[i] >= 0) {
-            t = row_pos[out_row[i]];
-            t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
-        }
-        out_r[i] = out_row[i] >= 0 ? num_routable(t, S, W) : 0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out_seq[i] = out_row[i] >= 0 ? tile_seq[wave * 16 + 4 * (lane >> 4) + i] : -1;
-    const int my_seq = rh_ok ? tile_seq[wave * 16 + (lane & 15)] : -1;
-
-    // largest routable count in the tile bounds the span loop
+    // row group gr of this wave: row-heads rh0 + (wave * RG + gr) * 16 + [0, 16); the lane's
+    // row-head (lane % 16) is both its query fragment's row and its outputs' column.  Per group:
+    // the score row offset and the routable count relative to the block's span range.
+    int64_t out_off[RG];
+    int out_r[RG];
     int64_t rmax = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rmax = out_r[i] > rmax ? out_r[i] : rmax;
+    for (int gr = 0; gr < RG; ++gr) {
+        const int64_t rh = rh0 + (wave * RG + gr) * 16 + (lane & 15);
+        int64_t r = 0;
+        out_off[gr] = 0;
+        if (rh < n_rh) {
+            const int64_t row = rh / G;
+            int64_t t = row_pos[row];
+            t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
+            r = num_routable(t, S, W);
+            out_off[gr] = (row * Hq + g * G + (int)(rh % G)) * stride + jc0;
+        }
+        rmax = r > rmax ? r : rmax;
+        int64_t rel = r - jc0;
+        rel = rel < 0 ? 0 : (rel > span_chunk ? span_chunk : rel);
+        out_r[gr] = (int)rel;
+    }
+    // largest routable count in the tile bounds the span loop
     for (int off = 32; off > 0; off >>= 1) {
         const int64_t o = __shfl_xor(rmax, off);
         rmax = o > rmax ? o : rmax;
     }
-    __shared__ int64_t rmax_w[4];
     if (lane == 0) rmax_w[wave] = rmax;
     __syncthreads();
     rmax = rmax_w[0];
     for (int w = 1; w < 4; ++w) rmax = rmax_w[w] > rmax ? rmax_w[w] : rmax;
-    int64_t jend = jc0 + kSpanChunk;
+    int64_t jend = jc0 + span_chunk;
     if (jend > rmax) jend = rmax;
     if (jc0 >= jend) return;
 
@@ -215,7 +215,7 @@ __global__ void __launch_bounds__(256) route_mfma(const uint16_t *__restrict__ q
         __syncthreads();
         if (tid == 0) {
             int nxt = 0x7fffffff;
-            for (int x = 0; x < kRowTile; ++x)
+            for (int x = 0; x < TILE; ++x)
                 if (tile_seq[x] > done_below && tile_seq[x] < nxt) nxt = tile_seq[x];
             pass_seq = nxt;
         }
@@ -223,41 +223,74 @@ __global__ void __launch_bounds__(256) route_mfma(const uint16_t *__restrict__ q
         const int seq = pass_seq;
         if (seq == 0x7fffffff) break;
         done_below = seq;
-        const bf16x8 zero8 = {};
-        bf16x8 aa[KS];
+        // query fragments of the pass's rows (zero for rows of other sequences or past the end)
+        bf16x8 qf[RG][KS];
+        int lim[RG];  // spans of the pass's rows (0 for rows of other sequences)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) aa[ks] = (my_seq == seq) ? a[ks] : zero8;
-        const float *mseq = mean + ((int64_t)seq * Hkv + g) * max_spans * D;
-        for (int64_t jb = jc0; jb < jend; jb += kSpanBlock) {
-            // stage kappa(mean) of spans [jb, jb+64) as bf16
-            for (int x = tid; x < kSpanBlock * (D / 4); x += 256) {
-                const int n = x / (D / 4), e4 = (x % (D / 4)) * 4;
-                const int64_t j = jb + n;
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (j < jend) v = *reinterpret_cast<const float4 *>(mseq + j * D + e4);
-                const uint32_t lo = f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16);
-                const uint32_t hi = f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16);
-                *reinterpret_cast<uint2 *>(&bstage[n * LDS_ROW + e4]) = make_uint2(lo, hi);
+        for (int gr = 0; gr < RG; ++gr) {
+            const int x = (wave * RG + gr) * 16 + (lane & 15);
+            const bool ok = tile_seq[x] == seq;  // -1 past the last row
+            const int64_t rh = ok ? rh0 + x : 0;
+            const uint16_t *qp = q + ((rh / G) * Hq + g * G + (int)(rh % G)) * D + 8 * (lane >> 4);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const uint4 raw = ok ? *reinterpret_cast<const uint4 *>(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
+                qf[gr][ks] = __builtin_bit_cast(bf16x8, raw);
             }
+            lim[gr] = ok ? out_r[gr] : 0;
+        }
+        const float *mseq = mean + ((int64_t)seq * Hkv + g) * max_spans * D;
+        float4 pre[PER];
+        auto fetch = [&](int64_t jb) {
+#pragma unroll
+            for (int p = 0; p < PER; ++p) {
+                const int x = tid + 256 * p;
+                const int64_t j = jb + x / (D / 4);
+                pre[p] = j < jend ? *reinterpret_cast<const float4 *>(mseq + j * D + (x % (D / 4)) * 4)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        };
+        fetch(jc0);
+        int buf = 0;
+        for (int64_t jb = jc0; jb < jend; jb += kSpanBlock, buf ^= 1) {
+            // stage kappa(mean) of spans [jb, jb+64) as bf16, then start loading the next 64
+#pragma unroll
+            for (int p = 0; p < PER; ++p) {
+                const int x = tid + 256 * p;
+                const uint32_t lo = f32_to_bf16_bits(pre[p].x) | (f32_to_bf16_bits(pre[p].y) << 16);
+                const uint32_t hi = f32_to_bf16_bits(pre[p].z) | (f32_to_bf16_bits(pre[p].w) << 16);
+                *reinterpret_cast<uint2 *>(&bstage[buf][(x / (D / 4)) * LDS_ROW + (x % (D / 4)) * 4]) =
+                    make_uint2(lo, hi);
+            }
+            if (jb + kSpanBlock < jend) fetch(jb + kSpanBlock);
             __syncthreads();
 #pragma unroll
             for (int nb = 0; nb < kSpanBlock / 16; ++nb) {
-                const uint16_t *bp = &bstage[(nb * 16 + (lane & 15)) * LDS_ROW + 8 * (lane >> 4)];
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                const uint16_t *bp = &bstage[buf][(nb * 16 + (lane & 15)) * LDS_ROW + 8 * (lane >> 4)];
+                bf16x8 sf[KS];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const uint4 raw = *reinterpret_cast<const uint4 *>(bp + 32 * ks);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa[ks], __builtin_bit_cast(bf16x8, raw), acc, 0, 0, 0);
-                }
-                const int64_t j = jb + nb * 16 + (lane & 15);
+                for (int ks = 0; ks < KS; ++ks)
+                    sf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(bp + 32 * ks));
+                // this lane's outputs: spans j0 .. j0+3 (relative to jc0) of its row-head
+                const int j0 = (int)(jb - jc0) + nb * 16 + 4 * (lane >> 4);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (out_seq[i] == seq && j < out_r[i] && j < jend)
-                        scores[(out_row[i] * Hq + g * G + out_h[i]) * stride + j] = acc[i];
+                for (int gr = 0; gr < RG; ++gr) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[ks], qf[gr][ks], acc, 0, 0, 0);
+                    float *dst = scores + out_off[gr] + j0;
+                    if (j0 + 3 < lim[gr]) {
+                        *reinterpret_cast<f32x4u *>(dst) = f32x4u{acc[0], acc[1], acc[2], acc[3]};
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (j0 + i < lim[gr]) dst[i] = acc[i];
+                    }
                 }
             }
-            __syncthreads();
         }
+        __syncthreads();
     }
 }
 
@@ -276,9 +309,17 @@ hipError_t route_mfma_launch(const RowArgs &a, const float *mean, float *scores,
     const int64_t rmax = num_routable(a.max_pos, a.S, a.W);
     if (rmax == 0 || a.n_rows == 0) return hipSuccess;
     const int64_t tiles = ceil_div(a.n_rows * a.G, kRowTile);
-    dim3 grid((unsigned)(tiles * a.Hkv), (unsigned)ceil_div(rmax, kSpanChunk));
-    hipLaunchKernelGGL((route_mfma<D>), grid, dim3(256), 0, st, (const uint16_t *)a.q, a.row_seq, a.row_pos, mean,
-                       scores, stride, a.n_rows, a.Hq, a.Hkv, a.G, a.S, a.W, a.B, a.max_spans, a.max_pos, tiles);
+    // split the spans only as far as needed for kRouteBlocks blocks
+    int64_t parts = ceil_div(kRouteBlocks, tiles * a.Hkv);
+    const int64_t max_parts = ceil_div(rmax, kSpanBlock);
+    parts = parts < 1 ? 1 : (parts > max_parts ? max_parts : parts);
+    const int64_t min_parts = ceil_div(rmax, (int64_t)1 << 30);  // span offsets inside a block fit in int
+    parts = parts < min_parts ? min_parts : parts;
+    const int64_t chunk = ceil_div(ceil_div(rmax, parts), kSpanBlock) * kSpanBlock;
+    dim3 grid((unsigned)(tiles * a.Hkv), (unsigned)ceil_div(rmax, chunk));
+    hipLaunchKernelGGL((route_mfma<D, kRouteGroups>), grid, dim3(256), 0, st, (const uint16_t *)a.q, a.row_seq,
+                       a.row_pos, mean, scores, stride, a.n_rows, a.Hq, a.Hkv, a.G, a.S, a.W, a.B, a.max_spans,
+                       a.max_pos, tiles, chunk);
     return hipGetLastError();
 }
 

@@ -515,3 +515,34 @@ def test_decode_step_replays_from_a_hip_graph():
         # eager work between replays
         c.attend(rows, ra.RA_OP_DECODE)
         assert torch.equal(c.pipe.out, eager_out)
+
+
+@pytest.mark.parametrize("d,G,S,W,nseq", [(128, 8, 32, 32, 1), (64, 4, 16, 40, 3), (128, 32, 64, 64, 2)])
+def test_route_and_topk_do_not_depend_on_the_score_stride(d, G, S, W, nseq):
+    """Scores and selections (bf16, enough rows for the MFMA routing kernel, rows of several
+    sequences mixed in its tiles) are bitwise the same for an odd stride, the stride plus one and
+    the 16-float multiple that score_stride gives; entries past a row's r(t) are never written."""
+    rng = np.random.default_rng(d + G + nseq)
+    Hkv = 2 if G < 32 else 1
+    n, cap, k = 300, 5000, 4
+    cfg = ra.Config(G * Hkv, Hkv, d, S, k, W, ra.RA_BF16, nseq, cap)
+    mean = torch.from_numpy(rng.standard_normal((nseq, Hkv, cfg.max_spans, d)).astype(np.float32)).cuda()
+    q = torch.from_numpy(rng.standard_normal((n, G * Hkv, d)).astype(np.float32)).to(torch.bfloat16).cuda()
+    seqs = np.sort(rng.integers(0, nseq, n)).astype(np.int32)
+    pos = rng.integers(0, cap, n)
+    rows = ra.Rows(q, torch.from_numpy(seqs).cuda(), torch.from_numpy(pos).cuda(), int(pos.max()))
+    r_max = cfg.num_routable(int(pos.max()))
+    r = np.array([cfg.num_routable(int(t)) for t in pos])
+    got = []
+    for stride in (r_max, r_max + 1, ra.score_stride(cfg, int(pos.max()))):
+        scores = torch.full((n, G * Hkv, stride), np.nan, dtype=torch.float32, device="cuda")
+        sel = torch.full((n, G * Hkv, k), -7, dtype=torch.int32, device="cuda")
+        ra.route_scores(cfg, rows, mean, scores)
+        ra.topk_spans(cfg, rows, scores, sel)
+        sc = scores.cpu().numpy()
+        for i in range(n):
+            assert not np.isnan(sc[i, :, :r[i]]).any() and np.isnan(sc[i, :, r[i]:]).all()
+        got.append((np.concatenate([sc[i, :, :r[i]].ravel() for i in range(n)]), sel.cpu().numpy()))
+    for sc, sel in got[1:]:
+        assert np.array_equal(sc.view(np.uint32), got[0][0].view(np.uint32))
+        assert np.array_equal(sel, got[0][1])
