@@ -404,49 +404,6 @@ __global__ void __launch_bounds__(NWAVE * 64) decode_attn(const void *__restrict
 
 }
 
-// Records of one row-head: entry e < k is selected span sel[e] (skipped unless 0 <= j < r),
-// entry k + w is window span w0/S + w (skipped once it starts after t); each covers its keys in
-// sub-tiles of TK.  Returns false for records that were not produced.
-__device__ __forceinline__ bool record_valid(const int32_t *sel_rh, int e, int sub, int64_t t, int64_t w0, int S,
-                                             int k, int TK) {
-    int64_t lo, hi;
-    if (e < k) {
-        const int64_t j = sel_rh[e];
-        if (j < 0 || j >= div_nonneg(w0, S)) return false;
-        lo = j * S;
-        hi = lo + S;
-    } else {
-        lo = w0 + (int64_t)(e - k) * S;
-        if (lo > t) return false;
-        hi = lo + S < t + 1 ? lo + S : t + 1;
-    }
-    return lo + (int64_t)sub * TK < hi;
-}
-
-// Loads the output slices of B records (x0, x0 + stride, ...; indices clamped into range) and
-// pins them: every load of the batch is issued before the first use, so a batch costs one
-// memory round trip.  (Left alone, the compiler turns a load whose value is used only under a
-// condition into a conditional load and waits for each one separately.)
-template <int B, int PER, int D>
-__device__ __forceinline__ void load_record_batch(const float *base, int x0, int stride, int nrec, int lane,
-                                                  float (&v)[B][PER]) {
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-        int x = x0 + stride * b;
-        x = x < nrec ? x : nrec - 1;
-        const float *rec = base + (int64_t)x * record_floats(D);
-#pragma unroll
-        for (int i = 0; i < PER; ++i) v[b][i] = rec[4 + lane + 64 * i];
-    }
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-#pragma unroll
-        for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(v[b][i]));
-}
-
-constexpr int kRecBatch = 8;
-
 // Merge for few row-heads with many records: one block of 16 waves per row-head.  Every record
 // slot is written by the decode kernel (empty ones have m = -inf), so each wave loads its records
 // (x = wave, wave + 16, ...) in batches with no dependent round trip, merges them with its own
@@ -563,84 +520,8 @@ __global__ void __launch_bounds__(kCombineWaves * 64) combine_append(const float
     }
 }
 
-// Merge for many row-heads with few records (prefill): one wave per row-head; lane x reads the
-// maximum of record x, then the records are summed in entry order with their weights.
-template <int D>
-__global__ void __launch_bounds__(256) combine_wave(const float *__restrict__ part, const int32_t *__restrict__ sel,
-                                                    const int64_t *__restrict__ row_pos, float *__restrict__ out,
-                                                    int64_t n_rowheads, int Hq, int S, int k, int W, int64_t max_pos,
-                                                    int NW, int nsub, int TK) {
-    constexpr int PER = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (rh >= n_rowheads) return;
-    int64_t t = row_pos[rh / Hq];
-    t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
-    const int64_t w0 = window_start(t, S, W);
-    const int NE = k + NW;
-    const int nrec = NE * nsub;
-    const int32_t *sel_rh = sel + rh * k;
-    const float *base = part + rh * (int64_t)nrec * record_floats(D);
-
-    // lane x holds record x's (m, l) (one round trip for up to 64 records); invalid -> m = -inf
-    float M = kNegInf;
-    float mine_m = kNegInf, mine_l = 0.f;
-    for (int x0 = 0; x0 < nrec; x0 += 64) {
-        const int x = x0 + lane;
-        const int xc = x < nrec ? x : nrec - 1;
-        const float2 ml = *reinterpret_cast<const float2 *>(base + (int64_t)xc * record_floats(D));
-        const bool ok = x < nrec && record_valid(sel_rh, x / nsub, x % nsub, t, w0, S, k, TK);
-        const float m = ok ? ml.x : kNegInf;
-        if (x0 == 0) {
-            mine_m = m;
-            mine_l = ok ? ml.y : 0.f;
-        }
-        M = fmaxf(M, wave_max(m));
-    }
-    float l = 0.f, o[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] = 0.f;
-    for (int x0 = 0; x0 < nrec; x0 += kRecBatch) {
-        float v[kRecBatch][PER];
-        load_record_batch<kRecBatch, PER, D>(base, x0, 1, nrec, lane, v);
-#pragma unroll
-        for (int b = 0; b < kRecBatch; ++b) {
-            const int x = x0 + b;
-            if (x >= nrec) break;
-            float m, lx;
-            if (x < 64) {
-                m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine_m), x));
-                lx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine_l), x));
-            } else {
-                const bool okx = record_valid(sel_rh, x / nsub, x % nsub, t, w0, S, k, TK);
-                const float2 ml = *reinterpret_cast<const float2 *>(base + (int64_t)x * record_floats(D));
-                m = okx ? ml.x : kNegInf;
-                lx = ml.y;
-            }
-            const bool ok = m != kNegInf;
-            const float f = ok ? exp2f(m - M) : 0.f;
-            l = ok ? fmaf(lx, f, l) : l;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) o[i] = ok ? fmaf(v[b][i], f, o[i]) : o[i];
-        }
-    }
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) out[rh * D + lane + 64 * i] = o[i] * inv;
-}
-
 }  // namespace
 
-// Prefill records of invalid entries are never written, so the prefill merge checks validity.
-hipError_t launch_combine(const RowArgs &a, const float *part, const int32_t *sel, float *out, int nsub, int TK,
-                          hipStream_t st) {
-    const int64_t n = a.n_rows * a.Hq;
-    const int NW = max_window_spans(a.S, a.W);
-    auto kern = a.d == 64 ? combine_wave<64> : combine_wave<128>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(n, 4)), dim3(256), 0, st, part, sel, a.row_pos, out, n, a.Hq,
-                       a.S, a.k, a.W, a.max_pos, NW, nsub, TK);
-    return hipGetLastError();
-}
 
 namespace {
 

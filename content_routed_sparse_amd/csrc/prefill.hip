@@ -16,16 +16,13 @@
 //   local[n_ent], list[n_ent]                               int32   (n_ent = n_rowheads * NE)
 //   list_t[n_ent]                                           int64   (position of the entry's row)
 //   tiles[max_tiles]                                        int4    (expert, first entry, entries)
-//   records[n_ent]                                          float x (4 + d)
+//   records[n_ent]                                          prefill_record_words(d, bf16) x 4 bytes
 #include "common.h"
 #include "kernels.h"
 #include "prefill_tiles.h"
+#include "wave_ops.h"
 
 namespace ra {
-
-hipError_t launch_combine(const RowArgs &a, const float *part, const int32_t *sel, float *out, int nsub, int TK,
-                          hipStream_t st);
-
 namespace {
 
 struct PrefillLayout {
@@ -51,7 +48,7 @@ PrefillLayout prefill_layout(const RowArgs &a) {
     L.off_list = o;     o = align256(o + L.n_ent * 4);
     L.off_list_t = o;   o = align256(o + L.n_ent * 8);
     L.off_tiles = o;    o = align256(o + L.max_tiles * 16);
-    L.off_records = o;  o = align256(o + (size_t)L.n_ent * record_floats(a.d) * 4);
+    L.off_records = o;  o = align256(o + (size_t)L.n_ent * prefill_record_words(a.d, a.dtype == RA_BF16) * 4);
     L.total = o;
     return L;
 }
@@ -241,6 +238,140 @@ __global__ void tiles_kernel(const int32_t *__restrict__ counts, const int32_t *
         tiles[base + i] = make_int4((int32_t)x, first + i * MT, c - i * MT < MT ? c - i * MT : MT, 0);
 }
 
+
+// Records of one row-head: entry e < k is the selected span sel[e] (no record unless 0 <= j <
+// r), entry k + w is window span w0/S + w (no record once it starts after t).
+__device__ __forceinline__ bool record_valid(const int32_t *sel_rh, int e, int64_t t, int64_t w0, int S, int k) {
+    if (e < k) {
+        const int64_t j = sel_rh[e];
+        return j >= 0 && j < div_nonneg(w0, S);
+    }
+    return w0 + (int64_t)(e - k) * S <= t;
+}
+
+constexpr int kRecBatch = 8;
+
+// This lane's slice of the output-sized part of a record: the values of elements
+// lane + 64 i (fp32 records), or of elements 2 lane, 2 lane + 1 (fp16 records, d = 128) or
+// lane (fp16 records, d = 64).
+template <int D, bool HALF>
+__device__ __forceinline__ void load_slice(const float *rec, int lane, float (&v)[D / 64]) {
+    if constexpr (!HALF) {
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) v[i] = rec[4 + lane + 64 * i];
+    } else if constexpr (D == 128) {
+        typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+        const half2_t h = __builtin_bit_cast(half2_t, reinterpret_cast<const uint32_t *>(rec + 4)[lane]);
+        v[0] = (float)h.x;
+        v[1] = (float)h.y;
+    } else {
+        v[0] = (float)reinterpret_cast<const _Float16 *>(rec + 4)[lane];
+    }
+}
+
+// Merge: one wave per row-head; lane x reads the header of record x, then the records are summed
+// in entry order with their weights.  Each batch of kRecBatch records is loaded (indices
+// clamped into range) and pinned before its first use: one memory round trip per batch.
+//   fp32 records (m, l, -, -, o[d]):       out = sum 2^(m - M) o / sum 2^(m - M) l
+//   fp16 records (m, l, s, -, h[d]), h = o / (l s):  o = 2^(m - M) l s h in the same sums
+template <int D, bool HALF>
+__global__ void __launch_bounds__(256) combine_wave(const float *__restrict__ part, const int32_t *__restrict__ sel,
+                                                    const int64_t *__restrict__ row_pos, float *__restrict__ out,
+                                                    int64_t n_rowheads, int Hq, int S, int k, int W, int64_t max_pos,
+                                                    int NW) {
+    constexpr int PER = D / 64;
+    constexpr int RW = prefill_record_words(D, HALF);
+    constexpr float kNegInf = -__builtin_huge_valf();
+    const int lane = threadIdx.x & 63;
+    const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (rh >= n_rowheads) return;
+    int64_t t = row_pos[rh / Hq];
+    t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
+    const int64_t w0 = window_start(t, S, W);
+    const int nrec = k + NW;
+    const int32_t *sel_rh = sel + rh * k;
+    const float *base = part + rh * (int64_t)nrec * RW;
+
+    // lane x holds record x's (m, l, s) (one round trip for up to 64 records); invalid: m = -inf
+    float M = kNegInf;
+    float mine_m = kNegInf, mine_l = 0.f, mine_s = 0.f;
+    for (int x0 = 0; x0 < nrec; x0 += 64) {
+        const int x = x0 + lane;
+        const int xc = x < nrec ? x : nrec - 1;
+        const float4 h = *reinterpret_cast<const float4 *>(base + (int64_t)xc * RW);
+        const bool ok = x < nrec && record_valid(sel_rh, x, t, w0, S, k);
+        const float m = ok ? h.x : kNegInf;
+        if (x0 == 0) {
+            mine_m = m;
+            mine_l = ok ? h.y : 0.f;
+            mine_s = ok ? h.z : 0.f;
+        }
+        M = fmaxf(M, wave_max(m));
+    }
+    float l = 0.f, o[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] = 0.f;
+    for (int x0 = 0; x0 < nrec; x0 += kRecBatch) {
+        float v[kRecBatch][PER];
+#pragma unroll
+        for (int b = 0; b < kRecBatch; ++b) {
+            const int x = x0 + b < nrec ? x0 + b : nrec - 1;
+            load_slice<D, HALF>(base + (int64_t)x * RW, lane, v[b]);
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int b = 0; b < kRecBatch; ++b)
+#pragma unroll
+            for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(v[b][i]));
+#pragma unroll
+        for (int b = 0; b < kRecBatch; ++b) {
+            const int x = x0 + b;
+            if (x >= nrec) break;
+            float m, lx, sx;
+            if (x < 64) {
+                m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine_m), x));
+                lx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine_l), x));
+                sx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine_s), x));
+            } else {
+                const float4 h = *reinterpret_cast<const float4 *>(base + (int64_t)x * RW);
+                m = record_valid(sel_rh, x, t, w0, S, k) ? h.x : kNegInf;
+                lx = h.y;
+                sx = h.z;
+            }
+            const bool ok = m != kNegInf;
+            const float f = ok ? exp2f(m - M) : 0.f;
+            l = ok ? fmaf(lx, f, l) : l;
+            const float c = HALF ? f * lx * sx : f;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) o[i] = ok ? fmaf(v[b][i], c, o[i]) : o[i];
+        }
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if constexpr (HALF && D == 128) {
+        *reinterpret_cast<float2 *>(out + rh * D + 2 * lane) = make_float2(o[0] * inv, o[1] * inv);
+    } else {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) out[rh * D + lane + 64 * i] = o[i] * inv;
+    }
+}
+
+template <int D, bool HALF>
+hipError_t launch_combine_t(const RowArgs &a, const float *part, const int32_t *sel, float *out, hipStream_t st) {
+    const int64_t n = a.n_rows * a.Hq;
+    hipLaunchKernelGGL((combine_wave<D, HALF>), dim3((unsigned)ceil_div(n, 4)), dim3(256), 0, st, part, sel,
+                       a.row_pos, out, n, a.Hq, a.S, a.k, a.W, a.max_pos, max_window_spans(a.S, a.W));
+    return hipGetLastError();
+}
+
+// Records of entries that attend to nothing are never written, so the merge checks validity.
+hipError_t launch_combine(const RowArgs &a, const float *part, const int32_t *sel, float *out, hipStream_t st) {
+    if (a.dtype == RA_BF16)
+        return a.d == 64 ? launch_combine_t<64, true>(a, part, sel, out, st)
+                         : launch_combine_t<128, true>(a, part, sel, out, st);
+    return a.d == 64 ? launch_combine_t<64, false>(a, part, sel, out, st)
+                     : launch_combine_t<128, false>(a, part, sel, out, st);
+}
+
 }  // namespace
 
 size_t prefill_workspace_bytes(const RowArgs &a) { return prefill_layout(a).total; }
@@ -285,7 +416,7 @@ hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const 
     TileArgs ta{a, K, V, tile_off, list, list_t, tiles, records, L.n_exp, L.max_tiles, L.span_slots, NE};
     e = launch_prefill_tiles(ta, st);
     if (e != hipSuccess) return e;
-    return launch_combine(a, records, sel, out, 1, a.S, st);
+    return launch_combine(a, records, sel, out, st);
 }
 
 }  // namespace ra

@@ -16,6 +16,11 @@ struct TileArgs {
     int NE;
 };
 
+// 4-byte words of one partial record: a 16-byte header (m, l, s, 0), then the row's output
+// vector: fp32 values o (fp32 inputs), or fp16 values o / (l s) with s a power of two chosen per
+// record (bf16 inputs).
+__host__ __device__ constexpr int prefill_record_words(int d, bool half) { return 4 + (half ? d / 2 : d); }
+
 // Entries per tile for this configuration.
 int prefill_tile_rows(const RowArgs &a);
 hipError_t launch_prefill_tiles(const TileArgs &t, hipStream_t st);

@@ -132,7 +132,7 @@ __global__ void __launch_bounds__(256) tile_valu(const T *__restrict__ q, const 
             for (int e = 0; e < EPL; ++e) o[e] = o[e] * a + co[e];
             m = mn;
         }
-        float *rec = records + x * record_floats(D);
+        float *rec = records + x * prefill_record_words(D, false);
         if (rr == 0) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) rec[4 + c * EPL + e] = o[e];
@@ -637,20 +637,39 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
         fast_sweep<D>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
     }
 
-    // records: (m, l, o[d]) per valid row; lane (lg, lr) holds o[16et + 4lg + i] of query lr
+    // records: header (m, l, s, 0), then o / (l s) as fp16 per valid row, s = 2^-k with k chosen
+    // so that the row's largest |o / l| lands in [2^14, 2^15): every value keeps 11 significant
+    // bits relative to that maximum, and the records take half the bytes of fp32 ones.  Lane
+    // (lg, lr) holds o[16et + 4lg + i] of query lr.
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
     for (int g = 0; g < kQG; ++g) {
         const float lt = group_sum4(l[g]);
-        if (x_own[g] >= 0) {
-            float *rec = records + (int64_t)x_own[g] * record_floats(D);
+        const float inv = 1.f / lt;
+        float amax = 0.f;
 #pragma unroll
-            for (int et = 0; et < ET; ++et)
-                *reinterpret_cast<float4 *>(rec + 4 + 16 * et + 4 * lg) =
-                    make_float4(o[g][et][0], o[g][et][1], o[g][et][2], o[g][et][3]);
-            if (lg == 0) {
-                rec[0] = m[g];
-                rec[1] = lt;
+        for (int et = 0; et < ET; ++et)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[g][et][i] * inv));
+        amax = group_max4(amax);
+        int k2 = 0;
+        if (amax > 0.f && amax <= 3.4028234663852886e38f) {
+            k2 = 14 - ((int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127);
+            k2 = k2 < -126 ? -126 : (k2 > 126 ? 126 : k2);
+        }
+        const float c = inv * __uint_as_float((uint32_t)(127 + k2) << 23);
+        if (x_own[g] >= 0) {
+            float *rec = records + (int64_t)x_own[g] * prefill_record_words(D, true);
+            uint32_t *hv = reinterpret_cast<uint32_t *>(rec + 4);
+#pragma unroll
+            for (int et = 0; et < ET; ++et) {
+                const half2_t lo = {(_Float16)(o[g][et][0] * c), (_Float16)(o[g][et][1] * c)};
+                const half2_t hi = {(_Float16)(o[g][et][2] * c), (_Float16)(o[g][et][3] * c)};
+                *reinterpret_cast<uint2 *>(hv + (16 * et + 4 * lg) / 2) =
+                    make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
             }
+            if (lg == 0)
+                *reinterpret_cast<float4 *>(rec) = make_float4(m[g], lt, __uint_as_float((uint32_t)(127 - k2) << 23), 0.f);
         }
     }
 }

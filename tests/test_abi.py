@@ -112,7 +112,10 @@ def test_workspace_sizes():
     # 32 heads x (16 selected + 2 window entries) x 4 sub-tiles x (4 + 128) floats
     assert d == 32 * 18 * 4 * 132 * 4
     p = ra.workspace_bytes(cfg(capacity=(1 << 20) + 8192), ra.RA_OP_PREFILL, 8192, (1 << 20) + 8191)
-    assert p > 8192 * 32 * 18 * 132 * 4  # at least the partial records
+    # at least the partial records: bf16 inputs keep them as a 16-byte header + d fp16 values
+    assert p > 8192 * 32 * 18 * (16 + 128 * 2)
+    p32 = ra.workspace_bytes(cfg(capacity=(1 << 20) + 8192, dtype=ra.RA_F32), ra.RA_OP_PREFILL, 8192, (1 << 20) + 8191)
+    assert p32 > 8192 * 32 * 18 * 132 * 4  # fp32 inputs: fp32 records
     assert ra.lib().ra_workspace_bytes(ctypes.byref(c.c()), 5, 1, 0) == 0
     assert ra.lib().ra_status_string(3) == b"buffer too small"
 
