@@ -7,8 +7,8 @@
 //    (4 waves x 2 groups of 16) and a range of spans; span summaries are rounded to bf16 once per
 //    block and staged in LDS, shared by the 4 waves and the 2 groups of each.  The kernel is
 //    bound by its score stores (1.08 GB for an 8192-row chunk on 1M tokens): 16-byte stores,
-//    which run fastest when score rows start on 64-byte boundaries (a score stride that is a
-//    multiple of 16 floats).  Rows of different sequences in one tile are handled
+//    which run fastest when score rows start on 128-byte cache lines (a score stride that is a
+//    multiple of 32 floats).  Rows of different sequences in one tile are handled
 //    in successive passes (one pass in the usual single-sequence chunk).
 //  * route_valu (fp32 inputs, or few rows as in decode): fp32 FMA; lanes split each summary
 //    row, 8 query heads per pass, butterfly reduction over the lanes of a row.

@@ -27,17 +27,17 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
 
 // PER_LANE candidates per lane kept in registers (r <= 64 * PER_LANE).
 //
-// Threshold first: T0 = the m-th largest of the 64 per-lane maxima (found by counting, per lane,
-// the lanes with a larger maximum).  The m lanes whose maxima are >= T0 hold at least m keys
-// >= T0, so every one of the m winners is >= T0.  The keys >= T0 (usually little more than m)
-// are compacted into LDS and each is ranked against the others; if more than 64 pass, the
-// selection falls back to m rounds of "largest key below the previous winner".
+// Threshold first: v = the m-th largest of the 64 per-lane maximum scores (the keys' upper
+// halves), found bit by bit from the top: a bit is kept when at least m lanes still reach the
+// value (one ballot per bit).  At least m lanes then hold a key >= T0 = v * 2^32, so every one of
+// the m winners is >= T0.  The keys >= T0 (usually little more than m; more only where scores
+// tie) are compacted into LDS in span order and each is ranked against the others; if more than
+// 64 pass, the selection falls back to m rounds of "largest key below the previous winner".
 template <int PER_LANE>
 __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ scores, int64_t stride,
                                                    const int64_t *__restrict__ row_pos, int32_t *__restrict__ sel,
                                                    int64_t n_rowheads, int Hq, int k, int S, int W, int64_t max_pos) {
     __shared__ uint64_t cand[4][64];
-    __shared__ uint32_t cidx[4][64];
     // all kernel arguments in one round trip (otherwise some are fetched only where first used)
     asm volatile("" ::"s"(scores), "s"(stride), "s"(row_pos), "s"(sel), "s"(n_rowheads), "s"(Hq), "s"(k), "s"(S),
                  "s"(W), "s"(max_pos));
@@ -82,14 +82,16 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
 #pragma unroll
         for (int i = 0; i + width < PER_LANE; i += 2 * width) f[i] = f[i + width] > f[i] ? f[i + width] : f[i];
     }
-    const uint64_t lmax = f[0];
-    int above = 0;  // lanes whose maximum is larger than this lane's
-#pragma unroll 8
-    for (int l2 = 0; l2 < 64; ++l2) above += readlane_u64(lmax, l2) > lmax ? 1 : 0;
     // at least m lanes hold a valid key (candidates are dealt round-robin and m <= r), so the
-    // m-th largest maximum is a valid, unique key
-    const uint64_t owner = __ballot(above == m - 1);
-    const uint64_t T0 = readlane_u64(lmax, (int)__builtin_ctzll(owner));
+    // search ends on the upper half of a valid key
+    const uint32_t lhi = (uint32_t)(f[0] >> 32);
+    uint32_t v = 0;
+#pragma unroll
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t test = v | (1u << bit);
+        if ((int)__builtin_popcountll(__ballot(lhi >= test)) >= m) v = test;
+    }
+    const uint64_t T0 = (uint64_t)v << 32;
 
     int C = 0;
 #pragma unroll
@@ -107,10 +109,11 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
         for (int j2 = 0; j2 < C; ++j2) rank += cand[wave][j2] > mine ? 1 : 0;
         const bool chosen = lane < C && rank < m;
         const uint32_t idx = 0xFFFFFFFFu - (uint32_t)(mine & 0xFFFFFFFFull);
-        cidx[wave][lane] = chosen ? idx : 0xFFFFFFFFu;
-        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        int pos = 0;
-        for (int j2 = 0; j2 < C; ++j2) pos += cidx[wave][j2] < idx ? 1 : 0;
+        // the list is in increasing span order (compacted register by register, lane by lane,
+        // and lane l of register i holds span l + 64 i), so a winner's output slot is the number
+        // of winners before it in the list
+        const uint64_t cb = __ballot(chosen);
+        const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(cb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cb, 0u));
         if (chosen) out[pos] = (int32_t)idx;
         if (lane >= m && lane < k) out[lane] = -1;
         return;

@@ -113,9 +113,9 @@ ra_status span_summary_update(const ra_config *cfg, const void *k_cache, float *
  * idea": score the O(L^0.5) candidate spans):  scores[row][h][j] = q[row][h] . kappa(mean_j)
  * for j < r(row_pos[row]); other entries are not written.  bf16 inputs run on bf16 MFMA with
  * fp32 accumulation; fp32 inputs use fp32 FMA.
- *   score_stride   floats per (row, head) in `scores`; must be >= r(max_pos).  A multiple of 16
- *                  (64-byte row starts) lets the bf16 kernel write whole 64-byte segments, which
- *                  is much faster when many rows are scored.
+ *   score_stride   floats per (row, head) in `scores`; must be >= r(max_pos).  A multiple of 32
+ *                  (rows starting on 128-byte cache lines) lets the bf16 kernel write whole
+ *                  lines, which is much faster when many rows are scored.
  */
 ra_status route_scores(const ra_config *cfg, const ra_rows *rows, const float *span_mean, float *scores,
                        int64_t score_stride, void *stream);

@@ -521,7 +521,7 @@ def test_decode_step_replays_from_a_hip_graph():
 def test_route_and_topk_do_not_depend_on_the_score_stride(d, G, S, W, nseq):
     """Scores and selections (bf16, enough rows for the MFMA routing kernel, rows of several
     sequences mixed in its tiles) are bitwise the same for an odd stride, the stride plus one and
-    the 16-float multiple that score_stride gives; entries past a row's r(t) are never written."""
+    the 32-float multiple that score_stride gives; entries past a row's r(t) are never written."""
     rng = np.random.default_rng(d + G + nseq)
     Hkv = 2 if G < 32 else 1
     n, cap, k = 300, 5000, 4
