@@ -345,10 +345,12 @@ ra_status cold_select(const ra_config *cfg, const ra_rows *rows, const uint8_t *
     if (!sig || !sel_cold) return fail(RA_EINVAL, "NULL sig or sel_cold");
     if ((uintptr_t)sig & 15) return fail(RA_EINVAL, "sig must be 16-byte aligned");
     const ra::RowArgs a = row_args(cfg, rows);
-    if (a.n_rows * a.Hkv * (int64_t)ra::cold_tiles(a.max_pos, hot_window) >= kMaxGrid)
+    const int n_tiles = ra::cold_tiles(a.max_pos, hot_window, a.G);
+    if (a.n_rows * a.Hkv * (int64_t)n_tiles >= kMaxGrid)
         return fail(RA_EUNSUPPORTED, "scan grid too large: use fewer rows per call");
-    if (ra::cold_tiles(a.max_pos, hot_window) > ra::kMergeTiles)
-        return fail(RA_EUNSUPPORTED, "cold retrieval scans at most %d x 8192 cold positions per row", ra::kMergeTiles);
+    if (n_tiles > ra::kMergeTiles)
+        return fail(RA_EUNSUPPORTED, "cold retrieval scans at most %d x %d cold positions per row", ra::kMergeTiles,
+                    ra::cold_tile_positions(a.G));
     const size_t need = ra::cold_workspace_bytes(a, hot_window, top_k_cold);
     if (!workspace || workspace_bytes < need)
         return fail(RA_ECAPACITY, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);

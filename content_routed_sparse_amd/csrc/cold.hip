@@ -23,9 +23,13 @@
 namespace ra {
 namespace {
 
-constexpr int kTile = 8192;                  // cold positions per scan block
-constexpr int kTileThreads = 512;
-constexpr int kPerThread = kTile / kTileThreads;
+// Scan tiles: TILE cold positions per block of THREADS threads, 16 signatures per thread.  Up to
+// 8 query heads per kv head: 16384 positions and 1024 threads (fewer, larger tiles: less per-tile
+// overhead here and fewer candidates for the merge); more heads: 8192 and 512, so that the
+// per-head LDS (histogram, tie bitmask, candidate buffers) of up to 32 heads fits.
+constexpr int kTileBig = 16384, kTileBigThreads = 1024;
+constexpr int kTileSmall = 8192, kTileSmallThreads = 512;
+constexpr int kTileBigMaxGroup = 8;
 constexpr int kMaxGroup = 32;                // query heads per kv head
 constexpr int kBins = 129;                   // distances 0 .. 128
 constexpr int kBinStride = 132;
@@ -110,16 +114,21 @@ __device__ __forceinline__ uint32_t distance(const SigWords<D> &s, const uint32_
 // LDS of cold_tile for G query heads (32-bit words): query signatures, distance histograms, tie
 // bitmasks, and per-wave candidate buffers of up to 128 entries per head within a 60 KB budget.
 constexpr int kTileLdsWords = 60 * 1024 / 4;
-constexpr int kTileWaves = kTileThreads / 64;
+template <int TILE, int THREADS>
 __host__ __device__ constexpr int tile_buf(int G, int WPR) {
-    const int room = (kTileLdsWords - G * (WPR + kBinStride + kTile / 32)) / (G * kTileWaves);
+    const int room = (kTileLdsWords - G * (WPR + kBinStride + TILE / 32)) / (G * (THREADS / 64));
     return room < 128 ? room : 128;
 }
+template <int TILE, int THREADS>
 __host__ __device__ constexpr int tile_lds_words(int G, int WPR) {
-    return G * (WPR + kBinStride + kTile / 32 + kTileWaves * tile_buf(G, WPR));
+    return G * (WPR + kBinStride + TILE / 32 + (THREADS / 64) * tile_buf<TILE, THREADS>(G, WPR));
 }
+static_assert(tile_buf<kTileBig, kTileBigThreads>(kTileBigMaxGroup, 4) >= 32 &&
+                  tile_buf<kTileSmall, kTileSmallThreads>(kMaxGroup, 4) >= 8,
+              "candidate buffers of a few entries per wave at least");
 
-// Exclusive prefix sum over the kTileThreads threads of a block (x >= 0); also returns the total.
+// Exclusive prefix sum over the NW waves of a block (x >= 0); also returns the total.
+template <int NW>
 __device__ __forceinline__ uint32_t tile_exclusive_scan(uint32_t x, uint32_t *wave_tot, uint32_t &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t inc = x;
@@ -133,7 +142,7 @@ __device__ __forceinline__ uint32_t tile_exclusive_scan(uint32_t x, uint32_t *wa
     uint32_t before = 0;
     total = 0;
 #pragma unroll
-    for (int w = 0; w < kTileWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
         const uint32_t t = wave_tot[w];
         if (w < wave) before += t;
         total += t;
@@ -170,15 +179,18 @@ __device__ __forceinline__ uint32_t wave_cut(const uint32_t *hist, int last, uin
     return kBins;
 }
 
-template <typename T, int D>
+template <typename T, int D, int kTile, int kTileThreads>
 __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ q, const int32_t *__restrict__ row_seq,
                                                           const int64_t *__restrict__ row_pos,
                                                           const uint32_t *__restrict__ sig, uint64_t *__restrict__ cand,
                                                           int Hq, int Hkv, int G, int B, int64_t cap, int64_t max_pos,
                                                           int H, int kc, int n_tiles) {
     constexpr int WPR = D / 32;
+    constexpr int kPerThread = kTile / kTileThreads;
+    constexpr int kTileWaves = kTileThreads / 64;
+    static_assert(kTile % kTileThreads == 0 && kTile / 32 <= kTileThreads && kTile <= 65536, "tile shape");
     extern __shared__ uint32_t lds[];
-    const int BW = tile_buf(G, WPR);
+    const int BW = tile_buf<kTile, kTileThreads>(G, WPR);
     uint32_t *qsig = lds;                              // [G][WPR]
     uint32_t *hist = qsig + G * WPR;                   // [G][kBinStride]
     uint32_t *tie = hist + G * kBinStride;             // [G][kTile / 32]
@@ -331,7 +343,7 @@ __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ 
     for (int h = 0; h < G; ++h) {
         uint32_t word = tid < kTile / 32 ? tie[h * (kTile / 32) + tid] : 0u;
         uint32_t total;
-        const uint32_t pre = tile_exclusive_scan(__popc(word), wave_tot, total);
+        const uint32_t pre = tile_exclusive_scan<kTileWaves>(__popc(word), wave_tot, total);
         const uint32_t nd = need[h];
         if (pre < nd) {
             const uint32_t take = nd - pre;
@@ -605,15 +617,23 @@ hipError_t sig_launch(const SigArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <typename T, int D, int TILE, int THREADS>
+void tile_launch(const RowArgs &a, const uint32_t *sig, int H, int kc, uint64_t *cand, int n_tiles, hipStream_t st) {
+    const size_t lds = tile_lds_words<TILE, THREADS>(a.G, D / 32) * sizeof(uint32_t);
+    hipLaunchKernelGGL((cold_tile<T, D, TILE, THREADS>), dim3((unsigned)(a.n_rows * a.Hkv * n_tiles)), dim3(THREADS),
+                       lds, st, (const T *)a.q, a.row_seq, a.row_pos, sig, cand, a.Hq, a.Hkv, a.G, a.B, a.cap,
+                       a.max_pos, H, kc, n_tiles);
+}
+
 template <typename T, int D>
 hipError_t select_launch(const RowArgs &a, const uint32_t *sig, int H, int kc, int32_t *sel, void *ws,
                          hipStream_t st) {
-    const int n_tiles = cold_tiles(a.max_pos, H);
+    const int n_tiles = cold_tiles(a.max_pos, H, a.G);
     uint64_t *cand = (uint64_t *)ws;
-    const size_t lds = tile_lds_words(a.G, D / 32) * sizeof(uint32_t);
-    hipLaunchKernelGGL((cold_tile<T, D>), dim3((unsigned)(a.n_rows * a.Hkv * n_tiles)), dim3(kTileThreads), lds, st,
-                       (const T *)a.q, a.row_seq, a.row_pos, sig, cand, a.Hq, a.Hkv, a.G, a.B, a.cap, a.max_pos, H, kc,
-                       n_tiles);
+    if (a.G <= kTileBigMaxGroup)
+        tile_launch<T, D, kTileBig, kTileBigThreads>(a, sig, H, kc, cand, n_tiles, st);
+    else
+        tile_launch<T, D, kTileSmall, kTileSmallThreads>(a, sig, H, kc, cand, n_tiles, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(cold_merge, dim3((unsigned)(a.n_rows * a.Hq)), dim3(kMergeThreads), 0, st, cand, sel, n_tiles,
@@ -633,13 +653,16 @@ hipError_t attn_launch(const RowArgs &a, const void *K, const void *V, const int
 
 }  // namespace
 
-int cold_tiles(int64_t max_pos, int H) {
+int cold_tile_positions(int G) { return G <= kTileBigMaxGroup ? kTileBig : kTileSmall; }
+
+int cold_tiles(int64_t max_pos, int H, int G) {
     const int64_t n = max_pos - H + 1;
-    return n <= 0 ? 1 : (int)((n + kTile - 1) / kTile);
+    const int tile = cold_tile_positions(G);
+    return n <= 0 ? 1 : (int)((n + tile - 1) / tile);
 }
 
 size_t cold_workspace_bytes(const RowArgs &a, int H, int kc) {
-    return (size_t)a.n_rows * a.Hq * cold_tiles(a.max_pos, H) * kc * sizeof(uint64_t);
+    return (size_t)a.n_rows * a.Hq * cold_tiles(a.max_pos, H, a.G) * kc * sizeof(uint64_t);
 }
 
 hipError_t launch_signatures(const SigArgs &a, hipStream_t st) {

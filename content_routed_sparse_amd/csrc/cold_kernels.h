@@ -9,7 +9,7 @@
 namespace ra {
 
 constexpr int kMaxCold = 128;      // largest top_k_cold
-constexpr int kMergeTiles = 4096;  // scan tiles (of 8192 cold positions) per row: 33.5M positions
+constexpr int kMergeTiles = 4096;  // scan tiles per row (of cold_tile_positions(G) positions each)
 
 struct SigArgs {  // signatures of rows [old_len[b], new_len[b]) of a K cache
     const void *k;
@@ -19,8 +19,10 @@ struct SigArgs {  // signatures of rows [old_len[b], new_len[b]) of a K cache
     int64_t cap, max_new;
 };
 
-// Scan tiles per (row, kv head) for rows up to max_pos, and the candidate workspace they fill.
-int cold_tiles(int64_t max_pos, int H);
+// Cold positions per scan tile for G query heads per kv head; scan tiles per (row, kv head) for
+// rows up to max_pos; and the candidate workspace they fill.
+int cold_tile_positions(int G);
+int cold_tiles(int64_t max_pos, int H, int G);
 size_t cold_workspace_bytes(const RowArgs &a, int H, int kc);
 
 hipError_t launch_signatures(const SigArgs &a, hipStream_t st);

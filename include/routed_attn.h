@@ -236,7 +236,8 @@ ra_status routed_attn_decode_fp8_append(const ra_config *cfg, const ra_rows *row
  * Query head h reads kv head h / (Hq / Hkv).  Layouts: sig [batch][Hkv][capacity][d/8] uint8
  * (16-byte aligned), sel_cold [n_rows][Hq][top_k_cold] int32, out [n_rows][Hq][d] float; K, V, q
  * as above.  Supported: 1 <= top_k_cold <= 128, hot_window >= 1, capacity < 2^31, at most
- * 4096 x 8192 cold positions per row (cold_select returns RA_EUNSUPPORTED beyond).  The span
+ * 4096 scan tiles of cold positions per row (tiles of 16384 positions when a kv head serves at
+ * most 8 query heads, else 8192; cold_select returns RA_EUNSUPPORTED beyond).  The span
  * fields of cfg (span_size, top_k, window) are validated but not used by these calls. */
 
 /* kv_signature_update -- signatures of K rows [old_len[b], new_len[b]) of every (sequence b, kv

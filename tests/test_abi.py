@@ -212,7 +212,9 @@ def test_cold_entry_points_validate_before_launch():
     r = rows()
     L = 1 << 20
     need = lib.ra_cold_workspace_bytes(ctypes.byref(cc), 1, L - 1, 256, 64)
-    assert need == 32 * ((L - 256 + 8191) // 8192) * 64 * 8
+    assert need == 32 * ((L - 256 + 16383) // 16384) * 64 * 8  # G = 8: tiles of 16384 positions
+    g32 = cfg(batch=1, num_q_heads=32, num_kv_heads=1).c()
+    assert lib.ra_cold_workspace_bytes(ctypes.byref(g32), 1, L - 1, 256, 64) == 32 * ((L - 256 + 8191) // 8192) * 64 * 8
     for hot, kc, status in ((0, 64, 1), (256, 0, 2), (256, 129, 2)):
         assert lib.cold_select(ctypes.byref(cc), ctypes.byref(r), FAKE, hot, kc, FAKE, FAKE, 1 << 30, None) == status
         assert lib.cold_attn_decode(ctypes.byref(cc), ctypes.byref(r), FAKE, FAKE, FAKE, hot, kc, FAKE, None) == status

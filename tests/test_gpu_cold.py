@@ -107,7 +107,7 @@ def few_sign_patterns(c):
 
 CASES = [
     # name, workload, lengths, H, top_k_cold, edit
-    ("d128_G8_kc64_3tiles", small("decode_1m", decode_len=20000), [20000], 256, 64, None),
+    ("d128_G8_kc64_20k", small("decode_1m", decode_len=20000), [20000], 256, 64, None),
     ("d64_G4_kc7_H16", small("decode_1m", num_q_heads=8, num_kv_heads=2, head_dim=64, decode_len=3000), [3000], 16,
      7, None),
     ("fp32_d64_kc96", W["tiny_prefill_fp32"], [9000], 256, 96, None),
