@@ -234,8 +234,8 @@ __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ 
     if (tid < G) cnt[tid] = 0;
     if (tid == 0) slow = 0;
     __syncthreads();
-    // 1. a sample of min(512, n) positions spread evenly over the tile sets a threshold per head
-    //    below which about 3 * kc of the tile's distances should fall
+    // 1. a sample of min(kTileThreads, n) positions spread evenly over the tile sets a threshold
+    //    per head below which about 3 * kc of the tile's distances should fall
     const int n_s = n_here < kTileThreads ? n_here : kTileThreads;
     if (tid < n_s) {
         const SigWords<D> smp = load_sig<D>(sbase + (int64_t)tid * (n_here / n_s) * WPR);
