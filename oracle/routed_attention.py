@@ -1,4 +1,8 @@
-"""CPU oracle for content-routed sparse attention -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for content-routed sparse attention (numpy) -- TEST INFRASTRUCTURE ONLY.
+
+This is the second of two implementations of the same definition; the plain C++ one
+(routed_attention.cpp, loaded through oracle/cpp.py) is written apart from it, and the pins in
+tests/test_oracle.py check both and compare them with each other.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
 import this package.  The GPU library never calls it, and it shares no code with the GPU path.

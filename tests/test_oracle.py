@@ -1,5 +1,10 @@
 """Pins for the CPU oracle: each test ties a part of it to something other than itself.
 
+The oracle exists twice, written apart: the plain C++ implementation (oracle/routed_attention.cpp,
+through oracle/cpp.py) and the numpy one (oracle/routed_attention.py).  Every pin of the method's
+steps runs against both (the ``impl`` fixture), and a cross-check compares the two on seeded
+problems (summaries and selections bit for bit, outputs within 1e-12).
+
 Kinds of pin used: exact arithmetic (Python integers / fractions), a library routine that is
 independent of the oracle's code (torch's bf16 conversion, torch's scaled-dot-product attention
 in float64), brute force on tiny inputs (rank counting instead of sorting), closed forms
@@ -17,48 +22,194 @@ import pytest
 import torch
 
 import oracle as O
+import oracle.cpp as CPP
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
+IMPLS = {"numpy": O, "cpp": CPP}
+
+
+@pytest.fixture(params=sorted(IMPLS))
+def impl(request):
+    """One oracle implementation: the numpy module or the C++ library's Python face."""
+    return IMPLS[request.param]
+
+
+def bf16_bits(a):
+    """float32 -> bf16 bit patterns (uint16) by torch's conversion (round to nearest even)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(
+        np.uint16)
+
+
+def torch_widen(bits_or_f32):
+    """Exact float64 values of stored inputs by torch's own conversions (independent of the
+    oracle's widening): bf16 bit patterns through torch.bfloat16, float32 through torch."""
+    a = np.ascontiguousarray(bits_or_f32)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    return torch.from_numpy(a).to(torch.float64).numpy()
+
 
 # ------------------------------------------------------------------------------------------ kappa
-def test_round_to_bf16_matches_torch_conversion():
+def test_round_to_bf16_matches_torch_conversion(impl):
     rng = np.random.default_rng(1)
     x = np.concatenate([rng.standard_normal(20000).astype(np.float32),
                         (rng.standard_normal(2000) * 1e-30).astype(np.float32),
                         (rng.standard_normal(2000) * 1e30).astype(np.float32),
                         np.array([0.0, -0.0, 1.0, -3.5, 2.0 ** -126, 2.0 ** -130], dtype=np.float32)])
     ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
-    assert np.array_equal(O.round_to_bf16(x), ref)
+    assert np.array_equal(impl.round_to_bf16(x), ref)
 
 
-def test_round_to_bf16_ties_to_even():
+def test_round_to_bf16_ties_to_even(impl):
     one = 1.0
     # 1 + 2^-8 is halfway between 1 and 1 + 2^-7 (odd significand) -> 1
-    assert O.round_to_bf16(np.float32(one + 2.0 ** -8)) == np.float32(1.0)
+    assert impl.round_to_bf16(np.float32(one + 2.0 ** -8)) == np.float32(1.0)
     # 1 + 3*2^-8 is halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even) -> 1 + 2^-6
-    assert O.round_to_bf16(np.float32(one + 3 * 2.0 ** -8)) == np.float32(1 + 2.0 ** -6)
+    assert impl.round_to_bf16(np.float32(one + 3 * 2.0 ** -8)) == np.float32(1 + 2.0 ** -6)
     # just above the halfway point rounds up
-    assert O.round_to_bf16(np.float32(one + 2.0 ** -8 + 2.0 ** -20)) == np.float32(1 + 2.0 ** -7)
+    assert impl.round_to_bf16(np.float32(one + 2.0 ** -8 + 2.0 ** -20)) == np.float32(1 + 2.0 ** -7)
+
+
+def test_widen_matches_torch_on_every_bf16_pattern(impl):
+    """All 65,536 bf16 bit patterns widen to torch's bf16 -> float value (NaN patterns to NaN),
+    through the float64 widening and, for the numpy oracle, the float32 one."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127  # exponent all ones, significand non-zero, either sign
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns raise the flag when widened
+        got = impl.widen(bits, True)
+    assert got.dtype == np.float64
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))  # -0 stays -0
+    if impl is O:
+        g32 = O.widen_f32(bits, True)
+        assert g32.dtype == np.float32
+        assert np.array_equal(np.isnan(g32), nan)
+        assert np.array_equal(g32[~nan].astype(np.float64), ref[~nan])
+        # float32 inputs pass through unchanged
+        x = np.array([1.5, -0.0, 3e-45, 3.4e38], dtype=np.float32)
+        assert np.array_equal(O.widen_f32(x, False).view(np.uint32), x.view(np.uint32))
+    x = np.array([1.5, -0.0, 3e-45, 3.4e38, -7.25], dtype=np.float32)
+    assert np.array_equal(impl.widen(x, False), torch.from_numpy(x).to(torch.float64).numpy())
+
+
+def test_score_abs_bound_equals_exact_rational_evaluation():
+    """gamma_d * max_j sum_e |q_e kappa(mean_j)_e| over j < r, evaluated with fractions.
+
+    Inputs: signed small integers (so that a missing absolute value changes the sum), the largest
+    term in a middle span (not the first or last), a huge span past r (must be ignored), and
+    means that kappa rounds (1 + 2^-9 -> 1) so that the bf16 and fp32 bounds differ."""
+    d = 8
+    u = Fraction(1, 2 ** 24)
+    gamma = Fraction(d) * u / (1 - Fraction(d) * u)
+    q = np.array([3, -2, 1, 0, -4, 5, -1, 2], dtype=np.float64)
+    means = np.array([[1, 1, -1, 0, 0, 0, 0, 0],
+                      [-2, 3, 1, 7, -1, 2, 0, -3],      # the largest sum of |q_e m_e|
+                      [1 + 2.0 ** -9, 0, 0, 0, 0, 0, 0, 0],
+                      [1000, 1000, 1000, 1000, 1000, 1000, 1000, 1000]], dtype=np.float32)
+    r = 3
+
+    def exact(kappa):
+        best = Fraction(0)
+        for j in range(r):
+            row = [Fraction(float(kappa(means[j, e]))) for e in range(d)]
+            best = max(best, sum(abs(Fraction(float(q[e])) * row[e]) for e in range(d)))
+        return gamma * best
+
+    ident = lambda x: x
+    to_bf16 = lambda x: torch.tensor(float(x), dtype=torch.float32).to(torch.bfloat16).to(torch.float64).item()
+    for is_bf16, kappa in ((False, ident), (True, to_bf16)):
+        got = O.score_abs_bound(q, means, r, is_bf16)
+        want = exact(kappa)
+        assert abs(Fraction(got) - want) <= want * Fraction(1, 2 ** 50), (is_bf16, got, float(want))
+    assert O.score_abs_bound(q, means, 0, True) == 0.0
+    # kappa changes the bound when the rounded span is the largest one
+    q2 = np.array([1, 0, 0, 0, 0, 0, 0, 0], dtype=np.float64)
+    m2 = np.array([[1 + 2.0 ** -9, 0, 0, 0, 0, 0, 0, 0]], dtype=np.float32)
+    close = lambda got, want: abs(Fraction(got) - want) <= want * Fraction(1, 2 ** 50)
+    assert close(O.score_abs_bound(q2, m2, 1, True), gamma)
+    assert close(O.score_abs_bound(q2, m2, 1, False), gamma * (1 + Fraction(1, 2 ** 9)))
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_cpp_and_numpy_oracles_agree(bf16):
+    """The two oracles on seeded problems: summaries (one-shot and appended in pieces) and
+    selections bit for bit, scores and outputs within 1e-12, weights summing to 1."""
+    rng = np.random.default_rng(21 + bf16)
+    for (L, S, W, k, d, hkv, hq) in [(700, 16, 20, 4, 32, 2, 4), (1200, 32, 32, 6, 64, 1, 3), (90, 8, 1, 64, 16, 2, 2)]:
+        keys = rng.standard_normal((hkv, L, d)).astype(np.float32)
+        keys[:, : L // 2] += rng.standard_normal((hkv, 1, d)).astype(np.float32)
+        vals = rng.standard_normal((hkv, L, d)).astype(np.float32)
+        qs = rng.standard_normal((40, hq, d)).astype(np.float32)
+        if bf16:
+            keys, vals, qs = bf16_bits(keys), bf16_bits(vals), bf16_bits(qs)
+        pn = O.Problem(keys, vals, L, hq, S, k, W, bf16)
+        pc = CPP.Problem(keys, vals, L, hq, S, k, W, bf16)
+        assert np.array_equal(pn.means.view(np.uint32), pc.means.view(np.uint32))
+        # appended in uneven pieces
+        m = np.zeros_like(pc.means)
+        run = np.zeros((hkv, d), dtype=np.float32)
+        cuts = sorted(set([0, L] + rng.integers(0, L, 6).tolist()))
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            CPP.summary_update(keys, m, run, a, b, S)
+        _, run_n = O.summaries(O.widen_f32(keys, bf16), L, S)
+        assert np.array_equal(m.view(np.uint32), pn.means.view(np.uint32))
+        assert np.array_equal(run.view(np.uint32), run_n.view(np.uint32))
+        pos = np.concatenate([[0, 1, L - 1], rng.integers(0, L, 37)])
+        res = pc.rows(qs, pos, scores=True)
+        for i, t in enumerate(pos):
+            for h in range(hq):
+                a = pn.row(qs[i, h], h, int(t))
+                assert np.array_equal(a["sel"], res["sel"][i, h]), (L, i, h)
+                assert a["n_attended"] == res["n_attended"][i, h]
+                assert np.abs(a["out"] - res["out"][i, h]).max() <= 1e-12
+                if len(a["scores"]):
+                    assert np.abs(a["scores"] - res["scores"][i][h]).max() <= 1e-12 * np.abs(a["scores"]).max()
+                assert abs(res["weight_sum"][i, h] - 1.0) <= 1e-12
+        dn = pc.rows(qs[:5], pos[:5], dense=True)
+        for i in range(5):
+            for h in range(hq):
+                assert np.abs(dn["out"][i, h] - pn.dense_row(qs[i, h], h, int(pos[i]))).max() <= 1e-12
+
+
+def test_cpp_oracle_skips_repeated_and_unroutable_entries_of_a_given_selection():
+    """A given selection with repeats, -1 and ids >= r attends the distinct routable spans once."""
+    rng = np.random.default_rng(31)
+    L, S, W, k, d = 900, 16, 16, 8, 16
+    keys = rng.standard_normal((1, L, d)).astype(np.float32)
+    vals = rng.standard_normal((1, L, d)).astype(np.float32)
+    pc = CPP.Problem(keys, vals, L, 1, S, k, W, False)
+    pn = O.Problem(keys, vals, L, 1, S, k, W, False)
+    q = rng.standard_normal(d).astype(np.float32)
+    t = 700
+    r = O.num_routable(t, S, W)
+    given = np.array([5, 9, 5, -1, r, r + 3, 9, 2], dtype=np.int64)
+    a = pc.row(q, 0, t, sel=given)
+    b = pn.row(q, 0, t, sel=np.array([2, 5, 9]))
+    assert a["n_attended"] == b["n_attended"] == 3 * S + (t - O.window_start(t, S, W) + 1)
+    assert np.abs(a["out"] - b["out"]).max() <= 1e-12
 
 
 # ---------------------------------------------------------------------------------- summaries
-def test_summary_of_constant_span_is_that_constant():
+def test_summary_of_constant_span_is_that_constant(impl):
     S, d = 16, 8
     for c in [0.375, -2.5, 1.0 / 1024]:  # dyadic constants: every partial sum is exact in fp32
         keys = np.full((2, 5 * S, d), c, dtype=np.float32)
-        means, run = O.summaries(keys, 5 * S, S)
+        means, run = impl.summaries(keys, 5 * S, S)
         assert np.all(means == np.float32(c))
         assert np.all(run == 0)
 
 
-def test_summary_integer_keys_exact_mean():
+def test_summary_integer_keys_exact_mean(impl):
     """Small-integer keys sum exactly in fp32; the mean must be the exact rational sum/S."""
     rng = np.random.default_rng(2)
     S, d, L = 8, 6, 8 * 7 + 3
     ints = rng.integers(-50, 51, size=(3, L, d))
     keys = ints.astype(np.float32)
-    means, run = O.summaries(keys, L, S)
+    means, run = impl.summaries(keys, L, S)
     assert means.shape == (3, L // S, d)
     for h in range(3):
         for j in range(L // S):
@@ -70,84 +221,84 @@ def test_summary_integer_keys_exact_mean():
             assert run[h, e] == float(ints[h, (L // S) * S:, e].sum())
 
 
-def test_summary_sums_in_token_order_in_fp32():
+def test_summary_sums_in_token_order_in_fp32(impl):
     """1 followed by S-1 copies of 2^-24: each fp32 addition 1 + 2^-24 ties to even -> 1."""
     S = 4
     keys = np.array([[[1.0], [2.0 ** -24], [2.0 ** -24], [2.0 ** -24]]], dtype=np.float32)
-    means, _ = O.summaries(keys, S, S)
+    means, _ = impl.summaries(keys, S, S)
     assert means[0, 0, 0] == np.float32(0.25)
     # the exactly rounded mean would differ: the order-of-addition reading is what is pinned
     assert np.float32((1 + 3 * 2.0 ** -24) / 4) != np.float32(0.25)
 
 
 @pytest.mark.parametrize("chunk", [1, 7, 16, 100])
-def test_summary_incremental_equals_one_shot(chunk):
+def test_summary_incremental_equals_one_shot(impl, chunk):
     rng = np.random.default_rng(3)
     S, d, L = 16, 8, 16 * 9 + 5
     keys = rng.standard_normal((2, L, d)).astype(np.float32)
-    m1, r1 = O.summaries(keys, L, S)
+    m1, r1 = impl.summaries(keys, L, S)
     means = np.zeros((2, L // S, d), dtype=np.float32)
     run = np.zeros((2, d), dtype=np.float32)
     p = 0
     while p < L:
         q = min(L, p + chunk)
-        O.summary_update(keys, means, run, p, q, S)
+        impl.summary_update(keys, means, run, p, q, S)
         p = q
     assert np.array_equal(means, m1) and np.array_equal(run, r1)
 
 
-def test_summary_close_to_exact_mean():
+def test_summary_close_to_exact_mean(impl):
     rng = np.random.default_rng(4)
     S, d, L = 64, 16, 64 * 6
     keys = rng.standard_normal((1, L, d)).astype(np.float32)
-    means, _ = O.summaries(keys, L, S)
+    means, _ = impl.summaries(keys, L, S)
     exact = keys.astype(np.float64).reshape(1, 6, S, d).mean(axis=2)
     bound = S * 2.0 ** -24 * np.abs(keys.astype(np.float64)).reshape(1, 6, S, d).mean(axis=2) * 1.01 + 1e-30
     assert np.all(np.abs(means - exact) <= bound)
 
 
 # ------------------------------------------------------------------------------ window / spans
-def test_window_and_routable_closed_forms():
+def test_window_and_routable_closed_forms(impl):
     S, W = 64, 64
-    assert O.window_start(0, S, W) == 0 and O.num_routable(0, S, W) == 0
-    assert O.num_routable(126, S, W) == 0
-    assert O.num_routable(127, S, W) == 1 and O.window_start(127, S, W) == 64
+    assert impl.window_start(0, S, W) == 0 and impl.num_routable(0, S, W) == 0
+    assert impl.num_routable(126, S, W) == 0
+    assert impl.num_routable(127, S, W) == 1 and impl.window_start(127, S, W) == 64
     for t in range(0, 2000):
-        w0 = O.window_start(t, S, W)
+        w0 = impl.window_start(t, S, W)
         assert w0 % S == 0 and w0 <= max(0, t - W + 1)
         size = t - w0 + 1
         assert size <= W + S - 1
         assert t < W - 1 or size >= W
     # W = 3S: window holds 3S .. 4S-1 tokens once t is large
     for t in range(1000, 1200):
-        assert 3 * 16 <= t - O.window_start(t, 16, 48) + 1 <= 4 * 16 - 1
+        assert 3 * 16 <= t - impl.window_start(t, 16, 48) + 1 <= 4 * 16 - 1
 
 
-def test_every_past_token_is_routable_or_in_window():
+def test_every_past_token_is_routable_or_in_window(impl):
     for S, W in [(8, 8), (8, 1), (8, 20), (5, 13)]:
         for t in range(0, 200):
-            r = O.num_routable(t, S, W)
-            covered = set(range(0, r * S)) | set(range(O.window_start(t, S, W), t + 1))
+            r = impl.num_routable(t, S, W)
+            covered = set(range(0, r * S)) | set(range(impl.window_start(t, S, W), t + 1))
             assert covered == set(range(t + 1)), (S, W, t)
 
 
 # ------------------------------------------------------------------------------------ scores
-def test_scores_exact_on_integers_and_unscaled():
+def test_scores_exact_on_integers_and_unscaled(impl):
     rng = np.random.default_rng(5)
     d, r = 32, 20
     q = rng.integers(-4, 5, size=d).astype(np.float32)
     means = rng.integers(-3, 4, size=(r + 3, d)).astype(np.float32)
-    s = O.route_scores(q, means, r, is_bf16=True)  # small integers are bf16-exact
+    s = impl.route_scores(q, means, r, is_bf16=True)  # small integers are bf16-exact
     for j in range(r):
         assert s[j] == sum(int(q[e]) * int(means[j, e]) for e in range(d))
     assert len(s) == r
 
 
-def test_scores_round_mean_to_bf16_for_bf16_inputs():
+def test_scores_round_mean_to_bf16_for_bf16_inputs(impl):
     means = np.array([[1.0 + 2.0 ** -9, 0.0]], dtype=np.float32)
     q = np.array([1.0, 0.0], dtype=np.float32)
-    assert O.route_scores(q, means, 1, is_bf16=True)[0] == 1.0
-    assert O.route_scores(q, means, 1, is_bf16=False)[0] == 1.0 + 2.0 ** -9
+    assert impl.route_scores(q, means, 1, is_bf16=True)[0] == 1.0
+    assert impl.route_scores(q, means, 1, is_bf16=False)[0] == 1.0 + 2.0 ** -9
 
 
 # --------------------------------------------------------------------------------- selection
@@ -160,16 +311,16 @@ def _brute_selection(scores, k):
     return keep + [-1] * (k - len(keep))
 
 
-def test_selection_matches_rank_counting_with_ties():
+def test_selection_matches_rank_counting_with_ties(impl):
     rng = np.random.default_rng(6)
     for trial in range(300):
         r = int(rng.integers(0, 25))
         k = int(rng.integers(1, 10))
         scores = rng.integers(-3, 4, size=r).astype(np.float64) * 0.5  # many exact ties
-        assert list(O.select_spans(scores, k)) == _brute_selection(list(scores), k)
+        assert list(impl.select_spans(scores, k)) == _brute_selection(list(scores), k)
 
 
-def test_selection_matches_exhaustive_subset_search():
+def test_selection_matches_exhaustive_subset_search(impl):
     """The kept set maximises the score sum; among maximisers, it is lexicographically smallest."""
     rng = np.random.default_rng(7)
     for _ in range(60):
@@ -178,15 +329,15 @@ def test_selection_matches_exhaustive_subset_search():
         scores = rng.standard_normal(r)
         m = min(k, r)
         best = max(itertools.combinations(range(r), m), key=lambda c: (sum(scores[j] for j in c), [-j for j in c]))
-        assert list(O.select_spans(scores, k)[:m]) == sorted(best)
+        assert list(impl.select_spans(scores, k)[:m]) == sorted(best)
 
 
-def test_selection_special_cases():
-    assert list(O.select_spans(np.zeros(10), 4)) == [0, 1, 2, 3]          # q = 0: lowest indices win
-    assert list(O.select_spans(np.array([1.0, 2.0]), 4)) == [0, 1, -1, -1]  # k > r: all spans
-    assert list(O.select_spans(np.array([]), 3)) == [-1, -1, -1]           # r = 0: window only
+def test_selection_special_cases(impl):
+    assert list(impl.select_spans(np.zeros(10), 4)) == [0, 1, 2, 3]          # q = 0: lowest indices win
+    assert list(impl.select_spans(np.array([1.0, 2.0]), 4)) == [0, 1, -1, -1]  # k > r: all spans
+    assert list(impl.select_spans(np.array([]), 3)) == [-1, -1, -1]           # r = 0: window only
     s = np.array([0.1, 5.0, 3.0, 5.0, 3.0])                               # duplicates: lower index wins
-    assert list(O.select_spans(s, 3)) == [1, 2, 3]
+    assert list(impl.select_spans(s, 3)) == [1, 2, 3]
 
 
 # ------------------------------------------------------------------------- attended set / softmax
@@ -207,16 +358,16 @@ def _bitcoded_problem(L, S, k, W, d, hkv=1, hq=1, bf16=False):
     return keys, values
 
 
-def test_zero_query_gives_uniform_average_over_exact_token_set():
+def test_zero_query_gives_uniform_average_over_exact_token_set(impl):
     L, S, k, W, d = 1500, 16, 5, 24, 12
     keys, values = _bitcoded_problem(L, S, k, W, d)
-    prob = O.Problem(keys, values, L, 1, S, k, W, is_bf16=False)
+    prob = impl.Problem(keys, values, L, 1, S, k, W, is_bf16=False)
     q = np.zeros(d, dtype=np.float32)
     for t in [0, 5, 38, 39, 40, 100, 777, 1499]:
         res = prob.row(q, 0, t)
-        r = O.num_routable(t, S, W)
+        r = impl.num_routable(t, S, W)
         m = min(k, r)
-        w0 = O.window_start(t, S, W)
+        w0 = impl.window_start(t, S, W)
         ranges = [(j * S, j * S + S - 1) for j in range(m)] + [(w0, t)]  # q = 0 -> spans 0..m-1
         n = sum(b - a + 1 for a, b in ranges)
         assert res["n_attended"] == n
@@ -226,12 +377,12 @@ def test_zero_query_gives_uniform_average_over_exact_token_set():
         assert abs(res["weight_sum"] - 1.0) < 1e-12
 
 
-def test_constant_values_give_constant_output_and_weights_sum_to_one():
+def test_constant_values_give_constant_output_and_weights_sum_to_one(impl):
     rng = np.random.default_rng(9)
     L, S, k, W, d = 900, 8, 3, 8, 16
     keys = (rng.standard_normal((2, L, d)) * 3).astype(np.float32)
     values = np.ones((2, L, d), dtype=np.float32)
-    prob = O.Problem(keys, values, L, 4, S, k, W, is_bf16=False)
+    prob = impl.Problem(keys, values, L, 4, S, k, W, is_bf16=False)
     for t in [3, 64, 899]:
         q = (rng.standard_normal(d) * 4).astype(np.float32)
         for hq in range(4):
@@ -240,13 +391,13 @@ def test_constant_values_give_constant_output_and_weights_sum_to_one():
             assert abs(res["weight_sum"] - 1.0) < 1e-12
 
 
-def test_dominant_key_wins():
+def test_dominant_key_wins(impl):
     L, S, k, W, d = 256, 8, 2, 8, 4
     keys = np.zeros((1, L, d), dtype=np.float32)
     values = np.random.default_rng(10).standard_normal((1, L, d)).astype(np.float32)
     keys[0, 37] = [100.0, 0, 0, 0]
     # span 4 (positions 32..39) holds the only large key; its mean dominates routing
-    prob = O.Problem(keys, values, L, 1, S, k, W, is_bf16=False)
+    prob = impl.Problem(keys, values, L, 1, S, k, W, is_bf16=False)
     res = prob.row(np.array([10.0, 0, 0, 0], dtype=np.float32), 0, 255)
     assert 4 in res["sel"]
     assert np.allclose(res["out"], values[0, 37], atol=1e-12)
@@ -263,18 +414,17 @@ def _sdpa_f64(q, keys, values, mask):
 
 
 @pytest.mark.parametrize("bf16", [False, True])
-def test_k_all_spans_equals_dense_causal_attention(bf16):
+def test_k_all_spans_equals_dense_causal_attention(impl, bf16):
     rng = np.random.default_rng(11)
     L, S, W, d, hkv, hq = 333, 8, 8, 16, 2, 4
     keys = rng.standard_normal((hkv, L, d)).astype(np.float32)
     values = rng.standard_normal((hkv, L, d)).astype(np.float32)
     qs = rng.standard_normal((L, hq, d)).astype(np.float32)
     if bf16:
-        to_bits = lambda a: (torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
-        keys, values, qs = to_bits(keys), to_bits(values), to_bits(qs)
+        keys, values, qs = bf16_bits(keys), bf16_bits(values), bf16_bits(qs)
     k_all = L // S + 1
-    prob = O.Problem(keys, values, L, hq, S, k_all, W, is_bf16=bf16)
-    kd, vd, qd = O.widen(keys, bf16), O.widen(values, bf16), O.widen(qs, bf16)
+    prob = impl.Problem(keys, values, L, hq, S, k_all, W, is_bf16=bf16)
+    kd, vd, qd = torch_widen(keys), torch_widen(values), torch_widen(qs)
     for t in list(range(0, 40)) + list(range(300, L)):
         for h in range(hq):
             res = prob.row(qs[t, h], h, t)
@@ -283,12 +433,12 @@ def test_k_all_spans_equals_dense_causal_attention(bf16):
             assert np.abs(res["out"] - ref).max() < 1e-12, (t, h)
 
 
-def test_routed_equals_masked_attention_over_selected_tokens():
+def test_routed_equals_masked_attention_over_selected_tokens(impl):
     rng = np.random.default_rng(12)
     L, S, W, k, d = 640, 16, 20, 3, 8
     keys = rng.standard_normal((1, L, d)).astype(np.float32)
     values = rng.standard_normal((1, L, d)).astype(np.float32)
-    prob = O.Problem(keys, values, L, 1, S, k, W, is_bf16=False)
+    prob = impl.Problem(keys, values, L, 1, S, k, W, is_bf16=False)
     for t in [100, 333, 639]:
         q = rng.standard_normal(d).astype(np.float32)
         res = prob.row(q, 0, t)
@@ -296,13 +446,13 @@ def test_routed_equals_masked_attention_over_selected_tokens():
         for j in res["sel"]:
             if j >= 0:
                 mask[j * S:(j + 1) * S] = True
-        mask[O.window_start(t, S, W):t + 1] = True
+        mask[impl.window_start(t, S, W):t + 1] = True
         assert not mask[t + 1:].any()
         ref = _sdpa_f64(q, keys[0], values[0], mask)
         assert np.abs(res["out"] - ref).max() < 1e-12
 
 
-def test_planted_needle_is_routed():
+def test_planted_needle_is_routed(impl):
     rng = np.random.default_rng(13)
     L, S, W, k, d = 4096, 64, 64, 2, 32
     keys = rng.standard_normal((1, L, d)).astype(np.float32)
@@ -310,7 +460,7 @@ def test_planted_needle_is_routed():
     u /= np.linalg.norm(u)
     keys[0, 17 * S:18 * S] += (4 * u).astype(np.float32)  # span 17 carries a strong direction
     values = rng.standard_normal((1, L, d)).astype(np.float32)
-    prob = O.Problem(keys, values, L, 1, S, k, W, is_bf16=False)
+    prob = impl.Problem(keys, values, L, 1, S, k, W, is_bf16=False)
     res = prob.row((8 * u).astype(np.float32), 0, L - 1)
     assert 17 in res["sel"]
 
