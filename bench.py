@@ -52,6 +52,7 @@ def parse():
     p.add_argument("--no-fp8", action="store_true", help="skip the decode step over the 8-bit cache")
     p.add_argument("--no-snapshot", action="store_true", help="skip the session snapshot / restore measurement")
     p.add_argument("--no-cold", action="store_true", help="skip the token-level cold retrieval decode step")
+    p.add_argument("--no-tiny", action="store_true", help="skip the tiny fp32 prefill (4096 tokens, d = 64)")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the decode steps of the 10M-token and ragged 16-sequence workloads")
     p.add_argument("--copy-calibration", action="store_true",
@@ -207,6 +208,9 @@ def main():
         per_seq.append(kv + w.num_q_heads * w.head_dim * (2 + 4) + w.num_kv_heads * w.head_dim * (2 + 8))
     bytes_step = float(np.mean([per_seq[i % NC] for i in timed_ev]))
     achieved = bytes_step / (attn_ms * 1e-3) / 1e9
+    # the whole step also reads the summaries of every routable span (routing)
+    route_bytes = ((L - w.window) // w.span_size) * w.num_kv_heads * w.head_dim * 4
+    step_gbs = (bytes_step + route_bytes) / (ms_per_step * 1e-3) / 1e9
 
     traffic = counter_traffic("routed_attn_decode_1m")
 
@@ -231,6 +235,10 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(bytes_step), "avg_launch_ms": round(attn_ms, 5)},
+        "step_roofline": {"bound": "hbm", "what": "the whole step (route + top-k + attention with the update)",
+                          "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                          "algorithmic_bytes_per_step": int(bytes_step + route_bytes)},
         "repeat_bitwise_identical": bool(same),
         "setup_seconds": round(gen_s, 1),
     }
@@ -252,19 +260,29 @@ def main():
         torch.cuda.synchronize()
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"], result["oracle_check"] = cpu_baseline(w, st[0], args.cpu_seconds)
+        kv0 = [(WL.kv_slab(w, 0, 0, L, "k"), WL.kv_slab(w, 0, 0, L, "v"))]
+        result["cpu_baseline"], result["oracle_check"] = oracle_decode_baseline(
+            w, kv0, [L], [WL.query_at(w, 0, L - 1)], args.cpu_seconds, st[0]["sel"].cpu().numpy(),
+            st[0]["out"].cpu().numpy())
+        del kv0
 
     if not args.no_prefill:
         del K, V, st
         torch.cuda.empty_cache()
-        result["prefill"] = bench_prefill(args.prefill_steps, args.dense_steps, not args.no_ladder)
+        result["prefill"] = bench_prefill(args.prefill_steps, args.dense_steps, not args.no_ladder,
+                                          0.0 if args.no_cpu_baseline else args.cpu_seconds)
 
     if not args.no_extra:
         if args.no_prefill:
             del K, V, st
             torch.cuda.empty_cache()
-        result["decode_other"] = [bench_decode_workload(name, max(8, args.steps // 2), args.warmup)
+        result["decode_other"] = [bench_decode_workload(name, max(8, args.steps // 2), args.warmup,
+                                                        0.0 if args.no_cpu_baseline else args.cpu_seconds)
                                   for name in ("decode_10m", "ragged_decode_16")]
+
+    if not args.no_tiny:
+        result["tiny_prefill"] = bench_tiny_prefill(max(20, args.steps // 4), 0.0 if args.no_cpu_baseline else
+                                                    args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
 
@@ -282,7 +300,7 @@ def counter_traffic(tag):
     return rec.get("bytes_per_launch") if rec.get("source_sha256") == h.hexdigest() else None
 
 
-def bench_prefill(steps, dense_steps=2, ladder=True):
+def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0):
     """Chunked prefill: 8192 new tokens appended to a 1M-token cache (the chunk's K/V are in
     the cache before timing).  A step = span_summary_update of the chunk + route_scores +
     topk_spans + routed_attn_prefill for its 8192 x 32 row-heads."""
@@ -296,9 +314,10 @@ def bench_prefill(steps, dense_steps=2, ladder=True):
     L = P + n
     dev = torch.device("cuda:0")
     cfg = ra.Config(w.num_q_heads, w.num_kv_heads, w.head_dim, w.span_size, w.top_k, w.window, ra.RA_BF16, 1, L)
-    K = torch.from_numpy(WL.kv_slab(w, 0, 0, L, "k").view(np.int16)).view(torch.bfloat16)[None].to(dev)
-    V = torch.from_numpy(WL.kv_slab(w, 0, 0, L, "v").view(np.int16)).view(torch.bfloat16)[None].to(dev)
-    q = torch.from_numpy(WL.queries(w, 0, P, n).view(np.int16)).view(torch.bfloat16).to(dev)
+    kh, vh, qh = WL.kv_slab(w, 0, 0, L, "k"), WL.kv_slab(w, 0, 0, L, "v"), WL.queries(w, 0, P, n)
+    K = torch.from_numpy(kh.view(np.int16)).view(torch.bfloat16)[None].to(dev)
+    V = torch.from_numpy(vh.view(np.int16)).view(torch.bfloat16)[None].to(dev)
+    q = torch.from_numpy(qh.view(np.int16)).view(torch.bfloat16).to(dev)
     rows = ra.Rows(q, torch.zeros(n, dtype=torch.int32, device=dev),
                    torch.arange(P, L, dtype=torch.int64, device=dev), L - 1)
     mean = torch.zeros(1, w.num_kv_heads, cfg.max_spans, w.head_dim, dtype=torch.float32, device=dev)
@@ -373,6 +392,10 @@ def bench_prefill(steps, dense_steps=2, ladder=True):
         rungs = prefill_ladder(w, cfg, K, V, q, mean, ws, dense_steps,
                                {"prefix": P, "routed_path_ms": None, "routed_attn_ms": round(attn_ms, 4),
                                 "dense_ms": dense["ms_per_call"] if dense else None})
+    cpu, check = None, None
+    if cpu_seconds > 0:
+        cpu, check = oracle_prefill_baseline(w, kh, vh, P, n, qh, cpu_seconds, sel.cpu().numpy(), out.cpu().numpy())
+    step_tflops = (attn_flops + route_flops) / (step_ms * 1e-3) / 1e12
     return {
         "workload": "prefill_8k_on_1m", "chunk": n, "context": L, "steps": steps,
         "value": round(n / (step_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(step_ms, 4),
@@ -381,7 +404,11 @@ def bench_prefill(steps, dense_steps=2, ladder=True):
                      "frac": round(tflops / 2500.0, 4), "traffic": counter_traffic("routed_attn_prefill_8k_on_1m"),
                      "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
         "step_flops": attn_flops + route_flops,
-        "step_tflops": round((attn_flops + route_flops) / (step_ms * 1e-3) / 1e12, 1),
+        "step_tflops": round(step_tflops, 1),
+        "step_roofline": {"bound": "mfma", "what": "the whole step (summary update + route + top-k + attention)",
+                          "achieved": round(step_tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                          "frac": round(step_tflops / 2500.0, 4)},
+        "cpu_baseline": cpu, "oracle_check": check,
         "dense_causal": dense,
         "ladder": rungs,
     }
@@ -696,7 +723,83 @@ def bench_snapshot(w, d0, cfg1, reps=3):
             "intact": intact, "restored_bitwise": bool(restored), "pcie_round_trip_bitwise": bool(round_trip)}
 
 
-def bench_decode_workload(name, steps, warmup):
+def bench_tiny_prefill(steps, cpu_seconds=0.0):
+    """The tiny causal prefill (fp32, 1 head, d = 64, 4096 tokens from an empty cache, spans of 64,
+    top-8 + window 64): a step is span_summary_update of the 4096 tokens + route_scores +
+    topk_spans + routed_attn_prefill for the 4096 rows, all fp32 FMA.  Its work (0.6 GFLOP) is far
+    too small to fill the GPU: the leg reports the time, and the fraction of the fp32 vector peak
+    as a number, not a target."""
+    import torch
+
+    import content_routed_sparse_amd as ra
+    from synth import workloads as WL
+
+    w = WL.WORKLOADS["tiny_prefill_fp32"]
+    n = w.chunk_len
+    dev = torch.device("cuda:0")
+    cfg = ra.Config(w.num_q_heads, w.num_kv_heads, w.head_dim, w.span_size, w.top_k, w.window, ra.RA_F32, 1, n)
+    kh, vh, qh = WL.kv_slab(w, 0, 0, n, "k"), WL.kv_slab(w, 0, 0, n, "v"), WL.queries(w, 0, 0, n)
+    K = torch.from_numpy(kh)[None].to(dev)
+    V = torch.from_numpy(vh)[None].to(dev)
+    q = torch.from_numpy(qh).to(dev)
+    rows = ra.Rows(q, torch.zeros(n, dtype=torch.int32, device=dev), torch.arange(n, dtype=torch.int64, device=dev),
+                   n - 1)
+    mean = torch.zeros(1, w.num_kv_heads, cfg.max_spans, w.head_dim, dtype=torch.float32, device=dev)
+    run = torch.zeros(1, w.num_kv_heads, w.head_dim, dtype=torch.float32, device=dev)
+    zero, full = torch.zeros(1, dtype=torch.int64, device=dev), torch.full((1,), n, dtype=torch.int64, device=dev)
+    scores = torch.empty(n, w.num_q_heads, ra.score_stride(cfg, n - 1), dtype=torch.float32, device=dev)
+    sel = torch.empty(n, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev)
+    out = torch.empty(n, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    ws = torch.empty(ra.workspace_bytes(cfg, ra.RA_OP_PREFILL, n, n - 1), dtype=torch.uint8, device=dev)
+    # every step starts from the empty cache: the summary update rebuilds all 64 means
+    calls = [ra.prepare("span_summary_update", cfg, K, mean, run, zero, full, n),
+             ra.prepare("route_scores", cfg, rows, mean, scores),
+             ra.prepare("topk_spans", cfg, rows, scores, sel)]
+    attn = ra.prepare("routed_attn_prefill", cfg, rows, K, V, sel, out, ws)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        for c in calls:
+            c()
+        attn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        for c in calls:
+            c()
+        a.record(stream)
+        attn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    pos = np.arange(n)
+    S, W = w.span_size, w.window
+    w0 = S * (np.maximum(0, pos - W + 1) // S)
+    r = w0 // S
+    keys = (np.minimum(w.top_k, r) * S + (pos - w0 + 1)).astype(np.float64)
+    attn_flops = 4.0 * w.head_dim * keys.sum() * w.num_q_heads
+    route_flops = 2.0 * w.head_dim * r.astype(np.float64).sum() * w.num_q_heads
+    FP32_PEAK = 157.3
+    tf = attn_flops / (attn_ms * 1e-3) / 1e12
+    stf = (attn_flops + route_flops) / (step_ms * 1e-3) / 1e12
+    cpu, check = None, None
+    if cpu_seconds > 0:
+        cpu, check = oracle_prefill_baseline(w, kh, vh, 0, n, qh, cpu_seconds, sel.cpu().numpy(), out.cpu().numpy())
+    return {"workload": "tiny_prefill_fp32", "chunk": n, "context": n, "steps": steps,
+            "value": round(n / (step_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(step_ms, 4),
+            "dtype": "f32",
+            "roofline": {"bound": "alu", "kernel": "routed_attn_prefill (dispatch + fp32 tiles + merge)",
+                         "achieved": round(tf, 3), "peak": FP32_PEAK, "unit": "TFLOP/s",
+                         "frac": round(tf / FP32_PEAK, 5), "traffic": None,
+                         "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
+            "step_roofline": {"bound": "alu", "what": "the whole step (summary update + route + top-k + attention)",
+                              "achieved": round(stf, 3), "peak": FP32_PEAK, "unit": "TFLOP/s",
+                              "frac": round(stf / FP32_PEAK, 5)},
+            "cpu_baseline": cpu, "oracle_check": check}
+
+
+def bench_decode_workload(name, steps, warmup, cpu_seconds=0.0):
     """The decode step of another decode workload: decode_10m (one 10M-token sequence, spans of
     4096) or ragged_decode_16 (16 sequences of 64K..512K tokens, spans of 512).  A step appends
     one token to every sequence: route_scores -> topk_spans -> routed_attn_decode_append (with the
@@ -715,11 +818,15 @@ def bench_decode_workload(name, steps, warmup):
     t0 = time.time()
     K = torch.empty(B, w.num_kv_heads, cap, w.head_dim, dtype=torch.bfloat16, device=dev)
     V = torch.empty_like(K)
+    kv = []  # host copies, kept for the oracle's baseline
     for b, L in enumerate(lengths):
-        for which, dst in (("k", K), ("v", V)):
-            dst[b, :, :L] = torch.from_numpy(WL.kv_slab(w, b, 0, int(L), which).view(np.int16)).view(torch.bfloat16).to(dev)
-    q = torch.from_numpy(np.stack([WL.query_at(w, b, int(L) - 1) for b, L in enumerate(lengths)]).view(np.int16))
-    q = q.view(torch.bfloat16).to(dev)
+        pair = (WL.kv_slab(w, b, 0, int(L), "k"), WL.kv_slab(w, b, 0, int(L), "v"))
+        K[b, :, :L] = torch.from_numpy(pair[0].view(np.int16)).view(torch.bfloat16).to(dev)
+        V[b, :, :L] = torch.from_numpy(pair[1].view(np.int16)).view(torch.bfloat16).to(dev)
+        if cpu_seconds > 0:
+            kv.append(pair)
+    qh = np.stack([WL.query_at(w, b, int(L) - 1) for b, L in enumerate(lengths)])
+    q = torch.from_numpy(qh.view(np.int16)).view(torch.bfloat16).to(dev)
     rows = ra.Rows(q, torch.arange(B, dtype=torch.int32, device=dev), torch.as_tensor(lengths - 1).to(dev), cap - 1)
     mean = torch.zeros(B, w.num_kv_heads, cfg.max_spans, w.head_dim, dtype=torch.float32, device=dev)
     run = torch.zeros(B, w.num_kv_heads, w.head_dim, dtype=torch.float32, device=dev)
@@ -774,59 +881,158 @@ def bench_decode_workload(name, steps, warmup):
             uni = len(set(selh[b, g * G:(g + 1) * G].ravel().tolist()) - {-1})
             rows_kv += uni * S + win
     nbytes = rows_kv * w.head_dim * 2 * 2 + B * w.num_q_heads * w.head_dim * (2 + 4)
+    # + the summary update: the new K row, the running sum read and written, per kv head
+    nbytes += B * w.num_kv_heads * w.head_dim * (2 + 8)
     achieved = nbytes / (attn_ms * 1e-3) / 1e9
+    # the whole step also reads the summaries of every routable span (routing)
+    route_bytes = sum(((int(L) - 1 - w.window + 1) // S) * w.num_kv_heads * w.head_dim * 4 for L in lengths)
+    step_gbs = (nbytes + route_bytes) / (ms * 1e-3) / 1e9
+    gsel, gout = sel.cpu().numpy(), out.cpu().numpy()
     del K, V
     torch.cuda.empty_cache()
+    cpu, check = None, None
+    if cpu_seconds > 0:
+        cpu, check = oracle_decode_baseline(w, kv, lengths, qh, cpu_seconds, gsel, gout)
+        del kv
     return {"workload": name, "sequences": B, "context_max": cap, "span": S, "top_k": w.top_k, "window": w.window,
             "value": round(B * 1000.0 / ms, 2), "unit": "tokens/s", "ms_per_step": round(ms, 5),
             "roofline": {"bound": "hbm",
                      "kernel": "routed_attn_decode_append (decode_attn + merge launch with the token's summary update)",
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": counter_traffic({"decode_10m": "routed_attn_decode_10m",
+                                                     "ragged_decode_16": "routed_attn_decode_ragged16"}[name]),
                          "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_ms": round(attn_ms, 5)},
-            "repeat_bitwise_identical": bool(same), "setup_seconds": round(setup, 1)}
+            "step_roofline": {"bound": "hbm", "what": "the whole step (route + top-k + attention with the update)",
+                              "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                              "algorithmic_bytes_per_step": int(nbytes + route_bytes)},
+            "repeat_bitwise_identical": bool(same), "setup_seconds": round(setup, 1),
+            "cpu_baseline": cpu, "oracle_check": check}
 
 
-def cpu_baseline(w, d0, seconds):
-    """The CPU oracle, untuned, on decode steps of sequence 0 (single thread)."""
-    import threadpoolctl
+# ------------------------------------------------------------------------------ CPU baseline
+BF16 = 1  # synth's code for bf16 inputs
+# The oracle (the plain C++ implementation in oracle/, fp64, one std::thread task per (row, head))
+# timed on the host's cores over a bounded sample of each workload, on the same seeded inputs.
+# Its setup (summaries of the cache that precedes the step) is untimed, as on the GPU.  The
+# oracle's results for the sampled rows are also compared with the GPU's (selection exact or a
+# valid near tie, largest output error).
 
+def _host_cpu():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_check(w, prob, q_rows, positions, gsel, gout):
+    """Oracle vs GPU for rows of one sequence (all heads): selection verdicts and max-abs error."""
     import oracle as O
-    from synth import workloads as WL
 
-    L = w.decode_len
-    kh = WL.kv_slab(w, 0, 0, L, "k")
-    vh = WL.kv_slab(w, 0, 0, L, "v")
-    q = WL.query_at(w, 0, L - 1)
-    with threadpoolctl.threadpool_limits(1):
-        kf = O.widen_f32(kh, True)
-        means, run = O.summaries(kf[:, :L - 1], L - 1, w.span_size, max_spans=L // w.span_size)  # setup, untimed
-        steps, outs = 0, None
-        t0 = time.perf_counter()
-        while True:
-            m2, r2 = means.copy(), run.copy()
-            O.summary_update(kf, m2, r2, L - 1, L, w.span_size)
-            prob = O.Problem(kh, vh, L, w.num_q_heads, w.span_size, w.top_k, w.window, True, means=m2)
-            outs = [prob.row(q[h], h, L - 1) for h in range(w.num_q_heads)]
-            steps += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        el = time.perf_counter() - t0
-    # the oracle's result for this step, compared with the GPU's (selection exact or near-tie)
-    gsel = d0["sel"][0].cpu().numpy()
-    gout = d0["out"][0].cpu().numpy()
-    worst, kinds = 0.0, {"exact": 0, "near_tie": 0, "fail": 0}
-    for h, res in enumerate(outs):
-        r = len(res["scores"])
-        bound = O.score_abs_bound(prob.q64(q[h]), prob.means[h // w.group], r, True)
-        v = O.selection_verdict(gsel[h], res["sel"], res["scores"], w.top_k, bound)
-        kinds["fail" if v.startswith("fail") else v] += 1
-        ref = res["out"] if v == "exact" else prob.row(q[h], h, L - 1, sel=gsel[h])["out"]
-        worst = max(worst, float(np.abs(gout[h] - ref).max()))
-    base = {"value": round(steps / el, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d decode steps of one 1M-token sequence (summary update + 32 rows), numpy float64, "
-                      "1 BLAS thread" % steps}
-    return base, {"selection": kinds, "max_abs_err": worst}
+    res = prob.rows(q_rows, positions, scores=True)
+    kinds, worst = {"exact": 0, "near_tie": 0, "fail": 0}, 0.0
+    mk = [O.round_to_bf16(prob.means[g]) if prob.is_bf16 else prob.means[g] for g in range(prob.hkv)]
+    for i, t in enumerate(positions):
+        for h in range(w.num_q_heads):
+            sc = res["scores"][i][h]
+            bound = O.score_abs_bound(prob.q64(q_rows[i][h]), mk[h // prob.group], len(sc), False)
+            v = O.selection_verdict(gsel[i, h], res["sel"][i, h], sc, w.top_k, bound)
+            kinds["fail" if v.startswith("fail") else v] += 1
+            if v.startswith("fail"):
+                continue
+            ref = res["out"][i, h] if v == "exact" else prob.row(q_rows[i][h], h, int(t), sel=gsel[i, h])["out"]
+            worst = max(worst, O.output_errors(gout[i, h], ref)[0])
+    return kinds, worst
+
+
+def oracle_decode_baseline(w, kv, lengths, q_rows, seconds, gsel=None, gout=None):
+    """Decode steps of the oracle: every sequence's new token folded into its summaries, then its
+    row (all query heads) routed, selected and attended; repeated until `seconds` have passed.
+    kv: per sequence (K, V) host arrays [Hkv][L_b][d]; q_rows [B][Hq][d]."""
+    import oracle.cpp as OC
+
+    threads = OC.default_threads()
+    S = w.span_size
+    base = []
+    for (kh, vh), L in zip(kv, lengths):
+        L = int(L)
+        means, run = OC.summaries(kh, L - 1, S, max_spans=L // S, threads=threads)  # setup, untimed
+        base.append((means, run))
+    steps, probs = 0, None
+    t0 = time.perf_counter()
+    while True:
+        probs = []
+        for b, ((kh, vh), L) in enumerate(zip(kv, lengths)):
+            L = int(L)
+            m2, r2 = base[b][0].copy(), base[b][1].copy()
+            OC.summary_update(kh, m2, r2, L - 1, L, S, threads=threads)
+            prob = OC.Problem(kh, vh, L, w.num_q_heads, S, w.top_k, w.window, True, means=m2, threads=threads)
+            prob.rows(q_rows[b][None], [L - 1])
+            probs.append(prob)
+        steps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    out = {"value": round(steps * len(lengths) / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": "%d decode steps of the %s workload (%d sequence%s: summary update of the new token + %d query "
+                     "heads each), C++ oracle, fp64, %d threads, %s" % (
+                         steps, w.name, len(lengths), "s" if len(lengths) > 1 else "", w.num_q_heads, threads,
+                         _host_cpu())}
+    check = None
+    if gsel is not None:
+        kinds, worst = {"exact": 0, "near_tie": 0, "fail": 0}, 0.0
+        for b, L in enumerate(lengths):
+            k_, w_ = _oracle_check(w, probs[b], q_rows[b][None], [int(L) - 1], gsel[b:b + 1], gout[b:b + 1])
+            for key in kinds:
+                kinds[key] += k_[key]
+            worst = max(worst, w_)
+        check = {"rows": int(len(lengths) * w.num_q_heads), "selection": kinds, "max_abs_err": worst}
+    return out, check
+
+
+def oracle_prefill_baseline(w, kh, vh, prefix, chunk, q, seconds, gsel=None, gout=None, sample_rows=None):
+    """Prefill of the oracle: the chunk's summary update (timed once), then rows of the chunk
+    (all query heads) spread evenly over it, in batches, until `seconds` have passed; the rate is
+    per token of the whole step: 1 / (update time / chunk + row time / rows done)."""
+    import oracle.cpp as OC
+
+    threads = OC.default_threads()
+    S = w.span_size
+    L = prefix + chunk
+    means, run = OC.summaries(kh, prefix, S, max_spans=L // S, threads=threads)  # setup, untimed
+    t0 = time.perf_counter()
+    OC.summary_update(kh, means, run, prefix, L, S, threads=threads)
+    t_upd = time.perf_counter() - t0
+    prob = OC.Problem(kh, vh, L, w.num_q_heads, S, w.top_k, w.window, w.dtype == BF16, means=means,
+                       threads=threads)
+    order = np.argsort((np.arange(chunk) * 0.6180339887498949) % 1.0, kind="stable")  # evenly spread rows
+    if sample_rows is not None:
+        order = order[:sample_rows]
+    done, t_rows = 0, 0.0
+    batch = 16 if chunk > 4096 else chunk
+    while done < len(order):
+        idx = np.sort(order[done:done + batch])
+        t1 = time.perf_counter()
+        prob.rows(q[idx], prefix + idx)
+        t_rows += time.perf_counter() - t1
+        done += len(idx)
+        if t_upd + t_rows >= seconds:
+            break
+    rate = 1.0 / (t_upd / chunk + t_rows / done)
+    out = {"value": round(rate, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": "the %s chunk's summary update (%d tokens) + %d of its %d rows (all %d query heads), "
+                     "C++ oracle, fp64, %d threads, %s" % (w.name, chunk, done, chunk, w.num_q_heads, threads,
+                                                           _host_cpu())}
+    check = None
+    if gsel is not None:
+        idx = np.sort(order[:min(done, 64)])
+        kinds, worst = _oracle_check(w, prob, q[idx], prefix + idx, gsel[idx], gout[idx])
+        check = {"rows": int(len(idx) * w.num_q_heads), "selection": kinds, "max_abs_err": worst}
+    return out, check
 
 
 if __name__ == "__main__":

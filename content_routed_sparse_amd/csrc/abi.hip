@@ -35,6 +35,7 @@ ra_status hip_status(hipError_t e, const char *what) {
 }
 
 constexpr int64_t kMaxGrid = 0x7fffffffLL;
+constexpr int64_t kMaxItems = 1LL << 32;  // work-items (blocks x threads) per grid dimension
 
 ra_status check_config(const ra_config *c) {
     if (!c) return fail(RA_EINVAL, "cfg is NULL");
@@ -89,7 +90,7 @@ ra::RowArgs row_args(const ra_config *c, const ra_rows *r) {
 }
 
 ra_status check_attn(const ra_config *c, const ra_rows *r, const void *k, const void *v, const int32_t *sel,
-                     const float *out, const void *ws, size_t ws_bytes, int op) {
+                     const float *out, const void *ws, size_t ws_bytes, int op, bool fp8 = false) {
     ra_status s = check_config(c);
     if (s) return s;
     if ((s = check_rows(c, r))) return s;
@@ -97,14 +98,20 @@ ra_status check_attn(const ra_config *c, const ra_rows *r, const void *k, const 
     const ra::RowArgs a = row_args(c, r);
     const int NW = ra::max_window_spans(a.S, a.W);
     if (op == RA_OP_DECODE) {
-        const int64_t nsub = ra::ceil_div(a.S, 64);  // upper bound on sub-tiles per span
-        if (a.n_rows * a.Hkv * (int64_t)(a.G * a.k + NW) * nsub >= kMaxGrid)
+        // (a bound in double first, so that the exact count below stays far inside int64)
+        if ((double)a.n_rows * a.Hkv * (double)(a.G * a.k + NW) * (double)a.S >= 0x1p52)
             return fail(RA_EUNSUPPORTED, "decode grid too large: use fewer rows per call");
+        if (ra::decode_grid_items(a, fp8) >= kMaxItems)
+            return fail(RA_EUNSUPPORTED, "decode grid of %lld work-items exceeds 2^32: use fewer rows per call",
+                        (long long)ra::decode_grid_items(a, fp8));
     } else {
         if (a.n_rows * a.Hq * (int64_t)(a.k + NW) >= kMaxGrid)
             return fail(RA_EUNSUPPORTED, "prefill has more than 2^31 (row, head, span) entries: split the chunk");
         if ((int64_t)a.B * a.Hkv * ra::ceil_div(a.cap, a.S) >= kMaxGrid)
             return fail(RA_EUNSUPPORTED, "too many (sequence, kv head, span) buckets");
+        if (ra::prefill_grid_items(a) >= kMaxItems)
+            return fail(RA_EUNSUPPORTED, "prefill grid of %lld work-items exceeds 2^32: split the chunk",
+                        (long long)ra::prefill_grid_items(a));
     }
     const size_t need = op == RA_OP_DECODE ? ra::decode_workspace_bytes(a) : ra::prefill_workspace_bytes(a);
     if (r->n_rows > 0 && (!ws || ws_bytes < need))
@@ -271,7 +278,7 @@ ra_status routed_attn_decode_fp8(const ra_config *cfg, const ra_rows *rows, cons
                                  const uint8_t *v_codes, const float *k_scales, const float *v_scales,
                                  const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
                                  void *stream) {
-    ra_status s = check_attn(cfg, rows, k_codes, v_codes, sel, out, workspace, workspace_bytes, RA_OP_DECODE);
+    ra_status s = check_attn(cfg, rows, k_codes, v_codes, sel, out, workspace, workspace_bytes, RA_OP_DECODE, true);
     if (s) return s;
     if (cfg->dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "8-bit caches go with bf16 queries (cfg->dtype RA_BF16)");
     if (rows->n_rows > 0 && (!k_scales || !v_scales)) return fail(RA_EINVAL, "NULL k_scales or v_scales");
@@ -745,7 +752,7 @@ ra_status routed_attn_decode_fp8_append(const ra_config *cfg, const ra_rows *row
                                         const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
                                         float *span_mean, float *run_sum, const int64_t *old_len,
                                         const int64_t *new_len, int64_t max_new_tokens, void *stream) {
-    ra_status s = check_attn(cfg, rows, k_codes, v_codes, sel, out, workspace, workspace_bytes, RA_OP_DECODE);
+    ra_status s = check_attn(cfg, rows, k_codes, v_codes, sel, out, workspace, workspace_bytes, RA_OP_DECODE, true);
     if (s) return s;
     if (cfg->dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "8-bit caches go with bf16 queries (cfg->dtype RA_BF16)");
     if (rows->n_rows > 0 && (!k_scales || !v_scales)) return fail(RA_EINVAL, "NULL k_scales or v_scales");

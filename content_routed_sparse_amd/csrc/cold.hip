@@ -517,6 +517,15 @@ __global__ void __launch_bounds__(kAttnWaves * 64) cold_attn(const T *__restrict
     const int64_t row = rh / Hq;
     const int h = (int)(rh % Hq), g = h / G;
     if (tid < kc) ssel[tid] = sel[rh * kc + tid];
+    __syncthreads();
+    // a position repeated in the selection counts once, at its first entry
+    bool dup = false;
+    if (tid < kc) {
+        const int32_t p = ssel[tid];
+        for (int x = 0; x < tid; ++x) dup = dup || ssel[x] == p;
+    }
+    __syncthreads();
+    if (dup) ssel[tid] = -1;
     int64_t t = row_pos[row];
     t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
     int seq = row_seq[row];

@@ -607,4 +607,14 @@ hipError_t launch_decode_fp8(const RowArgs &a, const uint8_t *K8, const uint8_t 
     return launch_decode_fp8_app(a, K8, V8, ks, vs, sel, out, ws, nullptr, st);
 }
 
+int64_t decode_grid_items(const RowArgs &a, bool fp8) {
+    const int NW = max_window_spans(a.S, a.W);
+    const int64_t tk = fp8 ? (int64_t)kDecodeWavesFp8 * 64 : decode_sub_tile(a);  // keys per unit
+    const int waves = fp8 ? kDecodeWavesFp8 : kDecodeWaves;
+    const int64_t units = a.n_rows * a.Hkv * (int64_t)(a.G * a.k + NW) * ceil_div(a.S, tk);
+    const int64_t merge = (a.n_rows * a.Hq + (int64_t)a.B * a.Hkv) * kCombineWaves * 64;
+    const int64_t attn = units * waves * 64;
+    return attn > merge ? attn : merge;
+}
+
 }  // namespace ra

@@ -45,6 +45,9 @@ hipError_t launch_topk(const RowArgs &a, const float *scores, int64_t stride, in
 
 // Decode: workspace holds partial records [n_rows][Hq][k + max_window_spans][n_sub].
 size_t decode_workspace_bytes(const RowArgs &a);
+// Work-items (blocks x threads) of the largest launch of a decode call (bf16/fp32 cache, or the
+// 8-bit cache with fp8 = true); a launch needs fewer than 2^32 per grid dimension.
+int64_t decode_grid_items(const RowArgs &a, bool fp8);
 hipError_t launch_decode(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out,
                          void *ws, hipStream_t st);
 // Decode over an 8-bit cache (bf16 queries): codes K8/V8 with row scales ks/vs.
@@ -53,6 +56,7 @@ hipError_t launch_decode_fp8(const RowArgs &a, const uint8_t *K8, const uint8_t 
 
 // Prefill: span-major dispatch + tiles + merge.
 size_t prefill_workspace_bytes(const RowArgs &a);
+int64_t prefill_grid_items(const RowArgs &a);  // as decode_grid_items
 hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out,
                           void *ws, hipStream_t st);
 

@@ -7,9 +7,11 @@
 // (sequence, kv head, span).  Buckets are cut into tiles of at most MT entries, a tile runs as
 // one block over the span's keys (a dense Q.K^T / softmax / P.V on MFMA for bf16), and the
 // per-span partial softmax states are merged per row in fixed order by the combine kernel.
-// Keys after a row's own position are masked (only window spans can contain them).  Results do
-// not depend on the order of entries inside a bucket: every row's state is computed from its
-// own query and the span's keys alone.
+// Keys after a row's own position are masked (only window spans can contain them).  Slots in a
+// bucket are handed out by atomics, so which entries share a tile varies from run to run; the
+// results do not: every entry's partial state is computed from its own query and the span's
+// keys alone (the tile kernels decide a second pass per entry, not per tile), and the merge
+// adds a row's records in entry order.
 //
 // Workspace (all offsets 256-byte aligned):
 //   counts[n_exp+1], offsets[n_exp+1], tile_off[n_exp+1]   int32
@@ -58,16 +60,29 @@ __global__ void fill_i32(int32_t *p, int64_t n, int32_t v) {
     if (i < n) p[i] = v;
 }
 
-// span id of entry e of a row-head; false if the entry attends to nothing
+// span id of entry e of a row-head; false if the entry attends to nothing: a selected span
+// (e < k) outside [0, r(t)) or equal to an earlier entry of the same row-head, or a window span
+// (e >= k) that starts after t.  (Selections from topk_spans are ascending and distinct; the
+// repeat check serves caller-made selections, whose first occurrence counts, as in decode.)
 __device__ __forceinline__ bool entry_span(const int32_t *sel, int64_t rh, int e, int k, int64_t t, int S, int W,
                                            int64_t &j) {
     const int64_t w0 = window_start(t, S, W);
     if (e < k) {
-        j = sel[rh * k + e];
-        return j >= 0 && j < div_nonneg(w0, S);
+        const int32_t *row = sel + rh * k;
+        j = row[e];
+        if (j < 0 || j >= div_nonneg(w0, S)) return false;
+        for (int x = 0; x < e; ++x)
+            if (row[x] == j) return false;
+        return true;
     }
     j = div_nonneg(w0, S) + (e - k);
     return j * S <= t;
+}
+
+// span id of an entry that entry_span accepted (no checks)
+__device__ __forceinline__ int64_t valid_entry_span(const int32_t *sel, int64_t rh, int e, int k, int64_t t, int S,
+                                                    int W) {
+    return e < k ? (int64_t)sel[rh * k + e] : div_nonneg(window_start(t, S, W), S) + (e - k);
 }
 
 __global__ void count_kernel(const int32_t *__restrict__ sel, const int32_t *__restrict__ row_seq,
@@ -149,9 +164,7 @@ __global__ void __launch_bounds__(256) count_kernel_lds(const int32_t *__restric
         if (v >= 0) {
             int64_t t = row_pos[row];
             t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
-            int64_t j;
-            entry_span(sel, rh, e, k, t, S, W, j);
-            local[x] = hist[j] + v;
+            local[x] = hist[valid_entry_span(sel, rh, e, k, t, S, W)] + v;
         } else if (v <= -2) {
             local[x] = -2 - v;  // slot taken directly in the global counter
         }
@@ -219,8 +232,7 @@ __global__ void scatter_kernel(const int32_t *__restrict__ sel, const int32_t *_
     t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
     int seq = row_seq[row];
     seq = seq < 0 ? 0 : (seq >= B ? B - 1 : seq);
-    int64_t j;
-    entry_span(sel, rh, e, k, t, S, W, j);
+    const int64_t j = valid_entry_span(sel, rh, e, k, t, S, W);
     const int64_t expert = ((int64_t)seq * Hkv + g) * span_slots + j;
     list[offsets[expert] + slot] = (int32_t)x;
     list_t[offsets[expert] + slot] = t;
@@ -239,15 +251,8 @@ __global__ void tiles_kernel(const int32_t *__restrict__ counts, const int32_t *
 }
 
 
-// Records of one row-head: entry e < k is the selected span sel[e] (no record unless 0 <= j <
-// r), entry k + w is window span w0/S + w (no record once it starts after t).
-__device__ __forceinline__ bool record_valid(const int32_t *sel_rh, int e, int64_t t, int64_t w0, int S, int k) {
-    if (e < k) {
-        const int64_t j = sel_rh[e];
-        return j >= 0 && j < div_nonneg(w0, S);
-    }
-    return w0 + (int64_t)(e - k) * S <= t;
-}
+// A record exists for entry x of a row-head iff the dispatch gave the entry a slot (local >= 0):
+// the same test as entry_span, taken once by the count kernel.
 
 constexpr int kRecBatch = 8;
 
@@ -275,21 +280,16 @@ __device__ __forceinline__ void load_slice(const float *rec, int lane, float (&v
 //   fp32 records (m, l, -, -, o[d]):       out = sum 2^(m - M) o / sum 2^(m - M) l
 //   fp16 records (m, l, s, -, h[d]), h = o / (l s):  o = 2^(m - M) l s h in the same sums
 template <int D, bool HALF>
-__global__ void __launch_bounds__(256) combine_wave(const float *__restrict__ part, const int32_t *__restrict__ sel,
-                                                    const int64_t *__restrict__ row_pos, float *__restrict__ out,
-                                                    int64_t n_rowheads, int Hq, int S, int k, int W, int64_t max_pos,
-                                                    int NW) {
+__global__ void __launch_bounds__(256) combine_wave(const float *__restrict__ part, const int32_t *__restrict__ local,
+                                                    float *__restrict__ out, int64_t n_rowheads, int k, int NW) {
     constexpr int PER = D / 64;
     constexpr int RW = prefill_record_words(D, HALF);
     constexpr float kNegInf = -__builtin_huge_valf();
     const int lane = threadIdx.x & 63;
     const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (rh >= n_rowheads) return;
-    int64_t t = row_pos[rh / Hq];
-    t = t < 0 ? 0 : (t > max_pos ? max_pos : t);
-    const int64_t w0 = window_start(t, S, W);
     const int nrec = k + NW;
-    const int32_t *sel_rh = sel + rh * k;
+    const int32_t *valid_rh = local + rh * (int64_t)nrec;  // slot of each entry, -1: no record
     const float *base = part + rh * (int64_t)nrec * RW;
 
     // lane x holds record x's (m, l, s) (one round trip for up to 64 records); invalid: m = -inf
@@ -299,7 +299,7 @@ __global__ void __launch_bounds__(256) combine_wave(const float *__restrict__ pa
         const int x = x0 + lane;
         const int xc = x < nrec ? x : nrec - 1;
         const float4 h = *reinterpret_cast<const float4 *>(base + (int64_t)xc * RW);
-        const bool ok = x < nrec && record_valid(sel_rh, x, t, w0, S, k);
+        const bool ok = x < nrec && valid_rh[xc] >= 0;
         const float m = ok ? h.x : kNegInf;
         if (x0 == 0) {
             mine_m = m;
@@ -334,7 +334,7 @@ __global__ void __launch_bounds__(256) combine_wave(const float *__restrict__ pa
                 sx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine_s), x));
             } else {
                 const float4 h = *reinterpret_cast<const float4 *>(base + (int64_t)x * RW);
-                m = record_valid(sel_rh, x, t, w0, S, k) ? h.x : kNegInf;
+                m = valid_rh[x] >= 0 ? h.x : kNegInf;
                 lx = h.y;
                 sx = h.z;
             }
@@ -356,20 +356,20 @@ __global__ void __launch_bounds__(256) combine_wave(const float *__restrict__ pa
 }
 
 template <int D, bool HALF>
-hipError_t launch_combine_t(const RowArgs &a, const float *part, const int32_t *sel, float *out, hipStream_t st) {
+hipError_t launch_combine_t(const RowArgs &a, const float *part, const int32_t *local, float *out, hipStream_t st) {
     const int64_t n = a.n_rows * a.Hq;
-    hipLaunchKernelGGL((combine_wave<D, HALF>), dim3((unsigned)ceil_div(n, 4)), dim3(256), 0, st, part, sel,
-                       a.row_pos, out, n, a.Hq, a.S, a.k, a.W, a.max_pos, max_window_spans(a.S, a.W));
+    hipLaunchKernelGGL((combine_wave<D, HALF>), dim3((unsigned)ceil_div(n, 4)), dim3(256), 0, st, part, local, out, n,
+                       a.k, max_window_spans(a.S, a.W));
     return hipGetLastError();
 }
 
 // Records of entries that attend to nothing are never written, so the merge checks validity.
-hipError_t launch_combine(const RowArgs &a, const float *part, const int32_t *sel, float *out, hipStream_t st) {
+hipError_t launch_combine(const RowArgs &a, const float *part, const int32_t *local, float *out, hipStream_t st) {
     if (a.dtype == RA_BF16)
-        return a.d == 64 ? launch_combine_t<64, true>(a, part, sel, out, st)
-                         : launch_combine_t<128, true>(a, part, sel, out, st);
-    return a.d == 64 ? launch_combine_t<64, false>(a, part, sel, out, st)
-                     : launch_combine_t<128, false>(a, part, sel, out, st);
+        return a.d == 64 ? launch_combine_t<64, true>(a, part, local, out, st)
+                         : launch_combine_t<128, true>(a, part, local, out, st);
+    return a.d == 64 ? launch_combine_t<64, false>(a, part, local, out, st)
+                     : launch_combine_t<128, false>(a, part, local, out, st);
 }
 
 }  // namespace
@@ -377,6 +377,15 @@ hipError_t launch_combine(const RowArgs &a, const float *part, const int32_t *se
 size_t prefill_workspace_bytes(const RowArgs &a) { return prefill_layout(a).total; }
 
 int64_t prefill_entry_count(const RowArgs &a) { return prefill_layout(a).n_ent; }
+
+int64_t prefill_grid_items(const RowArgs &a) {
+    const PrefillLayout L = prefill_layout(a);
+    const int64_t tiles = L.max_tiles * 256;                         // tile kernels: 256 threads
+    const int64_t merge = ceil_div(a.n_rows * a.Hq, 4) * 256;        // combine_wave: 4 row-heads per block
+    const int64_t count = ceil_div(L.n_ent, 256) * 256;              // count / scatter: one thread per entry
+    int64_t m = tiles > merge ? tiles : merge;
+    return m > count ? m : count;
+}
 
 hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out, void *ws,
                           hipStream_t st) {
@@ -416,7 +425,7 @@ hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const 
     TileArgs ta{a, K, V, tile_off, list, list_t, tiles, records, L.n_exp, L.max_tiles, L.span_slots, NE};
     e = launch_prefill_tiles(ta, st);
     if (e != hipSuccess) return e;
-    return launch_combine(a, records, sel, out, st);
+    return launch_combine(a, records, local, out, st);
 }
 
 }  // namespace ra

@@ -2,13 +2,16 @@
 // one (sequence, kv head); the tile produces each pair's partial softmax state over the span's
 // keys (masked to keys <= the row's position).
 //
-// tile_mfma (bf16): a block takes up to 128 entries (4 waves x 32 rows) and streams the span's
-// keys through LDS in chunks of 32: K row-major, V transposed, so that both products run on
-// v_mfma_f32_16x16x32_bf16 -- S = Q K^T (gathered query rows as the A operand, kept in
-// registers) and O += P V (P rounded to bf16 through a per-wave LDS tile).  The softmax is
-// online, per row, with DPP reductions across the 16 lanes that hold a row's scores.
-// Tiles of one span are consecutive in the tile list and are spread over the 8 XCDs in
-// contiguous ranges, so the blocks that reread a span's keys share an L2.
+// tile_mfma (bf16): a block of 4 waves takes up to 128 entries (each wave two groups of 16
+// queries) and streams the span's keys through LDS in chunks of 64, loaded straight from
+// global memory into LDS (K rows and V rows, XOR-swizzled), double-buffered.  The products run
+// transposed on v_mfma_f32_16x16x32_bf16: S^T = K Q^T (the gathered query rows are the B operand,
+// kept in registers), so each lane owns one query's scores and its softmax state, and
+// O^T += V^T P^T takes P (rounded to bf16) straight from the S^T registers, with V^T read by
+// transposed LDS reads.  Each query keeps one reference maximum fixed by its first chunk;
+// an entry whose row sum then overflows the fast range gets a second pass with its exact
+// maximum (decided per entry).  Tiles of one span are consecutive in the tile list and are
+// spread over the 8 XCDs in contiguous ranges, so the blocks that reread a span's keys share an L2.
 //
 // tile_valu: one wave per entry, keys streamed in chunks of KPW rows with an online softmax
 // (fp32 inputs).  The span's rows are shared by the tile's entries through the caches.
@@ -617,12 +620,60 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     for (int g = 0; g < kQG; ++g) unset[g] = NEG;
     reset(unset);
     fast_sweep<D>(st, tk, true, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
-    // a valid query whose row sum passed 2^kFastLog2 (or is not finite) sends the tile to a
-    // second pass; block-wide decision (every wave takes the same path through the chunk loads)
-    bool redo_q = false;
+
+    // records: header (m, l, s, 0), then o / (l s) as fp16 per valid row, s = 2^-k with k chosen
+    // so that the row's largest |o / l| lands in [2^14, 2^15): every value keeps 11 significant
+    // bits relative to that maximum, and the records take half the bytes of fp32 ones.  Lane
+    // (lg, lr) holds o[16et + 4lg + i] of query lr.  Only the entries flagged in `which` store.
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+    auto store = [&](const bool (&which)[kQG]) {
 #pragma unroll
-    for (int g = 0; g < kQG; ++g) redo_q = redo_q || (x_own[g] >= 0 && !(group_sum4(l[g]) <= kFastLimit));
-    const bool wave_redo = __ballot(redo_q) != 0;  // (all lanes vote: a ballot counts active lanes only)
+        for (int g = 0; g < kQG; ++g) {
+            const float lt = group_sum4(l[g]);
+            const float inv = 1.f / lt;
+            float amax = 0.f;
+#pragma unroll
+            for (int et = 0; et < ET; ++et)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[g][et][i] * inv));
+            amax = group_max4(amax);
+            int k2 = 0;
+            if (amax > 0.f && amax <= 3.4028234663852886e38f) {
+                k2 = 14 - ((int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127);
+                k2 = k2 < -126 ? -126 : (k2 > 126 ? 126 : k2);
+            }
+            const float c = inv * __uint_as_float((uint32_t)(127 + k2) << 23);
+            if (which[g]) {
+                float *rec = records + (int64_t)x_own[g] * prefill_record_words(D, true);
+                uint32_t *hv = reinterpret_cast<uint32_t *>(rec + 4);
+#pragma unroll
+                for (int et = 0; et < ET; ++et) {
+                    const half2_t lo = {(_Float16)(o[g][et][0] * c), (_Float16)(o[g][et][1] * c)};
+                    const half2_t hi = {(_Float16)(o[g][et][2] * c), (_Float16)(o[g][et][3] * c)};
+                    *reinterpret_cast<uint2 *>(hv + (16 * et + 4 * lg) / 2) =
+                        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                }
+                if (lg == 0)
+                    *reinterpret_cast<float4 *>(rec) =
+                        make_float4(m[g], lt, __uint_as_float((uint32_t)(127 - k2) << 23), 0.f);
+            }
+        }
+    };
+
+    // Each entry decides on its own whether it needs the second pass: its row sum passed
+    // 2^kFastLog2 (or is not finite).  Entries that do not store their records now, and keep
+    // them, so an entry's result never depends on which other entries share its tile.  The
+    // pass itself runs for the whole block (every wave takes the same path through the loads).
+    bool need[kQG], done[kQG];
+    bool need_any = false;
+#pragma unroll
+    for (int g = 0; g < kQG; ++g) {
+        need[g] = x_own[g] >= 0 && !(group_sum4(l[g]) <= kFastLimit);
+        done[g] = x_own[g] >= 0 && !need[g];
+        need_any = need_any || need[g];
+    }
+    store(done);
+    const bool wave_redo = __ballot(need_any) != 0;  // (all lanes vote: a ballot counts active lanes only)
     if (lane == 0) redo_s[wave] = wave_redo ? 1 : 0;
     __syncthreads();
     int redo = 0;
@@ -635,42 +686,7 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
         max_sweep<D>(st, tk, qlim, kof, qb, mx, wave, lane, lg, scale_log2);
         reset(mx);
         fast_sweep<D>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
-    }
-
-    // records: header (m, l, s, 0), then o / (l s) as fp16 per valid row, s = 2^-k with k chosen
-    // so that the row's largest |o / l| lands in [2^14, 2^15): every value keeps 11 significant
-    // bits relative to that maximum, and the records take half the bytes of fp32 ones.  Lane
-    // (lg, lr) holds o[16et + 4lg + i] of query lr.
-    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-#pragma unroll
-    for (int g = 0; g < kQG; ++g) {
-        const float lt = group_sum4(l[g]);
-        const float inv = 1.f / lt;
-        float amax = 0.f;
-#pragma unroll
-        for (int et = 0; et < ET; ++et)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[g][et][i] * inv));
-        amax = group_max4(amax);
-        int k2 = 0;
-        if (amax > 0.f && amax <= 3.4028234663852886e38f) {
-            k2 = 14 - ((int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127);
-            k2 = k2 < -126 ? -126 : (k2 > 126 ? 126 : k2);
-        }
-        const float c = inv * __uint_as_float((uint32_t)(127 + k2) << 23);
-        if (x_own[g] >= 0) {
-            float *rec = records + (int64_t)x_own[g] * prefill_record_words(D, true);
-            uint32_t *hv = reinterpret_cast<uint32_t *>(rec + 4);
-#pragma unroll
-            for (int et = 0; et < ET; ++et) {
-                const half2_t lo = {(_Float16)(o[g][et][0] * c), (_Float16)(o[g][et][1] * c)};
-                const half2_t hi = {(_Float16)(o[g][et][2] * c), (_Float16)(o[g][et][3] * c)};
-                *reinterpret_cast<uint2 *>(hv + (16 * et + 4 * lg) / 2) =
-                    make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-            }
-            if (lg == 0)
-                *reinterpret_cast<float4 *>(rec) = make_float4(m[g], lt, __uint_as_float((uint32_t)(127 - k2) << 23), 0.f);
-        }
+        store(need);
     }
 }
 

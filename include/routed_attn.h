@@ -147,7 +147,9 @@ ra_status routed_attn_decode(const ra_config *cfg, const ra_rows *rows, const vo
  * routed_attn_prefill -- the same result for many rows (a chunk of new tokens, causal in the
  * chunk).  Rows are grouped span by span (every (sequence, kv head, span) gathers the rows
  * that attend to it, as selected span or as window span), each group runs as dense tiles over
- * the span's keys, and the per-span partial states are merged per row.
+ * the span's keys, and the per-span partial states are merged per row in entry order.  A row's
+ * result does not depend on the other rows of the call.  Entries of `sel` outside [0, r(t))
+ * are ignored, and so is an entry that repeats an earlier entry of the same (row, head).
  *   workspace      at least ra_workspace_bytes(cfg, RA_OP_PREFILL, n_rows, max_pos) bytes.
  */
 ra_status routed_attn_prefill(const ra_config *cfg, const ra_rows *rows, const void *k_cache, const void *v_cache,
@@ -257,7 +259,8 @@ ra_status cold_select(const ra_config *cfg, const ra_rows *rows, const uint8_t *
 
 /* cold_attn_decode -- exact attention of each row over its selected cold positions and its hot
  * window; out as above.  Entries outside the row's cold set [0, t-H+1) (the -1 padding among
- * them) are ignored, so no position is counted twice. */
+ * them) are ignored, and so is an entry that repeats an earlier entry of the same row-head, so
+ * no position is counted twice. */
 ra_status cold_attn_decode(const ra_config *cfg, const ra_rows *rows, const void *k_cache, const void *v_cache,
                            const int32_t *sel_cold, int32_t hot_window, int32_t top_k_cold, float *out, void *stream);
 

@@ -234,6 +234,55 @@ class Problem:
         o, _ = attend(self.q64(q_row_h), self.keys[g], self.values[g], np.arange(t + 1), self.is_bf16)
         return o
 
+    def tasks(self, qvecs, heads, positions, sel=None, dense=False, scores=False):
+        """Many (query vector, head, position) tasks, one after another; the same results as the
+        C++ oracle's Problem.tasks.  A given selection keeps only the first occurrence of each
+        routable span id (ids outside [0, r(t)) and repeats attend nothing)."""
+        n = len(positions)
+        out = np.zeros((n, self.d))
+        sel_out = np.full((n, self.k), NO_SPAN, dtype=np.int64)
+        wsum = np.zeros(n)
+        n_att = np.zeros(n, dtype=np.int64)
+        sc = []
+        for i in range(n):
+            hq, t = int(heads[i]), int(positions[i])
+            if dense:
+                out[i] = self.dense_row(qvecs[i], hq, t)
+                wsum[i], n_att[i] = 1.0, t + 1
+                continue
+            use = None
+            if sel is not None:
+                r = num_routable(t, self.S, self.W)
+                use = []
+                for j in np.asarray(sel[i]).tolist():
+                    if 0 <= j < r and j not in use:
+                        use.append(j)
+                use = np.array(sorted(use), dtype=np.int64)
+            res = self.row(qvecs[i], hq, t, sel=use)
+            out[i], sel_out[i], wsum[i], n_att[i] = res["out"], res["sel"], res["weight_sum"], res["n_attended"]
+            sc.append(res["scores"])
+        res = {"out": out, "sel": sel_out, "weight_sum": wsum, "n_attended": n_att}
+        if scores:
+            res["scores"] = sc
+        return res
+
+    def rows(self, q_rows, positions, heads=None, sel=None, dense=False, scores=False):
+        """Every head in `heads` (default all) of rows q_rows[i] ([Hq][d]) at positions[i],
+        shaped [n][len(heads)] as the C++ oracle's Problem.rows."""
+        heads = list(range(self.hq)) if heads is None else list(heads)
+        n, nh = len(positions), len(heads)
+        q_rows = np.asarray(q_rows)
+        qv = [q_rows[i][h] for i in range(n) for h in heads]
+        hh = [h for _ in range(n) for h in heads]
+        pp = [int(positions[i]) for i in range(n) for _ in heads]
+        sl = None if sel is None else np.asarray(sel).reshape(n * nh, self.k)
+        res = self.tasks(qv, hh, pp, sel=sl, dense=dense, scores=scores)
+        shaped = {"out": res["out"].reshape(n, nh, self.d), "sel": res["sel"].reshape(n, nh, self.k),
+                  "weight_sum": res["weight_sum"].reshape(n, nh), "n_attended": res["n_attended"].reshape(n, nh)}
+        if scores:
+            shaped["scores"] = [res["scores"][i * nh:(i + 1) * nh] for i in range(n)]
+        return shaped
+
 
 def routed_rows(problem, q_rows, positions, heads=None):
     """Routed attention for rows q_rows[i] ([Hq][d]) at positions[i]; returns (out, sel).

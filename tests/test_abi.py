@@ -229,3 +229,23 @@ def test_cold_entry_points_validate_before_launch():
     assert lib.kv_signature_update(ctypes.byref(cc), FAKE, None, op, op, 1, None) == 1
     assert lib.kv_signature_update(ctypes.byref(cc), FAKE, ctypes.c_void_p(0x1008), op, op, 1, None) == 1  # alignment
     assert lib.kv_signature_update(ctypes.byref(cc), FAKE, FAKE, op, op, (1 << 20) + 1, None) == 3
+
+
+def test_grid_limits_are_checked_before_launch():
+    """A launch needs fewer than 2^32 work-items (blocks x threads) per grid dimension.  A
+    chunk-sized call through the decode entry point (8192 rows, 4 kv heads, 130 slots, 4
+    sub-tiles: 17.04M units of 256 threads) is rejected on the host as unsupported, while the
+    same call with 4096 rows (8.52M units) passes validation and fails only on the workspace."""
+    lib = ra.lib()
+    c = cfg(capacity=(1 << 20) + 8192).c()
+    big_ws = ctypes.c_size_t(1 << 62)
+    st = lib.routed_attn_decode(ctypes.byref(c), ctypes.byref(rows(8192, (1 << 20) + 8191)), FAKE, FAKE, FAKE, FAKE,
+                                FAKE, big_ws, None)
+    assert st == 2 and "2^32" in lib.ra_last_error().decode()
+    st = lib.routed_attn_decode(ctypes.byref(c), ctypes.byref(rows(4096, (1 << 20) + 8191)), FAKE, FAKE, FAKE, FAKE,
+                                FAKE, 16, None)
+    assert st == 3
+    # the 8-bit entry point has the same units
+    st = lib.routed_attn_decode_fp8(ctypes.byref(c), ctypes.byref(rows(8192, (1 << 20) + 8191)), FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, FAKE, FAKE, big_ws, None)
+    assert st == 2

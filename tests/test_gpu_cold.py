@@ -160,3 +160,36 @@ def test_cold_retrieval_at_1m():
     rows, q = c.rows_for([0], [L - 1])
     c.run(rows)
     c.check([0], [L - 1], q)
+
+
+def test_cold_attn_ignores_repeated_and_out_of_set_entries():
+    """cold_attn_decode on a hand-made selection with repeated positions, -1 and positions of the
+    hot window (outside the cold set): each distinct cold position is attended once."""
+    w = small("decode_1m", num_q_heads=8, num_kv_heads=2, decode_len=5000)
+    H, kc = 64, 16
+    c = ColdCase(w, [5000], H, kc)
+    t = 4999
+    rows, q = c.rows_for([0], [t])
+    n_cold = t - H + 1
+    rng = np.random.default_rng(23)
+    sel = np.empty((1, w.num_q_heads, kc), dtype=np.int32)
+    for h in range(w.num_q_heads):
+        pool = rng.choice(n_cold, size=6, replace=False)
+        row = rng.choice(pool, size=kc)
+        row[rng.random(kc) < 0.2] = -1
+        row[rng.random(kc) < 0.1] = n_cold + rng.integers(0, H)  # a hot position: not cold
+        sel[0, h] = row
+    out = torch.full((1, w.num_q_heads, w.head_dim), np.nan, dtype=torch.float32, device="cuda")
+    ra.cold_attn_decode(c.cfg, rows, c.K, c.V, torch.as_tensor(sel).cuda(), H, kc, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    prob = c.cold_problem(0)
+    for h in range(w.num_q_heads):
+        used = []
+        for p in sel[0, h]:
+            if 0 <= p < n_cold and p not in used:
+                used.append(int(p))
+        ref = prob.row(q[0][h], h, t, sel=np.array(sorted(used), dtype=np.int64))
+        assert ref["n_attended"] == len(used) + H
+        ma, rel = O.output_errors(got[0, h], ref["out"])
+        assert ma <= O.compare.TOL_ABS["bf16"] and rel <= O.compare.TOL_REL_L2_BF16, (h, ma, rel)

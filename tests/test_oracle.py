@@ -583,3 +583,24 @@ def test_fp8_problem_reads_the_dequantised_cache():
             assert np.array_equal(a["scores"], O.route_scores(O.widen(qb[h], True), probf.means[h // 2],
                                                               len(a["scores"]), True))
 
+
+
+def test_numpy_rows_and_tasks_match_the_cpp_oracle():
+    """The numpy oracle's batch interface (used by the 8-bit cache oracle) gives the C++
+    oracle's results, including a given selection with repeats and unroutable ids."""
+    rng = np.random.default_rng(41)
+    L, S, W, k, d, hkv, hq = 500, 16, 16, 4, 16, 2, 4
+    keys = bf16_bits(rng.standard_normal((hkv, L, d)).astype(np.float32))
+    vals = bf16_bits(rng.standard_normal((hkv, L, d)).astype(np.float32))
+    qs = bf16_bits(rng.standard_normal((6, hq, d)).astype(np.float32))
+    pos = np.array([0, 40, 200, 333, 450, 499])
+    pn, pc = O.Problem(keys, vals, L, hq, S, k, W, True), CPP.Problem(keys, vals, L, hq, S, k, W, True)
+    a, b = pn.rows(qs, pos, scores=True), pc.rows(qs, pos, scores=True)
+    assert np.array_equal(a["sel"], b["sel"]) and np.array_equal(a["n_attended"], b["n_attended"])
+    assert np.abs(a["out"] - b["out"]).max() <= 1e-12
+    given = np.tile(np.array([3, 3, -1, 99, 1, 0, 3, 2])[:k], (6, hq, 1))
+    a, b = pn.rows(qs, pos, sel=given), pc.rows(qs, pos, sel=given)
+    assert np.array_equal(a["n_attended"], b["n_attended"])
+    assert np.abs(a["out"] - b["out"]).max() <= 1e-12
+    d1, d2 = pn.rows(qs, pos, dense=True), pc.rows(qs, pos, dense=True)
+    assert np.abs(d1["out"] - d2["out"]).max() <= 1e-12
