@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(HERE, "libroutedattn.so")
 RA_F32, RA_BF16 = 0, 1
 RA_OP_DECODE, RA_OP_PREFILL = 0, 1
 EXPORTED = ("span_summary_update", "route_scores", "topk_spans", "routed_attn_decode", "routed_attn_prefill",
+            "routed_attn_decode_noalloc",
             "attn_dense_causal", "kv_quantize_fp8", "span_summary_update_fp8", "routed_attn_decode_fp8",
             "routed_attn_decode_append", "routed_attn_decode_fp8_append",
             "kv_signature_update", "ra_cold_workspace_bytes", "cold_select", "cold_attn_decode",
@@ -74,6 +75,7 @@ def lib():
             "route_scores": [CP, RP, P, P, I64, P],
             "topk_spans": [CP, RP, P, I64, P, P],
             "routed_attn_decode": [CP, RP, P, P, P, P, P, SZ, P],
+            "routed_attn_decode_noalloc": [CP, RP, P, P, P, P, P],
             "routed_attn_prefill": [CP, RP, P, P, P, P, P, SZ, P],
             "attn_dense_causal": [CP, RP, P, P, P, P],
             "kv_quantize_fp8": [CP, P, P, P, P, P, I64, P],
@@ -429,6 +431,18 @@ def routed_attn_decode(cfg, rows, k_cache, v_cache, sel, out, workspace, stream=
     """Exact attention over window + selected spans, split-K over span sub-tiles (few rows)."""
     args, _keep = _args_attn(cfg, rows, k_cache, v_cache, sel, out, workspace, stream)
     _check(lib().routed_attn_decode(*args))
+
+
+def routed_attn_decode_noalloc(cfg, rows, k_cache, v_cache, sel, out, stream=None):
+    """routed_attn_decode with the library's own fixed device scratch (no workspace, nothing
+    allocated); calls that overlap on one GPU race."""
+    c, r = cfg.c(), _rows(cfg, rows)
+    n = rows.q.shape[0]
+    _check(lib().routed_attn_decode_noalloc(
+        ctypes.byref(c), ctypes.byref(r), _dev(k_cache, cfg.torch_dtype, _kv_shape(cfg), "k_cache"),
+        _dev(v_cache, cfg.torch_dtype, _kv_shape(cfg), "v_cache"),
+        _dev(sel, torch.int32, (n, cfg.num_q_heads, cfg.top_k), "sel"),
+        _dev(out, torch.float32, (n, cfg.num_q_heads, cfg.head_dim), "out"), _stream(stream)))
 
 
 def routed_attn_prefill(cfg, rows, k_cache, v_cache, sel, out, workspace, stream=None):

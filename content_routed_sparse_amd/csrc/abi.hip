@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -188,6 +189,64 @@ ra_status routed_attn_decode(const ra_config *cfg, const ra_rows *rows, const vo
     if (rows->n_rows == 0) return ok();
     return hip_status(ra::launch_decode(row_args(cfg, rows), k_cache, v_cache, sel, out, workspace, (hipStream_t)stream),
                       "routed_attn_decode launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// The device scratch of routed_attn_decode_noalloc: one copy per GPU, held until the process
+// ends.  In host code `scratch` names a host-side stand-in, not the device array: its device
+// address comes from hipGetSymbolAddress, once per device (with that device current), and only
+// that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_ptr;  // per device ordinal; null until looked up
+
+// The device address of this device's scratch (looked up on the first call on the device).
+ra_status scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(RA_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status routed_attn_decode_noalloc(const ra_config *cfg, const ra_rows *rows, const void *k_cache,
+                                     const void *v_cache, const int32_t *sel, float *out, void *stream) {
+    ra_status s = check_config(cfg);
+    if (s) return s;
+    if ((s = check_rows(cfg, rows))) return s;
+    const size_t need = ra::decode_workspace_bytes(row_args(cfg, rows));
+    if (need > kNoAllocScratchBytes)
+        return fail(RA_ECAPACITY,
+                    "routed_attn_decode_noalloc needs %zu bytes of scratch, more than its fixed %zu: use fewer rows "
+                    "per call, or routed_attn_decode with a workspace",
+                    need, kNoAllocScratchBytes);
+    // the full validation, with the scratch standing in for the workspace (nothing is launched
+    // before it passes)
+    s = check_attn(cfg, rows, k_cache, v_cache, sel, out, &kNoAllocScratchBytes, kNoAllocScratchBytes, RA_OP_DECODE);
+    if (s) return s;
+    if (rows->n_rows == 0) return ok();
+    void *ws = nullptr;
+    if ((s = scratch_address(&ws))) return s;
+    return hip_status(ra::launch_decode(row_args(cfg, rows), k_cache, v_cache, sel, out, ws, (hipStream_t)stream),
+                      "routed_attn_decode_noalloc launch");
 }
 
 ra_status routed_attn_prefill(const ra_config *cfg, const ra_rows *rows, const void *k_cache, const void *v_cache,

@@ -144,6 +144,22 @@ ra_status routed_attn_decode(const ra_config *cfg, const ra_rows *rows, const vo
                              void *stream);
 
 /*
+ * routed_attn_decode_noalloc -- routed_attn_decode for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The same kernels and the same results, bit for bit; the partial records
+ * go to a device array inside the library, fixed at 32 MiB per GPU and held until the process
+ * ends (its address is looked up on the first call on each device).  No allocation, no
+ * host synchronisation.
+ *   Limit: ra_workspace_bytes(cfg, RA_OP_DECODE, n_rows, max_pos) <= 32 MiB, else RA_ECAPACITY
+ *   (32 query heads, d 128, top-16, window = span: about 1.16 MiB per row at spans of 1024,
+ *   0.58 MiB per row at spans of 512, 4.6 MiB per row at spans of 4096).
+ *   Calls that overlap on one GPU (other streams, other threads) share the array and race:
+ *   serialise them.  Every call writes every record it reads, so nothing needs clearing.
+ */
+ra_status routed_attn_decode_noalloc(const ra_config *cfg, const ra_rows *rows, const void *k_cache,
+                                     const void *v_cache, const int32_t *sel, float *out, void *stream);
+
+/*
  * routed_attn_prefill -- the same result for many rows (a chunk of new tokens, causal in the
  * chunk).  Rows are grouped span by span (every (sequence, kv head, span) gathers the rows
  * that attend to it, as selected span or as window span), each group runs as dense tiles over

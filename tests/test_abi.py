@@ -249,3 +249,15 @@ def test_grid_limits_are_checked_before_launch():
     st = lib.routed_attn_decode_fp8(ctypes.byref(c), ctypes.byref(rows(8192, (1 << 20) + 8191)), FAKE, FAKE, FAKE,
                                     FAKE, FAKE, FAKE, FAKE, big_ws, None)
     assert st == 2
+
+
+def test_noalloc_decode_validates_before_launch():
+    """routed_attn_decode_noalloc: invalid arguments and calls whose records would not fit the
+    library's fixed 32 MiB scratch are rejected on the host."""
+    lib = ra.lib()
+    c = cfg().c()
+    assert lib.routed_attn_decode_noalloc(None, ctypes.byref(rows()), FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.routed_attn_decode_noalloc(ctypes.byref(c), ctypes.byref(rows()), FAKE, FAKE, None, FAKE, None) == 1
+    # 1.16 MiB of records per 1M-context row: 40 rows need more than 32 MiB
+    assert lib.routed_attn_decode_noalloc(ctypes.byref(c), ctypes.byref(rows(40)), FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert "scratch" in lib.ra_last_error().decode()
