@@ -1,9 +1,10 @@
 """Benchmark: one decode step of content-routed sparse attention at 1M context, on one GPU.
 
 A step is the whole hot path for one new token of one sequence at L = 1,048,576 (32 query
-heads, 4 kv heads, d = 128, bf16 cache, spans of 1024, top-16 + window of 1024): route_scores ->
-topk_spans -> routed_attn_decode_append (the attention and, in its merge launch, the new token's
-span-summary update; equivalent to updating first, since the token completes no routable span).
+heads, 4 kv heads, d = 128, bf16 cache, spans of 1024, top-16 + window of 1024):
+route_topk_spans (route_scores and topk_spans in one launch) -> routed_attn_decode_append (the
+attention and, in its merge launch, the new token's span-summary update; equivalent to updating
+first, since the token completes no routable span).
 Inputs are synthetic (seeded generator), resident in HBM before timing starts.
 
 So that every step reads its keys and values from HBM rather than from the 256 MB Infinity
@@ -122,10 +123,7 @@ def main():
     # the window) and routing does not read the running sum, so this order selects exactly what
     # update-then-route does.  Re-running the step re-closes that span: every step is the same work.
     for d in st:
-        d["calls_front"] = [
-            ra.prepare("route_scores", cfg1, d["rows"], d["mean"], d["scores"]),
-            ra.prepare("topk_spans", cfg1, d["rows"], d["scores"], d["sel"]),
-        ]
+        d["calls_front"], front_kind = front_calls(ra, cfg1, d["rows"], d["mean"], d["scores"], d["sel"])
         d["call_attn"] = ra.prepare("routed_attn_decode_append", cfg1, d["rows"], d["k"], d["v"], d["sel"], d["out"],
                                     ws, d["mean"], d["run"], before, after, 1)
 
@@ -229,7 +227,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode_1m", "context": L, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "span": w.span_size, "top_k": w.top_k, "window": w.window, "batch": 1,
-                   "rotated_sequences": NC, "hip_graphs": bool(args.graph)},
+                   "rotated_sequences": NC, "hip_graphs": bool(args.graph), "routing_calls": front_kind},
         "roofline": {"bound": "hbm",
                      "kernel": "routed_attn_decode_append (decode_attn + merge launch with the token's summary update)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -285,6 +283,26 @@ def main():
                                                     args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def front_calls(ra, cfg, rows, mean, scores, sel):
+    """The step's routing and selection: route_topk_spans (one launch; its zeroed workspace is
+    allocated here, untimed) where supported, else route_scores then topk_spans."""
+    import torch
+
+    n = rows.q.shape[0]
+    ws = torch.zeros(ra.workspace_bytes(cfg, ra.RA_OP_ROUTE_TOPK, n, rows.max_pos), dtype=torch.uint8,
+                     device=rows.q.device)
+    try:
+        fused = ra.prepare("route_topk_spans", cfg, rows, mean, sel, ws)
+        fused()
+        fused._ws = ws  # keeps the workspace alive with the prepared call
+        return [fused], "route_topk_spans"
+    except ra.RoutedAttnError as e:
+        if e.status != 2:
+            raise
+    return [ra.prepare("route_scores", cfg, rows, mean, scores),
+            ra.prepare("topk_spans", cfg, rows, scores, sel)], "route_scores + topk_spans"
 
 
 def counter_traffic(tag):
@@ -498,8 +516,7 @@ def bench_decode_fp8(args, w, K, V, qs):
              "sel": torch.empty(1, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev),
              "out": torch.empty(1, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)}
         ra.span_summary_update_fp8(cfg1, d["k"], d["ks"], d["mean"], d["run"], zero, before, L - 1)
-        d["front"] = [ra.prepare("route_scores", cfg1, d["rows"], d["mean"], d["scores"]),
-                      ra.prepare("topk_spans", cfg1, d["rows"], d["scores"], d["sel"])]
+        d["front"], _ = front_calls(ra, cfg1, d["rows"], d["mean"], d["scores"], d["sel"])
         d["attn"] = ra.prepare("routed_attn_decode_fp8_append", cfg1, d["rows"], d["k"], d["v"], d["ks"], d["vs"],
                                d["sel"], d["out"], ws, d["mean"], d["run"], before, full, 1)
         st.append(d)
@@ -837,8 +854,7 @@ def bench_decode_workload(name, steps, warmup, cpu_seconds=0.0):
     sel = torch.empty(B, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev)
     out = torch.empty(B, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
     ws = torch.empty(ra.workspace_bytes(cfg, ra.RA_OP_DECODE, B, cap - 1), dtype=torch.uint8, device=dev)
-    front = [ra.prepare("route_scores", cfg, rows, mean, scores),
-             ra.prepare("topk_spans", cfg, rows, scores, sel)]
+    front, front_kind = front_calls(ra, cfg, rows, mean, scores, sel)
     attn = ra.prepare("routed_attn_decode_append", cfg, rows, K, V, sel, out, ws, mean, run, before, after, 1)
     torch.cuda.synchronize()
     setup = time.time() - t0
@@ -895,6 +911,7 @@ def bench_decode_workload(name, steps, warmup, cpu_seconds=0.0):
         cpu, check = oracle_decode_baseline(w, kv, lengths, qh, cpu_seconds, gsel, gout)
         del kv
     return {"workload": name, "sequences": B, "context_max": cap, "span": S, "top_k": w.top_k, "window": w.window,
+            "routing_calls": front_kind,
             "value": round(B * 1000.0 / ms, 2), "unit": "tokens/s", "ms_per_step": round(ms, 5),
             "roofline": {"bound": "hbm",
                      "kernel": "routed_attn_decode_append (decode_attn + merge launch with the token's summary update)",

@@ -20,8 +20,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libroutedattn.so")
 
 RA_F32, RA_BF16 = 0, 1
-RA_OP_DECODE, RA_OP_PREFILL = 0, 1
-EXPORTED = ("span_summary_update", "route_scores", "topk_spans", "routed_attn_decode", "routed_attn_prefill",
+RA_OP_DECODE, RA_OP_PREFILL, RA_OP_ROUTE_TOPK = 0, 1, 2
+EXPORTED = ("span_summary_update", "route_scores", "topk_spans", "route_topk_spans", "routed_attn_decode",
+            "routed_attn_prefill",
             "routed_attn_decode_noalloc",
             "attn_dense_causal", "kv_quantize_fp8", "span_summary_update_fp8", "routed_attn_decode_fp8",
             "routed_attn_decode_append", "routed_attn_decode_fp8_append",
@@ -74,6 +75,7 @@ def lib():
             "span_summary_update": [CP, P, P, P, P, P, I64, P],
             "route_scores": [CP, RP, P, P, I64, P],
             "topk_spans": [CP, RP, P, I64, P, P],
+            "route_topk_spans": [CP, RP, P, P, P, SZ, P],
             "routed_attn_decode": [CP, RP, P, P, P, P, P, SZ, P],
             "routed_attn_decode_noalloc": [CP, RP, P, P, P, P, P],
             "routed_attn_prefill": [CP, RP, P, P, P, P, P, SZ, P],
@@ -236,6 +238,15 @@ def _args_route_scores(cfg, rows, span_mean, scores, stream=None):
             _dev(scores, torch.float32, None, "scores"), scores.shape[2], _stream(stream)), (c, r)
 
 
+def _args_route_topk_spans(cfg, rows, span_mean, sel, workspace, stream=None):
+    c, r = cfg.c(), _rows(cfg, rows)
+    n = rows.q.shape[0]
+    return (ctypes.byref(c), ctypes.byref(r),
+            _dev(span_mean, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.max_spans, cfg.head_dim), "span_mean"),
+            _dev(sel, torch.int32, (n, cfg.num_q_heads, cfg.top_k), "sel"),
+            _dev(workspace, torch.uint8, None, "workspace"), workspace.numel(), _stream(stream)), (c, r)
+
+
 def _args_topk_spans(cfg, rows, scores, sel, stream=None):
     c, r = cfg.c(), _rows(cfg, rows)
     _scores_shape_check(cfg, rows, scores)
@@ -360,6 +371,7 @@ _BUILDERS = {
     "span_summary_update": _args_span_summary_update,
     "route_scores": _args_route_scores,
     "topk_spans": _args_topk_spans,
+    "route_topk_spans": _args_route_topk_spans,
     "routed_attn_decode": _args_attn,
     "routed_attn_prefill": _args_attn,
     "attn_dense_causal": _args_dense,
@@ -417,6 +429,13 @@ def topk_spans(cfg, rows, scores, sel, stream=None):
     """sel[row][h] = the row's top-k routable spans, ascending, padded with -1."""
     args, _keep = _args_topk_spans(cfg, rows, scores, sel, stream)
     _check(lib().topk_spans(*args))
+
+
+def route_topk_spans(cfg, rows, span_mean, sel, workspace, stream=None):
+    """route_scores then topk_spans in one launch (few rows).  The workspace (RA_OP_ROUTE_TOPK
+    bytes) must start zeroed (torch.zeros); every call leaves its counters at zero."""
+    args, _keep = _args_route_topk_spans(cfg, rows, span_mean, sel, workspace, stream)
+    _check(lib().route_topk_spans(*args))
 
 
 def workspace_bytes(cfg, op, n_rows, max_pos):

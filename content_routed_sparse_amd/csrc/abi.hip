@@ -182,6 +182,26 @@ ra_status topk_spans(const ra_config *cfg, const ra_rows *rows, const float *sco
                       "topk_spans launch");
 }
 
+ra_status route_topk_spans(const ra_config *cfg, const ra_rows *rows, const float *span_mean, int32_t *sel,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    ra_status s = check_config(cfg);
+    if (s) return s;
+    if ((s = check_rows(cfg, rows))) return s;
+    if (rows->n_rows == 0) return ok();
+    if (!span_mean || !sel) return fail(RA_EINVAL, "NULL span_mean or sel");
+    const ra::RowArgs a = row_args(cfg, rows);
+    const int64_t rmax = ra::num_routable(a.max_pos, a.S, a.W);
+    if (rmax > ra::route_topk_max_routable())
+        return fail(RA_EUNSUPPORTED, "route_topk_spans selects among at most %lld routable spans (%lld here): call "
+                    "route_scores, then topk_spans", (long long)ra::route_topk_max_routable(), (long long)rmax);
+    if (a.n_rows * a.Hkv >= kMaxGrid) return fail(RA_EUNSUPPORTED, "too many rows for one launch");
+    const size_t need = ra::route_topk_workspace_bytes(a);
+    if (!workspace || workspace_bytes < need)
+        return fail(RA_ECAPACITY, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+    return hip_status(ra::launch_route_topk(a, span_mean, sel, workspace, (hipStream_t)stream),
+                      "route_topk_spans launch");
+}
+
 ra_status routed_attn_decode(const ra_config *cfg, const ra_rows *rows, const void *k_cache, const void *v_cache,
                              const int32_t *sel, float *out, void *workspace, size_t workspace_bytes, void *stream) {
     ra_status s = check_attn(cfg, rows, k_cache, v_cache, sel, out, workspace, workspace_bytes, RA_OP_DECODE);
@@ -827,8 +847,8 @@ ra_status routed_attn_decode_fp8_append(const ra_config *cfg, const ra_rows *row
 
 size_t ra_workspace_bytes(const ra_config *cfg, int32_t op, int64_t n_rows, int64_t max_pos) {
     if (check_config(cfg)) return 0;
-    if (op != RA_OP_DECODE && op != RA_OP_PREFILL) {
-        fail(RA_EINVAL, "op must be RA_OP_DECODE or RA_OP_PREFILL");
+    if (op != RA_OP_DECODE && op != RA_OP_PREFILL && op != RA_OP_ROUTE_TOPK) {
+        fail(RA_EINVAL, "op must be RA_OP_DECODE, RA_OP_PREFILL or RA_OP_ROUTE_TOPK");
         return 0;
     }
     ra_rows r{nullptr, nullptr, nullptr, n_rows, max_pos};
@@ -837,6 +857,7 @@ size_t ra_workspace_bytes(const ra_config *cfg, int32_t op, int64_t n_rows, int6
         return 0;
     }
     const ra::RowArgs a = row_args(cfg, &r);
+    if (op == RA_OP_ROUTE_TOPK) return ra::route_topk_workspace_bytes(a);
     return op == RA_OP_DECODE ? ra::decode_workspace_bytes(a) : ra::prefill_workspace_bytes(a);
 }
 

@@ -7,32 +7,14 @@
 // The winners are written in ascending span order and padded with -1.
 #include "common.h"
 #include "kernels.h"
+#include "topk_body.h"
 #include "wave_ops.h"
 
 namespace ra {
 namespace {
 
-__device__ __forceinline__ uint64_t score_key(float s, int64_t j) {
-    uint32_t u = __float_as_uint(s);
-    if (s == 0.f) u = 0u;  // -0 and +0 are the same score: the lower index must win
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-}
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// PER_LANE candidates per lane kept in registers (r <= 64 * PER_LANE).
-//
-// Threshold first: v = the m-th largest of the 64 per-lane maximum scores (the keys' upper
-// halves), found bit by bit from the top: a bit is kept when at least m lanes still reach the
-// value (one ballot per bit).  At least m lanes then hold a key >= T0 = v * 2^32, so every one of
-// the m winners is >= T0.  The keys >= T0 (usually little more than m; more only where scores
-// tie) are compacted into LDS in span order and each is ranked against the others; if more than
-// 64 pass, the selection falls back to m rounds of "largest key below the previous winner".
+// One 64-lane wavefront per (row, query head): the row's scores are loaded into the lanes'
+// registers as keys, then wave_topk selects (topk_body.h).
 template <int PER_LANE>
 __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ scores, int64_t stride,
                                                    const int64_t *__restrict__ row_pos, int32_t *__restrict__ sel,
@@ -45,7 +27,6 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
     const int64_t rh = (int64_t)blockIdx.x * (blockDim.x / 64) + wave;
     if (rh >= n_rowheads) return;
     const float *srow = scores + rh * stride;
-    int32_t *out = sel + rh * k;
 
     // The row's position and its scores in one round trip: the score loads do not wait for r
     // (indices are clamped to the row's stride, which bounds r; entries j >= r are masked
@@ -69,79 +50,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
         const int64_t j = lane + 64 * i;
         key[i] = j < r ? score_key(sv[i], j) : 0ull;
     }
-    if (m == 0) {
-        if (lane < k) out[lane] = -1;
-        return;
-    }
-    // per-lane maximum (balanced tree)
-    uint64_t f[PER_LANE];
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) f[i] = key[i];
-#pragma unroll
-    for (int width = 1; width < PER_LANE; width *= 2) {
-#pragma unroll
-        for (int i = 0; i + width < PER_LANE; i += 2 * width) f[i] = f[i + width] > f[i] ? f[i + width] : f[i];
-    }
-    // at least m lanes hold a valid key (candidates are dealt round-robin and m <= r), so the
-    // search ends on the upper half of a valid key
-    const uint32_t lhi = (uint32_t)(f[0] >> 32);
-    uint32_t v = 0;
-#pragma unroll
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t test = v | (1u << bit);
-        if ((int)__builtin_popcountll(__ballot(lhi >= test)) >= m) v = test;
-    }
-    const uint64_t T0 = (uint64_t)v << 32;
-
-    int C = 0;
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) {
-        const bool c = key[i] >= T0;
-        const uint64_t b = __ballot(c);
-        const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-        if (c && pos < 64) cand[wave][pos] = key[i];
-        C += (int)__builtin_popcountll(b);
-    }
-    if (C <= 64) {
-        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const uint64_t mine = lane < C ? cand[wave][lane] : 0ull;
-        int rank = 0;
-        for (int j2 = 0; j2 < C; ++j2) rank += cand[wave][j2] > mine ? 1 : 0;
-        const bool chosen = lane < C && rank < m;
-        const uint32_t idx = 0xFFFFFFFFu - (uint32_t)(mine & 0xFFFFFFFFull);
-        // the list is in increasing span order (compacted register by register, lane by lane,
-        // and lane l of register i holds span l + 64 i), so a winner's output slot is the number
-        // of winners before it in the list
-        const uint64_t cb = __ballot(chosen);
-        const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(cb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cb, 0u));
-        if (chosen) out[pos] = (int32_t)idx;
-        if (lane >= m && lane < k) out[lane] = -1;
-        return;
-    }
-
-    // fallback: m rounds, each taking the wave maximum among keys below the previous winner
-    uint64_t last = ~0ull;
-    uint32_t win = 0xFFFFFFFFu;  // lane w keeps the w-th winner's span index
-    for (int w = 0; w < m; ++w) {
-        uint64_t g[PER_LANE];
-#pragma unroll
-        for (int i = 0; i < PER_LANE; ++i) g[i] = key[i] < last ? key[i] : 0ull;
-#pragma unroll
-        for (int width = 1; width < PER_LANE; width *= 2) {
-#pragma unroll
-            for (int i = 0; i + width < PER_LANE; i += 2 * width) g[i] = g[i + width] > g[i] ? g[i + width] : g[i];
-        }
-        const uint64_t best = wave_max_u64(g[0]);
-        last = best;
-        if (lane == w) win = 0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull);
-    }
-    int rank = 0;
-    for (int w = 0; w < m; ++w) {
-        const uint32_t o = __shfl(win, w);
-        rank += (o < win) ? 1 : 0;
-    }
-    if (lane < m) out[rank] = (int32_t)win;
-    else if (lane < k) out[lane] = -1;
+    wave_topk<PER_LANE>(key, m, k, lane, cand[wave], sel + rh * k);
 }
 
 // Candidates re-read from memory each round (any r).

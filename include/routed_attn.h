@@ -63,7 +63,7 @@ typedef enum {
 
 typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
 
-typedef enum { RA_OP_DECODE = 0, RA_OP_PREFILL = 1 } ra_op;
+typedef enum { RA_OP_DECODE = 0, RA_OP_PREFILL = 1, RA_OP_ROUTE_TOPK = 2 } ra_op;
 
 /* Shapes and method parameters.  Supported: head_dim in {64, 128}; num_q_heads a multiple of
  * num_kv_heads with Hq/Hkv <= 32; 1 <= top_k <= 64; span_size >= 1; window >= 1;
@@ -127,6 +127,22 @@ ra_status route_scores(const ra_config *cfg, const ra_rows *rows, const float *s
  */
 ra_status topk_spans(const ra_config *cfg, const ra_rows *rows, const float *scores, int64_t score_stride,
                      int32_t *sel, void *stream);
+
+/*
+ * route_topk_spans -- route_scores then topk_spans in one launch, for few rows (decode).  The
+ * blocks score the routable spans with the fp32 products of route_scores' few-row path (the same
+ * scores, bit for bit) into the workspace; the last block of each (row, kv head) to finish then
+ * selects for the kv head's query heads exactly as topk_spans does.
+ *   Supported when r(max_pos) <= 1088 (RA_EUNSUPPORTED otherwise: call route_scores, then
+ *   topk_spans).  Correct for any number of rows; with many rows per sequence (a prefill
+ *   chunk) route_scores + topk_spans is faster.
+ *   workspace      device memory of at least ra_workspace_bytes(cfg, RA_OP_ROUTE_TOPK, n_rows,
+ *                  max_pos) bytes: n_rows x Hkv counters, then the scores.  The counters must be
+ *                  zero before the first call (clear a new workspace once); every call leaves them
+ *                  zero.  Calls that share a workspace must not overlap.
+ */
+ra_status route_topk_spans(const ra_config *cfg, const ra_rows *rows, const float *span_mean, int32_t *sel,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * routed_attn_decode -- exact softmax attention of each row over its window and its selected
@@ -350,7 +366,8 @@ ra_status kv_snapshot_unpack(const ra_config *cfg, const void *header, size_t he
 ra_status kv_snapshot_write_file(const char *path, const void *data, size_t bytes);
 ra_status kv_snapshot_read_file(const char *path, void *buf, size_t capacity, size_t *bytes);
 
-/* Workspace bytes needed by routed_attn_decode / routed_attn_prefill (op = ra_op); 0 if the
+/* Workspace bytes needed by routed_attn_decode / routed_attn_prefill / route_topk_spans (op =
+ * ra_op); 0 if the
  * configuration is invalid (ra_last_error then says why). */
 size_t ra_workspace_bytes(const ra_config *cfg, int32_t op, int64_t n_rows, int64_t max_pos);
 

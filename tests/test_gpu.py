@@ -639,3 +639,51 @@ def test_route_and_topk_do_not_depend_on_the_score_stride(d, G, S, W, nseq):
     for sc, sel in got[1:]:
         assert np.array_equal(sc.view(np.uint32), got[0][0].view(np.uint32))
         assert np.array_equal(sel, got[0][1])
+
+
+ROUTE_TOPK_CASES = [
+    ("bf16_d128_G8", small("ragged_decode_16", batch=3, span_size=64, window=64, top_k=16, ragged=(3000, 60000))),
+    ("bf16_d64_G4_W3S", small("ragged_decode_16", batch=2, head_dim=64, num_q_heads=8, num_kv_heads=2, span_size=32,
+                              window=96, top_k=6, ragged=(700, 30000))),
+    ("bf16_G32_k16", small("ragged_decode_16", batch=2, num_q_heads=32, num_kv_heads=1, span_size=64, window=64,
+                           top_k=16, ragged=(2000, 20000))),
+    ("bf16_r1000_k64", small("ragged_decode_16", batch=2, num_q_heads=8, num_kv_heads=2, span_size=16, window=16,
+                             top_k=64, ragged=(12000, 17000))),
+    ("fp32_d128_G4", small("tiny_prefill_fp32", mode="decode", batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                           span_size=128, window=200, top_k=4, ragged=(129, 50000))),
+    ("bf16_short_rows_r0", small("ragged_decode_16", batch=3, span_size=64, window=64, top_k=8, ragged=(1, 130))),
+    ("bf16_all_rows_r0", small("ragged_decode_16", batch=2, span_size=64, window=64, top_k=8, ragged=(1, 100))),
+]
+
+
+@pytest.mark.parametrize("name,w", ROUTE_TOPK_CASES, ids=[c[0] for c in ROUTE_TOPK_CASES])
+def test_route_topk_spans_equals_route_then_topk(name, w):
+    """The fused routing + selection gives exactly the selection of route_scores then
+    topk_spans (the same fp32 scores, the same order), for every row and head; rows of several
+    sequences and extra rows at earlier positions (other r) in one call.  Twenty calls in a row on
+    one workspace (the last-arriving block of each (row, kv head) selects, and leaves its
+    counter at zero) all give the same selection."""
+    lengths = w.seq_lengths()
+    c, rows, q = run_decode(w, lengths)
+    rng = np.random.default_rng(5)
+    seqs = np.concatenate([np.arange(c.B), rng.integers(0, c.B, 5)])
+    pos = np.concatenate([lengths - 1, [rng.integers(0, lengths[s]) for s in seqs[c.B:]]])
+    rows2, q2 = c.rows_for(seqs, pos)
+    n = len(seqs)
+    scores = torch.empty(n, w.num_q_heads, ra.score_stride(c.cfg, int(pos.max())), device="cuda")
+    sel_ref = torch.full((n, w.num_q_heads, w.top_k), -7, dtype=torch.int32, device="cuda")
+    ra.route_scores(c.cfg, rows2, c.pipe.span_mean, scores)
+    ra.topk_spans(c.cfg, rows2, scores, sel_ref)
+    ws = torch.zeros(ra.workspace_bytes(c.cfg, ra.RA_OP_ROUTE_TOPK, n, int(pos.max())), dtype=torch.uint8,
+                     device="cuda")
+    for rep in range(20):
+        sel = torch.full_like(sel_ref, -9)
+        ra.route_topk_spans(c.cfg, rows2, c.pipe.span_mean, sel, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(sel, sel_ref), rep
+    counters = ws[:4 * n * w.num_kv_heads].view(torch.int32)
+    assert int(counters.abs().sum()) == 0
+    # and the decode rows' selection is the oracle's (exact or a valid near tie)
+    c.pipe.sel.copy_(sel[:c.B])
+    stats = c.check(np.arange(c.B), lengths - 1, q, np.arange(c.B), scores=False)
+    assert not stats["fail"], stats["fail"][:3]
