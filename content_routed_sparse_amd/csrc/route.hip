@@ -234,17 +234,15 @@ __global__ void __launch_bounds__(kRtWaves * 64) route_topk(const T *__restrict_
                                             : 0.f;
             }
         }
+        const int rl = (int)(r < 64 * PER_LANE ? r : 64 * PER_LANE);
 #pragma unroll
         for (int x = 0; x < HPW; ++x) {
             const int h = h0 + x * kRtWaves;
             if (h >= G) break;
-            uint64_t key[PER_LANE];
+            uint32_t img[PER_LANE];
 #pragma unroll
-            for (int i = 0; i < PER_LANE; ++i) {
-                const int64_t j = lane + 64 * i;
-                key[i] = j < r ? score_key(sv[x][i], j) : 0ull;
-            }
-            wave_topk<PER_LANE>(key, m, k, lane, cand[wave], sel + (row * Hq + g * G + h) * k);
+            for (int i = 0; i < PER_LANE; ++i) img[i] = lane + 64 * i < rl ? score_image(sv[x][i]) : 0u;
+            wave_topk<PER_LANE>(img, m, k, lane, cand[wave], sel + (row * Hq + g * G + h) * k);
         }
     }
 }

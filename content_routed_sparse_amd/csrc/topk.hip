@@ -32,7 +32,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
     // (indices are clamped to the row's stride, which bounds r; entries j >= r are masked
     // below).  Unconditional loads: a conditional load would be issued and waited for alone.
     const int64_t t_raw = row_pos[rh / Hq];
-    uint64_t key[PER_LANE];
+    uint32_t img[PER_LANE];
     float sv[PER_LANE];
     const int64_t jmax = stride - 1;
 #pragma unroll
@@ -44,13 +44,11 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ sco
     const int64_t t = t_raw < 0 ? 0 : (t_raw > max_pos ? max_pos : t_raw);
     const int64_t r = num_routable(t, S, W);
     const int m = (int)(r < k ? r : k);
-    // every valid key is > 0, invalid candidates get key 0
+    // every valid image is > 0, spans past r get 0
+    const int rl = (int)(r < 64 * PER_LANE ? r : 64 * PER_LANE);
 #pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) {
-        const int64_t j = lane + 64 * i;
-        key[i] = j < r ? score_key(sv[i], j) : 0ull;
-    }
-    wave_topk<PER_LANE>(key, m, k, lane, cand[wave], sel + rh * k);
+    for (int i = 0; i < PER_LANE; ++i) img[i] = lane + 64 * i < rl ? score_image(sv[i]) : 0u;
+    wave_topk<PER_LANE>(img, m, k, lane, cand[wave], sel + rh * k);
 }
 
 // Candidates re-read from memory each round (any r).

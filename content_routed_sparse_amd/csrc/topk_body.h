@@ -26,50 +26,51 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// One wave selects from key[] (lane l holds spans l + 64 i; 0 for j >= r) the m = min(k, r) largest
-// keys and writes their span indices to out[0..k) (ascending, -1 padded).  cand: 64 words of LDS
-// owned by the wave.
+// The order-preserving 32-bit image of a score (the upper half of its key); valid images are >= 1.
+__device__ __forceinline__ uint32_t score_image(float s) {
+    uint32_t u = __float_as_uint(s);
+    if (s == 0.f) u = 0u;  // -0 and +0 are the same score: the lower index must win
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave selects among the spans j = lane + 64 i (i < PER_LANE) whose score images img[i] are
+// given (0 for j >= r) the m = min(k, r) largest keys  img << 32 | (0xFFFFFFFF - j)  and writes
+// their span indices to out[0..k) (ascending, -1 padded).  cand: 64 words of LDS owned by the wave.
 //
-// Threshold first: v = the m-th largest of the 64 per-lane maximum scores (the keys' upper
-// halves), found bit by bit from the top: a bit is kept when at least m lanes still reach the
-// value (one ballot per bit).  At least m lanes then hold a key >= T0 = v * 2^32, so every one of
-// the m winners is >= T0.  The keys >= T0 (usually little more than m; more only where scores
-// tie) are compacted into LDS in span order and each is ranked against the others; if more than
-// 64 pass, the selection falls back to m rounds of "largest key below the previous winner".
+// Threshold first: v = the m-th largest of the 64 per-lane maximum images, found bit by bit from
+// the top: a bit is kept when at least m lanes still reach the value (one ballot per bit).  At
+// least m lanes then hold an image >= v, so every one of the m winners has an image >= v.  The
+// spans with images >= v (usually little more than m; more only where scores tie) are compacted
+// into LDS in span order as 64-bit keys and each is ranked against the others; if more than 64
+// pass, the selection falls back to m rounds of "largest key below the previous winner".  Only
+// the candidates become 64-bit keys: the rest of the work is on 32-bit images.
 template <int PER_LANE>
-__device__ __forceinline__ void wave_topk(const uint64_t (&key)[PER_LANE], int m, int k, int lane, uint64_t *cand,
+__device__ __forceinline__ void wave_topk(const uint32_t (&img)[PER_LANE], int m, int k, int lane, uint64_t *cand,
                                           int32_t *out) {
     if (m == 0) {
         if (lane < k) out[lane] = -1;
         return;
     }
-    // per-lane maximum (balanced tree)
-    uint64_t f[PER_LANE];
+    // per-lane maximum image
+    uint32_t lmax = img[0];
 #pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) f[i] = key[i];
-#pragma unroll
-    for (int width = 1; width < PER_LANE; width *= 2) {
-#pragma unroll
-        for (int i = 0; i + width < PER_LANE; i += 2 * width) f[i] = f[i + width] > f[i] ? f[i + width] : f[i];
-    }
-    // at least m lanes hold a valid key (candidates are dealt round-robin and m <= r), so the
-    // search ends on the upper half of a valid key
-    const uint32_t lhi = (uint32_t)(f[0] >> 32);
+    for (int i = 1; i < PER_LANE; ++i) lmax = img[i] > lmax ? img[i] : lmax;
+    // at least m lanes hold a valid image (candidates are dealt round-robin and m <= r), so the
+    // search ends on a valid image
     uint32_t v = 0;
 #pragma unroll
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t test = v | (1u << bit);
-        if ((int)__builtin_popcountll(__ballot(lhi >= test)) >= m) v = test;
+        if ((int)__builtin_popcountll(__ballot(lmax >= test)) >= m) v = test;
     }
-    const uint64_t T0 = (uint64_t)v << 32;
 
     int C = 0;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) {
-        const bool c = key[i] >= T0;
+        const bool c = img[i] >= v;
         const uint64_t b = __ballot(c);
         const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-        if (c && pos < 64) cand[pos] = key[i];
+        if (c && pos < 64) cand[pos] = ((uint64_t)img[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * i));
         C += (int)__builtin_popcountll(b);
     }
     if (C <= 64) {
@@ -93,15 +94,14 @@ __device__ __forceinline__ void wave_topk(const uint64_t (&key)[PER_LANE], int m
     uint64_t last = ~0ull;
     uint32_t win = 0xFFFFFFFFu;  // lane w keeps the w-th winner's span index
     for (int w = 0; w < m; ++w) {
-        uint64_t g[PER_LANE];
+        uint64_t best = 0;
 #pragma unroll
-        for (int i = 0; i < PER_LANE; ++i) g[i] = key[i] < last ? key[i] : 0ull;
-#pragma unroll
-        for (int width = 1; width < PER_LANE; width *= 2) {
-#pragma unroll
-            for (int i = 0; i + width < PER_LANE; i += 2 * width) g[i] = g[i + width] > g[i] ? g[i + width] : g[i];
+        for (int i = 0; i < PER_LANE; ++i) {
+            const uint64_t key = img[i] ? ((uint64_t)img[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * i))
+                                        : 0ull;
+            best = (key < last && key > best) ? key : best;
         }
-        const uint64_t best = wave_max_u64(g[0]);
+        best = wave_max_u64(best);
         last = best;
         if (lane == w) win = 0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull);
     }
