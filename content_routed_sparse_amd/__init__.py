@@ -25,6 +25,7 @@ EXPORTED = ("span_summary_update", "route_scores", "topk_spans", "route_topk_spa
             "routed_attn_prefill",
             "routed_attn_decode_noalloc",
             "attn_dense_causal", "kv_quantize_fp8", "span_summary_update_fp8", "routed_attn_decode_fp8",
+            "routed_attn_prefill_fp8",
             "routed_attn_decode_append", "routed_attn_decode_fp8_append",
             "kv_signature_update", "ra_cold_workspace_bytes", "cold_select", "cold_attn_decode",
             "kv_snapshot_bytes", "kv_snapshot_pack", "kv_snapshot_parse", "kv_snapshot_verify", "kv_snapshot_unpack",
@@ -83,6 +84,7 @@ def lib():
             "kv_quantize_fp8": [CP, P, P, P, P, P, I64, P],
             "span_summary_update_fp8": [CP, P, P, P, P, P, P, I64, P],
             "routed_attn_decode_fp8": [CP, RP, P, P, P, P, P, P, P, SZ, P],
+            "routed_attn_prefill_fp8": [CP, RP, P, P, P, P, P, P, P, SZ, P],
             "routed_attn_decode_append": [CP, RP, P, P, P, P, P, SZ, P, P, P, P, I64, P],
             "routed_attn_decode_fp8_append": [CP, RP, P, P, P, P, P, P, P, SZ, P, P, P, P, I64, P],
             "kv_signature_update": [CP, P, P, P, P, I64, P],
@@ -378,6 +380,7 @@ _BUILDERS = {
     "kv_quantize_fp8": _args_kv_quantize_fp8,
     "span_summary_update_fp8": _args_span_summary_update_fp8,
     "routed_attn_decode_fp8": _args_attn_fp8,
+    "routed_attn_prefill_fp8": _args_attn_fp8,
     "routed_attn_decode_append": _args_attn_append,
     "routed_attn_decode_fp8_append": _args_attn_fp8_append,
     "kv_signature_update": _args_kv_signature_update,
@@ -494,6 +497,12 @@ def routed_attn_decode_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel,
     """routed_attn_decode over an 8-bit K/V cache (bf16 queries)."""
     args, _keep = _args_attn_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, workspace, stream)
     _check(lib().routed_attn_decode_fp8(*args))
+
+
+def routed_attn_prefill_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, workspace, stream=None):
+    """routed_attn_prefill over an 8-bit K/V cache (bf16 queries); the prefill workspace."""
+    args, _keep = _args_attn_fp8(cfg, rows, k_codes, v_codes, k_scales, v_scales, sel, out, workspace, stream)
+    _check(lib().routed_attn_prefill_fp8(*args))
 
 
 def routed_attn_decode_append(cfg, rows, k_cache, v_cache, sel, out, workspace, span_mean, run_sum, old_len, new_len,

@@ -367,6 +367,20 @@ ra_status routed_attn_decode_fp8(const ra_config *cfg, const ra_rows *rows, cons
                       "routed_attn_decode_fp8 launch");
 }
 
+ra_status routed_attn_prefill_fp8(const ra_config *cfg, const ra_rows *rows, const uint8_t *k_codes,
+                                  const uint8_t *v_codes, const float *k_scales, const float *v_scales,
+                                  const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+    ra_status s = check_attn(cfg, rows, k_codes, v_codes, sel, out, workspace, workspace_bytes, RA_OP_PREFILL);
+    if (s) return s;
+    if (cfg->dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "8-bit caches go with bf16 queries (cfg->dtype RA_BF16)");
+    if (rows->n_rows > 0 && (!k_scales || !v_scales)) return fail(RA_EINVAL, "NULL k_scales or v_scales");
+    if (rows->n_rows == 0) return ok();
+    return hip_status(ra::launch_prefill_fp8(row_args(cfg, rows), k_codes, v_codes, k_scales, v_scales, sel, out,
+                                             workspace, (hipStream_t)stream),
+                      "routed_attn_prefill_fp8 launch");
+}
+
 // ------------------------------------------------------------------- token-level cold retrieval
 }  // extern "C"
 

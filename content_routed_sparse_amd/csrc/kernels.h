@@ -64,6 +64,10 @@ size_t prefill_workspace_bytes(const RowArgs &a);
 int64_t prefill_grid_items(const RowArgs &a);  // as decode_grid_items
 hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out,
                           void *ws, hipStream_t st);
+// Prefill over an 8-bit cache (bf16 queries): codes K8/V8 with row scales ks/vs; the same
+// workspace as bf16.
+hipError_t launch_prefill_fp8(const RowArgs &a, const uint8_t *K8, const uint8_t *V8, const float *ks,
+                              const float *vs, const int32_t *sel, float *out, void *ws, hipStream_t st);
 
 // Dense causal attention (bf16): every key at or before each row's position; no workspace.
 hipError_t launch_dense(const RowArgs &a, const void *K, const void *V, float *out, hipStream_t st);

@@ -387,8 +387,11 @@ int64_t prefill_grid_items(const RowArgs &a) {
     return m > count ? m : count;
 }
 
-hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out, void *ws,
-                          hipStream_t st) {
+namespace {
+
+// The dispatch, the tiles and the merge; ks, vs: row scales of an 8-bit cache (null for bf16/fp32).
+hipError_t prefill_impl(const RowArgs &a, const void *K, const void *V, const float *ks, const float *vs,
+                        const int32_t *sel, float *out, void *ws, hipStream_t st) {
     if (a.n_rows == 0) return hipSuccess;
     const PrefillLayout L = prefill_layout(a);
     char *w = (char *)ws;
@@ -422,10 +425,22 @@ hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const 
                        tile_off, tiles, L.n_exp, MT);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    TileArgs ta{a, K, V, tile_off, list, list_t, tiles, records, L.n_exp, L.max_tiles, L.span_slots, NE};
+    TileArgs ta{a, K, V, ks, vs, tile_off, list, list_t, tiles, records, L.n_exp, L.max_tiles, L.span_slots, NE};
     e = launch_prefill_tiles(ta, st);
     if (e != hipSuccess) return e;
     return launch_combine(a, records, local, out, st);
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const RowArgs &a, const void *K, const void *V, const int32_t *sel, float *out, void *ws,
+                          hipStream_t st) {
+    return prefill_impl(a, K, V, nullptr, nullptr, sel, out, ws, st);
+}
+
+hipError_t launch_prefill_fp8(const RowArgs &a, const uint8_t *K8, const uint8_t *V8, const float *ks,
+                              const float *vs, const int32_t *sel, float *out, void *ws, hipStream_t st) {
+    return prefill_impl(a, K8, V8, ks, vs, sel, out, ws, st);
 }
 
 }  // namespace ra

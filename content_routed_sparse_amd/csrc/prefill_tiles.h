@@ -8,6 +8,7 @@ namespace ra {
 struct TileArgs {
     RowArgs a;
     const void *K, *V;
+    const float *ks, *vs;            // row scales of an 8-bit cache (K, V are then E4M3 codes), else null
     const int32_t *tile_off, *list;  // tile count at tile_off[n_exp]; entries
     const int64_t *list_t;           // the entries' row positions
     const int4 *tiles;               // (expert, first entry, entries)

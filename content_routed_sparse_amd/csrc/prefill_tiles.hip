@@ -272,12 +272,23 @@ __device__ __forceinline__ float group_sum4(float x) {
 // exponentiate.  If some query's row sum ends above 2^kFastLog2 (or is not finite), a weight
 // may have grown past it: the tile then finds every query's largest score in a sweep over its
 // keys (max_chunk) and runs again with m set to it, so that no weight exceeds 1.  Weights thus
-// stay below 2^kFastLog2, far from fp32 overflow.
+// stay below 2^kFastLog2, far from fp32 overflow; a query whose output accumulator still overflows
+// (weights up to 2^kFastLog2 times values beyond ~2^87) takes the second pass as well.  So does
+// a query whose row sum ends below 2^-kFastLog2: in exact arithmetic the first chunk's largest
+// key alone weighs 1, but the fast pass forms each exponent with one fused multiply-add against
+// the rounded m, so with scores of magnitude ~2^30 and more the largest key's exponent is m's
+// rounding error, up to half an ulp of m either way, and every weight can underflow to 0.
 // Row sums l = sum_k P[q][k] are taken over the same bf16 weights that the P.V product uses:
 // one v_dot2_f32_bf16 against (1, 1) per packed pair, into a per-lane fp32 sum over the lane's
 // own keys (the 4 lane groups of a query are added once, at the end: group_sum4).
 constexpr float kFastLog2 = 40.f;
 constexpr float kFastLimit = 1099511627776.f;  // 2^kFastLog2
+
+// A query's fast-pass result stands when its row sum is in [2^-kFastLog2, 2^kFastLog2] (false for
+// NaN) and its output accumulator is finite.
+__device__ __forceinline__ bool fast_sum_ok(float l_total) {
+    return l_total >= 1.f / kFastLimit && l_total <= kFastLimit;
+}
 
 // S^T = K Q^T for one chunk and kQG query groups: sc[g][kt][i] = S^T[key 16kt + 4lg + i][query lr
 // of group g].  Each K operand read from LDS feeds the kQG groups' MFMAs.
@@ -302,9 +313,25 @@ __device__ __forceinline__ void qk_chunk(const uint16_t *Kc, const int (&kof)[D 
     }
 }
 
+// A key's weight 2^(s c - m).  The fast pass takes the exponent from one fused multiply-add
+// (exact before its final rounding).  The pass against the exact maximum (EXACT) rounds the
+// product first: with m = RN(max s * c), rounding's monotonicity makes every exponent <= 0 and the
+// largest key's exactly 0, whatever the scores' magnitude (with the fused form the largest key's
+// exponent is the rounding error of m, up to half an ulp of m: 2^64 and more once |m| >= 2^30).
+template <bool EXACT>
+__device__ __forceinline__ float key_weight(float s, float c, float nm) {
+    if constexpr (EXACT) {
+#pragma clang fp contract(off)
+        const float z = s * c;
+        return __builtin_amdgcn_exp2f(z + nm);
+    } else {
+        return __builtin_amdgcn_exp2f(fmaf(s, c, nm));
+    }
+}
+
 // The chunk's weights 2^(s c - m) as bf16 pairs (pk[kt][i/2]); with TRACK, the reference
 // bookkeeping (maxima) too.
-template <bool MASK, bool TRACK>
+template <bool MASK, bool TRACK, bool EXACT>
 __device__ __forceinline__ void softmax_chunk(f32x4_t (&sc)[kChunk / 16], int lim, int lg, float scale_log2, float &m,
                                               uint32_t (&pk)[kChunk / 16][2]) {
     constexpr int KT = kChunk / 16;
@@ -331,7 +358,7 @@ __device__ __forceinline__ void softmax_chunk(f32x4_t (&sc)[kChunk / 16], int li
     for (int kt = 0; kt < KT; ++kt) {
         float pv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], scale_log2, nm));
+        for (int i = 0; i < 4; ++i) pv[i] = key_weight<EXACT>(sc[kt][i], scale_log2, nm);
         pk[kt][0] = pack_bf16x2(pv[0], pv[1]);
         pk[kt][1] = pack_bf16x2(pv[2], pv[3]);
     }
@@ -408,7 +435,7 @@ struct Stage {
 // computed (the buffers are distinct arrays, so the compiler does not wait for those loads
 // before reading chunk c).  The first chunk takes maxima and fixes each query's reference where
 // it is unset.  `preloaded`: K(0) and V(0) are already being loaded.
-template <int D>
+template <int D, bool EXACT>
 __device__ __forceinline__ void fast_sweep(const Stage<D> &st, const TileKeys &tk, bool preloaded, const int (&qlim)[kQG],
                                            const int (&kof)[D / 32], const int (&vof)[D / 64][4],
                                            const bf16x8_t (&qb)[kQG][D / 32], float (&m)[kQG], float (&l)[kQG],
@@ -438,7 +465,7 @@ __device__ __forceinline__ void fast_sweep(const Stage<D> &st, const TileKeys &t
         for (int g = 0; g < kQG; ++g) {
             int lim = qlim[g] - c * kChunk;
             lim = lim < 0 ? 0 : (lim > kChunk ? kChunk : lim);
-            softmax_chunk<MASK, TRACK>(sc[g], lim, lg, scale_log2, m[g], pk[g]);
+            softmax_chunk<MASK, TRACK, EXACT>(sc[g], lim, lg, scale_log2, m[g], pk[g]);
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -486,16 +513,247 @@ __device__ __forceinline__ void max_sweep(const Stage<D> &st, const TileKeys &tk
     }
 }
 
+// ---------------------------------------------------------------------- 8-bit cache tiles
+// Over an 8-bit cache (E4M3 codes + one fp32 scale per row) the tiles stage a chunk's codes (kChunk
+// rows of D bytes, K and V) and its rows' scales into LDS with direct loads, then convert the codes
+// exactly to bf16 (an E4M3 value has a 4-bit significand, which bf16 holds exactly) into the
+// swizzled K and V buffers that the MFMA operand reads use.  The scales stay apart: each key's
+// score is s_k (q . code_k); the P.V weights carry s_v (P' = bf16(P s_v)) while the row sums add
+// the unscaled bf16 weights, so the result is sum P s_v code_v / sum P.  One bf16 buffer pair:
+// a chunk is converted after everyone has finished the previous one (two barriers per chunk),
+// and the next chunk's codes load during the current chunk's products.
+
+template <int D>
+struct StageF8 {
+    uint16_t *kb, *vb;     // bf16 codes of the current chunk, swizzled as chunk_rows lays them out
+    uint8_t *kc, *vc;      // the codes of the chunk being loaded, row-major
+    float *ks[2], *vs[2];  // the rows' scales, by chunk parity
+};
+
+struct TileKeysF8 {
+    const uint8_t *Ksp, *Vsp;  // codes of the tile's first key row
+    const float *ksp, *vsp;    // scales of the tile's first key row
+    int n_load, n_keys, full_end;
+};
+
+// Direct global -> LDS loads of chunk c's code rows (rows at or past n repeat row n - 1; masked
+// later) and of its rows' scales.  16 bytes per lane: 1024 / D rows per wave instruction.
+template <int D>
+__device__ __forceinline__ void chunk_codes(const uint8_t *base, uint8_t *dst, const float *sbase, float *sdst, int c,
+                                            int n, int wave, int lane) {
+    constexpr int ROWS = 1024 / D;
+    constexpr int NI = kChunk / ROWS;
+    constexpr int LPR = D / 16;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, n * D, 0x00020000);
+    const int rl = lane / LPR, piece = lane % LPR;
+#pragma unroll
+    for (int ii = wave; ii < NI; ii += kMfmaWaves) {
+        int g = c + ii * ROWS + rl;
+        g = g < n ? g : n - 1;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (RA_LDS void *)(dst + ii * ROWS * D), 16, g * D + piece * 16, 0, 0,
+                                                 0);
+    }
+    if (wave == kMfmaWaves - 1) {  // the chunk's kChunk = 64 scales: one dword per lane
+        const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc((void *)sbase, 0, n * 4, 0x00020000);
+        int g = c + lane;
+        g = g < n ? g : n - 1;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (RA_LDS void *)sdst, 4, g * 4, 0, 0, 0);
+    }
+}
+
+// The staged codes of a chunk -> bf16 in the swizzled buffers (K, and V when WITH_V): a thread
+// converts 32 codes of one row per step (v_cvt_pk_f32_fp8, then an exact bf16 packing).
+template <int D, bool WITH_V>
+__device__ __forceinline__ void codes_to_bf16(const StageF8<D> &st, int tid) {
+    constexpr int SEG = D / 32;         // 32-code segments per row
+    constexpr int U = kChunk * SEG;     // segments per tensor
+#pragma unroll 1
+    for (int u = tid; u < (WITH_V ? 2 : 1) * U; u += kMfmaThreads) {  // (one segment in registers at a time)
+        const bool is_v = u >= U;
+        const int uu = is_v ? u - U : u;
+        const int r = uu / SEG, sgm = uu % SEG;
+        const uint8_t *src = (is_v ? st.vc : st.kc) + r * D + sgm * 32;
+        const uint4 a = *reinterpret_cast<const uint4 *>(src);
+        const uint4 b = *reinterpret_cast<const uint4 *>(src + 16);
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t h[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);  // bytes 0, 1
+            const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);   // bytes 2, 3
+            h[2 * i] = pack_bf16x2(lo.x, lo.y);
+            h[2 * i + 1] = pack_bf16x2(hi.x, hi.y);
+        }
+        uint16_t *dst = is_v ? st.vb : st.kb;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int piece = 4 * sgm + qq;  // 8-element piece of the row
+            const int pos = piece ^ (is_v ? vswz<D>(r) : kswz<D>(r));
+            *reinterpret_cast<uint4 *>(dst + r * D + 8 * pos) =
+                make_uint4(h[4 * qq], h[4 * qq + 1], h[4 * qq + 2], h[4 * qq + 3]);
+        }
+    }
+}
+
+// softmax_chunk for the 8-bit tiles: the weights 2^(s c - m) are added to the lane's row sum l in
+// fp32, and pkv holds them times the keys' value scales as bf16 pairs (for P.V).  (The bf16 tiles
+// sum the bf16-rounded weights they multiply with; here the weights that multiply carry s_v, so
+// the sum takes the unrounded ones: a difference of bf16 rounding, ~2^-9 per weight.)
+template <bool MASK, bool TRACK, bool EXACT>
+__device__ __forceinline__ void softmax_chunk_f8(f32x4_t (&sc)[kChunk / 16], int lim, int lg, float scale_log2,
+                                                 float &m, float &l, const float *vs_chunk,
+                                                 uint32_t (&pkv)[kChunk / 16][2]) {
+    constexpr int KT = kChunk / 16;
+    constexpr float NEG = -__builtin_huge_valf();
+    if (MASK) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[kt][i] = 16 * kt + 4 * lg + i < lim ? sc[kt][i] : NEG;
+    }
+    if (TRACK) {
+        float cmax = NEG;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, sc[kt][i]);
+        const float mx = group_max4(cmax) * scale_log2;
+        m = m == NEG ? mx : m;
+    }
+    const float nm = m != NEG ? -m : 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[i] = key_weight<EXACT>(sc[kt][i], scale_log2, nm);
+        l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        const float4 vsc = *reinterpret_cast<const float4 *>(vs_chunk + 16 * kt + 4 * lg);  // keys' value scales
+        pkv[kt][0] = pack_bf16x2(pv[0] * vsc.x, pv[1] * vsc.y);
+        pkv[kt][1] = pack_bf16x2(pv[2] * vsc.z, pv[3] * vsc.w);
+    }
+}
+
+// The keys' scales applied to a chunk's raw scores: S = s_k (q . code_k) (lane keys 16 kt + 4 lg + i).
+__device__ __forceinline__ void scale_scores(f32x4_t (&sc)[kQG][kChunk / 16], const float *ks_chunk, int lg) {
+#pragma unroll
+    for (int kt = 0; kt < kChunk / 16; ++kt) {
+        const float4 k4 = *reinterpret_cast<const float4 *>(ks_chunk + 16 * kt + 4 * lg);
+#pragma unroll
+        for (int g = 0; g < kQG; ++g) {
+            sc[g][kt][0] *= k4.x;
+            sc[g][kt][1] *= k4.y;
+            sc[g][kt][2] *= k4.z;
+            sc[g][kt][3] *= k4.w;
+        }
+    }
+}
+
+// fast_sweep over the 8-bit cache.  Chunk c: codes(c) landed -> barrier (everyone done with
+// chunk c - 1's bf16 buffers) -> convert -> barrier -> the loads of chunk c + 1's codes -> products.
+template <int D, bool EXACT>
+__device__ __forceinline__ void fast_sweep_f8(const StageF8<D> &st, const TileKeysF8 &tk, bool preloaded,
+                                              const int (&qlim)[kQG], const int (&kof)[D / 32],
+                                              const int (&vof)[D / 64][4], const bf16x8_t (&qb)[kQG][D / 32],
+                                              float (&m)[kQG], float (&l)[kQG], f32x4_t (&o)[kQG][D / 16], int wave,
+                                              int lane, int lg, int tid, float scale_log2) {
+    constexpr int KT = kChunk / 16;
+    const int C = (tk.n_keys + kChunk - 1) / kChunk;
+    if (!preloaded) {
+        __syncthreads();  // everyone is done with the code buffers
+        chunk_codes<D>(tk.Ksp, st.kc, tk.ksp, st.ks[0], 0, tk.n_load, wave, lane);
+        chunk_codes<D>(tk.Vsp, st.vc, tk.vsp, st.vs[0], 0, tk.n_load, wave, lane);
+    }
+    auto iter = [&](auto mask, auto track, int c) {
+        constexpr bool MASK = decltype(mask)::value, TRACK = decltype(track)::value;
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of chunk c landed
+        __syncthreads();  // everyone's landed; everyone is done with chunk c - 1
+        codes_to_bf16<D, true>(st, tid);
+        __syncthreads();  // chunk c in bf16; the code buffers are free
+        if (c + 1 < C) {
+            chunk_codes<D>(tk.Ksp, st.kc, tk.ksp, st.ks[(c + 1) & 1], (c + 1) * kChunk, tk.n_load, wave, lane);
+            chunk_codes<D>(tk.Vsp, st.vc, tk.vsp, st.vs[(c + 1) & 1], (c + 1) * kChunk, tk.n_load, wave, lane);
+        }
+        f32x4_t sc[kQG][KT];
+        qk_chunk<D>(st.kb, kof, qb, sc);
+        scale_scores(sc, st.ks[c & 1], lg);
+        uint32_t pkv[kQG][KT][2];
+#pragma unroll
+        for (int g = 0; g < kQG; ++g) {
+            int lim = qlim[g] - c * kChunk;
+            lim = lim < 0 ? 0 : (lim > kChunk ? kChunk : lim);
+            softmax_chunk_f8<MASK, TRACK, EXACT>(sc[g], lim, lg, scale_log2, m[g], l[g], st.vs[c & 1], pkv[g]);
+        }
+        pv_chunk<D>(st.vb, vof, pkv, o);
+    };
+    using BF = std::integral_constant<bool, false>;
+    using BT = std::integral_constant<bool, true>;
+    if (kChunk <= tk.full_end) iter(BF{}, BT{}, 0);
+    else iter(BT{}, BT{}, 0);
+    for (int c = 1; c < C; ++c) {
+        if ((c + 1) * kChunk <= tk.full_end) iter(BF{}, BF{}, c);
+        else iter(BT{}, BF{}, c);
+    }
+}
+
+// max_sweep over the 8-bit cache: every query's largest scaled score (times scale_log2).
+template <int D>
+__device__ __forceinline__ void max_sweep_f8(const StageF8<D> &st, const TileKeysF8 &tk, const int (&qlim)[kQG],
+                                             const int (&kof)[D / 32], const bf16x8_t (&qb)[kQG][D / 32],
+                                             float (&mx)[kQG], int wave, int lane, int lg, int tid, float scale_log2) {
+    constexpr float NEG = -__builtin_huge_valf();
+    const int C = (tk.n_keys + kChunk - 1) / kChunk;
+    __syncthreads();  // everyone is done with the buffers
+    chunk_codes<D>(tk.Ksp, st.kc, tk.ksp, st.ks[0], 0, tk.n_load, wave, lane);
+    for (int c = 0; c < C; ++c) {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        codes_to_bf16<D, false>(st, tid);
+        __syncthreads();
+        if (c + 1 < C) chunk_codes<D>(tk.Ksp, st.kc, tk.ksp, st.ks[(c + 1) & 1], (c + 1) * kChunk, tk.n_load, wave, lane);
+        f32x4_t sc[kQG][kChunk / 16];
+        qk_chunk<D>(st.kb, kof, qb, sc);
+        scale_scores(sc, st.ks[c & 1], lg);
+#pragma unroll
+        for (int g = 0; g < kQG; ++g) {
+            int lim = qlim[g] - c * kChunk;
+            lim = lim < 0 ? 0 : (lim > kChunk ? kChunk : lim);
+            float cmax = NEG;
+#pragma unroll
+            for (int kt = 0; kt < kChunk / 16; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, 16 * kt + 4 * lg + i < lim ? sc[g][kt][i] : NEG);
+            mx[g] = fmaxf(mx[g], group_max4(cmax) * scale_log2);
+        }
+    }
+}
+
+// 1 when some element of a query's output accumulator (over the 4 lane groups that hold it) is not
+// finite: the fast pass's weights (up to 2^kFastLog2 against the first chunk's maximum) times large
+// values can overflow fp32 although the row sum stays in range; such a query takes the second pass
+// too (weights <= 1).
+template <int D>
+__device__ __forceinline__ bool acc_overflow(const f32x4_t (&og)[D / 16]) {
+    float bad = 0.f;
+#pragma unroll
+    for (int et = 0; et < D / 16; ++et)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bad = __builtin_isfinite(og[et][i]) ? bad : 1.f;
+    return group_max4(bad) > 0.f;
+}
+
 // Transposed formulation.  S^T = K Q^T puts keys on the MFMA rows and queries on the columns,
 // so lane (lg, lr) holds keys 16kt + 4lg + i of query lr: every per-query quantity (running
 // max, sum, rescale of the output) is lane-local, and only the max/sum across the 4 lane
 // groups of a query needs cross-lane steps.  O^T = V^T P^T then takes P straight from the S^T
 // registers: its 32-key K dimension is ordered as the lanes hold it (keys 4lg..4lg+3 of two
 // 16-key tiles per lane group), and V^T is read from LDS in the same order.
-template <int D>
+// F8: the cache holds E4M3 codes (K, V) with one fp32 scale per row (ks, vs); otherwise bf16.
+template <int D, bool F8>
 __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU))) tile_mfma(const uint16_t *__restrict__ q,
-                                                          const uint16_t *__restrict__ K,
-                                                          const uint16_t *__restrict__ V,
+                                                          const void *__restrict__ K,
+                                                          const void *__restrict__ V,
+                                                          const float *__restrict__ ks,
+                                                          const float *__restrict__ vs,
                                                           const int32_t *__restrict__ tile_off,
                                                           const int32_t *__restrict__ list,
                                                           const int64_t *__restrict__ list_t,
@@ -506,15 +764,29 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     constexpr int KS = D / 32;   // k-steps of the QK product
     constexpr int ET = D / 16;   // 16-wide e tiles of the PV product
     constexpr float NEG = -__builtin_huge_valf();
-    // staged chunks: K and V buffers 0 and 1 (kChunk rows of D bf16 each)
-    __shared__ uint16_t kb0[kChunk * D], kb1[kChunk * D], vb0[kChunk * D], vb1[kChunk * D];
+    // staged chunks: bf16 K and V buffers 0 and 1 (kChunk rows of D bf16 each); the 8-bit tiles
+    // use one bf16 pair and stage the codes and scales of the chunk being loaded beside it
+    __shared__ __align__(16) uint16_t kb0[kChunk * D], vb0[kChunk * D];
+    __shared__ __align__(16) uint16_t kb1[F8 ? 8 : kChunk * D], vb1[F8 ? 8 : kChunk * D];
+    __shared__ __align__(16) uint8_t kc8[F8 ? kChunk * D : 16], vc8[F8 ? kChunk * D : 16];
+    __shared__ __align__(16) float ks8[F8 ? 2 * kChunk : 4], vs8[F8 ? 2 * kChunk : 4];
     __shared__ int redo_s[kMfmaWaves];
     __shared__ unsigned long long wmax_s[kMfmaWaves], wmin_s[kMfmaWaves];
     const Stage<D> st{kb0, kb1, vb0, vb1};
+    StageF8<D> st8;  // (assigned field by field: a braced constant initializer of LDS addresses
+    st8.kb = kb0;    //  would become a static one, which the device compiler rejects)
+    st8.vb = vb0;
+    st8.kc = kc8;
+    st8.vc = vc8;
+    st8.ks[0] = ks8;
+    st8.ks[1] = ks8 + kChunk;
+    st8.vs[0] = vs8;
+    st8.vs[1] = vs8 + kChunk;
 
     // all kernel arguments in one round trip (otherwise some are fetched only where first used)
     asm volatile("" ::"s"(q), "s"(K), "s"(V), "s"(tile_off), "s"(list), "s"(list_t), "s"(tiles), "s"(records),
                  "s"(n_exp), "s"(span_slots), "s"(NE), "s"(S), "s"(cap), "s"(scale_log2), "s"(n_blocks));
+    if constexpr (F8) asm volatile("" ::"s"(ks), "s"(vs));
     const int64_t tile = xcd_tile(blockIdx.x, n_blocks);
     // the tile count and this tile's descriptor in one round trip (a descriptor past the count is
     // stale but in bounds: max_tiles of them are allocated)
@@ -529,8 +801,12 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     const int64_t j = expert % span_slots;
     const int64_t sg = expert / span_slots;
     const int64_t lo = j * S;
-    const uint16_t *Ksp = K + (sg * cap + lo) * D;  // the span's first key row
-    const uint16_t *Vsp = V + (sg * cap + lo) * D;
+    const uint16_t *Ksp = static_cast<const uint16_t *>(K) + (sg * cap + lo) * D;  // the span's first key row
+    const uint16_t *Vsp = static_cast<const uint16_t *>(V) + (sg * cap + lo) * D;
+    const uint8_t *Ksp8 = static_cast<const uint8_t *>(K) + (sg * cap + lo) * D;  // (8-bit cache)
+    const uint8_t *Vsp8 = static_cast<const uint8_t *>(V) + (sg * cap + lo) * D;
+    const float *ksp = F8 ? ks + sg * cap + lo : nullptr;
+    const float *vsp = F8 ? vs + sg * cap + lo : nullptr;
     const int n_span = (int)(cap - lo < S ? cap - lo : S);  // keys of the span inside the cache
 
     // One round trip: the tile's entries and their positions, this lane's own row (for its
@@ -568,8 +844,13 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     // the first chunk's LDS loads (K and V of chunk 0) fly with the query loads,
     // up to the span's end (issued after them: the compiler waits for everything before using a
     // load's register while LDS loads are outstanding)
-    chunk_rows<D, false>(Ksp, st.kb0, 0, n_span, wave, lane);
-    chunk_rows<D, true>(Vsp, st.vb0, 0, n_span, wave, lane);
+    if constexpr (F8) {
+        chunk_codes<D>(Ksp8, st8.kc, ksp, st8.ks[0], 0, n_span, wave, lane);
+        chunk_codes<D>(Vsp8, st8.vc, vsp, st8.vs[0], 0, n_span, wave, lane);
+    } else {
+        chunk_rows<D, false>(Ksp, st.kb0, 0, n_span, wave, lane);
+        chunk_rows<D, true>(Vsp, st.vb0, 0, n_span, wave, lane);
+    }
     // the tile's first and last positions (wave reductions, then across the waves in LDS)
     {
         unsigned long long vmax = tid < n ? (unsigned long long)t_blk : 0ull;
@@ -594,7 +875,9 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     if (hi > cap) hi = cap;
     const int n_keys = (int)(hi - lo);
     // chunks that end by full_end need no mask (key offsets from lo are ints: a span has S keys)
-    const TileKeys tk{Ksp, Vsp, n_keys, n_keys, (int)((tmin + 1 < hi ? tmin + 1 : hi) - lo)};
+    const int full_end = (int)((tmin + 1 < hi ? tmin + 1 : hi) - lo);
+    const TileKeys tk{Ksp, Vsp, n_keys, n_keys, full_end};
+    const TileKeysF8 tk8{Ksp8, Vsp8, ksp, vsp, n_keys, n_keys, full_end};
     int qlim[kQG];
 #pragma unroll
     for (int g = 0; g < kQG; ++g) {
@@ -619,7 +902,8 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int g = 0; g < kQG; ++g) unset[g] = NEG;
     reset(unset);
-    fast_sweep<D>(st, tk, true, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
+    if constexpr (F8) fast_sweep_f8<D, false>(st8, tk8, true, qlim, kof, vof, qb, m, l, o, wave, lane, lg, tid, scale_log2);
+    else fast_sweep<D, false>(st, tk, true, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
 
     // records: header (m, l, s, 0), then o / (l s) as fp16 per valid row, s = 2^-k with k chosen
     // so that the row's largest |o / l| lands in [2^14, 2^15): every value keeps 11 significant
@@ -660,15 +944,15 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
         }
     };
 
-    // Each entry decides on its own whether it needs the second pass: its row sum passed
-    // 2^kFastLog2 (or is not finite).  Entries that do not store their records now, and keep
+    // Each entry decides on its own whether it needs the second pass: its row sum left
+    // [2^-kFastLog2, 2^kFastLog2] (or is not finite), or its output accumulator overflowed.  Entries that do not store their records now, and keep
     // them, so an entry's result never depends on which other entries share its tile.  The
     // pass itself runs for the whole block (every wave takes the same path through the loads).
     bool need[kQG], done[kQG];
     bool need_any = false;
 #pragma unroll
     for (int g = 0; g < kQG; ++g) {
-        need[g] = x_own[g] >= 0 && !(group_sum4(l[g]) <= kFastLimit);
+        need[g] = x_own[g] >= 0 && (!fast_sum_ok(group_sum4(l[g])) || acc_overflow<D>(o[g]));
         done[g] = x_own[g] >= 0 && !need[g];
         need_any = need_any || need[g];
     }
@@ -683,19 +967,25 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
         float mx[kQG];
 #pragma unroll
         for (int g = 0; g < kQG; ++g) mx[g] = NEG;
-        max_sweep<D>(st, tk, qlim, kof, qb, mx, wave, lane, lg, scale_log2);
-        reset(mx);
-        fast_sweep<D>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
+        if constexpr (F8) {
+            max_sweep_f8<D>(st8, tk8, qlim, kof, qb, mx, wave, lane, lg, tid, scale_log2);
+            reset(mx);
+            fast_sweep_f8<D, true>(st8, tk8, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, tid, scale_log2);
+        } else {
+            max_sweep<D>(st, tk, qlim, kof, qb, mx, wave, lane, lg, scale_log2);
+            reset(mx);
+            fast_sweep<D, true>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
+        }
         store(need);
     }
 }
 
-template <int D>
+template <int D, bool F8>
 hipError_t mfma_launch(const TileArgs &t, hipStream_t st) {
     const RowArgs &a = t.a;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    hipLaunchKernelGGL((tile_mfma<D>), dim3((unsigned)t.max_tiles), dim3(kMfmaThreads), 0, st, (const uint16_t *)a.q,
-                       (const uint16_t *)t.K, (const uint16_t *)t.V, t.tile_off, t.list, t.list_t, t.tiles, t.records,
+    hipLaunchKernelGGL((tile_mfma<D, F8>), dim3((unsigned)t.max_tiles), dim3(kMfmaThreads), 0, st,
+                       (const uint16_t *)a.q, t.K, t.V, t.ks, t.vs, t.tile_off, t.list, t.list_t, t.tiles, t.records,
                        t.n_exp, t.span_slots, t.NE, a.S, a.cap, scale_log2, t.max_tiles);
     return hipGetLastError();
 }
@@ -843,11 +1133,13 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
 #pragma unroll
         for (int gi = 0; gi < kQG; ++gi) unset[gi] = NEG;
         reset(unset);
-        fast_sweep<D>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
-        // as in the routed tiles: a row sum past 2^kFastLog2 sends the tile to a second pass
+        fast_sweep<D, false>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
+        // as in the routed tiles: a row sum outside [2^-kFastLog2, 2^kFastLog2] or an overflowed
+        // accumulator sends the tile to a second pass
         bool redo_q = false;
 #pragma unroll
-        for (int gi = 0; gi < kQG; ++gi) redo_q = redo_q || (active[gi] && !(group_sum4(l[gi]) <= kFastLimit));
+        for (int gi = 0; gi < kQG; ++gi)
+            redo_q = redo_q || (active[gi] && (!fast_sum_ok(group_sum4(l[gi])) || acc_overflow<D>(o[gi])));
         const bool wave_redo = __ballot(redo_q) != 0;  // (all lanes vote: a ballot counts active lanes only)
         if (lane == 0) redo_s[wave] = wave_redo ? 1 : 0;
         __syncthreads();
@@ -860,7 +1152,7 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
         for (int g = 0; g < kQG; ++g) mx[g] = NEG;
             max_sweep<D>(st, tk, qlim, kof, qb, mx, wave, lane, lg, scale_log2);
             reset(mx);
-            fast_sweep<D>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
+            fast_sweep<D, true>(st, tk, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
         }
         // out = o / l (l summed over the query's 4 lane groups: every lane holds the total)
 #pragma unroll
@@ -901,7 +1193,8 @@ hipError_t launch_dense(const RowArgs &a, const void *K, const void *V, float *o
 
 hipError_t launch_prefill_tiles(const TileArgs &t, hipStream_t st) {
     const RowArgs &a = t.a;
-    if (a.dtype == RA_BF16) return a.d == 64 ? mfma_launch<64>(t, st) : mfma_launch<128>(t, st);
+    if (t.ks != nullptr) return a.d == 64 ? mfma_launch<64, true>(t, st) : mfma_launch<128, true>(t, st);
+    if (a.dtype == RA_BF16) return a.d == 64 ? mfma_launch<64, false>(t, st) : mfma_launch<128, false>(t, st);
     return a.d == 64 ? valu_launch<float, 64>(t, st) : valu_launch<float, 128>(t, st);
 }
 

@@ -233,6 +233,18 @@ ra_status routed_attn_decode_fp8(const ra_config *cfg, const ra_rows *rows, cons
                                  const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* routed_attn_prefill_fp8 -- routed_attn_prefill over an 8-bit K/V cache (bf16 queries), the
+ * path a chunk of new tokens takes when the cache is stored in 8 bits (the release post's
+ * "Limitations and next steps" plan 8-bit quantisation so that long contexts fit).  The same
+ * grouping, tiles and merge as routed_attn_prefill: each tile converts a staged chunk of codes
+ * exactly to bf16 for the MFMAs and applies the rows' scales to the scores (keys) and to the P.V
+ * weights (values), with fp32 softmax state.  Same workspace size as routed_attn_prefill; the
+ * same handling of repeated and unroutable selection entries. */
+ra_status routed_attn_prefill_fp8(const ra_config *cfg, const ra_rows *rows, const uint8_t *k_codes,
+                                  const uint8_t *v_codes, const float *k_scales, const float *v_scales,
+                                  const int32_t *sel, float *out, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
 /* routed_attn_decode_append / routed_attn_decode_fp8_append -- the decode call together with
  * the step's summary update: the same as routed_attn_decode (resp. _fp8) followed by
  * span_summary_update (resp. _fp8) of tokens [old_len[b], new_len[b]) into span_mean / run_sum.

@@ -109,12 +109,15 @@ class Case:
         assert np.array_equal(dm.view(np.uint32), means[:, :n].view(np.uint32)), "span means differ"
         assert np.array_equal(dr.view(np.uint32), run.view(np.uint32)), "running sums differ"
 
-    def check(self, seqs, positions, q_rows, row_index, heads=None, scores=True):
+    def check(self, seqs, positions, q_rows, row_index, heads=None, scores=True, scale_abs=False):
         """Compare selection (tie-aware), scores and outputs of the given rows with the oracle.
 
         The oracle computes every (row, head) of a sequence in one call; a row whose device
         selection is a valid near-tie alternative is compared with the oracle evaluated on that
-        selection (a second call for those rows only)."""
+        selection (a second call for those rows only).  With scale_abs, a row's max-abs error is
+        taken relative to max(1, the reference row's largest magnitude): for caches that hold
+        rows of values near 3e30, where an absolute bound made for unit-scale values means
+        nothing."""
         w = self.w
         sel = self.pipe.sel.cpu().numpy()
         out = self.pipe.out.cpu().numpy()
@@ -129,6 +132,8 @@ class Case:
 
         def record(ri, h, ref):
             ma, rel = O.output_errors(out[ri, h], ref)
+            if scale_abs:
+                ma /= max(1.0, float(np.abs(ref).max()))
             stats["max_abs"] = max(stats["max_abs"], ma)
             stats["max_rel"] = max(stats["max_rel"], rel)
 

@@ -104,6 +104,13 @@ def test_fp8_entry_points_validate_before_launch():
     assert lib.routed_attn_decode_fp8(ctypes.byref(c), ctypes.byref(rows()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                       FAKE, 16, None) == 3
     assert lib.ra_last_error().decode() != ""
+    # prefill over the 8-bit cache: the same checks
+    assert lib.routed_attn_prefill_fp8(ctypes.byref(c), ctypes.byref(rows()), FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                       FAKE, ws, None) == 1
+    assert lib.routed_attn_prefill_fp8(ctypes.byref(c32), ctypes.byref(rows()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, ws, None) == 2
+    assert lib.routed_attn_prefill_fp8(ctypes.byref(c), ctypes.byref(rows(8192)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, 16, None) == 3
 
 
 def test_workspace_sizes():

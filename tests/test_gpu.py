@@ -116,6 +116,56 @@ def test_prefill_outlier_keys_force_the_second_pass():
     assert_stats(stats, True)
 
 
+def _plant_ramp_rows(c, positions):
+    """Key and value rows that ramp from -3e30 to 3e30 (bf16) at the given positions of sequence
+    0, every kv head, host and device caches alike."""
+    t = torch.tensor(np.linspace(-3e30, 3e30, c.w.head_dim).astype(np.float32)).to(torch.bfloat16)
+    bits = t.view(torch.int16).numpy().view(np.uint16)
+    kh, vh = c.host[0]
+    for g in range(c.w.num_kv_heads):
+        for p in positions:
+            kh[g, p] = bits
+            vh[g, p] = bits
+            c.K[0, g, p] = t.cuda()
+            c.V[0, g, p] = t.cuda()
+    c._problems.clear()
+
+
+def test_prefill_and_dense_with_rows_near_3e30():
+    """Cache rows of values up to 3e30: scores against them reach ~1e30 (log2 units), where a
+    weight's exponent formed by one fused multiply-add against the rounded maximum would be that
+    rounding error (2^70 and more).  Routed prefill and dense attention stay finite and match the
+    oracle; max-abs is taken relative to the row's magnitude, relative L2 as usual."""
+    w = small("prefill_8k_on_1m", num_q_heads=8, num_kv_heads=2, span_size=32, window=32, top_k=4)
+    prefix, chunk = 1000, 200
+    c = Case(w, [prefix + chunk])
+    _plant_ramp_rows(c, [10, 75, 500, 1010, 1100])  # routable spans, chunk rows' windows
+    c.summarize([0], [prefix], prefix)
+    rows, q = c.chunk_rows(0, prefix, chunk)
+    c.summarize([prefix], [prefix + chunk], chunk)
+    c.attend(rows, ra.RA_OP_PREFILL)
+    c.check_summaries(0)
+    pos = np.arange(prefix, prefix + chunk)
+    stats = c.check([0] * chunk, pos, q, np.arange(chunk), scale_abs=True)
+    assert_stats(stats, True)
+    out = torch.empty(chunk, w.num_q_heads, w.head_dim, device="cuda")
+    ra.attn_dense_causal(c.cfg, rows, c.K, c.V, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = c.problem(0).rows(q, pos, dense=True)["out"]
+    worst_abs, worst_rel, huge = 0.0, 0.0, 0
+    for i in range(chunk):
+        for h in range(w.num_q_heads):
+            ma, rel = O.output_errors(got[i, h], ref[i, h])
+            mag = max(1.0, float(np.abs(ref[i, h]).max()))
+            huge += mag > 1e20
+            worst_abs, worst_rel = max(worst_abs, ma / mag), max(worst_rel, rel)
+    log("  dense: rows=%d (%d near 3e30) scaled max_abs=%.3g max_rel=%.3g" % (chunk * w.num_q_heads, huge,
+                                                                             worst_abs, worst_rel))
+    assert huge > 0
+    assert worst_abs <= O.compare.TOL_ABS["bf16"] and worst_rel <= O.compare.TOL_REL_L2_BF16
+
+
 def test_prefill_chunking_is_bitwise_invariant():
     w = small("prefill_8k_on_1m", span_size=32, window=32, top_k=4)
     _, _, out1, sel1 = run_prefill(w, 1000, 600, pieces=1)

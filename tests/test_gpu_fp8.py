@@ -197,3 +197,109 @@ def test_decode_1m_over_the_8bit_cache_full():
     stats = c.check([0], [L - 1], q, [0])
     log("  decode_1m fp8: max_abs %.3g max_rel %.3g" % (stats["max_abs"], stats["max_rel"]))
     assert_stats(stats, True)
+
+
+# ----------------------------------------------------------------------------- prefill, 8-bit
+def prefill_fp8(c, prefix, chunk, pieces=1):
+    """Setup summaries of the prefix, then per piece of the chunk: the piece's summary update,
+    routing, selection and routed_attn_prefill_fp8 of its rows; returns (out, sel) of the chunk."""
+    c.summarize([0], [prefix], max(prefix, 1))
+    bounds = np.linspace(0, chunk, pieces + 1).astype(int)
+    outs, sels = [], []
+    p = c.pipe
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        rows, _ = c.chunk_rows(0, prefix + a, b - a)
+        c.summarize([prefix + a], [prefix + b], b - a)
+        p.reserve(b - a, rows.max_pos, ra.RA_OP_PREFILL)
+        ra.route_scores(c.cfg, rows, p.span_mean, p.scores)
+        ra.topk_spans(c.cfg, rows, p.scores, p.sel)
+        ra.routed_attn_prefill_fp8(c.cfg, rows, c.K8, c.V8, c.KS, c.VS, p.sel, p.out, p.workspace)
+        torch.cuda.synchronize()
+        outs.append(p.out.clone())
+        sels.append(p.sel.clone())
+    return torch.cat(outs), torch.cat(sels)
+
+
+def outlier_rows(c):
+    """Keys planted along single queries' vectors past the first chunk of a window span: each of
+    these queries sees a score ~160 (log2 units) above the maximum of its first keys, so its entry
+    takes the 8-bit tile's second pass."""
+    w = c.w
+    G = w.num_q_heads // w.num_kv_heads
+    prefix = int(c.lengths[0]) - 256
+    qs = WL.queries(w, 0, prefix, 256)
+    for i, (r, h) in enumerate([(10, 0), (60, 3), (100, 5), (150, 2), (200, 7), (250, 1)]):
+        qf = (qs[r, h].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        alpha = 160.0 * np.sqrt(w.head_dim) / (np.log2(np.e) * np.linalg.norm(qf))
+        t = torch.tensor(alpha * qf / np.linalg.norm(qf), dtype=torch.float32).to(torch.bfloat16)
+        p = prefix - 256 + 70 + 23 * i  # window span of every chunk row, past its first 64 keys
+        c.host[0][0][h // G, p] = t.view(torch.int16).numpy().view(np.uint16)
+        c.K[0, h // G, p] = t.cuda()
+
+
+PREFILL_FP8_CASES = [
+    # name, workload, prefix, chunk, edit
+    ("d128_G8", small("prefill_8k_on_1m", span_size=32, window=32, top_k=4), 2048, 300, None),
+    ("d64_G8_S48_W100", small("prefill_8k_on_1m", num_q_heads=8, num_kv_heads=1, head_dim=64, span_size=48,
+                              window=100, top_k=5), 1500, 333, None),
+    ("d128_special_rows", small("prefill_8k_on_1m", num_q_heads=8, num_kv_heads=2, span_size=16, window=16,
+                                top_k=6), 700, 200, special_rows),
+    ("d128_outliers_second_pass", small("prefill_8k_on_1m", num_q_heads=8, num_kv_heads=2, span_size=256,
+                                        window=256, top_k=4), 3072, 256, outlier_rows),
+]
+
+
+@pytest.mark.parametrize("name,w,prefix,chunk,edit", PREFILL_FP8_CASES, ids=[c[0] for c in PREFILL_FP8_CASES])
+def test_prefill_over_the_8bit_cache(name, w, prefix, chunk, edit):
+    c = Fp8Case(w, [prefix + chunk], edit=edit)
+    out, sel = prefill_fp8(c, prefix, chunk)
+    c.check_summaries(0)
+    q = WL.queries(w, 0, prefix, chunk)
+    c.pipe.reserve(chunk, prefix + chunk - 1, ra.RA_OP_PREFILL)
+    c.pipe.out.copy_(out)
+    c.pipe.sel.copy_(sel)
+    # (rows of values near 3e30: max-abs relative to the row's magnitude)
+    stats = c.check([0] * chunk, np.arange(prefix, prefix + chunk), q, np.arange(chunk), scores=False,
+                    scale_abs=edit is special_rows)
+    log("  %s: max_abs %.3g max_rel %.3g" % (name, stats["max_abs"], stats["max_rel"]))
+    assert_stats(stats, True)
+
+
+def test_prefill_over_the_8bit_cache_chunking_and_decode_agree():
+    """Cut into 1 or 3 calls the 8-bit prefill gives the same bits, and its last row equals the
+    8-bit decode kernel's result for that row within the rounding of P to bf16."""
+    w = small("prefill_8k_on_1m", span_size=64, window=64, top_k=8)
+    prefix, chunk = 4000, 200
+    c = Fp8Case(w, [prefix + chunk])
+    out1, sel1 = prefill_fp8(c, prefix, chunk, pieces=1)
+    c3 = Fp8Case(w, [prefix + chunk])
+    out3, sel3 = prefill_fp8(c3, prefix, chunk, pieces=3)
+    assert torch.equal(sel1, sel3) and torch.equal(out1, out3)
+    rows, _ = c.rows_for([0], [prefix + chunk - 1])
+    outd = torch.empty(1, w.num_q_heads, w.head_dim, device="cuda")
+    ws = torch.empty(ra.workspace_bytes(c.cfg, ra.RA_OP_DECODE, 1, prefix + chunk - 1), dtype=torch.uint8,
+                     device="cuda")
+    ra.routed_attn_decode_fp8(c.cfg, rows, c.K8, c.V8, c.KS, c.VS, sel1[-1:].contiguous(), outd, ws)
+    torch.cuda.synchronize()
+    diff = (outd[0] - out1[-1]).abs().max().item()
+    assert diff <= max(outd.abs().max().item(), 0.1) * 2.0 ** -8, diff
+
+
+@pytest.mark.timeout(900)
+def test_prefill_8k_on_1m_over_the_8bit_cache_sampled():
+    """The 8192-token chunk on the 1M-token cache, quantised on the device: every row computed;
+    a seeded sample of 32 positions x 32 heads (chunk edges and span boundaries included) against
+    the oracle on the dequantised cache."""
+    w = W["prefill_8k_on_1m"]
+    P, n = w.prefix_len, w.chunk_len
+    c = Fp8Case(w, [P + n])
+    out, sel = prefill_fp8(c, P, n)
+    rng = np.random.default_rng(w.seed + 1)
+    must = [0, n - 1, 1022, 1023, 1024, 2047, 2048, 4095, 4096, n - 1025]
+    rest = sorted(set(rng.choice(n, 64, replace=False).tolist()) - set(must))[:32 - len(must)]
+    idx = np.array(sorted(set(must) | set(rest)))
+    q = WL.queries(w, 0, P, n)
+    stats = c.check([0] * len(idx), P + idx, q[idx], idx, scores=False)
+    log("  prefill_8k_on_1m fp8: rows %d max_abs %.3g max_rel %.3g" % (stats["rows"], stats["max_abs"],
+                                                                      stats["max_rel"]))
+    assert_stats(stats, True)
