@@ -114,6 +114,68 @@ def test_rows_past_the_length_are_not_saved():
     assert N.build_image(k2, v2, m2, run, lengths, S) == img
 
 
+def fp8_caches(B=3, Hkv=2, cap=300, d=64, S=16, lengths=(300, 17, 0), seed=3):
+    rng = np.random.default_rng(seed)
+    k = rng.integers(0, 256, size=(B, Hkv, cap, d), dtype=np.uint8)
+    v = rng.integers(0, 256, size=(B, Hkv, cap, d), dtype=np.uint8)
+    ks = rng.random((B, Hkv, cap)).astype(np.float32) + 0.5
+    vs = rng.random((B, Hkv, cap)).astype(np.float32) + 0.5
+    mean = rng.standard_normal((B, Hkv, cap // S, d)).astype(np.float32)
+    run = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+    return k, v, ks, vs, mean, run, np.array(lengths, dtype=np.int64), S
+
+
+def test_image_layout_of_the_8bit_cache():
+    """Element type 2 (N3): per (b, g) K codes, V codes, then the K and V scale runs of L_b
+    floats, each zero-padded to 16 bytes (17 rows: 68 bytes + 12 zeros).  Offsets by hand."""
+    k, v, ks, vs, mean, run, lengths, S = fp8_caches()
+    img = N.build_image(k, v, mean, run, lengths, S, ks, vs)
+    H = 96
+    assert struct.unpack("<I", img[12:16])[0] == 2
+    # codes 2 x 2 x 317 rows x 64 bytes; scale runs 2 x (2 x 1200 + 2 x 80); summaries 2 x 22 x 256
+    P = 81152 + 5120 + 11264
+    assert struct.unpack("<QQ", img[32:48]) == (P, H)
+    at = H
+    for b, L, run_bytes in ((0, 300, 1200), (1, 17, 80)):
+        for g in range(2):
+            assert img[at:at + 64 * L] == k[b, g, :L].tobytes()
+            at += 64 * L
+            assert img[at:at + 64 * L] == v[b, g, :L].tobytes()
+            at += 64 * L
+            for sc in (ks, vs):
+                assert img[at:at + 4 * L] == sc[b, g, :L].tobytes()
+                assert img[at + 4 * L:at + run_bytes] == b"\0" * (run_bytes - 4 * L)
+                at += run_bytes
+    for b, n in ((0, 18), (1, 1), (2, 0)):
+        for g in range(2):
+            assert img[at:at + n * 256] == mean[b, g, :n].tobytes()
+            at += n * 256 + 256
+    assert at == H + P
+    # (H + P) = 97632 bytes: 24 chunks, then 2 digests of groups of 16, then the root
+    assert len(img) == H + P + 32 * (24 + 2) + 32 == N.image_bytes(lengths, 2, 64, 16, 1)
+    assert N.verify(img) is None
+
+
+def test_8bit_image_parse_and_rows_past_the_length():
+    k, v, ks, vs, mean, run, lengths, S = fp8_caches(lengths=(250, 33, 1))
+    img = N.build_image(k, v, mean, run, lengths, S, ks, vs)
+    h, L, seqs = N.parse_image(img)
+    assert h["dtype"] == 2 and list(L) == [250, 33, 1]
+    for b in range(3):
+        for g in range(2):
+            assert np.array_equal(seqs[b]["k"][g], k[b, g, :L[b]])
+            assert np.array_equal(seqs[b]["v"][g], v[b, g, :L[b]])
+            assert np.array_equal(seqs[b]["k_scale"][g], ks[b, g, :L[b]])
+            assert np.array_equal(seqs[b]["v_scale"][g], vs[b, g, :L[b]])
+    ks2, vs2, k2 = ks.copy(), vs.copy(), k.copy()
+    ks2[1, :, 33:] = 9.0
+    vs2[2, :, 1:] = -2.0
+    k2[0, :, 250:] = 1
+    assert N.build_image(k2, v, mean, run, lengths, S, ks2, vs2) == img
+    ks2[1, 1, 32] = 9.0  # a saved scale changes the image
+    assert N.build_image(k, v, mean, run, lengths, S, ks2, vs) != img
+
+
 def two_level_image():
     # K and V: 2 x 2 x 300 rows of 256 bytes each (bf16, d = 128) = 614400 bytes; summaries
     # 2 kv heads x (4 + 4 means + 2 running sums) x 512 bytes = 10240; header 80 -> 624720 bytes
