@@ -50,7 +50,7 @@ def parse():
                    help="timed calls of dense causal attention on the prefill rows (0: skip)")
     p.add_argument("--no-ladder", action="store_true",
                    help="skip the routed-vs-dense ladder (the same chunk after 128K, 256K and 512K tokens)")
-    p.add_argument("--no-fp8", action="store_true", help="skip the decode step over the 8-bit cache")
+    p.add_argument("--no-fp8", action="store_true", help="skip the decode and prefill steps over the 8-bit cache")
     p.add_argument("--no-snapshot", action="store_true", help="skip the session snapshot / restore measurement")
     p.add_argument("--no-cold", action="store_true", help="skip the token-level cold retrieval decode step")
     p.add_argument("--no-tiny", action="store_true", help="skip the tiny fp32 prefill (4096 tokens, d = 64)")
@@ -268,7 +268,7 @@ def main():
         del K, V, st
         torch.cuda.empty_cache()
         result["prefill"] = bench_prefill(args.prefill_steps, args.dense_steps, not args.no_ladder,
-                                          0.0 if args.no_cpu_baseline else args.cpu_seconds)
+                                          0.0 if args.no_cpu_baseline else args.cpu_seconds, not args.no_fp8)
 
     if not args.no_extra:
         if args.no_prefill:
@@ -318,10 +318,11 @@ def counter_traffic(tag):
     return rec.get("bytes_per_launch") if rec.get("source_sha256") == h.hexdigest() else None
 
 
-def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0):
+def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0, fp8=True):
     """Chunked prefill: 8192 new tokens appended to a 1M-token cache (the chunk's K/V are in
     the cache before timing).  A step = span_summary_update of the chunk + route_scores +
-    topk_spans + routed_attn_prefill for its 8192 x 32 row-heads."""
+    topk_spans + routed_attn_prefill for its 8192 x 32 row-heads.  With fp8, the same step over
+    the cache quantised to E4M3 codes (kv_quantize_fp8, untimed setup)."""
     import torch
 
     import content_routed_sparse_amd as ra
@@ -381,6 +382,8 @@ def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0):
     route_flops = 2.0 * d * r.astype(np.float64).sum() * w.num_q_heads
     tflops = attn_flops / (attn_ms * 1e-3) / 1e12
 
+    fp8_leg = bench_prefill_fp8(w, cfg, K, V, rows, t_p, t_l, steps, attn_flops, route_flops, out) if fp8 else None
+
     # the same rows with dense causal attention over the whole prefix (the brute-force scan that
     # routing replaces; its flops are 4 d per (row-head, key <= t))
     dense = None
@@ -427,9 +430,70 @@ def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0):
                           "achieved": round(step_tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
                           "frac": round(step_tflops / 2500.0, 4)},
         "cpu_baseline": cpu, "oracle_check": check,
+        "fp8_cache": fp8_leg,
         "dense_causal": dense,
         "ladder": rungs,
     }
+
+
+def bench_prefill_fp8(w, cfg, K, V, rows, t_p, t_l, steps, attn_flops, route_flops, out_bf16):
+    """The prefill step over the 8-bit cache: span_summary_update_fp8 of the chunk + route_scores
+    + topk_spans + routed_attn_prefill_fp8.  The tiles convert the codes to bf16 in LDS and run the
+    same bf16 MFMA products, so the flops and the peak are those of the bf16 step."""
+    import torch
+
+    import content_routed_sparse_amd as ra
+
+    dev = K.device
+    P, n, L = w.prefix_len, w.chunk_len, w.prefix_len + w.chunk_len
+    K8 = torch.empty(K.shape, dtype=torch.uint8, device=dev)
+    V8 = torch.empty_like(K8)
+    KS = torch.empty(K.shape[:3], dtype=torch.float32, device=dev)
+    VS = torch.empty_like(KS)
+    zero = torch.zeros(1, dtype=torch.int64, device=dev)
+    ra.kv_quantize_fp8(cfg, K, K8, KS, zero, t_l, L)
+    ra.kv_quantize_fp8(cfg, V, V8, VS, zero, t_l, L)
+    mean = torch.zeros(1, w.num_kv_heads, cfg.max_spans, w.head_dim, dtype=torch.float32, device=dev)
+    run = torch.zeros(1, w.num_kv_heads, w.head_dim, dtype=torch.float32, device=dev)
+    ra.span_summary_update_fp8(cfg, K8, KS, mean, run, zero, t_p, P)  # setup
+    scores = torch.empty(n, w.num_q_heads, ra.score_stride(cfg, L - 1), dtype=torch.float32, device=dev)
+    sel = torch.empty(n, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev)
+    out = torch.empty(n, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    ws = torch.empty(ra.workspace_bytes(cfg, ra.RA_OP_PREFILL, n, L - 1), dtype=torch.uint8, device=dev)
+    calls = [ra.prepare("span_summary_update_fp8", cfg, K8, KS, mean, run, t_p, t_l, n),
+             ra.prepare("route_scores", cfg, rows, mean, scores),
+             ra.prepare("topk_spans", cfg, rows, scores, sel)]
+    attn = ra.prepare("routed_attn_prefill_fp8", cfg, rows, K8, V8, KS, VS, sel, out, ws)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for c in calls:
+        c()
+    attn()
+    torch.cuda.synchronize()
+    first = out.clone()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for c in calls:
+            c()
+        ev[i][0].record(stream)
+        attn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    step_tflops = (attn_flops + route_flops) / (step_ms * 1e-3) / 1e12
+    # quantisation's effect on the result: largest |out_fp8 - out_bf16| over the chunk
+    diff = float((out - out_bf16).abs().max().item())
+    return {"workload": "prefill_8k_on_1m, 8-bit cache (E4M3 codes, one fp32 scale per kv-head row)",
+            "value": round(n / (step_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(step_ms, 4),
+            "roofline": {"bound": "mfma", "kernel": "routed_attn_prefill_fp8 (dispatch + 8-bit MFMA tiles + merge)",
+                         "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                         "frac": round(tflops / 2500.0, 4), "traffic": None,
+                         "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
+            "step_tflops": round(step_tflops, 1),
+            "max_abs_vs_bf16_cache": round(diff, 5),
+            "repeat_bitwise_identical": bool(torch.equal(first, out))}
 
 
 def time_calls(calls, reps):

@@ -29,9 +29,11 @@ EXPORTED = ("span_summary_update", "route_scores", "topk_spans", "route_topk_spa
             "routed_attn_decode_append", "routed_attn_decode_fp8_append",
             "kv_signature_update", "ra_cold_workspace_bytes", "cold_select", "cold_attn_decode",
             "kv_snapshot_bytes", "kv_snapshot_pack", "kv_snapshot_parse", "kv_snapshot_verify", "kv_snapshot_unpack",
+            "kv_snapshot_bytes_fp8", "kv_snapshot_pack_fp8", "kv_snapshot_unpack_fp8",
             "kv_snapshot_write_file", "kv_snapshot_read_file", "ra_workspace_bytes", "ra_status_string",
             "ra_last_error")
 SNAPSHOT_INTACT = (1 << 64) - 1  # kv_snapshot_verify's word when every digest matches
+RA_SNAPSHOT_E4M3 = 2  # image element type of the 8-bit cache
 
 
 class RoutedAttnError(RuntimeError):
@@ -94,6 +96,8 @@ def lib():
             "kv_snapshot_parse": [P, SZ, ctypes.POINTER(_SnapshotInfo), P, I32],
             "kv_snapshot_verify": [P, SZ, P, SZ, P, P],
             "kv_snapshot_unpack": [CP, P, SZ, P, SZ, P, P, P, P, P, P],
+            "kv_snapshot_pack_fp8": [CP, P, P, P, P, P, P, P, P, SZ, P],
+            "kv_snapshot_unpack_fp8": [CP, P, SZ, P, SZ, P, P, P, P, P, P, P, P],
             "kv_snapshot_write_file": [ctypes.c_char_p, P, SZ],
             "kv_snapshot_read_file": [ctypes.c_char_p, P, SZ, ctypes.POINTER(SZ)],
         }
@@ -103,8 +107,9 @@ def lib():
             fn.restype = I32
         L.ra_cold_workspace_bytes.argtypes = [CP, I64, I64, I32, I32]
         L.ra_cold_workspace_bytes.restype = SZ
-        L.kv_snapshot_bytes.argtypes = [CP, P]
-        L.kv_snapshot_bytes.restype = SZ
+        for name in ("kv_snapshot_bytes", "kv_snapshot_bytes_fp8"):
+            getattr(L, name).argtypes = [CP, P]
+            getattr(L, name).restype = SZ
         L.ra_workspace_bytes.argtypes = [CP, I32, I64, I64]
         L.ra_workspace_bytes.restype = SZ
         L.ra_status_string.argtypes = [I32]
@@ -595,6 +600,45 @@ def kv_snapshot_pack(cfg, k_cache, v_cache, span_mean, run_sum, lengths, image, 
         _dev(image, torch.uint8, None, "image"), image.numel(), _stream(stream)))
 
 
+def _fp8_cache_args(cfg, k_codes, v_codes, k_scales, v_scales):
+    shape = _kv_shape(cfg)
+    return (_dev(k_codes, torch.uint8, shape, "k_codes"), _dev(v_codes, torch.uint8, shape, "v_codes"),
+            _dev(k_scales, torch.float32, shape[:3], "k_scales"), _dev(v_scales, torch.float32, shape[:3], "v_scales"))
+
+
+def snapshot_bytes_fp8(cfg, lengths):
+    """Image bytes of the state of sequences with these host lengths over the 8-bit cache."""
+    arr = _host_lengths(cfg, lengths)
+    c = cfg.c()
+    n = lib().kv_snapshot_bytes_fp8(ctypes.byref(c), arr.ctypes.data)
+    if n == 0:
+        raise RoutedAttnError(1, lib().ra_last_error().decode())
+    return n
+
+
+def kv_snapshot_pack_fp8(cfg, k_codes, v_codes, k_scales, v_scales, span_mean, run_sum, lengths, image, stream=None):
+    """Write the snapshot image of the 8-bit cache state (codes, row scales, summaries)."""
+    arr = _host_lengths(cfg, lengths)
+    c = cfg.c()
+    _check(lib().kv_snapshot_pack_fp8(
+        ctypes.byref(c), *_fp8_cache_args(cfg, k_codes, v_codes, k_scales, v_scales),
+        _dev(span_mean, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.max_spans, cfg.head_dim), "span_mean"),
+        _dev(run_sum, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.head_dim), "run_sum"), arr.ctypes.data,
+        _dev(image, torch.uint8, None, "image"), image.numel(), _stream(stream)))
+
+
+def kv_snapshot_unpack_fp8(cfg, header, image, k_codes, v_codes, k_scales, v_scales, span_mean, run_sum, guard=None,
+                           stream=None):
+    """Copy the saved 8-bit state of the device image into the caches (only if *guard reads intact)."""
+    ptr, n, _keep = _host_bytes(header)
+    g = None if guard is None else _dev(guard, torch.int64, (1,), "guard")
+    _check(lib().kv_snapshot_unpack_fp8(
+        ctypes.byref(cfg.c()), ctypes.c_void_p(ptr), n, _dev(image, torch.uint8, None, "image"), image.numel(), g,
+        *_fp8_cache_args(cfg, k_codes, v_codes, k_scales, v_scales),
+        _dev(span_mean, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.max_spans, cfg.head_dim), "span_mean"),
+        _dev(run_sum, torch.float32, (cfg.batch, cfg.num_kv_heads, cfg.head_dim), "run_sum"), _stream(stream)))
+
+
 def kv_snapshot_parse(header, max_batch=1 << 20):
     """(info dict, lengths numpy array) of a host header."""
     import numpy as np
@@ -662,6 +706,32 @@ def load_snapshot(path, cfg, k_cache, v_cache, span_mean, run_sum):
     header = host[:info["header_bytes"]]
     kv_snapshot_verify(header, image, bad)
     kv_snapshot_unpack(cfg, header, image, k_cache, v_cache, span_mean, run_sum, guard=bad)
+    b = int(bad.item()) & SNAPSHOT_INTACT
+    if b != SNAPSHOT_INTACT:
+        raise RoutedAttnError(6, "%s: digest mismatch in the chunk at byte %d; nothing restored" % (path, b))
+    return lengths
+
+
+def save_snapshot_fp8(path, cfg, k_codes, v_codes, k_scales, v_scales, span_mean, run_sum, lengths):
+    """save_snapshot for the 8-bit cache (codes and row scales).  Returns the root digest (hex)."""
+    image = torch.empty(snapshot_bytes_fp8(cfg, lengths), dtype=torch.uint8, device=k_codes.device)
+    kv_snapshot_pack_fp8(cfg, k_codes, v_codes, k_scales, v_scales, span_mean, run_sum, lengths, image)
+    host = torch.empty(image.numel(), dtype=torch.uint8, pin_memory=True)
+    host.copy_(image)
+    kv_snapshot_write_file(path, host)
+    return bytes(host[-32:].numpy()).hex()
+
+
+def load_snapshot_fp8(path, cfg, k_codes, v_codes, k_scales, v_scales, span_mean, run_sum):
+    """load_snapshot for the 8-bit cache: every digest checked on the device, then the state
+    restored (nothing restored if any digest differs, which raises).  Returns the lengths."""
+    host = kv_snapshot_read_file(path)
+    info, lengths = kv_snapshot_parse(host[:min(host.numel(), 64 + 8 * (1 << 20))])
+    image = host.to(k_codes.device, non_blocking=True)
+    bad = torch.empty(1, dtype=torch.int64, device=k_codes.device)
+    header = host[:info["header_bytes"]]
+    kv_snapshot_verify(header, image, bad)
+    kv_snapshot_unpack_fp8(cfg, header, image, k_codes, v_codes, k_scales, v_scales, span_mean, run_sum, guard=bad)
     b = int(bad.item()) & SNAPSHOT_INTACT
     if b != SNAPSHOT_INTACT:
         raise RoutedAttnError(6, "%s: digest mismatch in the chunk at byte %d; nothing restored" % (path, b))

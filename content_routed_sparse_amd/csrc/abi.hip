@@ -480,6 +480,7 @@ namespace {
 constexpr uint64_t kSnapMagic = 0x31504E5341535243ull;  // "CRSASNP1" read as a little-endian word
 constexpr uint32_t kSnapVersion = 1, kSnapChunk = 4096, kSnapFanIn = 16;
 constexpr int kMaxLevels = 16;  // 4096 * 16^15 bytes exceed any image
+constexpr int kSnapE4M3 = RA_SNAPSHOT_E4M3;  // element type of the 8-bit cache's images
 
 struct SnapLayout {
     int B, Hkv, d, S, dtype, esz;
@@ -491,6 +492,9 @@ struct SnapLayout {
 
 uint64_t snap_header_bytes(int B) { return (64 + 8 * (uint64_t)B + 15) / 16 * 16; }
 
+// Image bytes of one run of L fp32 row scales (8-bit cache): 4 L, zero-padded to 16.
+uint64_t snap_scale_run(int64_t L) { return (4 * (uint64_t)L + 15) / 16 * 16; }
+
 // Layout of the image of B sequences with the given lengths (checked by the callers).
 SnapLayout snap_layout(int B, int Hkv, int d, int S, int dtype, const int64_t *lengths) {
     SnapLayout L;
@@ -499,14 +503,16 @@ SnapLayout snap_layout(int B, int Hkv, int d, int S, int dtype, const int64_t *l
     L.d = d;
     L.S = S;
     L.dtype = dtype;
-    L.esz = dtype == RA_BF16 ? 2 : 4;
-    uint64_t rows = 0, spans = 0;
+    L.esz = dtype == kSnapE4M3 ? 1 : (dtype == RA_BF16 ? 2 : 4);
+    uint64_t rows = 0, spans = 0, runs = 0;
     for (int b = 0; b < B; ++b) {
         rows += (uint64_t)lengths[b];
         spans += (uint64_t)lengths[b] / (uint64_t)S;
+        runs += snap_scale_run(lengths[b]);
     }
     L.H = snap_header_bytes(B);
-    L.P = 2ull * Hkv * rows * d * L.esz + (uint64_t)Hkv * (spans + B) * d * 4;
+    L.P = 2ull * Hkv * rows * d * L.esz + (dtype == kSnapE4M3 ? 2ull * Hkv * runs : 0ull) +
+          (uint64_t)Hkv * (spans + B) * d * 4;
     L.data = L.H + L.P;
     uint64_t n = (L.data + kSnapChunk - 1) / kSnapChunk, at = L.data;
     L.n_levels = 0;
@@ -533,10 +539,10 @@ ra_status check_lengths(const ra_config *c, const int64_t *lengths, int B) {
 }
 
 // The payload's byte ranges in order, each paired with its place in the caches; `to_image`
-// selects the copy direction.
+// selects the copy direction.  ks / vs: the 8-bit cache's row scales (element type 2 only).
 ra_status snap_copy(const SnapLayout &L, const ra_config *c, const int64_t *lengths, uint8_t *image,
-                    const void *k, const void *v, const float *mean, const float *run, bool to_image,
-                    const unsigned long long *guard, hipStream_t st) {
+                    const void *k, const void *v, const float *ks, const float *vs, const float *mean,
+                    const float *run, bool to_image, const unsigned long long *guard, hipStream_t st) {
     ra::SegmentBatch sb;
     sb.n = 0;
     uint64_t at = L.H;
@@ -545,29 +551,52 @@ ra_status snap_copy(const SnapLayout &L, const ra_config *c, const int64_t *leng
         sb.n = 0;
         return e;
     };
-    auto add = [&](const void *cache_ptr, uint64_t bytes) -> hipError_t {
-        if (bytes == 0) return hipSuccess;
-        ra::Segment &s = sb.seg[sb.n++];
-        s.src = to_image ? cache_ptr : (const void *)(image + at);
-        s.dst = to_image ? (void *)(image + at) : const_cast<void *>(cache_ptr);
-        s.n16 = bytes / 16;
-        at += bytes;
-        return sb.n == ra::kSegs ? flush() : hipSuccess;
+    // `bytes` of the image at `at` <-> the cache at cache_ptr, in 16-byte units or (scales) 4-byte
+    // words; `pad` zero bytes follow in the image (written when packing, skipped when restoring)
+    auto add = [&](const void *cache_ptr, uint64_t bytes, bool words, uint64_t pad) -> hipError_t {
+        hipError_t e = hipSuccess;
+        if (bytes > 0) {
+            ra::Segment &s = sb.seg[sb.n++];
+            s.src = to_image ? cache_ptr : (const void *)(image + at);
+            s.dst = to_image ? (void *)(image + at) : const_cast<void *>(cache_ptr);
+            s.n = words ? bytes / 4 : bytes / 16;
+            s.mode = words ? ra::kSegCopy4 : ra::kSegCopy16;
+            at += bytes;
+            if (sb.n == ra::kSegs) e = flush();
+        }
+        if (e == hipSuccess && pad > 0) {
+            if (to_image) {
+                ra::Segment &s = sb.seg[sb.n++];
+                s.src = nullptr;
+                s.dst = image + at;
+                s.n = pad / 4;
+                s.mode = ra::kSegZero4;
+                if (sb.n == ra::kSegs) e = flush();
+            }
+            at += pad;
+        }
+        return e;
     };
     const uint64_t row = (uint64_t)L.d * L.esz;
     hipError_t e = hipSuccess;
     for (int b = 0; b < L.B && e == hipSuccess; ++b)
         for (int g = 0; g < L.Hkv && e == hipSuccess; ++g) {
-            const uint64_t base = ((uint64_t)b * c->num_kv_heads + g) * (uint64_t)c->capacity * row;
+            const uint64_t bg = (uint64_t)b * c->num_kv_heads + g;
+            const uint64_t base = bg * (uint64_t)c->capacity * row;
             const uint64_t n = (uint64_t)lengths[b] * row;
-            e = add((const uint8_t *)k + base, n);
-            if (e == hipSuccess) e = add((const uint8_t *)v + base, n);
+            e = add((const uint8_t *)k + base, n, false, 0);
+            if (e == hipSuccess) e = add((const uint8_t *)v + base, n, false, 0);
+            if (L.dtype == kSnapE4M3) {
+                const uint64_t sc = 4 * (uint64_t)lengths[b], pad = snap_scale_run(lengths[b]) - sc;
+                if (e == hipSuccess) e = add(ks + bg * (uint64_t)c->capacity, sc, true, pad);
+                if (e == hipSuccess) e = add(vs + bg * (uint64_t)c->capacity, sc, true, pad);
+            }
         }
     for (int b = 0; b < L.B && e == hipSuccess; ++b)
         for (int g = 0; g < L.Hkv && e == hipSuccess; ++g) {
             const uint64_t bg = (uint64_t)b * c->num_kv_heads + g;
-            e = add(mean + bg * (uint64_t)c->max_spans * L.d, (uint64_t)lengths[b] / L.S * L.d * 4);
-            if (e == hipSuccess) e = add(run + bg * L.d, (uint64_t)L.d * 4);
+            e = add(mean + bg * (uint64_t)c->max_spans * L.d, (uint64_t)lengths[b] / L.S * L.d * 4, false, 0);
+            if (e == hipSuccess) e = add(run + bg * L.d, (uint64_t)L.d * 4, false, 0);
         }
     if (e == hipSuccess) e = flush();
     if (e != hipSuccess) return hip_status(e, "snapshot copy launch");
@@ -611,7 +640,8 @@ ra_status snap_parse(const void *header, size_t avail, SnapLayout *L, std::vecto
     if (magic != kSnapMagic) return fail(RA_EFORMAT, "not a snapshot image (magic)");
     if (version != kSnapVersion || chunk != kSnapChunk || fan != kSnapFanIn || z != 0)
         return fail(RA_EFORMAT, "unsupported snapshot version or digest parameters");
-    if (dtype != RA_F32 && dtype != RA_BF16) return fail(RA_EFORMAT, "unknown element type %u", dtype);
+    if (dtype != RA_F32 && dtype != RA_BF16 && dtype != (uint32_t)kSnapE4M3)
+        return fail(RA_EFORMAT, "unknown element type %u", dtype);
     if (B < 1 || B > (1u << 24) || Hkv < 1 || Hkv > 4096 || (d != 64 && d != 128) || S < 1 || S > (1u << 30))
         return fail(RA_EFORMAT, "header shape fields out of range");
     if (H != snap_header_bytes((int)B)) return fail(RA_EFORMAT, "header size field inconsistent with B");
@@ -628,26 +658,17 @@ ra_status snap_parse(const void *header, size_t avail, SnapLayout *L, std::vecto
     return RA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t kv_snapshot_bytes(const ra_config *cfg, const int64_t *lengths) {
-    if (check_config(cfg) || check_lengths(cfg, lengths, cfg->batch)) return 0;
-    return (size_t)snap_layout(cfg->batch, cfg->num_kv_heads, cfg->head_dim, cfg->span_size, cfg->dtype, lengths).image;
-}
-
-ra_status kv_snapshot_pack(const ra_config *cfg, const void *k_cache, const void *v_cache, const float *span_mean,
-                           const float *run_sum, const int64_t *lengths, void *image, size_t image_bytes,
-                           void *stream) {
-    ra_status s = check_config(cfg);
+// Header words, payload copies and digest levels of an image of element type `elem` (cfg->dtype,
+// or kSnapE4M3 with the scale arrays); cfg is checked by the caller.
+ra_status snap_pack(const ra_config *cfg, int elem, const void *k_cache, const void *v_cache, const float *ks,
+                    const float *vs, const float *span_mean, const float *run_sum, const int64_t *lengths,
+                    void *image, size_t image_bytes, void *stream) {
+    ra_status s = check_lengths(cfg, lengths, cfg->batch);
     if (s) return s;
-    if ((s = check_lengths(cfg, lengths, cfg->batch))) return s;
     if (!k_cache || !v_cache || !span_mean || !run_sum || !image) return fail(RA_EINVAL, "NULL pointer argument");
     if (((uintptr_t)image | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)span_mean | (uintptr_t)run_sum) & 15)
         return fail(RA_EINVAL, "image and cache buffers must be 16-byte aligned");
-    const SnapLayout L =
-        snap_layout(cfg->batch, cfg->num_kv_heads, cfg->head_dim, cfg->span_size, cfg->dtype, lengths);
+    const SnapLayout L = snap_layout(cfg->batch, cfg->num_kv_heads, cfg->head_dim, cfg->span_size, elem, lengths);
     if (image_bytes < L.image)
         return fail(RA_ECAPACITY, "image buffer of %zu bytes, %llu needed", image_bytes, (unsigned long long)L.image);
     hipStream_t st = (hipStream_t)stream;
@@ -662,7 +683,7 @@ ra_status kv_snapshot_pack(const ra_config *cfg, const void *k_cache, const void
             uint64_t v = 0;
             switch (w) {
                 case 0: v = kSnapMagic; break;
-                case 1: v = kSnapVersion | ((uint64_t)(uint32_t)cfg->dtype << 32); break;
+                case 1: v = kSnapVersion | ((uint64_t)(uint32_t)elem << 32); break;
                 case 2: v = (uint64_t)(uint32_t)cfg->batch | ((uint64_t)(uint32_t)cfg->num_kv_heads << 32); break;
                 case 3: v = (uint64_t)(uint32_t)cfg->head_dim | ((uint64_t)(uint32_t)cfg->span_size << 32); break;
                 case 4: v = L.P; break;
@@ -676,8 +697,66 @@ ra_status kv_snapshot_pack(const ra_config *cfg, const void *k_cache, const void
         const hipError_t e = ra::launch_write_words((uint64_t *)(img + 8 * w0), wb, st);
         if (e != hipSuccess) return hip_status(e, "snapshot header launch");
     }
-    if ((s = snap_copy(L, cfg, lengths, img, k_cache, v_cache, span_mean, run_sum, true, nullptr, st))) return s;
+    if ((s = snap_copy(L, cfg, lengths, img, k_cache, v_cache, ks, vs, span_mean, run_sum, true, nullptr, st)))
+        return s;
     return hip_status(snap_hash(L, img, false, nullptr, st), "snapshot digest launch");
+}
+
+// Restore of an image of element type `elem` (cfg is checked by the caller).
+ra_status snap_unpack(const ra_config *cfg, int elem, const void *header, size_t header_avail, const void *image,
+                      size_t image_bytes, const uint64_t *guard, void *k_cache, void *v_cache, float *ks, float *vs,
+                      float *span_mean, float *run_sum, void *stream) {
+    SnapLayout L;
+    std::vector<int64_t> len;
+    ra_status s = snap_parse(header, header_avail, &L, len);
+    if (s) return s;
+    if (L.dtype != elem || L.Hkv != cfg->num_kv_heads || L.d != cfg->head_dim || L.S != cfg->span_size)
+        return fail(RA_EINVAL, "image (element type %d, Hkv %d, d %d, S %d) does not match (%d, %d, %d, %d)", L.dtype,
+                    L.Hkv, L.d, L.S, elem, cfg->num_kv_heads, cfg->head_dim, cfg->span_size);
+    if (L.B > cfg->batch) return fail(RA_ECAPACITY, "image holds %d sequences, cfg->batch is %d", L.B, cfg->batch);
+    if ((s = check_lengths(cfg, len.data(), L.B))) return s;
+    if (!image || !k_cache || !v_cache || !span_mean || !run_sum) return fail(RA_EINVAL, "NULL pointer argument");
+    if (((uintptr_t)image | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)span_mean | (uintptr_t)run_sum) & 15)
+        return fail(RA_EINVAL, "image and cache buffers must be 16-byte aligned");
+    if (image_bytes < L.image)
+        return fail(RA_EFORMAT, "image of %zu bytes, header describes %llu", image_bytes, (unsigned long long)L.image);
+    return snap_copy(L, cfg, len.data(), (uint8_t *)const_cast<void *>(image), k_cache, v_cache, ks, vs, span_mean,
+                     run_sum, false, (const unsigned long long *)guard, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kv_snapshot_bytes(const ra_config *cfg, const int64_t *lengths) {
+    if (check_config(cfg) || check_lengths(cfg, lengths, cfg->batch)) return 0;
+    return (size_t)snap_layout(cfg->batch, cfg->num_kv_heads, cfg->head_dim, cfg->span_size, cfg->dtype, lengths).image;
+}
+
+size_t kv_snapshot_bytes_fp8(const ra_config *cfg, const int64_t *lengths) {
+    if (check_config(cfg) || check_lengths(cfg, lengths, cfg->batch)) return 0;
+    return (size_t)snap_layout(cfg->batch, cfg->num_kv_heads, cfg->head_dim, cfg->span_size, kSnapE4M3, lengths).image;
+}
+
+ra_status kv_snapshot_pack(const ra_config *cfg, const void *k_cache, const void *v_cache, const float *span_mean,
+                           const float *run_sum, const int64_t *lengths, void *image, size_t image_bytes,
+                           void *stream) {
+    ra_status s = check_config(cfg);
+    if (s) return s;
+    return snap_pack(cfg, cfg->dtype, k_cache, v_cache, nullptr, nullptr, span_mean, run_sum, lengths, image,
+                     image_bytes, stream);
+}
+
+ra_status kv_snapshot_pack_fp8(const ra_config *cfg, const uint8_t *k_codes, const uint8_t *v_codes,
+                               const float *k_scales, const float *v_scales, const float *span_mean,
+                               const float *run_sum, const int64_t *lengths, void *image, size_t image_bytes,
+                               void *stream) {
+    ra_status s = check_config(cfg);
+    if (s) return s;
+    if (!k_scales || !v_scales) return fail(RA_EINVAL, "NULL scale array");
+    if (((uintptr_t)k_scales | (uintptr_t)v_scales) & 3) return fail(RA_EINVAL, "scale arrays must be 4-byte aligned");
+    return snap_pack(cfg, kSnapE4M3, k_codes, v_codes, k_scales, v_scales, span_mean, run_sum, lengths, image,
+                     image_bytes, stream);
 }
 
 ra_status kv_snapshot_parse(const void *header, size_t header_avail, ra_snapshot_info *info, int64_t *lengths,
@@ -726,21 +805,19 @@ ra_status kv_snapshot_unpack(const ra_config *cfg, const void *header, size_t he
                              float *span_mean, float *run_sum, void *stream) {
     ra_status s = check_config(cfg);
     if (s) return s;
-    SnapLayout L;
-    std::vector<int64_t> len;
-    if ((s = snap_parse(header, header_avail, &L, len))) return s;
-    if (L.dtype != cfg->dtype || L.Hkv != cfg->num_kv_heads || L.d != cfg->head_dim || L.S != cfg->span_size)
-        return fail(RA_EINVAL, "image (dtype %d, Hkv %d, d %d, S %d) does not match cfg (%d, %d, %d, %d)", L.dtype,
-                    L.Hkv, L.d, L.S, cfg->dtype, cfg->num_kv_heads, cfg->head_dim, cfg->span_size);
-    if (L.B > cfg->batch) return fail(RA_ECAPACITY, "image holds %d sequences, cfg->batch is %d", L.B, cfg->batch);
-    if ((s = check_lengths(cfg, len.data(), L.B))) return s;
-    if (!image || !k_cache || !v_cache || !span_mean || !run_sum) return fail(RA_EINVAL, "NULL pointer argument");
-    if (((uintptr_t)image | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)span_mean | (uintptr_t)run_sum) & 15)
-        return fail(RA_EINVAL, "image and cache buffers must be 16-byte aligned");
-    if (image_bytes < L.image)
-        return fail(RA_EFORMAT, "image of %zu bytes, header describes %llu", image_bytes, (unsigned long long)L.image);
-    return snap_copy(L, cfg, len.data(), (uint8_t *)const_cast<void *>(image), k_cache, v_cache, span_mean, run_sum, false,
-                     (const unsigned long long *)guard, (hipStream_t)stream);
+    return snap_unpack(cfg, cfg->dtype, header, header_avail, image, image_bytes, guard, k_cache, v_cache, nullptr,
+                       nullptr, span_mean, run_sum, stream);
+}
+
+ra_status kv_snapshot_unpack_fp8(const ra_config *cfg, const void *header, size_t header_avail, const void *image,
+                                 size_t image_bytes, const uint64_t *guard, uint8_t *k_codes, uint8_t *v_codes,
+                                 float *k_scales, float *v_scales, float *span_mean, float *run_sum, void *stream) {
+    ra_status s = check_config(cfg);
+    if (s) return s;
+    if (!k_scales || !v_scales) return fail(RA_EINVAL, "NULL scale array");
+    if (((uintptr_t)k_scales | (uintptr_t)v_scales) & 3) return fail(RA_EINVAL, "scale arrays must be 4-byte aligned");
+    return snap_unpack(cfg, kSnapE4M3, header, header_avail, image, image_bytes, guard, k_codes, v_codes, k_scales,
+                       v_scales, span_mean, run_sum, stream);
 }
 
 ra_status kv_snapshot_write_file(const char *path, const void *data, size_t bytes) {

@@ -6,8 +6,9 @@
 //  * write_words: the header's 64-bit words, passed by value;
 //  * copy_segments: up to kSegs contiguous byte ranges per launch (the live rows of K and V of
 //    each (sequence, kv head), the complete span means, the running sums), 16 bytes per lane,
-//    non-temporal; restore runs the same kernel the other way, behind a guard word so that a
-//    failed check leaves the caller's cache untouched;
+//    non-temporal; the 8-bit cache's row scales 4 bytes per lane (a scale run need not start on
+//    16 bytes in the cache), and the zero padding after each run; restore runs the same kernel
+//    the other way, behind a guard word so that a failed check leaves the caller's cache untouched;
 //  * sha_chunks: one lane per chunk (4096 bytes of data, or a group of 16 digests of the level
 //    below) computes its SHA-256 (the blocks in a row, the next block's four 16-byte loads issued
 //    before the current block's rounds) and either stores the digest or compares it with the
@@ -110,10 +111,19 @@ __global__ void __launch_bounds__(kHashThreads) sha_chunks(const uint8_t *__rest
 __global__ void __launch_bounds__(256) copy_segments(SegmentBatch sb, const unsigned long long *guard) {
     if (guard != nullptr && *guard != ~0ull) return;
     const Segment s = sb.seg[blockIdx.y];
-    const uint4 *src = reinterpret_cast<const uint4 *>(s.src);
-    uint4 *dst = reinterpret_cast<uint4 *>(s.dst);
-    for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < s.n16; i += (uint64_t)gridDim.x * 256)
-        st_once(dst + i, ld_once(src + i));
+    const uint64_t step = (uint64_t)gridDim.x * 256, i0 = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    if (s.mode == kSegCopy16) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(s.src);
+        uint4 *dst = reinterpret_cast<uint4 *>(s.dst);
+        for (uint64_t i = i0; i < s.n; i += step) st_once(dst + i, ld_once(src + i));
+    } else if (s.mode == kSegCopy4) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(s.src);
+        uint32_t *dst = reinterpret_cast<uint32_t *>(s.dst);
+        for (uint64_t i = i0; i < s.n; i += step) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+    } else {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(s.dst);
+        for (uint64_t i = i0; i < s.n; i += step) dst[i] = 0u;
+    }
 }
 
 __global__ void __launch_bounds__(256) write_words(uint64_t *dst, WordBatch wb) {
@@ -125,7 +135,7 @@ __global__ void __launch_bounds__(256) write_words(uint64_t *dst, WordBatch wb) 
 hipError_t launch_copy_segments(const SegmentBatch &sb, const unsigned long long *guard, hipStream_t st) {
     if (sb.n == 0) return hipSuccess;
     uint64_t most = 0;
-    for (int i = 0; i < sb.n; ++i) most = sb.seg[i].n16 > most ? sb.seg[i].n16 : most;
+    for (int i = 0; i < sb.n; ++i) most = sb.seg[i].n > most ? sb.seg[i].n : most;
     if (most == 0) return hipSuccess;
     uint64_t gx = (most + 255) / 256;
     if (gx > 4096) gx = 4096;

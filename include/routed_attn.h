@@ -315,10 +315,13 @@ ra_status cold_attn_decode(const ra_config *cfg, const ra_rows *rows, const void
  * receipts.  The image format is the library's own; all integers little-endian:
  *
  *   header   64 bytes of fields, then int64 lengths[B], zero-padded to a multiple of 16 bytes:
- *              0 magic "CRSASNP1" | 8 u32 version 1 | 12 u32 element type (0 fp32, 1 bf16)
+ *              0 magic "CRSASNP1" | 8 u32 version 1 | 12 u32 element type (0 fp32, 1 bf16,
+ *                2 the 8-bit cache: E4M3 codes + fp32 row scales)
  *             16 u32 B | 20 u32 Hkv | 24 u32 d | 28 u32 S | 32 u64 payload bytes
  *             40 u64 header bytes | 48 u32 chunk bytes 4096 | 52 u32 fan-in 16 | 56 u64 0
- *   payload  for b, for g: K[b][g][0:L_b][:] then V[b][g][0:L_b][:] (cache element bytes);
+ *   payload  for b, for g: K[b][g][0:L_b][:] then V[b][g][0:L_b][:] (cache element bytes; for
+ *            element type 2 the codes, then k_scale[b][g][0:L_b] and v_scale[b][g][0:L_b] (fp32),
+ *            each run zero-padded to a multiple of 16 bytes);
  *            then for b, for g: span_mean[b][g][0:floor(L_b/S)][:] then run_sum[b][g][:] (fp32)
  *   levels   D_1 = SHA-256 (FIPS 180-4) of each 4096-byte chunk of header|payload (the last one
  *            may be short); D_(l+1) = SHA-256 of each group of 16 digests (512 bytes) of D_l while
@@ -329,10 +332,13 @@ ra_status cold_attn_decode(const ra_config *cfg, const ra_rows *rows, const void
  * writes exactly those and leaves every other row and slot of the destination untouched.
  * `lengths` arguments are HOST arrays of cfg->batch int64 token counts; `header` arguments are
  * HOST copies of the first bytes of an image (at least the header); `image` is DEVICE memory.
- * The 8-bit cache is not covered (snapshots hold fp32 or bf16 caches). */
+ * The 8-bit cache (the release post's planned quantised cache, "Limitations and next steps")
+ * has its own pack / unpack / size calls (element type 2); parse and verify read every type. */
+
+#define RA_SNAPSHOT_E4M3 2 /* element type of images of the 8-bit cache */
 
 typedef struct {
-    int32_t dtype;         /* ra_dtype of the saved K/V rows */
+    int32_t dtype;         /* element type of the saved K/V rows: ra_dtype, or RA_SNAPSHOT_E4M3 */
     int32_t batch;         /* B */
     int32_t num_kv_heads;  /* Hkv */
     int32_t head_dim;      /* d */
@@ -372,6 +378,19 @@ ra_status kv_snapshot_verify(const void *header, size_t header_avail, const void
 ra_status kv_snapshot_unpack(const ra_config *cfg, const void *header, size_t header_avail, const void *image,
                              size_t image_bytes, const uint64_t *guard, void *k_cache, void *v_cache,
                              float *span_mean, float *run_sum, void *stream);
+
+/* kv_snapshot_bytes, _pack and _unpack for the 8-bit cache (image element type 2): codes
+ * [B][Hkv][capacity][d] (uint8, 16-byte aligned) and one fp32 scale per row [B][Hkv][capacity]
+ * (4-byte aligned) for K and V, as kv_quantize_fp8 writes them; cfg->dtype plays no part.
+ * Unpack restores codes, scales and summaries of the live rows only, as above. */
+size_t kv_snapshot_bytes_fp8(const ra_config *cfg, const int64_t *lengths);
+ra_status kv_snapshot_pack_fp8(const ra_config *cfg, const uint8_t *k_codes, const uint8_t *v_codes,
+                               const float *k_scales, const float *v_scales, const float *span_mean,
+                               const float *run_sum, const int64_t *lengths, void *image, size_t image_bytes,
+                               void *stream);
+ra_status kv_snapshot_unpack_fp8(const ra_config *cfg, const void *header, size_t header_avail, const void *image,
+                                 size_t image_bytes, const uint64_t *guard, uint8_t *k_codes, uint8_t *v_codes,
+                                 float *k_scales, float *v_scales, float *span_mean, float *run_sum, void *stream);
 
 /* Host file helpers: write `bytes` bytes (through a temporary file renamed into place), or read
  * a whole file into `buf` (capacity bytes); with buf NULL only *bytes (the file size) is set. */

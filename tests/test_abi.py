@@ -199,6 +199,43 @@ def test_snapshot_entry_points_validate_before_launch():
         assert st == status, (kw, st, lib.ra_last_error())
 
 
+def test_snapshot_of_the_8bit_cache_header_size_and_validation():
+    """Element type 2 (codes + row scales): the library parses the oracle's image, sizes it alike,
+    and rejects NULL or misaligned scale arrays, a short image and images of the other kind."""
+    from oracle import snapshot as N
+    rng = np.random.default_rng(5)
+    B, Hkv, cap, d, S = 3, 2, 300, 64, 16
+    lengths = np.array([300, 17, 0], dtype=np.int64)
+    k, v = (rng.integers(0, 256, (B, Hkv, cap, d), dtype=np.uint8) for _ in range(2))
+    ks, vs = (rng.random((B, Hkv, cap)).astype(np.float32) for _ in range(2))
+    mean = rng.standard_normal((B, Hkv, cap // S, d)).astype(np.float32)
+    run = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+    img = N.build_image(k, v, mean, run, lengths, S, ks, vs)
+    c = ra.Config(num_q_heads=4, num_kv_heads=Hkv, head_dim=d, span_size=S, top_k=4, window=S, dtype=ra.RA_BF16,
+                  batch=B, capacity=cap)
+    info, L = ra.kv_snapshot_parse(img)
+    assert info["dtype"] == ra.RA_SNAPSHOT_E4M3 and list(L) == [300, 17, 0]
+    assert info["image_bytes"] == len(img) == ra.snapshot_bytes_fp8(c, lengths)
+    assert ra.snapshot_bytes(c, lengths) != len(img)  # the bf16 image of the same state differs in size
+    lib = ra.lib()
+    cc = c.c()
+    Lp = ctypes.c_void_p(lengths.ctypes.data)
+    n = len(img)
+    pack = lib.kv_snapshot_pack_fp8
+    assert pack(ctypes.byref(cc), FAKE, FAKE, None, FAKE, FAKE, FAKE, Lp, FAKE, n, None) == 1
+    assert pack(ctypes.byref(cc), FAKE, FAKE, FAKE, ctypes.c_void_p(0x1002), FAKE, FAKE, Lp, FAKE, n, None) == 1
+    assert pack(ctypes.byref(cc), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, Lp, FAKE, n - 1, None) == 3
+    hdr = np.frombuffer(img, dtype=np.uint8)
+    assert lib.kv_snapshot_unpack(ctypes.byref(cc), ctypes.c_void_p(hdr.ctypes.data), 96, FAKE, n, None, FAKE, FAKE,
+                                  FAKE, FAKE, None) == 1
+    assert lib.kv_snapshot_unpack_fp8(ctypes.byref(cc), ctypes.c_void_p(hdr.ctypes.data), 96, FAKE, n - 1, None,
+                                      FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 6
+    _, img16 = small_snapshot()
+    h16 = np.frombuffer(img16, dtype=np.uint8)
+    assert lib.kv_snapshot_unpack_fp8(ctypes.byref(cc), ctypes.c_void_p(h16.ctypes.data), 96, FAKE, len(img16),
+                                      None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+
+
 def test_snapshot_file_helpers_round_trip(tmp_path):
     _, img = small_snapshot()
     p = str(tmp_path / "s.bin")

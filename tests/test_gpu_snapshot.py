@@ -206,3 +206,152 @@ def test_snapshot_of_the_1m_cache():
     img[x] ^= 0x40
     ra.kv_snapshot_verify(header, img, bad)
     assert int(bad.item()) == 4096 * (x // 4096)
+
+
+# ------------------------------------------------------------------------- the 8-bit cache
+class Fp8SnapCase(SnapCase):
+    """SnapCase whose bf16 cache is quantised on the device to the 8-bit cache (E4M3 codes and
+    one fp32 scale per row); rows past the lengths keep sentinel codes and scales."""
+
+    def __init__(self, w, lengths, capacity=None, seed=11):
+        super().__init__(w, lengths, capacity, seed)
+        c = self.cfg
+        shape = (c.batch, c.num_kv_heads, c.capacity, c.head_dim)
+        self.K8 = torch.full(shape, 0xAA, dtype=torch.uint8, device="cuda")
+        self.V8 = torch.full(shape, 0x55, dtype=torch.uint8, device="cuda")
+        self.KS = torch.full(shape[:3], -1.0, dtype=torch.float32, device="cuda")
+        self.VS = torch.full(shape[:3], -2.0, dtype=torch.float32, device="cuda")
+        zero = torch.zeros(c.batch, dtype=torch.int64, device="cuda")
+        L = torch.as_tensor(self.lengths).cuda()
+        most = max(1, int(self.lengths.max()))
+        ra.kv_quantize_fp8(c, self.K, self.K8, self.KS, zero, L, most)
+        ra.kv_quantize_fp8(c, self.V, self.V8, self.VS, zero, L, most)
+        torch.cuda.synchronize()
+
+    def oracle_image(self):
+        return N.build_image(self.K8.cpu().numpy(), self.V8.cpu().numpy(), self.mean_h, self.run_h, self.lengths,
+                             self.w.span_size, self.KS.cpu().numpy(), self.VS.cpu().numpy())
+
+    def pack(self, slack=0):
+        n = ra.snapshot_bytes_fp8(self.cfg, self.lengths)
+        img = torch.full((n + slack,), 0xAA, dtype=torch.uint8, device="cuda")
+        ra.kv_snapshot_pack_fp8(self.cfg, self.K8, self.V8, self.KS, self.VS, self.pipe.span_mean, self.pipe.run_sum,
+                                self.lengths, img)
+        torch.cuda.synchronize()
+        return img, n
+
+
+FP8_PACK_CASES = [
+    # capacities that are not multiples of 4: the scale rows of most (sequence, kv head) pairs do
+    # not start on 16 bytes; lengths 1 and 777 leave 12 bytes of padding after each scale run
+    ("d128_ragged_cap5003", small("decode_1m", span_size=64, window=64, top_k=4, decode_len=5000),
+     [5000, 1, 0, 777], 5003),
+    ("d64_Hkv2_cap2001", small("decode_1m", num_q_heads=8, num_kv_heads=2, head_dim=64, span_size=32, window=32,
+                               top_k=4, decode_len=2000), [2000, 30], 2001),
+]
+
+
+@pytest.mark.parametrize("name,w,lengths,cap", FP8_PACK_CASES, ids=[c[0] for c in FP8_PACK_CASES])
+def test_pack_of_the_8bit_cache_matches_the_oracle_image(name, w, lengths, cap):
+    c = Fp8SnapCase(w, lengths, capacity=cap)
+    img, n = c.pack(slack=4096)
+    dev = img.cpu().numpy()
+    ref = c.oracle_image()
+    assert n == len(ref)
+    assert first_difference(dev[:n].tobytes(), ref) is None, first_difference(dev[:n].tobytes(), ref)
+    assert (dev[n:] == 0xAA).all()
+    # the device check names the chunk of a flipped scale byte and of a flipped padding byte
+    h = N.parse_header(ref)
+    header = bytes(ref[:h["header"]])
+    bad = torch.empty(1, dtype=torch.int64, device="cuda")
+    L0 = int(c.lengths[0])
+    d = w.head_dim
+    k_scale_at = h["header"] + 2 * L0 * d  # sequence 0, kv head 0: after its K and V codes
+    L1 = int(c.lengths[1])
+    seq1 = h["header"] + w.num_kv_heads * (2 * L0 * d + 2 * N.scale_run_bytes(L0))
+    pad_at = seq1 + 2 * L1 * d + 4 * L1  # first padding byte after sequence 1's K scales
+    for x in (k_scale_at + 5, pad_at):
+        img2 = img.clone()
+        img2[x] ^= 0x10
+        ref2 = bytearray(ref)
+        ref2[x] ^= 0x10
+        ra.kv_snapshot_verify(header, img2, bad)
+        assert int(bad.item()) == N.verify(ref2, header) == 4096 * (x // 4096)
+
+
+def fp8_sentinels(c):
+    cfg = c.cfg
+    shape = (cfg.batch, cfg.num_kv_heads, cfg.capacity, cfg.head_dim)
+    return (torch.full(shape, 0x11, dtype=torch.uint8, device="cuda"),
+            torch.full(shape, 0x22, dtype=torch.uint8, device="cuda"),
+            torch.full(shape[:3], 3.0, dtype=torch.float32, device="cuda"),
+            torch.full(shape[:3], 4.0, dtype=torch.float32, device="cuda"),
+            torch.full(tuple(c.pipe.span_mean.shape), 7.0, dtype=torch.float32, device="cuda"),
+            torch.full(tuple(c.pipe.run_sum.shape), 9.0, dtype=torch.float32, device="cuda"))
+
+
+def test_unpack_of_the_8bit_cache_restores_exactly_the_saved_state():
+    """Codes, scales and summaries of the live rows restored; every other code, scale slot (the
+    image's padding included) and summary slot untouched; a damaged image restores nothing."""
+    w = small("decode_1m", span_size=64, window=64, top_k=4, decode_len=3000)
+    c = Fp8SnapCase(w, [3000, 101, 0], capacity=3103)
+    img, n = c.pack()
+    header = c.oracle_image()[:N.header_bytes(3)]
+    K8, V8, KS, VS, M, R = fp8_sentinels(c)
+    ra.kv_snapshot_unpack_fp8(c.cfg, header, img, K8, V8, KS, VS, M, R)
+    torch.cuda.synchronize()
+    src = [t.cpu().numpy() for t in (c.K8, c.V8, c.KS, c.VS)]
+    got = [t.cpu().numpy() for t in (K8, V8, KS, VS)]
+    fills = (0x11, 0x22, 3.0, 4.0)
+    for b, L in enumerate(c.lengths):
+        for s_, g_, f in zip(src, got, fills):
+            assert np.array_equal(g_[b, :, :L], s_[b, :, :L])
+            assert (g_[b, :, L:] == f).all()
+        ns = L // w.span_size
+        Mb, Rb = M.cpu().numpy(), R.cpu().numpy()
+        assert np.array_equal(Mb[b, :, :ns], c.mean_h[b, :, :ns]) and (Mb[b, :, ns:] == 7.0).all()
+        assert np.array_equal(Rb[b], c.run_h[b])
+    img[n // 2] ^= 1
+    bad = torch.empty(1, dtype=torch.int64, device="cuda")
+    K8b, V8b, KSb, VSb, Mb2, Rb2 = fp8_sentinels(c)
+    ra.kv_snapshot_verify(header, img, bad)
+    ra.kv_snapshot_unpack_fp8(c.cfg, header, img, K8b, V8b, KSb, VSb, Mb2, Rb2, guard=bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) != -1
+    assert (K8b == 0x11).all() and (KSb == 3.0).all() and (VSb == 4.0).all() and (Mb2 == 7.0).all()
+
+
+def test_8bit_file_round_trip_then_decode_continues(tmp_path):
+    """Summaries over the 8-bit cache, a decode step, save to a file, load into fresh buffers:
+    the same decode step gives the same bits."""
+    w = small("decode_1m", span_size=64, window=64, top_k=8, decode_len=6000)
+    L = np.array([6000, 2501])
+    c = Fp8SnapCase(w, L, capacity=6101)
+    cfg = c.cfg
+    zero = torch.zeros(2, dtype=torch.int64, device="cuda")
+    Ld = torch.as_tensor(L).cuda()
+    ra.span_summary_update_fp8(cfg, c.K8, c.KS, c.pipe.span_mean, c.pipe.run_sum, zero, Ld, int(L.max()))
+    rows, _ = c.rows_for([0, 1], L - 1)
+    p = c.pipe
+    p.reserve(2, int(L.max()) - 1, ra.RA_OP_DECODE)
+
+    def decode(K8, V8, KS, VS, M):
+        ra.route_scores(cfg, rows, M, p.scores)
+        ra.topk_spans(cfg, rows, p.scores, p.sel)
+        ra.routed_attn_decode_fp8(cfg, rows, K8, V8, KS, VS, p.sel, p.out, p.workspace)
+        torch.cuda.synchronize()
+        return p.sel.clone(), p.out.clone()
+
+    sel0, out0 = decode(c.K8, c.V8, c.KS, c.VS, p.span_mean)
+    path = str(tmp_path / "session8.crsnap")
+    root = ra.save_snapshot_fp8(path, cfg, c.K8, c.V8, c.KS, c.VS, p.span_mean, p.run_sum, L)
+    with open(path, "rb") as f:
+        on_disk = f.read()
+    assert N.verify(on_disk) is None and on_disk[-32:].hex() == root
+    assert N.parse_header(on_disk)["dtype"] == 2
+    K8, V8, KS, VS, M, R = fp8_sentinels(c)
+    got = ra.load_snapshot_fp8(path, cfg, K8, V8, KS, VS, M, R)
+    assert list(got) == list(L)
+    assert torch.equal(R, p.run_sum)
+    sel1, out1 = decode(K8, V8, KS, VS, M)
+    assert torch.equal(sel0, sel1) and torch.equal(out0, out1)
