@@ -70,10 +70,12 @@ __device__ __forceinline__ bool entry_span(const int32_t *sel, int64_t rh, int e
     if (e < k) {
         const int32_t *row = sel + rh * k;
         j = row[e];
-        if (j < 0 || j >= div_nonneg(w0, S)) return false;
-        for (int x = 0; x < e; ++x)
-            if (row[x] == j) return false;
-        return true;
+        // an entry that repeats an earlier entry of its row-head is not attended again; the
+        // earlier entries are compared without early exit, so their loads go out together
+        int rep = 0;
+#pragma unroll 8
+        for (int x = 0; x < e; ++x) rep |= row[x] == (int32_t)j;
+        return j >= 0 && j < div_nonneg(w0, S) && rep == 0;
     }
     j = div_nonneg(w0, S) + (e - k);
     return j * S <= t;

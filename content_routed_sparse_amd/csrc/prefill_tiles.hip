@@ -562,7 +562,8 @@ __device__ __forceinline__ void chunk_codes(const uint8_t *base, uint8_t *dst, c
 }
 
 // The staged codes of a chunk -> bf16 in the swizzled buffers (K, and V when WITH_V): a thread
-// converts 32 codes of one row per step (v_cvt_pk_f32_fp8, then an exact bf16 packing).
+// converts 32 codes of one row per step, two codes per v_cvt_scalef32_pk_bf16_fp8 with scale 1
+// (every E4M3 value is a bf16 value: the conversion is exact).
 template <int D, bool WITH_V>
 __device__ __forceinline__ void codes_to_bf16(const StageF8<D> &st, int tid) {
     constexpr int SEG = D / 32;         // 32-code segments per row
@@ -579,10 +580,8 @@ __device__ __forceinline__ void codes_to_bf16(const StageF8<D> &st, int tid) {
         uint32_t h[16];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);  // bytes 0, 1
-            const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);   // bytes 2, 3
-            h[2 * i] = pack_bf16x2(lo.x, lo.y);
-            h[2 * i + 1] = pack_bf16x2(hi.x, hi.y);
+            h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.f, false));
+            h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.f, true));
         }
         uint16_t *dst = is_v ? st.vb : st.kb;
 #pragma unroll
