@@ -217,9 +217,13 @@ __device__ __forceinline__ void chunk_rows(const uint16_t *base, uint16_t *dst, 
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (RA_LDS void *)(dst + ii * ROWS * D), 16, rl * D * 2 + part,
                                                      (c * D + ii * ROWS * D) * 2, 0, 0);
     } else {
+        // (the rows are recomputed at every call: hoisted out of the callers' loops, one register
+        // per load instruction would stay live through the whole sweep)
+        int rlv = rl;
+        asm volatile("" : "+v"(rlv));
 #pragma unroll
         for (int ii = wave; ii < NI; ii += kMfmaWaves) {
-            int g = c + ii * ROWS + rl;
+            int g = c + ii * ROWS + rlv;
             g = g < n ? g : n - 1;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (RA_LDS void *)(dst + ii * ROWS * D), 16, g * D * 2 + part, 0, 0, 0);
         }
@@ -1032,7 +1036,8 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
 
     // this lane's entries: query lr of group gi of wave `wave` is entry e = 16 (kQG wave + gi) + lr
     // of the tile, i.e. row r0 + e / G, query head g G + e mod G
-    int64_t row_e[kQG], qoff[kQG], t_e[kQG];
+    int64_t row_e[kQG], t_e[kQG];
+    uint32_t qrow[kQG];  // the entry's row-head (query and output row; n_rows Hq < 2^32, checked on the host)
     bool valid[kQG];
     int seq_e[kQG];
 #pragma unroll
@@ -1044,7 +1049,7 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
         const int hq = g * G + (valid[gi] ? e % G : 0);
         const int seq_raw = row_seq[row_c];
         const int64_t t_raw = row_pos[row_c];
-        qoff[gi] = (row_c * Hq + hq) * D;  // the entry's query row (and output row)
+        qrow[gi] = (uint32_t)(row_c * Hq + hq);
         seq_e[gi] = seq_raw < 0 ? 0 : (seq_raw >= B ? B - 1 : seq_raw);
         t_e[gi] = t_raw < 0 ? 0 : (t_raw > max_pos ? max_pos : t_raw);
     }
@@ -1110,7 +1115,7 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
         for (int gi = 0; gi < kQG; ++gi) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                uint4 raw = *reinterpret_cast<const uint4 *>(q + qoff[gi] + 32 * ks + 8 * lg);
+                uint4 raw = *reinterpret_cast<const uint4 *>(q + (int64_t)qrow[gi] * D + 32 * ks + 8 * lg);
                 if (!active[gi]) raw = make_uint4(0, 0, 0, 0);
                 qb[gi][ks] = __builtin_bit_cast(bf16x8_t, raw);
             }
@@ -1159,7 +1164,7 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
             const float lt = group_sum4(l[gi]);
             if (active[gi]) {
                 const float inv = 1.f / lt;
-                float *dst = out + qoff[gi];
+                float *dst = out + (int64_t)qrow[gi] * D;
 #pragma unroll
                 for (int et = 0; et < ET; ++et)
                     *reinterpret_cast<float4 *>(dst + 16 * et + 4 * lg) =
