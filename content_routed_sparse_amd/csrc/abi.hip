@@ -292,7 +292,6 @@ ra_status attn_dense_causal(const ra_config *cfg, const ra_rows *rows, const voi
     const ra::RowArgs a = row_args(cfg, rows);
     const int RT = 128 / a.G;
     if (a.Hkv * ra::ceil_div(a.n_rows, RT) >= kMaxGrid) return fail(RA_EUNSUPPORTED, "too many rows");
-    if (a.n_rows * (int64_t)a.Hq >= (1ll << 32)) return fail(RA_EUNSUPPORTED, "n_rows * num_q_heads must be below 2^32");
     return hip_status(ra::launch_dense(a, k_cache, v_cache, out, (hipStream_t)stream), "attn_dense_causal launch");
 }
 

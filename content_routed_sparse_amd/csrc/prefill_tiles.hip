@@ -1037,7 +1037,7 @@ dense_mfma(const uint16_t *__restrict__ q, const int32_t *__restrict__ row_seq, 
     // this lane's entries: query lr of group gi of wave `wave` is entry e = 16 (kQG wave + gi) + lr
     // of the tile, i.e. row r0 + e / G, query head g G + e mod G
     int64_t row_e[kQG], t_e[kQG];
-    uint32_t qrow[kQG];  // the entry's row-head (query and output row; n_rows Hq < 2^32, checked on the host)
+    uint32_t qrow[kQG];  // the entry's row-head (query and output row; n_rows Hq < 2^31, checked on the host)
     bool valid[kQG];
     int seq_e[kQG];
 #pragma unroll

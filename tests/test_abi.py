@@ -293,6 +293,11 @@ def test_grid_limits_are_checked_before_launch():
     st = lib.routed_attn_decode_fp8(ctypes.byref(c), ctypes.byref(rows(8192, (1 << 20) + 8191)), FAKE, FAKE, FAKE,
                                     FAKE, FAKE, FAKE, FAKE, big_ws, None)
     assert st == 2
+    # every entry point indexes row-heads with 32 bits: 2^26 rows x 32 query heads is refused
+    st = lib.attn_dense_causal(ctypes.byref(c), ctypes.byref(rows(1 << 26, (1 << 20) + 8191)), FAKE, FAKE, FAKE, None)
+    assert st == 2 and "too many rows" in lib.ra_last_error().decode()
+    st = lib.attn_dense_causal(ctypes.byref(c), ctypes.byref(rows(1 << 25, (1 << 20) + 8191)), FAKE, FAKE, None, None)
+    assert st == 1  # (below the limit: the NULL output is what fails)
 
 
 def test_noalloc_decode_validates_before_launch():
