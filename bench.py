@@ -369,6 +369,7 @@ def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0, fp8=True):
     torch.cuda.synchronize()
     step_ms = (time.perf_counter() - t0) * 1e3 / steps
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    alg_bytes = prefill_algorithmic_bytes(w, sel.cpu().numpy(), 2)
     # algorithmic work: 4 d flops per (row-head, attended key) for Q.K^T and P.V, plus 2 d per
     # (row-head, routable span) for routing; attended keys = selected spans' keys + window
     pos = np.arange(P, L)
@@ -423,7 +424,8 @@ def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0, fp8=True):
         "roofline": {"bound": "mfma", "kernel": "routed_attn_prefill (dispatch + bf16 MFMA tiles + merge)",
                      "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(tflops / 2500.0, 4), "traffic": counter_traffic("routed_attn_prefill_8k_on_1m"),
-                     "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
+                     "algorithmic_flops_per_launch": attn_flops, "algorithmic_bytes_per_launch": alg_bytes,
+                     "avg_launch_ms": round(attn_ms, 4)},
         "step_flops": attn_flops + route_flops,
         "step_tflops": round(step_tflops, 1),
         "step_roofline": {"bound": "mfma", "what": "the whole step (summary update + route + top-k + attention)",
@@ -434,6 +436,26 @@ def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0, fp8=True):
         "dense_causal": dense,
         "ladder": rungs,
     }
+
+
+def prefill_algorithmic_bytes(w, sel_h, elem_bytes, row_scale_bytes=0):
+    """Bytes a routed_attn_prefill call of the chunk must move at least: the K and V rows of every
+    attended (kv head, span) once (the routed spans the selection names, complete, and the window
+    spans up to the chunk's last row), with their row scales for an 8-bit cache, plus q (bf16),
+    the selection, the rows' positions and sequences, and out (fp32)."""
+    P, n, L = w.prefix_len, w.chunk_len, w.prefix_len + w.chunk_len
+    S, W, G, d = w.span_size, w.window, w.group, w.head_dim
+    w_first = (max(0, P - W + 1) // S) * S // S
+    w_last = (L - 1) // S
+    keys = 0
+    for g in range(w.num_kv_heads):
+        spans = np.unique(sel_h[:, g * G:(g + 1) * G, :])
+        spans = spans[(spans >= 0) & (spans < w_first)]
+        keys += len(spans) * S
+        for j in range(w_first, w_last + 1):
+            keys += min(S, L - j * S)
+    kv = keys * 2 * (d * elem_bytes + row_scale_bytes)
+    return int(kv + n * w.num_q_heads * (d * 2 + w.top_k * 4 + d * 4) + n * 12)
 
 
 def bench_prefill_fp8(w, cfg, K, V, rows, t_p, t_l, steps, attn_flops, route_flops, out_bf16):
@@ -483,14 +505,17 @@ def bench_prefill_fp8(w, cfg, K, V, rows, t_p, t_l, steps, attn_flops, route_flo
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     tflops = attn_flops / (attn_ms * 1e-3) / 1e12
     step_tflops = (attn_flops + route_flops) / (step_ms * 1e-3) / 1e12
+    alg_bytes = prefill_algorithmic_bytes(w, sel.cpu().numpy(), 1, 4)
     # quantisation's effect on the result: largest |out_fp8 - out_bf16| over the chunk
     diff = float((out - out_bf16).abs().max().item())
     return {"workload": "prefill_8k_on_1m, 8-bit cache (E4M3 codes, one fp32 scale per kv-head row)",
             "value": round(n / (step_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(step_ms, 4),
             "roofline": {"bound": "mfma", "kernel": "routed_attn_prefill_fp8 (dispatch + 8-bit MFMA tiles + merge)",
                          "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
-                         "frac": round(tflops / 2500.0, 4), "traffic": None,
-                         "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
+                         "frac": round(tflops / 2500.0, 4),
+                         "traffic": counter_traffic("routed_attn_prefill_fp8_8k_on_1m"),
+                         "algorithmic_flops_per_launch": attn_flops, "algorithmic_bytes_per_launch": alg_bytes,
+                         "avg_launch_ms": round(attn_ms, 4)},
             "step_tflops": round(step_tflops, 1),
             "max_abs_vs_bf16_cache": round(diff, 5),
             "repeat_bitwise_identical": bool(torch.equal(first, out))}
