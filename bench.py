@@ -286,23 +286,18 @@ def main():
 
 
 def front_calls(ra, cfg, rows, mean, scores, sel):
-    """The step's routing and selection: route_topk_spans (one launch; its zeroed workspace is
-    allocated here, untimed) where supported, else route_scores then topk_spans."""
+    """The step's routing and selection: route_topk_spans (its zeroed workspace is allocated here,
+    untimed; one launch for these shapes up to 1088 routable spans, route_scores + topk_spans inside
+    the call beyond).  `scores` is unused: the call keeps its scores in its workspace."""
     import torch
 
     n = rows.q.shape[0]
     ws = torch.zeros(ra.workspace_bytes(cfg, ra.RA_OP_ROUTE_TOPK, n, rows.max_pos), dtype=torch.uint8,
                      device=rows.q.device)
-    try:
-        fused = ra.prepare("route_topk_spans", cfg, rows, mean, sel, ws)
-        fused()
-        fused._ws = ws  # keeps the workspace alive with the prepared call
-        return [fused], "route_topk_spans"
-    except ra.RoutedAttnError as e:
-        if e.status != 2:
-            raise
-    return [ra.prepare("route_scores", cfg, rows, mean, scores),
-            ra.prepare("topk_spans", cfg, rows, scores, sel)], "route_scores + topk_spans"
+    fused = ra.prepare("route_topk_spans", cfg, rows, mean, sel, ws)
+    fused._ws = ws  # keeps the workspace alive with the prepared call
+    r = cfg.num_routable(rows.max_pos)
+    return [fused], "route_topk_spans" if r <= 64 * 17 else "route_topk_spans (route_scores + topk_spans inside)"
 
 
 def counter_traffic(tag):
@@ -320,9 +315,10 @@ def counter_traffic(tag):
 
 def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0, fp8=True):
     """Chunked prefill: 8192 new tokens appended to a 1M-token cache (the chunk's K/V are in
-    the cache before timing).  A step = span_summary_update of the chunk + route_scores +
-    topk_spans + routed_attn_prefill for its 8192 x 32 row-heads.  With fp8, the same step over
-    the cache quantised to E4M3 codes (kv_quantize_fp8, untimed setup)."""
+    the cache before timing).  A step = span_summary_update of the chunk + route_topk_spans
+    (route_scores + topk_spans in one call) + routed_attn_prefill for its 8192 x 32 row-heads.
+    With fp8, the same step over the cache quantised to E4M3 codes (kv_quantize_fp8, untimed
+    setup)."""
     import torch
 
     import content_routed_sparse_amd as ra
@@ -343,15 +339,16 @@ def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0, fp8=True):
     run = torch.zeros(1, w.num_kv_heads, w.head_dim, dtype=torch.float32, device=dev)
     t_p, t_l = torch.tensor([P], device=dev), torch.tensor([L], device=dev)
     ra.span_summary_update(cfg, K, mean, run, torch.zeros(1, dtype=torch.int64, device=dev), t_p, P)  # setup
-    scores = torch.empty(n, w.num_q_heads, ra.score_stride(cfg, L - 1), dtype=torch.float32, device=dev)
     sel = torch.empty(n, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev)
     out = torch.empty(n, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
     ws = torch.empty(ra.workspace_bytes(cfg, ra.RA_OP_PREFILL, n, L - 1), dtype=torch.uint8, device=dev)
     # the chunk starts and ends on span boundaries, so re-running the step recomputes the same
     # summaries and leaves the running sum at zero: every step is the same work
+    # routing + selection in one call (route_topk_spans: the scores stay on chip; the same selection
+    # as route_scores + topk_spans); its workspace starts zeroed, untimed
+    ws_rt = torch.zeros(ra.workspace_bytes(cfg, ra.RA_OP_ROUTE_TOPK, n, L - 1), dtype=torch.uint8, device=dev)
     calls = [ra.prepare("span_summary_update", cfg, K, mean, run, t_p, t_l, n),
-             ra.prepare("route_scores", cfg, rows, mean, scores),
-             ra.prepare("topk_spans", cfg, rows, scores, sel)]
+             ra.prepare("route_topk_spans", cfg, rows, mean, sel, ws_rt)]
     attn = ra.prepare("routed_attn_prefill", cfg, rows, K, V, sel, out, ws)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -459,8 +456,8 @@ def prefill_algorithmic_bytes(w, sel_h, elem_bytes, row_scale_bytes=0):
 
 
 def bench_prefill_fp8(w, cfg, K, V, rows, t_p, t_l, steps, attn_flops, route_flops, out_bf16):
-    """The prefill step over the 8-bit cache: span_summary_update_fp8 of the chunk + route_scores
-    + topk_spans + routed_attn_prefill_fp8.  The tiles convert the codes to bf16 in LDS and run the
+    """The prefill step over the 8-bit cache: span_summary_update_fp8 of the chunk +
+    route_topk_spans + routed_attn_prefill_fp8.  The tiles convert the codes to bf16 in LDS and run the
     same bf16 MFMA products, so the flops and the peak are those of the bf16 step."""
     import torch
 
@@ -478,13 +475,12 @@ def bench_prefill_fp8(w, cfg, K, V, rows, t_p, t_l, steps, attn_flops, route_flo
     mean = torch.zeros(1, w.num_kv_heads, cfg.max_spans, w.head_dim, dtype=torch.float32, device=dev)
     run = torch.zeros(1, w.num_kv_heads, w.head_dim, dtype=torch.float32, device=dev)
     ra.span_summary_update_fp8(cfg, K8, KS, mean, run, zero, t_p, P)  # setup
-    scores = torch.empty(n, w.num_q_heads, ra.score_stride(cfg, L - 1), dtype=torch.float32, device=dev)
     sel = torch.empty(n, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev)
     out = torch.empty(n, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
     ws = torch.empty(ra.workspace_bytes(cfg, ra.RA_OP_PREFILL, n, L - 1), dtype=torch.uint8, device=dev)
+    ws_rt = torch.zeros(ra.workspace_bytes(cfg, ra.RA_OP_ROUTE_TOPK, n, L - 1), dtype=torch.uint8, device=dev)
     calls = [ra.prepare("span_summary_update_fp8", cfg, K8, KS, mean, run, t_p, t_l, n),
-             ra.prepare("route_scores", cfg, rows, mean, scores),
-             ra.prepare("topk_spans", cfg, rows, scores, sel)]
+             ra.prepare("route_topk_spans", cfg, rows, mean, sel, ws_rt)]
     attn = ra.prepare("routed_attn_prefill_fp8", cfg, rows, K8, V8, KS, VS, sel, out, ws)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -543,7 +539,7 @@ def prefill_ladder(w, cfg, K, V, q, mean, ws, dense_steps, top):
     256K, 512K and 1M tokens (the last rung is the prefill leg's own chunk; its routed path is timed
     here like the others).  Every span the rows can route to lies in the cache's first 1M tokens,
     which the prefill leg has summarised, so the summaries need no update.  Reported per rung: the
-    routed attention call, the routed path (route_scores + topk_spans + routed_attn_prefill) and
+    routed attention call, the routed path (route_topk_spans + routed_attn_prefill) and
     attn_dense_causal, and the dense time over each."""
     import torch
 
@@ -556,10 +552,10 @@ def prefill_ladder(w, cfg, K, V, q, mean, ws, dense_steps, top):
         L = P + n
         rows = ra.Rows(q, torch.zeros(n, dtype=torch.int32, device=dev),
                        torch.arange(P, L, dtype=torch.int64, device=dev), L - 1)
-        scores = torch.empty(n, w.num_q_heads, ra.score_stride(cfg, L - 1), dtype=torch.float32, device=dev)
         sel = torch.empty(n, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev)
         o = torch.empty(n, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
-        front = [ra.prepare("route_scores", cfg, rows, mean, scores), ra.prepare("topk_spans", cfg, rows, scores, sel)]
+        ws_rt = torch.zeros(ra.workspace_bytes(cfg, ra.RA_OP_ROUTE_TOPK, n, L - 1), dtype=torch.uint8, device=dev)
+        front = [ra.prepare("route_topk_spans", cfg, rows, mean, sel, ws_rt)]
         attn = ra.prepare("routed_attn_prefill", cfg, rows, K, V, sel, o, ws)
         path_ms = time_calls(front + [attn], 3)
         attn_ms = time_calls([attn], 3)

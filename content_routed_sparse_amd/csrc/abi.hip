@@ -190,10 +190,6 @@ ra_status route_topk_spans(const ra_config *cfg, const ra_rows *rows, const floa
     if (rows->n_rows == 0) return ok();
     if (!span_mean || !sel) return fail(RA_EINVAL, "NULL span_mean or sel");
     const ra::RowArgs a = row_args(cfg, rows);
-    const int64_t rmax = ra::num_routable(a.max_pos, a.S, a.W);
-    if (rmax > ra::route_topk_max_routable())
-        return fail(RA_EUNSUPPORTED, "route_topk_spans selects among at most %lld routable spans (%lld here): call "
-                    "route_scores, then topk_spans", (long long)ra::route_topk_max_routable(), (long long)rmax);
     if (a.n_rows * a.Hkv >= kMaxGrid) return fail(RA_EUNSUPPORTED, "too many rows for one launch");
     const size_t need = ra::route_topk_workspace_bytes(a);
     if (!workspace || workspace_bytes < need)

@@ -45,7 +45,6 @@ hipError_t launch_topk(const RowArgs &a, const float *scores, int64_t stride, in
 // Routing and selection in one launch (few rows): the workspace holds one counter per (row, kv
 // head) -- zero before the first call, zero again after each -- and the scores.
 size_t route_topk_workspace_bytes(const RowArgs &a);
-int64_t route_topk_max_routable();  // largest r(max_pos) supported
 hipError_t launch_route_topk(const RowArgs &a, const float *mean, int32_t *sel, void *ws, hipStream_t st);
 
 // Decode: workspace holds partial records [n_rows][Hq][k + max_window_spans][n_sub].

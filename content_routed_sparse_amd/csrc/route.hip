@@ -472,20 +472,28 @@ size_t route_topk_workspace_bytes(const RowArgs &a) {
     return route_topk_counter_bytes(a) + (size_t)(a.n_rows * a.Hq * route_topk_stride(a)) * 4;
 }
 
-// (more spans: the two launches of route_scores + topk_spans were measured faster at 2559)
-int64_t route_topk_max_routable() { return 64 * 17; }
-
+// Routing and selection in one call; the path depends on the shape, the result does not (both
+// compute route_scores' scores and topk_spans' selection):
+//  * few rows (decode), r <= 64 * 17: route_topk (the last block of each (row, kv head) selects);
+//  * many bf16 rows (route_scores' MFMA regime) or more spans: route_scores then topk_spans through
+//    the workspace's score rows (for few rows and 2559 spans the two launches were measured
+//    faster than one; for a prefill chunk see the design notes on the fused sweep).
 hipError_t launch_route_topk(const RowArgs &a, const float *mean, int32_t *sel, void *ws, hipStream_t st) {
     const int64_t rmax = num_routable(a.max_pos, a.S, a.W);
     if (a.n_rows == 0) return hipSuccess;
     uint32_t *counters = (uint32_t *)ws;
     float *scores = (float *)((char *)ws + route_topk_counter_bytes(a));
     const int64_t stride = route_topk_stride(a);
-    if (a.dtype == RA_BF16)
-        return a.d == 64 ? route_topk_dispatch<uint16_t, 64>(a, mean, scores, stride, sel, counters, rmax, st)
-                         : route_topk_dispatch<uint16_t, 128>(a, mean, scores, stride, sel, counters, rmax, st);
-    return a.d == 64 ? route_topk_dispatch<float, 64>(a, mean, scores, stride, sel, counters, rmax, st)
-                     : route_topk_dispatch<float, 128>(a, mean, scores, stride, sel, counters, rmax, st);
+    const bool many = a.dtype == RA_BF16 && a.n_rows * a.G >= 256;
+    if (!many && rmax <= 64 * 17) {
+        if (a.dtype == RA_BF16)
+            return a.d == 64 ? route_topk_dispatch<uint16_t, 64>(a, mean, scores, stride, sel, counters, rmax, st)
+                             : route_topk_dispatch<uint16_t, 128>(a, mean, scores, stride, sel, counters, rmax, st);
+        return a.d == 64 ? route_topk_dispatch<float, 64>(a, mean, scores, stride, sel, counters, rmax, st)
+                         : route_topk_dispatch<float, 128>(a, mean, scores, stride, sel, counters, rmax, st);
+    }
+    const hipError_t e = launch_route(a, mean, scores, stride, st);
+    return e != hipSuccess ? e : launch_topk(a, scores, stride, sel, st);
 }
 
 hipError_t launch_route(const RowArgs &a, const float *mean, float *scores, int64_t stride, hipStream_t st) {

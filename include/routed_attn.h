@@ -129,17 +129,16 @@ ra_status topk_spans(const ra_config *cfg, const ra_rows *rows, const float *sco
                      int32_t *sel, void *stream);
 
 /*
- * route_topk_spans -- route_scores then topk_spans in one launch, for few rows (decode).  The
- * blocks score the routable spans with the fp32 products of route_scores' few-row path (the same
- * scores, bit for bit) into the workspace; the last block of each (row, kv head) to finish then
- * selects for the kv head's query heads exactly as topk_spans does.
- *   Supported when r(max_pos) <= 1088 (RA_EUNSUPPORTED otherwise: call route_scores, then
- *   topk_spans).  Correct for any number of rows; with many rows per sequence (a prefill
- *   chunk) route_scores + topk_spans is faster.
+ * route_topk_spans -- route_scores then topk_spans in one call: the same selection, bit for bit
+ * (both paths compute route_scores' scores with route_scores' own arithmetic).
+ *   - few rows (decode), r(max_pos) <= 1088: one launch; the blocks score the spans into the
+ *     workspace and the last block of each (row, kv head) to finish selects for its query heads;
+ *   - otherwise (many bf16 rows, as in a prefill chunk, or more spans): route_scores, then
+ *     topk_spans, through the workspace.
  *   workspace      device memory of at least ra_workspace_bytes(cfg, RA_OP_ROUTE_TOPK, n_rows,
- *                  max_pos) bytes: n_rows x Hkv counters, then the scores.  The counters must be
- *                  zero before the first call (clear a new workspace once); every call leaves them
- *                  zero.  Calls that share a workspace must not overlap.
+ *                  max_pos) bytes: n_rows x Hkv counters, then room for the scores.  The counters
+ *                  must be zero before the first call (clear a new workspace once); every call
+ *                  leaves them zero.  Calls that share a workspace must not overlap.
  */
 ra_status route_topk_spans(const ra_config *cfg, const ra_rows *rows, const float *span_mean, int32_t *sel,
                            void *workspace, size_t workspace_bytes, void *stream);

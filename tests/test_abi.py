@@ -313,15 +313,18 @@ def test_noalloc_decode_validates_before_launch():
 
 
 def test_route_topk_spans_validates_before_launch():
-    """The fused routing + selection: at most 1088 routable spans (else unsupported), a
-    workspace of the stated size (counters + scores), no NULL buffers."""
+    """The fused routing + selection: a workspace of the stated size (counters + room for the
+    scores) for every shape (2559 routable spans included), no NULL buffers."""
     lib = ra.lib()
     c = cfg().c()
     big = ctypes.c_size_t(1 << 40)
     assert lib.route_topk_spans(ctypes.byref(c), ctypes.byref(rows()), FAKE, None, FAKE, big, None) == 1
-    c10m = cfg(span_size=4096, window=4096, capacity=10485760).c()  # 2559 routable spans
-    st = lib.route_topk_spans(ctypes.byref(c10m), ctypes.byref(rows(1, 10485759)), FAKE, FAKE, FAKE, big, None)
-    assert st == 2 and "route_scores" in lib.ra_last_error().decode()
+    c10m = cfg(span_size=4096, window=4096, capacity=10485760)  # 2559 routable spans
+    need10 = ra.workspace_bytes(c10m, ra.RA_OP_ROUTE_TOPK, 1, 10485759)
+    assert need10 == 256 + 32 * 2560 * 4
+    st = lib.route_topk_spans(ctypes.byref(c10m.c()), ctypes.byref(rows(1, 10485759)), FAKE, FAKE, FAKE, need10 - 1,
+                              None)
+    assert st == 3
     need = ra.workspace_bytes(cfg(), ra.RA_OP_ROUTE_TOPK, 1, (1 << 20) - 1)
     assert need == 256 + 32 * 1024 * 4  # 4 counters (one 256-byte line), 32 heads x 1023 scores padded to 1024
     assert lib.route_topk_spans(ctypes.byref(c), ctypes.byref(rows()), FAKE, FAKE, FAKE, need - 1, None) == 3

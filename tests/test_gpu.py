@@ -737,3 +737,73 @@ def test_route_topk_spans_equals_route_then_topk(name, w):
     c.pipe.sel.copy_(sel[:c.B])
     stats = c.check(np.arange(c.B), lengths - 1, q, np.arange(c.B), scores=False)
     assert not stats["fail"], stats["fail"][:3]
+
+
+# many rows and long rows: route_topk_spans runs route_scores + topk_spans through its workspace;
+# the selection must be that of the two calls, bit for bit
+MANY_ROUTE_TOPK_CASES = [
+    # name, workload, lengths, rows: (sequence, position) pairs drawn per sequence, edit
+    ("d128_G8_r999", small("ragged_decode_16", batch=1, span_size=64, window=64, top_k=16), [64000], 48, None),
+    ("d128_G8_r1025_to_1061", small("ragged_decode_16", batch=1, span_size=64, window=64, top_k=16), [68000], 48,
+     "late_rows"),
+    ("d64_G4_two_seqs", small("ragged_decode_16", batch=2, head_dim=64, num_q_heads=16, num_kv_heads=4, span_size=32,
+                              window=32, top_k=8), [32000, 20000], 40, None),
+    ("d128_small_r", small("ragged_decode_16", batch=1, span_size=64, window=64, top_k=16), [64000], 0, "small_r"),
+    ("d128_all_scores_tie", small("ragged_decode_16", batch=1, span_size=64, window=64, top_k=16), [40000], 48,
+     "constant_keys"),
+    ("d128_k32", small("ragged_decode_16", batch=1, span_size=64, window=64, top_k=32), [64000], 48,
+     None),
+    ("d128_r1249", small("ragged_decode_16", batch=1, span_size=16, window=16, top_k=16), [20000], 48,
+     None),
+]
+
+
+@pytest.mark.parametrize("name,w,lengths,per_seq,edit", MANY_ROUTE_TOPK_CASES,
+                         ids=[c[0] for c in MANY_ROUTE_TOPK_CASES])
+def test_route_topk_spans_many_rows_equals_route_then_topk(name, w, lengths, per_seq, edit):
+    """Prefill-shaped calls (at least 256 row-heads per kv head): route_topk_spans equals
+    route_scores then topk_spans for every row and head, on two calls in a row.  Cases: r near
+    1000 and from 1025 to 1061, rows of two sequences interleaved, rows with r from 0 to 1000, a
+    cache whose keys are all equal (every score ties), k = 32, and r up to 1249."""
+    c = Case(w, lengths)
+    if edit == "constant_keys":
+        one = torch.full((w.head_dim,), 0.5, dtype=torch.bfloat16)
+        kh = c.host[0][0]
+        kh[:] = one.view(torch.int16).numpy().view(np.uint16)
+        c.K[0, :, :lengths[0]] = one.cuda()
+        c._problems.clear()
+    L = c.lengths
+    c.summarize(np.zeros(c.B, dtype=np.int64), L)
+    rng = np.random.default_rng(23)
+    if edit == "small_r":
+        S, W = w.span_size, w.window
+        want_r = [0, 1, 5, 16, 31, 32, 33, 40, 100, 255, 256, 300, 700, 999]
+        pos = np.array([min(int(L[0]) - 1, r * S + W - 1 + int(rng.integers(0, S))) for r in want_r for _ in range(24)])
+        seqs = np.zeros(len(pos), dtype=np.int64)
+    elif edit == "late_rows":  # r from 1025 to 1061
+        seqs = np.zeros(per_seq, dtype=np.int64)
+        pos = rng.integers(1025 * w.span_size + w.window - 1, int(L[0]), per_seq)
+    else:
+        seqs = np.repeat(np.arange(c.B), per_seq)
+        pos = np.concatenate([rng.integers(int(L[b]) // 2, int(L[b]), per_seq) for b in range(c.B)])
+        order = rng.permutation(len(seqs))  # sequences interleaved within tiles
+        seqs, pos = seqs[order], pos[order]
+    rows, _ = c.rows_for(seqs, pos)
+    n = len(seqs)
+    assert n * w.group >= 256  # the many-row regime
+    scores = torch.empty(n, w.num_q_heads, ra.score_stride(c.cfg, int(pos.max())), device="cuda")
+    sel_ref = torch.full((n, w.num_q_heads, w.top_k), -7, dtype=torch.int32, device="cuda")
+    ra.route_scores(c.cfg, rows, c.pipe.span_mean, scores)
+    ra.topk_spans(c.cfg, rows, scores, sel_ref)
+    ws = torch.zeros(ra.workspace_bytes(c.cfg, ra.RA_OP_ROUTE_TOPK, n, int(pos.max())), dtype=torch.uint8,
+                     device="cuda")
+    for rep in range(2):
+        sel = torch.full_like(sel_ref, -9)
+        ra.route_topk_spans(c.cfg, rows, c.pipe.span_mean, sel, ws)
+        torch.cuda.synchronize()
+        if not torch.equal(sel, sel_ref):
+            bad = (sel != sel_ref).any(dim=2).nonzero()[:4].tolist()
+            raise AssertionError("rep %d: %d row-heads differ, e.g. %s: %s vs %s" % (
+                rep, int((sel != sel_ref).any(dim=2).sum()), bad, sel[bad[0][0], bad[0][1]].tolist(),
+                sel_ref[bad[0][0], bad[0][1]].tolist()))
+    log("  %s: %d rows x %d heads, r up to %d" % (name, n, w.num_q_heads, c.cfg.num_routable(int(pos.max()))))
