@@ -13,24 +13,22 @@
 
 namespace ra {
 
+// The order-preserving 32-bit image of a score (the upper half of its key); valid images are >= 1.
+// s + 0 is +0 for both zeros (round to nearest), so -0 and +0 share one image and the lower index
+// wins; then negative scores flip every bit and the others set the sign bit (4 VALU instructions).
+__device__ __forceinline__ uint32_t score_image(float s) {
+    const uint32_t u = __float_as_uint(s + 0.f);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
 __device__ __forceinline__ uint64_t score_key(float s, int64_t j) {
-    uint32_t u = __float_as_uint(s);
-    if (s == 0.f) u = 0u;  // -0 and +0 are the same score: the lower index must win
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+    return ((uint64_t)score_image(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
 }
 
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
     return ((uint64_t)hi << 32) | lo;
-}
-
-// The order-preserving 32-bit image of a score (the upper half of its key); valid images are >= 1.
-__device__ __forceinline__ uint32_t score_image(float s) {
-    uint32_t u = __float_as_uint(s);
-    if (s == 0.f) u = 0u;  // -0 and +0 are the same score: the lower index must win
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // One wave selects among the spans j = lane + 64 i (i < PER_LANE) whose score images img[i] are
@@ -69,6 +67,7 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&img)[PER_LANE], int m
     for (int i = 0; i < PER_LANE; ++i) {
         const bool c = img[i] >= v;
         const uint64_t b = __ballot(c);
+        if (b == 0ull) continue;  // (most registers hold no candidate)
         const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
         if (c && pos < 64) cand[pos] = ((uint64_t)img[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * i));
         C += (int)__builtin_popcountll(b);
