@@ -518,20 +518,40 @@ __device__ __forceinline__ void max_sweep(const Stage<D> &st, const TileKeys &tk
 }
 
 // ---------------------------------------------------------------------- 8-bit cache tiles
-// Over an 8-bit cache (E4M3 codes + one fp32 scale per row) the tiles stage a chunk's codes (kChunk
-// rows of D bytes, K and V) and its rows' scales into LDS with direct loads, then convert the codes
-// exactly to bf16 (an E4M3 value has a 4-bit significand, which bf16 holds exactly) into the
-// swizzled K and V buffers that the MFMA operand reads use.  The scales stay apart: each key's
-// score is s_k (q . code_k); the P.V weights carry s_v (P' = bf16(P s_v)) while the row sums add
-// the unscaled bf16 weights, so the result is sum P s_v code_v / sum P.  One bf16 buffer pair:
-// a chunk is converted after everyone has finished the previous one (two barriers per chunk),
-// and the next chunk's codes load during the current chunk's products.
-
+// Over an 8-bit cache (E4M3 codes + one fp32 scale per row) the tiles stage each chunk's codes
+// (kChunk rows of D bytes, K and V) and its rows' scales into LDS with direct loads, double-
+// buffered like the bf16 rows (one barrier per chunk), and turn codes into MFMA operands as they
+// read them: a K operand is 8 codes of one row (one 8-byte read), a V operand 8 codes of one column
+// (one transposing read, ds_read_b64_tr_b8), each converted exactly to bf16 by four
+// v_cvt_scalef32_pk_bf16_fp8 (an E4M3 value has a 4-bit significand, which bf16 holds exactly).
+// The operand reads move half the LDS bytes of the bf16 tiles'.  The scales stay apart: each
+// key's score is s_k (q . code_k); the P.V weights carry s_v (P' = bf16(P s_v)) while the row sums
+// add the unrounded weights, so the result is sum P s_v code_v / sum P.
+//
+// LDS layout of a staged code chunk: rows of D bytes, unpadded (a direct load fills 1 KB = 1024 / D
+// rows per wave instruction), the 16-byte pieces of each row permuted by an XOR so that each
+// half-wave's operand reads (32 lanes x 8 bytes) fall on distinct banks.  Piece p of row r sits at
+// position p ^ f(r):
+//   D = 128 (two rows per 256-byte line of the 64 banks): K  f = (r >> 1 & 3) | (r >> 3 & 1) << 2
+//                                                         V  f = (r >> 1 & 3) | ((r >> 3 ^ r >> 4) & 1) << 2
+//   D = 64 (four rows per line):                          K  f = r >> 2 & 3
+//                                                         V  f = (r >> 2 & 1) | (r >> 4 & 1) << 1
+// (a K read of a half-wave takes rows 16 kt + 0..15 at one piece; a V read takes rows
+// 32 kk + 16 (j >> 2) + 4 lg + (j & 3), j < 8, lg < 2 or lg >= 2, at one piece.)
 template <int D>
+__device__ __forceinline__ int kswz8(int r) {
+    return D >= 128 ? (((r >> 1) & 3) | (((r >> 3) & 1) << 2)) : ((r >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int vswz8(int r) {
+    return D >= 128 ? (((r >> 1) & 3) | ((((r >> 3) ^ (r >> 4)) & 1) << 2)) : (((r >> 2) & 1) | (((r >> 4) & 1) << 1));
+}
+
+// The staged chunks of the 8-bit tiles: the codes of chunk x in kc[x & 1], vc[x & 1] (four distinct
+// arrays, as in Stage), its rows' scales in ks[x & 1], vs[x & 1].
 struct StageF8 {
-    uint16_t *kb, *vb;     // bf16 codes of the current chunk, swizzled as chunk_rows lays them out
-    uint8_t *kc, *vc;      // the codes of the chunk being loaded, row-major
-    float *ks[2], *vs[2];  // the rows' scales, by chunk parity
+    uint8_t *kc0, *kc1, *vc0, *vc1;
+    float *ks[2], *vs[2];
 };
 
 struct TileKeysF8 {
@@ -541,21 +561,22 @@ struct TileKeysF8 {
 };
 
 // Direct global -> LDS loads of chunk c's code rows (rows at or past n repeat row n - 1; masked
-// later) and of its rows' scales.  16 bytes per lane: 1024 / D rows per wave instruction.
-template <int D>
+// later) in the swizzled layout, and of the chunk's kChunk row scales.
+template <int D, bool IS_V>
 __device__ __forceinline__ void chunk_codes(const uint8_t *base, uint8_t *dst, const float *sbase, float *sdst, int c,
                                             int n, int wave, int lane) {
-    constexpr int ROWS = 1024 / D;
+    constexpr int ROWS = 1024 / D;  // rows per wave instruction
     constexpr int NI = kChunk / ROWS;
-    constexpr int LPR = D / 16;
+    constexpr int P = D / 16;       // 16-byte pieces per row
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, n * D, 0x00020000);
-    const int rl = lane / LPR, piece = lane % LPR;
+    const int rl = lane / P, phys = lane % P;
 #pragma unroll
     for (int ii = wave; ii < NI; ii += kMfmaWaves) {
-        int g = c + ii * ROWS + rl;
+        const int r = ii * ROWS + rl;  // the lane's row in the chunk; its LDS piece phys holds piece phys ^ f(r)
+        const int part = 16 * (phys ^ (IS_V ? vswz8<D>(r) : kswz8<D>(r)));
+        int g = c + r;
         g = g < n ? g : n - 1;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (RA_LDS void *)(dst + ii * ROWS * D), 16, g * D + piece * 16, 0, 0,
-                                                 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (RA_LDS void *)(dst + ii * ROWS * D), 16, g * D + part, 0, 0, 0);
     }
     if (wave == kMfmaWaves - 1) {  // the chunk's kChunk = 64 scales: one dword per lane
         const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc((void *)sbase, 0, n * 4, 0x00020000);
@@ -565,35 +586,75 @@ __device__ __forceinline__ void chunk_codes(const uint8_t *base, uint8_t *dst, c
     }
 }
 
-// The staged codes of a chunk -> bf16 in the swizzled buffers (K, and V when WITH_V): a thread
-// converts 32 codes of one row per step, two codes per v_cvt_scalef32_pk_bf16_fp8 with scale 1
-// (every E4M3 value is a bf16 value: the conversion is exact).
-template <int D, bool WITH_V>
-__device__ __forceinline__ void codes_to_bf16(const StageF8<D> &st, int tid) {
-    constexpr int SEG = D / 32;         // 32-code segments per row
-    constexpr int U = kChunk * SEG;     // segments per tensor
-#pragma unroll 1
-    for (int u = tid; u < (WITH_V ? 2 : 1) * U; u += kMfmaThreads) {  // (one segment in registers at a time)
-        const bool is_v = u >= U;
-        const int uu = is_v ? u - U : u;
-        const int r = uu / SEG, sgm = uu % SEG;
-        const uint8_t *src = (is_v ? st.vc : st.kc) + r * D + sgm * 32;
-        const uint4 a = *reinterpret_cast<const uint4 *>(src);
-        const uint4 b = *reinterpret_cast<const uint4 *>(src + 16);
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        uint32_t h[16];
+// 8 E4M3 codes (little-endian bytes of lo, then hi) -> 8 bf16, exactly.
+__device__ __forceinline__ bf16x8_t codes8_to_bf16(uint32_t lo, uint32_t hi) {
+    return __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false)),
+                                                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true)),
+                                                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false)),
+                                                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true))));
+}
+
+// Per-lane LDS offsets of the 8-bit operand reads.  K: lane (lg, lr) reads row 16 kt + lr, bytes
+// 32 ks + 8 lg .. + 7 (kof8[ks], plus 16 kt D); V: lane (lg, lr) names row
+// 32 kk + 16 (j >> 2) + 4 lg + (j & 3) with j = lr >> 1 and the half lr & 1 of column piece et, so
+// that the transposing read gives lane lr the codes of column 16 et + lr for the 8 keys of K-slots
+// 8 lg .. 8 lg + 7 (the P.V order): vbase + 32 kk D + 16 (et ^ vsw).
+template <int D>
+__device__ __forceinline__ void operand_offsets8(int lg, int lr, int (&kof8)[D / 32], int &vbase, int &vsw) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.f, false));
-            h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.f, true));
+    for (int ks = 0; ks < D / 32; ++ks) kof8[ks] = lr * D + 16 * ((2 * ks + (lg >> 1)) ^ kswz8<D>(lr)) + 8 * (lg & 1);
+    const int j = lr >> 1;
+    const int vrow = 16 * (j >> 2) + 4 * lg + (j & 3);
+    vbase = vrow * D + 8 * (lr & 1);
+    vsw = vswz8<D>(vrow);
+}
+
+// S^T = K Q^T for one chunk of codes and kQG query groups (the raw products q . code; the caller
+// applies the keys' scales).
+template <int D>
+__device__ __forceinline__ void qk_chunk_f8(const uint8_t *Kc, const int (&kof8)[D / 32],
+                                            const bf16x8_t (&qb)[kQG][D / 32], f32x4_t (&sc)[kQG][kChunk / 16]) {
+    constexpr int KS = D / 32, KT = kChunk / 16;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        bf16x8_t ka[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint2 raw = *reinterpret_cast<const uint2 *>(Kc + kof8[ks] + 16 * kt * D);
+            ka[ks] = codes8_to_bf16(raw.x, raw.y);
         }
-        uint16_t *dst = is_v ? st.vb : st.kb;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            const int piece = 4 * sgm + qq;  // 8-element piece of the row
-            const int pos = piece ^ (is_v ? vswz<D>(r) : kswz<D>(r));
-            *reinterpret_cast<uint4 *>(dst + r * D + 8 * pos) =
-                make_uint4(h[4 * qq], h[4 * qq + 1], h[4 * qq + 2], h[4 * qq + 3]);
+        for (int g = 0; g < kQG; ++g) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qb[g][ks], acc, 0, 0, 0);
+            sc[g][kt] = acc;
+        }
+    }
+}
+
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
+
+// O^T += V^T P^T over a chunk of codes (pk: the weights times the keys' value scales, as bf16
+// pairs in the K-slot order of pv_chunk); each V operand read feeds the kQG groups.
+template <int D>
+__device__ __forceinline__ void pv_chunk_f8(const uint8_t *Vc, int vbase, int vsw,
+                                            const uint32_t (&pk)[kQG][kChunk / 16][2], f32x4_t (&o)[kQG][D / 16]) {
+    constexpr int ET = D / 16, KT = kChunk / 16;
+#pragma unroll
+    for (int kk = 0; kk < KT / 2; ++kk) {
+        bf16x8_t pb[kQG];
+#pragma unroll
+        for (int g = 0; g < kQG; ++g)
+            pb[g] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[g][2 * kk][0], pk[g][2 * kk][1], pk[g][2 * kk + 1][0],
+                                                            pk[g][2 * kk + 1][1]));
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+            const v2i32_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (RA_LDS v2i32_t *)(Vc + vbase + 32 * kk * D + 16 * (et ^ vsw)));
+            const bf16x8_t va = codes8_to_bf16((uint32_t)w.x, (uint32_t)w.y);
+#pragma unroll
+            for (int g = 0; g < kQG; ++g) o[g][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[g], o[g][et], 0, 0, 0);
         }
     }
 }
@@ -651,71 +712,79 @@ __device__ __forceinline__ void scale_scores(f32x4_t (&sc)[kQG][kChunk / 16], co
     }
 }
 
-// fast_sweep over the 8-bit cache.  Chunk c: codes(c) landed -> barrier (everyone done with
-// chunk c - 1's bf16 buffers) -> convert -> barrier -> the loads of chunk c + 1's codes -> products.
+// fast_sweep over the 8-bit cache: the same pipeline as fast_sweep (chunk c's codes and scales in
+// buffers c & 1, chunk c + 1's loads issued behind the barrier of chunk c), operands from codes.
 template <int D, bool EXACT>
-__device__ __forceinline__ void fast_sweep_f8(const StageF8<D> &st, const TileKeysF8 &tk, bool preloaded,
-                                              const int (&qlim)[kQG], const int (&kof)[D / 32],
-                                              const int (&vof)[D / 64][4], const bf16x8_t (&qb)[kQG][D / 32],
-                                              float (&m)[kQG], float (&l)[kQG], f32x4_t (&o)[kQG][D / 16], int wave,
-                                              int lane, int lg, int tid, float scale_log2) {
+__device__ __forceinline__ void fast_sweep_f8(const StageF8 &st, const TileKeysF8 &tk, bool preloaded,
+                                              const int (&qlim)[kQG], const int (&kof8)[D / 32], int vbase, int vsw,
+                                              const bf16x8_t (&qb)[kQG][D / 32], float (&m)[kQG], float (&l)[kQG],
+                                              f32x4_t (&o)[kQG][D / 16], int wave, int lane, int lg,
+                                              float scale_log2) {
     constexpr int KT = kChunk / 16;
     const int C = (tk.n_keys + kChunk - 1) / kChunk;
     if (!preloaded) {
-        __syncthreads();  // everyone is done with the code buffers
-        chunk_codes<D>(tk.Ksp, st.kc, tk.ksp, st.ks[0], 0, tk.n_load, wave, lane);
-        chunk_codes<D>(tk.Vsp, st.vc, tk.vsp, st.vs[0], 0, tk.n_load, wave, lane);
+        __syncthreads();  // everyone is done with the buffers
+        chunk_codes<D, false>(tk.Ksp, st.kc0, tk.ksp, st.ks[0], 0, tk.n_load, wave, lane);
+        chunk_codes<D, true>(tk.Vsp, st.vc0, tk.vsp, st.vs[0], 0, tk.n_load, wave, lane);
     }
-    auto iter = [&](auto mask, auto track, int c) {
+    auto iter = [&](auto par, auto mask, auto track, int c) {
+        constexpr int P = decltype(par)::value;
         constexpr bool MASK = decltype(mask)::value, TRACK = decltype(track)::value;
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of chunk c landed
         __syncthreads();  // everyone's landed; everyone is done with chunk c - 1
-        codes_to_bf16<D, true>(st, tid);
-        __syncthreads();  // chunk c in bf16; the code buffers are free
         if (c + 1 < C) {
-            chunk_codes<D>(tk.Ksp, st.kc, tk.ksp, st.ks[(c + 1) & 1], (c + 1) * kChunk, tk.n_load, wave, lane);
-            chunk_codes<D>(tk.Vsp, st.vc, tk.vsp, st.vs[(c + 1) & 1], (c + 1) * kChunk, tk.n_load, wave, lane);
+            chunk_codes<D, false>(tk.Ksp, P ? st.kc0 : st.kc1, tk.ksp, st.ks[P ^ 1], (c + 1) * kChunk, tk.n_load, wave,
+                                  lane);
+            chunk_codes<D, true>(tk.Vsp, P ? st.vc0 : st.vc1, tk.vsp, st.vs[P ^ 1], (c + 1) * kChunk, tk.n_load, wave,
+                                 lane);
         }
         f32x4_t sc[kQG][KT];
-        qk_chunk<D>(st.kb, kof, qb, sc);
-        scale_scores(sc, st.ks[c & 1], lg);
+        qk_chunk_f8<D>(P ? st.kc1 : st.kc0, kof8, qb, sc);
+        scale_scores(sc, st.ks[P], lg);
         uint32_t pkv[kQG][KT][2];
 #pragma unroll
         for (int g = 0; g < kQG; ++g) {
             int lim = qlim[g] - c * kChunk;
             lim = lim < 0 ? 0 : (lim > kChunk ? kChunk : lim);
-            softmax_chunk_f8<MASK, TRACK, EXACT>(sc[g], lim, lg, scale_log2, m[g], l[g], st.vs[c & 1], pkv[g]);
+            softmax_chunk_f8<MASK, TRACK, EXACT>(sc[g], lim, lg, scale_log2, m[g], l[g], st.vs[P], pkv[g]);
         }
-        pv_chunk<D>(st.vb, vof, pkv, o);
+        pv_chunk_f8<D>(P ? st.vc1 : st.vc0, vbase, vsw, pkv, o);
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
     using BF = std::integral_constant<bool, false>;
     using BT = std::integral_constant<bool, true>;
-    if (kChunk <= tk.full_end) iter(BF{}, BT{}, 0);
-    else iter(BT{}, BT{}, 0);
-    for (int c = 1; c < C; ++c) {
-        if ((c + 1) * kChunk <= tk.full_end) iter(BF{}, BF{}, c);
-        else iter(BT{}, BF{}, c);
+    if (kChunk <= tk.full_end) iter(I0{}, BF{}, BT{}, 0);
+    else iter(I0{}, BT{}, BT{}, 0);
+    for (int c = 1; c < C; c += 2) {
+        if ((c + 1) * kChunk <= tk.full_end) iter(I1{}, BF{}, BF{}, c);
+        else iter(I1{}, BT{}, BF{}, c);
+        if (c + 1 >= C) break;
+        if ((c + 2) * kChunk <= tk.full_end) iter(I0{}, BF{}, BF{}, c + 1);
+        else iter(I0{}, BT{}, BF{}, c + 1);
     }
 }
 
-// max_sweep over the 8-bit cache: every query's largest scaled score (times scale_log2).
+// max_sweep over the 8-bit cache: every query's largest scaled score (times scale_log2).  K codes
+// and scales only, one chunk ahead.
 template <int D>
-__device__ __forceinline__ void max_sweep_f8(const StageF8<D> &st, const TileKeysF8 &tk, const int (&qlim)[kQG],
-                                             const int (&kof)[D / 32], const bf16x8_t (&qb)[kQG][D / 32],
-                                             float (&mx)[kQG], int wave, int lane, int lg, int tid, float scale_log2) {
+__device__ __forceinline__ void max_sweep_f8(const StageF8 &st, const TileKeysF8 &tk, const int (&qlim)[kQG],
+                                             const int (&kof8)[D / 32], const bf16x8_t (&qb)[kQG][D / 32],
+                                             float (&mx)[kQG], int wave, int lane, int lg, float scale_log2) {
     constexpr float NEG = -__builtin_huge_valf();
     const int C = (tk.n_keys + kChunk - 1) / kChunk;
     __syncthreads();  // everyone is done with the buffers
-    chunk_codes<D>(tk.Ksp, st.kc, tk.ksp, st.ks[0], 0, tk.n_load, wave, lane);
+    chunk_codes<D, false>(tk.Ksp, st.kc0, tk.ksp, st.ks[0], 0, tk.n_load, wave, lane);
     for (int c = 0; c < C; ++c) {
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        codes_to_bf16<D, false>(st, tid);
-        __syncthreads();
-        if (c + 1 < C) chunk_codes<D>(tk.Ksp, st.kc, tk.ksp, st.ks[(c + 1) & 1], (c + 1) * kChunk, tk.n_load, wave, lane);
+        const bool odd = c & 1;  // (selects, not a runtime index into st.ks: that would live in memory)
+        if (c + 1 < C)
+            chunk_codes<D, false>(tk.Ksp, odd ? st.kc0 : st.kc1, tk.ksp, odd ? st.ks[0] : st.ks[1], (c + 1) * kChunk,
+                                  tk.n_load, wave, lane);
         f32x4_t sc[kQG][kChunk / 16];
-        qk_chunk<D>(st.kb, kof, qb, sc);
-        scale_scores(sc, st.ks[c & 1], lg);
+        qk_chunk_f8<D>(odd ? st.kc1 : st.kc0, kof8, qb, sc);
+        scale_scores(sc, odd ? st.ks[1] : st.ks[0], lg);
 #pragma unroll
         for (int g = 0; g < kQG; ++g) {
             int lim = qlim[g] - c * kChunk;
@@ -767,20 +836,21 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     constexpr int KS = D / 32;   // k-steps of the QK product
     constexpr int ET = D / 16;   // 16-wide e tiles of the PV product
     constexpr float NEG = -__builtin_huge_valf();
-    // staged chunks: bf16 K and V buffers 0 and 1 (kChunk rows of D bf16 each); the 8-bit tiles
-    // use one bf16 pair and stage the codes and scales of the chunk being loaded beside it
-    __shared__ __align__(16) uint16_t kb0[kChunk * D], vb0[kChunk * D];
+    // staged chunks, buffers 0 and 1 of kChunk rows: bf16 K and V (D bf16 per row), or for the
+    // 8-bit tiles K and V codes (D bytes per row) with the rows' scales
+    __shared__ __align__(16) uint16_t kb0[F8 ? 8 : kChunk * D], vb0[F8 ? 8 : kChunk * D];
     __shared__ __align__(16) uint16_t kb1[F8 ? 8 : kChunk * D], vb1[F8 ? 8 : kChunk * D];
-    __shared__ __align__(16) uint8_t kc8[F8 ? kChunk * D : 16], vc8[F8 ? kChunk * D : 16];
+    __shared__ __align__(16) uint8_t kc0[F8 ? kChunk * D : 16], vc0[F8 ? kChunk * D : 16];
+    __shared__ __align__(16) uint8_t kc1[F8 ? kChunk * D : 16], vc1[F8 ? kChunk * D : 16];
     __shared__ __align__(16) float ks8[F8 ? 2 * kChunk : 4], vs8[F8 ? 2 * kChunk : 4];
     __shared__ int redo_s[kMfmaWaves];
     __shared__ unsigned long long wmax_s[kMfmaWaves], wmin_s[kMfmaWaves];
     const Stage<D> st{kb0, kb1, vb0, vb1};
-    StageF8<D> st8;  // (assigned field by field: a braced constant initializer of LDS addresses
-    st8.kb = kb0;    //  would become a static one, which the device compiler rejects)
-    st8.vb = vb0;
-    st8.kc = kc8;
-    st8.vc = vc8;
+    StageF8 st8;    // (assigned field by field: a braced constant initializer of LDS addresses
+    st8.kc0 = kc0;  //  would become a static one, which the device compiler rejects)
+    st8.kc1 = kc1;
+    st8.vc0 = vc0;
+    st8.vc1 = vc1;
     st8.ks[0] = ks8;
     st8.ks[1] = ks8 + kChunk;
     st8.vs[0] = vs8;
@@ -848,8 +918,8 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
     // up to the span's end (issued after them: the compiler waits for everything before using a
     // load's register while LDS loads are outstanding)
     if constexpr (F8) {
-        chunk_codes<D>(Ksp8, st8.kc, ksp, st8.ks[0], 0, n_span, wave, lane);
-        chunk_codes<D>(Vsp8, st8.vc, vsp, st8.vs[0], 0, n_span, wave, lane);
+        chunk_codes<D, false>(Ksp8, st8.kc0, ksp, st8.ks[0], 0, n_span, wave, lane);
+        chunk_codes<D, true>(Vsp8, st8.vc0, vsp, st8.vs[0], 0, n_span, wave, lane);
     } else {
         chunk_rows<D, false>(Ksp, st.kb0, 0, n_span, wave, lane);
         chunk_rows<D, true>(Vsp, st.vb0, 0, n_span, wave, lane);
@@ -888,7 +958,9 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
         qlim[g] = tq[g] < 0 ? 0 : (int)(v < n_keys ? v : n_keys);
     }
     int kof[KS], vof[D / 64][4];
-    operand_offsets<D>(lg, lr, kof, vof);
+    int kof8[KS], vbase8 = 0, vsw8 = 0;
+    if constexpr (F8) operand_offsets8<D>(lg, lr, kof8, vbase8, vsw8);
+    else operand_offsets<D>(lg, lr, kof, vof);
 
     float m[kQG], l[kQG];
     f32x4_t o[kQG][ET];
@@ -905,7 +977,7 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int g = 0; g < kQG; ++g) unset[g] = NEG;
     reset(unset);
-    if constexpr (F8) fast_sweep_f8<D, false>(st8, tk8, true, qlim, kof, vof, qb, m, l, o, wave, lane, lg, tid, scale_log2);
+    if constexpr (F8) fast_sweep_f8<D, false>(st8, tk8, true, qlim, kof8, vbase8, vsw8, qb, m, l, o, wave, lane, lg, scale_log2);
     else fast_sweep<D, false>(st, tk, true, qlim, kof, vof, qb, m, l, o, wave, lane, lg, scale_log2);
 
     // records: header (m, l, s, 0), then o / (l s) as fp16 per valid row, s = 2^-k with k chosen
@@ -971,9 +1043,9 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
 #pragma unroll
         for (int g = 0; g < kQG; ++g) mx[g] = NEG;
         if constexpr (F8) {
-            max_sweep_f8<D>(st8, tk8, qlim, kof, qb, mx, wave, lane, lg, tid, scale_log2);
+            max_sweep_f8<D>(st8, tk8, qlim, kof8, qb, mx, wave, lane, lg, scale_log2);
             reset(mx);
-            fast_sweep_f8<D, true>(st8, tk8, false, qlim, kof, vof, qb, m, l, o, wave, lane, lg, tid, scale_log2);
+            fast_sweep_f8<D, true>(st8, tk8, false, qlim, kof8, vbase8, vsw8, qb, m, l, o, wave, lane, lg, scale_log2);
         } else {
             max_sweep<D>(st, tk, qlim, kof, qb, mx, wave, lane, lg, scale_log2);
             reset(mx);
