@@ -12,6 +12,8 @@
 // an entry whose row sum then overflows the fast range gets a second pass with its exact
 // maximum (decided per entry).  Tiles of one span are consecutive in the tile list and are
 // spread over the 8 XCDs in contiguous ranges, so the blocks that reread a span's keys share an L2.
+// Over an 8-bit cache the same pipeline stages E4M3 codes and turns them into bf16 operands as it
+// reads them (the 8-bit cache tiles, below).
 //
 // tile_valu: one wave per entry, keys streamed in chunks of KPW rows with an online softmax
 // (fp32 inputs).  The span's rows are shared by the tile's entries through the caches.
