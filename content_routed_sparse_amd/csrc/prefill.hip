@@ -17,7 +17,8 @@
 //   counts[n_exp+1], offsets[n_exp+1], tile_off[n_exp+1]   int32
 //   local[n_ent], list[n_ent]                               int32   (n_ent = n_rowheads * NE)
 //   list_t[n_ent]                                           int64   (position of the entry's row)
-//   tiles[max_tiles]                                        int4    (expert, first entry, entries)
+//   tiles[max_tiles]                                        int4    (expert, first entry, entries),
+//                                                                   tile t at slot 8 (t mod Q) + t / Q
 //   records[n_ent]                                          prefill_record_words(d, bf16) x 4 bytes
 #include "common.h"
 #include "kernels.h"
@@ -41,7 +42,9 @@ PrefillLayout prefill_layout(const RowArgs &a) {
     L.n_exp = (int64_t)a.B * a.Hkv * L.span_slots;
     L.n_ent = a.n_rows * a.Hq * NE;
     const int MT = prefill_tile_rows(a);
-    L.max_tiles = ceil_div(L.n_ent, MT) + (L.n_exp < L.n_ent ? L.n_exp : L.n_ent);
+    // an upper bound on the tile count (every bucket's last tile may be partial), rounded up to a
+    // multiple of 8 so that the XCD-ordered descriptor slots of any tile count fit
+    L.max_tiles = 8 * ceil_div(ceil_div(L.n_ent, MT) + (L.n_exp < L.n_ent ? L.n_exp : L.n_ent), 8);
     size_t o = 0;
     L.off_counts = o;   o = align256(o + (L.n_exp + 1) * 4);
     L.off_offsets = o;  o = align256(o + (L.n_exp + 1) * 4);
@@ -248,8 +251,11 @@ __global__ void tiles_kernel(const int32_t *__restrict__ counts, const int32_t *
     const int32_t c = counts[x];
     const int32_t base = tile_off[x];
     const int32_t first = offsets[x];
-    for (int32_t i = 0; i * MT < c; ++i)
-        tiles[base + i] = make_int4((int32_t)x, first + i * MT, c - i * MT < MT ? c - i * MT : MT, 0);
+    const int32_t Q = (tile_off[n_exp] + 7) / 8;  // tiles per XCD
+    for (int32_t i = 0; i * MT < c; ++i) {
+        const int32_t t = base + i;
+        tiles[tile_slot(t, Q)] = make_int4((int32_t)x, first + i * MT, c - i * MT < MT ? c - i * MT : MT, 0);
+    }
 }
 
 

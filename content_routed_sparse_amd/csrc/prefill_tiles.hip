@@ -63,9 +63,8 @@ __global__ void __launch_bounds__(256) tile_valu(const T *__restrict__ q, const 
                                                  int NE, int S, int64_t cap, float scale_log2) {
     using L = WaveLayout<T, D>;
     constexpr int EPL = L::EPL, LPR = L::LPR, RPI = L::RPI, KPW = L::KPW, STEPS = L::STEPS;
-    const int64_t tile = blockIdx.x;
-    if (tile >= tile_off[n_exp]) return;
-    const int4 tl = tiles[tile];
+    if (slot_tile(blockIdx.x, tile_off[n_exp]) < 0) return;
+    const int4 tl = tiles[blockIdx.x];
     const int64_t expert = tl.x;
     const int n = tl.z;
     const int64_t j = expert % span_slots;
@@ -163,8 +162,8 @@ constexpr int kMfmaThreads = kMfmaWaves * 64;
 constexpr int kWavesPerEU = kQG == 1 ? 4 : 2;   // register budget: 128 or 256 per lane
 static_assert(kMfmaTile <= kMfmaThreads, "one thread per entry in the tile reductions");
 
-// XCD-aware order: the hardware hands block b to XCD b % 8; give XCD x a contiguous range of
-// the tile list (tiles of one span are consecutive) so that they share its L2.
+// XCD-aware order for a grid of exactly `grid` tiles (the dense tiles): the hardware hands block b
+// to XCD b % 8; give XCD x a contiguous range of the tile list so that its tiles share an L2.
 // Bijective on [0, grid): XCD x owns the range starting at x * (grid / 8) + min(x, grid % 8).
 __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t grid) {
     const int64_t q = grid / 8, rem = grid % 8, x = b % 8, i = b / 8;
@@ -834,7 +833,7 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
                                                           const int4 *__restrict__ tiles,
                                                           float *__restrict__ records, int64_t n_exp,
                                                           int64_t span_slots, int NE, int S, int64_t cap,
-                                                          float scale_log2, int64_t n_blocks) {
+                                                          float scale_log2) {
     constexpr int KS = D / 32;   // k-steps of the QK product
     constexpr int ET = D / 16;   // 16-wide e tiles of the PV product
     constexpr float NEG = -__builtin_huge_valf();
@@ -860,15 +859,14 @@ __global__ void __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_
 
     // all kernel arguments in one round trip (otherwise some are fetched only where first used)
     asm volatile("" ::"s"(q), "s"(K), "s"(V), "s"(tile_off), "s"(list), "s"(list_t), "s"(tiles), "s"(records),
-                 "s"(n_exp), "s"(span_slots), "s"(NE), "s"(S), "s"(cap), "s"(scale_log2), "s"(n_blocks));
+                 "s"(n_exp), "s"(span_slots), "s"(NE), "s"(S), "s"(cap), "s"(scale_log2));
     if constexpr (F8) asm volatile("" ::"s"(ks), "s"(vs));
-    const int64_t tile = xcd_tile(blockIdx.x, n_blocks);
-    // the tile count and this tile's descriptor in one round trip (a descriptor past the count is
-    // stale but in bounds: max_tiles of them are allocated)
+    // the tile count and this block's descriptor slot in one round trip (a slot that holds no
+    // tile is stale but in bounds: the grid has max_tiles blocks, one per slot)
     const int64_t total = tile_off[n_exp];
-    const int4 tl = tiles[tile];
+    const int4 tl = tiles[blockIdx.x];
     asm volatile("" ::"s"(total), "s"(tl.x), "s"(tl.y), "s"(tl.z));
-    if (tile >= total) return;
+    if (slot_tile(blockIdx.x, total) < 0) return;
     const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: scalar chunk-load offsets)
     const int64_t expert = tl.x;
@@ -1063,7 +1061,7 @@ hipError_t mfma_launch(const TileArgs &t, hipStream_t st) {
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     hipLaunchKernelGGL((tile_mfma<D, F8>), dim3((unsigned)t.max_tiles), dim3(kMfmaThreads), 0, st,
                        (const uint16_t *)a.q, t.K, t.V, t.ks, t.vs, t.tile_off, t.list, t.list_t, t.tiles, t.records,
-                       t.n_exp, t.span_slots, t.NE, a.S, a.cap, scale_log2, t.max_tiles);
+                       t.n_exp, t.span_slots, t.NE, a.S, a.cap, scale_log2);
     return hipGetLastError();
 }
 
