@@ -14,6 +14,7 @@
 //    row, 8 query heads per pass, butterfly reduction over the lanes of a row.
 #include "common.h"
 #include "kernels.h"
+#include "route_body.h"
 #include "topk_body.h"
 #include "wave_ops.h"
 
@@ -22,101 +23,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// Few rows (decode) or fp32 inputs: lanes split each fp32 summary row (8 elements per lane, LPR
-// lanes per row, coalesced 32-byte loads); a wave takes 16 spans, each lane forms partial dot
-// products for 8 query heads at once, and a butterfly reduce-scatter over the LPR lanes leaves
-// KEEP finished scores per lane.  The same steps serve route_valu (scores to memory) and
-// route_topk (scores to LDS, then the selection), so both give the same fp32 scores.
-template <typename T, int D>
-struct ValuScore {
-    static constexpr int LPR = D / 8, RPI = 64 / LPR, STEPS = 16 / RPI, N = STEPS * 8, KEEP = N / LPR;
-    static constexpr int QV = sizeof(T) == 2 ? 1 : 2;  // 16-byte pieces per head slice of 8 elements
-
-    // q slices of query heads hc..hc+7 of kv head g (a head past G loads head G-1; score() zeroes it)
-    __device__ static __forceinline__ void load_q(uint4 (&qraw)[8][QV], const T *q, int64_t row, int Hq, int g,
-                                                  int G, int hc, int c) {
-#pragma unroll
-        for (int h = 0; h < 8; ++h) {
-            const int hh = hc + h < G ? hc + h : G - 1;
-            const uint4 *qp = reinterpret_cast<const uint4 *>(q + (row * Hq + g * G + hh) * D + c * 8);
-#pragma unroll
-            for (int v = 0; v < QV; ++v) qraw[h][v] = qp[v];
-        }
-    }
-
-    // kappa of the summaries of spans jw + s RPI + rr (clamped to r - 1): every load of the wave
-    // issued before any use and pinned there
-    __device__ static __forceinline__ void load_means(float (&mv)[STEPS][8], const float *mbase, int64_t jw,
-                                                      int64_t r, int c, int rr) {
-        float4 mraw[STEPS][2];
-#pragma unroll
-        for (int s = 0; s < STEPS; ++s) {
-            int64_t n = jw + s * RPI + rr;
-            n = n < r ? n : r - 1;
-            mraw[s][0] = *reinterpret_cast<const float4 *>(mbase + n * D + c * 8);
-            mraw[s][1] = *reinterpret_cast<const float4 *>(mbase + n * D + c * 8 + 4);
-        }
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int s = 0; s < STEPS; ++s)
-#pragma unroll
-            for (int v = 0; v < 2; ++v)
-                asm volatile("" : "+v"(mraw[s][v].x), "+v"(mraw[s][v].y), "+v"(mraw[s][v].z), "+v"(mraw[s][v].w));
-#pragma unroll
-        for (int s = 0; s < STEPS; ++s) {
-            const float f[8] = {mraw[s][0].x, mraw[s][0].y, mraw[s][0].z, mraw[s][0].w,
-                                mraw[s][1].x, mraw[s][1].y, mraw[s][1].z, mraw[s][1].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) mv[s][e] = sizeof(T) == 2 ? round_bf16(f[e]) : f[e];
-        }
-    }
-
-    // scores of spans jw.. (16) for query heads hc..hc+7: store(head, span, score) for every
-    // finished score with span < r and head < G
-    template <typename F>
-    __device__ static __forceinline__ void score(const uint4 (&qraw)[8][QV], const float (&mv)[STEPS][8], int hc,
-                                                 int G, int lane, int64_t jw, int64_t r, F &&store) {
-        const int c = lane % LPR, rr = lane / LPR;
-        float acc[N];
-#pragma unroll
-        for (int h = 0; h < 8; ++h) {
-            float qf[8];
-            if constexpr (sizeof(T) == 2) {
-                const uint32_t w[4] = {qraw[h][0].x, qraw[h][0].y, qraw[h][0].z, qraw[h][0].w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    qf[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
-                    qf[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-                }
-            } else {
-                const uint32_t w[8] = {qraw[h][0].x, qraw[h][0].y, qraw[h][0].z, qraw[h][0].w,
-                                       qraw[h][1].x, qraw[h][1].y, qraw[h][1].z, qraw[h][1].w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) qf[i] = __uint_as_float(w[i]);
-            }
-            if (hc + h >= G) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qf[e] = 0.f;
-            }
-#pragma unroll
-            for (int s = 0; s < STEPS; ++s) {
-                float d = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) d = fmaf(qf[e], mv[s][e], d);
-                acc[s * 8 + h] = d;
-            }
-        }
-        ReduceScatter<N, ilog2(LPR), LPR / 2>::run(acc, lane);
-#pragma unroll
-        for (int i = 0; i < KEEP; ++i) {
-            const int v = c * KEEP + i;
-            const int s = v / 8, h = v % 8;
-            const int64_t n = jw + s * RPI + rr;
-            if (n < r && hc + h < G) store(hc + h, n, acc[i]);
-        }
-    }
-};
 
 // A block scores 64 spans of one (row, kv head) for all the kv head's query heads (4 waves of 16).
 template <typename T, int D>
@@ -156,95 +62,29 @@ __global__ void __launch_bounds__(256) route_valu(const T *__restrict__ q, const
     }
 }
 
-// Decode routing and selection in one launch.  A block of kRtWaves waves scores 16 spans per wave
-// of one (row, kv head) for all the kv head's query heads (ValuScore: the scores route_valu
-// writes, bit for bit).  The scores go to the workspace with system-coherent stores (they reach
-// memory, past every XCD's L2); each block then counts itself in its (row, kv head) counter, and
-// the block that arrives last -- all the others' scores are in memory by then -- reads the
-// scores back with system-coherent loads and selects for every query head of the kv head
-// (wave_topk: the selection topk_spans makes).  The last block resets the counter, so counters
-// that start at zero are at zero again after every call.
-constexpr int kRtWaves = 8;  // waves per block: 16 spans each; in the last block, one query head each
+// Decode routing and selection in one launch: one block of route_select_block per (row, kv head,
+// span block of 16 kRtWaves spans); each block selects its own candidates, the last block of each
+// (row, kv head) to finish selects among them.
+constexpr int kRtWaves = 8;  // waves per block: 16 spans each; in the selections, one query head each
+constexpr int kRtSpans = 16 * kRtWaves;
 
 template <typename T, int D, int PER_LANE>
 __global__ void __launch_bounds__(kRtWaves * 64) route_topk(const T *__restrict__ q,
                                                             const int32_t *__restrict__ row_seq,
                                                             const int64_t *__restrict__ row_pos,
-                                                            const float *__restrict__ mean, float *__restrict__ scores,
-                                                            int64_t stride, int32_t *__restrict__ sel,
-                                                            uint32_t *__restrict__ counters, int Hq, int Hkv, int G,
-                                                            int S, int k, int W, int B, int64_t max_spans,
-                                                            int64_t max_pos) {
-    using VS = ValuScore<T, D>;
-    constexpr int HPW = 4;  // query heads per wave whose scores are fetched together (G <= 32)
+                                                            const float *__restrict__ mean, uint64_t *cands,
+                                                            int32_t *__restrict__ sel, uint32_t *__restrict__ counters,
+                                                            int Hq, int Hkv, int G, int S, int k, int W, int B,
+                                                            int64_t max_spans, int64_t max_pos) {
     __shared__ uint64_t cand[kRtWaves][64];
+    __shared__ __align__(16) float stile[32 * kRtSpans];
+    __shared__ int32_t lsel[kRtWaves][64];
     __shared__ int is_last;
-    asm volatile("" ::"s"(q), "s"(row_seq), "s"(row_pos), "s"(mean), "s"(scores), "s"(stride), "s"(sel),
-                 "s"(counters), "s"(Hq), "s"(Hkv), "s"(G), "s"(S), "s"(k), "s"(W), "s"(B), "s"(max_spans),
-                 "s"(max_pos));
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int c = lane % VS::LPR, rr = lane / VS::LPR;
-    const int rg = blockIdx.x;
-    const int64_t row = rg / Hkv;
-    const int g = rg % Hkv;
-    uint4 qraw[8][VS::QV];
-    const int64_t t_raw = row_pos[row];
-    const int seq_raw = row_seq[row];
-    VS::load_q(qraw, q, row, Hq, g, G, 0, c);
-    asm volatile("" ::"s"(t_raw), "s"(seq_raw));
-    const int64_t t = t_raw < 0 ? 0 : (t_raw > max_pos ? max_pos : t_raw);
-    const int seq = seq_raw < 0 ? 0 : (seq_raw >= B ? B - 1 : seq_raw);
-    const int64_t r = num_routable(t, S, W);
-    const int64_t jw = (int64_t)blockIdx.y * (16 * kRtWaves) + wave * 16;  // this wave's first span
-    float *srow = scores + (row * Hq + g * G) * stride;
-    if (jw < r) {
-        const float *mbase = mean + ((int64_t)seq * Hkv + g) * max_spans * D;
-        float mv[VS::STEPS][8];
-        VS::load_means(mv, mbase, jw, r, c, rr);
-        for (int hc = 0; hc < G; hc += 8) {
-            if (hc > 0) VS::load_q(qraw, q, row, Hq, g, G, hc, c);
-            VS::score(qraw, mv, hc, G, lane, jw, r, [&](int h, int64_t n, float v) {
-                __hip_atomic_store(srow + h * stride + n, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            });
-        }
-    }
-    // this block's scores have reached memory (stores are counted by vmcnt) before it counts itself
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t before = __hip_atomic_fetch_add(counters + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = before == gridDim.y - 1;
-        if (is_last) __hip_atomic_store(counters + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!is_last) return;
-    const int m = (int)(r < k ? r : k);
-    // wave w selects for query heads w, w + kRtWaves, ...: the scores of up to HPW of them are
-    // fetched in one round trip (a row with r = 0 reads nothing; indices past r read span 0)
-    for (int h0 = wave; h0 < G; h0 += kRtWaves * HPW) {
-        float sv[HPW][PER_LANE];
-#pragma unroll
-        for (int x = 0; x < HPW; ++x) {
-            const int h = h0 + x * kRtWaves;
-#pragma unroll
-            for (int i = 0; i < PER_LANE; ++i) {
-                const int64_t j = lane + 64 * i;
-                sv[x][i] = (r > 0 && h < G) ? __hip_atomic_load(srow + h * stride + (j < r ? j : 0), __ATOMIC_RELAXED,
-                                                               __HIP_MEMORY_SCOPE_SYSTEM)
-                                            : 0.f;
-            }
-        }
-        const int rl = (int)(r < 64 * PER_LANE ? r : 64 * PER_LANE);
-#pragma unroll
-        for (int x = 0; x < HPW; ++x) {
-            const int h = h0 + x * kRtWaves;
-            if (h >= G) break;
-            uint32_t img[PER_LANE];
-#pragma unroll
-            for (int i = 0; i < PER_LANE; ++i) img[i] = lane + 64 * i < rl ? score_image(sv[x][i]) : 0u;
-            wave_topk<PER_LANE>(img, m, k, lane, cand[wave], sel + (row * Hq + g * G + h) * k);
-        }
-    }
+    asm volatile("" ::"s"(q), "s"(row_seq), "s"(row_pos), "s"(mean), "s"(cands), "s"(sel), "s"(counters), "s"(Hq),
+                 "s"(Hkv), "s"(G), "s"(S), "s"(k), "s"(W), "s"(B), "s"(max_spans), "s"(max_pos));
+    route_select_block<T, D, PER_LANE, kRtWaves>(q, row_seq, row_pos, mean, cands, sel, counters, Hq, Hkv, G, S, k, W,
+                                                  B, max_spans, max_pos, (int)blockIdx.x, (int)blockIdx.y,
+                                                  (int)gridDim.y, cand, stile, lsel, &is_last);
 }
 
 constexpr int kRouteGroups = 2;                // 16-row MFMA groups per wave (measured: 2 beats 1, 4 and 8)
@@ -441,25 +281,30 @@ hipError_t route_mfma_launch(const RowArgs &a, const float *mean, float *scores,
     return hipGetLastError();
 }
 
+// span blocks of the one-launch routing (at least one per (row, kv head): with no routable span it
+// writes the -1 padding)
+int64_t route_topk_blocks(int64_t rmax) { return rmax > 0 ? ceil_div(rmax, kRtSpans) : 1; }
+
 template <typename T, int D, int PL>
-hipError_t route_topk_launch(const RowArgs &a, const float *mean, float *scores, int64_t stride, int32_t *sel,
+hipError_t route_topk_launch(const RowArgs &a, const float *mean, uint64_t *cands, int32_t *sel,
                              uint32_t *counters, int64_t rmax, hipStream_t st) {
-    // (at least one block per (row, kv head): with no routable span it writes the -1 padding)
-    dim3 grid((unsigned)(a.n_rows * a.Hkv), (unsigned)(rmax > 0 ? ceil_div(rmax, 16 * kRtWaves) : 1));
+    dim3 grid((unsigned)(a.n_rows * a.Hkv), (unsigned)route_topk_blocks(rmax));
     hipLaunchKernelGGL((route_topk<T, D, PL>), grid, dim3(kRtWaves * 64), 0, st, (const T *)a.q, a.row_seq, a.row_pos, mean,
-                       scores, stride, sel, counters, a.Hq, a.Hkv, a.G, a.S, a.k, a.W, a.B, a.max_spans, a.max_pos);
+                       cands, sel, counters, a.Hq, a.Hkv, a.G, a.S, a.k, a.W, a.B, a.max_spans, a.max_pos);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t route_topk_dispatch(const RowArgs &a, const float *mean, float *scores, int64_t stride, int32_t *sel,
+hipError_t route_topk_dispatch(const RowArgs &a, const float *mean, uint64_t *cands, int32_t *sel,
                                uint32_t *counters, int64_t rmax, hipStream_t st) {
-    if (rmax <= 64 * 2) return route_topk_launch<T, D, 2>(a, mean, scores, stride, sel, counters, rmax, st);
-    if (rmax <= 64 * 8) return route_topk_launch<T, D, 8>(a, mean, scores, stride, sel, counters, rmax, st);
-    return route_topk_launch<T, D, 17>(a, mean, scores, stride, sel, counters, rmax, st);
+    if (rmax <= 64 * 2) return route_topk_launch<T, D, 2>(a, mean, cands, sel, counters, rmax, st);
+    if (rmax <= 64 * 8) return route_topk_launch<T, D, 8>(a, mean, cands, sel, counters, rmax, st);
+    return route_topk_launch<T, D, 17>(a, mean, cands, sel, counters, rmax, st);
 }
 
-// Workspace of route_topk_spans: n_rows x Hkv counters (256-byte aligned), then the scores.
+// Workspace of route_topk_spans: n_rows x Hkv counters (256-byte aligned), then room for either the
+// one-launch path's candidates (n_rows x Hq x blocks x k words of 8 bytes) or the two launches'
+// score rows.
 int64_t route_topk_stride(const RowArgs &a) {
     const int64_t r = num_routable(a.max_pos, a.S, a.W);
     return r > 0 ? ceil_div(r, 32) * 32 : 32;
@@ -469,7 +314,9 @@ size_t route_topk_counter_bytes(const RowArgs &a) { return (size_t)ceil_div(a.n_
 }  // namespace
 
 size_t route_topk_workspace_bytes(const RowArgs &a) {
-    return route_topk_counter_bytes(a) + (size_t)(a.n_rows * a.Hq * route_topk_stride(a)) * 4;
+    const int64_t scores = a.n_rows * a.Hq * route_topk_stride(a) * 4;
+    const int64_t cands = a.n_rows * a.Hq * route_topk_blocks(num_routable(a.max_pos, a.S, a.W)) * a.k * 8;
+    return route_topk_counter_bytes(a) + (size_t)(scores > cands ? scores : cands);
 }
 
 // Routing and selection in one call; the path depends on the shape, the result does not (both
@@ -483,14 +330,15 @@ hipError_t launch_route_topk(const RowArgs &a, const float *mean, int32_t *sel, 
     if (a.n_rows == 0) return hipSuccess;
     uint32_t *counters = (uint32_t *)ws;
     float *scores = (float *)((char *)ws + route_topk_counter_bytes(a));
+    uint64_t *cands = (uint64_t *)scores;
     const int64_t stride = route_topk_stride(a);
     const bool many = a.dtype == RA_BF16 && a.n_rows * a.G >= 256;
     if (!many && rmax <= 64 * 17) {
         if (a.dtype == RA_BF16)
-            return a.d == 64 ? route_topk_dispatch<uint16_t, 64>(a, mean, scores, stride, sel, counters, rmax, st)
-                             : route_topk_dispatch<uint16_t, 128>(a, mean, scores, stride, sel, counters, rmax, st);
-        return a.d == 64 ? route_topk_dispatch<float, 64>(a, mean, scores, stride, sel, counters, rmax, st)
-                         : route_topk_dispatch<float, 128>(a, mean, scores, stride, sel, counters, rmax, st);
+            return a.d == 64 ? route_topk_dispatch<uint16_t, 64>(a, mean, cands, sel, counters, rmax, st)
+                             : route_topk_dispatch<uint16_t, 128>(a, mean, cands, sel, counters, rmax, st);
+        return a.d == 64 ? route_topk_dispatch<float, 64>(a, mean, cands, sel, counters, rmax, st)
+                         : route_topk_dispatch<float, 128>(a, mean, cands, sel, counters, rmax, st);
     }
     const hipError_t e = launch_route(a, mean, scores, stride, st);
     return e != hipSuccess ? e : launch_topk(a, scores, stride, sel, st);
