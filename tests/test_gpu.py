@@ -755,6 +755,9 @@ MANY_ROUTE_TOPK_CASES = [
      None),
     ("d128_r1249", small("ragged_decode_16", batch=1, span_size=16, window=16, top_k=16), [20000], 48,
      None),
+    ("d128_k64", small("ragged_decode_16", batch=1, span_size=64, window=64, top_k=64), [64000], 48, None),
+    ("d128_k64_small_r", small("ragged_decode_16", batch=1, span_size=64, window=64, top_k=64), [64000], 0,
+     "small_r"),
 ]
 
 
@@ -764,7 +767,8 @@ def test_route_topk_spans_many_rows_equals_route_then_topk(name, w, lengths, per
     """Prefill-shaped calls (at least 256 row-heads per kv head): route_topk_spans equals
     route_scores then topk_spans for every row and head, on two calls in a row.  Cases: r near
     1000 and from 1025 to 1061, rows of two sequences interleaved, rows with r from 0 to 1000, a
-    cache whose keys are all equal (every score ties), k = 32, and r up to 1249."""
+    cache whose keys are all equal (every score ties), k = 32 and 64 (the largest, also with r
+    from 0 to 1000), and r up to 1249."""
     c = Case(w, lengths)
     if edit == "constant_keys":
         one = torch.full((w.head_dim,), 0.5, dtype=torch.bfloat16)
