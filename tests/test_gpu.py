@@ -739,6 +739,80 @@ def test_route_topk_spans_equals_route_then_topk(name, w):
     assert not stats["fail"], stats["fail"][:3]
 
 
+# few rows up to 4000 routable spans: one launch up to 1088 spans (the largest call, 1088, with
+# rows at block edges below it), route_scores + topk_spans inside the call beyond
+FEW_LONG_ROUTE_TOPK_CASES = [
+    # name, workload, cache length, the r of each row, edit
+    ("r1088_k16_one_launch", small("ragged_decode_16", batch=1, span_size=16, window=16, top_k=16), 17450,
+     [1088, 1087, 1024, 1023, 257, 256, 255, 129, 128, 127, 16, 15, 0], None),
+    ("r1088_k64_one_launch", small("ragged_decode_16", batch=1, span_size=16, window=16, top_k=64), 17450,
+     [1088, 1000, 200, 65, 64, 63, 0], None),
+    ("r2559_k16", small("ragged_decode_16", batch=1, span_size=16, window=16, top_k=16), 41000,
+     [2559, 2000, 1500, 1089, 1088, 700, 257, 256, 255, 128, 127, 5, 0], None),
+    ("r4000_k16", small("ragged_decode_16", batch=1, span_size=16, window=16, top_k=16), 64100,
+     [4000, 3999, 3000, 2049, 2048, 33], None),
+    ("r4000_k1", small("ragged_decode_16", batch=1, span_size=16, window=16, top_k=1), 64100, [4000, 300, 1, 0],
+     None),
+    ("r2048_k64", small("ragged_decode_16", batch=1, span_size=16, window=16, top_k=64), 32800,
+     [2048, 1500, 129, 64, 63, 0], None),
+    ("r2100_k64_two_calls", small("ragged_decode_16", batch=1, span_size=16, window=16, top_k=64), 34000,
+     [2100, 1000], None),
+    ("r2559_all_scores_tie", small("ragged_decode_16", batch=1, span_size=16, window=16, top_k=16), 41000,
+     [2559, 1000, 129, 3], "constant_keys"),
+]
+
+
+@pytest.mark.parametrize("name,w,length,want_r,edit", FEW_LONG_ROUTE_TOPK_CASES,
+                         ids=[c[0] for c in FEW_LONG_ROUTE_TOPK_CASES])
+def test_route_topk_spans_few_rows_many_spans(name, w, length, want_r, edit):
+    """Decode-shaped calls (fewer than 256 row-heads per kv head) with up to 4000 routable spans:
+    route_topk_spans equals route_scores then topk_spans for every row and head, on three calls in
+    a row, with its counters back at zero; rows with r from 0 up, across the one-launch path's
+    128-span block edges and its largest call (r = 1088), k = 1, 16 and 64, a cache whose keys are
+    all equal (every score ties: the lowest indices win), and calls past the one-launch limit."""
+    c = Case(w, [length])
+    if edit == "constant_keys":
+        one = torch.full((w.head_dim,), 0.5, dtype=torch.bfloat16)
+        kh = c.host[0][0]
+        kh[:] = one.view(torch.int16).numpy().view(np.uint16)
+        c.K[0, :, :length] = one.cuda()
+        c._problems.clear()
+    L = c.lengths
+    c.summarize(np.zeros(c.B, dtype=np.int64), L)
+    rng = np.random.default_rng(31)
+    S, Wn = w.span_size, w.window
+    pos = np.array([min(length - 1, r * S + Wn - 1 + int(rng.integers(0, S))) for r in want_r])
+    got_r = [c.cfg.num_routable(int(t)) for t in pos]
+    assert got_r == want_r, got_r
+    seqs = np.zeros(len(pos), dtype=np.int64)
+    rows, _ = c.rows_for(seqs, pos)
+    n = len(seqs)
+    assert n * w.group < 256  # the few-row regime
+    scores = torch.empty(n, w.num_q_heads, ra.score_stride(c.cfg, int(pos.max())), device="cuda")
+    sel_ref = torch.full((n, w.num_q_heads, w.top_k), -7, dtype=torch.int32, device="cuda")
+    ra.route_scores(c.cfg, rows, c.pipe.span_mean, scores)
+    ra.topk_spans(c.cfg, rows, scores, sel_ref)
+    ws = torch.zeros(ra.workspace_bytes(c.cfg, ra.RA_OP_ROUTE_TOPK, n, int(pos.max())), dtype=torch.uint8,
+                     device="cuda")
+    for rep in range(3):
+        sel = torch.full_like(sel_ref, -9)
+        ra.route_topk_spans(c.cfg, rows, c.pipe.span_mean, sel, ws)
+        torch.cuda.synchronize()
+        if not torch.equal(sel, sel_ref):
+            bad = (sel != sel_ref).any(dim=2).nonzero()[:4].tolist()
+            raise AssertionError("rep %d: %d row-heads differ, e.g. %s: %s vs %s" % (
+                rep, int((sel != sel_ref).any(dim=2).sum()), bad, sel[bad[0][0], bad[0][1]].tolist(),
+                sel_ref[bad[0][0], bad[0][1]].tolist()))
+    counters = ws[:4 * n * w.num_kv_heads].view(torch.int32)
+    assert int(counters.abs().sum()) == 0
+    if edit == "constant_keys":  # every score ties: the m lowest routable indices
+        for i, r in enumerate(want_r):
+            m = min(w.top_k, r)
+            want = np.concatenate([np.arange(m), np.full(w.top_k - m, -1)]).astype(np.int32)
+            assert (sel[i].cpu().numpy() == want[None, :]).all(), (r, sel[i, 0].tolist())
+    log("  %s: %d rows x %d heads, r up to %d" % (name, n, w.num_q_heads, max(want_r)))
+
+
 # many rows and long rows: route_topk_spans runs route_scores + topk_spans through its workspace;
 # the selection must be that of the two calls, bit for bit
 MANY_ROUTE_TOPK_CASES = [
