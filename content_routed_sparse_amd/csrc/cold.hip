@@ -20,6 +20,8 @@
 #include "cold_kernels.h"
 #include "common.h"
 
+#include <type_traits>
+
 namespace ra {
 namespace {
 
@@ -42,13 +44,24 @@ __device__ __forceinline__ int64_t key_pos(uint64_t k) { return (int64_t)(k & ((
 // Word w (elements 32w .. 32w+31) of the signature of a d-element vector: bit i is the sign bit
 // of element 32w + i (bit 15 of a bf16 pattern, bit 31 of an fp32 value).
 template <typename T>
-__device__ __forceinline__ uint32_t sig_word(const T *x, int w) {
+struct WordRaw {
+    uint4 r[32 * sizeof(T) / 16];  // the 32 elements of one signature word
+};
+template <typename T>
+__device__ __forceinline__ WordRaw<T> load_word(const T *x, int w) {
+    WordRaw<T> raw;
+    constexpr int EPL = 16 / sizeof(T);
+#pragma unroll
+    for (int c = 0; c < 32 / EPL; ++c) raw.r[c] = *reinterpret_cast<const uint4 *>(x + 32 * w + c * EPL);
+    return raw;
+}
+template <typename T>
+__device__ __forceinline__ uint32_t pack_word(const WordRaw<T> &raw) {
     uint32_t s = 0;
     constexpr int EPL = 16 / sizeof(T);
 #pragma unroll
     for (int c = 0; c < 32 / EPL; ++c) {
-        const uint4 raw = *reinterpret_cast<const uint4 *>(x + 32 * w + c * EPL);
-        const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+        const uint32_t u[4] = {raw.r[c].x, raw.r[c].y, raw.r[c].z, raw.r[c].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if constexpr (sizeof(T) == 2) {
@@ -60,6 +73,10 @@ __device__ __forceinline__ uint32_t sig_word(const T *x, int w) {
         }
     }
     return s;
+}
+template <typename T>
+__device__ __forceinline__ uint32_t sig_word(const T *x, int w) {
+    return pack_word<T>(load_word<T>(x, w));
 }
 
 template <typename T, int D>
@@ -103,11 +120,16 @@ __device__ __forceinline__ SigWords<D> load_sig(const uint32_t *p) {
     }
     return s;
 }
+// Hamming distance plus d: one XOR and one v_bcnt_u32_b32 (popcount added to its second operand)
+// per word, the counts chained through that operand (written out: the compiler would otherwise
+// sum separate counts with extra adds).
 template <int D>
-__device__ __forceinline__ uint32_t distance(const SigWords<D> &s, const uint32_t *q) {
-    uint32_t d = 0;
+__device__ __forceinline__ uint32_t distance(const SigWords<D> &s, const uint32_t *q, uint32_t d = 0) {
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) d += __popc(s.v[i] ^ q[i]);
+    for (int i = 0; i < D / 32; ++i) {
+        const uint32_t x = s.v[i] ^ q[i];
+        asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(d) : "v"(x), "v"(d));
+    }
     return d;
 }
 
@@ -217,18 +239,25 @@ __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ 
         for (int x = tid; x < G * kc; x += kTileThreads) out0[(x / kc) * head_stride + x % kc] = kNoKey;
         return;
     }
-    // the tile's signatures, kept in registers: token x = i * kTileThreads + tid
+    // Loads in the order they are needed (each wait is for a load and every load before it): the
+    // sample position of this thread and the query words, then the tile's signatures, which stay
+    // in registers (token x = i * kTileThreads + tid) and are still arriving while the sample
+    // sets the thresholds.
     const uint32_t *sbase = sig + (((int64_t)seq * Hkv + g) * cap + lo) * WPR;
+    const int n_s = n_here < kTileThreads ? n_here : kTileThreads;  // sample size
+    const SigWords<D> smp = load_sig<D>(sbase + (int64_t)(tid < n_s ? tid * (n_here / n_s) : 0) * WPR);
+    static_assert(kMaxGroup * WPR <= kTileThreads, "one query word per thread");
+    const bool q_wave = wave * 64 < G * WPR;  // (uniform per wave)
+    const int qx = tid < G * WPR ? tid : 0;
+    WordRaw<T> qraw;
+    if (q_wave) qraw = load_word<T>(q + ((row * Hq + (int64_t)g * G + qx / WPR) * D), qx % WPR);
     SigWords<D> sg[kPerThread];
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         const int x = i * kTileThreads + tid;
         sg[i] = load_sig<D>(sbase + (int64_t)(x < n_here ? x : 0) * WPR);
     }
-    for (int x = tid; x < G * WPR; x += kTileThreads) {
-        const int h = x / WPR, w = x % WPR;
-        qsig[x] = sig_word(q + ((row * Hq + (int64_t)g * G + h) * D), w);
-    }
+    if (q_wave && tid < G * WPR) qsig[tid] = pack_word<T>(qraw);
     for (int x = tid; x < G * kBinStride; x += kTileThreads) hist[x] = 0;
     for (int x = tid; x < G * (kTile / 32); x += kTileThreads) tie[x] = 0;
     if (tid < G) cnt[tid] = 0;
@@ -236,9 +265,7 @@ __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ 
     __syncthreads();
     // 1. a sample of min(kTileThreads, n) positions spread evenly over the tile sets a threshold
     //    per head below which about 3 * kc of the tile's distances should fall
-    const int n_s = n_here < kTileThreads ? n_here : kTileThreads;
     if (tid < n_s) {
-        const SigWords<D> smp = load_sig<D>(sbase + (int64_t)tid * (n_here / n_s) * WPR);
         for (int h = 0; h < G; ++h) atomicAdd(&hist[h * kBinStride + distance<D>(smp, qsig + h * WPR)], 1u);
     }
     __syncthreads();
@@ -249,29 +276,35 @@ __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ 
         if (lane == 0) theta[h] = th < kBins ? th : kBins - 1;
     }
     __syncthreads();
-    // 2. candidates at or below the threshold, appended per wave (ballot + mbcnt: no atomics)
-    for (int h = 0; h < G; ++h) {
-        const uint32_t th = theta[h];
-        uint32_t qw[WPR];
+    // 2. candidates at or below the threshold, appended per wave (ballot + mbcnt: no atomics).
+    //    In the tile's last (partial) block of positions, those past n_here start their distance
+    //    at 256, above every threshold; a full tile needs no such test.
+    auto append = [&](auto ragged) {
+        constexpr bool RAGGED = decltype(ragged)::value;
+        for (int h = 0; h < G; ++h) {
+            const uint32_t th = theta[h];
+            uint32_t qw[WPR];
 #pragma unroll
-        for (int w = 0; w < WPR; ++w) qw[w] = qsig[h * WPR + w];
-        uint32_t *wb = cbuf + (h * kTileWaves + wave) * BW;
-        uint32_t wc = 0;
+            for (int w = 0; w < WPR; ++w) qw[w] = qsig[h * WPR + w];
+            uint32_t *wb = cbuf + (h * kTileWaves + wave) * BW;
+            uint32_t wc = 0;
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            const int x = i * kTileThreads + tid;
-            const uint32_t dd = distance<D>(sg[i], qw);
-            const bool pass = x < n_here && dd <= th;
-            const uint64_t bal = __ballot(pass);
-            if (bal) {
-                const uint32_t idx = wc + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-                if (pass && idx < (uint32_t)BW) wb[idx] = (dd << 16) | (uint32_t)x;
-                wc += (uint32_t)__popcll(bal);
+            for (int i = 0; i < kPerThread; ++i) {
+                const int x = i * kTileThreads + tid;
+                const uint32_t dd = distance<D>(sg[i], qw, RAGGED && x >= n_here ? 256u : 0u);
+                const uint64_t bal = __builtin_amdgcn_ballot_w64(dd <= th);
+                if (bal) {
+                    const uint32_t idx = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, wc));
+                    if (dd <= th && idx < (uint32_t)BW) wb[idx] = (dd << 16) | (uint32_t)x;
+                    wc += (uint32_t)__popcll(bal);
+                }
             }
+            if (lane == 0) wcount[h][wave] = wc;
         }
-        if (lane == 0) wcount[h][wave] = wc;
-    }
+    };
+    if (n_here == kTile) append(std::integral_constant<bool, false>{});
+    else append(std::integral_constant<bool, true>{});
     for (int x = tid; x < G * kBinStride; x += kTileThreads) hist[x] = 0;
     __syncthreads();
     // 3. histograms of the candidates; the cut per head, or the slow path when a wave's buffer
