@@ -10,7 +10,8 @@
 //    against the G query heads of the kv head.  Per head it keeps the tile's kc smallest
 //    (distance, position) keys: an LDS histogram of the distances gives the cut distance D*
 //    (all keys below it are kept, in any order), and the first ties at D* in position order come
-//    from a tie bitmask and a block-wide prefix count.  Tiles write kc keys per head (padded).
+//    from ranking the listed ties by position (or, with many ties, from a tie bitmask and a
+//    block-wide prefix count).  Tiles write kc keys per head (padded).
 //  * cold_merge: one block per (row, query head) selects the kc smallest keys among the tiles'
 //    candidates the same way (histogram -> D*; ties taken tile by tile in position order) and
 //    writes them ascending, padded with -1.
@@ -218,6 +219,7 @@ __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ 
     uint32_t *tie = hist + G * kBinStride;             // [G][kTile / 32]
     uint32_t *cbuf = tie + G * (kTile / 32);           // [G][kTileWaves][BW]: (distance << 16) | index
     __shared__ uint32_t theta[kMaxGroup], cut[kMaxGroup], below[kMaxGroup], need[kMaxGroup], cnt[kMaxGroup];
+    __shared__ uint32_t ntie[kMaxGroup], tlist[kMaxGroup][64];  // ties at the cut per head (fast path)
     __shared__ uint32_t wcount[kMaxGroup][kTileWaves];
     __shared__ uint32_t wave_tot[kTileWaves], slow;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -307,12 +309,15 @@ __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ 
     else append(std::integral_constant<bool, true>{});
     for (int x = tid; x < G * kBinStride; x += kTileThreads) hist[x] = 0;
     __syncthreads();
-    // 3. histograms of the candidates; the cut per head, or the slow path when a wave's buffer
-    //    overflowed or the threshold left fewer than kc_eff candidates
-    for (int e = tid; e < G * kTileWaves * BW; e += kTileThreads) {
-        const int h = e / (kTileWaves * BW), w = (e / BW) % kTileWaves, k = e % BW;
-        if ((uint32_t)k < wcount[h][w]) atomicAdd(&hist[h * kBinStride + (cbuf[e] >> 16)], 1u);
-    }
+    // 3. histograms of the candidates (each wave its own buffers); the cut per head, or the slow
+    //    path when a wave's buffer overflowed or the threshold left fewer than kc_eff candidates
+    auto wave_cands = [&](int h, auto f) {
+        const uint32_t wc = wcount[h][wave] < (uint32_t)BW ? wcount[h][wave] : (uint32_t)BW;
+        const uint32_t *wb = cbuf + (h * kTileWaves + wave) * BW;
+        for (uint32_t k = lane; k < wc; k += 64) f(wb[k]);
+    };
+    for (int h = 0; h < G; ++h)
+        wave_cands(h, [&](uint32_t v) { atomicAdd(&hist[h * kBinStride + (v >> 16)], 1u); });
     __syncthreads();
     for (int h = wave; h < G; h += kTileWaves) {
         uint32_t b;
@@ -323,10 +328,16 @@ __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ 
             cut[h] = ct;
             below[h] = b;
             need[h] = kc_eff - b;
+            ntie[h] = 0;
             if (over || ct == kBins) atomicOr(&slow, 1u);
         }
     }
     __syncthreads();
+    // 4. keys below the cut, and the ties at the cut: the first need[h] of them in position order.
+    //    Fast path: the ties of each head (usually a few) are listed and ranked by position in one
+    //    wave; with more than 64 ties for some head, or after the slow path, they are marked in a
+    //    bitmask per head and counted in position order by a block-wide prefix sum.
+    bool use_mask = slow != 0;
     if (slow) {
         // exact histograms of every distance, then the keys below the cut and the tie bitmasks
         for (int x = tid; x < G * kBinStride; x += kTileThreads) hist[x] = 0;
@@ -360,33 +371,54 @@ __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ 
             }
     } else {
         // every distance up to the cut is among the candidates
-        for (int e = tid; e < G * kTileWaves * BW; e += kTileThreads) {
-            const int h = e / (kTileWaves * BW), w = (e / BW) % kTileWaves, k = e % BW;
-            if ((uint32_t)k >= wcount[h][w]) continue;
-            const uint32_t v = cbuf[e], dd = v >> 16, x = v & 0xFFFFu;
-            if (dd < cut[h]) {
-                out0[h * head_stride + atomicAdd(&cnt[h], 1u)] = cold_key(dd, lo + x);
-            } else if (dd == cut[h]) {
-                atomicOr(&tie[h * (kTile / 32) + (x >> 5)], 1u << (x & 31));
-            }
+        for (int h = 0; h < G; ++h)
+            wave_cands(h, [&](uint32_t v) {
+                const uint32_t dd = v >> 16, x = v & 0xFFFFu;
+                if (dd < cut[h]) {
+                    out0[h * head_stride + atomicAdd(&cnt[h], 1u)] = cold_key(dd, lo + x);
+                } else if (dd == cut[h]) {
+                    const uint32_t i = atomicAdd(&ntie[h], 1u);
+                    if (i < 64) tlist[h][i] = x;
+                }
+            });
+        __syncthreads();
+        for (int h = 0; h < G; ++h) use_mask = use_mask || ntie[h] > 64u;
+        if (use_mask) {
+            for (int h = 0; h < G; ++h)
+                wave_cands(h, [&](uint32_t v) {
+                    const uint32_t x = v & 0xFFFFu;
+                    if ((v >> 16) == cut[h]) atomicOr(&tie[h * (kTile / 32) + (x >> 5)], 1u << (x & 31));
+                });
         }
     }
     __syncthreads();
-    // the first need[h] ties in position order: thread tid < kTile / 32 owns mask word tid
-    for (int h = 0; h < G; ++h) {
-        uint32_t word = tid < kTile / 32 ? tie[h * (kTile / 32) + tid] : 0u;
-        uint32_t total;
-        const uint32_t pre = tile_exclusive_scan<kTileWaves>(__popc(word), wave_tot, total);
-        const uint32_t nd = need[h];
-        if (pre < nd) {
-            const uint32_t take = nd - pre;
-            uint32_t j = 0;
-            while (word && j < take) {
-                const int bit = __builtin_ctz(word);
-                word &= word - 1;
-                out0[h * head_stride + below[h] + pre + j] = cold_key(cut[h], lo + 32 * tid + bit);
-                ++j;
+    if (use_mask) {
+        // thread tid < kTile / 32 owns mask word tid
+        for (int h = 0; h < G; ++h) {
+            uint32_t word = tid < kTile / 32 ? tie[h * (kTile / 32) + tid] : 0u;
+            uint32_t total;
+            const uint32_t pre = tile_exclusive_scan<kTileWaves>(__popc(word), wave_tot, total);
+            const uint32_t nd = need[h];
+            if (pre < nd) {
+                const uint32_t take = nd - pre;
+                uint32_t j = 0;
+                while (word && j < take) {
+                    const int bit = __builtin_ctz(word);
+                    word &= word - 1;
+                    out0[h * head_stride + below[h] + pre + j] = cold_key(cut[h], lo + 32 * tid + bit);
+                    ++j;
+                }
             }
+        }
+    } else {
+        // lane i of a head's wave ranks tie i among the head's ties (positions in the tile are
+        // distinct, so the ranks are 0 .. ntie - 1)
+        for (int h = wave; h < G; h += kTileWaves) {
+            const uint32_t nt = ntie[h], nd = need[h];
+            const uint32_t x = (uint32_t)lane < nt ? tlist[h][lane] : 0xFFFFFFFFu;
+            uint32_t rank = 0;
+            for (uint32_t j = 0; j < nt; ++j) rank += tlist[h][j] < x ? 1u : 0u;
+            if ((uint32_t)lane < nt && rank < nd) out0[h * head_stride + below[h] + rank] = cold_key(cut[h], lo + x);
         }
     }
     // padding past kc_eff

@@ -105,6 +105,28 @@ def few_sign_patterns(c):
         c.K[0, g, :L] = t.cuda()
 
 
+def query_copies(c):
+    """Every 150th key of sequence 0 (about 109 per scan tile of 16384 positions) gets the signs
+    of the query of head G g of its kv head g at the last position, so that head has more than 64
+    ties at distance 0 in every tile: the ties are ranked from the bitmask, not the short list."""
+    rng = np.random.default_rng(22)
+    w = c.w
+    L = int(c.lengths[0])
+    qh = WL.query_at(w, 0, L - 1)
+    qf = torch.from_numpy(qh.view(np.int16)).view(torch.bfloat16).float().numpy() if c.is_bf16 else qh
+    pos = np.arange(0, L - 256, 150)
+    for g in range(w.num_kv_heads):
+        signs = np.where(np.signbit(qf[g * w.group]), -1.0, 1.0)
+        vals = (np.abs(rng.standard_normal((len(pos), w.head_dim))) + 0.1) * signs
+        t = torch.from_numpy(vals.astype(np.float32))
+        if c.is_bf16:
+            t = t.to(torch.bfloat16)
+            c.host[0][0][g, pos] = t.view(torch.int16).numpy().view(np.uint16)
+        else:
+            c.host[0][0][g, pos] = t.numpy()
+        c.K[0, g, torch.from_numpy(pos).cuda()] = t.cuda()
+
+
 CASES = [
     # name, workload, lengths, H, top_k_cold, edit
     ("d128_G8_kc64_20k", small("decode_1m", decode_len=20000), [20000], 256, 64, None),
@@ -115,6 +137,7 @@ CASES = [
     ("G32_kc32", small("decode_1m", num_q_heads=32, num_kv_heads=1, decode_len=12000), [12000], 64, 32, None),
     ("heavy_ties", small("decode_1m", num_q_heads=8, num_kv_heads=2, decode_len=30000), [30000], 256, 64,
      few_sign_patterns),
+    ("over_64_ties_per_tile", small("decode_1m", decode_len=40000), [40000], 256, 64, query_copies),
 ]
 
 
