@@ -61,6 +61,14 @@ def parse():
     return p.parse_args()
 
 
+def progress(msg):
+    """One line on stderr as each leg ends (stdout carries only the JSON line)."""
+    print("[bench] %s (%.0f s)" % (msg, time.time() - T_START), file=sys.stderr, flush=True)
+
+
+T_START = time.time()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -92,6 +100,7 @@ def main():
           for s in range(NC)]
     torch.cuda.synchronize()
     gen_s = time.time() - t0
+    progress("decode_1m caches ready")
 
     # ---- per-sequence state and buffers (allocated once)
     stride = ra.score_stride(cfg1, L - 1)
@@ -240,15 +249,19 @@ def main():
         "repeat_bitwise_identical": bool(same),
         "setup_seconds": round(gen_s, 1),
     }
+    progress("decode_1m done")
 
     if not args.no_fp8:
         result["decode_fp8"] = bench_decode_fp8(args, w, K, V, qs)
+        progress("decode_fp8 done")
 
     if not args.no_cold:
         result["cold_retrieval"] = bench_cold(args, w, K, V, qs)
+        progress("cold_retrieval done")
 
     if not args.no_snapshot:
         result["snapshot"] = bench_snapshot(w, st[0], cfg1)
+        progress("snapshot done")
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -263,12 +276,14 @@ def main():
             w, kv0, [L], [WL.query_at(w, 0, L - 1)], args.cpu_seconds, st[0]["sel"].cpu().numpy(),
             st[0]["out"].cpu().numpy())
         del kv0
+        progress("decode_1m cpu baseline done")
 
     if not args.no_prefill:
         del K, V, st
         torch.cuda.empty_cache()
         result["prefill"] = bench_prefill(args.prefill_steps, args.dense_steps, not args.no_ladder,
                                           0.0 if args.no_cpu_baseline else args.cpu_seconds, not args.no_fp8)
+        progress("prefill done")
 
     if not args.no_extra:
         if args.no_prefill:
@@ -277,10 +292,12 @@ def main():
         result["decode_other"] = [bench_decode_workload(name, max(8, args.steps // 2), args.warmup,
                                                         0.0 if args.no_cpu_baseline else args.cpu_seconds)
                                   for name in ("decode_10m", "ragged_decode_16")]
+        progress("decode_other done")
 
     if not args.no_tiny:
         result["tiny_prefill"] = bench_tiny_prefill(max(20, args.steps // 4), 0.0 if args.no_cpu_baseline else
                                                     args.cpu_seconds)
+        progress("tiny_prefill done")
 
     print(json.dumps(result), flush=True)
 
@@ -339,6 +356,7 @@ def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0, fp8=True):
     run = torch.zeros(1, w.num_kv_heads, w.head_dim, dtype=torch.float32, device=dev)
     t_p, t_l = torch.tensor([P], device=dev), torch.tensor([L], device=dev)
     ra.span_summary_update(cfg, K, mean, run, torch.zeros(1, dtype=torch.int64, device=dev), t_p, P)  # setup
+    progress("prefill cache ready")
     sel = torch.empty(n, w.num_q_heads, w.top_k, dtype=torch.int32, device=dev)
     out = torch.empty(n, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
     ws = torch.empty(ra.workspace_bytes(cfg, ra.RA_OP_PREFILL, n, L - 1), dtype=torch.uint8, device=dev)
@@ -380,7 +398,10 @@ def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0, fp8=True):
     route_flops = 2.0 * d * r.astype(np.float64).sum() * w.num_q_heads
     tflops = attn_flops / (attn_ms * 1e-3) / 1e12
 
+    progress("prefill bf16 done")
     fp8_leg = bench_prefill_fp8(w, cfg, K, V, rows, t_p, t_l, steps, attn_flops, route_flops, out) if fp8 else None
+    if fp8:
+        progress("prefill fp8 done")
 
     # the same rows with dense causal attention over the whole prefix (the brute-force scan that
     # routing replaces; its flops are 4 d per (row-head, key <= t))
