@@ -426,16 +426,34 @@ __global__ void __launch_bounds__(kTileThreads) cold_tile(const T *__restrict__ 
         if ((uint32_t)(x % kc) >= kc_eff) out0[(x / kc) * head_stride + x % kc] = kNoKey;
 }
 
-// kc <= kMaxCold, n_tiles <= kMergeTiles.  Candidates are read three times, coalesced and in
-// batches of kMergeBatch independent loads per thread (they stay in L2): the distance histogram;
+// kc <= kMaxCold, n_tiles <= kMergeTiles.  Candidates are visited three times, coalesced and in
+// batches of kMergeBatch independent loads per thread (the first batch kept in registers, later
+// ones read again from L2): the distance histogram;
 // keys below the cut and per-tile tie counts; the ties of every tile whose ties are all taken.
 // The one tile whose ties are taken in part ranks them by position.
 constexpr int kMergeThreads = 512;
 constexpr int kMergeBatch = 8;
 
+// The first kMergeThreads * kMergeBatch keys (all of them at 1M: 64 tiles x 64) are loaded once
+// and kept in registers for the three passes; later batches are loaded again by each pass.
+struct KeyRegs {
+    uint64_t k[kMergeBatch];
+};
+__device__ __forceinline__ KeyRegs load_first_keys(const uint64_t *c, int M) {
+    KeyRegs r;
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) {
+        const int x = threadIdx.x + b * kMergeThreads;
+        r.k[b] = x < M ? c[x] : kNoKey;
+    }
+    return r;
+}
 template <typename F>
-__device__ __forceinline__ void for_each_key(const uint64_t *c, int M, F f) {
-    for (int x0 = threadIdx.x; x0 < M; x0 += kMergeThreads * kMergeBatch) {
+__device__ __forceinline__ void for_each_key(const uint64_t *c, int M, const KeyRegs &r, F f) {
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b)
+        if (r.k[b] != kNoKey) f((int)threadIdx.x + b * kMergeThreads, r.k[b]);
+    for (int x0 = threadIdx.x + kMergeThreads * kMergeBatch; x0 < M; x0 += kMergeThreads * kMergeBatch) {
         uint64_t k[kMergeBatch];
 #pragma unroll
         for (int b = 0; b < kMergeBatch; ++b) {
@@ -459,6 +477,7 @@ __global__ void __launch_bounds__(kMergeThreads) cold_merge(const uint64_t *__re
     const int64_t rh = blockIdx.x;
     const uint64_t *c = cand + rh * (int64_t)n_tiles * kc;
     const int M = n_tiles * kc;
+    const KeyRegs kr = load_first_keys(c, M);  // (in flight while the LDS is cleared)
     for (int x = tid; x < kBinStride; x += kMergeThreads) hist[x] = 0;
     for (int x = tid; x < n_tiles; x += kMergeThreads) tcnt[x] = 0;
     if (tid == 0) {
@@ -469,7 +488,7 @@ __global__ void __launch_bounds__(kMergeThreads) cold_merge(const uint64_t *__re
     }
     __syncthreads();
     uint32_t mine = 0;
-    for_each_key(c, M, [&](int, uint64_t k) {
+    for_each_key(c, M, kr, [&](int, uint64_t k) {
         atomicAdd(&hist[key_dist(k)], 1u);
         ++mine;
     });
@@ -487,7 +506,7 @@ __global__ void __launch_bounds__(kMergeThreads) cold_merge(const uint64_t *__re
     __syncthreads();
     const uint32_t dstar = s_cut, nd = s_need;
     if (kc_eff > 0) {
-        for_each_key(c, M, [&](int x, uint64_t k) {
+        for_each_key(c, M, kr, [&](int x, uint64_t k) {
             const uint32_t dd = key_dist(k);
             if (dd < dstar) lst[atomicAdd(&n_lst, 1u)] = key_pos(k);
             else if (dd == dstar) atomicAdd(&tcnt[x / kc], 1u);
@@ -523,7 +542,7 @@ __global__ void __launch_bounds__(kMergeThreads) cold_merge(const uint64_t *__re
     }
     __syncthreads();
     if (kc_eff > 0) {
-        for_each_key(c, M, [&](int x, uint64_t k) {
+        for_each_key(c, M, kr, [&](int x, uint64_t k) {
             const int j = x / kc;
             if (key_dist(k) == dstar && tpre[j] + tcnt[j] <= nd) lst[atomicAdd(&n_lst, 1u)] = key_pos(k);
         });
@@ -550,8 +569,12 @@ __global__ void __launch_bounds__(kMergeThreads) cold_merge(const uint64_t *__re
     if (tid < kc) {
         if ((uint32_t)tid < kc_eff) {
             const int64_t p = lst[tid];
-            uint32_t rank = 0;
-            for (uint32_t x = 0; x < kc_eff; ++x) rank += lst[x] < p ? 1u : 0u;
+            uint32_t rank = 0, x = 0;
+            for (; x + 4 <= kc_eff; x += 4) {  // (four independent reads per step)
+                const int64_t a0 = lst[x], a1 = lst[x + 1], a2 = lst[x + 2], a3 = lst[x + 3];
+                rank += (a0 < p ? 1u : 0u) + (a1 < p ? 1u : 0u) + (a2 < p ? 1u : 0u) + (a3 < p ? 1u : 0u);
+            }
+            for (; x < kc_eff; ++x) rank += lst[x] < p ? 1u : 0u;
             out[rank] = (int32_t)p;
         } else {
             out[tid] = -1;

@@ -138,6 +138,8 @@ CASES = [
     ("heavy_ties", small("decode_1m", num_q_heads=8, num_kv_heads=2, decode_len=30000), [30000], 256, 64,
      few_sign_patterns),
     ("over_64_ties_per_tile", small("decode_1m", decode_len=40000), [40000], 256, 64, query_copies),
+    # 37 tiles x 128 candidates per head: more than the merge keeps in registers (4096)
+    ("kc128_600k_merge_batches", small("decode_1m", decode_len=600000), [600000], 256, 128, None),
 ]
 
 
