@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true", help="replay the step from HIP graphs instead of launching")
     p.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
-    p.add_argument("--prefill-steps", type=int, default=5)
+    p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--dense-steps", type=int, default=2,
                    help="timed calls of dense causal attention on the prefill rows (0: skip)")
     p.add_argument("--no-ladder", action="store_true",
@@ -282,7 +282,8 @@ def main():
         del K, V, st
         torch.cuda.empty_cache()
         result["prefill"] = bench_prefill(args.prefill_steps, args.dense_steps, not args.no_ladder,
-                                          0.0 if args.no_cpu_baseline else args.cpu_seconds, not args.no_fp8)
+                                          0.0 if args.no_cpu_baseline else args.cpu_seconds, not args.no_fp8,
+                                          args.warmup)
         progress("prefill done")
 
     if not args.no_extra:
@@ -330,7 +331,7 @@ def counter_traffic(tag):
     return rec.get("bytes_per_launch") if rec.get("source_sha256") == h.hexdigest() else None
 
 
-def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0, fp8=True):
+def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0, fp8=True, warmup=10):
     """Chunked prefill: 8192 new tokens appended to a 1M-token cache (the chunk's K/V are in
     the cache before timing).  A step = span_summary_update of the chunk + route_topk_spans
     (route_scores + topk_spans in one call) + routed_attn_prefill for its 8192 x 32 row-heads.
@@ -370,9 +371,10 @@ def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0, fp8=True):
     attn = ra.prepare("routed_attn_prefill", cfg, rows, K, V, sel, out, ws)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for c in calls:
-        c()
-    attn()
+    for _ in range(max(1, warmup)):  # untimed steps, as for decode (clocks and caches settle)
+        for c in calls:
+            c()
+        attn()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -399,7 +401,7 @@ def bench_prefill(steps, dense_steps=2, ladder=True, cpu_seconds=0.0, fp8=True):
     tflops = attn_flops / (attn_ms * 1e-3) / 1e12
 
     progress("prefill bf16 done")
-    fp8_leg = bench_prefill_fp8(w, cfg, K, V, rows, t_p, t_l, steps, attn_flops, route_flops, out) if fp8 else None
+    fp8_leg = bench_prefill_fp8(w, cfg, K, V, rows, t_p, t_l, steps, attn_flops, route_flops, out, warmup) if fp8 else None
     if fp8:
         progress("prefill fp8 done")
 
@@ -476,7 +478,7 @@ def prefill_algorithmic_bytes(w, sel_h, elem_bytes, row_scale_bytes=0):
     return int(kv + n * w.num_q_heads * (d * 2 + w.top_k * 4 + d * 4) + n * 12)
 
 
-def bench_prefill_fp8(w, cfg, K, V, rows, t_p, t_l, steps, attn_flops, route_flops, out_bf16):
+def bench_prefill_fp8(w, cfg, K, V, rows, t_p, t_l, steps, attn_flops, route_flops, out_bf16, warmup=10):
     """The prefill step over the 8-bit cache: span_summary_update_fp8 of the chunk +
     route_topk_spans + routed_attn_prefill_fp8.  The tiles convert the codes to bf16 in LDS and run the
     same bf16 MFMA products, so the flops and the peak are those of the bf16 step."""
@@ -505,9 +507,10 @@ def bench_prefill_fp8(w, cfg, K, V, rows, t_p, t_l, steps, attn_flops, route_flo
     attn = ra.prepare("routed_attn_prefill_fp8", cfg, rows, K8, V8, KS, VS, sel, out, ws)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for c in calls:
-        c()
-    attn()
+    for _ in range(max(1, warmup)):
+        for c in calls:
+            c()
+        attn()
     torch.cuda.synchronize()
     first = out.clone()
     t0 = time.perf_counter()

@@ -35,9 +35,11 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
 // given (0 for j >= r) the m = min(k, r) largest keys  img << 32 | (0xFFFFFFFF - j)  and writes
 // their span indices to out[0..k) (ascending, -1 padded).  cand: 64 words of LDS owned by the wave.
 //
-// Threshold first: v = the m-th largest of the 64 per-lane maximum images, found bit by bit from
-// the top: a bit is kept when at least m lanes still reach the value (one ballot per bit).  At
-// least m lanes then hold an image >= v, so every one of the m winners has an image >= v.  The
+// Threshold first: v = the m-th largest of the 64 per-lane maximum images with its low 16 bits
+// cleared, found bit by bit from the top: a bit is kept when at least m lanes still reach the
+// value (one ballot per bit, 16 bits: sign, exponent and 7 significand bits of the score).  At
+// least m lanes then hold an image >= v, so every one of the m winners has an image >= v (the
+// cleared bits only lower v: the extra candidates are scores within 2^-7 of the threshold).  The
 // spans with images >= v (usually little more than m; more only where scores tie) are compacted
 // into LDS in span order as 64-bit keys and each is ranked against the others; if more than 64
 // pass, the selection falls back to m rounds of "largest key below the previous winner".  Only
@@ -57,7 +59,7 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&img)[PER_LANE], int m
     // search ends on a valid image
     uint32_t v = 0;
 #pragma unroll
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = 31; bit >= 16; --bit) {
         const uint32_t test = v | (1u << bit);
         if ((int)__builtin_popcountll(__ballot(lmax >= test)) >= m) v = test;
     }
