@@ -243,16 +243,24 @@ __global__ void scatter_kernel(const int32_t *__restrict__ sel, const int32_t *_
     list_t[offsets[expert] + slot] = t;
 }
 
-// Tile descriptors: (expert, first entry in the list, entries in the tile).
-__global__ void tiles_kernel(const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
-                             const int32_t *__restrict__ tile_off, int4 *__restrict__ tiles, int64_t n_exp, int MT) {
-    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Tile descriptors: (expert, first entry in the list, entries in the tile).  One wave per expert,
+// its lanes taking the bucket's tiles in turn: the buckets of the spans inside a chunk's windows
+// hold many times the entries of a routed span's bucket (one thread per expert left those few
+// threads with a long serial loop of stores).
+constexpr int kTilesWaves = 4;  // experts per block
+
+__global__ void __launch_bounds__(kTilesWaves * 64) tiles_kernel(const int32_t *__restrict__ counts,
+                                                                 const int32_t *__restrict__ offsets,
+                                                                 const int32_t *__restrict__ tile_off,
+                                                                 int4 *__restrict__ tiles, int64_t n_exp, int MT) {
+    const int64_t x = (int64_t)blockIdx.x * kTilesWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     if (x >= n_exp) return;
     const int32_t c = counts[x];
     const int32_t base = tile_off[x];
     const int32_t first = offsets[x];
     const int32_t Q = (tile_off[n_exp] + 7) / 8;  // tiles per XCD
-    for (int32_t i = 0; i * MT < c; ++i) {
+    for (int32_t i = lane; i * MT < c; i += 64) {
         const int32_t t = base + i;
         tiles[tile_slot(t, Q)] = make_int4((int32_t)x, first + i * MT, c - i * MT < MT ? c - i * MT : MT, 0);
     }
@@ -391,7 +399,9 @@ int64_t prefill_grid_items(const RowArgs &a) {
     const int64_t tiles = L.max_tiles * 256;                         // tile kernels: 256 threads
     const int64_t merge = ceil_div(a.n_rows * a.Hq, 4) * 256;        // combine_wave: 4 row-heads per block
     const int64_t count = ceil_div(L.n_ent, 256) * 256;              // count / scatter: one thread per entry
+    const int64_t descs = L.n_exp * 64;                               // tiles_kernel: one wave per expert
     int64_t m = tiles > merge ? tiles : merge;
+    m = m > descs ? m : descs;
     return m > count ? m : count;
 }
 
@@ -429,8 +439,8 @@ hipError_t prefill_impl(const RowArgs &a, const void *K, const void *V, const fl
                        a.row_pos, offsets, local, list, list_t, L.n_ent, NE, a.Hq, a.Hkv, a.G, a.S, a.k, a.W, a.B,
                        a.max_pos,
                        L.span_slots);
-    hipLaunchKernelGGL(tiles_kernel, dim3((unsigned)ceil_div(L.n_exp, 256)), dim3(256), 0, st, counts, offsets,
-                       tile_off, tiles, L.n_exp, MT);
+    hipLaunchKernelGGL(tiles_kernel, dim3((unsigned)ceil_div(L.n_exp, kTilesWaves)), dim3(kTilesWaves * 64), 0, st,
+                       counts, offsets, tile_off, tiles, L.n_exp, MT);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     TileArgs ta{a, K, V, ks, vs, tile_off, list, list_t, tiles, records, L.n_exp, L.max_tiles, L.span_slots, NE};
